@@ -1,0 +1,300 @@
+"""CPU oracle of the top-k Mixture-of-Experts SwiGLU FFN layer forward.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The
+product path (the HIP library and its Python binding) never does; this code
+shares nothing with it but the seeded inputs of ``moe_inputs``.
+
+What it computes is the plain definition of the layer, token by token, with
+no permutation buffer, no blocking and no fusion:
+
+1. router logits, one dot product per (token, expert), accumulated in fp64
+   and rounded once to fp32, plus an optional per-expert fp32 offset;
+2. selection keys (logit plus an optional selection-only bias, in fp32) and
+   top-k by (key descending, expert index ascending);
+3. gate values in fp64 from the fp32 logits, rounded to fp32;
+4. per-expert token counts and ranks in token order; with a capacity C an
+   assignment whose rank is C or more is dropped;
+5. for every kept (token, slot): the expert's SwiGLU FFN in fp64;
+6. the gate-weighted sum of the kept expert outputs, in slot order, plus the
+   shared expert's output when there is one.
+
+Sources (pages and the part of each that is followed):
+
+* "Megatron-LM 分布式训练（六）：MoE 专家并行 EP 与上下文并行 CP"
+  (swordlidev.github.io): section "MoE 层的数据流" (router → dispatch →
+  experts → combine, optional shared experts added) and section
+  "Router：token 怎么选专家" (logits = hidden · W_router, then top-k with
+  softmax or sigmoid weights).
+* "v6:长序列和 MoE:Context Parallel 与 Expert Parallel"
+  (charliedreemur.github.io, infra-l7): section "MoE:参数很多,每个 token
+  只算一点" (an expert is the SwiGLU FFN h → F → h with three matrices) and
+  section "NVIDIA 原题" (dimension table [T,h] → [T,E] → [T,k] → [E,C,h] →
+  [T,h]; capacity C = cf·k·T/E with overflow dropped; DeepSeek-V3's
+  selection-only bias), and its "自测" answers (an overflowing token is
+  dropped on that expert only; padding fills unused capacity slots; sorting
+  tokens by expert before one grouped GEMM).
+* "专家并行" (formulaic.cloudchewie.com, 7-expert-parallel): section "EP+DP",
+  forward of the MoE layer (each token's expert outputs are gathered back and
+  summed with the top-k weights).
+* "10.5 序列并行与专家并行" (paper.xwysyy.cn): 10.5.5 (combine weights the
+  expert outputs by the routing weights) and 10.5.6 (capacity factor, excess
+  tokens dropped or passed on by the residual).
+
+Readings where the pages are silent or disagree (all listed in the design doc):
+
+* gate modes: "softmax_topk" = softmax over the k selected logits;
+  "softmax_all_topk" = softmax over all E logits, the selected k values
+  taken without renormalising (the worked example's order);
+  "sigmoid_topk_norm" = per-expert sigmoid, normalised over the selected k;
+* top-k always compares the fp32 selection key, ties to the lower index;
+* C = ceil(cf·k·T/E) in exact integer arithmetic (cf given as num/den);
+* overflow keeps the first C assignments in token order; a dropped slot adds
+  nothing and the other gates are not renormalised;
+* the expert FFN is W2 · (silu(W1 x) ⊙ (W3 x)) with silu(z) = z/(1+e^-z);
+* the layer output excludes the residual; the shared expert has weight 1.
+
+Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
+against hand-worked fixtures, closed forms and brute force; none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+GATE_MODES = ("softmax_topk", "softmax_all_topk", "sigmoid_topk_norm")
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# 1. Router logits.  Megatron-LM part 6, "Router：token 怎么选专家": the gating
+# step multiplies the hidden states by the router weight; infra-l7,
+# "NVIDIA 原题" table, row "router": x [T,h] times Wr [h,E] gives [T,E].
+# The router weight is stored [E,h] here (its transpose).
+# ---------------------------------------------------------------------------
+def router_logits(x, w_router, logit_bias=None) -> np.ndarray:
+    """fp32 [T,E]: l[t,e] = fp32(sum_i x[t,i] * w_router[e,i]) (+ bias[e] in fp32)."""
+    l = (_f64(x) @ _f64(w_router).T).astype(np.float32)
+    if logit_bias is not None:
+        l = (l + np.asarray(logit_bias, dtype=np.float32)[None, :]).astype(np.float32)
+    return l
+
+
+def selection_keys(logits, select_bias=None) -> np.ndarray:
+    """fp32 [T,E] key the top-k compares.
+
+    infra-l7, "NVIDIA 原题", load-balancing bullet: the aux-loss-free scheme
+    adds a per-expert bias that only takes part in choosing the top-k.
+    """
+    k = np.asarray(logits, dtype=np.float32)
+    if select_bias is not None:
+        k = (k + np.asarray(select_bias, dtype=np.float32)[None, :]).astype(np.float32)
+    return k
+
+
+# ---------------------------------------------------------------------------
+# 2. Top-k.  Megatron-LM part 6, "Router": top-k over the logits picks each
+# token's k experts; infra-l7 table row "top-k": [T,k].  Order: key
+# descending, lower expert index first on equal keys.
+# ---------------------------------------------------------------------------
+def topk(keys, k: int) -> np.ndarray:
+    """int32 [T,k]; slot 0 holds the largest key."""
+    keys = np.asarray(keys, dtype=np.float32)
+    E = keys.shape[1]
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    # A stable sort of the negated keys keeps equal keys in index order.
+    order = np.argsort(-keys, axis=1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def near_tie(keys, k: int, threshold: float = 1e-5) -> np.ndarray:
+    """bool [T]: gap between the k-th and (k+1)-th largest key below threshold.
+
+    Either choice is correct for such a token when two implementations round
+    the logits differently; with k = E there is no (k+1)-th key.
+    """
+    keys = np.asarray(keys, dtype=np.float32)
+    T, E = keys.shape
+    if k >= E:
+        return np.zeros(T, dtype=bool)
+    s = -np.sort(-keys.astype(np.float64), axis=1)
+    return (s[:, k - 1] - s[:, k]) < threshold
+
+
+# ---------------------------------------------------------------------------
+# 3. Gates.  Megatron-LM part 6, "Router": weights by softmax or sigmoid;
+# infra-l7 table rows "router"/"top-k": softmax over E, then the top-k gate
+# values.  Computed in fp64 from the fp32 logits, rounded to fp32.
+# ---------------------------------------------------------------------------
+def gates(logits, idx, mode: str) -> np.ndarray:
+    """fp32 [T,k] gate of each selected slot."""
+    l = _f64(logits)
+    idx = np.asarray(idx)
+    sel = np.take_along_axis(l, idx, axis=1)            # [T,k] selected logits
+    if mode == "softmax_topk":
+        m = sel.max(axis=1, keepdims=True)
+        ex = np.exp(sel - m)
+        g = ex / ex.sum(axis=1, keepdims=True)
+    elif mode == "softmax_all_topk":
+        m = l.max(axis=1, keepdims=True)
+        ex = np.exp(l - m)
+        p = ex / ex.sum(axis=1, keepdims=True)
+        g = np.take_along_axis(p, idx, axis=1)
+    elif mode == "sigmoid_topk_norm":
+        s = 1.0 / (1.0 + np.exp(-sel))
+        g = s / s.sum(axis=1, keepdims=True)
+    else:
+        raise ValueError(f"unknown gate mode {mode!r}")
+    return g.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# 4. Capacity and routing maps.  infra-l7, "NVIDIA 原题": dispatch groups
+# tokens by expert, at most C per group, unfilled places padded, giving
+# [E,C,h]; C = cf·k·T/E (1280 at T=4096, E=8, k=2, cf=1.25) and tokens past
+# it are dropped; Megatron's default has no capacity (dropless).  "自测": a
+# token past capacity is dropped on that expert only; sorting the tokens by
+# expert lets one grouped GEMM run all experts.
+# ---------------------------------------------------------------------------
+def capacity(T: int, E: int, k: int, cf_num: int, cf_den: int) -> int:
+    """C = ceil(cf_num * k * T / (cf_den * E)), exact integers."""
+    if min(T, E, k, cf_num, cf_den) <= 0:
+        raise ValueError("capacity needs positive T, E, k and cf")
+    num = cf_num * k * T
+    den = cf_den * E
+    return -(-num // den)
+
+
+def route_maps(idx, E: int, C: Optional[int] = None) -> dict:
+    """Per-expert counts, group offsets and the (token, slot) -> row map.
+
+    rank(t, j): number of tokens t' < t that also chose expert idx[t, j]
+    (a token picks an expert at most once).  Dropless: rows of expert e are
+    offsets[e] .. offsets[e+1]-1, row = offsets[e] + rank.  With capacity C:
+    expert e owns rows e*C .. e*C+C-1, kept iff rank < C, row = e*C + rank,
+    else -1 (dropped).  row_token[row] = token, -1 for padding rows.
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    counter = [0] * E
+    rank = np.empty((T, k), dtype=np.int64)
+    for t in range(T):              # token order decides the ranks
+        for j in range(k):
+            e = int(idx[t, j])
+            rank[t, j] = counter[e]
+            counter[e] += 1
+    counts = np.array(counter, dtype=np.int64)
+    if C is None:
+        offsets = np.zeros(E + 1, dtype=np.int64)
+        offsets[1:] = np.cumsum(counts)
+        rows = int(offsets[-1])
+        assign_row = offsets[idx] + rank
+    else:
+        offsets = np.arange(E + 1, dtype=np.int64) * C
+        rows = E * C
+        assign_row = np.where(rank < C, idx.astype(np.int64) * C + rank, -1)
+    row_token = np.full(rows, -1, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            r = int(assign_row[t, j])
+            if r >= 0:
+                row_token[r] = t
+    kept = counts if C is None else np.minimum(counts, C)
+    return {
+        "counts": counts,
+        "offsets": offsets,
+        "kept": kept,
+        "rank": rank,
+        "assign_row": assign_row,
+        "row_token": row_token,
+        "rows": rows,
+    }
+
+
+# ---------------------------------------------------------------------------
+# 5. Expert FFN.  infra-l7, "MoE:参数很多" section: each expert is the dense
+# SwiGLU FFN h → F → h with three h×F matrices; "NVIDIA 原题" table row
+# "expert".  Reading: W1 carries the SiLU, W3 the linear branch.
+# ---------------------------------------------------------------------------
+def silu(z):
+    z = _f64(z)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(xrows, w1, w3, w2) -> np.ndarray:
+    """fp64 [n,h] = W2 · (silu(W1 x) ⊙ (W3 x)) for each row x of xrows."""
+    xr = _f64(xrows)
+    a1 = xr @ _f64(w1).T          # [n,F]
+    a3 = xr @ _f64(w3).T          # [n,F]
+    u = silu(a1) * a3
+    return u @ _f64(w2).T         # [n,h]
+
+
+# ---------------------------------------------------------------------------
+# 6. Whole layer.  Megatron-LM part 6, "MoE 层的数据流": router, dispatch,
+# experts, combine, plus shared experts every token passes through;
+# 专家并行, "EP+DP" forward: the top-k outputs of a token are summed with
+# their gate weights; infra-l7 table row "combine" and "自测" (a dropped slot
+# contributes nothing; the rest of the token goes on by the residual, which
+# this layer's output excludes).
+# ---------------------------------------------------------------------------
+def moe_forward(x, w_router, w1, w3, w2, *, k: int, gate: str,
+                C: Optional[int] = None, logit_bias=None, select_bias=None,
+                shared=None, tokens=None, idx=None, maps_only=False) -> dict:
+    """Reference forward.
+
+    x [T,h]; w_router [E,h]; w1, w3 [E,F,h]; w2 [E,h,F] (any array-likes of
+    the exact values the device gets).  ``shared`` = (ws1, ws3, ws2) or None.
+    ``tokens``: optional 1-D array of token ids whose outputs are computed
+    (routing, ranks and drops still cover all T tokens).  ``idx``: optional
+    externally chosen top-k (used to recompute maps from another selection);
+    when given, gates still come from this oracle's logits.
+    Returns logits, keys, idx, gates, near_tie, maps, and ``y`` (fp64) for the
+    requested tokens, in the order of ``tokens``.
+    """
+    x = np.asarray(x)
+    T = x.shape[0]
+    E = np.asarray(w_router).shape[0]
+    logits = router_logits(x, w_router, logit_bias)
+    keys = selection_keys(logits, select_bias)
+    if idx is None:
+        idx = topk(keys, k)
+    idx = np.asarray(idx).astype(np.int32)
+    g = gates(logits, idx, gate)
+    maps = route_maps(idx, E, C)
+    out = {"logits": logits, "keys": keys, "idx": idx, "gates": g,
+           "near_tie": near_tie(keys, k), "maps": maps}
+    if maps_only:
+        return out
+
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    h = x.shape[1]
+    y = np.zeros((len(tok), h), dtype=np.float64)
+    xs = _f64(x[tok])
+    # Expert outputs of every kept (token, slot); experts are independent,
+    # so each expert's rows are one matrix product.
+    o = np.zeros((len(tok), k, h), dtype=np.float64)
+    sel = idx[tok]                                  # [n,k]
+    kept = maps["assign_row"][tok] >= 0             # [n,k]
+    for e in range(E):
+        mask = (sel == e) & kept
+        if not mask.any():
+            continue
+        rows_n, slots = np.nonzero(mask)
+        o[rows_n, slots] = swiglu_ffn(xs[rows_n], w1[e], w3[e], w2[e])
+    gsel = _f64(g[tok])
+    for j in range(k):                              # slot order
+        y += np.where(kept[:, j:j + 1], gsel[:, j:j + 1] * o[:, j], 0.0)
+    if shared is not None:
+        ws1, ws3, ws2 = shared
+        y += swiglu_ffn(xs, ws1, ws3, ws2)
+    out["y"] = y
+    out["tokens"] = tok
+    return out

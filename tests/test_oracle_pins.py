@@ -1,0 +1,370 @@
+"""Pins of the CPU oracle to facts outside itself (no GPU needed).
+
+Every pin is a hand-worked fixture under tests/golden/ (with its citation), a
+closed form, a special case that reduces to something simpler, or brute
+force on tiny inputs.  Each is chosen so that a plausible slip in the oracle
+(a transposed operand, a wrong sign, the SiLU on the wrong branch, ranks in
+slot order instead of token order, renormalised gates after a drop) fails.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from moe_inputs import CONFIGS, make_inputs
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------- capacity
+def test_capacity_worked_example(golden_dir):
+    g = _load(golden_dir, "worked_example.json")
+    C = oracle.capacity(g["T"], g["E"], g["k"], g["cf_num"], g["cf_den"])
+    assert C == g["capacity"] == 1280
+
+
+@pytest.mark.parametrize("T,E,k,num,den,C", [
+    (10, 4, 1, 1, 1, 3),        # 2.5 rounds up
+    (8, 4, 1, 1, 1, 2),         # exact
+    (16384, 64, 4, 1, 1, 1024),
+    (6, 4, 2, 1, 1, 3),
+    (7, 3, 2, 5, 4, 6),         # 70/12 = 5.83 -> 6
+])
+def test_capacity_closed_form(T, E, k, num, den, C):
+    assert oracle.capacity(T, E, k, num, den) == C
+
+
+# ----------------------------------------------------------------- logits
+def test_router_logits_orientation():
+    rng = np.random.default_rng(1)
+    E, h = 5, 7
+    w = rng.standard_normal((E, h)).astype(np.float32)
+    x = np.eye(h, dtype=np.float32)[[3, 0, 6]]          # one-hot tokens
+    l = oracle.router_logits(x, w)
+    assert l.dtype == np.float32 and l.shape == (3, E)
+    np.testing.assert_array_equal(l[0], w[:, 3])
+    np.testing.assert_array_equal(l[1], w[:, 0])
+    np.testing.assert_array_equal(l[2], w[:, 6])
+    b = np.arange(E, dtype=np.float32) * 0.5
+    np.testing.assert_array_equal(oracle.router_logits(x, w, b)[0],
+                                  (w[:, 3] + b).astype(np.float32))
+
+
+def test_router_logits_rounding_once():
+    # sum of 1 + 2^-30 * 4 terms: fp32 accumulation would lose the small
+    # terms one by one; fp64 accumulation then one rounding keeps their sum.
+    x = np.array([[1.0, 1.0, 1.0, 1.0, 1.0]], dtype=np.float32)
+    w = np.array([[1.0, 2.0 ** -24, 2.0 ** -24, 2.0 ** -24, 2.0 ** -24]], dtype=np.float32)
+    l = oracle.router_logits(x, w)
+    assert l[0, 0] == np.float32(1.0 + 4 * 2.0 ** -24)
+
+
+# ------------------------------------------------------------------ top-k
+def _brute_rank(keys_row):
+    """Position of each expert in the (key desc, index asc) order, by counting
+    the experts that beat it pairwise."""
+    E = len(keys_row)
+    pos = []
+    for a in range(E):
+        beaten_by = sum(
+            1 for b in range(E)
+            if keys_row[b] > keys_row[a] or (keys_row[b] == keys_row[a] and b < a))
+        pos.append(beaten_by)
+    return pos
+
+
+@pytest.mark.parametrize("E,k", [(6, 3), (4, 4), (5, 1), (8, 2)])
+def test_topk_brute_force(E, k):
+    rng = np.random.default_rng(E * 10 + k)
+    # integer-valued keys from a small range: many exact ties
+    keys = rng.integers(-3, 4, size=(300, E)).astype(np.float32)
+    idx = oracle.topk(keys, k)
+    for t in range(keys.shape[0]):
+        pos = _brute_rank(list(keys[t]))
+        expect = [pos.index(j) for j in range(k)]
+        assert list(idx[t]) == expect
+        # the chosen set dominates every subset of the same size
+        best = max(itertools.combinations(range(E), k),
+                   key=lambda s: (sorted([keys[t][e] for e in s], reverse=True),
+                                  [-e for e in s]))
+        assert set(idx[t]) == set(best)
+
+
+def test_topk_ties_and_signed_zero():
+    keys = np.array([[0.5, 0.5, 0.5, 0.5],
+                     [-0.0, 0.0, -1.0, -0.0],
+                     [1.0, 2.0, 2.0, 3.0]], dtype=np.float32)
+    idx = oracle.topk(keys, 2)
+    assert idx.tolist() == [[0, 1], [0, 1], [3, 1]]
+
+
+def test_topk_hand_fixture(golden_dir):
+    g = _load(golden_dir, "routing_hand.json")
+    idx = oracle.topk(np.array(g["keys"], dtype=np.float32), g["k"])
+    assert idx.tolist() == g["idx"]
+
+
+def test_near_tie():
+    keys = np.array([[3.0, 1.0, 1.0 + 5e-6, 0.0],
+                     [3.0, 1.0, 1.0 + 2e-5, 0.0],
+                     [3.0, 2.0, 1.0, 0.0]], dtype=np.float32)
+    assert oracle.near_tie(keys, 2).tolist() == [True, False, False]
+    assert oracle.near_tie(keys, 4).tolist() == [False, False, False]
+
+
+# ------------------------------------------------------------------ gates
+def test_gates_closed_forms(golden_dir):
+    g = _load(golden_dir, "gates_closed_form.json")
+    for case in g["cases"]:
+        l = np.array([case["logits"]], dtype=np.float32)
+        keys = oracle.selection_keys(l, case["select_bias"])
+        idx = oracle.topk(keys, case["k"])
+        assert idx[0].tolist() == case["idx"], case
+        gv = oracle.gates(l, idx, case["mode"])
+        np.testing.assert_allclose(gv[0], case["gates"], rtol=0, atol=2e-7, err_msg=str(case))
+
+
+def test_gate_sums():
+    rng = np.random.default_rng(7)
+    l = rng.standard_normal((500, 8)).astype(np.float32)
+    for k in (1, 2, 3, 8):
+        idx = oracle.topk(l, k)
+        for mode in ("softmax_topk", "sigmoid_topk_norm"):
+            s = oracle.gates(l, idx, mode).astype(np.float64).sum(1)
+            np.testing.assert_allclose(s, 1.0, atol=3e-7)
+        s_all = oracle.gates(l, idx, "softmax_all_topk").astype(np.float64).sum(1)
+        if k < 8:
+            assert (s_all < 1.0).all()
+        else:
+            np.testing.assert_allclose(s_all, 1.0, atol=3e-7)
+        if k == 1:
+            assert (oracle.gates(l, idx, "softmax_topk") == 1.0).all()
+            assert (oracle.gates(l, idx, "sigmoid_topk_norm") == 1.0).all()
+        # gates follow slot order: non-increasing for softmax modes
+        g = oracle.gates(l, idx, "softmax_topk")
+        assert (np.diff(g, axis=1) <= 0).all()
+
+
+# ----------------------------------------------------------- routing maps
+def test_route_maps_hand_fixture(golden_dir):
+    g = _load(golden_dir, "routing_hand.json")
+    idx = np.array(g["idx"])
+    m = oracle.route_maps(idx, g["E"], None)
+    assert m["counts"].tolist() == g["counts"]
+    assert m["rank"].tolist() == g["rank"]
+    assert m["offsets"].tolist() == g["dropless"]["offsets"]
+    assert m["assign_row"].tolist() == g["dropless"]["assign_row"]
+    assert m["row_token"].tolist() == g["dropless"]["row_token"]
+    c = g["capacity"]
+    C = oracle.capacity(g["T"], g["E"], g["k"], c["cf_num"], c["cf_den"])
+    assert C == c["C"]
+    m = oracle.route_maps(idx, g["E"], C)
+    assert m["offsets"].tolist() == c["offsets"]
+    assert m["kept"].tolist() == c["kept"]
+    assert m["assign_row"].tolist() == c["assign_row"]
+    assert m["row_token"].tolist() == c["row_token"]
+
+
+@pytest.mark.parametrize("C", [None, 1, 5, 40])
+def test_route_maps_invariants(C):
+    rng = np.random.default_rng(3)
+    T, E, k = 257, 7, 3
+    keys = rng.standard_normal((T, E)).astype(np.float32)
+    keys[:, 2] += 1.5                       # one hot expert so drops happen
+    idx = oracle.topk(keys, k)
+    m = oracle.route_maps(idx, E, C)
+    counts, ar, rt = m["counts"], m["assign_row"], m["row_token"]
+    assert counts.sum() == T * k
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    kept = ar >= 0
+    cap = C if C is not None else T
+    assert kept.sum() == np.minimum(counts, cap).sum()
+    for e in range(E):
+        rows_e = np.sort(ar[(idx == e) & kept])
+        lo = m["offsets"][e]
+        # the kept rows of an expert are the first places of its group
+        assert rows_e.tolist() == list(range(lo, lo + min(counts[e], cap)))
+        # the kept tokens are the earliest ones that chose e
+        toks = np.nonzero((idx == e).any(1))[0]
+        kept_toks = np.nonzero(((idx == e) & kept).any(1))[0]
+        assert kept_toks.tolist() == toks[:cap].tolist()
+    tt = np.repeat(np.arange(T)[:, None], k, 1)
+    assert np.array_equal(rt[ar[kept]], tt[kept])      # row -> token inverts
+    assert (rt >= 0).sum() == kept.sum()
+
+
+# -------------------------------------------------------------- SwiGLU FFN
+def test_silu_closed_forms():
+    ln3 = math.log(3.0)
+    v = oracle.silu(np.array([0.0, ln3, -ln3, 40.0, -40.0]))
+    np.testing.assert_allclose(v[:3], [0.0, 0.75 * ln3, -0.25 * ln3], rtol=1e-15, atol=0)
+    assert abs(v[3] - 40.0) < 1e-15 * 40 + 1e-15
+    assert abs(v[4]) < 1e-15
+
+
+def test_swiglu_one_hot_weights():
+    """Rows of W1, W3, W2 with a single non-zero: each product is a gather, so
+    the FFN has a closed form that exposes operand orientation and which
+    branch carries the SiLU."""
+    h, F = 5, 7
+    rng = np.random.default_rng(11)
+    p1 = rng.integers(0, h, F)
+    p3 = rng.integers(0, h, F)
+    p2 = rng.integers(0, F, h)
+    a, b, c = 0.7, -1.3, 2.1
+    w1 = np.zeros((F, h)); w1[np.arange(F), p1] = a
+    w3 = np.zeros((F, h)); w3[np.arange(F), p3] = b
+    w2 = np.zeros((h, F)); w2[np.arange(h), p2] = c
+    x = rng.standard_normal((3, h))
+    y = oracle.swiglu_ffn(x, w1, w3, w2)
+    for r in range(3):
+        for i in range(h):
+            f = p2[i]
+            z = a * x[r, p1[f]]
+            expect = c * (z / (1.0 + math.exp(-z))) * (b * x[r, p3[f]])
+            assert abs(y[r, i] - expect) <= 1e-14 * (1 + abs(expect))
+
+
+# ------------------------------------------------------------ whole layer
+def _rand_layer(T, h, E, F, seed, shared=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, h)).astype(np.float32)
+    wr = (rng.standard_normal((E, h)) / math.sqrt(h)).astype(np.float32)
+    w1 = (rng.standard_normal((E, F, h)) / math.sqrt(h)).astype(np.float32)
+    w3 = (rng.standard_normal((E, F, h)) / math.sqrt(h)).astype(np.float32)
+    w2 = (rng.standard_normal((E, h, F)) / math.sqrt(F)).astype(np.float32)
+    sh = None
+    if shared:
+        sh = ((rng.standard_normal((F, h)) / math.sqrt(h)).astype(np.float32),
+              (rng.standard_normal((F, h)) / math.sqrt(h)).astype(np.float32),
+              (rng.standard_normal((h, F)) / math.sqrt(F)).astype(np.float32))
+    return x, wr, w1, w3, w2, sh
+
+
+def test_e1_k1_is_dense_ffn():
+    x, wr, w1, w3, w2, _ = _rand_layer(33, 16, 1, 24, 5)
+    for gate in oracle.GATE_MODES:
+        out = oracle.moe_forward(x, wr, w1, w3, w2, k=1, gate=gate)
+        assert (out["gates"] == 1.0).all()
+        np.testing.assert_array_equal(out["y"], oracle.swiglu_ffn(x, w1[0], w3[0], w2[0]))
+
+
+def test_k_equals_e_is_dense_soft_mixture():
+    T, h, E, F = 40, 12, 4, 20
+    x, wr, w1, w3, w2, _ = _rand_layer(T, h, E, F, 6)
+    out = oracle.moe_forward(x, wr, w1, w3, w2, k=E, gate="softmax_topk")
+    # dense mixture: every expert on every token, softmax weights over all E
+    l = (x.astype(np.float64) @ wr.astype(np.float64).T).astype(np.float32).astype(np.float64)
+    p = np.exp(l - l.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    dense = sum(p[:, e:e + 1] * oracle.swiglu_ffn(x, w1[e], w3[e], w2[e]) for e in range(E))
+    np.testing.assert_allclose(out["y"], dense, rtol=0, atol=1e-6 * np.abs(dense).max())
+
+
+@pytest.mark.parametrize("gate", ["softmax_topk", "sigmoid_topk_norm"])
+def test_identical_experts_give_the_ffn(gate):
+    T, h, E, F = 50, 16, 6, 24
+    x, wr, w1, w3, w2, _ = _rand_layer(T, h, E, F, 8)
+    w1[:] = w1[0]; w3[:] = w3[0]; w2[:] = w2[0]
+    out = oracle.moe_forward(x, wr, w1, w3, w2, k=3, gate=gate)
+    ffn = oracle.swiglu_ffn(x, w1[0], w3[0], w2[0])
+    np.testing.assert_allclose(out["y"], ffn, rtol=0, atol=1e-6 * np.abs(ffn).max())
+
+
+def test_large_capacity_equals_dropless():
+    T, h, E, F, k = 64, 16, 4, 24, 2
+    x, wr, w1, w3, w2, _ = _rand_layer(T, h, E, F, 9)
+    C = oracle.capacity(T, E, k, E, k)           # cf = E/k  ->  C = T
+    assert C == T
+    a = oracle.moe_forward(x, wr, w1, w3, w2, k=k, gate="softmax_topk")
+    b = oracle.moe_forward(x, wr, w1, w3, w2, k=k, gate="softmax_topk", C=C)
+    assert (b["maps"]["assign_row"] >= 0).all()
+    np.testing.assert_array_equal(a["y"], b["y"])
+
+
+def test_dropped_slot_adds_nothing_and_no_renormalisation(golden_dir):
+    g = _load(golden_dir, "routing_hand.json")
+    T, E, k, h, F = g["T"], g["E"], g["k"], 8, 12
+    x, wr, w1, w3, w2, _ = _rand_layer(T, h, E, F, 10)
+    idx = np.array(g["idx"], dtype=np.int32)
+    C = g["capacity"]["C"]
+    out = oracle.moe_forward(x, wr, w1, w3, w2, k=k, gate="softmax_topk", C=C, idx=idx)
+    gts = out["gates"].astype(np.float64)
+    # token 4: slot 0 (expert 0) dropped, slot 1 (expert 1) kept
+    e1 = oracle.swiglu_ffn(x[4:5], w1[1], w3[1], w2[1])[0]
+    np.testing.assert_allclose(out["y"][4], gts[4, 1] * e1, rtol=1e-15, atol=0)
+    assert gts[4, 1] < 1.0
+    # token 5: slot 0 (expert 1, rank 3) dropped, slot 1 (expert 2) kept
+    e2 = oracle.swiglu_ffn(x[5:6], w1[2], w3[2], w2[2])[0]
+    np.testing.assert_allclose(out["y"][5], gts[5, 1] * e2, rtol=1e-15, atol=0)
+
+
+def test_all_slots_dropped_gives_zero():
+    x, wr, w1, w3, w2, _ = _rand_layer(12, 8, 2, 8, 12)
+    out = oracle.moe_forward(x, wr, w1, w3, w2, k=2, gate="softmax_topk", C=3)
+    # k = E = 2: every token picks both experts; tokens 3.. are dropped twice
+    assert (out["maps"]["assign_row"][3:] == -1).all()
+    assert (out["y"][3:] == 0.0).all()
+    assert np.abs(out["y"][:3]).max() > 0
+
+
+def test_shared_expert_is_added_with_weight_one():
+    x, wr, w1, w3, w2, sh = _rand_layer(20, 8, 4, 12, 13, shared=True)
+    a = oracle.moe_forward(x, wr, w1, w3, w2, k=2, gate="sigmoid_topk_norm")
+    b = oracle.moe_forward(x, wr, w1, w3, w2, k=2, gate="sigmoid_topk_norm", shared=sh)
+    np.testing.assert_allclose(b["y"] - a["y"], oracle.swiglu_ffn(x, *sh), rtol=0, atol=1e-12)
+
+
+def test_token_subset_matches_full():
+    x, wr, w1, w3, w2, sh = _rand_layer(30, 8, 4, 12, 14, shared=True)
+    full = oracle.moe_forward(x, wr, w1, w3, w2, k=2, gate="softmax_topk", C=10, shared=sh)
+    tok = np.array([29, 0, 7, 7])
+    sub = oracle.moe_forward(x, wr, w1, w3, w2, k=2, gate="softmax_topk", C=10, shared=sh, tokens=tok)
+    np.testing.assert_array_equal(sub["y"], full["y"][tok])
+
+
+def test_permute_then_unpermute_is_identity():
+    """k = 1, unit gates: scattering token rows to their group rows and
+    gathering them back through the same map returns every token."""
+    rng = np.random.default_rng(15)
+    T, E, h = 90, 5, 6
+    x = rng.standard_normal((T, h))
+    idx = rng.integers(0, E, (T, 1))
+    for C in (None, 100):
+        m = oracle.route_maps(idx, E, C)
+        perm = np.zeros((m["rows"], h))
+        perm[m["assign_row"][:, 0]] = x
+        back = perm[m["assign_row"][:, 0]]
+        np.testing.assert_array_equal(back, x)
+        pads = m["row_token"] < 0
+        assert (perm[pads] == 0).all()
+
+
+# ---------------------------------------------- worked example dimensions
+def test_worked_example_dimension_chain(golden_dir):
+    g = _load(golden_dir, "worked_example.json")
+    cfg = CONFIGS["worked_example"]
+    assert (cfg.T, cfg.h, cfg.E, cfg.k, cfg.F) == (g["T"], g["h"], g["E"], g["k"], g["F"])
+    inp = make_inputs(cfg, device="cpu", with_experts=False)
+    x = inp["x"].float().numpy()
+    wr = inp["w_router"].float().numpy()
+    assert list(x.shape) == g["shapes"]["x"]
+    C = oracle.capacity(cfg.T, cfg.E, cfg.k, *cfg.cf)
+    out = oracle.moe_forward(x, wr, None, None, None, k=cfg.k, gate=cfg.gate, C=C,
+                             maps_only=True)
+    assert list(out["logits"].shape) == g["shapes"]["router"]
+    assert list(out["idx"].shape) == g["shapes"]["topk"]
+    assert [cfg.E, out["maps"]["rows"] // cfg.E, cfg.h] == g["shapes"]["dispatch"]
+    # each expert FFN: three h x F matrices (about 151M), E of them per layer
+    per_expert = 3 * cfg.h * cfg.F
+    assert abs(per_expert / g["params_per_expert_approx"] - 1) < 0.01
+    assert abs(cfg.E * per_expert / g["params_per_layer_approx"] - 1) < 0.01
