@@ -1,0 +1,203 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+A step is one fused moe_forward (router GEMM, top-k/gates, scan, assign,
+permute, grouped GEMM 1 + SwiGLU, grouped GEMM 2, combine) over one batch of
+seeded synthetic input already resident in HBM.  Default workload: the
+worked example T=4096, h=4096, E=8, k=2, F=12288, capacity factor 5/4
+(C = 1280), softmax over all E then the top-2 gate values.
+
+Prints ONE JSON line: tokens/s over the K timed steps, per-stage kernel
+durations from HIP events recorded on the launch stream inside the timed
+region, the grouped-GEMM roofline (algorithmic FLOPs / event duration vs the
+bf16 dense MFMA peak), permute/combine algorithmic bytes vs HBM, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("MoE-layer fwd tokens/s and grouped-GEMM TFLOPS (% MFMA peak), "
+          "T=4096 h=4096 E=8 k=2")
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+# ---------------------------------------------------------------- accounting
+def gemm1_flops(kept_rows: int, h: int, F: int) -> int:
+    """GEMM 1: two [rows,h] x [h,F] products (w1 and w3), 2 flops per MAC."""
+    return 4 * kept_rows * h * F
+
+
+def gemm2_flops(kept_rows: int, h: int, F: int) -> int:
+    """GEMM 2: one [rows,F] x [F,h] product."""
+    return 2 * kept_rows * h * F
+
+
+def expert_flops(kept_rows: int, h: int, F: int) -> int:
+    return gemm1_flops(kept_rows, h, F) + gemm2_flops(kept_rows, h, F)
+
+
+def permute_bytes(T: int, h: int, rows: int, esz: int) -> int:
+    """Read every token row once, write every row of the dispatch buffer
+    (kept copies and zero padding)."""
+    return (T + rows) * h * esz
+
+
+def combine_bytes(kept_rows: int, T: int, h: int, esz: int, shared: bool) -> int:
+    """Read every kept expert-output row (and the shared rows), write y."""
+    return (kept_rows + T + (T if shared else 0)) * h * esz
+
+
+# --------------------------------------------------------------------- bench
+def _workload_name(cfg, C):
+    s = (f"{cfg.name}: T={cfg.T} h={cfg.h} E={cfg.E} k={cfg.k} F={cfg.F} {cfg.dtype} "
+         f"{cfg.gate}")
+    s += f" C={C}" if C else " dropless"
+    if cfg.shared:
+        s += " +1 shared expert"
+    return s
+
+
+def cpu_baseline(cfg, inp, C, sample_tokens: int) -> dict:
+    """The oracle, as it stands, on the first `sample_tokens` tokens' outputs
+    (routing, ranks and drops still over all T tokens)."""
+    import numpy as np
+    import oracle
+    f32 = lambda t: t.float().cpu().numpy()  # noqa: E731
+    x, wr = f32(inp["x"]), f32(inp["w_router"])
+    w1, w3, w2 = f32(inp["w1"]), f32(inp["w3"]), f32(inp["w2"])
+    lb = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
+    sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
+    shared = (f32(inp["ws1"]), f32(inp["ws3"]), f32(inp["ws2"])) if cfg.shared else None
+    tok = np.arange(min(sample_tokens, cfg.T))
+    t0 = time.perf_counter()
+    oracle.moe_forward(x, wr, w1, w3, w2, k=cfg.k, gate=cfg.gate, C=C or None,
+                       logit_bias=lb, select_bias=sb, shared=shared, tokens=tok)
+    dt = time.perf_counter() - t0
+    try:
+        import threadpoolctl
+        cores = max(i["num_threads"] for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    return {"value": len(tok) / dt, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"outputs of the first {len(tok)} of {cfg.T} tokens (routing of all "
+                      f"{cfg.T}), fp64 numpy oracle"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="worked_example")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the layer "
+              "has no multi-GPU path in this library", file=sys.stderr)
+        return 2
+
+    import torch
+    import mixture_experts_layer_25_amd as moe
+    from moe_inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = make_inputs(cfg, device=dev)
+    C = moe.moe_capacity(cfg.T, cfg.E, cfg.k, *cfg.cf) if cfg.cf else 0
+    c = moe.make_cfg(cfg.T, cfg.h, cfg.F, cfg.E, cfg.k, cfg.dtype, cfg.gate, capacity=C,
+                     has_shared=cfg.shared)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    esz = 2 if cfg.dtype == "bf16" else 4
+    rows = moe.moe_num_rows(c)
+    ws = torch.empty(moe.moe_workspace_bytes(c), dtype=torch.uint8, device=dev)
+    y = torch.empty((cfg.T, cfg.h), dtype=tdt, device=dev)
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    route = {"expert_counts": counts}
+    weights = {n: inp[n] for n in ("w_router", "w1", "w3", "w2", "logit_bias",
+                                   "select_bias", "ws1", "ws3", "ws2")}
+
+    for _ in range(args.warmup):
+        moe.moe_forward(c, weights, inp["x"], y, route, ws)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_EVENTS)]
+           for _ in range(K)]
+    for es in evs:             # create the events outside the timed region
+        for e in es:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        moe.moe_forward(c, weights, inp["x"], y, route, ws, events=evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {}
+    for s, name in enumerate(moe.STAGE_NAMES):
+        stage_ms[name] = sum(evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(K)) / K
+    cnt = counts.cpu().tolist()
+    kept = sum(min(n, C) for n in cnt) if C else sum(cnt)
+    kept_all = kept + (cfg.T if cfg.shared else 0)
+    ms_step = elapsed * 1e3 / K
+    g1 = gemm1_flops(kept_all, cfg.h, cfg.F) / (stage_ms["gemm1_swiglu"] * 1e-3) / 1e12
+    g2 = gemm2_flops(kept_all, cfg.h, cfg.F) / (stage_ms["gemm2"] * 1e-3) / 1e12
+    gg = expert_flops(kept_all, cfg.h, cfg.F) / (
+        (stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    pb = permute_bytes(cfg.T, cfg.h, rows, esz)
+    cb = combine_bytes(kept, cfg.T, cfg.h, esz, cfg.shared)
+    perm_gbs = pb / (stage_ms["permute"] * 1e-3) / 1e9
+    comb_gbs = cb / (stage_ms["combine"] * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.T * K / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) tokens, fan-in-scaled N(0,1/fan_in) random weights)",
+        "config": {"workload": _workload_name(cfg, C), "T": cfg.T, "h": cfg.h, "E": cfg.E,
+                   "k": cfg.k, "F": cfg.F, "capacity": C, "gate": cfg.gate,
+                   "kept_rows": kept, "dispatch_rows": rows, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma" if cfg.dtype == "bf16" else "alu",
+                     "kernel": "gemm1_swiglu",
+                     "achieved": round(g1, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(g1 / peak, 4), "traffic": None},
+        "grouped_gemm": {"tflops": round(gg, 1), "frac_of_peak": round(gg / peak, 4),
+                         "gemm1_tflops": round(g1, 1), "gemm2_tflops": round(g2, 1)},
+        "permute": {"gbs": round(perm_gbs, 1), "frac_hbm": round(perm_gbs / PEAK_HBM_GBS, 4),
+                    "bytes": pb},
+        "combine": {"gbs": round(comb_gbs, 1), "frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
+                    "bytes": cb},
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, C, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

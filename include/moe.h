@@ -1,0 +1,223 @@
+/*
+ * moe.h - C ABI of libmoe: the forward pass of a top-k Mixture-of-Experts
+ * SwiGLU FFN layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages describe it:
+ *   - "Megatron-LM 分布式训练（六）：MoE 专家并行 EP 与上下文并行 CP",
+ *     section "MoE 层的数据流": router -> dispatch -> experts (one grouped
+ *     GEMM) -> combine, plus optional shared experts added to the result;
+ *     section "Router": logits = hidden states times the router weight,
+ *     then top-k with softmax or sigmoid weights.
+ *   - "v6:长序列和 MoE:Context Parallel 与 Expert Parallel" (infra-l7),
+ *     section "NVIDIA 原题": the dimension chain [T,h] -> [T,E] -> [T,k] ->
+ *     [E,C,h] -> [T,h], capacity C = cf*k*T/E with overflow dropped, or no
+ *     capacity at all (dropless); section "MoE:参数很多": every expert is a
+ *     SwiGLU FFN h -> F -> h.
+ * One ABI entry point per stage of that chain, plus the fused layer.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Memory    All tensor pointers are DEVICE pointers owned by the caller.
+ *             The library never allocates or frees device memory; scratch
+ *             comes from a caller workspace of moe_workspace_bytes() bytes.
+ *             Pointers must be 16-byte aligned.  Tensors are dense,
+ *             row-major, with the last dimension contiguous.
+ *   Weights   Stored [out, in] (torch Linear layout): w_router [E,h],
+ *             w1/w3 [E,F,h], w2 [E,h,F].  The page's router weight [h,E]
+ *             is the transpose of w_router.
+ *   Streams   `stream` is a hipStream_t passed as void* (NULL = default
+ *             stream).  Calls only enqueue work; none synchronises.
+ *   Errors    Arguments are checked on the host, synchronously, before any
+ *             device work; on a bad argument nothing is enqueued and the
+ *             call returns MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED.
+ *             MOE_ERR_HIP reports a failed kernel launch.  Device faults
+ *             surface at the caller's next synchronisation.  No C++
+ *             exception crosses the ABI.
+ *   Threads   Stateless: concurrent calls are safe on different streams
+ *             with different workspaces and outputs.
+ *   Shapes    h % 128 == 0, F % 128 == 0, 1 <= k <= min(E, 16), E <= 1024,
+ *             T >= 0 (T == 0 enqueues nothing and reads no pointer).  Otherwise
+ *             MOE_ERR_UNSUPPORTED.
+ *   Numerics  bf16 layers: bf16 inputs, fp32 accumulation, fp32 router
+ *             logits and gates, bf16 round-to-nearest-even stores of the
+ *             expert activation, expert outputs and the layer output.
+ *             fp32 layers compute and store everything in fp32.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG 1  /* null pointer, bad enum, inconsistent sizes */
+#define MOE_ERR_UNSUPPORTED 2  /* shape outside the supported set above */
+#define MOE_ERR_WORKSPACE 3    /* workspace missing or too small */
+#define MOE_ERR_HIP 4          /* a kernel launch failed */
+
+/* ---- element types --------------------------------------------------- */
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+
+/* ---- gate modes -------------------------------------------------------
+ * Megatron-LM part 6, section "Router" (top-k over the logits, weights by
+ * softmax or sigmoid); infra-l7, section "NVIDIA 原题" (softmax over all E
+ * then the selected gate values; DeepSeek-V3's selection-only bias).
+ *   SOFTMAX_TOPK        g_j = softmax over the k selected logits
+ *   SOFTMAX_ALL_TOPK    g_j = softmax over all E logits, at the selected
+ *                       experts, not renormalised
+ *   SIGMOID_TOPK_NORM   g_j = sigmoid(l_j) / sum over the k selected
+ * Selection always compares the fp32 key l[e] (+ select_bias[e]) and breaks
+ * ties toward the lower expert index; select_bias never enters a gate.   */
+#define MOE_GATE_SOFTMAX_TOPK 0
+#define MOE_GATE_SOFTMAX_ALL_TOPK 1
+#define MOE_GATE_SIGMOID_TOPK_NORM 2
+
+/* Kernels moe_forward launches, in order, each one a timed stage:
+ *   0 router GEMM, 1 top-k + gates + chunk histogram, 2 scan (counts,
+ *   offsets, GEMM tile table), 3 assign (ranks, rows), 4 permute copy,
+ *   5 grouped GEMM 1 + SwiGLU, 6 grouped GEMM 2, 7 combine.
+ * MOE_NUM_EVENTS events bracket them (see moe_forward).                   */
+#define MOE_NUM_STAGES 8
+#define MOE_NUM_EVENTS (MOE_NUM_STAGES + 1)
+
+typedef struct moe_cfg {
+  int32_t struct_size; /* sizeof(moe_cfg_t) */
+  int32_t dtype;       /* MOE_DTYPE_*: x, weights, activation and y */
+  int64_t T;           /* tokens (batch x sequence flattened) */
+  int32_t h;           /* model width */
+  int32_t F;           /* expert FFN width */
+  int32_t E;           /* routed experts */
+  int32_t k;           /* experts per token */
+  int32_t gate;        /* MOE_GATE_* */
+  int32_t has_shared;  /* 1: one shared expert of shape (h, F) on every token */
+  int64_t capacity;    /* 0: dropless; > 0: capacity C rows per expert */
+} moe_cfg_t;
+
+typedef struct moe_weights {
+  const void* w_router;     /* [E,h] dtype */
+  const void* w1;           /* [E,F,h] dtype, SiLU branch */
+  const void* w3;           /* [E,F,h] dtype, linear branch */
+  const void* w2;           /* [E,h,F] dtype, down projection */
+  const float* logit_bias;  /* [E] fp32 added to the logits, or NULL */
+  const float* select_bias; /* [E] fp32 added for selection only, or NULL */
+  const void* ws1;          /* shared expert [F,h], NULL unless has_shared */
+  const void* ws3;          /* shared expert [F,h] */
+  const void* ws2;          /* shared expert [h,F] */
+} moe_weights_t;
+
+/* Optional device outputs of moe_forward (each field may be NULL; a NULL
+ * field is kept in the workspace instead).  Layouts as in the stage calls. */
+typedef struct moe_route_out {
+  float* logits;           /* [T,E] */
+  int32_t* topk_idx;       /* [T,k] */
+  float* topk_gate;        /* [T,k] */
+  int32_t* expert_counts;  /* [E]   assignments per expert, before any drop */
+  int32_t* expert_offsets; /* [E+1] first row of each expert's group */
+  int32_t* assign_row;     /* [T*k] row of (t,j) in x_perm, -1 if dropped */
+  int32_t* row_token;      /* [rows] token of each row, -1 for padding */
+} moe_route_out_t;
+
+/* Host-only helpers (no device work, callable without a GPU). ---------- */
+
+/* Static string for a status code. */
+const char* moe_strerror(int status);
+
+/* Capacity C = ceil(cf_num * k * T / (cf_den * E)) in exact integer
+ * arithmetic (infra-l7, "NVIDIA 原题", capacity bullet: 1280 at T=4096,
+ * E=8, k=2, cf=5/4).  All arguments > 0, else MOE_ERR_INVALID_ARG.       */
+int moe_capacity(int64_t T, int32_t E, int32_t k, int64_t cf_num,
+                 int64_t cf_den, int64_t* C);
+
+/* Rows of the dispatch buffer x_perm: T*k when dropless, E*C otherwise. */
+int moe_num_rows(const moe_cfg_t* cfg, int64_t* rows);
+
+/* Workspace bytes moe_forward needs for cfg (the stage calls need at most
+ * this much too). */
+int moe_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes);
+
+/* Stage 1: router GEMM, gating and top-k ----------------------------------
+ * Megatron-LM part 6, "Router"; infra-l7, "NVIDIA 原题" rows router/top-k.
+ *   x            [T,h] dtype
+ *   w_router     [E,h] dtype
+ *   logit_bias   [E] fp32 or NULL   (added to the logits)
+ *   select_bias  [E] fp32 or NULL   (added to the selection key only)
+ *   logits       [T,E] fp32 out, or NULL (then kept in the workspace)
+ *   topk_idx     [T,k] int32 out: slot 0 = largest key
+ *   topk_gate    [T,k] fp32 out: gate of each slot (cfg->gate)
+ *   ws, ws_bytes workspace (moe_workspace_bytes)                          */
+int moe_router_topk(const moe_cfg_t* cfg, const void* x, const void* w_router,
+                    const float* logit_bias, const float* select_bias,
+                    float* logits, int32_t* topk_idx, float* topk_gate,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 2: dispatch / permute ---------------------------------------------
+ * infra-l7, "NVIDIA 原题" row dispatch and capacity bullet, "自测" (sort by
+ * expert, drop past capacity on that expert only, pad unused places).
+ *   x              [T,h] dtype
+ *   topk_idx       [T,k] int32 (from stage 1, any valid selection)
+ *   expert_counts  [E] int32 out: assignments per expert before dropping
+ *   expert_offsets [E+1] int32 out: dropless = exclusive prefix of counts;
+ *                  capacity = e*C
+ *   assign_row     [T*k] int32 out: row of (t,j); rank = number of earlier
+ *                  tokens that chose the same expert; dropless row =
+ *                  offsets[e] + rank; capacity row = e*C + rank if rank < C,
+ *                  else -1 (dropped)
+ *   row_token      [rows] int32 out: token of each row, -1 for padding
+ *   x_perm         [rows,h] dtype out: x_perm[assign_row[t,j]] = x[t];
+ *                  padding rows are zero                                  */
+int moe_permute(const moe_cfg_t* cfg, const void* x, const int32_t* topk_idx,
+                int32_t* expert_counts, int32_t* expert_offsets,
+                int32_t* assign_row, int32_t* row_token, void* x_perm,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 3: grouped GEMM running every expert's SwiGLU FFN ------------------
+ * infra-l7, "MoE:参数很多" (SwiGLU FFN h->F->h) and "自测" (one grouped GEMM
+ * over tokens sorted by expert); Megatron-LM part 6 (experts as GroupedGEMM).
+ * Group e owns rows expert_offsets[e] .. and min(expert_counts[e],
+ * expert_offsets[e+1]-expert_offsets[e]) of them are computed; other rows
+ * of act/y_perm are left unspecified.
+ *   act[r,f]    = bf16( silu(x_perm[r]·w1[e,f]) * (x_perm[r]·w3[e,f]) )
+ *   y_perm[r,i] = bf16( act[r]·w2[e,i] )       silu(z) = z/(1+exp(-z))
+ *   x_perm [rows,h], act [rows,F], y_perm [rows,h] dtype; rows =
+ *   expert_offsets[E].  A shared expert is this call with E=1,
+ *   counts=[T], offsets=[0,T].                                            */
+int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
+                            const int32_t* expert_counts,
+                            const int32_t* expert_offsets, const void* w1,
+                            const void* w3, const void* w2, void* act,
+                            void* y_perm, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Stage 4: combine / unpermute -----------------------------------------------
+ * 专家并行, "EP+DP" forward (each token's top-k outputs summed with their
+ * weights); infra-l7 "NVIDIA 原题" row combine.
+ *   y[t] = sum over kept slots j in slot order of topk_gate[t,j] *
+ *          y_perm[assign_row[t,j]]  (+ shared_y[t]), summed in fp32
+ *   shared_y [T,h] dtype or NULL;  y [T,h] dtype out.                     */
+int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
+                          const int32_t* assign_row, const float* topk_gate,
+                          const void* shared_y, void* y, void* stream);
+
+/* The fused layer: stages 1-4 (+ the shared expert as one more group of
+ * the grouped GEMM) on one stream, no host synchronisation.
+ *   w        weights (device pointers inside a host struct)
+ *   x [T,h]  in;  y [T,h] out
+ *   route    optional extra outputs (host struct of device pointers) or NULL
+ *   events   NULL, or MOE_NUM_EVENTS hipEvent_t (as void*) created by the
+ *            caller; event i is recorded on `stream` before stage i and the
+ *            last one after the final stage, for per-stage timing.        */
+int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
+                void* y, const moe_route_out_t* route, void* ws,
+                size_t ws_bytes, void* const* events, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

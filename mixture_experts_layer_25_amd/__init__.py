@@ -1,0 +1,249 @@
+"""Python binding of libmoe (MoE layer forward on MI355X / gfx950).
+
+Argument marshalling only: every function passes torch tensors' device
+pointers and the current HIP stream to the function of the same name in
+libmoe.so (declared in include/moe.h) and raises on a non-zero status.  No
+step of the layer runs here.  torch provides device memory and streams.
+
+If libmoe.so has not been built, every call raises ``RuntimeError``: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_HIP = 4
+
+MOE_DTYPE_F32 = 0
+MOE_DTYPE_BF16 = 1
+
+MOE_GATE_SOFTMAX_TOPK = 0
+MOE_GATE_SOFTMAX_ALL_TOPK = 1
+MOE_GATE_SIGMOID_TOPK_NORM = 2
+
+MOE_NUM_STAGES = 8
+MOE_NUM_EVENTS = MOE_NUM_STAGES + 1
+STAGE_NAMES = ("router", "topk", "scan", "assign", "permute", "gemm1_swiglu",
+               "gemm2", "combine")
+
+GATE_BY_NAME = {
+    "softmax_topk": MOE_GATE_SOFTMAX_TOPK,
+    "softmax_all_topk": MOE_GATE_SOFTMAX_ALL_TOPK,
+    "sigmoid_topk_norm": MOE_GATE_SIGMOID_TOPK_NORM,
+}
+DTYPE_BY_NAME = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16}
+
+# Every symbol include/moe.h declares.
+ABI_SYMBOLS = (
+    "moe_strerror", "moe_capacity", "moe_num_rows", "moe_workspace_bytes",
+    "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu",
+    "moe_unpermute_combine", "moe_forward",
+)
+
+
+class MoECfg(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("T", ctypes.c_int64),
+        ("h", ctypes.c_int32),
+        ("F", ctypes.c_int32),
+        ("E", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("gate", ctypes.c_int32),
+        ("has_shared", ctypes.c_int32),
+        ("capacity", ctypes.c_int64),
+    ]
+
+
+class MoEWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_router", "w1", "w3", "w2", "logit_bias", "select_bias", "ws1", "ws3", "ws2")]
+
+
+class MoERouteOut(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "logits", "topk_idx", "topk_gate", "expert_counts", "expert_offsets",
+        "assign_row", "row_token")]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({strerror(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mixture_experts_layer_25_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        cfgp = ctypes.POINTER(MoECfg)
+        sig = {
+            "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+            "moe_capacity": (ctypes.c_int, [I64, I32, I32, I64, I64, ctypes.POINTER(I64)]),
+            "moe_num_rows": (ctypes.c_int, [cfgp, ctypes.POINTER(I64)]),
+            "moe_workspace_bytes": (ctypes.c_int, [cfgp, ctypes.POINTER(SZ)]),
+            "moe_router_topk": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, SZ, P]),
+            "moe_permute": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, SZ, P]),
+            "moe_grouped_gemm_swiglu": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "moe_unpermute_combine": (ctypes.c_int, [cfgp, P, P, P, P, P, P]),
+            "moe_forward": (ctypes.c_int, [cfgp, ctypes.POINTER(MoEWeights), P, P,
+                                           ctypes.POINTER(MoERouteOut), P, SZ, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().moe_strerror(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoEError(fn, status)
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (None stays NULL)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def make_cfg(T: int, h: int, F: int, E: int, k: int, dtype="bf16",
+             gate="softmax_topk", capacity: int = 0, has_shared: bool = False) -> MoECfg:
+    c = MoECfg()
+    c.struct_size = ctypes.sizeof(MoECfg)
+    c.dtype = DTYPE_BY_NAME[dtype] if isinstance(dtype, str) else int(dtype)
+    c.T, c.h, c.F, c.E, c.k = T, h, F, E, k
+    c.gate = GATE_BY_NAME[gate] if isinstance(gate, str) else int(gate)
+    c.has_shared = int(bool(has_shared))
+    c.capacity = int(capacity)
+    return c
+
+
+def moe_capacity(T: int, E: int, k: int, cf_num: int, cf_den: int) -> int:
+    out = ctypes.c_int64()
+    _check("moe_capacity", lib().moe_capacity(T, E, k, cf_num, cf_den, ctypes.byref(out)))
+    return out.value
+
+
+def moe_num_rows(cfg: MoECfg) -> int:
+    out = ctypes.c_int64()
+    _check("moe_num_rows", lib().moe_num_rows(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def moe_workspace_bytes(cfg: MoECfg) -> int:
+    out = ctypes.c_size_t()
+    _check("moe_workspace_bytes", lib().moe_workspace_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def moe_router_topk(cfg, x, w_router, logit_bias, select_bias, logits, topk_idx,
+                    topk_gate, ws=None, stream=None) -> None:
+    wp, wb = _ws(ws)
+    _check("moe_router_topk", lib().moe_router_topk(
+        ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias),
+        _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), wp, wb, _stream(stream)))
+
+
+def moe_permute(cfg, x, topk_idx, expert_counts, expert_offsets, assign_row,
+                row_token, x_perm, ws, stream=None) -> None:
+    wp, wb = _ws(ws)
+    _check("moe_permute", lib().moe_permute(
+        ctypes.byref(cfg), _ptr(x), _ptr(topk_idx), _ptr(expert_counts),
+        _ptr(expert_offsets), _ptr(assign_row), _ptr(row_token), _ptr(x_perm), wp, wb,
+        _stream(stream)))
+
+
+def moe_grouped_gemm_swiglu(cfg, x_perm, expert_counts, expert_offsets, w1, w3, w2,
+                            act, y_perm, ws, stream=None) -> None:
+    wp, wb = _ws(ws)
+    _check("moe_grouped_gemm_swiglu", lib().moe_grouped_gemm_swiglu(
+        ctypes.byref(cfg), _ptr(x_perm), _ptr(expert_counts), _ptr(expert_offsets),
+        _ptr(w1), _ptr(w3), _ptr(w2), _ptr(act), _ptr(y_perm), wp, wb, _stream(stream)))
+
+
+def moe_unpermute_combine(cfg, y_perm, assign_row, topk_gate, shared_y, y,
+                          stream=None) -> None:
+    _check("moe_unpermute_combine", lib().moe_unpermute_combine(
+        ctypes.byref(cfg), _ptr(y_perm), _ptr(assign_row), _ptr(topk_gate),
+        _ptr(shared_y), _ptr(y), _stream(stream)))
+
+
+def weights_struct(w: dict) -> MoEWeights:
+    s = MoEWeights()
+    for name, _ in MoEWeights._fields_:
+        setattr(s, name, _ptr(w.get(name)))
+    return s
+
+
+def route_struct(r: Optional[dict]) -> Optional[MoERouteOut]:
+    if r is None:
+        return None
+    s = MoERouteOut()
+    for name, _ in MoERouteOut._fields_:
+        setattr(s, name, _ptr(r.get(name)))
+    return s
+
+
+def moe_forward(cfg, weights: dict, x, y, route: Optional[dict] = None, ws=None,
+                events=None, stream=None) -> None:
+    """Fused layer.  ``weights``: dict with w_router, w1, w3, w2 and optional
+    logit_bias, select_bias, ws1, ws3, ws2.  ``route``: optional dict of
+    output tensors (logits, topk_idx, topk_gate, expert_counts,
+    expert_offsets, assign_row, row_token).  ``events``: None or
+    MOE_NUM_EVENTS ``torch.cuda.Event(enable_timing=True)``."""
+    wp, wb = _ws(ws)
+    ws_struct = weights_struct(weights)
+    rs = route_struct(route)
+    ev = None
+    if events is not None:
+        if len(events) != MOE_NUM_EVENTS:
+            raise ValueError(f"need {MOE_NUM_EVENTS} events")
+        handles = []
+        for e in events:
+            if not e.cuda_event:      # torch creates its events on first record
+                e.record()
+            handles.append(e.cuda_event)
+        ev = (ctypes.c_void_p * MOE_NUM_EVENTS)(*handles)
+    _check("moe_forward", lib().moe_forward(
+        ctypes.byref(cfg), ctypes.byref(ws_struct), _ptr(x), _ptr(y),
+        ctypes.byref(rs) if rs is not None else None, wp, wb, ev, _stream(stream)))

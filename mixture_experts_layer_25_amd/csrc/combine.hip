@@ -1,0 +1,138 @@
+// Combine / unpermute: y[t] = sum_j gate[t,j] * y_perm[assign_row[t,j]]
+//                             (+ shared_y[t]).
+//
+// 专家并行, "EP+DP" forward: the results of a token's top-k experts are
+// gathered back and summed with their weights; infra-l7, "NVIDIA 原题" row
+// combine (back to the original place, k outputs weighted by the gates);
+// "自测": a slot dropped past capacity contributes nothing.
+//
+// One workgroup per token (kCombTok tokens per workgroup); each thread
+// gathers 16-byte vectors of the k expert rows, sums in fp32 in slot order
+// (shared expert last) and stores one 16-byte vector of y.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kCombTok = 2;
+
+template <int KMAX>
+__global__ __launch_bounds__(256) void combine_bf16_kernel(
+    const uint4* __restrict__ yp, const int32_t* __restrict__ assign_row,
+    const float* __restrict__ gate, const uint4* __restrict__ shared_y,
+    uint4* __restrict__ y, int64_t T, int nv, int k) {
+  for (int tt = 0; tt < kCombTok; ++tt) {
+    const int64_t t = (int64_t)blockIdx.x * kCombTok + tt;
+    if (t >= T) return;
+    int rows[KMAX];
+    float g[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      rows[j] = j < k ? assign_row[t * k + j] : -1;
+      g[j] = j < k ? gate[t * k + j] : 0.f;
+    }
+    for (int v = threadIdx.x; v < nv; v += 256) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (rows[j] >= 0) {
+          const uint4 q = yp[(int64_t)rows[j] * nv + v];
+          const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            acc[2 * p] = fmaf(g[j], bf16_bits_to_f32(u[p] & 0xFFFFu), acc[2 * p]);
+            acc[2 * p + 1] = fmaf(g[j], bf16_bits_to_f32(u[p] >> 16), acc[2 * p + 1]);
+          }
+        }
+      }
+      if (shared_y) {
+        const uint4 q = shared_y[t * nv + v];
+        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          acc[2 * p] += bf16_bits_to_f32(u[p] & 0xFFFFu);
+          acc[2 * p + 1] += bf16_bits_to_f32(u[p] >> 16);
+        }
+      }
+      uint4 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+      y[t * nv + v] = o;
+    }
+  }
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(256) void combine_f32_kernel(
+    const float4* __restrict__ yp, const int32_t* __restrict__ assign_row,
+    const float* __restrict__ gate, const float4* __restrict__ shared_y,
+    float4* __restrict__ y, int64_t T, int nv, int k) {
+  for (int tt = 0; tt < kCombTok; ++tt) {
+    const int64_t t = (int64_t)blockIdx.x * kCombTok + tt;
+    if (t >= T) return;
+    int rows[KMAX];
+    float g[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      rows[j] = j < k ? assign_row[t * k + j] : -1;
+      g[j] = j < k ? gate[t * k + j] : 0.f;
+    }
+    for (int v = threadIdx.x; v < nv; v += 256) {
+      float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (rows[j] >= 0) {
+          const float4 q = yp[(int64_t)rows[j] * nv + v];
+          acc.x = fmaf(g[j], q.x, acc.x);
+          acc.y = fmaf(g[j], q.y, acc.y);
+          acc.z = fmaf(g[j], q.z, acc.z);
+          acc.w = fmaf(g[j], q.w, acc.w);
+        }
+      }
+      if (shared_y) {
+        const float4 q = shared_y[t * nv + v];
+        acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
+      }
+      y[t * nv + v] = acc;
+    }
+  }
+}
+
+template <int KMAX>
+void launch_combine_t(int dtype, const void* yp, const int32_t* ar, const float* g,
+                      const void* sy, void* y, int64_t T, int h, int k,
+                      hipStream_t s) {
+  const int64_t nb = (T + kCombTok - 1) / kCombTok;
+  if (dtype == 1)
+    hipLaunchKernelGGL((combine_bf16_kernel<KMAX>), dim3((unsigned)nb), dim3(256), 0, s,
+                       (const uint4*)yp, ar, g, (const uint4*)sy, (uint4*)y, T, h / 8, k);
+  else
+    hipLaunchKernelGGL((combine_f32_kernel<KMAX>), dim3((unsigned)nb), dim3(256), 0, s,
+                       (const float4*)yp, ar, g, (const float4*)sy, (float4*)y, T, h / 4, k);
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* assign_row,
+                          const float* gate, const void* shared_y, void* y,
+                          int64_t T, int h, int k, hipStream_t s) {
+  if (k <= 1)
+    launch_combine_t<1>(dtype, y_perm, assign_row, gate, shared_y, y, T, h, k, s);
+  else if (k <= 2)
+    launch_combine_t<2>(dtype, y_perm, assign_row, gate, shared_y, y, T, h, k, s);
+  else if (k <= 4)
+    launch_combine_t<4>(dtype, y_perm, assign_row, gate, shared_y, y, T, h, k, s);
+  else if (k <= 8)
+    launch_combine_t<8>(dtype, y_perm, assign_row, gate, shared_y, y, T, h, k, s);
+  else
+    launch_combine_t<16>(dtype, y_perm, assign_row, gate, shared_y, y, T, h, k, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

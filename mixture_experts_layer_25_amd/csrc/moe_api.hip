@@ -1,0 +1,336 @@
+// libmoe C ABI: argument checks, workspace layout and launch sequencing.
+// The operations themselves are documented in include/moe.h.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using moe::gtab_ints;
+
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int esize(const moe_cfg_t& c) { return c.dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+int64_t rows_of(const moe_cfg_t& c) {
+  return c.capacity > 0 ? (int64_t)c.E * c.capacity : c.T * c.k;
+}
+
+int row_tile(const moe_cfg_t& c) {
+  return c.dtype == MOE_DTYPE_BF16 ? moe::kGemmBM_bf16 : moe::kGemmBM_f32;
+}
+
+int check_cfg(const moe_cfg_t* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->struct_size != (int32_t)sizeof(moe_cfg_t)) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->gate < MOE_GATE_SOFTMAX_TOPK || c->gate > MOE_GATE_SIGMOID_TOPK_NORM)
+    return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->h <= 0 || c->F <= 0 || c->E <= 0 || c->k <= 0 || c->capacity < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->has_shared != 0 && c->has_shared != 1) return MOE_ERR_INVALID_ARG;
+  if (c->k > c->E) return MOE_ERR_INVALID_ARG;
+  if (c->h % 128 != 0 || c->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (c->E > 1024 || c->k > 16 || c->E + c->has_shared > 1024) return MOE_ERR_UNSUPPORTED;
+  if (c->T > kMaxRows || c->capacity > kMaxRows) return MOE_ERR_UNSUPPORTED;
+  const int64_t rows_all = rows_of(*c) + (c->has_shared ? c->T : 0);
+  if (rows_all > kMaxRows) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t logits, idx, gate, hist, base, counts, offsets, assign, rowtok, gtab;
+  size_t xperm, act, yperm, total;
+};
+
+Layout layout_of(const moe_cfg_t& c) {
+  Layout L{};
+  const int64_t T = c.T, E = c.E, k = c.k;
+  const int64_t nch = (T + moe::kChunkTokens - 1) / moe::kChunkTokens;
+  const int64_t rows = rows_of(c);
+  const int64_t rows_all = rows + (c.has_shared ? T : 0);
+  const int64_t G = E + c.has_shared;
+  const size_t es = (size_t)esize(c);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.logits = take((size_t)(T * E) * 4);
+  L.idx = take((size_t)(T * k) * 4);
+  L.gate = take((size_t)(T * k) * 4);
+  L.hist = take((size_t)(nch * E) * 4);
+  L.base = take((size_t)(nch * E) * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.assign = take((size_t)(T * k) * 4);
+  L.rowtok = take((size_t)rows * 4);
+  L.gtab = take((size_t)gtab_ints((int)G) * 4);
+  L.xperm = take((size_t)rows * c.h * es);
+  L.act = take((size_t)rows_all * c.F * es);
+  L.yperm = take((size_t)rows_all * c.h * es);
+  L.total = off;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+int check_ws(const moe_cfg_t& c, void* ws, size_t ws_bytes) {
+  const Layout L = layout_of(c);
+  if (L.total > 0 && (ws == nullptr || ws_bytes < L.total)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                                   \
+  do {                                                  \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP;       \
+  } while (0)
+
+int64_t max_m_tiles(int64_t rows, int64_t groups, int BM) {
+  return (rows + BM - 1) / BM + groups;
+}
+
+}  // namespace
+
+MOE_API const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+MOE_API int moe_capacity(int64_t T, int32_t E, int32_t k, int64_t cf_num,
+                         int64_t cf_den, int64_t* C) {
+  if (!C || T <= 0 || E <= 0 || k <= 0 || cf_num <= 0 || cf_den <= 0)
+    return MOE_ERR_INVALID_ARG;
+  const __int128 num = (__int128)cf_num * k * T;
+  const __int128 den = (__int128)cf_den * E;
+  const __int128 q = (num + den - 1) / den;
+  if (q > (__int128)INT64_MAX) return MOE_ERR_UNSUPPORTED;
+  *C = (int64_t)q;
+  return MOE_OK;
+}
+
+MOE_API int moe_num_rows(const moe_cfg_t* cfg, int64_t* rows) {
+  const int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!rows) return MOE_ERR_INVALID_ARG;
+  *rows = rows_of(*cfg);
+  return MOE_OK;
+}
+
+MOE_API int moe_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes) {
+  const int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = layout_of(*cfg).total;
+  return MOE_OK;
+}
+
+MOE_API int moe_router_topk(const moe_cfg_t* cfg, const void* x, const void* w_router,
+                            const float* logit_bias, const float* select_bias,
+                            float* logits, int32_t* topk_idx, float* topk_gate,
+                            void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const moe_cfg_t& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  if (!logits && (st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  float* lg = logits ? logits : at<float>(ws, layout_of(c).logits);
+  MOE_TRY(moe::launch_router(c.dtype, x, w_router, logit_bias, lg, c.T, c.h, c.E, s));
+  MOE_TRY(moe::launch_topk(lg, select_bias, c.gate, c.T, c.E, c.k, topk_idx, topk_gate,
+                           nullptr, s));
+  return MOE_OK;
+}
+
+MOE_API int moe_permute(const moe_cfg_t* cfg, const void* x, const int32_t* topk_idx,
+                        int32_t* expert_counts, int32_t* expert_offsets,
+                        int32_t* assign_row, int32_t* row_token, void* x_perm,
+                        void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const moe_cfg_t& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (!x || !topk_idx || !expert_counts || !expert_offsets || !assign_row || !row_token ||
+      !x_perm)
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  const Layout L = layout_of(c);
+  const int64_t nch = (c.T + moe::kChunkTokens - 1) / moe::kChunkTokens;
+  int32_t* hist = at<int32_t>(ws, L.hist);
+  int32_t* base = at<int32_t>(ws, L.base);
+  MOE_TRY(moe::launch_hist(topk_idx, c.T, c.E, c.k, hist, s));
+  MOE_TRY(moe::launch_scan(hist, nch, c.E, c.capacity, c.T, c.k, 0, row_tile(c), base,
+                           expert_counts, expert_offsets, at<int32_t>(ws, L.gtab), s));
+  MOE_TRY(moe::launch_assign(topk_idx, base, expert_offsets, c.T, c.E, c.k, c.capacity,
+                             assign_row, row_token, s));
+  MOE_TRY(moe::launch_permute(c.dtype, x, assign_row, expert_counts, c.T, c.h, c.E, c.k,
+                              c.capacity, x_perm, row_token, s));
+  return MOE_OK;
+}
+
+MOE_API int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
+                                    const int32_t* expert_counts,
+                                    const int32_t* expert_offsets, const void* w1,
+                                    const void* w3, const void* w2, void* act,
+                                    void* y_perm, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const moe_cfg_t& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (!x_perm || !expert_counts || !expert_offsets || !w1 || !w3 || !w2 || !act || !y_perm)
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  const Layout L = layout_of(c);
+  const int BM = row_tile(c);
+  const int64_t rows = rows_of(c);
+  int32_t* gtab = at<int32_t>(ws, L.gtab);
+  MOE_TRY(moe::launch_gtab(expert_counts, expert_offsets, c.E, BM, (int)rows, gtab, s));
+  moe::GroupedGemmArgs a{};
+  a.A = x_perm;
+  a.B0 = w1;
+  a.B1 = w3;
+  a.b_stride = (int64_t)c.F * c.h;
+  a.out = act;
+  a.K = c.h;
+  a.N = c.F;
+  a.gtab = gtab;
+  a.G = c.E;
+  a.E_routed = c.E;
+  a.a_from_out_rows = 0;
+  a.max_m_tiles = max_m_tiles(rows, c.E, BM);
+  MOE_TRY(moe::launch_grouped_gemm(c.dtype, true, a, s));
+  a.A = act;
+  a.B0 = w2;
+  a.B1 = nullptr;
+  a.out = y_perm;
+  a.K = c.F;
+  a.N = c.h;
+  a.a_from_out_rows = 1;
+  MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
+  return MOE_OK;
+}
+
+MOE_API int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
+                                  const int32_t* assign_row, const float* topk_gate,
+                                  const void* shared_y, void* y, void* stream) {
+  const int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const moe_cfg_t& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (!y_perm || !assign_row || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(moe::launch_combine(c.dtype, y_perm, assign_row, topk_gate, shared_y, y, c.T,
+                              c.h, c.k, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
+                        void* y, const moe_route_out_t* route, void* ws,
+                        size_t ws_bytes, void* const* events, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const moe_cfg_t& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (!w || !x || !y || !w->w_router || !w->w1 || !w->w3 || !w->w2)
+    return MOE_ERR_INVALID_ARG;
+  if (c.has_shared && (!w->ws1 || !w->ws3 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  const Layout L = layout_of(c);
+  const moe_route_out_t none{};
+  const moe_route_out_t& r = route ? *route : none;
+  float* logits = r.logits ? r.logits : at<float>(ws, L.logits);
+  int32_t* idx = r.topk_idx ? r.topk_idx : at<int32_t>(ws, L.idx);
+  float* gate = r.topk_gate ? r.topk_gate : at<float>(ws, L.gate);
+  int32_t* counts = r.expert_counts ? r.expert_counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = r.expert_offsets ? r.expert_offsets : at<int32_t>(ws, L.offsets);
+  int32_t* assign = r.assign_row ? r.assign_row : at<int32_t>(ws, L.assign);
+  int32_t* rowtok = r.row_token ? r.row_token : at<int32_t>(ws, L.rowtok);
+  int32_t* hist = at<int32_t>(ws, L.hist);
+  int32_t* base = at<int32_t>(ws, L.base);
+  int32_t* gtab = at<int32_t>(ws, L.gtab);
+  void* xperm = at<char>(ws, L.xperm);
+  void* act = at<char>(ws, L.act);
+  void* yperm = at<char>(ws, L.yperm);
+  const int64_t nch = (c.T + moe::kChunkTokens - 1) / moe::kChunkTokens;
+  const int64_t rows = rows_of(c);
+  const int BM = row_tile(c);
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
+  };
+
+  MOE_TRY(mark(0));
+  MOE_TRY(moe::launch_router(c.dtype, x, w->w_router, w->logit_bias, logits, c.T, c.h,
+                             c.E, s));
+  MOE_TRY(mark(1));
+  MOE_TRY(moe::launch_topk(logits, w->select_bias, c.gate, c.T, c.E, c.k, idx, gate,
+                           hist, s));
+  MOE_TRY(mark(2));
+  MOE_TRY(moe::launch_scan(hist, nch, c.E, c.capacity, c.T, c.k, c.has_shared, BM, base,
+                           counts, offsets, gtab, s));
+  MOE_TRY(mark(3));
+  MOE_TRY(moe::launch_assign(idx, base, offsets, c.T, c.E, c.k, c.capacity, assign,
+                             rowtok, s));
+  MOE_TRY(mark(4));
+  MOE_TRY(moe::launch_permute(c.dtype, x, assign, counts, c.T, c.h, c.E, c.k, c.capacity,
+                              xperm, rowtok, s));
+  MOE_TRY(mark(5));
+  moe::GroupedGemmArgs a{};
+  a.A = xperm;
+  a.A_shared = x;
+  a.B0 = w->w1;
+  a.B1 = w->w3;
+  a.B0s = w->ws1;
+  a.B1s = w->ws3;
+  a.b_stride = (int64_t)c.F * c.h;
+  a.out = act;
+  a.K = c.h;
+  a.N = c.F;
+  a.gtab = gtab;
+  a.G = c.E + c.has_shared;
+  a.E_routed = c.E;
+  a.a_from_out_rows = 0;
+  a.max_m_tiles = max_m_tiles(rows, c.E, BM) + (c.has_shared ? (c.T + BM - 1) / BM : 0);
+  MOE_TRY(moe::launch_grouped_gemm(c.dtype, true, a, s));
+  MOE_TRY(mark(6));
+  a.A = act;
+  a.A_shared = nullptr;
+  a.B0 = w->w2;
+  a.B1 = nullptr;
+  a.B0s = w->ws2;
+  a.B1s = nullptr;
+  a.out = yperm;
+  a.K = c.F;
+  a.N = c.h;
+  a.a_from_out_rows = 1;
+  MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
+  MOE_TRY(mark(7));
+  const void* shared_y =
+      c.has_shared ? (const void*)(at<char>(yperm, (size_t)rows * c.h * esize(c))) : nullptr;
+  MOE_TRY(moe::launch_combine(c.dtype, yperm, assign, gate, shared_y, y, c.T, c.h, c.k, s));
+  MOE_TRY(mark(8));
+  return MOE_OK;
+}

@@ -1,0 +1,73 @@
+// Internal launchers of the libmoe kernels (host side, not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tile table written by the scan kernels and read by the grouped GEMMs.
+// For G groups it holds 4*G+1 int32:
+//   [0 .. G]        exclusive prefix of row tiles per group (entry G = total)
+//   [G+1 .. 2G]     first A row of each group
+//   [2G+1 .. 3G]    rows computed in each group
+//   [3G+1 .. 4G]    first output row of each group
+inline int64_t gtab_ints(int G) { return 4 * (int64_t)G + 1; }
+
+struct GroupedGemmArgs {
+  const void* A;         // routed-group rows: x_perm (GEMM1) or act (GEMM2)
+  const void* A_shared;  // GEMM1: the tokens x for the shared group; else unused
+  const void* B0;        // GEMM1: w1 [E,F,h]; GEMM2: w2 [E,h,F]
+  const void* B1;        // GEMM1: w3 [E,F,h]; GEMM2: unused
+  const void* B0s;       // shared-expert weights (group index E_routed)
+  const void* B1s;
+  int64_t b_stride;      // elements between consecutive experts' matrices
+  void* out;             // act [rows,F] (GEMM1) or y_perm [rows,h] (GEMM2)
+  int K;                 // reduction length (h for GEMM1, F for GEMM2)
+  int N;                 // output columns (F for GEMM1, h for GEMM2)
+  const int32_t* gtab;
+  int G;                 // groups in gtab
+  int E_routed;          // groups 0..E_routed-1 use B0/B1, group E_routed B0s/B1s
+  int a_from_out_rows;   // 1: A row of a tile = its output row (GEMM2)
+  int64_t max_m_tiles;   // host-side bound on the total row tiles
+};
+
+hipError_t launch_router(int dtype, const void* x, const void* w_router,
+                         const float* logit_bias, float* logits, int64_t T,
+                         int h, int E, hipStream_t s);
+
+hipError_t launch_topk(const float* logits, const float* select_bias,
+                       int gate, int64_t T, int E, int k, int32_t* idx,
+                       float* gate_out, int32_t* chunk_hist, hipStream_t s);
+
+hipError_t launch_hist(const int32_t* idx, int64_t T, int E, int k,
+                       int32_t* chunk_hist, hipStream_t s);
+
+hipError_t launch_scan(const int32_t* chunk_hist, int64_t nch, int E,
+                       int64_t C, int64_t T, int k, int has_shared, int BM,
+                       int32_t* chunk_base, int32_t* counts, int32_t* offsets,
+                       int32_t* gtab, hipStream_t s);
+
+hipError_t launch_assign(const int32_t* idx, const int32_t* chunk_base,
+                         const int32_t* offsets, int64_t T, int E, int k,
+                         int64_t C, int32_t* assign_row, int32_t* row_token,
+                         hipStream_t s);
+
+hipError_t launch_permute(int dtype, const void* x, const int32_t* assign_row,
+                          const int32_t* counts, int64_t T, int h, int E,
+                          int k, int64_t C, void* x_perm, int32_t* row_token,
+                          hipStream_t s);
+
+// Groups from caller-provided counts/offsets, clamped to rows [0, rows).
+hipError_t launch_gtab(const int32_t* counts, const int32_t* offsets, int E,
+                       int BM, int rows, int32_t* gtab, hipStream_t s);
+
+hipError_t launch_grouped_gemm(int dtype, bool swiglu,
+                               const GroupedGemmArgs& a, hipStream_t s);
+
+hipError_t launch_combine(int dtype, const void* y_perm,
+                          const int32_t* assign_row, const float* gate,
+                          const void* shared_y, void* y, int64_t T, int h,
+                          int k, hipStream_t s);
+
+}  // namespace moe

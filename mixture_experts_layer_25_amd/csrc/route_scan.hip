@@ -1,0 +1,340 @@
+// Dispatch bookkeeping and the permute copy.
+//
+// infra-l7, "NVIDIA 原题": dispatch groups the tokens by expert, at most C
+// per group (C = cf*k*T/E, excess dropped), unused places padded, giving
+// [E,C,h]; without a capacity (Megatron's default) nothing is dropped.
+// "自测": a token past capacity is dropped on that expert only; sorting the
+// tokens by expert lets one grouped GEMM run every expert.
+//
+// rank(t,j) = number of tokens t' < t that chose the same expert.  Ranks
+// come from counts, never from the order atomics happen to run in:
+//   hist    per chunk of 256 tokens, assignments per expert (order-free
+//           LDS counts; fused into the top-k kernel on the fused path)
+//   scan    one workgroup: per-expert exclusive prefix over chunks, the
+//           counts, group offsets, and the grouped-GEMM tile table
+//   assign  per chunk: per-wave counts, then within a wave the lanes below
+//           with the same expert, found by ballots over the expert's bits
+//   permute x_perm[assign_row[t,j]] = x[t], 16-byte vectors; padding rows
+//           (capacity mode) are zeroed and get row_token = -1.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+// Exclusive scan over one value per thread of a 1024-thread workgroup.
+// `tmp` holds at least 17 ints of LDS.  Returns the prefix, total in *tot.
+__device__ int block_exclusive_scan_1024(int v, int* tmp, int* tot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) tmp[w] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int c = tmp[i];
+      tmp[i] = run;
+      run += c;
+    }
+    tmp[16] = run;
+  }
+  __syncthreads();
+  const int res = tmp[w] + incl - v;
+  *tot = tmp[16];
+  __syncthreads();
+  return res;
+}
+
+// Tile table of G groups (rows computed per group `valid`, first rows
+// a_row0 / o_row0) for row tiles of BM.  Called by all 1024 threads of the
+// scan workgroups with g = threadIdx.x (G <= 1024).
+__device__ void write_gtab(int g, int G, int valid, int a_row0, int o_row0,
+                           int BM, int* tmp, int32_t* gtab) {
+  const int mt = (g < G) ? (valid + BM - 1) / BM : 0;
+  int tot;
+  const int pre = block_exclusive_scan_1024(mt, tmp, &tot);
+  if (g < G) {
+    gtab[g] = pre;
+    gtab[G + 1 + g] = a_row0;
+    gtab[2 * G + 1 + g] = valid;
+    gtab[3 * G + 1 + g] = o_row0;
+  }
+  if (g == 0) gtab[G] = tot;
+}
+
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ idx,
+                                                   int64_t T, int E, int k,
+                                                   int32_t* __restrict__ chunk_hist) {
+  __shared__ int32_t hist[1024];
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * kChunkTokens + threadIdx.x;
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+    }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) chunk_hist[blockIdx.x * (int64_t)E + e] = hist[e];
+}
+
+// One workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void scan_kernel(
+    const int32_t* __restrict__ chunk_hist, int64_t nch, int E, int64_t C,
+    int64_t T, int k, int has_shared, int BM, int32_t* __restrict__ chunk_base,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ gtab) {
+  __shared__ int tmp[32];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E) {
+    for (int64_t c = 0; c < nch; ++c) {
+      chunk_base[c * E + e] = cnt;
+      cnt += chunk_hist[c * E + e];
+    }
+    counts[e] = cnt;
+  }
+  int rows_routed;
+  int off;
+  if (C == 0) {
+    int tot;
+    off = block_exclusive_scan_1024(e < E ? cnt : 0, tmp, &tot);
+    rows_routed = tot;  // == T*k
+  } else {
+    off = e * (int)C;
+    rows_routed = E * (int)C;
+  }
+  if (e < E) offsets[e] = off;
+  if (e == 0) offsets[E] = rows_routed;
+  const int G = E + (has_shared ? 1 : 0);
+  int valid = 0, a0 = 0, o0 = 0;
+  if (e < E) {
+    valid = (C == 0) ? cnt : min(cnt, (int)C);
+    a0 = off;
+    o0 = off;
+  } else if (e == E && has_shared) {
+    valid = (int)T;
+    a0 = 0;                 // the shared group reads the tokens x directly
+    o0 = rows_routed;       // and writes after the routed rows
+  }
+  write_gtab(e, G, valid, a0, o0, BM, tmp, gtab);
+}
+
+// Standalone grouped GEMM: groups straight from counts and offsets, each
+// clamped to the rows [0, rows) of the caller's buffers.
+__global__ __launch_bounds__(1024) void gtab_kernel(const int32_t* __restrict__ counts,
+                                                    const int32_t* __restrict__ offsets,
+                                                    int E, int BM, int rows,
+                                                    int32_t* __restrict__ gtab) {
+  __shared__ int tmp[32];
+  const int e = threadIdx.x;
+  int valid = 0, off = 0;
+  if (e < E) {
+    off = min(max(offsets[e], 0), rows);
+    valid = min(counts[e], offsets[e + 1] - off);
+    valid = max(min(valid, rows - off), 0);
+  }
+  write_gtab(e, E, valid, off, off, BM, tmp, gtab);
+}
+
+// One workgroup (4 waves) per chunk of 256 tokens; lane = token.
+template <int KMAX>
+__global__ __launch_bounds__(256) void assign_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ offsets, int64_t T, int E, int k, int nbits,
+    int64_t C, int32_t* __restrict__ assign_row, int32_t* __restrict__ row_token) {
+  __shared__ int32_t cnt[4][1024];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t chunk = blockIdx.x;
+  const int64_t t = chunk * kChunkTokens + tid;
+  const bool valid = t < T;
+
+  // Expert ids outside [0, E) (possible only through the standalone permute
+  // call) take no row and do not count.
+  int ex[KMAX];
+  bool ok[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    ex[j] = (valid && j < k) ? idx[t * k + j] : 0;
+    ok[j] = valid && j < k && (unsigned)ex[j] < (unsigned)E;
+    if (!ok[j]) ex[j] = 0;
+  }
+
+  for (int i = tid; i < 4 * E; i += 256) cnt[i / E][i % E] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (ok[j]) atomicAdd(&cnt[w][ex[j]], 1);
+  __syncthreads();
+  // wave bases: chunk base of the expert plus the counts of earlier waves
+  for (int e = tid; e < E; e += 256) {
+    int run = chunk_base[chunk * E + e];
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const int c = cnt[ww][e];
+      cnt[ww][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+
+  // local[j]: lanes below this one (earlier tokens of the wave) whose slot
+  // jp holds the same expert as slot j here, summed over jp.  Equality is
+  // tested bit by bit against one ballot per (slot, bit).
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int local[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) local[j] = 0;
+#pragma unroll
+  for (int jp = 0; jp < KMAX; ++jp) {
+    if (jp < k) {
+      const uint64_t vmask = __ballot(ok[jp]);
+      uint64_t bits[10];
+#pragma unroll
+      for (int b = 0; b < 10; ++b) bits[b] = (b < nbits) ? __ballot((ex[jp] >> b) & 1) : 0ull;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+          uint64_t m = vmask & below;
+#pragma unroll
+          for (int b = 0; b < 10; ++b)
+            if (b < nbits) m &= ((ex[j] >> b) & 1) ? bits[b] : ~bits[b];
+          local[j] += __popcll(m);
+        }
+      }
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k) {
+        const int e = ex[j];
+        int row = -1;
+        if (ok[j]) {
+          const int rank = cnt[w][e] + local[j];
+          if (C == 0)
+            row = offsets[e] + rank;
+          else
+            row = (rank < C) ? e * (int)C + rank : -1;
+        }
+        assign_row[t * k + j] = row;
+        if (row >= 0) row_token[row] = (int32_t)t;
+      }
+    }
+  }
+}
+
+template <int KMAX>
+void launch_assign_t(const int32_t* idx, const int32_t* base, const int32_t* off,
+                     int64_t T, int E, int k, int nbits, int64_t C, int32_t* ar,
+                     int32_t* rt, hipStream_t s) {
+  const int64_t nch = (T + kChunkTokens - 1) / kChunkTokens;
+  hipLaunchKernelGGL((assign_kernel<KMAX>), dim3((unsigned)nch), dim3(256), 0, s,
+                     idx, base, off, T, E, k, nbits, C, ar, rt);
+}
+
+constexpr int kPermTok = 2;      // tokens per permute workgroup
+constexpr int kPadBlocks = 256;  // workgroups that clear padding rows
+
+// Token part: blocks [0, ntb) copy kPermTok tokens each.  Padding part
+// (capacity mode): the remaining kPadBlocks blocks walk every expert's
+// unused rows e*C + kept_e .. e*C + C - 1.
+__global__ __launch_bounds__(256) void permute_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ assign_row,
+    const int32_t* __restrict__ counts, int64_t T, int nv, int E, int k,
+    int64_t C, int64_t ntb, uint4* __restrict__ x_perm,
+    int32_t* __restrict__ row_token) {
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  if (b < ntb) {
+    for (int tt = 0; tt < kPermTok; ++tt) {
+      const int64_t t = b * kPermTok + tt;
+      if (t >= T) return;
+      const uint4* src = x + t * nv;
+      for (int v = tid; v < nv; v += 256) {
+        const uint4 val = src[v];
+        for (int j = 0; j < k; ++j) {
+          const int r = assign_row[t * k + j];
+          if (r >= 0) x_perm[(int64_t)r * nv + v] = val;
+        }
+      }
+    }
+    return;
+  }
+  const int64_t pb = b - ntb;
+  for (int e = 0; e < E; ++e) {
+    const int64_t kept = min((int64_t)counts[e], C);
+    for (int64_t r = e * C + kept + pb; r < (e + 1) * C; r += kPadBlocks) {
+      uint4* dst = x_perm + r * nv;
+      for (int v = tid; v < nv; v += 256) dst[v] = uint4{0u, 0u, 0u, 0u};
+      if (tid == 0) row_token[r] = -1;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_hist(const int32_t* idx, int64_t T, int E, int k,
+                       int32_t* chunk_hist, hipStream_t s) {
+  const int64_t nch = (T + kChunkTokens - 1) / kChunkTokens;
+  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nch), dim3(256), 0, s, idx, T,
+                     E, k, chunk_hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const int32_t* chunk_hist, int64_t nch, int E, int64_t C,
+                       int64_t T, int k, int has_shared, int BM,
+                       int32_t* chunk_base, int32_t* counts, int32_t* offsets,
+                       int32_t* gtab, hipStream_t s) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_hist, nch, E,
+                     C, T, k, has_shared, BM, chunk_base, counts, offsets, gtab);
+  return hipGetLastError();
+}
+
+hipError_t launch_gtab(const int32_t* counts, const int32_t* offsets, int E,
+                       int BM, int rows, int32_t* gtab, hipStream_t s) {
+  hipLaunchKernelGGL(gtab_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E,
+                     BM, rows, gtab);
+  return hipGetLastError();
+}
+
+hipError_t launch_assign(const int32_t* idx, const int32_t* chunk_base,
+                         const int32_t* offsets, int64_t T, int E, int k,
+                         int64_t C, int32_t* assign_row, int32_t* row_token,
+                         hipStream_t s) {
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  if (k <= 1)
+    launch_assign_t<1>(idx, chunk_base, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+  else if (k <= 2)
+    launch_assign_t<2>(idx, chunk_base, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+  else if (k <= 4)
+    launch_assign_t<4>(idx, chunk_base, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+  else if (k <= 8)
+    launch_assign_t<8>(idx, chunk_base, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+  else
+    launch_assign_t<16>(idx, chunk_base, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(int dtype, const void* x, const int32_t* assign_row,
+                          const int32_t* counts, int64_t T, int h, int E, int k,
+                          int64_t C, void* x_perm, int32_t* row_token,
+                          hipStream_t s) {
+  const int esz = dtype == 1 ? 2 : 4;
+  const int nv = h * esz / 16;
+  const int64_t ntb = (T + kPermTok - 1) / kPermTok;
+  const int64_t nb = ntb + (C > 0 ? kPadBlocks : 0);
+  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)nb), dim3(256), 0, s,
+                     (const uint4*)x, assign_row, counts, T, nv, E, k, C, ntb,
+                     (uint4*)x_perm, row_token);
+  return hipGetLastError();
+}
+
+}  // namespace moe

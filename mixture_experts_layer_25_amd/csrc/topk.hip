@@ -1,0 +1,172 @@
+// Top-k selection, gates and the per-chunk expert histogram.
+//
+// Megatron-LM part 6, section "Router": top-k over the router scores picks
+// each token's k experts, weighted by softmax or sigmoid.  infra-l7,
+// "NVIDIA 原题": softmax over [T,E] and the top-k gate values; the
+// DeepSeek-V3 bias only takes part in choosing the top-k.
+//
+// A token is handled by a segment of G lanes of one wave (G = the next
+// power of two >= E, at most 64); lane s of the segment holds experts
+// s, s+G, s+2G, ...  Each of the k rounds takes the segment maximum of a
+// 64-bit key (ordered fp32 key bits << 32 | ~expert), so the largest key
+// wins and equal keys go to the lower expert index; the winner clears its
+// entry.  Gates use the fp32 logits (never the selection bias).  Each
+// workgroup covers one chunk of 256 tokens and writes that chunk's expert
+// histogram, which the scan kernel turns into ranks and offsets.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+template <int G>
+__device__ __forceinline__ uint64_t seg_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) {
+    const uint64_t o = __shfl_xor(v, m, G);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+template <int G>
+__device__ __forceinline__ float seg_max_f32(float v) {
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, G));
+  return v;
+}
+
+template <int G>
+__device__ __forceinline__ float seg_sum_f32(float v) {
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, G);
+  return v;
+}
+
+template <int G, int NPL>
+__global__ __launch_bounds__(256) void topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ sbias,
+    int gate_mode, int64_t T, int E, int k, int32_t* __restrict__ idx_out,
+    float* __restrict__ gate_out, int32_t* __restrict__ chunk_hist) {
+  __shared__ int32_t hist[1024];
+  __shared__ int32_t sel_e[kChunkTokens][16];
+  __shared__ float sel_l[kChunkTokens][16];
+
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+
+  const int seg = tid / G;           // token slot within a pass
+  const int s = tid % G;             // lane within the segment
+  constexpr int kTokPerPass = 256 / G;
+  const int64_t chunk0 = (int64_t)blockIdx.x * kChunkTokens;
+
+  for (int pass = 0; pass < kChunkTokens / kTokPerPass; ++pass) {
+    const int tl = pass * kTokPerPass + seg;   // token within the chunk
+    const int64_t t = chunk0 + tl;
+    const bool valid = t < T;
+    uint64_t key[NPL];
+    float lg[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = s + G * i;
+      key[i] = 0;
+      lg[i] = -INFINITY;
+      if (valid && e < E) {
+        const float l = logits[t * E + e];
+        const float kv = sbias ? l + sbias[e] : l;
+        lg[i] = l;
+        key[i] = ((uint64_t)ordered_bits(kv) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+      }
+    }
+    for (int r = 0; r < k; ++r) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) best = key[i] > best ? key[i] : best;
+      const uint64_t win = seg_max_u64<G>(best);
+      if (win != 0) {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+          if (key[i] == win) {
+            key[i] = 0;
+            const int e = (int)(0xFFFFFFFFu - (uint32_t)win);
+            sel_e[tl][r] = e;
+            sel_l[tl][r] = lg[i];
+            atomicAdd(&hist[e], 1);
+          }
+        }
+      }
+    }
+    // Segment lanes see the winners written by other lanes of the same wave.
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    const bool slot = valid && s < k;
+    const float l = slot ? sel_l[tl][s] : -INFINITY;
+    float g = 0.f;
+    if (gate_mode == 0) {          // softmax over the k selected
+      const float m = seg_max_f32<G>(l);
+      const float num = slot ? expf(l - m) : 0.f;
+      const float den = seg_sum_f32<G>(num);
+      g = num / den;
+    } else if (gate_mode == 1) {   // softmax over all E, selected values
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) m = fmaxf(m, lg[i]);
+      m = seg_max_f32<G>(m);
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) part += (s + G * i < E) ? expf(lg[i] - m) : 0.f;
+      const float den = seg_sum_f32<G>(part);
+      g = (slot ? expf(l - m) : 0.f) / den;
+    } else {                       // sigmoid, normalised over the k selected
+      const float sg = slot ? 1.f / (1.f + expf(-l)) : 0.f;
+      const float den = seg_sum_f32<G>(sg);
+      g = sg / den;
+    }
+    if (slot) {
+      idx_out[t * k + s] = sel_e[tl][s];
+      gate_out[t * k + s] = g;
+    }
+  }
+  if (chunk_hist) {
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) chunk_hist[blockIdx.x * (int64_t)E + e] = hist[e];
+  }
+}
+
+template <int G, int NPL>
+void launch_topk_t(const float* logits, const float* sb, int gate, int64_t T,
+                   int E, int k, int32_t* idx, float* g, int32_t* hist,
+                   hipStream_t s) {
+  const int64_t nch = (T + kChunkTokens - 1) / kChunkTokens;
+  hipLaunchKernelGGL((topk_kernel<G, NPL>), dim3((unsigned)nch), dim3(256), 0,
+                     s, logits, sb, gate, T, E, k, idx, g, hist);
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float* logits, const float* select_bias, int gate,
+                       int64_t T, int E, int k, int32_t* idx, float* gate_out,
+                       int32_t* chunk_hist, hipStream_t s) {
+  if (E <= 8)
+    launch_topk_t<8, 1>(logits, select_bias, gate, T, E, k, idx, gate_out, chunk_hist, s);
+  else if (E <= 16)
+    launch_topk_t<16, 1>(logits, select_bias, gate, T, E, k, idx, gate_out, chunk_hist, s);
+  else if (E <= 32)
+    launch_topk_t<32, 1>(logits, select_bias, gate, T, E, k, idx, gate_out, chunk_hist, s);
+  else if (E <= 64)
+    launch_topk_t<64, 1>(logits, select_bias, gate, T, E, k, idx, gate_out, chunk_hist, s);
+  else if (E <= 128)
+    launch_topk_t<64, 2>(logits, select_bias, gate, T, E, k, idx, gate_out, chunk_hist, s);
+  else if (E <= 256)
+    launch_topk_t<64, 4>(logits, select_bias, gate, T, E, k, idx, gate_out, chunk_hist, s);
+  else if (E <= 512)
+    launch_topk_t<64, 8>(logits, select_bias, gate, T, E, k, idx, gate_out, chunk_hist, s);
+  else
+    launch_topk_t<64, 16>(logits, select_bias, gate, T, E, k, idx, gate_out, chunk_hist, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

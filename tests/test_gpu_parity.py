@@ -1,0 +1,218 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars (written in each check):
+* routing on the GPU's own fp32 keys: bit-exact for every token;
+* routing vs the oracle's logits: identical expert sets except on tokens whose
+  k-th / (k+1)-th key gap is below 1e-5, where the GPU choice must be valid;
+* gates within 2e-6 of the oracle's fp64 gates from the same logits;
+* counts, offsets, assign_row, row_token, drops: bit-exact;
+* x_perm: bit-exact copies, padding rows exactly zero;
+* y: max|y_gpu - y_ref| / max|y_ref| <= 2e-2 (bf16), <= 1e-5 (fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_25_amd as moe
+from helpers import (DEV, capacity_of, check_routing, gen_inputs, lib_cfg, np32,
+                     oracle_forward, rel_err, run_forward, tol_of)
+from moe_inputs import CONFIGS, MoEConfig
+
+pytestmark = pytest.mark.gpu
+
+# Sizes the oracle finishes in seconds that still span several GEMM tiles
+# (256-row and 256/128-column tiles, 64-deep K steps) with ragged tails.
+MEDIUM = [
+    CONFIGS["tiny_fp32"],
+    MoEConfig("dropless_softmax", T=1000, h=512, E=4, k=2, F=640, gate="softmax_topk"),
+    MoEConfig("capacity_heavy_drop", T=1000, h=384, E=8, k=2, F=384,
+              gate="softmax_all_topk", cf=(1, 2)),
+    MoEConfig("worked_example_small", T=512, h=256, E=8, k=2, F=384,
+              gate="softmax_all_topk", cf=(5, 4)),
+    MoEConfig("sigmoid_bias_shared", T=700, h=256, E=16, k=4, F=256,
+              gate="sigmoid_topk_norm", select_bias=("normal", 0.1), shared=True),
+    MoEConfig("zipf_dropless", T=2048, h=256, E=64, k=4, F=128,
+              logit_bias=("zipf", 1.2)),
+    MoEConfig("zipf_cf1", T=2048, h=256, E=64, k=4, F=128,
+              logit_bias=("zipf", 1.2), cf=(1, 1)),
+    MoEConfig("e256_k8_shared", T=300, h=256, E=256, k=8, F=128,
+              gate="sigmoid_topk_norm", select_bias=("normal", 0.1), shared=True),
+    MoEConfig("mixtral_bias", T=777, h=256, E=8, k=2, F=384, logit_bias=("normal", 0.5)),
+    MoEConfig("e1_k1_dense", T=333, h=256, E=1, k=1, F=256),
+    MoEConfig("k_equals_e", T=257, h=128, E=4, k=4, F=128),
+    MoEConfig("one_token", T=1, h=128, E=8, k=2, F=128, cf=(5, 4)),
+    MoEConfig("e1024_k16", T=70, h=128, E=1024, k=16, F=128, gate="softmax_all_topk"),
+    MoEConfig("f32_capacity", T=300, h=256, E=8, k=2, F=256, dtype="f32",
+              gate="softmax_all_topk", cf=(1, 1)),
+    MoEConfig("f32_sigmoid_shared", T=200, h=128, E=16, k=4, F=256, dtype="f32",
+              gate="sigmoid_topk_norm", select_bias=("normal", 0.1), shared=True),
+]
+
+
+def _report(name, **kw):
+    print(f"[parity] {name}: " + ", ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+@pytest.mark.parametrize("cfg", MEDIUM, ids=lambda c: c.name)
+def test_forward_matches_oracle(cfg):
+    print(f"[case] forward {cfg.name} T={cfg.T} h={cfg.h} E={cfg.E} k={cfg.k} "
+          f"F={cfg.F} {cfg.dtype} {cfg.gate} cf={cfg.cf}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    gpu = run_forward(cfg, inp, C_lib)
+    ref = oracle_forward(cfg, inp, C_ref, maps_only=True)
+    rep = check_routing(cfg, gpu, ref, C_ref, inp)
+    g_idx = gpu["topk_idx"].cpu().numpy()
+    ref_y = oracle_forward(cfg, inp, C_ref, idx=g_idx)["y"]
+    y = np32(gpu["y"])
+    assert np.isfinite(y).all()
+    err = rel_err(y, ref_y)
+    _report(cfg.name, rel_err=f"{err:.2e}", **rep)
+    assert err <= tol_of(cfg)
+
+
+STAGED = ["dropless_softmax", "capacity_heavy_drop", "sigmoid_bias_shared",
+          "f32_capacity", "f32_sigmoid_shared"]
+
+
+@pytest.mark.parametrize("name", STAGED)
+def test_stage_calls_equal_fused_call(name):
+    """router_topk -> permute -> grouped_gemm_swiglu (+ the shared expert as
+    its own E=1 call) -> combine gives bit-for-bit the fused layer's output;
+    x_perm holds exact copies of token rows and zero padding rows."""
+    cfg = next(c for c in MEDIUM if c.name == name)
+    print(f"[case] staged {name}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, _ = capacity_of(cfg)
+    fused = run_forward(cfg, inp, C_lib)
+    c = lib_cfg(cfg, C_lib)
+    T, E, k, h, F = cfg.T, cfg.E, cfg.k, cfg.h, cfg.F
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    rows = moe.moe_num_rows(c)
+    ws = torch.empty(moe.moe_workspace_bytes(c), dtype=torch.uint8, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    moe.moe_router_topk(c, inp["x"], inp["w_router"], inp["logit_bias"], inp["select_bias"],
+                        None, idx, gate, ws)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    assign = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    rowtok = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+    xperm = torch.full((rows, h), 7.0, dtype=tdt, device=DEV)
+    moe.moe_permute(c, inp["x"], idx, counts, offsets, assign, rowtok, xperm, ws)
+    act = torch.empty((rows, F), dtype=tdt, device=DEV)
+    yperm = torch.empty((rows, h), dtype=tdt, device=DEV)
+    moe.moe_grouped_gemm_swiglu(c, xperm, counts, offsets, inp["w1"], inp["w3"], inp["w2"],
+                                act, yperm, ws)
+    shared_y = None
+    if cfg.shared:
+        cs = moe.make_cfg(T, h, F, 1, 1, cfg.dtype, cfg.gate)
+        ws_s = torch.empty(moe.moe_workspace_bytes(cs), dtype=torch.uint8, device=DEV)
+        cnt_s = torch.tensor([T], dtype=torch.int32, device=DEV)
+        off_s = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+        act_s = torch.empty((T, F), dtype=tdt, device=DEV)
+        shared_y = torch.empty((T, h), dtype=tdt, device=DEV)
+        moe.moe_grouped_gemm_swiglu(cs, inp["x"], cnt_s, off_s, inp["ws1"].unsqueeze(0),
+                                    inp["ws3"].unsqueeze(0), inp["ws2"].unsqueeze(0),
+                                    act_s, shared_y, ws_s)
+    y = torch.empty((T, h), dtype=tdt, device=DEV)
+    moe.moe_unpermute_combine(c, yperm, assign, gate, shared_y, y)
+    torch.cuda.synchronize()
+
+    assert torch.equal(idx, fused["topk_idx"])
+    assert torch.equal(gate, fused["topk_gate"])
+    assert torch.equal(assign, fused["assign_row"])
+    assert torch.equal(rowtok, fused["row_token"])
+    assert torch.equal(counts, fused["expert_counts"])
+    assert torch.equal(offsets, fused["expert_offsets"])
+    assert torch.equal(y.view(torch.int16 if cfg.dtype == "bf16" else torch.int32),
+                       fused["y"].view(torch.int16 if cfg.dtype == "bf16" else torch.int32))
+    # dispatch buffer: row r holds token row_token[r] exactly; pads are zero
+    rt = rowtok.long()
+    kept = rt >= 0
+    xb = inp["x"].view(torch.int16 if cfg.dtype == "bf16" else torch.int32)
+    pb = xperm.view(torch.int16 if cfg.dtype == "bf16" else torch.int32)
+    assert torch.equal(pb[kept], xb[rt[kept]])
+    assert (pb[~kept] == 0).all()
+    # unpermute of the dispatch buffer (k = 1 view of slot 0) is the identity
+    a0 = assign.view(T, k)[:, 0].long()
+    ok = a0 >= 0
+    assert torch.equal(pb[a0[ok]], xb[ok])
+
+
+def test_deterministic():
+    cfg = next(c for c in MEDIUM if c.name == "zipf_cf1")
+    inp = gen_inputs(cfg)
+    C_lib, _ = capacity_of(cfg)
+    a = run_forward(cfg, inp, C_lib)
+    b = run_forward(cfg, inp, C_lib)
+    for key in ("topk_idx", "topk_gate", "expert_counts", "assign_row", "row_token"):
+        assert torch.equal(a[key], b[key]), key
+    assert torch.equal(a["y"].view(torch.int16), b["y"].view(torch.int16))
+
+
+def test_empty_input_is_a_no_op():
+    cfg = MoEConfig("empty", T=0, h=128, E=4, k=2, F=128)
+    c = lib_cfg(cfg, 0)
+    inp = gen_inputs(cfg.with_(T=1))
+    y = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(moe.moe_workspace_bytes(c), 1), dtype=torch.uint8, device=DEV)
+    moe.moe_forward(c, {n: inp[n] for n in ("w_router", "w1", "w3", "w2")},
+                    inp["x"], y, None, ws)
+    torch.cuda.synchronize()
+
+
+def test_errors_are_reported_before_launch():
+    cfg = CONFIGS["tiny_fp32"]
+    inp = gen_inputs(cfg)
+    c = lib_cfg(cfg, 0)
+    y = torch.empty((cfg.T, cfg.h), dtype=torch.float32, device=DEV)
+    small = torch.empty(16, dtype=torch.uint8, device=DEV)
+    w = {n: inp[n] for n in ("w_router", "w1", "w3", "w2")}
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward(c, w, inp["x"], y, None, small)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    bad = lib_cfg(cfg.with_(k=5), 0)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward(bad, w, inp["x"], y, None, small)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------ full sizes
+FULL = ["worked_example", "mixtral", "deepseek_v3", "skewed", "skewed_cf1"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_routing_and_sampled_outputs(name):
+    """The full workloads, launched exactly as the benchmark launches them:
+    routing, counts, maps and drops compared in full; outputs on sampled
+    tokens (always including the first, the last and dropped ones)."""
+    cfg = CONFIGS[name]
+    print(f"[case] full {name} T={cfg.T} h={cfg.h} E={cfg.E} k={cfg.k} F={cfg.F}", flush=True)
+    torch.cuda.empty_cache()
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    if name == "worked_example":
+        assert C_lib == 1280
+    gpu = run_forward(cfg, inp, C_lib)
+    ref = oracle_forward(cfg, inp, C_ref, maps_only=True)
+    rep = check_routing(cfg, gpu, ref, C_ref, inp)
+    counts = gpu["expert_counts"].cpu().numpy()
+    if cfg.logit_bias is not None and cfg.logit_bias[0] == "zipf":
+        assert counts.max() > 10 * counts.mean()
+    g_idx = gpu["topk_idx"].cpu().numpy()
+    assign = gpu["assign_row"].cpu().numpy().reshape(cfg.T, cfg.k)
+    rng = np.random.default_rng(0)
+    n = 6 if cfg.E > 64 else 16
+    tok = set(rng.choice(cfg.T, n, replace=False).tolist()) | {0, cfg.T - 1}
+    dropped = np.nonzero((assign < 0).any(1))[0]
+    tok |= set(dropped[:4].tolist())
+    tok = np.array(sorted(tok))
+    ref_y = oracle_forward(cfg, inp, C_ref, tokens=tok, idx=g_idx)["y"]
+    y = np32(gpu["y"][torch.as_tensor(tok, device=DEV)])
+    err = rel_err(y, ref_y)
+    _report(name, rel_err=f"{err:.2e}", sampled=len(tok), max_count=int(counts.max()),
+            mean_count=float(counts.mean()), **rep)
+    assert err <= 2e-2
+    del gpu, inp
+    torch.cuda.empty_cache()
