@@ -20,7 +20,7 @@ constexpr int kCombTok = 2;
 
 template <int KMAX>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(
-    const uint4* __restrict__ yp, const int32_t* __restrict__ assign_row,
+    const uint4* __restrict__ yp, int64_t pv, const int32_t* __restrict__ assign_row,
     const float* __restrict__ gate, const uint4* __restrict__ shared_y,
     uint4* __restrict__ y, int64_t T, int nv, int k) {
   for (int tt = 0; tt < kCombTok; ++tt) {
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         if (rows[j] >= 0) {
-          const uint4 q = yp[(int64_t)rows[j] * nv + v];
+          const uint4 q = yp[(int64_t)rows[j] * pv + v];
           const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
         }
       }
       if (shared_y) {
-        const uint4 q = shared_y[t * nv + v];
+        const uint4 q = shared_y[t * pv + v];
         const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
 
 template <int KMAX>
 __global__ __launch_bounds__(256) void combine_f32_kernel(
-    const float4* __restrict__ yp, const int32_t* __restrict__ assign_row,
+    const float4* __restrict__ yp, int64_t pv, const int32_t* __restrict__ assign_row,
     const float* __restrict__ gate, const float4* __restrict__ shared_y,
     float4* __restrict__ y, int64_t T, int nv, int k) {
   for (int tt = 0; tt < kCombTok; ++tt) {
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         if (rows[j] >= 0) {
-          const float4 q = yp[(int64_t)rows[j] * nv + v];
+          const float4 q = yp[(int64_t)rows[j] * pv + v];
           acc.x = fmaf(g[j], q.x, acc.x);
           acc.y = fmaf(g[j], q.y, acc.y);
           acc.z = fmaf(g[j], q.z, acc.z);
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(
         }
       }
       if (shared_y) {
-        const float4 q = shared_y[t * nv + v];
+        const float4 q = shared_y[t * pv + v];
         acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
       }
       y[t * nv + v] = acc;
@@ -105,33 +105,36 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(
 }
 
 template <int KMAX>
-void launch_combine_t(int dtype, const void* yp, const int32_t* ar, const float* g,
+void launch_combine_t(int dtype, const void* yp, int ld, const int32_t* ar, const float* g,
                       const void* sy, void* y, int64_t T, int h, int k,
                       hipStream_t s) {
   const int64_t nb = (T + kCombTok - 1) / kCombTok;
   if (dtype == 1)
     hipLaunchKernelGGL((combine_bf16_kernel<KMAX>), dim3((unsigned)nb), dim3(256), 0, s,
-                       (const uint4*)yp, ar, g, (const uint4*)sy, (uint4*)y, T, h / 8, k);
+                       (const uint4*)yp, (int64_t)ld / 8, ar, g, (const uint4*)sy, (uint4*)y, T,
+                       h / 8, k);
   else
     hipLaunchKernelGGL((combine_f32_kernel<KMAX>), dim3((unsigned)nb), dim3(256), 0, s,
-                       (const float4*)yp, ar, g, (const float4*)sy, (float4*)y, T, h / 4, k);
+                       (const float4*)yp, (int64_t)ld / 4, ar, g, (const float4*)sy, (float4*)y,
+                       T, h / 4, k);
 }
 
 }  // namespace
 
-hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* assign_row,
-                          const float* gate, const void* shared_y, void* y,
-                          int64_t T, int h, int k, hipStream_t s) {
+hipError_t launch_combine(int dtype, const void* y_perm, int ld_perm,
+                          const int32_t* assign_row, const float* gate,
+                          const void* shared_y, void* y, int64_t T, int h, int k,
+                          hipStream_t s) {
   if (k <= 1)
-    launch_combine_t<1>(dtype, y_perm, assign_row, gate, shared_y, y, T, h, k, s);
+    launch_combine_t<1>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, s);
   else if (k <= 2)
-    launch_combine_t<2>(dtype, y_perm, assign_row, gate, shared_y, y, T, h, k, s);
+    launch_combine_t<2>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, s);
   else if (k <= 4)
-    launch_combine_t<4>(dtype, y_perm, assign_row, gate, shared_y, y, T, h, k, s);
+    launch_combine_t<4>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, s);
   else if (k <= 8)
-    launch_combine_t<8>(dtype, y_perm, assign_row, gate, shared_y, y, T, h, k, s);
+    launch_combine_t<8>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, s);
   else
-    launch_combine_t<16>(dtype, y_perm, assign_row, gate, shared_y, y, T, h, k, s);
+    launch_combine_t<16>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, s);
   return hipGetLastError();
 }
 

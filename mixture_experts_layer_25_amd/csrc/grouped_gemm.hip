@@ -11,16 +11,21 @@
 // C = A · B^T with 16-byte loads along K for A and B alike.
 //
 // bf16 kernel (gfx950): 256 threads = 4 waves in a 2x2 grid, a 256x256
-// output tile per workgroup (BK = 64), each wave a 128x128 sub-tile held as
-// 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane).  A and B
-// tiles are staged through LDS in two 64 KiB stages (double buffering):
-// while the MFMAs consume one stage, the next K slice is loaded into
-// registers and written to the other stage.  Rows are 128 B; the 16-byte
-// chunk c of row r is stored at chunk c ^ (r & 7), so the 8 lanes that an
-// LDS access services together touch 8 different bank groups, for both the
-// row-wise stores and the column-of-rows MFMA operand reads.
+// output tile per workgroup, each wave a 128x128 sub-tile held as 4x4
+// v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, in AGPRs).
+// K advances in slices of 64 (128-byte rows, whole cache lines per row).
+// Slices are copied global -> LDS directly (buffer_load_dwordx4 ... lds, no
+// registers in between) into a ring of three A slots and two B slots of
+// 32 KiB each (all 160 KiB of LDS), A two slices and B one slice ahead of the
+// MFMAs; buffer bounds return zeros for rows past a ragged group's end.  The
+// instruction order is fixed by hand: every MFMA pair is accompanied by one
+// LDS fragment read for the next sub-step and, after the barrier, by the
+// copies of the next slices, so the wave never stalls on a burst of memory
+// instructions.  Routed group g starts its K loop at slice g*nk/8: groups
+// run on different XCDs, and staggered K offsets spread their weight reads
+// over the memory channels (the row strides are powers of two).
 //
-// For GEMM 1 the 256 B rows of a tile are [w1 f0..f0+63 | w3 f0..f0+63 |
+// For GEMM 1 the 256 B-tile rows are [w1 f0..f0+63 | w3 f0..f0+63 |
 // w1 f0+64..f0+127 | w3 f0+64..f0+127]: each wave's 128 columns hold 64 w1
 // columns and the matching 64 w3 columns, so silu(a1) * a3 is formed in
 // registers and a tile writes 128 activation columns.
@@ -39,8 +44,17 @@ namespace moe {
 namespace {
 
 constexpr int BM = kGemmBM_bf16, BN = 256, BK = 64;
-constexpr int kHalf = BM * BK * 2;         // bytes of the A (or B) stage part
-constexpr int kStage = 2 * kHalf;          // 64 KiB
+constexpr int kPart = BM * BK * 2;          // 32 KiB: one K slice of the A (or B) tile
+constexpr int kSlotsA = 3, kSlotsB = 2;     // LDS ring slots for A and for B slices
+constexpr int kOffB = kSlotsA * kPart;      // B slots follow the A slots
+constexpr int kLds = (kSlotsA + kSlotsB) * kPart;   // 160 KiB
+
+// LDS rows are BK * 2 = 128 bytes (8 chunks of 16 B); chunk c of row r is
+// stored at c ^ swz(r).  An MFMA operand read has 16 lanes on 16 consecutive
+// rows and one chunk: with this swizzle they fall in 16 distinct 16-byte
+// slots of 256 bytes (64 banks), and any 8 consecutive rows in 8 distinct
+// slots of 128 bytes (32 banks).
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Largest g with mtp[g] * NT <= L (mtp non-decreasing, mtp[0] = 0,
 // mtp[G] * NT > L).
@@ -87,56 +101,96 @@ __device__ __forceinline__ bool map_tile(const GroupedGemmArgs& a, int NT,
   return true;
 }
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+#define LDS_AS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zero, which is how rows beyond a ragged group's end enter the MFMAs.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint8_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
 template <bool SWIGLU>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];   // 160 KiB
 
   const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
   Tile tl;
   if (!map_tile(a, NT, blockIdx.x, true, BM, tl)) return;
+  // Tile fields and the wave index are wave-uniform; saying so keeps the
+  // buffer descriptors below in scalar registers.
+  tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+  tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
+  tl.m_valid = __builtin_amdgcn_readfirstlane(tl.m_valid);
+  tl.a_row = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tl.a_row >> 32)) << 32) |
+             (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.a_row);
+  tl.o_row = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tl.o_row >> 32)) << 32) |
+             (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.o_row);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
-  const int K = a.K, N = a.N;
+  const int K = a.K, N = a.N, ldo = a.ldo;
   const bool shared = tl.g >= a.E_routed;
-  const uint16_t* A = (const uint16_t*)((shared && !a.a_from_out_rows) ? a.A_shared : a.A);
+  const bool a_shared = shared && !a.a_from_out_rows;
+  const uint16_t* A = (const uint16_t*)(a_shared ? a.A_shared : a.A);
+  const int lda = a_shared ? a.lda_shared : a.lda;
+  const uint32_t browbytes = (uint32_t)K * 2;     // weights are dense [out, K]
+  const uint32_t arowbytes = (uint32_t)lda * 2;
   const uint16_t* B0 = (const uint16_t*)(shared ? a.B0s : a.B0);
   const uint16_t* B1 = (const uint16_t*)(shared ? a.B1s : a.B1);
   if (!shared) {
     B0 += (int64_t)tl.g * a.b_stride;
     if (SWIGLU) B1 += (int64_t)tl.g * a.b_stride;
   }
+  const int nk = K / BK;   // even: K % 128 == 0
+  const int krot = (a.rotate_k && !shared) ? (int)(((int64_t)tl.g * nk / 8) % nk) : 0;
 
-  // Global -> register -> LDS copy: thread covers chunk (tid & 7) of rows
-  // j*32 + (tid >> 3), j = 0..7, of both the A and the B tile.
-  const int lrow = tid >> 3, lch = tid & 7;
-  const uint16_t* asrc[8];
-  const uint16_t* bsrc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = j * 32 + lrow;
-    const int ar = row < tl.m_valid ? row : tl.m_valid - 1;
-    asrc[j] = A + (tl.a_row + ar) * K + lch * 8;
-    if (SWIGLU) {
-      const int blk = j >> 1;  // 64-row blocks: w1, w3, w1, w3
-      const uint16_t* W = (blk & 1) ? B1 : B0;
-      const int64_t wrow = (int64_t)tl.nt * 128 + (blk >> 1) * 64 + (row & 63);
-      bsrc[j] = W + wrow * K + lch * 8;
-    } else {
-      int64_t wrow = (int64_t)tl.nt * BN + row;
-      if (wrow > N - 1) wrow = N - 1;
-      bsrc[j] = B0 + wrow * K + lch * 8;
-    }
+  // Global -> LDS copies: wave w fills rows w*64 .. w*64+63 of the A and the
+  // B slice, 8 rows (1 KiB) per instruction; lane l lands at byte 16*l of
+  // the block: row l >> 3, stored chunk l & 7, which holds logical chunk
+  // (l & 7) ^ (l >> 3) ^ i in the i-th block (swz of row w*64 + 8*i + (l>>3)).
+  const int a_rows = __builtin_amdgcn_readfirstlane(min(max(tl.m_valid - w * 64, 0), 64));
+  const rsrc_t rsA = make_rsrc(A + (tl.a_row + w * 64) * (int64_t)lda, (uint32_t)a_rows * arowbytes);
+  rsrc_t rsB;
+  if (SWIGLU) {
+    // B rows of the tile: [w1 f0.. | w3 f0.. | w1 f0+64.. | w3 f0+64..], 64 each
+    const uint16_t* W = (w & 1) ? B1 : B0;
+    rsB = make_rsrc(W + ((int64_t)tl.nt * 128 + (w >> 1) * 64) * K, 64u * browbytes);
+  } else {
+    const int64_t brow = (int64_t)tl.nt * BN + w * 64;
+    const int nb = __builtin_amdgcn_readfirstlane(
+        (int)min(max((int64_t)N - brow, (int64_t)0), (int64_t)64));
+    rsB = make_rsrc(B0 + min(brow, (int64_t)N - 1) * K, (uint32_t)nb * browbytes);
   }
-  const int st_off = lrow * 128 + ((lch ^ (lrow & 7)) << 4);
+  uint32_t voffA[8], voffB[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = (uint32_t)((((lane & 7) ^ (lane >> 3) ^ i) & 7) << 4);
+    voffA[i] = (uint32_t)(lane >> 3) * arowbytes + c;
+    voffB[i] = (uint32_t)(lane >> 3) * browbytes + c;
+  }
+  uint8_t* const dstA = smem + w * 8192;
+  uint8_t* const dstB = smem + kOffB + w * 8192;
 
   // MFMA operand reads: lane l reads row (l & 31) of a 32-row fragment and
-  // the 16-byte chunk 2*s + (l >> 5) of K sub-step s.
-  const int rA = wm * (128 * 128) + (lane & 31) * 128;
-  const int rB = kHalf + wn * (128 * 128) + (lane & 31) * 128;
-  int cx[4];
+  // logical chunk 2*s + (l >> 5) of sub-step s; swz of that row is
+  // (l & 7) ^ (4*(i & 1) + ((l >> 3) & 3)) for fragment i.
+  const int rA = (wm * 128 + (lane & 31)) * (BK * 2);
+  const int rB = (wn * 128 + (lane & 31)) * (BK * 2);
+  const int fe = (lane & 7) ^ ((lane >> 3) & 3);
+  const int fo = (lane & 7) ^ (4 | ((lane >> 3) & 3));
+  int cx[4][2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) cx[s] = ((2 * s + (lane >> 5)) ^ (lane & 7)) << 4;
+  for (int s = 0; s < 4; ++s) {
+    cx[s][0] = ((2 * s + (lane >> 5)) ^ fe) << 4;
+    cx[s][1] = ((2 * s + (lane >> 5)) ^ fo) << 4;
+  }
 
   floatx16 acc[4][4];
 #pragma unroll
@@ -146,58 +200,98 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 ra[8], rb[8];
-  const int nk = K / BK;
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
 
+#define SB() __builtin_amdgcn_sched_barrier(0)
+#define MF(FA, FB, I, J) \
+  acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[I], FB[J], acc[I][J], 0, 0, 0)
+#define RDA(F, SA, S, I) F[I] = lds_frag((SA) + rA + (I) * 4096 + cx[S][(I) & 1])
+#define RDB(F, SBP, S, J) F[J] = lds_frag((SBP) + rB + (J) * 4096 + cx[S][(J) & 1])
+// K slice of step KT (rotated); past the end the offset leaves the buffer
+// and the copy returns zeros
+#define KSL(KT) ((KT) + krot >= nk ? (KT) + krot - nk : (KT) + krot)
+#define KOFF(KT) ((KT) < nk ? (uint32_t)KSL(KT) * (BK * 2) : 0x7FFFFFF0u)
+#define DMA_A(KT, I)                                                                          \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                   \
+      rsA, LDS_AS(dstA + ((KT) % kSlotsA) * kPart + (I) * 1024), 16, voffA[I],                \
+      (KT) < nk ? (uint32_t)(I) * 8u * arowbytes + KOFF(KT) : KOFF(KT), 0, 0)
+#define DMA_B(KT, I)                                                                          \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                   \
+      rsB, LDS_AS(dstB + ((KT) & 1) * kPart + (I) * 1024), 16, voffB[I],                      \
+      (KT) < nk ? (uint32_t)(I) * 8u * browbytes + KOFF(KT) : KOFF(KT), 0, 0)
+// one sub-step: 8 groups of [copy] [fragment read] [2 MFMAs]
+#define SUBSTEP(FA, FB, RFA, RFB, SA, SBP, S, COPY)                                   \
+  COPY(0); RDA(RFA, SA, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                \
+  COPY(1); RDA(RFA, SA, S, 1); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                \
+  COPY(2); RDA(RFA, SA, S, 2); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB();                \
+  COPY(3); RDA(RFA, SA, S, 3); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                \
+  COPY(4); RDB(RFB, SBP, S, 0); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();               \
+  COPY(5); RDB(RFB, SBP, S, 1); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();               \
+  COPY(6); RDB(RFB, SBP, S, 2); MF(FA, FB, 3, 0); MF(FA, FB, 3, 1); SB();               \
+  COPY(7); RDB(RFB, SBP, S, 3); MF(FA, FB, 3, 2); MF(FA, FB, 3, 3); SB()
+
+  // s_waitcnt immediates (gfx9 encoding; expcnt and lgkmcnt left at "no wait")
+  constexpr int kWaitVm0 = 0x0F70, kWaitVm8 = 0x0F78, kWaitVm24 = 0x4F78;
+
+  // Prologue: A(0), B(0), A(1), B(1), A(2) in flight; wait for slice 0.
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    ra[j] = ld16(asrc[j]);
-    rb[j] = ld16(bsrc[j]);
-  }
+  for (int i = 0; i < 8; ++i) DMA_A(0, i);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    *reinterpret_cast<uint4*>(smem + j * 4096 + st_off) = ra[j];
-    *reinterpret_cast<uint4*>(smem + kHalf + j * 4096 + st_off) = rb[j];
-  }
+  for (int i = 0; i < 8; ++i) DMA_B(0, i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) DMA_A(1, i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) DMA_B(1, i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) DMA_A(2, i);
+  __builtin_amdgcn_s_waitcnt(kWaitVm24);
   __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) RDA(fa0, smem, 0, i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) RDB(fb0, smem + kOffB, 0, j);
 
+  // Step kt (slice kt in A slot kt%3, B slot kt%2; sub-step 0 fragments
+  // already in registers):
+  //   s0..s2: MFMAs of sub-steps 0..2, reads of sub-steps 1..3
+  //   wait until at most 8 copies (A(kt+2)'s) may be in flight -> A(kt+1),
+  //   B(kt+1) landed;
+  //   barrier: slice kt+1 visible to all, slice kt's slots free
+  //   s3: MFMAs of sub-step 3, reads of slice kt+1 sub-step 0, copies of
+  //       all of B(kt+2) and then all of A(kt+3) into slice kt's slots.
+  //       Copies complete in issue order, so "at most 8 copies in flight"
+  //       at the next barrier means everything up to B(kt+2) has landed.
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = (kt + 1) * BK;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ra[j] = ld16(asrc[j] + k0);
-        rb[j] = ld16(bsrc[j] + k0);
-      }
-    }
-    const uint8_t* sb = smem + cur * kStage;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sb + rA + i * 4096 + cx[s]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + rB + j * 4096 + cx[s]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      uint8_t* sn = smem + (cur ^ 1) * kStage;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        *reinterpret_cast<uint4*>(sn + j * 4096 + st_off) = ra[j];
-        *reinterpret_cast<uint4*>(sn + kHalf + j * 4096 + st_off) = rb[j];
-      }
-    }
-    __syncthreads();
+    const uint8_t* sa = smem + (kt % kSlotsA) * kPart;
+    const uint8_t* sbb = smem + kOffB + (kt & 1) * kPart;
+    const uint8_t* na = smem + ((kt + 1) % kSlotsA) * kPart;
+    const uint8_t* nbb = smem + kOffB + ((kt + 1) & 1) * kPart;
+#define COPY_NONE(I)
+#define COPY_BA(I)                                   \
+  if ((I) < 4) {                                     \
+    DMA_B(kt + 2, 2 * (I)); DMA_B(kt + 2, 2 * (I) + 1); \
+  } else {                                           \
+    DMA_A(kt + 3, 2 * (I) - 8); DMA_A(kt + 3, 2 * (I) - 7); \
   }
+    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 1, COPY_NONE);
+    SUBSTEP(fa1, fb1, fa0, fb0, sa, sbb, 2, COPY_NONE);
+    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 3, COPY_NONE);
+    __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    __syncthreads();
+    SUBSTEP(fa1, fb1, fa0, fb0, na, nbb, 0, COPY_BA);
+#undef COPY_NONE
+#undef COPY_BA
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#undef SB
+#undef MF
+#undef RDA
+#undef RDB
+#undef KSL
+#undef KOFF
+#undef DMA_A
+#undef DMA_B
+#undef SUBSTEP
 
   // 32x32 accumulator layout: lane l holds column (l & 31); register r of a
   // fragment is row 8*(r/4) + 4*(l/32) + r%4.
@@ -216,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
           if (row < tl.m_valid) {
             const float z = acc[i][j][r];
             const float v = z / (1.f + __expf(-z)) * acc[i][j + 2][r];
-            out[(tl.o_row + row) * N + col] = f32_to_bf16_bits(v);
+            out[(tl.o_row + row) * ldo + col] = f32_to_bf16_bits(v);
           }
         }
       }
@@ -231,7 +325,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
           for (int r = 0; r < 16; ++r) {
             const int row = wm * 128 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
             if (row < tl.m_valid)
-              out[(tl.o_row + row) * N + col] = f32_to_bf16_bits(acc[i][j][r]);
+              out[(tl.o_row + row) * ldo + col] = f32_to_bf16_bits(acc[i][j][r]);
           }
         }
       }
@@ -254,7 +348,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GroupedGemmArgs a) {
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int K = a.K, N = a.N;
   const bool shared = tl.g >= a.E_routed;
-  const float* A = (const float*)((shared && !a.a_from_out_rows) ? a.A_shared : a.A);
+  const bool a_shared = shared && !a.a_from_out_rows;
+  const float* A = (const float*)(a_shared ? a.A_shared : a.A);
+  const int lda = a_shared ? a.lda_shared : a.lda;
   const float* B0 = (const float*)(shared ? a.B0s : a.B0);
   const float* B1 = (const float*)(shared ? a.B1s : a.B1);
   if (!shared) {
@@ -263,7 +359,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GroupedGemmArgs a) {
   }
   const int lr = tid >> 2, lk = (tid & 3) * 4;
   const int ar = lr < tl.m_valid ? lr : tl.m_valid - 1;
-  const float* ap = A + (tl.a_row + ar) * K + lk;
+  const float* ap = A + (tl.a_row + ar) * lda + lk;
   const int64_t n0 = (int64_t)tl.nt * FBN;
   const float* bp = B0 + (n0 + lr) * K + lk;
   const float* b3p = SWIGLU ? B1 + (n0 + lr) * K + lk : nullptr;
@@ -316,7 +412,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GroupedGemmArgs a) {
       const int64_t col = n0 + tx + 16 * c;
       float v = acc[i][c];
       if (SWIGLU) v = v / (1.f + expf(-v)) * acc3[i][c];
-      out[(tl.o_row + row) * N + col] = v;
+      out[(tl.o_row + row) * a.ldo + col] = v;
     }
   }
 }

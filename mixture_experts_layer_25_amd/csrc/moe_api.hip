@@ -26,6 +26,12 @@ int64_t rows_of(const moe_cfg_t& c) {
   return c.capacity > 0 ? (int64_t)c.E * c.capacity : c.T * c.k;
 }
 
+// Row strides (elements) of the workspace buffers x_perm / y_perm and act:
+// 128 bytes of padding keep consecutive rows of these power-of-two widths
+// off the same memory channels.
+int ld_h(const moe_cfg_t& c) { return c.h + 128 / esize(c); }
+int ld_f(const moe_cfg_t& c) { return c.F + 128 / esize(c); }
+
 int row_tile(const moe_cfg_t& c) {
   return c.dtype == MOE_DTYPE_BF16 ? moe::kGemmBM_bf16 : moe::kGemmBM_f32;
 }
@@ -77,9 +83,9 @@ Layout layout_of(const moe_cfg_t& c) {
   L.assign = take((size_t)(T * k) * 4);
   L.rowtok = take((size_t)rows * 4);
   L.gtab = take((size_t)gtab_ints((int)G) * 4);
-  L.xperm = take((size_t)rows * c.h * es);
-  L.act = take((size_t)rows_all * c.F * es);
-  L.yperm = take((size_t)rows_all * c.h * es);
+  L.xperm = take((size_t)rows * ld_h(c) * es);
+  L.act = take((size_t)rows_all * ld_f(c) * es);
+  L.yperm = take((size_t)rows_all * ld_h(c) * es);
   L.total = off;
   return L;
 }
@@ -186,7 +192,7 @@ MOE_API int moe_permute(const moe_cfg_t* cfg, const void* x, const int32_t* topk
   MOE_TRY(moe::launch_assign(topk_idx, base, expert_offsets, c.T, c.E, c.k, c.capacity,
                              assign_row, row_token, s));
   MOE_TRY(moe::launch_permute(c.dtype, x, assign_row, expert_counts, c.T, c.h, c.E, c.k,
-                              c.capacity, x_perm, row_token, s));
+                              c.capacity, x_perm, c.h, row_token, s));
   return MOE_OK;
 }
 
@@ -217,6 +223,10 @@ MOE_API int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
   a.out = act;
   a.K = c.h;
   a.N = c.F;
+  a.lda = c.h;
+  a.lda_shared = c.h;
+  a.ldo = c.F;
+  a.rotate_k = 1;
   a.gtab = gtab;
   a.G = c.E;
   a.E_routed = c.E;
@@ -229,6 +239,8 @@ MOE_API int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
   a.out = y_perm;
   a.K = c.F;
   a.N = c.h;
+  a.lda = c.F;
+  a.ldo = c.h;
   a.a_from_out_rows = 1;
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
   return MOE_OK;
@@ -242,8 +254,8 @@ MOE_API int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
   const moe_cfg_t& c = *cfg;
   if (c.T == 0) return MOE_OK;
   if (!y_perm || !assign_row || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
-  MOE_TRY(moe::launch_combine(c.dtype, y_perm, assign_row, topk_gate, shared_y, y, c.T,
-                              c.h, c.k, (hipStream_t)stream));
+  MOE_TRY(moe::launch_combine(c.dtype, y_perm, c.h, assign_row, topk_gate, shared_y, y,
+                              c.T, c.h, c.k, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -296,7 +308,7 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
                              rowtok, s));
   MOE_TRY(mark(4));
   MOE_TRY(moe::launch_permute(c.dtype, x, assign, counts, c.T, c.h, c.E, c.k, c.capacity,
-                              xperm, rowtok, s));
+                              xperm, ld_h(c), rowtok, s));
   MOE_TRY(mark(5));
   moe::GroupedGemmArgs a{};
   a.A = xperm;
@@ -309,6 +321,10 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   a.out = act;
   a.K = c.h;
   a.N = c.F;
+  a.lda = ld_h(c);
+  a.lda_shared = c.h;
+  a.ldo = ld_f(c);
+  a.rotate_k = 1;
   a.gtab = gtab;
   a.G = c.E + c.has_shared;
   a.E_routed = c.E;
@@ -325,12 +341,15 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   a.out = yperm;
   a.K = c.F;
   a.N = c.h;
+  a.lda = ld_f(c);
+  a.ldo = ld_h(c);
   a.a_from_out_rows = 1;
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
   MOE_TRY(mark(7));
   const void* shared_y =
-      c.has_shared ? (const void*)(at<char>(yperm, (size_t)rows * c.h * esize(c))) : nullptr;
-  MOE_TRY(moe::launch_combine(c.dtype, yperm, assign, gate, shared_y, y, c.T, c.h, c.k, s));
+      c.has_shared ? (const void*)(at<char>(yperm, (size_t)rows * ld_h(c) * esize(c))) : nullptr;
+  MOE_TRY(moe::launch_combine(c.dtype, yperm, ld_h(c), assign, gate, shared_y, y, c.T, c.h, c.k,
+                              s));
   MOE_TRY(mark(8));
   return MOE_OK;
 }

@@ -25,6 +25,10 @@ struct GroupedGemmArgs {
   void* out;             // act [rows,F] (GEMM1) or y_perm [rows,h] (GEMM2)
   int K;                 // reduction length (h for GEMM1, F for GEMM2)
   int N;                 // output columns (F for GEMM1, h for GEMM2)
+  int lda;               // row stride (elements) of A for the routed groups
+  int lda_shared;        // row stride of A_shared
+  int ldo;               // row stride of out
+  int rotate_k;          // 1: routed group g starts its K loop at slice g*nk/8
   const int32_t* gtab;
   int G;                 // groups in gtab
   int E_routed;          // groups 0..E_routed-1 use B0/B1, group E_routed B0s/B1s
@@ -53,10 +57,11 @@ hipError_t launch_assign(const int32_t* idx, const int32_t* chunk_base,
                          int64_t C, int32_t* assign_row, int32_t* row_token,
                          hipStream_t s);
 
+// x_perm rows are ld_perm elements apart (>= h).
 hipError_t launch_permute(int dtype, const void* x, const int32_t* assign_row,
                           const int32_t* counts, int64_t T, int h, int E,
-                          int k, int64_t C, void* x_perm, int32_t* row_token,
-                          hipStream_t s);
+                          int k, int64_t C, void* x_perm, int ld_perm,
+                          int32_t* row_token, hipStream_t s);
 
 // Groups from caller-provided counts/offsets, clamped to rows [0, rows).
 hipError_t launch_gtab(const int32_t* counts, const int32_t* offsets, int E,
@@ -65,7 +70,8 @@ hipError_t launch_gtab(const int32_t* counts, const int32_t* offsets, int E,
 hipError_t launch_grouped_gemm(int dtype, bool swiglu,
                                const GroupedGemmArgs& a, hipStream_t s);
 
-hipError_t launch_combine(int dtype, const void* y_perm,
+// y_perm and shared_y rows are ld_perm elements apart (>= h).
+hipError_t launch_combine(int dtype, const void* y_perm, int ld_perm,
                           const int32_t* assign_row, const float* gate,
                           const void* shared_y, void* y, int64_t T, int h,
                           int k, hipStream_t s);

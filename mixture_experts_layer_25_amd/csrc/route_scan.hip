@@ -248,7 +248,7 @@ constexpr int kPadBlocks = 256;  // workgroups that clear padding rows
 __global__ __launch_bounds__(256) void permute_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ assign_row,
     const int32_t* __restrict__ counts, int64_t T, int nv, int E, int k,
-    int64_t C, int64_t ntb, uint4* __restrict__ x_perm,
+    int64_t C, int64_t ntb, uint4* __restrict__ x_perm, int64_t pv,
     int32_t* __restrict__ row_token) {
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void permute_kernel(
         const uint4 val = src[v];
         for (int j = 0; j < k; ++j) {
           const int r = assign_row[t * k + j];
-          if (r >= 0) x_perm[(int64_t)r * nv + v] = val;
+          if (r >= 0) x_perm[(int64_t)r * pv + v] = val;
         }
       }
     }
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(256) void permute_kernel(
   for (int e = 0; e < E; ++e) {
     const int64_t kept = min((int64_t)counts[e], C);
     for (int64_t r = e * C + kept + pb; r < (e + 1) * C; r += kPadBlocks) {
-      uint4* dst = x_perm + r * nv;
+      uint4* dst = x_perm + r * pv;
       for (int v = tid; v < nv; v += 256) dst[v] = uint4{0u, 0u, 0u, 0u};
       if (tid == 0) row_token[r] = -1;
     }
@@ -325,15 +325,16 @@ hipError_t launch_assign(const int32_t* idx, const int32_t* chunk_base,
 
 hipError_t launch_permute(int dtype, const void* x, const int32_t* assign_row,
                           const int32_t* counts, int64_t T, int h, int E, int k,
-                          int64_t C, void* x_perm, int32_t* row_token,
+                          int64_t C, void* x_perm, int ld_perm, int32_t* row_token,
                           hipStream_t s) {
   const int esz = dtype == 1 ? 2 : 4;
   const int nv = h * esz / 16;
+  const int64_t pv = (int64_t)ld_perm * esz / 16;
   const int64_t ntb = (T + kPermTok - 1) / kPermTok;
   const int64_t nb = ntb + (C > 0 ? kPadBlocks : 0);
   hipLaunchKernelGGL(permute_kernel, dim3((unsigned)nb), dim3(256), 0, s,
                      (const uint4*)x, assign_row, counts, T, nv, E, k, C, ntb,
-                     (uint4*)x_perm, row_token);
+                     (uint4*)x_perm, pv, row_token);
   return hipGetLastError();
 }
 
