@@ -17,8 +17,10 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -57,6 +59,38 @@ def permute_bytes(T: int, h: int, rows: int, esz: int) -> int:
 def combine_bytes(kept_rows: int, T: int, h: int, esz: int, shared: bool) -> int:
     """Read every kept expert-output row (and the shared rows), write y."""
     return (kept_rows + T + (T if shared else 0)) * h * esz
+
+
+# ------------------------------------------------------------ HBM traffic
+GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_25_amd", "csrc", "grouped_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_swiglu_worked_example_traffic.txt")
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of GEMM 1 from the committed counter summary, or
+    None when the summary is missing, is for another workload, or was taken
+    on a different version of the kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            m = re.match(r"^([a-z_0-9]+):\s*(\S+)", line)
+            if m:
+                kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_source_sha256_16") != source_hash(GEMM_SOURCE):
+        return None
+    if kv.get("workload") != workload.split(":")[0]:
+        return None
+    try:
+        return int(kv["gemm1_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 # --------------------------------------------------------------------- bench
@@ -104,6 +138,9 @@ def main() -> int:
     ap.add_argument("--config", default="worked_example")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this size before the timed steps "
+                         "(reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the layer "
@@ -134,6 +171,14 @@ def main() -> int:
     for _ in range(args.warmup):
         moe.moe_forward(c, weights, inp["x"], y, route, ws)
     torch.cuda.synchronize()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_EVENTS)]
@@ -184,7 +229,8 @@ def main() -> int:
         "roofline": {"bound": "mfma" if cfg.dtype == "bf16" else "alu",
                      "kernel": "gemm1_swiglu",
                      "achieved": round(g1, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(g1 / peak, 4), "traffic": None},
+                     "frac": round(g1 / peak, 4),
+                     "traffic": measured_traffic(_workload_name(cfg, C))},
         "grouped_gemm": {"tflops": round(gg, 1), "frac_of_peak": round(gg / peak, 4),
                          "gemm1_tflops": round(g1, 1), "gemm2_tflops": round(g2, 1)},
         "permute": {"gbs": round(perm_gbs, 1), "frac_hbm": round(perm_gbs / PEAK_HBM_GBS, 4),
