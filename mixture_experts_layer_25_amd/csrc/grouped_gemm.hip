@@ -76,18 +76,11 @@ struct Tile {
   int64_t a_row, o_row;
 };
 
-__device__ __forceinline__ bool map_tile(const GroupedGemmArgs& a, int NT,
-                                         int64_t b, bool xcd_remap, int BMx,
-                                         Tile& t) {
+// Tile of logical index L (row tile fastest within (group, column tile)).
+__device__ __forceinline__ Tile tile_of(const GroupedGemmArgs& a, int NT, int64_t L, int BMx) {
   const int G = a.G;
   const int32_t* gt = a.gtab;
-  const int64_t V = (int64_t)gt[G] * NT;
-  if (b >= V) return false;
-  int64_t L = b;
-  if (xcd_remap) {
-    const int64_t x = b & 7, q = V >> 3, r = V & 7;
-    L = x * q + (x < r ? x : r) + (b >> 3);
-  }
+  Tile t;
   const int g = find_group(gt, G, L, NT);
   const int me = gt[g + 1] - gt[g];
   const int64_t local = L - (int64_t)gt[g] * NT;
@@ -98,7 +91,58 @@ __device__ __forceinline__ bool map_tile(const GroupedGemmArgs& a, int NT,
   t.m_valid = min(BMx, valid - t.mt * BMx);
   t.o_row = (int64_t)gt[3 * G + 1 + g] + (int64_t)t.mt * BMx;
   t.a_row = a.a_from_out_rows ? t.o_row : (int64_t)gt[G + 1 + g] + (int64_t)t.mt * BMx;
-  return true;
+  return t;
+}
+
+// Logical index of the tile workgroup b computes when every tile is whole
+// (fp32 kernel), or -1.
+__device__ __forceinline__ int64_t plain_tile(const GroupedGemmArgs& a, int NT, int64_t b) {
+  const int64_t V = (int64_t)a.gtab[a.G] * NT;
+  return b < V ? b : -1;
+}
+
+// Work of a bf16 workgroup.  With V tiles on P compute units the first
+// V - r tiles (r = V mod P) run whole, in rounds of P; if r > 0 the last r
+// tiles would leave most units idle in a final round, so each is split
+// along K into s = min(P / r, nk / 8) parts (when s >= 2), computed by r*s
+// workgroups that write fp32 partial tiles; a reduce kernel sums them.
+// Whole tiles: workgroup b runs on XCD b % 8, and consecutive logical tiles
+// are handed to the same XCD so that they share its L2.
+struct Work {
+  int64_t L;        // logical tile, -1: nothing to do
+  int part, parts;  // K part of a split tile (parts == 1: whole tile)
+  int64_t slot;     // split tiles: index among the split tiles
+};
+
+__device__ __forceinline__ void split_shape(const GroupedGemmArgs& a, int NT, int nk,
+                                            int64_t& V, int64_t& whole, int& s) {
+  V = (int64_t)a.gtab[a.G] * NT;
+  const int64_t P = a.num_cu > 0 ? a.num_cu : 1;
+  const int64_t r = V % P;
+  s = 1;
+  if (r > 0 && a.partials) {
+    const int64_t byu = P / r, byk = nk / 8;
+    s = (int)min(min(byu, byk), (int64_t)16);
+  }
+  whole = s >= 2 ? V - r : V;
+}
+
+__device__ __forceinline__ Work plan_work(const GroupedGemmArgs& a, int NT, int nk, int64_t b) {
+  int64_t V, whole;
+  int s;
+  split_shape(a, NT, nk, V, whole, s);
+  Work wk{-1, 0, 1, 0};
+  if (b < whole) {
+    const int64_t x = b & 7, q = whole >> 3, r8 = whole & 7;
+    wk.L = x * q + (x < r8 ? x : r8) + (b >> 3);
+  } else if (s >= 2 && b < whole + (V - whole) * s) {
+    const int64_t qd = b - whole;
+    wk.slot = qd / s;
+    wk.L = whole + wk.slot;
+    wk.part = (int)(qd - wk.slot * s);
+    wk.parts = s;
+  }
+  return wk;
 }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -115,13 +159,58 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+// Epilogue of a 256x256 tile.  32x32 accumulator layout: lane l holds
+// column (l & 31); register r of a fragment is row 8*(r/4) + 4*(l/32) + r%4.
+// GEMM 1 writes silu(a1) * a3 (w1 fragments j = 0, 1 pair with the w3
+// fragments j + 2 of the same columns); GEMM 2 writes the product.
+template <bool SWIGLU>
+__device__ __forceinline__ void store_tile(const floatx16 (&acc)[4][4], const Tile& tl, int lane,
+                                           int wm, int wn, uint16_t* out, int ldo, int N) {
+  const int col_l = lane & 31;
+  const int row_l = 4 * (lane >> 5);
+  if (SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = (int64_t)tl.nt * 128 + wn * 64 + j * 32 + col_l;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 128 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
+          if (row < tl.m_valid) {
+            const float z = acc[i][j][r];
+            const float v = z / (1.f + __expf(-z)) * acc[i][j + 2][r];
+            out[(tl.o_row + row) * ldo + col] = f32_to_bf16_bits(v);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = (int64_t)tl.nt * BN + wn * 128 + j * 32 + col_l;
+        if (col < N) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm * 128 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
+            if (row < tl.m_valid)
+              out[(tl.o_row + row) * ldo + col] = f32_to_bf16_bits(acc[i][j][r]);
+          }
+        }
+      }
+  }
+}
+
 template <bool SWIGLU>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];   // 160 KiB
 
   const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
-  Tile tl;
-  if (!map_tile(a, NT, blockIdx.x, true, BM, tl)) return;
+  const int nk = a.K / BK;
+  const Work wk = plan_work(a, NT, nk, blockIdx.x);
+  if (wk.L < 0) return;
+  Tile tl = tile_of(a, NT, wk.L, BM);
   // Tile fields and the wave index are wave-uniform; saying so keeps the
   // buffer descriptors below in scalar registers.
   tl.g = __builtin_amdgcn_readfirstlane(tl.g);
@@ -131,6 +220,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
              (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.a_row);
   tl.o_row = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tl.o_row >> 32)) << 32) |
              (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.o_row);
+  const int part = __builtin_amdgcn_readfirstlane(wk.part);
+  const int parts = __builtin_amdgcn_readfirstlane(wk.parts);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -148,8 +239,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
     B0 += (int64_t)tl.g * a.b_stride;
     if (SWIGLU) B1 += (int64_t)tl.g * a.b_stride;
   }
-  const int nk = K / BK;   // even: K % 128 == 0
-  const int krot = (a.rotate_k && !shared) ? (int)(((int64_t)tl.g * nk / 8) % nk) : 0;
+  // K slices [kbeg, kbeg + nsteps); a whole tile of a routed group starts
+  // at slice g*nk/8 and wraps around
+  const int kbeg = (int)((int64_t)part * nk / parts);
+  const int nsteps = (int)((int64_t)(part + 1) * nk / parts) - kbeg;
+  const int krot = (parts == 1 && a.rotate_k && !shared) ? (int)(((int64_t)tl.g * nk / 8) % nk) : 0;
 
   // Global -> LDS copies: wave w fills rows w*64 .. w*64+63 of the A and the
   // B slice, 8 rows (1 KiB) per instruction; lane l lands at byte 16*l of
@@ -209,16 +303,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
 #define RDB(F, SBP, S, J) F[J] = lds_frag((SBP) + rB + (J) * 4096 + cx[S][(J) & 1])
 // K slice of step KT (rotated); past the end the offset leaves the buffer
 // and the copy returns zeros
-#define KSL(KT) ((KT) + krot >= nk ? (KT) + krot - nk : (KT) + krot)
-#define KOFF(KT) ((KT) < nk ? (uint32_t)KSL(KT) * (BK * 2) : 0x7FFFFFF0u)
+#define KSL(KT) (kbeg + ((KT) + krot >= nsteps ? (KT) + krot - nsteps : (KT) + krot))
+#define KOFF(KT) ((KT) < nsteps ? (uint32_t)KSL(KT) * (BK * 2) : 0x7FFFFFF0u)
 #define DMA_A(KT, I)                                                                          \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                   \
       rsA, LDS_AS(dstA + ((KT) % kSlotsA) * kPart + (I) * 1024), 16, voffA[I],                \
-      (KT) < nk ? (uint32_t)(I) * 8u * arowbytes + KOFF(KT) : KOFF(KT), 0, 0)
+      (KT) < nsteps ? (uint32_t)(I) * 8u * arowbytes + KOFF(KT) : KOFF(KT), 0, 0)
 #define DMA_B(KT, I)                                                                          \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                   \
       rsB, LDS_AS(dstB + ((KT) & 1) * kPart + (I) * 1024), 16, voffB[I],                      \
-      (KT) < nk ? (uint32_t)(I) * 8u * browbytes + KOFF(KT) : KOFF(KT), 0, 0)
+      (KT) < nsteps ? (uint32_t)(I) * 8u * browbytes + KOFF(KT) : KOFF(KT), 0, 0)
 // one sub-step: 8 groups of [copy] [fragment read] [2 MFMAs]
 #define SUBSTEP(FA, FB, RFA, RFB, SA, SBP, S, COPY)                                   \
   COPY(0); RDA(RFA, SA, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                \
@@ -261,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
   //       all of B(kt+2) and then all of A(kt+3) into slice kt's slots.
   //       Copies complete in issue order, so "at most 8 copies in flight"
   //       at the next barrier means everything up to B(kt+2) has landed.
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt < nsteps; ++kt) {
     const uint8_t* sa = smem + (kt % kSlotsA) * kPart;
     const uint8_t* sbb = smem + kOffB + (kt & 1) * kPart;
     const uint8_t* na = smem + ((kt + 1) % kSlotsA) * kPart;
@@ -293,43 +387,56 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
 #undef DMA_B
 #undef SUBSTEP
 
-  // 32x32 accumulator layout: lane l holds column (l & 31); register r of a
-  // fragment is row 8*(r/4) + 4*(l/32) + r%4.
-  uint16_t* out = (uint16_t*)a.out;
-  const int col_l = lane & 31;
-  const int row_l = 4 * (lane >> 5);
-  if (SWIGLU) {
+  if (parts > 1) {
+    // split tile: fp32 partial in register order, 1 KiB per store instruction
+    float* P = a.partials + (wk.slot * parts + part) * (int64_t)(256 * 256);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t col = (int64_t)tl.nt * 128 + wn * 64 + j * 32 + col_l;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-          if (row < tl.m_valid) {
-            const float z = acc[i][j][r];
-            const float v = z / (1.f + __expf(-z)) * acc[i][j + 2][r];
-            out[(tl.o_row + row) * ldo + col] = f32_to_bf16_bits(v);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int c = (i * 4 + j) * 4 + q;
+          *reinterpret_cast<floatx4*>(P + ((int64_t)(w * 64 + c) * 64 + lane) * 4) =
+              floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = (int64_t)tl.nt * BN + wn * 128 + j * 32 + col_l;
-        if (col < N) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = wm * 128 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-            if (row < tl.m_valid)
-              out[(tl.o_row + row) * ldo + col] = f32_to_bf16_bits(acc[i][j][r]);
-          }
-        }
-      }
+    return;
   }
+  store_tile<SWIGLU>(acc, tl, lane, wm, wn, (uint16_t*)a.out, ldo, N);
+}
+
+// Sums the K parts of the split tiles (in part order) and stores them like
+// the GEMM kernel does.  Workgroup b handles split tile b.
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void gemm_bf16_reduce_kernel(GroupedGemmArgs a) {
+  const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
+  const int nk = a.K / BK;
+  int64_t V, whole;
+  int s;
+  split_shape(a, NT, nk, V, whole, s);
+  const int64_t slot = blockIdx.x;
+  if (s < 2 || whole + slot >= V) return;
+  const Tile tl = tile_of(a, NT, whole + slot, BM);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = (i * 4 + j) * 4 + q;
+        floatx4 sum = {0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < s; ++p) {
+          const float* P = a.partials + (slot * s + p) * (int64_t)(256 * 256);
+          sum += *reinterpret_cast<const floatx4*>(P + ((int64_t)(w * 64 + c) * 64 + lane) * 4);
+        }
+        acc[i][j][4 * q] = sum[0];
+        acc[i][j][4 * q + 1] = sum[1];
+        acc[i][j][4 * q + 2] = sum[2];
+        acc[i][j][4 * q + 3] = sum[3];
+      }
+  store_tile<SWIGLU>(acc, tl, lane, w >> 1, w & 1, (uint16_t*)a.out, a.ldo, a.N);
 }
 
 // fp32 layers: 64x64 tiles, BK = 16, fp32 FMA, each thread 4 rows x 4
@@ -343,8 +450,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GroupedGemmArgs a) {
   __shared__ float B3s[SWIGLU ? FBK : 1][FBN + 4];
 
   const int NT = a.N / FBN;
-  Tile tl;
-  if (!map_tile(a, NT, blockIdx.x, false, FBM, tl)) return;
+  const int64_t L = plain_tile(a, NT, blockIdx.x);
+  if (L < 0) return;
+  const Tile tl = tile_of(a, NT, L, FBM);
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int K = a.K, N = a.N;
   const bool shared = tl.g >= a.E_routed;
@@ -423,12 +531,22 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, const GroupedGemmArgs& a,
                                hipStream_t s) {
   if (dtype == 1) {
     const int NT = swiglu ? a.N / 128 : (a.N + BN - 1) / BN;
-    const int64_t nb = a.max_m_tiles * NT;
+    // whole tiles plus at most num_cu split-part workgroups
+    const int64_t nb = a.max_m_tiles * NT + (a.partials ? a.num_cu : 0);
     if (nb <= 0) return hipSuccess;
     if (swiglu)
       hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, a);
+    if (a.partials) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      // one workgroup per possible split tile (fewer than num_cu)
+      if (swiglu)
+        hipLaunchKernelGGL(gemm_bf16_reduce_kernel<true>, dim3((unsigned)a.num_cu), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL(gemm_bf16_reduce_kernel<false>, dim3((unsigned)a.num_cu), dim3(256), 0, s, a);
+    }
   } else {
     const int NT = a.N / FBN;
     const int64_t nb = a.max_m_tiles * NT;

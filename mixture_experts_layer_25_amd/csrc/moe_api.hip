@@ -56,7 +56,7 @@ int check_cfg(const moe_cfg_t* c) {
 
 struct Layout {
   size_t logits, idx, gate, hist, base, counts, offsets, assign, rowtok, gtab;
-  size_t xperm, act, yperm, total;
+  size_t partials, xperm, act, yperm, total;
 };
 
 Layout layout_of(const moe_cfg_t& c) {
@@ -83,6 +83,7 @@ Layout layout_of(const moe_cfg_t& c) {
   L.assign = take((size_t)(T * k) * 4);
   L.rowtok = take((size_t)rows * 4);
   L.gtab = take((size_t)gtab_ints((int)G) * 4);
+  L.partials = take(c.dtype == MOE_DTYPE_BF16 ? (size_t)moe::kSplitPartialFloats * 4 : 0);
   L.xperm = take((size_t)rows * ld_h(c) * es);
   L.act = take((size_t)rows_all * ld_f(c) * es);
   L.yperm = take((size_t)rows_all * ld_h(c) * es);
@@ -108,6 +109,21 @@ int check_ws(const moe_cfg_t& c, void* ws, size_t ws_bytes) {
 
 int64_t max_m_tiles(int64_t rows, int64_t groups, int BM) {
   return (rows + BM - 1) / BM + groups;
+}
+
+// Compute units of the current device (at most 256: the split-K partial
+// buffer holds 256 parts).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  return n < 256 ? n : 256;
+}
+
+void set_split(moe::GroupedGemmArgs& a, const moe_cfg_t& c, void* ws, const Layout& L) {
+  a.num_cu = device_cus();
+  a.partials = c.dtype == MOE_DTYPE_BF16 ? at<float>(ws, L.partials) : nullptr;
 }
 
 }  // namespace
@@ -232,6 +248,7 @@ MOE_API int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
   a.E_routed = c.E;
   a.a_from_out_rows = 0;
   a.max_m_tiles = max_m_tiles(rows, c.E, BM);
+  set_split(a, c, ws, L);
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, true, a, s));
   a.A = act;
   a.B0 = w2;
@@ -330,6 +347,7 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   a.E_routed = c.E;
   a.a_from_out_rows = 0;
   a.max_m_tiles = max_m_tiles(rows, c.E, BM) + (c.has_shared ? (c.T + BM - 1) / BM : 0);
+  set_split(a, c, ws, L);
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, true, a, s));
   MOE_TRY(mark(6));
   a.A = act;

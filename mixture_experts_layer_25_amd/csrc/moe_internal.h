@@ -14,6 +14,11 @@ namespace moe {
 //   [3G+1 .. 4G]    first output row of each group
 inline int64_t gtab_ints(int G) { return 4 * (int64_t)G + 1; }
 
+// Tiles of the last, partial round of a bf16 grouped GEMM are split along K
+// into up to num_cu/r parts whose fp32 partial tiles go to this many floats
+// of workspace (num_cu <= 256 parts of 256x256).
+constexpr int64_t kSplitPartialFloats = (int64_t)256 * 256 * 256;
+
 struct GroupedGemmArgs {
   const void* A;         // routed-group rows: x_perm (GEMM1) or act (GEMM2)
   const void* A_shared;  // GEMM1: the tokens x for the shared group; else unused
@@ -29,6 +34,8 @@ struct GroupedGemmArgs {
   int lda_shared;        // row stride of A_shared
   int ldo;               // row stride of out
   int rotate_k;          // 1: routed group g starts its K loop at slice g*nk/8
+  int num_cu;            // compute units of the device (tile rounds)
+  float* partials;       // split-K partial tiles, kSplitPartialFloats floats
   const int32_t* gtab;
   int G;                 // groups in gtab
   int E_routed;          // groups 0..E_routed-1 use B0/B1, group E_routed B0s/B1s

@@ -42,6 +42,11 @@ MEDIUM = [
     MoEConfig("k_equals_e", T=257, h=128, E=4, k=4, F=128),
     MoEConfig("one_token", T=1, h=128, E=8, k=2, F=128, cf=(5, 4)),
     MoEConfig("e1024_k16", T=70, h=128, E=1024, k=16, F=128, gate="softmax_all_topk"),
+    # K long enough (>= 16 slices of 64) that the tiles of the last partial
+    # round are split along K and reduced (GEMM 1 and GEMM 2)
+    MoEConfig("split_k_tail", T=600, h=1024, E=4, k=2, F=1024, gate="softmax_topk"),
+    MoEConfig("split_k_tail_capacity_shared", T=500, h=1024, E=4, k=2, F=1024,
+              gate="sigmoid_topk_norm", cf=(1, 1), shared=True),
     MoEConfig("f32_capacity", T=300, h=256, E=8, k=2, F=256, dtype="f32",
               gate="softmax_all_topk", cf=(1, 1)),
     MoEConfig("f32_sigmoid_shared", T=200, h=128, E=16, k=4, F=256, dtype="f32",
@@ -71,7 +76,7 @@ def test_forward_matches_oracle(cfg):
     assert err <= tol_of(cfg)
 
 
-STAGED = ["dropless_softmax", "capacity_heavy_drop", "sigmoid_bias_shared",
+STAGED = ["dropless_softmax", "capacity_heavy_drop", "sigmoid_bias_shared", "split_k_tail",
           "f32_capacity", "f32_sigmoid_shared"]
 
 
