@@ -20,7 +20,8 @@
  *   Memory    All tensor pointers are DEVICE pointers owned by the caller.
  *             The library never allocates or frees device memory; scratch
  *             comes from a caller workspace of moe_workspace_bytes() bytes.
- *             Pointers must be 16-byte aligned.  Tensors are dense,
+ *             Pointers must be 16-byte aligned (else MOE_ERR_INVALID_ARG,
+ *             before any device work).  Tensors are dense,
  *             row-major, with the last dimension contiguous.
  *   Weights   Stored [out, in] (torch Linear layout): w_router [E,h],
  *             w1/w3 [E,F,h], w2 [E,h,F].  The page's router weight [h,E]

@@ -16,12 +16,12 @@
 // K advances in slices of 64 (128-byte rows, whole cache lines per row).
 // Slices are copied global -> LDS directly (buffer_load_dwordx4 ... lds, no
 // registers in between) into a ring of three A slots and two B slots of
-// 32 KiB each (all 160 KiB of LDS), A two slices and B one slice ahead of the
-// MFMAs; buffer bounds return zeros for rows past a ragged group's end.  The
+// 32 KiB each (all 160 KiB of LDS), A up to two slices and B one slice ahead
+// of the MFMAs; buffer bounds return zeros for rows past a ragged group's end.  The
 // instruction order is fixed by hand: every MFMA pair is accompanied by one
-// LDS fragment read for the next sub-step and, after the barrier, by the
-// copies of the next slices, so the wave never stalls on a burst of memory
-// instructions.  Routed group g starts its K loop at slice g*nk/8: groups
+// LDS fragment read for the next sub-step, and the copies of the next slices
+// are spread over the step (one or two per MFMA pair), so the wave never
+// stalls on a burst of memory instructions.  Routed group g starts its K loop at slice g*nk/8: groups
 // run on different XCDs, and staggered K offsets spread their weight reads
 // over the memory channels (the row strides are powers of two).
 //
@@ -159,46 +159,59 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Epilogue of a 256x256 tile.  32x32 accumulator layout: lane l holds
-// column (l & 31); register r of a fragment is row 8*(r/4) + 4*(l/32) + r%4.
-// GEMM 1 writes silu(a1) * a3 (w1 fragments j = 0, 1 pair with the w3
-// fragments j + 2 of the same columns); GEMM 2 writes the product.
+// Epilogue of a 256x256 tile.  The MFMAs take the weight fragment first, so
+// fragment (i, j) holds C^T: lane l has output row (l & 31) of row block i
+// and, in registers 4b..4b+3, the 4 consecutive columns 8b + 4*(l >> 5) + 0..3
+// of column block j.  Lanes l and l ^ 32 (same row) trade one 4-column run
+// so that each ends up with 8 consecutive columns: 16-byte stores, the two
+// lanes of a row writing 32 contiguous bytes.  GEMM 1 writes silu(a1) * a3
+// (w1 blocks j = 0, 1 pair with the w3 blocks j + 2 of the same columns);
+// GEMM 2 writes the product.
 template <bool SWIGLU>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[4][4], const Tile& tl, int lane,
                                            int wm, int wn, uint16_t* out, int ldo, int N) {
-  const int col_l = lane & 31;
-  const int row_l = 4 * (lane >> 5);
-  if (SWIGLU) {
+  const int hi = lane >> 5;
+  constexpr int NJ = SWIGLU ? 2 : 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int row = wm * 128 + i * 32 + (lane & 31);
+    const bool ok = row < tl.m_valid;
+    uint16_t* orow = out + (tl.o_row + row) * (int64_t)ldo;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t col = (int64_t)tl.nt * 128 + wn * 64 + j * 32 + col_l;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t col0 = SWIGLU ? (int64_t)tl.nt * 128 + wn * 64 + j * 32
+                                  : (int64_t)tl.nt * BN + wn * 128 + j * 32;
+      if (!SWIGLU && col0 >= N) continue;
+      uint32_t q[4][2];   // run b as two bf16 pairs
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-          if (row < tl.m_valid) {
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          float v[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 4 * b + 2 * p + e;
             const float z = acc[i][j][r];
-            const float v = z / (1.f + __expf(-z)) * acc[i][j + 2][r];
-            out[(tl.o_row + row) * ldo + col] = f32_to_bf16_bits(v);
+            v[e] = SWIGLU ? z / (1.f + __expf(-z)) * acc[i][j + 2][r] : z;
           }
+          q[b][p] = pack_bf16x2(v[0], v[1]);
         }
-      }
-  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int c = 0; c < 2; ++c) {
+        // the low lane keeps run 2c and receives the high lane's run 2c;
+        // the high lane keeps run 2c+1 and receives the low lane's run 2c+1
+        uint32_t keep[2], give[2], got[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = (int64_t)tl.nt * BN + wn * 128 + j * 32 + col_l;
-        if (col < N) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = wm * 128 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-            if (row < tl.m_valid)
-              out[(tl.o_row + row) * ldo + col] = f32_to_bf16_bits(acc[i][j][r]);
-          }
+        for (int p = 0; p < 2; ++p) {
+          keep[p] = hi ? q[2 * c + 1][p] : q[2 * c][p];
+          give[p] = hi ? q[2 * c][p] : q[2 * c + 1][p];
+          got[p] = (uint32_t)__shfl_xor((int)give[p], 32, 64);
         }
+        const uint4 v = hi ? uint4{got[0], got[1], keep[0], keep[1]}
+                           : uint4{keep[0], keep[1], got[0], got[1]};
+        if (ok) *reinterpret_cast<uint4*>(orow + col0 + 16 * c + 8 * hi) = v;
       }
+    }
   }
 }
 
@@ -297,8 +310,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
   bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
 
 #define SB() __builtin_amdgcn_sched_barrier(0)
+// weight fragment as the MFMA's first operand: the accumulator holds C^T,
+// so each lane ends up with runs of 4 consecutive output columns of one row
 #define MF(FA, FB, I, J) \
-  acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[I], FB[J], acc[I][J], 0, 0, 0)
+  acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[J], FA[I], acc[I][J], 0, 0, 0)
 #define RDA(F, SA, S, I) F[I] = lds_frag((SA) + rA + (I) * 4096 + cx[S][(I) & 1])
 #define RDB(F, SBP, S, J) F[J] = lds_frag((SBP) + rB + (J) * 4096 + cx[S][(J) & 1])
 // K slice of step KT (rotated); past the end the offset leaves the buffer
@@ -325,9 +340,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
   COPY(7); RDB(RFB, SBP, S, 3); MF(FA, FB, 3, 2); MF(FA, FB, 3, 3); SB()
 
   // s_waitcnt immediates (gfx9 encoding; expcnt and lgkmcnt left at "no wait")
-  constexpr int kWaitVm0 = 0x0F70, kWaitVm8 = 0x0F78, kWaitVm24 = 0x4F78;
+  constexpr int kWaitVm0 = 0x0F70, kWaitVm8 = 0x0F78, kWaitVm16 = 0x4F70;
 
-  // Prologue: A(0), B(0), A(1), B(1), A(2) in flight; wait for slice 0.
+  // Prologue: A(0), B(0), A(1), B(1) in flight; wait for slice 0.
 #pragma unroll
   for (int i = 0; i < 8; ++i) DMA_A(0, i);
 #pragma unroll
@@ -336,9 +351,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
   for (int i = 0; i < 8; ++i) DMA_A(1, i);
 #pragma unroll
   for (int i = 0; i < 8; ++i) DMA_B(1, i);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) DMA_A(2, i);
-  __builtin_amdgcn_s_waitcnt(kWaitVm24);
+  __builtin_amdgcn_s_waitcnt(kWaitVm16);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) RDA(fa0, smem, 0, i);
@@ -347,34 +360,39 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
 
   // Step kt (slice kt in A slot kt%3, B slot kt%2; sub-step 0 fragments
   // already in registers):
-  //   s0..s2: MFMAs of sub-steps 0..2, reads of sub-steps 1..3
+  //   s0..s2: MFMAs of sub-steps 0..2, reads of sub-steps 1..3, and the 8
+  //       copies of A(kt+2) spread over them (its slot held slice kt-1,
+  //       retired at the previous barrier);
   //   wait until at most 8 copies (A(kt+2)'s) may be in flight -> A(kt+1),
   //   B(kt+1) landed;
   //   barrier: slice kt+1 visible to all, slice kt's slots free
-  //   s3: MFMAs of sub-step 3, reads of slice kt+1 sub-step 0, copies of
-  //       all of B(kt+2) and then all of A(kt+3) into slice kt's slots.
-  //       Copies complete in issue order, so "at most 8 copies in flight"
-  //       at the next barrier means everything up to B(kt+2) has landed.
+  //   s3: MFMAs of sub-step 3, reads of slice kt+1 sub-step 0, the 8 copies
+  //       of B(kt+2) into slice kt's B slot.
+  //   Copies complete in issue order, so "at most 8 copies in flight" at
+  //   the next barrier means everything up to B(kt+2) has landed.  Keeping
+  //   the copies apart keeps the address unit from backing up the waves'
+  //   in-order issue (and with it the MFMAs).
   for (int kt = 0; kt < nsteps; ++kt) {
     const uint8_t* sa = smem + (kt % kSlotsA) * kPart;
     const uint8_t* sbb = smem + kOffB + (kt & 1) * kPart;
     const uint8_t* na = smem + ((kt + 1) % kSlotsA) * kPart;
     const uint8_t* nbb = smem + kOffB + ((kt + 1) & 1) * kPart;
-#define COPY_NONE(I)
-#define COPY_BA(I)                                   \
-  if ((I) < 4) {                                     \
-    DMA_B(kt + 2, 2 * (I)); DMA_B(kt + 2, 2 * (I) + 1); \
-  } else {                                           \
-    DMA_A(kt + 3, 2 * (I) - 8); DMA_A(kt + 3, 2 * (I) - 7); \
-  }
-    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 1, COPY_NONE);
-    SUBSTEP(fa1, fb1, fa0, fb0, sa, sbb, 2, COPY_NONE);
-    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 3, COPY_NONE);
+// A(kt+2) blocks 0-2, 3-5 and 6-7 in sub-steps 1, 2 and 3; B(kt+2) one
+// block per MFMA pair after the barrier
+#define COPY_A1(I) if ((I) == 1 || (I) == 4 || (I) == 7) DMA_A(kt + 2, (I) / 3);
+#define COPY_A2(I) if ((I) == 1 || (I) == 4 || (I) == 7) DMA_A(kt + 2, 3 + (I) / 3);
+#define COPY_A3(I) if ((I) == 2 || (I) == 6) DMA_A(kt + 2, 6 + (I) / 4);
+#define COPY_B(I) DMA_B(kt + 2, (I));
+    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 1, COPY_A1);
+    SUBSTEP(fa1, fb1, fa0, fb0, sa, sbb, 2, COPY_A2);
+    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 3, COPY_A3);
     __builtin_amdgcn_s_waitcnt(kWaitVm8);
     __syncthreads();
-    SUBSTEP(fa1, fb1, fa0, fb0, na, nbb, 0, COPY_BA);
-#undef COPY_NONE
-#undef COPY_BA
+    SUBSTEP(fa1, fb1, fa0, fb0, na, nbb, 0, COPY_B);
+#undef COPY_A1
+#undef COPY_A2
+#undef COPY_A3
+#undef COPY_B
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #undef SB

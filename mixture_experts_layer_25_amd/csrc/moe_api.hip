@@ -62,7 +62,9 @@ struct Layout {
 Layout layout_of(const moe_cfg_t& c) {
   Layout L{};
   const int64_t T = c.T, E = c.E, k = c.k;
-  const int64_t nch = (T + moe::kChunkTokens - 1) / moe::kChunkTokens;
+  // histogram rows: one per top-k workgroup (the finest grouping used)
+  const int hg = moe::topk_tokens_per_wg(c.E);
+  const int64_t nch = (T + hg - 1) / hg;
   const int64_t rows = rows_of(c);
   const int64_t rows_all = rows + (c.has_shared ? T : 0);
   const int64_t G = E + c.has_shared;
@@ -100,6 +102,13 @@ int check_ws(const moe_cfg_t& c, void* ws, size_t ws_bytes) {
   const Layout L = layout_of(c);
   if (L.total > 0 && (ws == nullptr || ws_bytes < L.total)) return MOE_ERR_WORKSPACE;
   return MOE_OK;
+}
+
+// True if any non-null pointer breaks the 16-byte alignment every entry
+// point requires (the kernels move 16-byte vectors).
+template <typename... P>
+bool misaligned(const P*... p) {
+  return ((((uintptr_t)p & 15u) != 0) || ...);
 }
 
 #define MOE_TRY(expr)                                   \
@@ -176,6 +185,8 @@ MOE_API int moe_router_topk(const moe_cfg_t* cfg, const void* x, const void* w_r
   const moe_cfg_t& c = *cfg;
   if (c.T == 0) return MOE_OK;
   if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  if (misaligned(x, w_router, logit_bias, select_bias, logits, topk_idx, topk_gate, ws))
+    return MOE_ERR_INVALID_ARG;
   if (!logits && (st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
   float* lg = logits ? logits : at<float>(ws, layout_of(c).logits);
@@ -196,6 +207,8 @@ MOE_API int moe_permute(const moe_cfg_t* cfg, const void* x, const int32_t* topk
   if (!x || !topk_idx || !expert_counts || !expert_offsets || !assign_row || !row_token ||
       !x_perm)
     return MOE_ERR_INVALID_ARG;
+  if (misaligned(x, topk_idx, expert_counts, expert_offsets, assign_row, row_token, x_perm, ws))
+    return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
   const Layout L = layout_of(c);
@@ -205,8 +218,8 @@ MOE_API int moe_permute(const moe_cfg_t* cfg, const void* x, const int32_t* topk
   MOE_TRY(moe::launch_hist(topk_idx, c.T, c.E, c.k, hist, s));
   MOE_TRY(moe::launch_scan(hist, nch, c.E, c.capacity, c.T, c.k, 0, row_tile(c), base,
                            expert_counts, expert_offsets, at<int32_t>(ws, L.gtab), s));
-  MOE_TRY(moe::launch_assign(topk_idx, base, expert_offsets, c.T, c.E, c.k, c.capacity,
-                             assign_row, row_token, s));
+  MOE_TRY(moe::launch_assign(topk_idx, base, moe::kChunkTokens, expert_offsets, c.T, c.E,
+                             c.k, c.capacity, assign_row, row_token, s));
   MOE_TRY(moe::launch_permute(c.dtype, x, assign_row, expert_counts, c.T, c.h, c.E, c.k,
                               c.capacity, x_perm, c.h, row_token, s));
   return MOE_OK;
@@ -223,6 +236,8 @@ MOE_API int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
   const moe_cfg_t& c = *cfg;
   if (c.T == 0) return MOE_OK;
   if (!x_perm || !expert_counts || !expert_offsets || !w1 || !w3 || !w2 || !act || !y_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (misaligned(x_perm, expert_counts, expert_offsets, w1, w3, w2, act, y_perm, ws))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
@@ -271,6 +286,7 @@ MOE_API int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
   const moe_cfg_t& c = *cfg;
   if (c.T == 0) return MOE_OK;
   if (!y_perm || !assign_row || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
+  if (misaligned(y_perm, assign_row, topk_gate, shared_y, y)) return MOE_ERR_INVALID_ARG;
   MOE_TRY(moe::launch_combine(c.dtype, y_perm, c.h, assign_row, topk_gate, shared_y, y,
                               c.T, c.h, c.k, (hipStream_t)stream));
   return MOE_OK;
@@ -286,6 +302,12 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   if (!w || !x || !y || !w->w_router || !w->w1 || !w->w3 || !w->w2)
     return MOE_ERR_INVALID_ARG;
   if (c.has_shared && (!w->ws1 || !w->ws3 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+  if (misaligned(x, y, ws, w->w_router, w->w1, w->w3, w->w2, w->logit_bias, w->select_bias) ||
+      misaligned(w->ws1, w->ws3, w->ws2))
+    return MOE_ERR_INVALID_ARG;
+  if (route && misaligned(route->logits, route->topk_idx, route->topk_gate, route->expert_counts,
+                          route->expert_offsets, route->assign_row, route->row_token))
+    return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
   const Layout L = layout_of(c);
@@ -304,7 +326,8 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   void* xperm = at<char>(ws, L.xperm);
   void* act = at<char>(ws, L.act);
   void* yperm = at<char>(ws, L.yperm);
-  const int64_t nch = (c.T + moe::kChunkTokens - 1) / moe::kChunkTokens;
+  const int hg = moe::topk_tokens_per_wg(c.E);
+  const int64_t nch = (c.T + hg - 1) / hg;
   const int64_t rows = rows_of(c);
   const int BM = row_tile(c);
   auto mark = [&](int i) -> hipError_t {
@@ -321,7 +344,7 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   MOE_TRY(moe::launch_scan(hist, nch, c.E, c.capacity, c.T, c.k, c.has_shared, BM, base,
                            counts, offsets, gtab, s));
   MOE_TRY(mark(3));
-  MOE_TRY(moe::launch_assign(idx, base, offsets, c.T, c.E, c.k, c.capacity, assign,
+  MOE_TRY(moe::launch_assign(idx, base, hg, offsets, c.T, c.E, c.k, c.capacity, assign,
                              rowtok, s));
   MOE_TRY(mark(4));
   MOE_TRY(moe::launch_permute(c.dtype, x, assign, counts, c.T, c.h, c.E, c.k, c.capacity,

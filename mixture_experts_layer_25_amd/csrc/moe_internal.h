@@ -47,19 +47,28 @@ hipError_t launch_router(int dtype, const void* x, const void* w_router,
                          const float* logit_bias, float* logits, int64_t T,
                          int h, int E, hipStream_t s);
 
+// Tokens one top-k workgroup handles (4 passes of 256/G tokens, G = lanes
+// per token); its expert histogram covers that many tokens.  Always a
+// divisor of 256.
+inline int topk_tokens_per_wg(int E) {
+  const int G = E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64));
+  return 4 * 256 / G;
+}
+
 hipError_t launch_topk(const float* logits, const float* select_bias,
                        int gate, int64_t T, int E, int k, int32_t* idx,
-                       float* gate_out, int32_t* chunk_hist, hipStream_t s);
+                       float* gate_out, int32_t* hist, hipStream_t s);
 
 hipError_t launch_hist(const int32_t* idx, int64_t T, int E, int k,
                        int32_t* chunk_hist, hipStream_t s);
 
-hipError_t launch_scan(const int32_t* chunk_hist, int64_t nch, int E,
+// hist/base: one row of E counts per group of hg tokens (hg divides 256).
+hipError_t launch_scan(const int32_t* hist, int64_t ngroups, int E,
                        int64_t C, int64_t T, int k, int has_shared, int BM,
-                       int32_t* chunk_base, int32_t* counts, int32_t* offsets,
+                       int32_t* base, int32_t* counts, int32_t* offsets,
                        int32_t* gtab, hipStream_t s);
 
-hipError_t launch_assign(const int32_t* idx, const int32_t* chunk_base,
+hipError_t launch_assign(const int32_t* idx, const int32_t* base, int hg,
                          const int32_t* offsets, int64_t T, int E, int k,
                          int64_t C, int32_t* assign_row, int32_t* row_token,
                          hipStream_t s);

@@ -8,8 +8,9 @@
 //
 // rank(t,j) = number of tokens t' < t that chose the same expert.  Ranks
 // come from counts, never from the order atomics happen to run in:
-//   hist    per chunk of 256 tokens, assignments per expert (order-free
-//           LDS counts; fused into the top-k kernel on the fused path)
+//   hist    per group of tokens (256 here; the top-k workgroup's tokens
+//           on the fused path, where the top-k kernel writes it), the
+//           assignments per expert as order-free LDS counts
 //   scan    one workgroup: per-expert exclusive prefix over chunks, the
 //           counts, group offsets, and the grouped-GEMM tile table
 //   assign  per chunk: per-wave counts, then within a wave the lanes below
@@ -84,22 +85,51 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   for (int e = threadIdx.x; e < E; e += 256) chunk_hist[blockIdx.x * (int64_t)E + e] = hist[e];
 }
 
-// One workgroup of 1024 threads.
+// One workgroup of 1024 threads; hist has one row of E counts per group of
+// tokens (nch groups, in token order).  Thread (sl, e) = (tid / E, tid % E)
+// owns the sl-th of S contiguous slices of the groups of expert e: it sums
+// its slice, the slice totals are scanned in LDS, and it writes the bases
+// of its groups from its slice's prefix.
 __global__ __launch_bounds__(1024) void scan_kernel(
     const int32_t* __restrict__ chunk_hist, int64_t nch, int E, int64_t C,
     int64_t T, int k, int has_shared, int BM, int32_t* __restrict__ chunk_base,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ gtab) {
   __shared__ int tmp[32];
-  const int e = threadIdx.x;
-  int cnt = 0;
-  if (e < E) {
-    for (int64_t c = 0; c < nch; ++c) {
-      chunk_base[c * E + e] = cnt;
-      cnt += chunk_hist[c * E + e];
+  __shared__ int slice_sum[1024];
+  int S = 1;
+  while (2 * S * E <= 1024) S *= 2;
+  const int tid = threadIdx.x;
+  const int sl = tid / E, es = tid % E;
+  const int64_t L = (nch + S - 1) / S;
+  const int64_t g0 = sl * L, g1 = min(nch, g0 + L);
+  if (sl < S) {
+    int sum = 0;
+    int64_t c = g0;
+    for (; c + 8 <= g1; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = chunk_hist[(c + i) * E + es];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += v[i];
     }
-    counts[e] = cnt;
+    for (; c < g1; ++c) sum += chunk_hist[c * E + es];
+    slice_sum[tid] = sum;
   }
+  __syncthreads();
+  if (sl < S) {
+    int run = 0;
+    for (int q = 0; q < sl; ++q) run += slice_sum[q * E + es];
+    for (int64_t c = g0; c < g1; ++c) {
+      chunk_base[c * E + es] = run;
+      run += chunk_hist[c * E + es];
+    }
+  }
+  const int e = tid;
+  int cnt = 0;
+  if (e < E)
+    for (int q = 0; q < S; ++q) cnt += slice_sum[q * E + e];
+  if (e < E) counts[e] = cnt;
   int rows_routed;
   int off;
   if (C == 0) {
@@ -144,9 +174,11 @@ __global__ __launch_bounds__(1024) void gtab_kernel(const int32_t* __restrict__ 
 }
 
 // One workgroup (4 waves) per chunk of 256 tokens; lane = token.
+// chunk_base rows are per group of hg tokens; chunk c starts at group
+// c * 256 / hg.
 template <int KMAX>
 __global__ __launch_bounds__(256) void assign_kernel(
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ chunk_base, int gpc,
     const int32_t* __restrict__ offsets, int64_t T, int E, int k, int nbits,
     int64_t C, int32_t* __restrict__ assign_row, int32_t* __restrict__ row_token) {
   __shared__ int32_t cnt[4][1024];
@@ -174,7 +206,7 @@ __global__ __launch_bounds__(256) void assign_kernel(
   __syncthreads();
   // wave bases: chunk base of the expert plus the counts of earlier waves
   for (int e = tid; e < E; e += 256) {
-    int run = chunk_base[chunk * E + e];
+    int run = chunk_base[chunk * gpc * E + e];
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
       const int c = cnt[ww][e];
@@ -231,12 +263,12 @@ __global__ __launch_bounds__(256) void assign_kernel(
 }
 
 template <int KMAX>
-void launch_assign_t(const int32_t* idx, const int32_t* base, const int32_t* off,
+void launch_assign_t(const int32_t* idx, const int32_t* base, int gpc, const int32_t* off,
                      int64_t T, int E, int k, int nbits, int64_t C, int32_t* ar,
                      int32_t* rt, hipStream_t s) {
   const int64_t nch = (T + kChunkTokens - 1) / kChunkTokens;
   hipLaunchKernelGGL((assign_kernel<KMAX>), dim3((unsigned)nch), dim3(256), 0, s,
-                     idx, base, off, T, E, k, nbits, C, ar, rt);
+                     idx, base, gpc, off, T, E, k, nbits, C, ar, rt);
 }
 
 constexpr int kPermTok = 2;      // tokens per permute workgroup
@@ -304,22 +336,23 @@ hipError_t launch_gtab(const int32_t* counts, const int32_t* offsets, int E,
   return hipGetLastError();
 }
 
-hipError_t launch_assign(const int32_t* idx, const int32_t* chunk_base,
+hipError_t launch_assign(const int32_t* idx, const int32_t* chunk_base, int hg,
                          const int32_t* offsets, int64_t T, int E, int k,
                          int64_t C, int32_t* assign_row, int32_t* row_token,
                          hipStream_t s) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  const int gpc = kChunkTokens / hg;
   if (k <= 1)
-    launch_assign_t<1>(idx, chunk_base, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+    launch_assign_t<1>(idx, chunk_base, gpc, offsets, T, E, k, nbits, C, assign_row, row_token, s);
   else if (k <= 2)
-    launch_assign_t<2>(idx, chunk_base, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+    launch_assign_t<2>(idx, chunk_base, gpc, offsets, T, E, k, nbits, C, assign_row, row_token, s);
   else if (k <= 4)
-    launch_assign_t<4>(idx, chunk_base, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+    launch_assign_t<4>(idx, chunk_base, gpc, offsets, T, E, k, nbits, C, assign_row, row_token, s);
   else if (k <= 8)
-    launch_assign_t<8>(idx, chunk_base, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+    launch_assign_t<8>(idx, chunk_base, gpc, offsets, T, E, k, nbits, C, assign_row, row_token, s);
   else
-    launch_assign_t<16>(idx, chunk_base, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+    launch_assign_t<16>(idx, chunk_base, gpc, offsets, T, E, k, nbits, C, assign_row, row_token, s);
   return hipGetLastError();
 }
 

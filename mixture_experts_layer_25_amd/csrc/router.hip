@@ -4,11 +4,14 @@
 // hidden states by the router weight; infra-l7, "NVIDIA 原题" table row
 // "router" ([T,h] x [h,E] -> [T,E]).  Logits are fp32.
 //
-// bf16 layers use MFMA v_mfma_f32_16x16x32_bf16: one workgroup takes 16
-// tokens, its 4 waves split the reduction over h into quarters and the
-// experts are walked 16 at a time (up to 256 per pass), so x is read from
-// HBM once; the four partial sums meet in LDS.  bf16 x bf16 products are
-// exact in fp32 and accumulate in fp32.
+// bf16 layers use MFMA v_mfma_f32_16x16x32_bf16, and in both kernels the
+// 4 waves of a workgroup split the reduction over h into quarters whose
+// partial sums meet in LDS in a fixed order.  Up to 16 experts: one
+// workgroup takes 16 tokens and every expert, so x and the small w_router
+// are each read once.  More experts: one workgroup per tile of 64 tokens x
+// 64 experts (4x4 MFMA tiles per wave), which bounds the re-reads of
+// w_router to one per 64 tokens and keeps the grid wide.  bf16 x bf16
+// products are exact in fp32 and accumulate in fp32.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -16,67 +19,156 @@ namespace moe {
 
 namespace {
 
-constexpr int kRouterTok = 16;       // tokens per workgroup
-constexpr int kRouterChunks = 16;    // 16-expert chunks per pass
+constexpr int kRouterTok = 16;       // tokens per workgroup (up to 16 experts)
+constexpr int kRouterBatch = 8;      // 32-deep steps whose loads are issued together
 
 __global__ __launch_bounds__(256) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, float* __restrict__ logits, int64_t T,
     int h, int E) {
-  __shared__ float red[4][kRouterTok][kRouterChunks * 16];  // 64 KiB
+  __shared__ float red[4][kRouterTok][16];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * kRouterTok;
   const int kq = h >> 2;                  // h % 128 == 0: kq % 32 == 0
-  const int kbeg = w * kq;
-  int64_t trow = t0 + (lane & 15);
-  if (trow > T - 1) trow = T - 1;
+  const int koff = w * kq + (lane >> 4) * 8;
   // MFMA 16x16x32 operands: lane l holds row (l & 15) and 8 consecutive k
-  // values at k-group (l >> 4); A and B use the same k placement.
-  const uint16_t* xp = x + trow * h + kbeg + (lane >> 4) * 8;
-  const int nch = (E + 15) >> 4;
+  // values at k-group (l >> 4); A and B use the same k placement.  Rows
+  // past T or E are clamped; their sums are dropped (experts past E are
+  // zeroed so every lane's MFMA input is defined).
+  int64_t trow = t0 + (lane & 15);
+  trow = trow < T ? trow : T - 1;
+  const int e = lane & 15;
+  const bool ez = e >= E;
+  const uint16_t* xp = x + trow * h + koff;
+  const uint16_t* wp = wr + (int64_t)(ez ? E - 1 : e) * h + koff;
 
-  for (int cg = 0; cg < nch; cg += kRouterChunks) {
-    floatx4 acc[kRouterChunks];
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  int kk = 0;
+  for (; kk + 32 * kRouterBatch <= kq; kk += 32 * kRouterBatch) {
+    uint4 a[kRouterBatch], b[kRouterBatch];
 #pragma unroll
-    for (int c = 0; c < kRouterChunks; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < kRouterBatch; ++u) {
+      a[u] = ld16(xp + kk + 32 * u);
+      b[u] = ld16(wp + kk + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < kRouterBatch; ++u) {
+      if (ez) b[u] = uint4{0u, 0u, 0u, 0u};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                    __builtin_bit_cast(bf16x8, b[u]), acc,
+                                                    0, 0, 0);
+    }
+  }
+  for (; kk < kq; kk += 32) {
+    const uint4 a = ld16(xp + kk);
+    uint4 b = ld16(wp + kk);
+    if (ez) b = uint4{0u, 0u, 0u, 0u};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+  // C layout: lane l holds expert column (l & 15), token rows 4*(l>>4)+i.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[w][4 * (lane >> 4) + i][lane & 15] = acc[i];
+  __syncthreads();
+  const int tk = threadIdx.x >> 4, ee = threadIdx.x & 15;
+  const int64_t t = t0 + tk;
+  if (ee < E && t < T) {
+    float s = red[0][tk][ee] + red[1][tk][ee];
+    s += red[2][tk][ee];
+    s += red[3][tk][ee];
+    if (bias) s += bias[ee];
+    logits[t * E + ee] = s;
+  }
+}
 
-    for (int kk = 0; kk < kq; kk += 32) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(xp + kk));
+constexpr int kTileT = 64;           // tokens per tile
+constexpr int kTileE = 64;           // experts per tile
+constexpr int kRedLd = kTileE + 4;   // LDS row stride of the partial sums
+
+__global__ __launch_bounds__(256) void router_bf16_tile_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, float* __restrict__ logits, int64_t T,
+    int h, int E) {
+  __shared__ float red[4][kTileT][kRedLd];  // 68 KiB
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * kTileT;
+  const int e0 = blockIdx.y * kTileE;
+  const int kq = h >> 2;                  // h % 128 == 0: kq % 32 == 0
+  const int koff = w * kq + (lane >> 4) * 8;
+  // Rows past T or E are clamped to the last one; their sums are dropped.
+  const uint16_t* ap[4];
+  const uint16_t* bp[4];
 #pragma unroll
-      for (int c = 0; c < kRouterChunks; ++c) {
-        if (cg + c < nch) {
-          const int e = (cg + c) * 16 + (lane & 15);
-          const int ec = e < E ? e : E - 1;
-          uint4 braw = ld16(wr + (int64_t)ec * h + kbeg + (lane >> 4) * 8 + kk);
-          if (e >= E) braw = uint4{0u, 0u, 0u, 0u};
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              a, __builtin_bit_cast(bf16x8, braw), acc[c], 0, 0, 0);
-        }
+  for (int i = 0; i < 4; ++i) {
+    int64_t t = t0 + 16 * i + (lane & 15);
+    t = t < T ? t : T - 1;
+    ap[i] = x + t * h + koff;
+    int e = e0 + 16 * i + (lane & 15);
+    e = e < E ? e : E - 1;
+    bp[i] = wr + (int64_t)e * h + koff;
+  }
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // Two 32-deep steps per iteration so 16 loads are in flight; a 32-deep
+  // tail when kq is an odd multiple of 32.
+  int kk = 0;
+  for (; kk + 64 <= kq; kk += 64) {
+    bf16x8 a[2][4], b[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[u][i] = __builtin_bit_cast(bf16x8, ld16(ap[i] + kk + 32 * u));
+        b[u][i] = __builtin_bit_cast(bf16x8, ld16(bp[i] + kk + 32 * u));
       }
-    }
-    // C layout: lane l holds expert column (l & 15), token rows 4*(l>>4)+i.
 #pragma unroll
-    for (int c = 0; c < kRouterChunks; ++c) {
-      if (cg + c < nch) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          red[w][4 * (lane >> 4) + i][c * 16 + (lane & 15)] = acc[c][i];
-      }
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
+  }
+  if (kk < kq) {
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = __builtin_bit_cast(bf16x8, ld16(ap[i] + kk));
+      b[i] = __builtin_bit_cast(bf16x8, ld16(bp[i] + kk));
     }
-    __syncthreads();
-    const int ne = min(kRouterChunks * 16, E - cg * 16);
-    for (int p = threadIdx.x; p < kRouterTok * ne; p += 256) {
-      const int tk = p / ne, ee = p - tk * ne;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+  // C layout: lane l holds expert column (l & 15), token rows 4*(l>>4)+r.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[w][16 * i + 4 * (lane >> 4) + r][16 * j + (lane & 15)] = acc[i][j][r];
+  __syncthreads();
+  for (int p = threadIdx.x; p < kTileT * kTileE; p += 256) {
+    const int tk = p / kTileE, ee = p % kTileE;
+    const int64_t t = t0 + tk;
+    const int e = e0 + ee;
+    if (t < T && e < E) {
       float s = red[0][tk][ee] + red[1][tk][ee];
       s += red[2][tk][ee];
       s += red[3][tk][ee];
-      const int e = cg * 16 + ee;
       if (bias) s += bias[e];
-      const int64_t t = t0 + tk;
-      if (t < T) logits[t * E + e] = s;
+      logits[t * E + e] = s;
     }
-    __syncthreads();
   }
 }
 
@@ -102,7 +194,12 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 hipError_t launch_router(int dtype, const void* x, const void* w_router,
                          const float* logit_bias, float* logits, int64_t T,
                          int h, int E, hipStream_t s) {
-  if (dtype == 1) {
+  if (dtype == 1 && E > 16) {
+    const dim3 grid((unsigned)((T + kTileT - 1) / kTileT), (unsigned)((E + kTileE - 1) / kTileE));
+    hipLaunchKernelGGL(router_bf16_tile_kernel, grid, dim3(256), 0, s,
+                       (const uint16_t*)x, (const uint16_t*)w_router,
+                       logit_bias, logits, T, h, E);
+  } else if (dtype == 1) {
     const int64_t nb = (T + kRouterTok - 1) / kRouterTok;
     hipLaunchKernelGGL(router_bf16_kernel, dim3((unsigned)nb), dim3(256), 0, s,
                        (const uint16_t*)x, (const uint16_t*)w_router,

@@ -11,8 +11,8 @@
 // 64-bit key (ordered fp32 key bits << 32 | ~expert), so the largest key
 // wins and equal keys go to the lower expert index; the winner clears its
 // entry.  Gates use the fp32 logits (never the selection bias).  Each
-// workgroup covers one chunk of 256 tokens and writes that chunk's expert
-// histogram, which the scan kernel turns into ranks and offsets.
+// workgroup covers 4 passes of 256/G tokens and writes the expert histogram
+// of those tokens, which the scan kernel turns into ranks and offsets.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -49,9 +49,12 @@ __global__ __launch_bounds__(256) void topk_kernel(
     const float* __restrict__ logits, const float* __restrict__ sbias,
     int gate_mode, int64_t T, int E, int k, int32_t* __restrict__ idx_out,
     float* __restrict__ gate_out, int32_t* __restrict__ chunk_hist) {
+  constexpr int kTokPerPass = 256 / G;
+  constexpr int kPasses = 4;
+  constexpr int kTok = kPasses * kTokPerPass;
   __shared__ int32_t hist[1024];
-  __shared__ int32_t sel_e[kChunkTokens][16];
-  __shared__ float sel_l[kChunkTokens][16];
+  __shared__ int32_t sel_e[kTok][16];
+  __shared__ float sel_l[kTok][16];
 
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 256) hist[e] = 0;
@@ -59,10 +62,9 @@ __global__ __launch_bounds__(256) void topk_kernel(
 
   const int seg = tid / G;           // token slot within a pass
   const int s = tid % G;             // lane within the segment
-  constexpr int kTokPerPass = 256 / G;
-  const int64_t chunk0 = (int64_t)blockIdx.x * kChunkTokens;
+  const int64_t chunk0 = (int64_t)blockIdx.x * kTok;
 
-  for (int pass = 0; pass < kChunkTokens / kTokPerPass; ++pass) {
+  for (int pass = 0; pass < kPasses; ++pass) {
     const int tl = pass * kTokPerPass + seg;   // token within the chunk
     const int64_t t = chunk0 + tl;
     const bool valid = t < T;
@@ -140,8 +142,8 @@ template <int G, int NPL>
 void launch_topk_t(const float* logits, const float* sb, int gate, int64_t T,
                    int E, int k, int32_t* idx, float* g, int32_t* hist,
                    hipStream_t s) {
-  const int64_t nch = (T + kChunkTokens - 1) / kChunkTokens;
-  hipLaunchKernelGGL((topk_kernel<G, NPL>), dim3((unsigned)nch), dim3(256), 0,
+  const int64_t nwg = (T + 4 * (256 / G) - 1) / (4 * (256 / G));
+  hipLaunchKernelGGL((topk_kernel<G, NPL>), dim3((unsigned)nwg), dim3(256), 0,
                      s, logits, sb, gate, T, E, k, idx, g, hist);
 }
 
@@ -150,6 +152,7 @@ void launch_topk_t(const float* logits, const float* sb, int gate, int64_t T,
 hipError_t launch_topk(const float* logits, const float* select_bias, int gate,
                        int64_t T, int E, int k, int32_t* idx, float* gate_out,
                        int32_t* chunk_hist, hipStream_t s) {
+  // G and the tokens per workgroup must agree with topk_tokens_per_wg(E)
   if (E <= 8)
     launch_topk_t<8, 1>(logits, select_bias, gate, T, E, k, idx, gate_out, chunk_hist, s);
   else if (E <= 16)

@@ -87,7 +87,7 @@ def _raw_status(cfg, **over):
     """moe_router_topk with fake (never dereferenced) pointers: only the host
     checks run, so no GPU is touched."""
     L = moe.lib()
-    args = dict(x=1, w=1, lb=None, sb=None, logits=16, idx=16, gate=16, ws=None, wsb=0)
+    args = dict(x=16, w=32, lb=None, sb=None, logits=48, idx=64, gate=80, ws=None, wsb=0)
     args.update(over)
     return L.moe_router_topk(ctypes.byref(cfg) if cfg is not None else None, args["x"],
                              args["w"], args["lb"], args["sb"], args["logits"], args["idx"],
@@ -125,6 +125,13 @@ def test_validation_of_struct_and_pointers():
     assert _raw_status(_cfg(T=0), x=None) == moe.MOE_OK     # nothing to read
     # no logits pointer and no workspace: the workspace is required
     assert _raw_status(_cfg(T=5), logits=None) == moe.MOE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("arg", ["x", "w", "lb", "sb", "logits", "idx", "gate"])
+def test_misaligned_pointers_are_rejected(arg):
+    # every pointer must be 16-byte aligned; the check runs before any launch
+    assert _raw_status(_cfg(T=5), **{arg: 16 * 7 + 8}) == moe.MOE_ERR_INVALID_ARG
+    assert _raw_status(_cfg(T=0), **{arg: 16 * 7 + 8}) == moe.MOE_OK   # nothing to read
 
 
 def test_strerror():

@@ -42,6 +42,10 @@ MEDIUM = [
     MoEConfig("k_equals_e", T=257, h=128, E=4, k=4, F=128),
     MoEConfig("one_token", T=1, h=128, E=8, k=2, F=128, cf=(5, 4)),
     MoEConfig("e1024_k16", T=70, h=128, E=1024, k=16, F=128, gate="softmax_all_topk"),
+    # expert count that fills neither a 16- nor a 64-expert router tile, h an
+    # odd multiple of 128 (router K loop tail)
+    MoEConfig("e40_ragged", T=333, h=384, E=40, k=3, F=256, gate="softmax_all_topk",
+              cf=(3, 2)),
     # K long enough (>= 16 slices of 64) that the tiles of the last partial
     # round are split along K and reduced (GEMM 1 and GEMM 2)
     MoEConfig("split_k_tail", T=600, h=1024, E=4, k=2, F=1024, gate="softmax_topk"),
