@@ -12,7 +12,10 @@
 //
 // bf16 kernel (gfx950): 256 threads = 4 waves in a 2x2 grid, a 256x256
 // output tile per workgroup, each wave a 128x128 sub-tile held as 4x4
-// v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, in AGPRs).
+// v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, in AGPRs).  The
+// last row tile of a group is cut to 64 or 128 rows when that holds its
+// rows (waves then hold 1x4 or 2x4 fragments), so a group's leftover rows
+// cost a quarter or half of a tile instead of a whole one.
 // K advances in slices of 64 (128-byte rows, whole cache lines per row).
 // Slices are copied global -> LDS directly (buffer_load_dwordx4 ... lds, no
 // registers in between) into a ring of three A slots and two B slots of
@@ -159,22 +162,29 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Epilogue of a 256x256 tile.  The MFMAs take the weight fragment first, so
-// fragment (i, j) holds C^T: lane l has output row (l & 31) of row block i
-// and, in registers 4b..4b+3, the 4 consecutive columns 8b + 4*(l >> 5) + 0..3
-// of column block j.  Lanes l and l ^ 32 (same row) trade one 4-column run
-// so that each ends up with 8 consecutive columns: 16-byte stores, the two
-// lanes of a row writing 32 contiguous bytes.  GEMM 1 writes silu(a1) * a3
-// (w1 blocks j = 0, 1 pair with the w3 blocks j + 2 of the same columns);
-// GEMM 2 writes the product.
-template <bool SWIGLU>
-__device__ __forceinline__ void store_tile(const floatx16 (&acc)[4][4], const Tile& tl, int lane,
+// Row fragments (32 rows) per wave for a tile of m_valid rows.  The last
+// row tile of a group is only as tall as its rows need (64, 128 or 256), so
+// a group's few leftover rows do not cost a whole 256-row tile.
+__device__ __forceinline__ int frags_of(int m_valid) {
+  return m_valid > 128 ? 4 : (m_valid > 64 ? 2 : 1);
+}
+
+// Epilogue of a (64*FI) x 256 tile.  The MFMAs take the weight fragment
+// first, so fragment (i, j) holds C^T: lane l has output row (l & 31) of row
+// block i and, in registers 4b..4b+3, the 4 consecutive columns
+// 8b + 4*(l >> 5) + 0..3 of column block j.  Lanes l and l ^ 32 (same row)
+// trade one 4-column run so that each ends up with 8 consecutive columns:
+// 16-byte stores, the two lanes of a row writing 32 contiguous bytes.
+// GEMM 1 writes silu(a1) * a3 (w1 blocks j = 0, 1 pair with the w3 blocks
+// j + 2 of the same columns); GEMM 2 writes the product.
+template <bool SWIGLU, int FI>
+__device__ __forceinline__ void store_tile(const floatx16 (&acc)[FI][4], const Tile& tl, int lane,
                                            int wm, int wn, uint16_t* out, int ldo, int N) {
   const int hi = lane >> 5;
   constexpr int NJ = SWIGLU ? 2 : 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wm * 128 + i * 32 + (lane & 31);
+  for (int i = 0; i < FI; ++i) {
+    const int row = wm * 32 * FI + i * 32 + (lane & 31);
     const bool ok = row < tl.m_valid;
     uint16_t* orow = out + (tl.o_row + row) * (int64_t)ldo;
 #pragma unroll
@@ -215,31 +225,26 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[4][4], const Ti
   }
 }
 
-template <bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];   // 160 KiB
+// fp32 partial of a split tile, in register order: register group q of
+// fragment (i, j) of wave w, c = (i*4 + j)*4 + q, lands at
+// ((w*16*FI + c)*64 + lane)*4 (1 KiB per store instruction).
+template <int FI>
+__device__ __forceinline__ int64_t part_off(int w, int c, int lane) {
+  return ((int64_t)(w * 16 * FI + c) * 64 + lane) * 4;
+}
 
-  const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
-  const int nk = a.K / BK;
-  const Work wk = plan_work(a, NT, nk, blockIdx.x);
-  if (wk.L < 0) return;
-  Tile tl = tile_of(a, NT, wk.L, BM);
-  // Tile fields and the wave index are wave-uniform; saying so keeps the
-  // buffer descriptors below in scalar registers.
-  tl.g = __builtin_amdgcn_readfirstlane(tl.g);
-  tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
-  tl.m_valid = __builtin_amdgcn_readfirstlane(tl.m_valid);
-  tl.a_row = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tl.a_row >> 32)) << 32) |
-             (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.a_row);
-  tl.o_row = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tl.o_row >> 32)) << 32) |
-             (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.o_row);
-  const int part = __builtin_amdgcn_readfirstlane(wk.part);
-  const int parts = __builtin_amdgcn_readfirstlane(wk.parts);
-
+// One (64*FI) x 256 output tile, or one K part of it.  Waves form a 2x2
+// grid: wave (wm, wn) owns rows wm*32*FI + [0, 32*FI) and columns
+// wn*128 + [0, 128), i.e. FI x 4 MFMA fragments.
+template <bool SWIGLU, int FI>
+__device__ __forceinline__ void tile_body(const GroupedGemmArgs& a, const Tile& tl, int part,
+                                          int parts, int64_t slot, uint8_t* smem) {
+  constexpr int WR = 16 * FI;   // A rows each wave copies: 2*FI blocks of 8
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
   const int K = a.K, N = a.N, ldo = a.ldo;
+  const int nk = K / BK;
   const bool shared = tl.g >= a.E_routed;
   const bool a_shared = shared && !a.a_from_out_rows;
   const uint16_t* A = (const uint16_t*)(a_shared ? a.A_shared : a.A);
@@ -258,12 +263,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
   const int nsteps = (int)((int64_t)(part + 1) * nk / parts) - kbeg;
   const int krot = (parts == 1 && a.rotate_k && !shared) ? (int)(((int64_t)tl.g * nk / 8) % nk) : 0;
 
-  // Global -> LDS copies: wave w fills rows w*64 .. w*64+63 of the A and the
-  // B slice, 8 rows (1 KiB) per instruction; lane l lands at byte 16*l of
-  // the block: row l >> 3, stored chunk l & 7, which holds logical chunk
-  // (l & 7) ^ (l >> 3) ^ i in the i-th block (swz of row w*64 + 8*i + (l>>3)).
-  const int a_rows = __builtin_amdgcn_readfirstlane(min(max(tl.m_valid - w * 64, 0), 64));
-  const rsrc_t rsA = make_rsrc(A + (tl.a_row + w * 64) * (int64_t)lda, (uint32_t)a_rows * arowbytes);
+  // Global -> LDS copies: wave w fills rows w*WR .. w*WR+WR-1 of the A slice
+  // and rows w*64 .. w*64+63 of the B slice, 8 rows (1 KiB) per instruction;
+  // lane l lands at byte 16*l of the block: row l >> 3, stored chunk l & 7,
+  // which holds logical chunk (l & 7) ^ swz(row).  For block i of A,
+  // row = w*WR + 8*i + (l >> 3), so swz(row) = (l >> 3) ^ ((2*FI*w + i) & 7);
+  // for B it is (l >> 3) ^ i.
+  const int a_rows = __builtin_amdgcn_readfirstlane(min(max(tl.m_valid - w * WR, 0), WR));
+  const rsrc_t rsA = make_rsrc(A + (tl.a_row + w * WR) * (int64_t)lda, (uint32_t)a_rows * arowbytes);
   rsrc_t rsB;
   if (SWIGLU) {
     // B rows of the tile: [w1 f0.. | w3 f0.. | w1 f0+64.. | w3 f0+64..], 64 each
@@ -275,46 +282,55 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
         (int)min(max((int64_t)N - brow, (int64_t)0), (int64_t)64));
     rsB = make_rsrc(B0 + min(brow, (int64_t)N - 1) * K, (uint32_t)nb * browbytes);
   }
-  uint32_t voffA[8], voffB[8];
+  uint32_t voffA[2 * FI], voffB[8];
+#pragma unroll
+  for (int i = 0; i < 2 * FI; ++i) {
+    const uint32_t c = (uint32_t)((((lane & 7) ^ (lane >> 3) ^ (2 * FI * w + i)) & 7) << 4);
+    voffA[i] = (uint32_t)(lane >> 3) * arowbytes + c;
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t c = (uint32_t)((((lane & 7) ^ (lane >> 3) ^ i) & 7) << 4);
-    voffA[i] = (uint32_t)(lane >> 3) * arowbytes + c;
     voffB[i] = (uint32_t)(lane >> 3) * browbytes + c;
   }
-  uint8_t* const dstA = smem + w * 8192;
+  uint8_t* const dstA = smem + w * (WR * BK * 2);
   uint8_t* const dstB = smem + kOffB + w * 8192;
 
   // MFMA operand reads: lane l reads row (l & 31) of a 32-row fragment and
-  // logical chunk 2*s + (l >> 5) of sub-step s; swz of that row is
-  // (l & 7) ^ (4*(i & 1) + ((l >> 3) & 3)) for fragment i.
-  const int rA = (wm * 128 + (lane & 31)) * (BK * 2);
+  // logical chunk 2*s + (l >> 5) of sub-step s.  The fragment's first row
+  // is a multiple of 32, 32*q say, and swz of its row is
+  // (l & 7) ^ (4*(q & 1) + ((l >> 3) & 3)): q = FI*wm + i for A fragment i,
+  // q = 4*wn + j for B fragment j.
+  const int rA = (wm * 32 * FI + (lane & 31)) * (BK * 2);
   const int rB = (wn * 128 + (lane & 31)) * (BK * 2);
   const int fe = (lane & 7) ^ ((lane >> 3) & 3);
   const int fo = (lane & 7) ^ (4 | ((lane >> 3) & 3));
-  int cx[4][2];
+  const bool aflip = (FI * wm) & 1;   // A fragment i has parity (i & 1) ^ aflip
+  int cx[4][2], cxa[4][2];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     cx[s][0] = ((2 * s + (lane >> 5)) ^ fe) << 4;
     cx[s][1] = ((2 * s + (lane >> 5)) ^ fo) << 4;
+    cxa[s][0] = aflip ? cx[s][1] : cx[s][0];
+    cxa[s][1] = aflip ? cx[s][0] : cx[s][1];
   }
 
-  floatx16 acc[4][4];
+  floatx16 acc[FI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  bf16x8 fa0[FI], fb0[4], fa1[FI], fb1[4];
 
 #define SB() __builtin_amdgcn_sched_barrier(0)
 // weight fragment as the MFMA's first operand: the accumulator holds C^T,
 // so each lane ends up with runs of 4 consecutive output columns of one row
 #define MF(FA, FB, I, J) \
   acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[J], FA[I], acc[I][J], 0, 0, 0)
-#define RDA(F, SA, S, I) F[I] = lds_frag((SA) + rA + (I) * 4096 + cx[S][(I) & 1])
+#define RDA(F, SA, S, I) F[I] = lds_frag((SA) + rA + (I) * 4096 + cxa[S][(I) & 1])
 #define RDB(F, SBP, S, J) F[J] = lds_frag((SBP) + rB + (J) * 4096 + cx[S][(J) & 1])
 // K slice of step KT (rotated); past the end the offset leaves the buffer
 // and the copy returns zeros
@@ -328,47 +344,72 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                   \
       rsB, LDS_AS(dstB + ((KT) & 1) * kPart + (I) * 1024), 16, voffB[I],                      \
       (KT) < nsteps ? (uint32_t)(I) * 8u * browbytes + KOFF(KT) : KOFF(KT), 0, 0)
-// one sub-step: 8 groups of [copy] [fragment read] [2 MFMAs]
-#define SUBSTEP(FA, FB, RFA, RFB, SA, SBP, S, COPY)                                   \
-  COPY(0); RDA(RFA, SA, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                \
-  COPY(1); RDA(RFA, SA, S, 1); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                \
-  COPY(2); RDA(RFA, SA, S, 2); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB();                \
-  COPY(3); RDA(RFA, SA, S, 3); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                \
-  COPY(4); RDB(RFB, SBP, S, 0); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();               \
-  COPY(5); RDB(RFB, SBP, S, 1); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();               \
-  COPY(6); RDB(RFB, SBP, S, 2); MF(FA, FB, 3, 0); MF(FA, FB, 3, 1); SB();               \
-  COPY(7); RDB(RFB, SBP, S, 3); MF(FA, FB, 3, 2); MF(FA, FB, 3, 3); SB()
+// One sub-step: groups of [copy] [fragment reads for the next sub-step]
+// [2 MFMAs]; 4*FI MFMAs and FI + 4 reads per sub-step.
+#define SUBSTEP(FA, FB, RFA, RFB, SA, SBP, S, COPY)                                        \
+  if constexpr (FI == 4) {                                                                 \
+    COPY(0); RDA(RFA, SA, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                   \
+    COPY(1); RDA(RFA, SA, S, 1); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                   \
+    COPY(2); RDA(RFA, SA, S, 2); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB();                   \
+    COPY(3); RDA(RFA, SA, S, 3); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                   \
+    COPY(4); RDB(RFB, SBP, S, 0); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();                  \
+    COPY(5); RDB(RFB, SBP, S, 1); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                  \
+    COPY(6); RDB(RFB, SBP, S, 2); MF(FA, FB, 3, 0); MF(FA, FB, 3, 1); SB();                  \
+    COPY(7); RDB(RFB, SBP, S, 3); MF(FA, FB, 3, 2); MF(FA, FB, 3, 3); SB();                  \
+  } else if constexpr (FI == 2) {                                                          \
+    COPY(0); RDA(RFA, SA, S, 0); RDB(RFB, SBP, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB(); \
+    COPY(1); RDA(RFA, SA, S, 1); RDB(RFB, SBP, S, 1); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB(); \
+    COPY(2); RDB(RFB, SBP, S, 2); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB();                  \
+    COPY(3); RDB(RFB, SBP, S, 3); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                  \
+  } else {                                                                                 \
+    COPY(0); RDA(RFA, SA, S, 0); RDB(RFB, SBP, S, 0); RDB(RFB, SBP, S, 1);                   \
+    MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                                              \
+    COPY(1); RDB(RFB, SBP, S, 2); RDB(RFB, SBP, S, 3); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB(); \
+  }
 
-  // s_waitcnt immediates (gfx9 encoding; expcnt and lgkmcnt left at "no wait")
-  constexpr int kWaitVm0 = 0x0F70, kWaitVm8 = 0x0F78, kWaitVm16 = 0x4F70;
+  // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+  // expcnt and lgkmcnt left at "no wait")
+#define VMCNT(n) (0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+#define VMCNT_LGKM0(n) (VMCNT(n) & ~0x0F00)
+  constexpr int kWaitAll = VMCNT(0);
+  constexpr int kWaitLoop = VMCNT_LGKM0(2 * FI);       // A(kt+2) may stay in flight
+  constexpr int kWaitPrologue = VMCNT_LGKM0(2 * FI + 8);
+// Workgroup barrier without a memory fence.  __syncthreads() would release
+// every copy issued so far (a wait for all of them, in-flight A(kt+2)
+// included); what the ring needs is narrower and is waited for explicitly
+// just before: this wave's copies up to slice kt+1 landed (vmcnt) and its
+// fragment reads of the retiring slots done (lgkmcnt).  The asm's memory
+// clobber keeps the compiler from moving LDS accesses across it.
+#define WG_BARRIER(WAIT)                      \
+  __builtin_amdgcn_s_waitcnt(WAIT);           \
+  asm volatile("s_barrier" ::: "memory")
 
   // Prologue: A(0), B(0), A(1), B(1) in flight; wait for slice 0.
 #pragma unroll
-  for (int i = 0; i < 8; ++i) DMA_A(0, i);
+  for (int i = 0; i < 2 * FI; ++i) DMA_A(0, i);
 #pragma unroll
   for (int i = 0; i < 8; ++i) DMA_B(0, i);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) DMA_A(1, i);
+  for (int i = 0; i < 2 * FI; ++i) DMA_A(1, i);
 #pragma unroll
   for (int i = 0; i < 8; ++i) DMA_B(1, i);
-  __builtin_amdgcn_s_waitcnt(kWaitVm16);
-  __syncthreads();
+  WG_BARRIER(kWaitPrologue);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) RDA(fa0, smem, 0, i);
+  for (int i = 0; i < FI; ++i) RDA(fa0, smem, 0, i);
 #pragma unroll
   for (int j = 0; j < 4; ++j) RDB(fb0, smem + kOffB, 0, j);
 
   // Step kt (slice kt in A slot kt%3, B slot kt%2; sub-step 0 fragments
   // already in registers):
-  //   s0..s2: MFMAs of sub-steps 0..2, reads of sub-steps 1..3, and the 8
-  //       copies of A(kt+2) spread over them (its slot held slice kt-1,
-  //       retired at the previous barrier);
-  //   wait until at most 8 copies (A(kt+2)'s) may be in flight -> A(kt+1),
-  //   B(kt+1) landed;
+  //   s0..s2: MFMAs of sub-steps 0..2, reads of sub-steps 1..3, and the
+  //       2*FI copies of A(kt+2) spread over them (its slot held slice
+  //       kt-1, retired at the previous barrier);
+  //   wait until at most 2*FI copies (A(kt+2)'s) may be in flight ->
+  //   A(kt+1), B(kt+1) landed;
   //   barrier: slice kt+1 visible to all, slice kt's slots free
   //   s3: MFMAs of sub-step 3, reads of slice kt+1 sub-step 0, the 8 copies
   //       of B(kt+2) into slice kt's B slot.
-  //   Copies complete in issue order, so "at most 8 copies in flight" at
+  //   Copies complete in issue order, so "at most 2*FI copies in flight" at
   //   the next barrier means everything up to B(kt+2) has landed.  Keeping
   //   the copies apart keeps the address unit from backing up the waves'
   //   in-order issue (and with it the MFMAs).
@@ -377,24 +418,43 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
     const uint8_t* sbb = smem + kOffB + (kt & 1) * kPart;
     const uint8_t* na = smem + ((kt + 1) % kSlotsA) * kPart;
     const uint8_t* nbb = smem + kOffB + ((kt + 1) & 1) * kPart;
-// A(kt+2) blocks 0-2, 3-5 and 6-7 in sub-steps 1, 2 and 3; B(kt+2) one
-// block per MFMA pair after the barrier
-#define COPY_A1(I) if ((I) == 1 || (I) == 4 || (I) == 7) DMA_A(kt + 2, (I) / 3);
-#define COPY_A2(I) if ((I) == 1 || (I) == 4 || (I) == 7) DMA_A(kt + 2, 3 + (I) / 3);
-#define COPY_A3(I) if ((I) == 2 || (I) == 6) DMA_A(kt + 2, 6 + (I) / 4);
-#define COPY_B(I) DMA_B(kt + 2, (I));
+// A(kt+2): FI = 4: blocks 0-2, 3-5, 6-7 in sub-steps 1, 2, 3; FI = 2:
+// blocks 0-1, 2, 3; FI = 1: blocks 0, 1.  B(kt+2) after the barrier.
+#define COPY_A1(I)                                                                 \
+  if constexpr (FI == 4) {                                                         \
+    if ((I) == 1 || (I) == 4 || (I) == 7) DMA_A(kt + 2, (I) / 3);                  \
+  } else if constexpr (FI == 2) {                                                  \
+    if ((I) == 1 || (I) == 3) DMA_A(kt + 2, (I) / 2);                              \
+  } else {                                                                         \
+    if ((I) == 1) DMA_A(kt + 2, 0);                                                \
+  }
+#define COPY_A2(I)                                                                 \
+  if constexpr (FI == 4) {                                                         \
+    if ((I) == 1 || (I) == 4 || (I) == 7) DMA_A(kt + 2, 3 + (I) / 3);              \
+  } else if constexpr (FI == 2) {                                                  \
+    if ((I) == 2) DMA_A(kt + 2, 2);                                                \
+  } else {                                                                         \
+    if ((I) == 1) DMA_A(kt + 2, 1);                                                \
+  }
+#define COPY_A3(I)                                                                 \
+  if constexpr (FI == 4) {                                                         \
+    if ((I) == 2 || (I) == 6) DMA_A(kt + 2, 6 + (I) / 4);                          \
+  } else if constexpr (FI == 2) {                                                  \
+    if ((I) == 2) DMA_A(kt + 2, 3);                                                \
+  }
+#define COPY_B(I)                                                                  \
+  _Pragma("unroll") for (int u = 0; u < 8 / (2 * FI); ++u) DMA_B(kt + 2, (I) * (8 / (2 * FI)) + u);
     SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 1, COPY_A1);
     SUBSTEP(fa1, fb1, fa0, fb0, sa, sbb, 2, COPY_A2);
     SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 3, COPY_A3);
-    __builtin_amdgcn_s_waitcnt(kWaitVm8);
-    __syncthreads();
+    WG_BARRIER(kWaitLoop);
     SUBSTEP(fa1, fb1, fa0, fb0, na, nbb, 0, COPY_B);
 #undef COPY_A1
 #undef COPY_A2
 #undef COPY_A3
 #undef COPY_B
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
 #undef SB
 #undef MF
 #undef RDA
@@ -404,23 +464,79 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
 #undef DMA_A
 #undef DMA_B
 #undef SUBSTEP
+#undef VMCNT
+#undef VMCNT_LGKM0
+#undef WG_BARRIER
 
   if (parts > 1) {
-    // split tile: fp32 partial in register order, 1 KiB per store instruction
-    float* P = a.partials + (wk.slot * parts + part) * (int64_t)(256 * 256);
+    float* P = a.partials + (slot * parts + part) * (int64_t)(256 * 256);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = (i * 4 + j) * 4 + q;
-          *reinterpret_cast<floatx4*>(P + ((int64_t)(w * 64 + c) * 64 + lane) * 4) =
+          *reinterpret_cast<floatx4*>(P + part_off<FI>(w, c, lane)) =
               floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
     return;
   }
-  store_tile<SWIGLU>(acc, tl, lane, wm, wn, (uint16_t*)a.out, ldo, N);
+  store_tile<SWIGLU, FI>(acc, tl, lane, wm, wn, (uint16_t*)a.out, ldo, N);
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];   // 160 KiB
+
+  const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
+  const int nk = a.K / BK;
+  const Work wk = plan_work(a, NT, nk, blockIdx.x);
+  if (wk.L < 0) return;
+  Tile tl = tile_of(a, NT, wk.L, BM);
+  // Tile fields are workgroup-uniform; saying so keeps the buffer
+  // descriptors in scalar registers.
+  tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+  tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
+  tl.m_valid = __builtin_amdgcn_readfirstlane(tl.m_valid);
+  tl.a_row = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tl.a_row >> 32)) << 32) |
+             (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.a_row);
+  tl.o_row = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tl.o_row >> 32)) << 32) |
+             (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.o_row);
+  const int part = __builtin_amdgcn_readfirstlane(wk.part);
+  const int parts = __builtin_amdgcn_readfirstlane(wk.parts);
+  const int fi = frags_of(tl.m_valid);
+  if (fi == 4)
+    tile_body<SWIGLU, 4>(a, tl, part, parts, wk.slot, smem);
+  else if (fi == 2)
+    tile_body<SWIGLU, 2>(a, tl, part, parts, wk.slot, smem);
+  else
+    tile_body<SWIGLU, 1>(a, tl, part, parts, wk.slot, smem);
+}
+
+template <bool SWIGLU, int FI>
+__device__ __forceinline__ void reduce_body(const GroupedGemmArgs& a, const Tile& tl, int s,
+                                            int64_t slot) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  floatx16 acc[FI][4];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = (i * 4 + j) * 4 + q;
+        floatx4 sum = {0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < s; ++p) {
+          const float* P = a.partials + (slot * s + p) * (int64_t)(256 * 256);
+          sum += *reinterpret_cast<const floatx4*>(P + part_off<FI>(w, c, lane));
+        }
+        acc[i][j][4 * q] = sum[0];
+        acc[i][j][4 * q + 1] = sum[1];
+        acc[i][j][4 * q + 2] = sum[2];
+        acc[i][j][4 * q + 3] = sum[3];
+      }
+  store_tile<SWIGLU, FI>(acc, tl, lane, w >> 1, w & 1, (uint16_t*)a.out, a.ldo, a.N);
 }
 
 // Sums the K parts of the split tiles (in part order) and stores them like
@@ -435,26 +551,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_reduce_kernel(GroupedGemmArgs a
   const int64_t slot = blockIdx.x;
   if (s < 2 || whole + slot >= V) return;
   const Tile tl = tile_of(a, NT, whole + slot, BM);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  floatx16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = (i * 4 + j) * 4 + q;
-        floatx4 sum = {0.f, 0.f, 0.f, 0.f};
-        for (int p = 0; p < s; ++p) {
-          const float* P = a.partials + (slot * s + p) * (int64_t)(256 * 256);
-          sum += *reinterpret_cast<const floatx4*>(P + ((int64_t)(w * 64 + c) * 64 + lane) * 4);
-        }
-        acc[i][j][4 * q] = sum[0];
-        acc[i][j][4 * q + 1] = sum[1];
-        acc[i][j][4 * q + 2] = sum[2];
-        acc[i][j][4 * q + 3] = sum[3];
-      }
-  store_tile<SWIGLU>(acc, tl, lane, w >> 1, w & 1, (uint16_t*)a.out, a.ldo, a.N);
+  const int fi = frags_of(tl.m_valid);
+  if (fi == 4)
+    reduce_body<SWIGLU, 4>(a, tl, s, slot);
+  else if (fi == 2)
+    reduce_body<SWIGLU, 2>(a, tl, s, slot);
+  else
+    reduce_body<SWIGLU, 1>(a, tl, s, slot);
 }
 
 // fp32 layers: 64x64 tiles, BK = 16, fp32 FMA, each thread 4 rows x 4
