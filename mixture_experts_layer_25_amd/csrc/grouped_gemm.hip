@@ -519,23 +519,29 @@ __device__ __forceinline__ void reduce_body(const GroupedGemmArgs& a, const Tile
                                             int64_t slot) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   floatx16 acc[FI][4];
+  const float* P0 = a.partials + slot * s * (int64_t)(256 * 256);
+  // Per row block: the 16 loads of a part are issued together, then added;
+  // parts are added in part order (the sum is the same for every launch).
 #pragma unroll
-  for (int i = 0; i < FI; ++i)
+  for (int i = 0; i < FI; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = (i * 4 + j) * 4 + q;
-        floatx4 sum = {0.f, 0.f, 0.f, 0.f};
-        for (int p = 0; p < s; ++p) {
-          const float* P = a.partials + (slot * s + p) * (int64_t)(256 * 256);
-          sum += *reinterpret_cast<const floatx4*>(P + part_off<FI>(w, c, lane));
-        }
-        acc[i][j][4 * q] = sum[0];
-        acc[i][j][4 * q + 1] = sum[1];
-        acc[i][j][4 * q + 2] = sum[2];
-        acc[i][j][4 * q + 3] = sum[3];
-      }
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int p = 0; p < s; ++p) {
+      const float* P = P0 + p * (int64_t)(256 * 256);
+      floatx4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        v[u] = *reinterpret_cast<const floatx4*>(P + part_off<FI>(w, i * 16 + u, lane));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[j * 4 + q][e];
+    }
+  }
   store_tile<SWIGLU, FI>(acc, tl, lane, w >> 1, w & 1, (uint16_t*)a.out, a.ldo, a.N);
 }
 
