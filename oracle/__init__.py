@@ -3,9 +3,11 @@ from .moe_oracle import (  # noqa: F401
     GATE_MODES,
     capacity,
     gates,
+    load_balance,
     moe_forward,
     near_tie,
     route_maps,
+    router_probs,
     router_logits,
     selection_keys,
     silu,

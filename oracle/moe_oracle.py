@@ -17,7 +17,10 @@ no permutation buffer, no blocking and no fusion:
    assignment whose rank is C or more is dropped;
 5. for every kept (token, slot): the expert's SwiGLU FFN in fp64;
 6. the gate-weighted sum of the kept expert outputs, in slot order, plus the
-   shared expert's output when there is one.
+   shared expert's output when there is one;
+7. (separately) the load-balance statistics of a routing: the share of
+   assignments per expert, the router's mean probability per expert and the
+   Switch auxiliary loss built from them.
 
 Sources (pages and the part of each that is followed):
 
@@ -52,7 +55,11 @@ Readings where the pages are silent or disagree (all listed in the design doc):
 * overflow keeps the first C assignments in token order; a dropped slot adds
   nothing and the other gates are not renormalised;
 * the expert FFN is W2 · (silu(W1 x) ⊙ (W3 x)) with silu(z) = z/(1+e^-z);
-* the layer output excludes the residual; the shared expert has weight 1.
+* the layer output excludes the residual; the shared expert has weight 1;
+* load balance: f_i counts routed assignments over T*k (before capacity
+  drops); P_i averages the router's distribution over all E (softmax of the
+  logits, or the sigmoids normalised over E); the loss coefficient alpha is
+  an input.
 
 Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
 against hand-worked fixtures, closed forms and brute force; none is
@@ -298,3 +305,39 @@ def moe_forward(x, w_router, w1, w3, w2, *, k: int, gate: str,
     out["y"] = y
     out["tokens"] = tok
     return out
+
+
+# ---------------------------------------------------------------------------
+# 7. Load-balance statistics.  infra-l7, "NVIDIA 原题" notes on the load
+# balancing loss: Switch Transformer adds alpha*E*sum_i f_i*P_i, with f_i the
+# share of tokens sent to expert i and P_i the router's mean probability for
+# i, smallest when the load is even.  Megatron-LM part 6, "负载均衡":
+# aux_loss penalises the gap between where tokens go and how likely the
+# router makes each expert (logged as load_balancing_loss).
+# ---------------------------------------------------------------------------
+def router_probs(logits, gate: str) -> np.ndarray:
+    """fp64 [T,E]: the router's distribution over all E experts per token:
+    softmax of the logits for the softmax gates, the per-expert sigmoids
+    normalised over all E for the sigmoid gate.  The selection-only bias is
+    not part of it."""
+    l = _f64(logits)
+    if gate in ("softmax_topk", "softmax_all_topk"):
+        ex = np.exp(l - l.max(axis=1, keepdims=True))
+        return ex / ex.sum(axis=1, keepdims=True)
+    if gate == "sigmoid_topk_norm":
+        s = 1.0 / (1.0 + np.exp(-l))
+        return s / s.sum(axis=1, keepdims=True)
+    raise ValueError(f"unknown gate mode {gate!r}")
+
+
+def load_balance(logits, counts, k: int, gate: str, alpha: float) -> dict:
+    """f [E] = counts / (T*k) (routed assignments, before any capacity drop),
+    P [E] = mean over tokens of router_probs, loss = alpha*E*sum_i f_i*P_i.
+    Sums in fp64; f, P and loss returned rounded to fp32."""
+    l = _f64(logits)
+    T, E = l.shape
+    f = np.asarray(counts, dtype=np.float64) / float(T * k)
+    P = router_probs(l, gate).mean(axis=0)
+    loss = float(alpha) * E * float(np.dot(f, P))
+    return {"f": f.astype(np.float32), "P": P.astype(np.float32),
+            "loss": np.float32(loss)}

@@ -368,3 +368,55 @@ def test_worked_example_dimension_chain(golden_dir):
     per_expert = 3 * cfg.h * cfg.F
     assert abs(per_expert / g["params_per_expert_approx"] - 1) < 0.01
     assert abs(cfg.E * per_expert / g["params_per_layer_approx"] - 1) < 0.01
+
+
+# ---------------------------------------------------------------- load balance
+def test_load_balance_hand_cases(golden_dir):
+    """Hand-worked Switch losses (closed-form probabilities)."""
+    g = _load(golden_dir, "load_balance_hand.json")
+    for c in g["cases"]:
+        lg = np.asarray(c["logits"], dtype=np.float32)
+        r = oracle.load_balance(lg, c["counts"], c["k"], c["gate"], c["alpha"])
+        np.testing.assert_allclose(r["f"], c["f"], rtol=0, atol=1e-7)
+        np.testing.assert_allclose(r["P"], c["P"], rtol=0, atol=1e-7)
+        assert abs(float(r["loss"]) - c["loss"]) <= 2e-7 * max(1.0, c["loss"])
+
+
+@pytest.mark.parametrize("gate", oracle.GATE_MODES)
+def test_load_balance_even_load_gives_alpha(gate):
+    """Equal logits and equal counts: f = P = 1/E, loss = alpha exactly."""
+    T, E, k, alpha = 48, 6, 2, 0.37
+    lg = np.full((T, E), 0.8125, dtype=np.float32)
+    counts = [T * k // E] * E
+    r = oracle.load_balance(lg, counts, k, gate, alpha)
+    np.testing.assert_allclose(r["f"], 1.0 / E, rtol=1e-7)
+    np.testing.assert_allclose(r["P"], 1.0 / E, rtol=1e-7)
+    assert abs(float(r["loss"]) - alpha) <= 1e-7
+
+
+def test_load_balance_collapse_gives_alpha_times_e():
+    """Every token on expert 0 with the router near-certain of it: loss -> alpha*E."""
+    T, E, alpha = 40, 8, 0.01
+    lg = np.zeros((T, E), dtype=np.float32)
+    lg[:, 0] = 60.0
+    r = oracle.load_balance(lg, [T] + [0] * (E - 1), 1, "softmax_topk", alpha)
+    assert abs(float(r["loss"]) - alpha * E) <= 1e-7 * alpha * E
+
+
+@pytest.mark.parametrize("gate", oracle.GATE_MODES)
+def test_load_balance_invariants(gate):
+    """sum f = sum P = 1; for k = E every expert is selected by every token, so
+    T*P_i equals the sum of the softmax-over-all gates of expert i."""
+    rng = np.random.default_rng(5)
+    T, E = 37, 5
+    lg = rng.normal(0, 2, (T, E)).astype(np.float32)
+    idx = oracle.topk(lg, E)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    r = oracle.load_balance(lg, counts, E, gate, 1.0)
+    assert abs(float(r["f"].astype(np.float64).sum()) - 1.0) <= 1e-6
+    assert abs(float(r["P"].astype(np.float64).sum()) - 1.0) <= 1e-6
+    if gate == "softmax_all_topk":
+        g = oracle.gates(lg, idx, gate).astype(np.float64)
+        per_e = np.zeros(E)
+        np.add.at(per_e, idx.ravel(), g.ravel())
+        np.testing.assert_allclose(r["P"], per_e / T, rtol=1e-6)
