@@ -193,6 +193,23 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    # load-balance statistics of the last step's routing (not part of the
+    # step): reads the logits once (T*E*4 bytes)
+    logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+    route_lb = {"logits": logits, "expert_counts": counts}
+    moe.moe_forward(c, weights, inp["x"], y, route_lb, ws)
+    lb_out = [torch.empty(cfg.E, dtype=torch.float32, device=dev) for _ in range(2)]
+    lb_loss = torch.empty(1, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        moe.moe_load_balance(c, logits, counts, 0.01, lb_out[0], lb_out[1], lb_loss, ws)
+    lb_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    lb_ev[0].record()
+    for _ in range(K):
+        moe.moe_load_balance(c, logits, counts, 0.01, lb_out[0], lb_out[1], lb_loss, ws)
+    lb_ev[1].record()
+    torch.cuda.synchronize()
+    lb_us = lb_ev[0].elapsed_time(lb_ev[1]) * 1e3 / K
+
     stage_ms = {}
     for s, name in enumerate(moe.STAGE_NAMES):
         stage_ms[name] = sum(evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(K)) / K
@@ -238,6 +255,9 @@ def main() -> int:
         "combine": {"gbs": round(comb_gbs, 1), "frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
                     "bytes": cb},
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "load_balance": {"us": round(lb_us, 2),
+                         "gbs": round(cfg.T * cfg.E * 4 / (lb_us * 1e-6) / 1e9, 1),
+                         "aux_loss": round(float(lb_loss.item()), 6)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, C, args.cpu_sample)

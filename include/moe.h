@@ -205,6 +205,26 @@ int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
                           const int32_t* assign_row, const float* topk_gate,
                           const void* shared_y, void* y, void* stream);
 
+/* Load-balance statistics of a routing --------------------------------------
+ * infra-l7 "NVIDIA 原题" notes on the load balancing loss (Switch
+ * Transformer's alpha*E*sum_i f_i*P_i, f_i the share of tokens sent to
+ * expert i, P_i the router's mean probability for i); Megatron-LM part 6,
+ * "负载均衡" (aux loss and the load_balancing_loss metric).
+ *   logits [T,E] fp32 in (as written by moe_router_topk / moe_forward);
+ *   expert_counts [E] int32 in (routed assignments per expert, before any
+ *       capacity drop, as written by moe_permute / moe_forward);
+ *   f [E] out: expert_counts[i] / (T*k);
+ *   P [E] out: mean over the T tokens of the router's distribution over all
+ *       E experts: softmax of the logits for the two softmax gate modes, the
+ *       per-expert sigmoids normalised over E for SIGMOID_TOPK_NORM (the
+ *       selection bias takes no part);
+ *   aux_loss [1] out: alpha * E * sum_i f[i] * P[i] (alpha finite).
+ * Sums are fp32 in a fixed order: identical results on every run.  Needs
+ * the workspace of moe_workspace_bytes(cfg).                               */
+int moe_load_balance(const moe_cfg_t* cfg, const float* logits,
+                     const int32_t* expert_counts, float alpha, float* f, float* P,
+                     float* aux_loss, void* ws, size_t ws_bytes, void* stream);
+
 /* The fused layer: stages 1-4 (+ the shared expert as one more group of
  * the grouped GEMM) on one stream, no host synchronisation.
  *   w        weights (device pointers inside a host struct)

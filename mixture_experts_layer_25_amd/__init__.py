@@ -46,7 +46,7 @@ DTYPE_BY_NAME = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16}
 ABI_SYMBOLS = (
     "moe_strerror", "moe_capacity", "moe_num_rows", "moe_workspace_bytes",
     "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu",
-    "moe_unpermute_combine", "moe_forward",
+    "moe_unpermute_combine", "moe_load_balance", "moe_forward",
 )
 
 
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
             "moe_permute": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_grouped_gemm_swiglu": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_unpermute_combine": (ctypes.c_int, [cfgp, P, P, P, P, P, P]),
+            "moe_load_balance": (ctypes.c_int, [cfgp, P, P, ctypes.c_float, P, P, P, P, SZ,
+                                                P]),
             "moe_forward": (ctypes.c_int, [cfgp, ctypes.POINTER(MoEWeights), P, P,
                                            ctypes.POINTER(MoERouteOut), P, SZ, P, P]),
         }
@@ -206,6 +208,16 @@ def moe_unpermute_combine(cfg, y_perm, assign_row, topk_gate, shared_y, y,
     _check("moe_unpermute_combine", lib().moe_unpermute_combine(
         ctypes.byref(cfg), _ptr(y_perm), _ptr(assign_row), _ptr(topk_gate),
         _ptr(shared_y), _ptr(y), _stream(stream)))
+
+
+def moe_load_balance(cfg, logits, expert_counts, alpha: float, f, P, aux_loss, ws,
+                     stream=None) -> None:
+    """Share of assignments f [E], mean router probability P [E] and the
+    Switch loss alpha*E*sum(f*P) [1] of a routing (fp32 device outputs)."""
+    wp, wb = _ws(ws)
+    _check("moe_load_balance", lib().moe_load_balance(
+        ctypes.byref(cfg), _ptr(logits), _ptr(expert_counts), float(alpha), _ptr(f), _ptr(P),
+        _ptr(aux_loss), wp, wb, _stream(stream)))
 
 
 def weights_struct(w: dict) -> MoEWeights:

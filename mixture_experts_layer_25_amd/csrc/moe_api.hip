@@ -55,7 +55,7 @@ int check_cfg(const moe_cfg_t* c) {
 }
 
 struct Layout {
-  size_t logits, idx, gate, hist, base, counts, offsets, assign, rowtok, gtab;
+  size_t logits, idx, gate, hist, base, pbal, counts, offsets, assign, rowtok, gtab;
   size_t partials, xperm, act, yperm, total;
 };
 
@@ -80,6 +80,7 @@ Layout layout_of(const moe_cfg_t& c) {
   L.gate = take((size_t)(T * k) * 4);
   L.hist = take((size_t)(nch * E) * 4);
   L.base = take((size_t)(nch * E) * 4);
+  L.pbal = take((size_t)(nch * E) * 4);
   L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);
   L.assign = take((size_t)(T * k) * 4);
@@ -289,6 +290,23 @@ MOE_API int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
   if (misaligned(y_perm, assign_row, topk_gate, shared_y, y)) return MOE_ERR_INVALID_ARG;
   MOE_TRY(moe::launch_combine(c.dtype, y_perm, c.h, assign_row, topk_gate, shared_y, y,
                               c.T, c.h, c.k, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+MOE_API int moe_load_balance(const moe_cfg_t* cfg, const float* logits,
+                             const int32_t* expert_counts, float alpha, float* f, float* P,
+                             float* aux_loss, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const moe_cfg_t& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (!logits || !expert_counts || !f || !P || !aux_loss) return MOE_ERR_INVALID_ARG;
+  if (misaligned(logits, expert_counts, f, P, aux_loss, ws)) return MOE_ERR_INVALID_ARG;
+  if (!(alpha == alpha)) return MOE_ERR_INVALID_ARG;     // NaN
+  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  MOE_TRY(moe::launch_load_balance(logits, expert_counts, c.gate, c.T, c.E, c.k, alpha,
+                                   at<float>(ws, layout_of(c).pbal), f, P, aux_loss,
+                                   (hipStream_t)stream));
   return MOE_OK;
 }
 

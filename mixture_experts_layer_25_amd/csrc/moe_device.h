@@ -52,4 +52,24 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Max / sum over aligned segments of G lanes (G a power of two <= 64);
+// every lane of a segment gets the result.
+template <int G>
+__device__ __forceinline__ float seg_max_f32(float v) {
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, G));
+  return v;
+}
+
+template <int G>
+__device__ __forceinline__ float seg_sum_f32(float v) {
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, G);
+  return v;
+}
+
+// Lanes per token of the segment kernels (top-k, router probabilities):
+// the next power of two >= E, at most 64.
+inline int seg_lanes(int E) { return E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64)); }
+
 }  // namespace moe

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_device.h"
+
 namespace moe {
 
 // Tile table written by the scan kernels and read by the grouped GEMMs.
@@ -50,10 +52,14 @@ hipError_t launch_router(int dtype, const void* x, const void* w_router,
 // Tokens one top-k workgroup handles (4 passes of 256/G tokens, G = lanes
 // per token); its expert histogram covers that many tokens.  Always a
 // divisor of 256.
-inline int topk_tokens_per_wg(int E) {
-  const int G = E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64));
-  return 4 * 256 / G;
-}
+inline int topk_tokens_per_wg(int E) { return 4 * 256 / seg_lanes(E); }
+
+// Router distribution summed per expert over token groups (partial:
+// [ceil(T / topk_tokens_per_wg(E))][E] floats), then f, P and the Switch
+// loss (one workgroup).
+hipError_t launch_load_balance(const float* logits, const int32_t* counts, int gate, int64_t T,
+                               int E, int k, float alpha, float* partial, float* f, float* P,
+                               float* loss, hipStream_t st);
 
 hipError_t launch_topk(const float* logits, const float* select_bias,
                        int gate, int64_t T, int E, int k, int32_t* idx,

@@ -30,20 +30,6 @@ __device__ __forceinline__ uint64_t seg_max_u64(uint64_t v) {
   return v;
 }
 
-template <int G>
-__device__ __forceinline__ float seg_max_f32(float v) {
-#pragma unroll
-  for (int m = 1; m < G; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, G));
-  return v;
-}
-
-template <int G>
-__device__ __forceinline__ float seg_sum_f32(float v) {
-#pragma unroll
-  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, G);
-  return v;
-}
-
 template <int G, int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float* __restrict__ logits, const float* __restrict__ sbias,

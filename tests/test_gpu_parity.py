@@ -81,6 +81,44 @@ def test_forward_matches_oracle(cfg):
     assert err <= tol_of(cfg)
 
 
+BALANCE = ["worked_example_small", "sigmoid_bias_shared", "zipf_dropless", "e256_k8_shared",
+           "e1024_k16", "one_token", "e40_ragged", "k_equals_e", "f32_capacity"]
+
+
+@pytest.mark.parametrize("name", BALANCE)
+def test_load_balance_matches_oracle(name):
+    """f, P and the Switch loss of the GPU's own routing (its logits and
+    counts) against the oracle on the same values; a second call gives the
+    same bits."""
+    cfg = next(c for c in MEDIUM if c.name == name)
+    print(f"[case] load balance {name}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, _ = capacity_of(cfg)
+    out = run_forward(cfg, inp, C_lib)
+    c = lib_cfg(cfg, C_lib)
+    alpha = 0.01
+    res = []
+    for _ in range(2):
+        f = torch.full((cfg.E,), float("nan"), dtype=torch.float32, device=DEV)
+        P = torch.full((cfg.E,), float("nan"), dtype=torch.float32, device=DEV)
+        loss = torch.full((1,), float("nan"), dtype=torch.float32, device=DEV)
+        moe.moe_load_balance(c, out["logits"], out["expert_counts"], alpha, f, P, loss, out["ws"])
+        torch.cuda.synchronize()
+        res.append((f.cpu().numpy(), P.cpu().numpy(), float(loss.item())))
+    (f, P, loss), (f2, P2, loss2) = res
+    assert np.array_equal(f, f2) and np.array_equal(P, P2) and loss == loss2
+    ref = oracle.load_balance(np32(out["logits"]), out["expert_counts"].cpu().numpy(), cfg.k,
+                              cfg.gate, alpha)
+    # f: the same integer ratio on both sides (one rounding each)
+    np.testing.assert_allclose(f, ref["f"], rtol=2.0 ** -23, atol=0)
+    # P: fp32 sums in a fixed tree over T tokens vs fp64 sums
+    dP = float(np.abs(P.astype(np.float64) - ref["P"].astype(np.float64)).max())
+    assert dP <= 2e-5 * float(ref["P"].max()), dP
+    dl = abs(loss - float(ref["loss"])) / max(abs(float(ref["loss"])), 1e-30)
+    assert dl <= 2e-5, dl
+    _report(f"load_balance_{name}", dP=f"{dP:.2e}", dloss=f"{dl:.2e}", loss=f"{loss:.6g}")
+
+
 STAGED = ["dropless_softmax", "capacity_heavy_drop", "sigmoid_bias_shared", "split_k_tail",
           "f32_capacity", "f32_sigmoid_shared"]
 
@@ -259,8 +297,21 @@ def test_full_size_routing_and_sampled_outputs(name):
     ref_y = oracle_forward(cfg, inp, C_ref, tokens=tok, idx=g_idx)["y"]
     y = np32(gpu["y"][torch.as_tensor(tok, device=DEV)])
     err = rel_err(y, ref_y)
+    # load-balance statistics of this routing, against the oracle's own
+    # logits and counts (so the whole chain router -> counts -> stats)
+    c = lib_cfg(cfg, C_lib)
+    lb = [torch.full((n_,), float("nan"), dtype=torch.float32, device=DEV)
+          for n_ in (cfg.E, cfg.E, 1)]
+    moe.moe_load_balance(c, gpu["logits"], gpu["expert_counts"], 0.01, *lb, gpu["ws"])
+    torch.cuda.synchronize()
+    ref_lb = oracle.load_balance(ref["logits"], np.bincount(ref["idx"].ravel(), minlength=cfg.E),
+                                 cfg.k, cfg.gate, 0.01)
+    lb_err = abs(float(lb[2].item()) - float(ref_lb["loss"])) / float(ref_lb["loss"])
     _report(name, rel_err=f"{err:.2e}", sampled=len(tok), max_count=int(counts.max()),
-            mean_count=float(counts.mean()), **rep)
+            mean_count=float(counts.mean()), aux_loss=f"{float(lb[2].item()):.6g}",
+            aux_loss_rel_err=f"{lb_err:.1e}", **rep)
     assert err <= 2e-2
+    # near-tie tokens may route differently; each moves at most 1/(T*k) of f
+    assert lb_err <= 1e-4
     del gpu, inp
     torch.cuda.empty_cache()
