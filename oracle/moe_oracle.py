@@ -20,7 +20,9 @@ no permutation buffer, no blocking and no fusion:
    shared expert's output when there is one;
 7. (separately) the load-balance statistics of a routing: the share of
    assignments per expert, the router's mean probability per expert and the
-   Switch auxiliary loss built from them.
+   Switch auxiliary loss built from them;
+8. two routing variants: capacity drops by gate score instead of token
+   order, and expert choice (every expert takes its C best-scoring tokens).
 
 Sources (pages and the part of each that is followed):
 
@@ -341,3 +343,89 @@ def load_balance(logits, counts, k: int, gate: str, alpha: float) -> dict:
     loss = float(alpha) * E * float(np.dot(f, P))
     return {"f": f.astype(np.float32), "P": P.astype(np.float32),
             "loss": np.float32(loss)}
+
+
+# ---------------------------------------------------------------------------
+# 8. Routing variants.  专家并行 page, "EP+TP+DP": MoE theory drops the
+# lower-priority tokens by their gate score (as opposed to cutting along C
+# for parallelism).  10.5 §10.5.6: expert-choice routing turns the direction
+# round: every expert takes the fixed number of tokens that score highest
+# for it, so the load is balanced by construction.
+# ---------------------------------------------------------------------------
+def route_maps_score_drop(idx, gates_fp32, E: int, C: int) -> dict:
+    """Capacity C with score priority.  Of the assignments to expert e (a
+    token picks e at most once), the C with the largest fp32 gate are kept,
+    ties going to the earlier token; the kept ones take rows e*C, e*C+1, ...
+    in token order and the rest are dropped (row -1)."""
+    idx = np.asarray(idx)
+    g = np.asarray(gates_fp32, dtype=np.float32)
+    T, k = idx.shape
+    assign_row = np.full((T, k), -1, dtype=np.int64)
+    counts = np.zeros(E, dtype=np.int64)
+    for e in range(E):
+        cand = [(t, j) for t in range(T) for j in range(k) if int(idx[t, j]) == e]
+        counts[e] = len(cand)
+        # position i in `cand` is token order; priority = (gate desc, i asc)
+        order = sorted(range(len(cand)), key=lambda i: (-float(g[cand[i]]), i))
+        for r, i in enumerate(sorted(order[:C])):
+            t, j = cand[i]
+            assign_row[t, j] = e * C + r
+    row_token = np.full(E * C, -1, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            if assign_row[t, j] >= 0:
+                row_token[assign_row[t, j]] = t
+    return {"counts": counts, "offsets": np.arange(E + 1, dtype=np.int64) * C,
+            "kept": np.minimum(counts, C), "assign_row": assign_row,
+            "row_token": row_token, "rows": E * C}
+
+
+def expert_choice(logits, C: int, gate: str, scores=None) -> dict:
+    """Every expert takes the C tokens with the largest router probability
+    (router_probs rounded to fp32; ties to the earlier token) and lays them
+    out in token order at rows e*C .. e*C+C-1.  ``scores``: optional fp32
+    [T,E] to decide on instead (e.g. the device's own probabilities).
+
+    sel_row [T,E]: row of (t, e) or -1; gate [T,E]: the chosen token's score
+    (0 where not chosen); row_token [E*C]; counts [E] = C."""
+    if scores is None:
+        p = router_probs(logits, gate).astype(np.float32)
+    else:
+        p = np.asarray(scores, dtype=np.float32)
+    T, E = p.shape
+    if not 0 < C <= T:
+        raise ValueError("expert choice needs 0 < C <= T")
+    sel_row = np.full((T, E), -1, dtype=np.int64)
+    g = np.zeros((T, E), dtype=np.float32)
+    row_token = np.empty(E * C, dtype=np.int64)
+    for e in range(E):
+        top = np.argsort(-p[:, e].astype(np.float64), kind="stable")[:C]
+        for r, t in enumerate(np.sort(top)):
+            sel_row[t, e] = e * C + r
+            g[t, e] = p[t, e]
+            row_token[e * C + r] = t
+    return {"scores": p, "sel_row": sel_row, "gate": g, "row_token": row_token,
+            "counts": np.full(E, C, dtype=np.int64),
+            "offsets": np.arange(E + 1, dtype=np.int64) * C, "rows": E * C}
+
+
+def expert_choice_forward(x, w_router, w1, w3, w2, *, C: int, gate: str, logit_bias=None,
+                          shared=None, tokens=None, scores=None) -> dict:
+    """Layer forward with expert-choice routing: y[t] = sum over the experts
+    that chose t, in expert order, of gate[t,e] * FFN_e(x[t]) (+ shared)."""
+    logits = router_logits(x, w_router, logit_bias)
+    m = expert_choice(logits, C, gate, scores)
+    T, E = m["sel_row"].shape
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    xs = _f64(x[tok])
+    y = np.zeros((len(tok), x.shape[1]), dtype=np.float64)
+    for e in range(E):                      # expert order
+        chosen = m["sel_row"][tok, e] >= 0
+        if chosen.any():
+            o = swiglu_ffn(xs[chosen], w1[e], w3[e], w2[e])
+            y[chosen] += _f64(m["gate"][tok[chosen], e])[:, None] * o
+    if shared is not None:
+        ws1, ws3, ws2 = shared
+        y += swiglu_ffn(xs, ws1, ws3, ws2)
+    m.update({"logits": logits, "y": y, "tokens": tok})
+    return m
