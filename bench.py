@@ -94,9 +94,11 @@ def measured_traffic(workload: str):
 
 
 # --------------------------------------------------------------------- bench
-def _workload_name(cfg, C):
+def _workload_name(cfg, C, routing="topk"):
     s = (f"{cfg.name}: T={cfg.T} h={cfg.h} E={cfg.E} k={cfg.k} F={cfg.F} {cfg.dtype} "
          f"{cfg.gate}")
+    if routing != "topk":
+        s += f" {routing}"
     s += f" C={C}" if C else " dropless"
     if cfg.shared:
         s += " +1 shared expert"
@@ -136,6 +138,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="worked_example")
+    ap.add_argument("--routing", default="topk",
+                    choices=("topk", "topk_score_drop", "expert_choice"),
+                    help="routing variant (the headline workload uses topk)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -156,8 +161,14 @@ def main() -> int:
     torch.cuda.set_device(0)
     inp = make_inputs(cfg, device=dev)
     C = moe.moe_capacity(cfg.T, cfg.E, cfg.k, *cfg.cf) if cfg.cf else 0
+    if args.routing != "topk" and C == 0:
+        print(f"--routing {args.routing} needs a workload with a capacity", file=sys.stderr)
+        return 2
+    if args.routing == "expert_choice":
+        C = min(C, cfg.T)
+        inp["select_bias"] = None      # expert choice ranks by probability only
     c = moe.make_cfg(cfg.T, cfg.h, cfg.F, cfg.E, cfg.k, cfg.dtype, cfg.gate, capacity=C,
-                     has_shared=cfg.shared)
+                     has_shared=cfg.shared, routing=args.routing)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     esz = 2 if cfg.dtype == "bf16" else 4
     rows = moe.moe_num_rows(c)
@@ -214,7 +225,7 @@ def main() -> int:
     for s, name in enumerate(moe.STAGE_NAMES):
         stage_ms[name] = sum(evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(K)) / K
     cnt = counts.cpu().tolist()
-    kept = sum(min(n, C) for n in cnt) if C else sum(cnt)
+    kept = sum(min(n, C) for n in cnt) if C else sum(cnt)   # expert choice: E*C
     kept_all = kept + (cfg.T if cfg.shared else 0)
     ms_step = elapsed * 1e3 / K
     g1 = gemm1_flops(kept_all, cfg.h, cfg.F) / (stage_ms["gemm1_swiglu"] * 1e-3) / 1e12
@@ -223,6 +234,8 @@ def main() -> int:
         (stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     pb = permute_bytes(cfg.T, cfg.h, rows, esz)
+    if args.routing == "expert_choice":      # a row gather: every row read and written
+        pb = 2 * rows * cfg.h * esz
     cb = combine_bytes(kept, cfg.T, cfg.h, esz, cfg.shared)
     perm_gbs = pb / (stage_ms["permute"] * 1e-3) / 1e9
     comb_gbs = cb / (stage_ms["combine"] * 1e-3) / 1e9
@@ -240,14 +253,15 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) tokens, fan-in-scaled N(0,1/fan_in) random weights)",
-        "config": {"workload": _workload_name(cfg, C), "T": cfg.T, "h": cfg.h, "E": cfg.E,
+        "config": {"workload": _workload_name(cfg, C, args.routing), "routing": args.routing, "T": cfg.T, "h": cfg.h, "E": cfg.E,
                    "k": cfg.k, "F": cfg.F, "capacity": C, "gate": cfg.gate,
                    "kept_rows": kept, "dispatch_rows": rows, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma" if cfg.dtype == "bf16" else "alu",
                      "kernel": "gemm1_swiglu",
                      "achieved": round(g1, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(g1 / peak, 4),
-                     "traffic": measured_traffic(_workload_name(cfg, C))},
+                     "traffic": (measured_traffic(_workload_name(cfg, C))
+                                 if args.routing == "topk" else None)},
         "grouped_gemm": {"tflops": round(gg, 1), "frac_of_peak": round(gg / peak, 4),
                          "gemm1_tflops": round(g1, 1), "gemm2_tflops": round(g2, 1)},
         "permute": {"gbs": round(perm_gbs, 1), "frac_hbm": round(perm_gbs / PEAK_HBM_GBS, 4),
@@ -259,7 +273,7 @@ def main() -> int:
                          "gbs": round(cfg.T * cfg.E * 4 / (lb_us * 1e-6) / 1e9, 1),
                          "aux_loss": round(float(lb_loss.item()), 6)},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.routing == "topk":
         out["cpu_baseline"] = cpu_baseline(cfg, inp, C, args.cpu_sample)
     print(json.dumps(out), flush=True)
     return 0

@@ -79,6 +79,33 @@ extern "C" {
 #define MOE_GATE_SOFTMAX_ALL_TOPK 1
 #define MOE_GATE_SIGMOID_TOPK_NORM 2
 
+/* ---- routing ----------------------------------------------------------
+ *   TOPK              token choice: each token's top-k experts (gate modes
+ *                     above); with a capacity C the first C assignments of
+ *                     an expert in token order are kept, the rest dropped.
+ *   TOPK_SCORE_DROP   token choice with a capacity C (> 0 required) where an
+ *                     expert keeps the C assignments with the largest gate
+ *                     (ties to the earlier token), laid out in token order:
+ *                     专家并行 page, "EP+TP+DP" (MoE theory drops the
+ *                     lower-priority tokens by gate score).
+ *   EXPERT_CHOICE     every expert takes the C = capacity tokens (0 < C <= T)
+ *                     with the largest router probability (softmax over E of
+ *                     the logits, or for SIGMOID_TOPK_NORM the sigmoids
+ *                     normalised over E; ties to the earlier token), in
+ *                     token order at rows e*C ..; a token gets the sum over
+ *                     the experts that chose it, in expert order, of
+ *                     probability x expert output: 10.5 序列并行与专家并行,
+ *                     section 10.5.6 (expert-choice routing).  k only enters
+ *                     the caller's choice of C (moe_capacity); a
+ *                     select_bias is rejected (MOE_ERR_INVALID_ARG).  Only
+ *                     moe_forward, moe_grouped_gemm_swiglu,
+ *                     moe_unpermute_combine and moe_load_balance accept it.
+ * Selection decisions are integer compares of fp32 keys on the device, so
+ * every run routes the same.                                              */
+#define MOE_ROUTE_TOPK 0
+#define MOE_ROUTE_TOPK_SCORE_DROP 1
+#define MOE_ROUTE_EXPERT_CHOICE 2
+
 /* Kernels moe_forward launches, in order, each one a timed stage:
  *   0 router GEMM, 1 top-k + gates + chunk histogram, 2 scan (counts,
  *   offsets, GEMM tile table), 3 assign (ranks, rows), 4 permute copy,
@@ -98,6 +125,8 @@ typedef struct moe_cfg {
   int32_t gate;        /* MOE_GATE_* */
   int32_t has_shared;  /* 1: one shared expert of shape (h, F) on every token */
   int64_t capacity;    /* 0: dropless; > 0: capacity C rows per expert */
+  int32_t routing;     /* MOE_ROUTE_* */
+  int32_t reserved;    /* 0 */
 } moe_cfg_t;
 
 typedef struct moe_weights {
@@ -113,15 +142,20 @@ typedef struct moe_weights {
 } moe_weights_t;
 
 /* Optional device outputs of moe_forward (each field may be NULL; a NULL
- * field is kept in the workspace instead).  Layouts as in the stage calls. */
+ * field is kept in the workspace instead).  Layouts as in the stage calls.
+ * With MOE_ROUTE_EXPERT_CHOICE the per-token slots are the E experts:
+ * topk_idx is not written, topk_gate and assign_row are [T,E] (the
+ * probability and row of (t, e) if e chose t, else 0 and -1), and probs
+ * holds the router probabilities the experts chose by, laid out [E,T].     */
 typedef struct moe_route_out {
   float* logits;           /* [T,E] */
   int32_t* topk_idx;       /* [T,k] */
-  float* topk_gate;        /* [T,k] */
+  float* topk_gate;        /* [T,k] ([T,E] for expert choice) */
   int32_t* expert_counts;  /* [E]   assignments per expert, before any drop */
   int32_t* expert_offsets; /* [E+1] first row of each expert's group */
   int32_t* assign_row;     /* [T*k] row of (t,j) in x_perm, -1 if dropped */
   int32_t* row_token;      /* [rows] token of each row, -1 for padding */
+  float* probs;            /* [E,T] expert choice only */
 } moe_route_out_t;
 
 /* Host-only helpers (no device work, callable without a GPU). ---------- */

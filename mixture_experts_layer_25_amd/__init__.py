@@ -41,6 +41,14 @@ GATE_BY_NAME = {
     "sigmoid_topk_norm": MOE_GATE_SIGMOID_TOPK_NORM,
 }
 DTYPE_BY_NAME = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16}
+MOE_ROUTE_TOPK = 0
+MOE_ROUTE_TOPK_SCORE_DROP = 1
+MOE_ROUTE_EXPERT_CHOICE = 2
+ROUTING_BY_NAME = {
+    "topk": MOE_ROUTE_TOPK,
+    "topk_score_drop": MOE_ROUTE_TOPK_SCORE_DROP,
+    "expert_choice": MOE_ROUTE_EXPERT_CHOICE,
+}
 
 # Every symbol include/moe.h declares.
 ABI_SYMBOLS = (
@@ -62,6 +70,8 @@ class MoECfg(ctypes.Structure):
         ("gate", ctypes.c_int32),
         ("has_shared", ctypes.c_int32),
         ("capacity", ctypes.c_int64),
+        ("routing", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -73,7 +83,7 @@ class MoEWeights(ctypes.Structure):
 class MoERouteOut(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_idx", "topk_gate", "expert_counts", "expert_offsets",
-        "assign_row", "row_token")]
+        "assign_row", "row_token", "probs")]
 
 
 class MoEError(RuntimeError):
@@ -143,7 +153,8 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_cfg(T: int, h: int, F: int, E: int, k: int, dtype="bf16",
-             gate="softmax_topk", capacity: int = 0, has_shared: bool = False) -> MoECfg:
+             gate="softmax_topk", capacity: int = 0, has_shared: bool = False,
+             routing="topk") -> MoECfg:
     c = MoECfg()
     c.struct_size = ctypes.sizeof(MoECfg)
     c.dtype = DTYPE_BY_NAME[dtype] if isinstance(dtype, str) else int(dtype)
@@ -151,6 +162,8 @@ def make_cfg(T: int, h: int, F: int, E: int, k: int, dtype="bf16",
     c.gate = GATE_BY_NAME[gate] if isinstance(gate, str) else int(gate)
     c.has_shared = int(bool(has_shared))
     c.capacity = int(capacity)
+    c.routing = ROUTING_BY_NAME[routing] if isinstance(routing, str) else int(routing)
+    c.reserved = 0
     return c
 
 

@@ -6,7 +6,8 @@
 // load is even.  Megatron-LM part 6, "负载均衡": the aux loss penalises the
 // gap between where tokens go and how likely the router makes each expert.
 //
-//   probsum  a workgroup covers the same token group as a top-k workgroup
+//   probsum  (also writes the distribution itself for expert-choice
+//            routing) a workgroup covers the same token group as a top-k workgroup
 //            (4 passes of 256/G tokens, G lanes per token): each token's
 //            distribution over all E experts (softmax of the logits, or the
 //            sigmoids normalised over E), summed per expert in a fixed
@@ -22,10 +23,13 @@ namespace moe {
 
 namespace {
 
+// partial (the group sums) and probs_et (the distribution itself, [E,T])
+// are each optional.
 template <int G, int NPL>
 __global__ __launch_bounds__(256) void probsum_kernel(const float* __restrict__ logits,
                                                       int gate_mode, int64_t T, int E,
-                                                      float* __restrict__ partial) {
+                                                      float* __restrict__ partial,
+                                                      float* __restrict__ probs_et) {
   constexpr int kTokPerPass = 256 / G;
   constexpr int kPasses = 4;
   constexpr int kTok = kPasses * kTokPerPass;
@@ -72,6 +76,11 @@ __global__ __launch_bounds__(256) void probsum_kernel(const float* __restrict__ 
 #pragma unroll
       for (int i = 0; i < NPL; ++i) p[i] = valid ? v[i] / den : 0.f;
     }
+    if (probs_et && valid) {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i)
+        if (s + G * i < E) probs_et[(int64_t)(s + G * i) * T + t] = p[i];
+    }
 #pragma unroll
     for (int i = 0; i < NPL; ++i) pl[seg][s + G * i] = p[i];
     __syncthreads();
@@ -83,15 +92,37 @@ __global__ __launch_bounds__(256) void probsum_kernel(const float* __restrict__ 
     }
     __syncthreads();
   }
-  for (int e = tid; e < E; e += 256) partial[blockIdx.x * (int64_t)E + e] = acc[e];
+  if (partial)
+    for (int e = tid; e < E; e += 256) partial[blockIdx.x * (int64_t)E + e] = acc[e];
 }
 
 template <int G, int NPL>
 void launch_probsum_t(const float* logits, int gate, int64_t T, int E, float* partial,
-                      hipStream_t st) {
+                      float* probs_et, hipStream_t st) {
   const int64_t nwg = (T + 4 * (256 / G) - 1) / (4 * (256 / G));
   hipLaunchKernelGGL((probsum_kernel<G, NPL>), dim3((unsigned)nwg), dim3(256), 0, st, logits,
-                     gate, T, E, partial);
+                     gate, T, E, partial, probs_et);
+}
+
+void launch_probsum(const float* logits, int gate, int64_t T, int E, float* partial,
+                    float* probs_et, hipStream_t st) {
+  const int G = seg_lanes(E);
+  if (G == 8)
+    launch_probsum_t<8, 1>(logits, gate, T, E, partial, probs_et, st);
+  else if (G == 16)
+    launch_probsum_t<16, 1>(logits, gate, T, E, partial, probs_et, st);
+  else if (G == 32)
+    launch_probsum_t<32, 1>(logits, gate, T, E, partial, probs_et, st);
+  else if (E <= 64)
+    launch_probsum_t<64, 1>(logits, gate, T, E, partial, probs_et, st);
+  else if (E <= 128)
+    launch_probsum_t<64, 2>(logits, gate, T, E, partial, probs_et, st);
+  else if (E <= 256)
+    launch_probsum_t<64, 4>(logits, gate, T, E, partial, probs_et, st);
+  else if (E <= 512)
+    launch_probsum_t<64, 8>(logits, gate, T, E, partial, probs_et, st);
+  else
+    launch_probsum_t<64, 16>(logits, gate, T, E, partial, probs_et, st);
 }
 
 // One workgroup of 1024 threads.  Thread (sl, e) = (tid / E, tid % E) sums
@@ -146,28 +177,18 @@ __global__ __launch_bounds__(1024) void balance_final_kernel(
 hipError_t launch_load_balance(const float* logits, const int32_t* counts, int gate, int64_t T,
                                int E, int k, float alpha, float* partial, float* f, float* P,
                                float* loss, hipStream_t st) {
-  const int G = seg_lanes(E);
-  if (G == 8)
-    launch_probsum_t<8, 1>(logits, gate, T, E, partial, st);
-  else if (G == 16)
-    launch_probsum_t<16, 1>(logits, gate, T, E, partial, st);
-  else if (G == 32)
-    launch_probsum_t<32, 1>(logits, gate, T, E, partial, st);
-  else if (E <= 64)
-    launch_probsum_t<64, 1>(logits, gate, T, E, partial, st);
-  else if (E <= 128)
-    launch_probsum_t<64, 2>(logits, gate, T, E, partial, st);
-  else if (E <= 256)
-    launch_probsum_t<64, 4>(logits, gate, T, E, partial, st);
-  else if (E <= 512)
-    launch_probsum_t<64, 8>(logits, gate, T, E, partial, st);
-  else
-    launch_probsum_t<64, 16>(logits, gate, T, E, partial, st);
+  launch_probsum(logits, gate, T, E, partial, nullptr, st);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t ngroups = (T + topk_tokens_per_wg(E) - 1) / topk_tokens_per_wg(E);
   hipLaunchKernelGGL(balance_final_kernel, dim3(1), dim3(1024), 0, st, partial, ngroups, counts,
                      T, E, k, alpha, f, P, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_probs(const float* logits, int gate, int64_t T, int E, float* probs_et,
+                               hipStream_t st) {
+  launch_probsum(logits, gate, T, E, nullptr, probs_et, st);
   return hipGetLastError();
 }
 

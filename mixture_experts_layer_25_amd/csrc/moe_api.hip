@@ -45,6 +45,12 @@ int check_cfg(const moe_cfg_t* c) {
   if (c->T < 0 || c->h <= 0 || c->F <= 0 || c->E <= 0 || c->k <= 0 || c->capacity < 0)
     return MOE_ERR_INVALID_ARG;
   if (c->has_shared != 0 && c->has_shared != 1) return MOE_ERR_INVALID_ARG;
+  if (c->routing < MOE_ROUTE_TOPK || c->routing > MOE_ROUTE_EXPERT_CHOICE || c->reserved != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->routing == MOE_ROUTE_TOPK_SCORE_DROP && c->capacity <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->routing == MOE_ROUTE_EXPERT_CHOICE && c->T > 0 &&
+      (c->capacity <= 0 || c->capacity > c->T))
+    return MOE_ERR_INVALID_ARG;
   if (c->k > c->E) return MOE_ERR_INVALID_ARG;
   if (c->h % 128 != 0 || c->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (c->E > 1024 || c->k > 16 || c->E + c->has_shared > 1024) return MOE_ERR_UNSUPPORTED;
@@ -56,6 +62,9 @@ int check_cfg(const moe_cfg_t* c) {
 
 struct Layout {
   size_t logits, idx, gate, hist, base, pbal, counts, offsets, assign, rowtok, gtab;
+  // routing variants: expert choice (probs, selection rows and gates per
+  // (token, expert)); score drop (the dropless maps it ranks within)
+  size_t probs, selrow, gatete, offs_dl, gtab_dl, assign_dl, rowtok_dl, key_dl, aid_dl;
   size_t partials, xperm, act, yperm, total;
 };
 
@@ -86,6 +95,17 @@ Layout layout_of(const moe_cfg_t& c) {
   L.assign = take((size_t)(T * k) * 4);
   L.rowtok = take((size_t)rows * 4);
   L.gtab = take((size_t)gtab_ints((int)G) * 4);
+  const bool ec = c.routing == MOE_ROUTE_EXPERT_CHOICE;
+  const bool sd = c.routing == MOE_ROUTE_TOPK_SCORE_DROP;
+  L.probs = take(ec ? (size_t)(T * E) * 4 : 0);
+  L.selrow = take(ec ? (size_t)(T * E) * 4 : 0);
+  L.gatete = take(ec ? (size_t)(T * E) * 4 : 0);
+  L.offs_dl = take(sd ? (size_t)(E + 1) * 4 : 0);
+  L.gtab_dl = take(sd ? (size_t)gtab_ints((int)G) * 4 : 0);
+  L.assign_dl = take(sd ? (size_t)(T * k) * 4 : 0);
+  L.rowtok_dl = take(sd ? (size_t)(T * k) * 4 : 0);
+  L.key_dl = take(sd ? (size_t)(T * k) * 8 : 0);
+  L.aid_dl = take(sd ? (size_t)(T * k) * 4 : 0);
   L.partials = take(c.dtype == MOE_DTYPE_BF16 ? (size_t)moe::kSplitPartialFloats * 4 : 0);
   L.xperm = take((size_t)rows * ld_h(c) * es);
   L.act = take((size_t)rows_all * ld_f(c) * es);
@@ -185,6 +205,7 @@ MOE_API int moe_router_topk(const moe_cfg_t* cfg, const void* x, const void* w_r
   if (st != MOE_OK) return st;
   const moe_cfg_t& c = *cfg;
   if (c.T == 0) return MOE_OK;
+  if (c.routing == MOE_ROUTE_EXPERT_CHOICE) return MOE_ERR_UNSUPPORTED;
   if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
   if (misaligned(x, w_router, logit_bias, select_bias, logits, topk_idx, topk_gate, ws))
     return MOE_ERR_INVALID_ARG;
@@ -205,6 +226,7 @@ MOE_API int moe_permute(const moe_cfg_t* cfg, const void* x, const int32_t* topk
   if (st != MOE_OK) return st;
   const moe_cfg_t& c = *cfg;
   if (c.T == 0) return MOE_OK;
+  if (c.routing != MOE_ROUTE_TOPK) return MOE_ERR_UNSUPPORTED;
   if (!x || !topk_idx || !expert_counts || !expert_offsets || !assign_row || !row_token ||
       !x_perm)
     return MOE_ERR_INVALID_ARG;
@@ -288,8 +310,9 @@ MOE_API int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
   if (c.T == 0) return MOE_OK;
   if (!y_perm || !assign_row || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
   if (misaligned(y_perm, assign_row, topk_gate, shared_y, y)) return MOE_ERR_INVALID_ARG;
+  const int slots = c.routing == MOE_ROUTE_EXPERT_CHOICE ? c.E : c.k;
   MOE_TRY(moe::launch_combine(c.dtype, y_perm, c.h, assign_row, topk_gate, shared_y, y,
-                              c.T, c.h, c.k, (hipStream_t)stream));
+                              c.T, c.h, slots, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -320,11 +343,15 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   if (!w || !x || !y || !w->w_router || !w->w1 || !w->w3 || !w->w2)
     return MOE_ERR_INVALID_ARG;
   if (c.has_shared && (!w->ws1 || !w->ws3 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+  // expert choice ranks by router probability; a selection-only bias has
+  // no meaning there
+  if (c.routing == MOE_ROUTE_EXPERT_CHOICE && w->select_bias) return MOE_ERR_INVALID_ARG;
   if (misaligned(x, y, ws, w->w_router, w->w1, w->w3, w->w2, w->logit_bias, w->select_bias) ||
       misaligned(w->ws1, w->ws3, w->ws2))
     return MOE_ERR_INVALID_ARG;
-  if (route && misaligned(route->logits, route->topk_idx, route->topk_gate, route->expert_counts,
-                          route->expert_offsets, route->assign_row, route->row_token))
+  if (route && (misaligned(route->logits, route->topk_idx, route->topk_gate, route->expert_counts,
+                           route->expert_offsets, route->assign_row, route->row_token) ||
+                misaligned(route->probs)))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
@@ -352,21 +379,59 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
     return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
   };
 
+  const bool ec = c.routing == MOE_ROUTE_EXPERT_CHOICE;
+  // expert choice: per-(token, expert) slots
+  if (ec) {
+    gate = r.topk_gate ? r.topk_gate : at<float>(ws, L.gatete);
+    assign = r.assign_row ? r.assign_row : at<int32_t>(ws, L.selrow);
+  }
+  const int slots = ec ? c.E : c.k;
+
   MOE_TRY(mark(0));
   MOE_TRY(moe::launch_router(c.dtype, x, w->w_router, w->logit_bias, logits, c.T, c.h,
                              c.E, s));
   MOE_TRY(mark(1));
-  MOE_TRY(moe::launch_topk(logits, w->select_bias, c.gate, c.T, c.E, c.k, idx, gate,
-                           hist, s));
-  MOE_TRY(mark(2));
-  MOE_TRY(moe::launch_scan(hist, nch, c.E, c.capacity, c.T, c.k, c.has_shared, BM, base,
-                           counts, offsets, gtab, s));
-  MOE_TRY(mark(3));
-  MOE_TRY(moe::launch_assign(idx, base, hg, offsets, c.T, c.E, c.k, c.capacity, assign,
-                             rowtok, s));
-  MOE_TRY(mark(4));
-  MOE_TRY(moe::launch_permute(c.dtype, x, assign, counts, c.T, c.h, c.E, c.k, c.capacity,
-                              xperm, ld_h(c), rowtok, s));
+  if (ec) {
+    // probabilities -> each expert's C best tokens -> fixed groups -> gather
+    float* probs = r.probs ? r.probs : at<float>(ws, L.probs);
+    MOE_TRY(moe::launch_router_probs(logits, c.gate, c.T, c.E, probs, s));
+    MOE_TRY(mark(2));
+    MOE_TRY(moe::launch_expert_choice(probs, c.T, c.E, (int)c.capacity, assign, gate, rowtok, s));
+    MOE_TRY(mark(3));
+    MOE_TRY(moe::launch_fixed_groups(c.E, (int)c.capacity, c.T, c.has_shared, BM, counts, offsets,
+                                     gtab, s));
+    MOE_TRY(mark(4));
+    MOE_TRY(moe::launch_gather_rows(c.dtype, x, rowtok, rows, c.T, c.h, xperm, ld_h(c), s));
+  } else {
+    MOE_TRY(moe::launch_topk(logits, w->select_bias, c.gate, c.T, c.E, c.k, idx, gate,
+                             hist, s));
+    MOE_TRY(mark(2));
+    if (c.routing == MOE_ROUTE_TOPK_SCORE_DROP) {
+      // dropless ranks first: each expert's assignments in token order
+      int32_t* offs_dl = at<int32_t>(ws, L.offs_dl);
+      int32_t* assign_dl = at<int32_t>(ws, L.assign_dl);
+      MOE_TRY(moe::launch_scan(hist, nch, c.E, 0, c.T, c.k, c.has_shared, BM, base, counts,
+                               offs_dl, at<int32_t>(ws, L.gtab_dl), s));
+      MOE_TRY(mark(3));
+      MOE_TRY(moe::launch_assign(idx, base, hg, offs_dl, c.T, c.E, c.k, 0, assign_dl,
+                                 at<int32_t>(ws, L.rowtok_dl), s));
+      MOE_TRY(moe::launch_score_drop(idx, gate, assign_dl, offs_dl, c.T, c.E, c.k,
+                                     (int)c.capacity, at<uint64_t>(ws, L.key_dl),
+                                     at<int32_t>(ws, L.aid_dl), assign, rowtok, s));
+      // the capacity layout's counts, offsets and tile table
+      MOE_TRY(moe::launch_scan(hist, nch, c.E, c.capacity, c.T, c.k, c.has_shared, BM, base,
+                               counts, offsets, gtab, s));
+    } else {
+      MOE_TRY(moe::launch_scan(hist, nch, c.E, c.capacity, c.T, c.k, c.has_shared, BM, base,
+                               counts, offsets, gtab, s));
+      MOE_TRY(mark(3));
+      MOE_TRY(moe::launch_assign(idx, base, hg, offsets, c.T, c.E, c.k, c.capacity, assign,
+                                 rowtok, s));
+    }
+    MOE_TRY(mark(4));
+    MOE_TRY(moe::launch_permute(c.dtype, x, assign, counts, c.T, c.h, c.E, c.k, c.capacity,
+                                xperm, ld_h(c), rowtok, s));
+  }
   MOE_TRY(mark(5));
   moe::GroupedGemmArgs a{};
   a.A = xperm;
@@ -407,8 +472,8 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   MOE_TRY(mark(7));
   const void* shared_y =
       c.has_shared ? (const void*)(at<char>(yperm, (size_t)rows * ld_h(c) * esize(c))) : nullptr;
-  MOE_TRY(moe::launch_combine(c.dtype, yperm, ld_h(c), assign, gate, shared_y, y, c.T, c.h, c.k,
-                              s));
+  MOE_TRY(moe::launch_combine(c.dtype, yperm, ld_h(c), assign, gate, shared_y, y, c.T, c.h,
+                              slots, s));
   MOE_TRY(mark(8));
   return MOE_OK;
 }

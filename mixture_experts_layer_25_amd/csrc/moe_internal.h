@@ -54,12 +54,32 @@ hipError_t launch_router(int dtype, const void* x, const void* w_router,
 // divisor of 256.
 inline int topk_tokens_per_wg(int E) { return 4 * 256 / seg_lanes(E); }
 
+// Routing variants (choice.hip, route_scan.hip).  Expert choice: expert e
+// takes its C best tokens by probs_et[e][t]; sel_row/gate_te [T,E],
+// row_token [E*C].  Score drop: from the dropless rows (assign_dl,
+// offsets_dl) of a top-k routing, expert e keeps its C largest gates;
+// key_dl/aid_dl [T*k] scratch, assign_row [T*k], row_token [E*C] (kept
+// rows only).
+hipError_t launch_expert_choice(const float* probs_et, int64_t T, int E, int C, int32_t* sel_row,
+                                float* gate_te, int32_t* row_token, hipStream_t s);
+hipError_t launch_score_drop(const int32_t* idx, const float* gate, const int32_t* assign_dl,
+                             const int32_t* offsets_dl, int64_t T, int E, int k, int C,
+                             uint64_t* key_dl, int32_t* aid_dl, int32_t* assign_row,
+                             int32_t* row_token, hipStream_t s);
+hipError_t launch_fixed_groups(int E, int C, int64_t T, int has_shared, int BM, int32_t* counts,
+                               int32_t* offsets, int32_t* gtab, hipStream_t s);
+hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token, int64_t rows,
+                              int64_t T, int h, void* x_perm, int ld_perm, hipStream_t s);
+
 // Router distribution summed per expert over token groups (partial:
 // [ceil(T / topk_tokens_per_wg(E))][E] floats), then f, P and the Switch
 // loss (one workgroup).
 hipError_t launch_load_balance(const float* logits, const int32_t* counts, int gate, int64_t T,
                                int E, int k, float alpha, float* partial, float* f, float* P,
                                float* loss, hipStream_t st);
+// The router distribution itself, written transposed: probs_et [E,T].
+hipError_t launch_router_probs(const float* logits, int gate, int64_t T, int E, float* probs_et,
+                               hipStream_t st);
 
 hipError_t launch_topk(const float* logits, const float* select_bias,
                        int gate, int64_t T, int E, int k, int32_t* idx,

@@ -310,7 +310,72 @@ __global__ __launch_bounds__(256) void permute_kernel(
   }
 }
 
+// Expert choice: every routed group holds exactly C rows (e*C ..), plus
+// the shared group (T rows, read from x) when there is one.  One workgroup
+// of 1024 threads.
+__global__ __launch_bounds__(1024) void fixed_groups_kernel(int E, int C, int64_t T,
+                                                            int has_shared, int BM,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ gtab) {
+  __shared__ int tmp[32];
+  const int e = threadIdx.x;
+  if (e < E) {
+    counts[e] = C;
+    offsets[e] = e * C;
+  }
+  if (e == 0) offsets[E] = E * C;
+  const int G = E + (has_shared ? 1 : 0);
+  int valid = 0, a0 = 0, o0 = 0;
+  if (e < E) {
+    valid = C;
+    a0 = o0 = e * C;
+  } else if (e == E && has_shared) {
+    valid = (int)T;
+    a0 = 0;
+    o0 = E * C;
+  }
+  write_gtab(e, G, valid, a0, o0, BM, tmp, gtab);
+}
+
+// x_perm[r] = x[row_token[r]] for every row (expert choice fills each
+// expert's C rows), kPermTok rows per workgroup, 16-byte vectors.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
+                                                          const int32_t* __restrict__ row_token,
+                                                          int64_t rows, int64_t T, int nv,
+                                                          uint4* __restrict__ x_perm, int64_t pv) {
+  for (int rr = 0; rr < kPermTok; ++rr) {
+    const int64_t r = (int64_t)blockIdx.x * kPermTok + rr;
+    if (r >= rows) return;
+    const int64_t t = row_token[r];
+    uint4* dst = x_perm + r * pv;
+    if ((uint64_t)t >= (uint64_t)T) {   // no token: a zero row
+      for (int v = threadIdx.x; v < nv; v += 256) dst[v] = uint4{0u, 0u, 0u, 0u};
+      continue;
+    }
+    const uint4* src = x + t * nv;
+    for (int v = threadIdx.x; v < nv; v += 256) dst[v] = src[v];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fixed_groups(int E, int C, int64_t T, int has_shared, int BM, int32_t* counts,
+                               int32_t* offsets, int32_t* gtab, hipStream_t s) {
+  hipLaunchKernelGGL(fixed_groups_kernel, dim3(1), dim3(1024), 0, s, E, C, T, has_shared, BM,
+                     counts, offsets, gtab);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token, int64_t rows,
+                              int64_t T, int h, void* x_perm, int ld_perm, hipStream_t s) {
+  const int esz = dtype == 1 ? 2 : 4;
+  const int64_t nb = (rows + kPermTok - 1) / kPermTok;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)nb), dim3(256), 0, s, (const uint4*)x,
+                     row_token, rows, T, h * esz / 16, (uint4*)x_perm,
+                     (int64_t)ld_perm * esz / 16);
+  return hipGetLastError();
+}
 
 hipError_t launch_hist(const int32_t* idx, int64_t T, int E, int k,
                        int32_t* chunk_hist, hipStream_t s) {

@@ -256,7 +256,8 @@ def swiglu_ffn(xrows, w1, w3, w2) -> np.ndarray:
 # ---------------------------------------------------------------------------
 def moe_forward(x, w_router, w1, w3, w2, *, k: int, gate: str,
                 C: Optional[int] = None, logit_bias=None, select_bias=None,
-                shared=None, tokens=None, idx=None, maps_only=False) -> dict:
+                shared=None, tokens=None, idx=None, maps_only=False,
+                drop: str = "token", priority=None) -> dict:
     """Reference forward.
 
     x [T,h]; w_router [E,h]; w1, w3 [E,F,h]; w2 [E,h,F] (any array-likes of
@@ -264,7 +265,11 @@ def moe_forward(x, w_router, w1, w3, w2, *, k: int, gate: str,
     ``tokens``: optional 1-D array of token ids whose outputs are computed
     (routing, ranks and drops still cover all T tokens).  ``idx``: optional
     externally chosen top-k (used to recompute maps from another selection);
-    when given, gates still come from this oracle's logits.
+    when given, gates still come from this oracle's logits.  ``drop``: with
+    a capacity, "token" keeps the first C assignments of an expert in token
+    order, "score" the C with the largest gate (route_maps_score_drop),
+    deciding on ``priority`` [T,k] fp32 when given (e.g. the device's own
+    gates) and on this oracle's gates otherwise.
     Returns logits, keys, idx, gates, near_tie, maps, and ``y`` (fp64) for the
     requested tokens, in the order of ``tokens``.
     """
@@ -277,7 +282,14 @@ def moe_forward(x, w_router, w1, w3, w2, *, k: int, gate: str,
         idx = topk(keys, k)
     idx = np.asarray(idx).astype(np.int32)
     g = gates(logits, idx, gate)
-    maps = route_maps(idx, E, C)
+    if drop == "score":
+        if C is None:
+            raise ValueError("the score drop needs a capacity")
+        maps = route_maps_score_drop(idx, g if priority is None else priority, E, C)
+    elif drop == "token":
+        maps = route_maps(idx, E, C)
+    else:
+        raise ValueError(f"unknown drop rule {drop!r}")
     out = {"logits": logits, "keys": keys, "idx": idx, "gates": g,
            "near_tie": near_tie(keys, k), "maps": maps}
     if maps_only:

@@ -41,26 +41,30 @@ def capacity_of(cfg: MoEConfig):
     return c_lib, c_ref
 
 
-def lib_cfg(cfg: MoEConfig, C: int):
+def lib_cfg(cfg: MoEConfig, C: int, routing: str = "topk"):
     return moe.make_cfg(cfg.T, cfg.h, cfg.F, cfg.E, cfg.k, cfg.dtype, cfg.gate,
-                        capacity=C, has_shared=cfg.shared)
+                        capacity=C, has_shared=cfg.shared, routing=routing)
 
 
-def run_forward(cfg: MoEConfig, inp: dict, C: int) -> dict:
-    """moe_forward with every routing output requested; tensors stay on GPU."""
-    c = lib_cfg(cfg, C)
+def run_forward(cfg: MoEConfig, inp: dict, C: int, routing: str = "topk") -> dict:
+    """moe_forward with every routing output requested; tensors stay on GPU.
+    With expert choice the per-token slots are the E experts."""
+    c = lib_cfg(cfg, C, routing)
     T, E, k, h = cfg.T, cfg.E, cfg.k, cfg.h
+    slots = E if routing == "expert_choice" else k
     rows = moe.moe_num_rows(c)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     route = {
         "logits": torch.empty((T, E), dtype=torch.float32, device=DEV),
         "topk_idx": torch.empty((T, k), dtype=torch.int32, device=DEV),
-        "topk_gate": torch.empty((T, k), dtype=torch.float32, device=DEV),
+        "topk_gate": torch.empty((T, slots), dtype=torch.float32, device=DEV),
         "expert_counts": torch.empty((E,), dtype=torch.int32, device=DEV),
         "expert_offsets": torch.empty((E + 1,), dtype=torch.int32, device=DEV),
-        "assign_row": torch.empty((T * k,), dtype=torch.int32, device=DEV),
+        "assign_row": torch.empty((T * slots,), dtype=torch.int32, device=DEV),
         "row_token": torch.empty((rows,), dtype=torch.int32, device=DEV),
     }
+    if routing == "expert_choice":
+        route["probs"] = torch.empty((E, T), dtype=torch.float32, device=DEV)
     # fill outputs with garbage so that an unwritten entry shows up
     for v in route.values():
         v.fill_(-7)
@@ -77,8 +81,18 @@ def run_forward(cfg: MoEConfig, inp: dict, C: int) -> dict:
     return out
 
 
+def oracle_weights(cfg: MoEConfig, inp: dict):
+    """(x, w_router, w1, w3, w2, logit_bias, shared) as the oracle takes them."""
+    lb = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
+    shared = None
+    if cfg.shared:
+        shared = (np32(inp["ws1"]), np32(inp["ws3"]), np32(inp["ws2"]))
+    return (np32(inp["x"]), np32(inp["w_router"]), LazyExperts(inp["w1"]),
+            LazyExperts(inp["w3"]), LazyExperts(inp["w2"]), lb, shared)
+
+
 def oracle_forward(cfg: MoEConfig, inp: dict, C_ref, tokens=None, idx=None,
-                   maps_only=False):
+                   maps_only=False, drop="token", priority=None):
     x = np32(inp["x"])
     wr = np32(inp["w_router"])
     lb = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
@@ -91,11 +105,14 @@ def oracle_forward(cfg: MoEConfig, inp: dict, C_ref, tokens=None, idx=None,
     w2 = LazyExperts(inp["w2"]) if inp["w2"] is not None else None
     return oracle.moe_forward(x, wr, w1, w3, w2, k=cfg.k, gate=cfg.gate, C=C_ref,
                               logit_bias=lb, select_bias=sb, shared=shared,
-                              tokens=tokens, idx=idx, maps_only=maps_only)
+                              tokens=tokens, idx=idx, maps_only=maps_only, drop=drop,
+                              priority=priority)
 
 
-def check_routing(cfg: MoEConfig, gpu: dict, ref: dict, C_ref, inp: dict) -> dict:
-    """Routing checks; returns a small report."""
+def check_routing(cfg: MoEConfig, gpu: dict, ref: dict, C_ref, inp: dict,
+                  drop: str = "token") -> dict:
+    """Routing checks; returns a small report.  drop="score": the capacity
+    maps are the score-priority ones, decided on the GPU's own gates."""
     g_logits = gpu["logits"].cpu().numpy()
     g_idx = gpu["topk_idx"].cpu().numpy()
     g_gate = gpu["topk_gate"].cpu().numpy()
@@ -120,7 +137,10 @@ def check_routing(cfg: MoEConfig, gpu: dict, ref: dict, C_ref, inp: dict) -> dic
     dg = float(np.abs(g_gate - g_ref).max())
     assert dg <= 2e-6, f"gates differ by {dg}"
     # 4. maps recomputed by the oracle from the GPU's selection: bit-exact
-    m = oracle.route_maps(g_idx, cfg.E, C_ref)
+    if drop == "score":
+        m = oracle.route_maps_score_drop(g_idx, g_gate, cfg.E, C_ref)
+    else:
+        m = oracle.route_maps(g_idx, cfg.E, C_ref)
     np.testing.assert_array_equal(gpu["expert_counts"].cpu().numpy(), m["counts"])
     np.testing.assert_array_equal(gpu["expert_offsets"].cpu().numpy(), m["offsets"])
     np.testing.assert_array_equal(gpu["assign_row"].cpu().numpy().reshape(-1, cfg.k),

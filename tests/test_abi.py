@@ -38,9 +38,10 @@ def test_struct_layouts_match_header(tmp_path):
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
         "int main(void){\n"
-        'printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_cfg_t), offsetof(moe_cfg_t, T),'
+        'printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_cfg_t), offsetof(moe_cfg_t, T),'
         " offsetof(moe_cfg_t, gate), offsetof(moe_cfg_t, capacity), sizeof(moe_weights_t),"
-        " sizeof(moe_route_out_t), offsetof(moe_weights_t, ws2));\n"
+        " sizeof(moe_route_out_t), offsetof(moe_weights_t, ws2), offsetof(moe_cfg_t, routing),"
+        " offsetof(moe_route_out_t, probs));\n"
         'printf("%d %d\\n", MOE_NUM_STAGES, MOE_NUM_EVENTS);\n'
         "return 0;}\n")
     exe = tmp_path / "layout"
@@ -49,7 +50,8 @@ def test_struct_layouts_match_header(tmp_path):
     c = [int(v) for v in lines[0].split()]
     py = [ctypes.sizeof(moe.MoECfg), moe.MoECfg.T.offset, moe.MoECfg.gate.offset,
           moe.MoECfg.capacity.offset, ctypes.sizeof(moe.MoEWeights),
-          ctypes.sizeof(moe.MoERouteOut), moe.MoEWeights.ws2.offset]
+          ctypes.sizeof(moe.MoERouteOut), moe.MoEWeights.ws2.offset, moe.MoECfg.routing.offset,
+          moe.MoERouteOut.probs.offset]
     assert c == py
     assert [int(v) for v in lines[1].split()] == [moe.MOE_NUM_STAGES, moe.MOE_NUM_EVENTS]
 

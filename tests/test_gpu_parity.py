@@ -16,7 +16,7 @@ import torch
 import mixture_experts_layer_25_amd as moe
 import oracle
 from helpers import (DEV, LazyExperts, capacity_of, check_routing, gen_inputs, lib_cfg, np32,
-                     oracle_forward, rel_err, run_forward, tol_of)
+                     oracle_forward, oracle_weights, rel_err, run_forward, tol_of)
 from moe_inputs import CONFIGS, MoEConfig
 
 pytestmark = pytest.mark.gpu
@@ -78,6 +78,90 @@ def test_forward_matches_oracle(cfg):
     assert np.isfinite(y).all()
     err = rel_err(y, ref_y)
     _report(cfg.name, rel_err=f"{err:.2e}", **rep)
+    assert err <= tol_of(cfg)
+
+
+# ------------------------------------------------------------ routing variants
+SCORE_DROP = ["capacity_heavy_drop", "zipf_cf1", "worked_example_small",
+              "split_k_tail_capacity_shared", "f32_capacity"]
+
+
+@pytest.mark.parametrize("name", SCORE_DROP)
+def test_score_drop_matches_oracle(name):
+    """Capacity drop by gate score: maps bit-exact against the oracle's
+    score-priority maps decided on the GPU's own gates; every output row
+    against the oracle's layer with those maps."""
+    cfg = next(c for c in MEDIUM if c.name == name)
+    print(f"[case] score drop {name}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    gpu = run_forward(cfg, inp, C_lib, routing="topk_score_drop")
+    g_idx = gpu["topk_idx"].cpu().numpy()
+    g_gate = gpu["topk_gate"].cpu().numpy()
+    ref = oracle_forward(cfg, inp, C_ref, idx=g_idx, drop="score", priority=g_gate)
+    rep = check_routing(cfg, gpu, ref, C_ref, inp, drop="score")
+    token_order = oracle.route_maps(g_idx, cfg.E, C_ref)["assign_row"]
+    changed = int((token_order != ref["maps"]["assign_row"]).sum())
+    err = rel_err(np32(gpu["y"]), ref["y"])
+    _report(f"score_drop_{name}", rel_err=f"{err:.2e}", rows_moved=changed, **rep)
+    assert err <= tol_of(cfg)
+
+
+def test_score_drop_with_equal_gates_is_token_order():
+    """k = 1 with softmax over the selected expert: every gate is 1.0, so the
+    score-priority drop keeps exactly the token-order assignments."""
+    cfg = MoEConfig("k1_capacity", T=500, h=256, E=8, k=1, F=256, gate="softmax_topk",
+                    cf=(1, 2))
+    inp = gen_inputs(cfg)
+    C_lib, _ = capacity_of(cfg)
+    a = run_forward(cfg, inp, C_lib, routing="topk_score_drop")
+    b = run_forward(cfg, inp, C_lib, routing="topk")
+    for key in ("assign_row", "row_token", "expert_counts", "expert_offsets"):
+        assert torch.equal(a[key], b[key]), key
+    assert torch.equal(a["y"].view(torch.int16), b["y"].view(torch.int16))
+
+
+EXPERT_CHOICE = [
+    MoEConfig("ec_softmax", T=1000, h=256, E=8, k=2, F=256, gate="softmax_topk", cf=(1, 1)),
+    MoEConfig("ec_sigmoid_shared", T=700, h=256, E=16, k=4, F=256, gate="sigmoid_topk_norm",
+              shared=True, cf=(1, 1)),
+    MoEConfig("ec_e256", T=300, h=256, E=256, k=8, F=128, gate="softmax_all_topk", cf=(1, 1)),
+    MoEConfig("ec_e40_ragged_f32", T=333, h=128, E=40, k=3, F=128, dtype="f32",
+              gate="softmax_topk", cf=(1, 1)),
+    MoEConfig("ec_all_tokens", T=200, h=128, E=4, k=4, F=128, gate="softmax_all_topk",
+              cf=(1, 1)),
+    MoEConfig("ec_zipf", T=2048, h=256, E=64, k=4, F=128, logit_bias=("zipf", 1.2), cf=(1, 1)),
+]
+
+
+@pytest.mark.parametrize("cfg", EXPERT_CHOICE, ids=lambda c: c.name)
+def test_expert_choice_matches_oracle(cfg):
+    """Expert-choice routing: probabilities against the oracle's on the GPU's
+    logits; selection, rows and gates bit-exact against the oracle deciding on
+    the GPU's own probabilities; the layer output against the oracle's."""
+    print(f"[case] expert choice {cfg.name}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    assert 0 < C_lib <= cfg.T
+    gpu = run_forward(cfg, inp, C_lib, routing="expert_choice")
+    T, E = cfg.T, cfg.E
+    g_logits = gpu["logits"].cpu().numpy()
+    scores = gpu["probs"].cpu().numpy().T          # [T,E]
+    dp = float(np.abs(scores - oracle.router_probs(g_logits, cfg.gate)).max())
+    assert dp <= 1e-6, dp
+    m = oracle.expert_choice(g_logits, C_ref, cfg.gate, scores=scores)
+    np.testing.assert_array_equal(gpu["assign_row"].cpu().numpy().reshape(T, E), m["sel_row"])
+    np.testing.assert_array_equal(gpu["topk_gate"].cpu().numpy(), m["gate"])
+    np.testing.assert_array_equal(gpu["row_token"].cpu().numpy(), m["row_token"])
+    np.testing.assert_array_equal(gpu["expert_counts"].cpu().numpy(), m["counts"])
+    np.testing.assert_array_equal(gpu["expert_offsets"].cpu().numpy(), m["offsets"])
+    x, wr, w1, w3, w2, lb, shared = oracle_weights(cfg, inp)
+    ref = oracle.expert_choice_forward(x, wr, w1, w3, w2, C=C_ref, gate=cfg.gate, logit_bias=lb,
+                                       shared=shared, scores=scores)
+    err = rel_err(np32(gpu["y"]), ref["y"])
+    per_token = (m["sel_row"] >= 0).sum(1)
+    _report(f"expert_choice_{cfg.name}", rel_err=f"{err:.2e}", max_dprob=f"{dp:.1e}", C=C_lib,
+            unrouted_tokens=int((per_token == 0).sum()), max_experts_per_token=int(per_token.max()))
     assert err <= tol_of(cfg)
 
 
