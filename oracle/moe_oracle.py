@@ -22,7 +22,9 @@ no permutation buffer, no blocking and no fusion:
    assignments per expert, the router's mean probability per expert and the
    Switch auxiliary loss built from them;
 8. two routing variants: capacity drops by gate score instead of token
-   order, and expert choice (every expert takes its C best-scoring tokens).
+   order, and expert choice (every expert takes its C best-scoring tokens);
+9. the backward of the layer: gradients of sum(y * dy) with respect to the
+   input, the router and every expert weight, with the routing held fixed.
 
 Sources (pages and the part of each that is followed):
 
@@ -441,3 +443,109 @@ def expert_choice_forward(x, w_router, w1, w3, w2, *, C: int, gate: str, logit_b
         y += swiglu_ffn(xs, ws1, ws3, ws2)
     m.update({"logits": logits, "y": y, "tokens": tok})
     return m
+
+
+# ---------------------------------------------------------------------------
+# 9. Backward.  专家并行 page, "EP+DP" BWD: every GPU computes the gradients
+# of its experts' weights, and the gradients go back along the routing path
+# (the reverse all-to-all) into the layers before; Megatron-LM part 6, "MoE
+# 层的数据流" (the same chain, reversed).  This is the gradient of the
+# forward above by the chain rule, in fp64, with the top-k choice and the
+# capacity drops held fixed (they are not differentiable): a dropped slot
+# passes no gradient, the selection-only bias gets none.
+# ---------------------------------------------------------------------------
+def _gates_backward(l, idx, dg, mode: str) -> np.ndarray:
+    """dL/dlogits [T,E] from dL/dgates [T,k] (fp64), for the gate modes of
+    gates()."""
+    T, E = l.shape
+    dl = np.zeros((T, E))
+    rows = np.arange(T)[:, None]
+    if mode == "softmax_topk":
+        sel = np.take_along_axis(l, idx, axis=1)
+        ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+        g = ex / ex.sum(axis=1, keepdims=True)
+        dsel = g * (dg - (g * dg).sum(axis=1, keepdims=True))
+        np.add.at(dl, (rows, idx), dsel)
+    elif mode == "softmax_all_topk":
+        ex = np.exp(l - l.max(axis=1, keepdims=True))
+        p = ex / ex.sum(axis=1, keepdims=True)
+        dp = np.zeros((T, E))
+        np.add.at(dp, (rows, idx), dg)
+        dl = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    elif mode == "sigmoid_topk_norm":
+        sel = np.take_along_axis(l, idx, axis=1)
+        sg = 1.0 / (1.0 + np.exp(-sel))
+        S = sg.sum(axis=1, keepdims=True)
+        g = sg / S
+        ds = (dg - (g * dg).sum(axis=1, keepdims=True)) / S
+        np.add.at(dl, (rows, idx), ds * sg * (1.0 - sg))
+    else:
+        raise ValueError(f"unknown gate mode {mode!r}")
+    return dl
+
+
+def _ffn_backward(xr, dO, w1, w3, w2):
+    """SwiGLU expert on rows xr with output gradient dO: returns the expert
+    output o, dx, dw1, dw3, dw2 (fp64)."""
+    W1, W3, W2 = _f64(w1), _f64(w3), _f64(w2)
+    a1 = xr @ W1.T
+    a3 = xr @ W3.T
+    s = 1.0 / (1.0 + np.exp(-a1))
+    u = a1 * s * a3
+    o = u @ W2.T
+    dW2 = dO.T @ u
+    dU = dO @ W2
+    dA1 = dU * a3 * (s + a1 * s * (1.0 - s))     # d silu(z)/dz = s + z s (1 - s)
+    dA3 = dU * a1 * s
+    return o, dA1 @ W1 + dA3 @ W3, dA1.T @ xr, dA3.T @ xr, dW2
+
+
+def moe_backward(x, w_router, w1, w3, w2, dy, *, k: int, gate: str, C: Optional[int] = None,
+                 logit_bias=None, select_bias=None, shared=None, idx=None,
+                 drop: str = "token", priority=None) -> dict:
+    """Gradients of L = sum(y * dy) for the layer forward (same arguments as
+    moe_forward; ``idx``/``priority`` fix the routing to another choice).
+    Returns fp64 dx [T,h], dw_router [E,h], dlogit_bias [E], dw1/dw3 [E,F,h],
+    dw2 [E,h,F], dws1/dws3/dws2 (shared expert), dgate [T,k], dlogits [T,E]."""
+    x = np.asarray(x)
+    T, h = x.shape
+    E = np.asarray(w_router).shape[0]
+    fwd = moe_forward(x, w_router, w1, w3, w2, k=k, gate=gate, C=C, logit_bias=logit_bias,
+                      select_bias=select_bias, idx=idx, maps_only=True, drop=drop,
+                      priority=priority)
+    l = _f64(fwd["logits"])
+    idx = fwd["idx"].astype(np.int64)
+    kept = fwd["maps"]["assign_row"] >= 0
+    g = _f64(fwd["gates"])
+    xs = _f64(x)
+    dY = _f64(dy)
+    dx = np.zeros((T, h))
+    dg = np.zeros((T, k))
+    dw1 = [None] * E
+    dw3 = [None] * E
+    dw2 = [None] * E
+    for e in range(E):
+        tt, jj = np.nonzero((idx == e) & kept)
+        if len(tt) == 0:
+            F = np.asarray(w1[e]).shape[0]
+            dw1[e] = np.zeros((F, h))
+            dw3[e] = np.zeros((F, h))
+            dw2[e] = np.zeros((h, F))
+            continue
+        dO = g[tt, jj][:, None] * dY[tt]
+        o, dxe, dw1[e], dw3[e], dw2[e] = _ffn_backward(xs[tt], dO, w1[e], w3[e], w2[e])
+        dg[tt, jj] = (dY[tt] * o).sum(axis=1)
+        np.add.at(dx, tt, dxe)
+    out = {"dw1": np.stack(dw1), "dw3": np.stack(dw3), "dw2": np.stack(dw2), "dgate": dg}
+    if shared is not None:
+        ws1, ws3, ws2 = shared
+        _, dxs, out["dws1"], out["dws3"], out["dws2"] = _ffn_backward(xs, dY, ws1, ws3, ws2)
+        dx += dxs
+    dl = _gates_backward(l, idx, dg, gate)
+    out["dlogits"] = dl
+    out["dlogit_bias"] = dl.sum(axis=0)
+    out["dw_router"] = dl.T @ xs
+    out["dx"] = dx + dl @ _f64(w_router)
+    out["idx"] = idx
+    out["maps"] = fwd["maps"]
+    return out

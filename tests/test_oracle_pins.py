@@ -516,3 +516,79 @@ def test_expert_choice_all_tokens_is_dense_soft_mixture():
     tc = oracle.moe_forward(x, wr, w1, w3, w2, k=E, gate="softmax_all_topk")
     # the same gate values reach each expert output; sums differ only by order
     np.testing.assert_allclose(ec["y"], tc["y"], rtol=1e-6, atol=1e-7)
+
+
+# ------------------------------------------------------------------- backward
+def _tiny_layer(seed, shared=False, T=6, h=5, E=3, F=4):
+    rng = np.random.default_rng(seed)
+    p = {"x": rng.normal(0, 1, (T, h)), "w_router": rng.normal(0, 1.0, (E, h)),
+         "w1": rng.normal(0, 0.5, (E, F, h)), "w3": rng.normal(0, 0.5, (E, F, h)),
+         "w2": rng.normal(0, 0.5, (E, h, F)), "logit_bias": rng.normal(0, 0.3, E)}
+    if shared:
+        p["ws1"] = rng.normal(0, 0.5, (F, h))
+        p["ws3"] = rng.normal(0, 0.5, (F, h))
+        p["ws2"] = rng.normal(0, 0.5, (h, F))
+    dy = rng.normal(0, 1, (T, h))
+    return p, dy
+
+
+def _loss(p, dy, **kw):
+    sh = (p["ws1"], p["ws3"], p["ws2"]) if "ws1" in p else None
+    y = oracle.moe_forward(p["x"], p["w_router"], p["w1"], p["w3"], p["w2"],
+                           logit_bias=p["logit_bias"], shared=sh, **kw)["y"]
+    return float((y * dy).sum())
+
+
+@pytest.mark.parametrize("gate,C,drop,shared", [
+    ("softmax_topk", None, "token", False),
+    ("softmax_all_topk", 3, "token", False),
+    ("sigmoid_topk_norm", None, "token", True),
+    ("softmax_topk", 3, "score", False),
+])
+def test_backward_matches_finite_differences(gate, C, drop, shared):
+    """Every gradient of the oracle's backward against central differences
+    of sum(y * dy) through the oracle's forward, on a tiny layer whose
+    top-k choice and drops do not move under the perturbation."""
+    kw = dict(k=2, gate=gate, C=C, drop=drop)
+    for seed in range(11, 60):       # first layer whose top-2 keys are well apart
+        p, dy = _tiny_layer(seed, shared)
+        fwd = oracle.moe_forward(p["x"], p["w_router"], p["w1"], p["w3"], p["w2"],
+                                 logit_bias=p["logit_bias"], maps_only=True, **kw)
+        srt = -np.sort(-fwd["keys"].astype(np.float64), axis=1)
+        if (srt[:, 1] - srt[:, 2]).min() > 0.02:          # routing stays put
+            break
+    else:
+        raise AssertionError("no well-separated layer")
+    sh = (p["ws1"], p["ws3"], p["ws2"]) if shared else None
+    g = oracle.moe_backward(p["x"], p["w_router"], p["w1"], p["w3"], p["w2"], dy,
+                            logit_bias=p["logit_bias"], shared=sh, **kw)
+    if C is not None:
+        assert (g["maps"]["assign_row"] < 0).any()          # the drop path is exercised
+    names = {"x": "dx", "w_router": "dw_router", "w1": "dw1", "w3": "dw3", "w2": "dw2",
+             "logit_bias": "dlogit_bias"}
+    if shared:
+        names.update({"ws1": "dws1", "ws3": "dws3", "ws2": "dws2"})
+    eps = 1e-3
+    for name, gname in names.items():
+        grad = g[gname]
+        fd = np.zeros_like(grad)
+        for i in np.ndindex(grad.shape):
+            old = p[name][i]
+            p[name][i] = old + eps
+            lp = _loss(p, dy, **kw)
+            p[name][i] = old - eps
+            lm = _loss(p, dy, **kw)
+            p[name][i] = old
+            fd[i] = (lp - lm) / (2 * eps)
+        scale = max(1.0, float(np.abs(fd).max()))
+        assert float(np.abs(fd - grad).max()) <= 2e-3 * scale, name
+
+
+def test_backward_gate_gradient_is_the_output_dot():
+    """k = 1 with softmax over the selected expert: the gate is 1 whatever
+    the logits, so the router gets no gradient at all."""
+    p, dy = _tiny_layer(12)
+    g = oracle.moe_backward(p["x"], p["w_router"], p["w1"], p["w3"], p["w2"], dy, k=1,
+                            gate="softmax_topk", logit_bias=p["logit_bias"])
+    assert np.abs(g["dlogits"]).max() == 0.0
+    assert np.abs(g["dw_router"]).max() == 0.0
