@@ -158,6 +158,20 @@ typedef struct moe_route_out {
   float* probs;            /* [E,T] expert choice only */
 } moe_route_out_t;
 
+/* Gradients written by moe_backward (device pointers in a host struct). */
+typedef struct moe_grads {
+  void* dx;            /* [T,h] dtype, required */
+  void* dw_router;     /* [E,h] dtype, or NULL (not computed) */
+  float* dlogit_bias;  /* [E] fp32, or NULL */
+  void* dw1;           /* [E,F,h] dtype, required */
+  void* dw3;           /* [E,F,h] dtype, required */
+  void* dw2;           /* [E,h,F] dtype, required */
+  void* dws1;          /* shared expert [F,h], required iff has_shared */
+  void* dws3;          /* [F,h] */
+  void* dws2;          /* [h,F] */
+  float* dgate;        /* [T,k] fp32 dL/dgate, or NULL (kept in the workspace) */
+} moe_grads_t;
+
 /* Host-only helpers (no device work, callable without a GPU). ---------- */
 
 /* Static string for a status code. */
@@ -258,6 +272,33 @@ int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
 int moe_load_balance(const moe_cfg_t* cfg, const float* logits,
                      const int32_t* expert_counts, float alpha, float* f, float* P,
                      float* aux_loss, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the layer -------------------------------------------------
+ * 专家并行 page, "EP+DP" BWD (each GPU computes its experts' weight
+ * gradients; the gradients go back along the routing path) and Megatron-LM
+ * part 6, "MoE 层的数据流" (the same chain, reversed).  Gradients of
+ * L = sum(y * dy) with the routing of a moe_forward call held fixed (the
+ * top-k choice and capacity drops are not differentiated; a dropped slot
+ * passes nothing back; select_bias gets no gradient):
+ *   per kept slot (t, j) of expert e:  dO = g[t,j] dy[t],  dg[t,j] = dy[t].o,
+ *   SwiGLU and expert weights by the chain rule, the gate mode's Jacobian
+ *   from dg to the logits dl, dw_router = dl^T x, dlogit_bias = sum_t dl,
+ *   dx = (sum over the kept slots of the expert's input gradient) + the
+ *   shared expert's + dl w_router.
+ * The expert activations are recomputed from x (one grouped GEMM for
+ * [a1 | a3], one for the expert outputs), so nothing of the forward's
+ * workspace is needed.
+ *   route    the routing outputs of the forward: logits, topk_idx, topk_gate,
+ *            expert_counts, expert_offsets, assign_row (all required)
+ *   dy [T,h] dtype in;  grads  see moe_grads_t.
+ * bf16 layers and the TOPK / TOPK_SCORE_DROP routings only (else
+ * MOE_ERR_UNSUPPORTED).  Gradient sums in fp32; dx, weight gradients and the
+ * intermediates (a1, a3, u, dO, dU, dA, dx_perm) stored as bf16.  Every sum
+ * has a fixed order: the same bits on every run.                          */
+int moe_backward_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes);
+int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
+                 const void* dy, const moe_route_out_t* route, const moe_grads_t* grads,
+                 void* ws, size_t ws_bytes, void* stream);
 
 /* The fused layer: stages 1-4 (+ the shared expert as one more group of
  * the grouped GEMM) on one stream, no host synchronisation.

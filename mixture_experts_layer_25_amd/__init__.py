@@ -54,7 +54,8 @@ ROUTING_BY_NAME = {
 ABI_SYMBOLS = (
     "moe_strerror", "moe_capacity", "moe_num_rows", "moe_workspace_bytes",
     "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu",
-    "moe_unpermute_combine", "moe_load_balance", "moe_forward",
+    "moe_unpermute_combine", "moe_load_balance", "moe_backward_workspace_bytes",
+    "moe_backward", "moe_forward",
 )
 
 
@@ -84,6 +85,12 @@ class MoERouteOut(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_idx", "topk_gate", "expert_counts", "expert_offsets",
         "assign_row", "row_token", "probs")]
+
+
+class MoEGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "dx", "dw_router", "dlogit_bias", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2",
+        "dgate")]
 
 
 class MoEError(RuntimeError):
@@ -117,6 +124,10 @@ def lib() -> ctypes.CDLL:
             "moe_unpermute_combine": (ctypes.c_int, [cfgp, P, P, P, P, P, P]),
             "moe_load_balance": (ctypes.c_int, [cfgp, P, P, ctypes.c_float, P, P, P, P, SZ,
                                                 P]),
+            "moe_backward_workspace_bytes": (ctypes.c_int, [cfgp, ctypes.POINTER(SZ)]),
+            "moe_backward": (ctypes.c_int, [cfgp, ctypes.POINTER(MoEWeights), P, P,
+                                            ctypes.POINTER(MoERouteOut),
+                                            ctypes.POINTER(MoEGrads), P, SZ, P]),
             "moe_forward": (ctypes.c_int, [cfgp, ctypes.POINTER(MoEWeights), P, P,
                                            ctypes.POINTER(MoERouteOut), P, SZ, P, P]),
         }
@@ -231,6 +242,28 @@ def moe_load_balance(cfg, logits, expert_counts, alpha: float, f, P, aux_loss, w
     _check("moe_load_balance", lib().moe_load_balance(
         ctypes.byref(cfg), _ptr(logits), _ptr(expert_counts), float(alpha), _ptr(f), _ptr(P),
         _ptr(aux_loss), wp, wb, _stream(stream)))
+
+
+def moe_backward_workspace_bytes(cfg: MoECfg) -> int:
+    out = ctypes.c_size_t()
+    _check("moe_backward_workspace_bytes",
+           lib().moe_backward_workspace_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def moe_backward(cfg, weights: dict, x, dy, route: dict, grads: dict, ws, stream=None) -> None:
+    """Gradients of sum(y * dy) with the routing of a forward call held
+    fixed.  ``route``: that call's logits, topk_idx, topk_gate,
+    expert_counts, expert_offsets and assign_row; ``grads``: dict of output
+    tensors (dx, dw1, dw3, dw2 required; dw_router, dlogit_bias, dgate and
+    the shared expert's dws1/dws3/dws2 as needed)."""
+    wp, wb = _ws(ws)
+    g = MoEGrads()
+    for name, _ in MoEGrads._fields_:
+        setattr(g, name, _ptr(grads.get(name)))
+    _check("moe_backward", lib().moe_backward(
+        ctypes.byref(cfg), ctypes.byref(weights_struct(weights)), _ptr(x), _ptr(dy),
+        ctypes.byref(route_struct(route)), ctypes.byref(g), wp, wb, _stream(stream)))
 
 
 def weights_struct(w: dict) -> MoEWeights:

@@ -169,6 +169,29 @@ __device__ __forceinline__ int frags_of(int m_valid) {
   return m_valid > 128 ? 4 : (m_valid > 64 ? 2 : 1);
 }
 
+// Where output row r (within the tile's group) lives: out0 + r*ldo, or
+// out1 + (r - split)*ldo from row `split` on (weight gradients of w1 and w3
+// computed as one [2F, h] product).
+struct OutMap {
+  uint16_t* out0;
+  uint16_t* out1;
+  int64_t split;
+  int64_t ldo;
+  __device__ __forceinline__ uint16_t* row(int64_t r) const {
+    return r < split ? out0 + r * ldo : out1 + (r - split) * ldo;
+  }
+};
+
+__device__ __forceinline__ OutMap out_map(const GroupedGemmArgs& a, int g) {
+  OutMap m;
+  const int64_t go = a.kgroup ? (int64_t)(g - a.kg0) * a.out_stride : 0;
+  m.out0 = (uint16_t*)a.out + go;
+  m.out1 = a.out1 ? (uint16_t*)a.out1 + go : nullptr;
+  m.split = (a.out1 && a.split_rows > 0) ? a.split_rows : INT64_MAX;
+  m.ldo = a.ldo;
+  return m;
+}
+
 // Epilogue of a (64*FI) x 256 tile.  The MFMAs take the weight fragment
 // first, so fragment (i, j) holds C^T: lane l has output row (l & 31) of row
 // block i and, in registers 4b..4b+3, the 4 consecutive columns
@@ -179,14 +202,14 @@ __device__ __forceinline__ int frags_of(int m_valid) {
 // j + 2 of the same columns); GEMM 2 writes the product.
 template <bool SWIGLU, int FI>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FI][4], const Tile& tl, int lane,
-                                           int wm, int wn, uint16_t* out, int ldo, int N) {
+                                           int wm, int wn, const OutMap& om, int N) {
   const int hi = lane >> 5;
   constexpr int NJ = SWIGLU ? 2 : 4;
 #pragma unroll
   for (int i = 0; i < FI; ++i) {
     const int row = wm * 32 * FI + i * 32 + (lane & 31);
     const bool ok = row < tl.m_valid;
-    uint16_t* orow = out + (tl.o_row + row) * (int64_t)ldo;
+    uint16_t* orow = om.row(tl.o_row + row);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int64_t col0 = SWIGLU ? (int64_t)tl.nt * 128 + wn * 64 + j * 32
@@ -243,25 +266,34 @@ __device__ __forceinline__ void tile_body(const GroupedGemmArgs& a, const Tile& 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
-  const int K = a.K, N = a.N, ldo = a.ldo;
+  const int K = a.K, N = a.N;
   const int nk = K / BK;
-  const bool shared = tl.g >= a.E_routed;
+  const bool shared = !a.kgroup && tl.g >= a.E_routed;
   const bool a_shared = shared && !a.a_from_out_rows;
   const uint16_t* A = (const uint16_t*)(a_shared ? a.A_shared : a.A);
   const int lda = a_shared ? a.lda_shared : a.lda;
-  const uint32_t browbytes = (uint32_t)K * 2;     // weights are dense [out, K]
+  const int ldb = a.ldb ? a.ldb : K;              // weights: dense [out, K]
+  const uint32_t browbytes = (uint32_t)ldb * 2;
   const uint32_t arowbytes = (uint32_t)lda * 2;
   const uint16_t* B0 = (const uint16_t*)(shared ? a.B0s : a.B0);
   const uint16_t* B1 = (const uint16_t*)(shared ? a.B1s : a.B1);
-  if (!shared) {
+  if (!shared && !a.kgroup) {
     B0 += (int64_t)tl.g * a.b_stride;
-    if (SWIGLU) B1 += (int64_t)tl.g * a.b_stride;
+    if (SWIGLU || a.b_split) B1 += (int64_t)tl.g * a.b_stride;
   }
-  // K slices [kbeg, kbeg + nsteps); a whole tile of a routed group starts
+  // K slices [kbeg, kbeg + nsteps): the group's own K range (weight
+  // gradients), or part `part` of K; a whole tile of a routed group starts
   // at slice g*nk/8 and wraps around
-  const int kbeg = (int)((int64_t)part * nk / parts);
-  const int nsteps = (int)((int64_t)(part + 1) * nk / parts) - kbeg;
-  const int krot = (parts == 1 && a.rotate_k && !shared) ? (int)(((int64_t)tl.g * nk / 8) % nk) : 0;
+  int kbeg, nsteps;
+  if (a.kgroup) {
+    kbeg = __builtin_amdgcn_readfirstlane(a.ktab[tl.g] / BK);
+    nsteps = __builtin_amdgcn_readfirstlane(a.ktab[a.kt_size + tl.g] / BK);
+  } else {
+    kbeg = (int)((int64_t)part * nk / parts);
+    nsteps = (int)((int64_t)(part + 1) * nk / parts) - kbeg;
+  }
+  const int krot = (parts == 1 && a.rotate_k && !shared && !a.kgroup)
+                       ? (int)(((int64_t)tl.g * nk / 8) % nk) : 0;
 
   // Global -> LDS copies: wave w fills rows w*WR .. w*WR+WR-1 of the A slice
   // and rows w*64 .. w*64+63 of the B slice, 8 rows (1 KiB) per instruction;
@@ -277,10 +309,21 @@ __device__ __forceinline__ void tile_body(const GroupedGemmArgs& a, const Tile& 
     const uint16_t* W = (w & 1) ? B1 : B0;
     rsB = make_rsrc(W + ((int64_t)tl.nt * 128 + (w >> 1) * 64) * K, 64u * browbytes);
   } else {
-    const int64_t brow = (int64_t)tl.nt * BN + w * 64;
+    // b_split: rows [0, N/2) of B come from B0, [N/2, N) from B1 (64-row
+    // blocks never straddle N/2, a multiple of 64)
+    int64_t brow = (int64_t)tl.nt * BN + w * 64;
+    int64_t nrows = N;
+    const uint16_t* Bb = B0;
+    if (a.b_split) {
+      nrows = N / 2;
+      if (brow >= nrows) {
+        Bb = B1;
+        brow -= nrows;
+      }
+    }
     const int nb = __builtin_amdgcn_readfirstlane(
-        (int)min(max((int64_t)N - brow, (int64_t)0), (int64_t)64));
-    rsB = make_rsrc(B0 + min(brow, (int64_t)N - 1) * K, (uint32_t)nb * browbytes);
+        (int)min(max(nrows - brow, (int64_t)0), (int64_t)64));
+    rsB = make_rsrc(Bb + min(brow, nrows - 1) * ldb, (uint32_t)nb * browbytes);
   }
   uint32_t voffA[2 * FI], voffB[8];
 #pragma unroll
@@ -482,7 +525,7 @@ __device__ __forceinline__ void tile_body(const GroupedGemmArgs& a, const Tile& 
         }
     return;
   }
-  store_tile<SWIGLU, FI>(acc, tl, lane, wm, wn, (uint16_t*)a.out, ldo, N);
+  store_tile<SWIGLU, FI>(acc, tl, lane, wm, wn, out_map(a, tl.g), N);
 }
 
 template <bool SWIGLU>
@@ -491,9 +534,28 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
 
   const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
   const int nk = a.K / BK;
-  const Work wk = plan_work(a, NT, nk, blockIdx.x);
-  if (wk.L < 0) return;
-  Tile tl = tile_of(a, NT, wk.L, BM);
+  Work wk{-1, 0, 1, 0};
+  Tile tl;
+  if (a.kgroup) {
+    // every group: MT x NT tiles of its m_fixed x N output, row tile fastest
+    const int MT = (a.m_fixed + BM - 1) / BM;
+    const int64_t L = blockIdx.x;
+    if (L >= (int64_t)a.G * MT * NT) return;
+    const int64_t per = (int64_t)MT * NT;
+    const int gl = (int)(L / per);                // group within this launch
+    tl.g = a.kg0 + gl;
+    const int64_t rem = L - (int64_t)gl * per;
+    tl.nt = (int)(rem / MT);
+    tl.mt = (int)(rem - (int64_t)tl.nt * MT);
+    tl.m_valid = min(BM, a.m_fixed - tl.mt * BM);
+    tl.a_row = (int64_t)tl.mt * BM;
+    tl.o_row = tl.a_row;
+    wk.L = L;
+  } else {
+    wk = plan_work(a, NT, nk, blockIdx.x);
+    if (wk.L < 0) return;
+    tl = tile_of(a, NT, wk.L, BM);
+  }
   // Tile fields are workgroup-uniform; saying so keeps the buffer
   // descriptors in scalar registers.
   tl.g = __builtin_amdgcn_readfirstlane(tl.g);
@@ -542,7 +604,7 @@ __device__ __forceinline__ void reduce_body(const GroupedGemmArgs& a, const Tile
           for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[j * 4 + q][e];
     }
   }
-  store_tile<SWIGLU, FI>(acc, tl, lane, w >> 1, w & 1, (uint16_t*)a.out, a.ldo, a.N);
+  store_tile<SWIGLU, FI>(acc, tl, lane, w >> 1, w & 1, out_map(a, tl.g), a.N);
 }
 
 // Sums the K parts of the split tiles (in part order) and stores them like
@@ -658,14 +720,16 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, const GroupedGemmArgs& a,
                                hipStream_t s) {
   if (dtype == 1) {
     const int NT = swiglu ? a.N / 128 : (a.N + BN - 1) / BN;
-    // whole tiles plus at most num_cu split-part workgroups
-    const int64_t nb = a.max_m_tiles * NT + (a.partials ? a.num_cu : 0);
+    // whole tiles plus at most num_cu split-part workgroups; groups split
+    // along K: exactly G x MT x NT tiles
+    const int64_t nb = a.kgroup ? (int64_t)a.G * ((a.m_fixed + BM - 1) / BM) * NT
+                                : a.max_m_tiles * NT + (a.partials ? a.num_cu : 0);
     if (nb <= 0) return hipSuccess;
     if (swiglu)
       hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, a);
-    if (a.partials) {
+    if (a.partials && !a.kgroup) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       // one workgroup per possible split tile (fewer than num_cu)

@@ -333,6 +333,210 @@ MOE_API int moe_load_balance(const moe_cfg_t* cfg, const float* logits,
   return MOE_OK;
 }
 
+namespace {
+
+// Workspace of moe_backward (bf16): tile and K tables, the recomputed and
+// backward activations (rows padded like the forward's), the transposed
+// weights, and the K-major copies the weight-gradient GEMMs read.
+struct BwdLayout {
+  size_t gtab, kta, kto, rowtok, dg, dl, partials, xp, a13, u, o, dO, dU, dA, dxp;
+  size_t w2t, w13t, dOT, uT, dAT, xpT, total;
+  int ldh, ldf, ld13;
+  int64_t ktb;
+};
+
+BwdLayout bwd_layout_of(const moe_cfg_t& c) {
+  BwdLayout L{};
+  const int64_t T = c.T, E = c.E, k = c.k, h = c.h, F = c.F;
+  const int64_t G = E + c.has_shared;
+  const int64_t rows = rows_of(c);
+  const int64_t rows_all = rows + (c.has_shared ? T : 0);
+  L.ldh = (int)h + 64;
+  L.ldf = (int)F + 64;
+  L.ld13 = 2 * (int)F + 64;
+  L.ktb = (rows_all + 64 * G + 63) / 64 * 64;   // every group's rows rounded up to 64
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.gtab = take((size_t)gtab_ints((int)G) * 4);
+  L.kta = take((size_t)(4 * G) * 4);
+  L.kto = take((size_t)(4 * G) * 4);
+  L.rowtok = take((size_t)rows * 4);
+  L.dg = take((size_t)(T * k) * 4);
+  L.dl = take((size_t)(T * E) * 4);
+  L.partials = take((size_t)moe::kSplitPartialFloats * 4);
+  L.xp = take((size_t)rows * L.ldh * 2);
+  L.a13 = take((size_t)rows_all * L.ld13 * 2);
+  L.u = take((size_t)rows_all * L.ldf * 2);
+  L.o = take((size_t)rows_all * L.ldh * 2);
+  L.dO = take((size_t)rows_all * L.ldh * 2);
+  L.dU = take((size_t)rows_all * L.ldf * 2);
+  L.dA = take((size_t)rows_all * L.ld13 * 2);
+  L.dxp = take((size_t)rows_all * L.ldh * 2);
+  L.w2t = take((size_t)(G * F * h) * 2);
+  L.w13t = take((size_t)(G * h * 2 * F) * 2);
+  L.dOT = take((size_t)(h * L.ktb) * 2);
+  L.uT = take((size_t)(F * L.ktb) * 2);
+  L.dAT = take((size_t)(2 * F * L.ktb) * 2);
+  L.xpT = take((size_t)(h * L.ktb) * 2);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+MOE_API int moe_backward_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes) {
+  const int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = cfg->T == 0 ? 0 : bwd_layout_of(*cfg).total;
+  return MOE_OK;
+}
+
+MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
+                         const void* dy, const moe_route_out_t* route, const moe_grads_t* grads,
+                         void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const moe_cfg_t& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (c.dtype != MOE_DTYPE_BF16 || c.routing == MOE_ROUTE_EXPERT_CHOICE)
+    return MOE_ERR_UNSUPPORTED;
+  if (!w || !x || !dy || !route || !grads || !w->w_router || !w->w1 || !w->w3 || !w->w2)
+    return MOE_ERR_INVALID_ARG;
+  const moe_route_out_t& r = *route;
+  const moe_grads_t& gr = *grads;
+  if (!r.logits || !r.topk_idx || !r.topk_gate || !r.expert_counts || !r.expert_offsets ||
+      !r.assign_row || !gr.dx || !gr.dw1 || !gr.dw3 || !gr.dw2)
+    return MOE_ERR_INVALID_ARG;
+  if (c.has_shared && (!w->ws1 || !w->ws3 || !w->ws2 || !gr.dws1 || !gr.dws3 || !gr.dws2))
+    return MOE_ERR_INVALID_ARG;
+  if (misaligned(x, dy, ws, w->w_router, w->w1, w->w3, w->w2, w->ws1, w->ws3) ||
+      misaligned(w->ws2, r.logits, r.topk_idx, r.topk_gate, r.expert_counts, r.expert_offsets,
+                 r.assign_row) ||
+      misaligned(gr.dx, gr.dw_router, gr.dlogit_bias, gr.dw1, gr.dw3, gr.dw2, gr.dws1, gr.dws3,
+                 gr.dws2) ||
+      misaligned(gr.dgate))
+    return MOE_ERR_INVALID_ARG;
+  const BwdLayout L = bwd_layout_of(c);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  const int E = c.E, k = c.k, h = c.h, F = c.F;
+  const int G = E + c.has_shared;
+  const int64_t T = c.T;
+  const int64_t rows = rows_of(c);
+  const int64_t rows_all = rows + (c.has_shared ? T : 0);
+  const int BM = row_tile(c);
+  int32_t* gtab = at<int32_t>(ws, L.gtab);
+  int32_t* kta = at<int32_t>(ws, L.kta);
+  int32_t* kto = at<int32_t>(ws, L.kto);
+  float* dg = gr.dgate ? gr.dgate : at<float>(ws, L.dg);
+  float* dl = at<float>(ws, L.dl);
+  void* xp = at<char>(ws, L.xp);
+  void* a13 = at<char>(ws, L.a13);
+  void* u = at<char>(ws, L.u);
+  void* o = at<char>(ws, L.o);
+  void* dO = at<char>(ws, L.dO);
+  void* dU = at<char>(ws, L.dU);
+  void* dA = at<char>(ws, L.dA);
+  void* dxp = at<char>(ws, L.dxp);
+  char* w2t = at<char>(ws, L.w2t);
+  char* w13t = at<char>(ws, L.w13t);
+  void* dOT = at<char>(ws, L.dOT);
+  void* uT = at<char>(ws, L.uT);
+  void* dAT = at<char>(ws, L.dAT);
+  void* xpT = at<char>(ws, L.xpT);
+  const int ktb = (int)L.ktb;
+
+  // groups, K tables, the dispatch buffer
+  MOE_TRY(moe::launch_groups_from_counts(r.expert_counts, r.expert_offsets, E, c.capacity, T,
+                                         c.has_shared, BM, rows, gtab, s));
+  MOE_TRY(moe::launch_ktab(gtab, G, 1, kta, s));
+  MOE_TRY(moe::launch_ktab(gtab, G, 0, kto, s));
+  MOE_TRY(moe::launch_permute(c.dtype, x, r.assign_row, r.expert_counts, T, h, E, k, c.capacity,
+                              xp, L.ldh, at<int32_t>(ws, L.rowtok), s));
+  // transposed weights: w2t[g] = w2[g]^T [F,h]; w13t[g] = [w1[g]^T | w3[g]^T] [h,2F]
+  MOE_TRY(moe::launch_transpose(w->w2, (int64_t)h * F, h, F, w2t, (int64_t)F * h, h, 0, E, s));
+  MOE_TRY(moe::launch_transpose(w->w1, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F, 2 * F, 0,
+                                E, s));
+  MOE_TRY(moe::launch_transpose(w->w3, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F, 2 * F, F,
+                                E, s));
+  if (c.has_shared) {
+    MOE_TRY(moe::launch_transpose(w->ws2, 0, h, F, w2t + (size_t)E * F * h * 2, 0, h, 0, 1, s));
+    MOE_TRY(moe::launch_transpose(w->ws1, 0, F, h, w13t + (size_t)E * h * 2 * F * 2, 0, 2 * F, 0,
+                                  1, s));
+    MOE_TRY(moe::launch_transpose(w->ws3, 0, F, h, w13t + (size_t)E * h * 2 * F * 2, 0, 2 * F, F,
+                                  1, s));
+  }
+
+  moe::GroupedGemmArgs base{};
+  base.gtab = gtab;
+  base.G = G;
+  base.E_routed = E;
+  base.max_m_tiles = max_m_tiles(rows, E, BM) + (c.has_shared ? (T + BM - 1) / BM : 0);
+  base.num_cu = device_cus();
+  base.partials = at<float>(ws, L.partials);
+  // [a1 | a3] = x_perm [w1; w3]^T (the shared group reads x)
+  moe::GroupedGemmArgs a = base;
+  a.A = xp; a.lda = L.ldh; a.A_shared = x; a.lda_shared = h;
+  a.B0 = w->w1; a.B1 = w->w3; a.B0s = w->ws1; a.B1s = w->ws3; a.b_split = 1;
+  a.b_stride = (int64_t)F * h; a.K = h; a.N = 2 * F; a.out = a13; a.ldo = L.ld13;
+  MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
+  MOE_TRY(moe::launch_swiglu_fwd(a13, L.ld13, rows_all, F, u, L.ldf, s));
+  // expert outputs o = u w2^T (the forward's y_perm)
+  a = base;
+  a.A = u; a.lda = L.ldf; a.a_from_out_rows = 1;
+  a.B0 = w->w2; a.B0s = w->ws2; a.b_stride = (int64_t)h * F; a.K = F; a.N = h;
+  a.out = o; a.ldo = L.ldh;
+  MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
+  // dO rows, gate gradients
+  MOE_TRY(moe::launch_scatter_dy(dy, r.assign_row, r.topk_gate, r.expert_counts, T, h, E, k,
+                                 c.capacity, rows, c.has_shared, dO, L.ldh, s));
+  MOE_TRY(moe::launch_gate_grad(dy, o, L.ldh, r.assign_row, T, h, k, dg, s));
+  // dU = dO w2, then dA, then dx_perm = dA [w1; w3]
+  a = base;
+  a.A = dO; a.lda = L.ldh; a.a_from_out_rows = 1;
+  a.B0 = w2t; a.B0s = w2t + (size_t)E * F * h * 2; a.b_stride = (int64_t)F * h;
+  a.K = h; a.N = F; a.out = dU; a.ldo = L.ldf;
+  MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
+  MOE_TRY(moe::launch_swiglu_bwd(a13, L.ld13, dU, L.ldf, rows_all, F, dA, L.ld13, s));
+  a = base;
+  a.A = dA; a.lda = L.ld13; a.a_from_out_rows = 1;
+  a.B0 = w13t; a.B0s = w13t + (size_t)E * h * 2 * F * 2; a.b_stride = (int64_t)h * 2 * F;
+  a.K = 2 * F; a.N = h; a.out = dxp; a.ldo = L.ldh;
+  MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
+  // K-major copies of each group's rows, then the weight gradients
+  MOE_TRY(moe::launch_transpose_groups(dO, L.ldh, dO, L.ldh, G, kto, G, h, L.ktb, dOT, ktb, s));
+  MOE_TRY(moe::launch_transpose_groups(u, L.ldf, u, L.ldf, G, kto, G, F, L.ktb, uT, ktb, s));
+  MOE_TRY(moe::launch_transpose_groups(dA, L.ld13, dA, L.ld13, G, kto, G, 2 * F, L.ktb, dAT, ktb,
+                                       s));
+  MOE_TRY(moe::launch_transpose_groups(xp, L.ldh, x, h, E, kta, G, h, L.ktb, xpT, ktb, s));
+  for (int pass = 0; pass < (c.has_shared ? 2 : 1); ++pass) {
+    const bool sh = pass == 1;
+    moe::GroupedGemmArgs wg{};
+    wg.kgroup = 1; wg.ktab = kto; wg.kt_size = G; wg.kg0 = sh ? E : 0; wg.G = sh ? 1 : E;
+    wg.E_routed = wg.G; wg.num_cu = device_cus();
+    // dw2[g] [h,F] = dO_g^T u_g
+    wg.A = dOT; wg.lda = ktb; wg.m_fixed = h; wg.B0 = uT; wg.ldb = ktb; wg.N = F; wg.K = 0;
+    wg.out = sh ? gr.dws2 : gr.dw2; wg.ldo = F; wg.out_stride = (int64_t)h * F;
+    MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, wg, s));
+    // [dw1; dw3][g] [2F,h] = dA_g^T x_g
+    wg.A = dAT; wg.m_fixed = 2 * F; wg.B0 = xpT; wg.N = h;
+    wg.out = sh ? gr.dws1 : gr.dw1; wg.out1 = sh ? gr.dws3 : gr.dw3; wg.split_rows = F;
+    wg.ldo = h; wg.out_stride = (int64_t)F * h;
+    MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, wg, s));
+  }
+  // router: dl, dw_router, dlogit_bias; then dx
+  MOE_TRY(moe::launch_router_bwd(r.logits, r.topk_idx, r.topk_gate, dg, c.gate, T, E, k, x, h,
+                                 dl, gr.dw_router, gr.dlogit_bias, s));
+  MOE_TRY(moe::launch_dx_final(dxp, L.ldh, r.assign_row, k, rows, c.has_shared, dl, w->w_router,
+                               T, h, E, gr.dx, s));
+  return MOE_OK;
+}
+
 MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
                         void* y, const moe_route_out_t* route, void* ws,
                         size_t ws_bytes, void* const* events, void* stream) {

@@ -43,6 +43,23 @@ struct GroupedGemmArgs {
   int E_routed;          // groups 0..E_routed-1 use B0/B1, group E_routed B0s/B1s
   int a_from_out_rows;   // 1: A row of a tile = its output row (GEMM2)
   int64_t max_m_tiles;   // host-side bound on the total row tiles
+  // Plain (non-SwiGLU) mode only:
+  int b_split;           // 1: B rows [0, N/2) from B0, [N/2, N) from B1
+  int ldb;               // B row stride in elements (0: K, dense)
+  // Groups split along K (weight gradients): every group g has the same
+  // m_fixed x N output out + g*out_stride, reduced over its own K range
+  // ktab[g] .. ktab[g] + ktab[G+g] (elements, multiples of 64) of A [m_fixed,
+  // lda] and B [N, ldb]; no split-K, no rotation; gtab unused.
+  int kgroup;
+  int m_fixed;
+  const int32_t* ktab;   // ktab[g], ktab[kt_size + g] (ktab of kt_size groups)
+  int kt_size;
+  int kg0;               // first group of this launch (G groups from kg0)
+  int64_t out_stride;
+  // Output rows at or past split_rows (within a group) go to out1 + the
+  // group's offset, row - split_rows (0: no split).
+  void* out1;
+  int split_rows;
 };
 
 hipError_t launch_router(int dtype, const void* x, const void* w_router,
@@ -68,6 +85,38 @@ hipError_t launch_score_drop(const int32_t* idx, const float* gate, const int32_
                              int32_t* row_token, hipStream_t s);
 hipError_t launch_fixed_groups(int E, int C, int64_t T, int has_shared, int BM, int32_t* counts,
                                int32_t* offsets, int32_t* gtab, hipStream_t s);
+// Tile table for the backward from the forward's counts and offsets:
+// valid rows min(count, C) (C = 0: count) at offsets[e], plus the shared
+// group (T rows read from x, written after the routed rows).
+hipError_t launch_groups_from_counts(const int32_t* counts, const int32_t* offsets, int E,
+                                     int64_t C, int64_t T, int has_shared, int BM,
+                                     int64_t rows, int32_t* gtab, hipStream_t s);
+
+// Backward kernels (backward.hip).
+hipError_t launch_transpose(const void* src, int64_t src_bs, int R, int Cc, void* dst,
+                            int64_t dst_bs, int dld, int col0, int batches, hipStream_t s);
+hipError_t launch_ktab(const int32_t* gtab, int G, int use_a_rows, int32_t* kt, hipStream_t s);
+hipError_t launch_transpose_groups(const void* src, int sld, const void* src_shared,
+                                   int sld_shared, int E_routed, const int32_t* kt, int G,
+                                   int Cc, int64_t ktot_bound, void* dst, int dld,
+                                   hipStream_t s);
+hipError_t launch_scatter_dy(const void* dy, const int32_t* assign_row, const float* gate,
+                             const int32_t* counts, int64_t T, int h, int E, int k, int64_t C,
+                             int64_t rows, int has_shared, void* dO, int ld, hipStream_t s);
+hipError_t launch_gate_grad(const void* dy, const void* o, int ld, const int32_t* assign_row,
+                            int64_t T, int h, int k, float* dg, hipStream_t s);
+hipError_t launch_swiglu_fwd(const void* a13, int lda13, int64_t rows, int F, void* u, int ldu,
+                             hipStream_t s);
+hipError_t launch_swiglu_bwd(const void* a13, int lda13, const void* dU, int ldu, int64_t rows,
+                             int F, void* dA, int ldda, hipStream_t s);
+hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gate,
+                             const float* dg, int gate_mode, int64_t T, int E, int k,
+                             const void* x, int h, float* dl, void* dw_router,
+                             float* dlogit_bias, hipStream_t s);
+hipError_t launch_dx_final(const void* dxp, int ldp, const int32_t* assign_row, int k,
+                           int64_t rows, int has_shared, const float* dl, const void* w_router,
+                           int64_t T, int h, int E, void* dx, hipStream_t s);
+
 hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token, int64_t rows,
                               int64_t T, int h, void* x_perm, int ld_perm, hipStream_t s);
 

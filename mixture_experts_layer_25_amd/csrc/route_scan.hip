@@ -338,6 +338,26 @@ __global__ __launch_bounds__(1024) void fixed_groups_kernel(int E, int C, int64_
   write_gtab(e, G, valid, a0, o0, BM, tmp, gtab);
 }
 
+// Backward: groups from the forward's counts and offsets.  One workgroup of
+// 1024 threads.
+__global__ __launch_bounds__(1024) void groups_from_counts_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int E, int64_t C,
+    int64_t T, int has_shared, int BM, int64_t rows, int32_t* __restrict__ gtab) {
+  __shared__ int tmp[32];
+  const int e = threadIdx.x;
+  const int G = E + (has_shared ? 1 : 0);
+  int valid = 0, a0 = 0, o0 = 0;
+  if (e < E) {
+    valid = C > 0 ? min(counts[e], (int)C) : counts[e];
+    a0 = o0 = offsets[e];
+  } else if (e == E && has_shared) {
+    valid = (int)T;
+    a0 = 0;
+    o0 = (int)rows;
+  }
+  write_gtab(e, G, valid, a0, o0, BM, tmp, gtab);
+}
+
 // x_perm[r] = x[row_token[r]] for every row (expert choice fills each
 // expert's C rows), kPermTok rows per workgroup, 16-byte vectors.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
@@ -364,6 +384,14 @@ hipError_t launch_fixed_groups(int E, int C, int64_t T, int has_shared, int BM, 
                                int32_t* offsets, int32_t* gtab, hipStream_t s) {
   hipLaunchKernelGGL(fixed_groups_kernel, dim3(1), dim3(1024), 0, s, E, C, T, has_shared, BM,
                      counts, offsets, gtab);
+  return hipGetLastError();
+}
+
+hipError_t launch_groups_from_counts(const int32_t* counts, const int32_t* offsets, int E,
+                                     int64_t C, int64_t T, int has_shared, int BM,
+                                     int64_t rows, int32_t* gtab, hipStream_t s) {
+  hipLaunchKernelGGL(groups_from_counts_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E,
+                     C, T, has_shared, BM, rows, gtab);
   return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ _TENSOR_ID = {
     "ws2": 8,
     "logit_bias": 9,
     "select_bias": 10,
+    "dy": 11,           # output gradient of the backward tests and benchmark
 }
 
 

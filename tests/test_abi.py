@@ -42,6 +42,7 @@ def test_struct_layouts_match_header(tmp_path):
         " offsetof(moe_cfg_t, gate), offsetof(moe_cfg_t, capacity), sizeof(moe_weights_t),"
         " sizeof(moe_route_out_t), offsetof(moe_weights_t, ws2), offsetof(moe_cfg_t, routing),"
         " offsetof(moe_route_out_t, probs));\n"
+        'printf("%zu %zu\\n", sizeof(moe_grads_t), offsetof(moe_grads_t, dgate));\n'
         'printf("%d %d\\n", MOE_NUM_STAGES, MOE_NUM_EVENTS);\n'
         "return 0;}\n")
     exe = tmp_path / "layout"
@@ -53,7 +54,9 @@ def test_struct_layouts_match_header(tmp_path):
           ctypes.sizeof(moe.MoERouteOut), moe.MoEWeights.ws2.offset, moe.MoECfg.routing.offset,
           moe.MoERouteOut.probs.offset]
     assert c == py
-    assert [int(v) for v in lines[1].split()] == [moe.MOE_NUM_STAGES, moe.MOE_NUM_EVENTS]
+    assert [int(v) for v in lines[2].split()] == [moe.MOE_NUM_STAGES, moe.MOE_NUM_EVENTS]
+    assert [int(v) for v in lines[1].split()] == [ctypes.sizeof(moe.MoEGrads),
+                                                  moe.MoEGrads.dgate.offset]
 
 
 @pytest.mark.parametrize("T,E,k,num,den", [

@@ -17,7 +17,7 @@ import mixture_experts_layer_25_amd as moe
 import oracle
 from helpers import (DEV, LazyExperts, capacity_of, check_routing, gen_inputs, lib_cfg, np32,
                      oracle_forward, oracle_weights, rel_err, run_forward, tol_of)
-from moe_inputs import CONFIGS, MoEConfig
+from moe_inputs import CONFIGS, MoEConfig, normal
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +79,81 @@ def test_forward_matches_oracle(cfg):
     err = rel_err(y, ref_y)
     _report(cfg.name, rel_err=f"{err:.2e}", **rep)
     assert err <= tol_of(cfg)
+
+
+# ------------------------------------------------------------------ backward
+BACKWARD = ["dropless_softmax", "capacity_heavy_drop", "worked_example_small",
+            "sigmoid_bias_shared", "zipf_dropless", "split_k_tail", "e40_ragged",
+            "mixtral_bias", "e256_k8_shared", "k_equals_e"]
+
+
+def run_backward(cfg, inp, C_lib, gpu, dy, routing="topk"):
+    c = lib_cfg(cfg, C_lib, routing)
+    T, E, k, h, F = cfg.T, cfg.E, cfg.k, cfg.h, cfg.F
+    bf = torch.bfloat16
+
+    def nan(*shape, dtype=bf):
+        return torch.full(shape, float("nan"), dtype=dtype, device=DEV)
+
+    grads = {"dx": nan(T, h), "dw_router": nan(E, h), "dlogit_bias": nan(E, dtype=torch.float32),
+             "dw1": nan(E, F, h), "dw3": nan(E, F, h), "dw2": nan(E, h, F),
+             "dgate": nan(T, k, dtype=torch.float32)}
+    if cfg.shared:
+        grads.update({"dws1": nan(F, h), "dws3": nan(F, h), "dws2": nan(h, F)})
+    ws = torch.empty(moe.moe_backward_workspace_bytes(c), dtype=torch.uint8, device=DEV)
+    weights = {n: inp[n] for n in ("w_router", "w1", "w3", "w2", "logit_bias", "select_bias",
+                                   "ws1", "ws3", "ws2")}
+    route = {n: gpu[n] for n in ("logits", "topk_idx", "topk_gate", "expert_counts",
+                                 "expert_offsets", "assign_row")}
+    moe.moe_backward(c, weights, inp["x"], dy, route, grads, ws)
+    torch.cuda.synchronize()
+    return grads
+
+
+@pytest.mark.parametrize("name", BACKWARD)
+def test_backward_matches_oracle(name):
+    """Every gradient of sum(y * dy) against the oracle's chain rule on the
+    GPU's own routing (top-k choice and drops held fixed)."""
+    cfg = next(c for c in MEDIUM if c.name == name)
+    print(f"[case] backward {name}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    gpu = run_forward(cfg, inp, C_lib)
+    dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=DEV)
+    g = run_backward(cfg, inp, C_lib, gpu, dy)
+    x, wr, w1, w3, w2, lb, shared = oracle_weights(cfg, inp)
+    sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
+    ref = oracle.moe_backward(x, wr, w1, w3, w2, np32(dy), k=cfg.k, gate=cfg.gate, C=C_ref,
+                              logit_bias=lb, select_bias=sb, shared=shared,
+                              idx=gpu["topk_idx"].cpu().numpy())
+    pairs = [("dx", "dx"), ("dw1", "dw1"), ("dw3", "dw3"), ("dw2", "dw2"),
+             ("dw_router", "dw_router"), ("dlogit_bias", "dlogit_bias"), ("dgate", "dgate")]
+    if cfg.shared:
+        pairs += [("dws1", "dws1"), ("dws3", "dws3"), ("dws2", "dws2")]
+    errs = {}
+    for gk, rk in pairs:
+        r = ref[rk]
+        if np.abs(r).max() == 0:
+            assert float(np.abs(np32(g[gk])).max()) == 0.0, gk
+            errs[gk] = 0.0
+            continue
+        errs[gk] = rel_err(np32(g[gk]), r)
+    _report(f"backward_{name}", **{kk: f"{v:.2e}" for kk, v in errs.items()})
+    for kk, v in errs.items():
+        assert v <= 2e-2, (kk, v)
+
+
+def test_backward_is_deterministic():
+    cfg = next(c for c in MEDIUM if c.name == "sigmoid_bias_shared")
+    inp = gen_inputs(cfg)
+    C_lib, _ = capacity_of(cfg)
+    gpu = run_forward(cfg, inp, C_lib)
+    dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=DEV)
+    a = run_backward(cfg, inp, C_lib, gpu, dy)
+    b = run_backward(cfg, inp, C_lib, gpu, dy)
+    for key in a:
+        assert torch.equal(a[key].view(torch.int16) if a[key].dtype == torch.bfloat16 else a[key],
+                           b[key].view(torch.int16) if b[key].dtype == torch.bfloat16 else b[key]), key
 
 
 # ------------------------------------------------------------ routing variants
