@@ -142,6 +142,7 @@ def main() -> int:
                     choices=("topk", "topk_score_drop", "expert_choice"),
                     help="routing variant (the headline workload uses topk)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this size before the timed steps "
@@ -221,6 +222,42 @@ def main() -> int:
     torch.cuda.synchronize()
     lb_us = lb_ev[0].elapsed_time(lb_ev[1]) * 1e3 / K
 
+    # backward of the same layer with this routing (not part of the step):
+    # gradients of sum(y * dy) for x, the router and every expert weight
+    bwd = None
+    if args.routing != "expert_choice" and cfg.dtype == "bf16" and not args.no_backward:
+        from moe_inputs import normal
+        dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=dev)
+        full_route = {"logits": logits,
+                      "topk_idx": torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev),
+                      "topk_gate": torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev),
+                      "expert_counts": counts,
+                      "expert_offsets": torch.empty(cfg.E + 1, dtype=torch.int32, device=dev),
+                      "assign_row": torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev)}
+        moe.moe_forward(c, weights, inp["x"], y, full_route, ws)
+        bf = torch.bfloat16
+        grads = {"dx": torch.empty((cfg.T, cfg.h), dtype=bf, device=dev),
+                 "dw_router": torch.empty((cfg.E, cfg.h), dtype=bf, device=dev),
+                 "dw1": torch.empty((cfg.E, cfg.F, cfg.h), dtype=bf, device=dev),
+                 "dw3": torch.empty((cfg.E, cfg.F, cfg.h), dtype=bf, device=dev),
+                 "dw2": torch.empty((cfg.E, cfg.h, cfg.F), dtype=bf, device=dev)}
+        if cfg.shared:
+            grads.update({"dws1": torch.empty((cfg.F, cfg.h), dtype=bf, device=dev),
+                          "dws3": torch.empty((cfg.F, cfg.h), dtype=bf, device=dev),
+                          "dws2": torch.empty((cfg.h, cfg.F), dtype=bf, device=dev)})
+        wsb = torch.empty(moe.moe_backward_workspace_bytes(c), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            moe.moe_backward(c, weights, inp["x"], dy, full_route, grads, wsb)
+        bw_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        nb = max(3, K // 4)
+        bw_ev[0].record()
+        for _ in range(nb):
+            moe.moe_backward(c, weights, inp["x"], dy, full_route, grads, wsb)
+        bw_ev[1].record()
+        torch.cuda.synchronize()
+        bwd = bw_ev[0].elapsed_time(bw_ev[1]) / nb
+        del wsb, grads
+
     stage_ms = {}
     for s, name in enumerate(moe.STAGE_NAMES):
         stage_ms[name] = sum(evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(K)) / K
@@ -269,6 +306,13 @@ def main() -> int:
         "combine": {"gbs": round(comb_gbs, 1), "frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
                     "bytes": cb},
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "backward": (None if bwd is None else {
+            "ms": round(bwd, 4),
+            # 12*kept*h*F: dgrad and wgrad of both GEMMs; 18*kept*h*F counts
+            # the recomputed [a1 | a3] and expert outputs as well
+            "tflops": round(12 * kept_all * cfg.h * cfg.F / (bwd * 1e-3) / 1e12, 1),
+            "tflops_with_recompute": round(18 * kept_all * cfg.h * cfg.F / (bwd * 1e-3) / 1e12, 1),
+            "frac_of_peak": round(18 * kept_all * cfg.h * cfg.F / (bwd * 1e-3) / 1e12 / peak, 4)}),
         "load_balance": {"us": round(lb_us, 2),
                          "gbs": round(cfg.T * cfg.E * 4 / (lb_us * 1e-6) / 1e9, 1),
                          "aux_loss": round(float(lb_loss.item()), 6)},

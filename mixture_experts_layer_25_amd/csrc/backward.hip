@@ -308,28 +308,32 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const float* __restrict_
   }
 }
 
-// dW_router[e, i] = sum_t dl[t,e] x[t,i] (bf16 out) over 64 columns and 32
-// experts per workgroup, tokens in order (64 at a time through LDS).
+// dW_router[e, i] = sum_t dl[t,e] x[t,i]: workgroup (column tile, 32
+// experts, token slice z) sums its slice of tokens in order (64 at a time
+// through LDS) into part[z][e][i] (fp32); router_wgrad_sum adds the
+// slices in order and rounds to bf16.
 constexpr int kRbE = 32;
+constexpr int kRbSlices = 32;
 __global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ dl,
                                                            const uint16_t* __restrict__ x,
-                                                           int64_t T, int h, int E,
-                                                           uint16_t* __restrict__ dwr) {
+                                                           int64_t T, int h, int E, int64_t tc,
+                                                           float* __restrict__ part) {
   __shared__ float sdl[64][kRbE];
   __shared__ float sx[64][64];
   const int i0 = blockIdx.x * 64, e0 = blockIdx.y * kRbE;
+  const int64_t tb = (int64_t)blockIdx.z * tc, te = min(T, tb + tc);
   const int ii = threadIdx.x & 63, eg = threadIdx.x >> 6;   // experts eg, eg+4, ...
   float acc[kRbE / 4];
 #pragma unroll
   for (int q = 0; q < kRbE / 4; ++q) acc[q] = 0.f;
-  for (int64_t t0 = 0; t0 < T; t0 += 64) {
+  for (int64_t t0 = tb; t0 < te; t0 += 64) {
     for (int q = threadIdx.x; q < 64 * kRbE; q += 256) {
       const int tt = q / kRbE, ee = q % kRbE;
-      sdl[tt][ee] = (t0 + tt < T && e0 + ee < E) ? dl[(t0 + tt) * E + e0 + ee] : 0.f;
+      sdl[tt][ee] = (t0 + tt < te && e0 + ee < E) ? dl[(t0 + tt) * E + e0 + ee] : 0.f;
     }
     for (int q = threadIdx.x; q < 64 * 64; q += 256) {
       const int tt = q >> 6, c = q & 63;
-      sx[tt][c] = t0 + tt < T ? bf16_bits_to_f32(x[(t0 + tt) * h + i0 + c]) : 0.f;
+      sx[tt][c] = t0 + tt < te ? bf16_bits_to_f32(x[(t0 + tt) * h + i0 + c]) : 0.f;
     }
     __syncthreads();
     for (int tt = 0; tt < 64; ++tt) {
@@ -342,8 +346,18 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restri
 #pragma unroll
   for (int q = 0; q < kRbE / 4; ++q) {
     const int e = e0 + eg + 4 * q;
-    if (e < E) dwr[(int64_t)e * h + i0 + ii] = f32_to_bf16_bits(acc[q]);
+    if (e < E) part[((int64_t)blockIdx.z * E + e) * h + i0 + ii] = acc[q];
   }
+}
+
+__global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __restrict__ part,
+                                                               int slices, int64_t n,
+                                                               uint16_t* __restrict__ dwr) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= n) return;
+  float s = 0.f;
+  for (int z = 0; z < slices; ++z) s += part[z * n + q];
+  dwr[q] = f32_to_bf16_bits(s);
 }
 
 // dlogit_bias[e] = sum_t dl[t,e]: one workgroup per expert, fixed tree.
@@ -472,15 +486,21 @@ hipError_t launch_swiglu_bwd(const void* a13, int lda13, const void* dU, int ldu
 
 hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gate,
                              const float* dg, int gate_mode, int64_t T, int E, int k,
-                             const void* x, int h, float* dl, void* dw_router,
+                             const void* x, int h, float* dl, float* rpart, void* dw_router,
                              float* dlogit_bias, hipStream_t s) {
   hipLaunchKernelGGL(gates_bwd_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s,
                      logits, idx, gate, dg, gate_mode, T, E, k, dl);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (dw_router) {
-    hipLaunchKernelGGL(router_wgrad_kernel, dim3(h / 64, (E + kRbE - 1) / kRbE), dim3(256), 0,
-                       s, dl, (const uint16_t*)x, T, h, E, (uint16_t*)dw_router);
+    const int64_t tc = ((T + kRbSlices - 1) / kRbSlices + 63) / 64 * 64;   // tokens per slice
+    const int slices = (int)((T + tc - 1) / tc);
+    hipLaunchKernelGGL(router_wgrad_kernel, dim3(h / 64, (E + kRbE - 1) / kRbE, slices),
+                       dim3(256), 0, s, dl, (const uint16_t*)x, T, h, E, tc, rpart);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int64_t n = (int64_t)E * h;
+    hipLaunchKernelGGL(router_wgrad_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       s, rpart, slices, n, (uint16_t*)dw_router);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (dlogit_bias) {

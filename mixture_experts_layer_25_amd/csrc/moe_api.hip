@@ -339,7 +339,7 @@ namespace {
 // backward activations (rows padded like the forward's), the transposed
 // weights, and the K-major copies the weight-gradient GEMMs read.
 struct BwdLayout {
-  size_t gtab, kta, kto, rowtok, dg, dl, partials, xp, a13, u, o, dO, dU, dA, dxp;
+  size_t gtab, kta, kto, rowtok, dg, dl, rpart, partials, xp, a13, u, o, dO, dU, dA, dxp;
   size_t w2t, w13t, dOT, uT, dAT, xpT, total;
   int ldh, ldf, ld13;
   int64_t ktb;
@@ -367,6 +367,7 @@ BwdLayout bwd_layout_of(const moe_cfg_t& c) {
   L.rowtok = take((size_t)rows * 4);
   L.dg = take((size_t)(T * k) * 4);
   L.dl = take((size_t)(T * E) * 4);
+  L.rpart = take((size_t)(32 * E * h) * 4);
   L.partials = take((size_t)moe::kSplitPartialFloats * 4);
   L.xp = take((size_t)rows * L.ldh * 2);
   L.a13 = take((size_t)rows_all * L.ld13 * 2);
@@ -531,7 +532,7 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
   }
   // router: dl, dw_router, dlogit_bias; then dx
   MOE_TRY(moe::launch_router_bwd(r.logits, r.topk_idx, r.topk_gate, dg, c.gate, T, E, k, x, h,
-                                 dl, gr.dw_router, gr.dlogit_bias, s));
+                                 dl, at<float>(ws, L.rpart), gr.dw_router, gr.dlogit_bias, s));
   MOE_TRY(moe::launch_dx_final(dxp, L.ldh, r.assign_row, k, rows, c.has_shared, dl, w->w_router,
                                T, h, E, gr.dx, s));
   return MOE_OK;

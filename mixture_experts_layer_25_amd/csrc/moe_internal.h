@@ -109,9 +109,10 @@ hipError_t launch_swiglu_fwd(const void* a13, int lda13, int64_t rows, int F, vo
                              hipStream_t s);
 hipError_t launch_swiglu_bwd(const void* a13, int lda13, const void* dU, int ldu, int64_t rows,
                              int F, void* dA, int ldda, hipStream_t s);
+// rpart: 32 * E * h floats of slice sums for dw_router.
 hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gate,
                              const float* dg, int gate_mode, int64_t T, int E, int k,
-                             const void* x, int h, float* dl, void* dw_router,
+                             const void* x, int h, float* dl, float* rpart, void* dw_router,
                              float* dlogit_bias, hipStream_t s);
 hipError_t launch_dx_final(const void* dxp, int ldp, const int32_t* assign_row, int k,
                            int64_t rows, int has_shared, const float* dl, const void* w_router,

@@ -502,11 +502,17 @@ def _ffn_backward(xr, dO, w1, w3, w2):
 
 def moe_backward(x, w_router, w1, w3, w2, dy, *, k: int, gate: str, C: Optional[int] = None,
                  logit_bias=None, select_bias=None, shared=None, idx=None,
-                 drop: str = "token", priority=None) -> dict:
+                 drop: str = "token", priority=None, tokens=None) -> dict:
     """Gradients of L = sum(y * dy) for the layer forward (same arguments as
     moe_forward; ``idx``/``priority`` fix the routing to another choice).
     Returns fp64 dx [T,h], dw_router [E,h], dlogit_bias [E], dw1/dw3 [E,F,h],
-    dw2 [E,h,F], dws1/dws3/dws2 (shared expert), dgate [T,k], dlogits [T,E]."""
+    dw2 [E,h,F], dws1/dws3/dws2 (shared expert), dgate [T,k], dlogits [T,E].
+    ``tokens``: only dx, dgate and dlogits of these tokens (rows in that
+    order), token by token; the weight gradients are not computed."""
+    if tokens is not None:
+        return _backward_rows(x, w_router, w1, w3, w2, dy, k=k, gate=gate, C=C,
+                              logit_bias=logit_bias, select_bias=select_bias, shared=shared,
+                              idx=idx, drop=drop, priority=priority, tokens=tokens)
     x = np.asarray(x)
     T, h = x.shape
     E = np.asarray(w_router).shape[0]
@@ -549,3 +555,42 @@ def moe_backward(x, w_router, w1, w3, w2, dy, *, k: int, gate: str, C: Optional[
     out["idx"] = idx
     out["maps"] = fwd["maps"]
     return out
+
+
+def _backward_rows(x, w_router, w1, w3, w2, dy, *, k, gate, C, logit_bias, select_bias, shared,
+                   idx, drop, priority, tokens) -> dict:
+    """dx, dgate and dlogits of the given tokens only (see moe_backward)."""
+    fwd = moe_forward(x, w_router, w1, w3, w2, k=k, gate=gate, C=C, logit_bias=logit_bias,
+                      select_bias=select_bias, idx=idx, maps_only=True, drop=drop,
+                      priority=priority)
+    tok = np.asarray(tokens, dtype=np.int64)
+    l = _f64(fwd["logits"])[tok]
+    sel = fwd["idx"].astype(np.int64)[tok]
+    kept = fwd["maps"]["assign_row"][tok] >= 0
+    g = _f64(fwd["gates"])[tok]
+    xs = _f64(np.asarray(x)[tok])
+    dY = _f64(np.asarray(dy)[tok])
+    dx = np.zeros_like(xs)
+    dg = np.zeros((len(tok), k))
+    for n in range(len(tok)):
+        for j in range(k):
+            if not kept[n, j]:
+                continue
+            e = int(sel[n, j])
+            W1, W3, W2 = _f64(w1[e]), _f64(w3[e]), _f64(w2[e])
+            a1 = W1 @ xs[n]
+            a3 = W3 @ xs[n]
+            s = 1.0 / (1.0 + np.exp(-a1))
+            u = a1 * s * a3
+            dg[n, j] = float(dY[n] @ (W2 @ u))
+            dU = (g[n, j] * dY[n]) @ W2
+            dx[n] += (dU * a3 * (s + a1 * s * (1.0 - s))) @ W1 + (dU * a1 * s) @ W3
+    if shared is not None:
+        ws1, ws3, ws2 = (_f64(w) for w in shared)
+        a1 = xs @ ws1.T
+        a3 = xs @ ws3.T
+        s = 1.0 / (1.0 + np.exp(-a1))
+        dU = dY @ ws2
+        dx += (dU * a3 * (s + a1 * s * (1.0 - s))) @ ws1 + (dU * a1 * s) @ ws3
+    dl = _gates_backward(l, sel, dg, gate)
+    return {"dx": dx + dl @ _f64(w_router), "dgate": dg, "dlogits": dl, "tokens": tok}

@@ -474,3 +474,35 @@ def test_full_size_routing_and_sampled_outputs(name):
     assert lb_err <= 1e-4
     del gpu, inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["worked_example", "deepseek_v3"])
+def test_full_size_backward_sampled(name):
+    """The backward at full size, launched as the benchmark launches it:
+    dx and the gate gradients of sampled tokens against the oracle's
+    token-by-token rows; every gradient finite."""
+    cfg = CONFIGS[name]
+    print(f"[case] full backward {name} T={cfg.T} h={cfg.h} E={cfg.E} k={cfg.k} F={cfg.F}",
+          flush=True)
+    torch.cuda.empty_cache()
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    gpu = run_forward(cfg, inp, C_lib)
+    dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=DEV)
+    g = run_backward(cfg, inp, C_lib, gpu, dy)
+    for key, v in g.items():
+        assert bool(torch.isfinite(v.float()).all()), key
+    rng = np.random.default_rng(1)
+    tok = np.array(sorted(set(rng.choice(cfg.T, 6, replace=False).tolist()) | {0, cfg.T - 1}))
+    x, wr, w1, w3, w2, lb, shared = oracle_weights(cfg, inp)
+    sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
+    ref = oracle.moe_backward(x, wr, w1, w3, w2, np32(dy), k=cfg.k, gate=cfg.gate, C=C_ref,
+                              logit_bias=lb, select_bias=sb, shared=shared,
+                              idx=gpu["topk_idx"].cpu().numpy(), tokens=tok)
+    t = torch.as_tensor(tok, device=DEV)
+    e_dx = rel_err(np32(g["dx"][t]), ref["dx"])
+    e_dg = rel_err(np32(g["dgate"][t]), ref["dgate"])
+    _report(f"full_backward_{name}", sampled=len(tok), dx=f"{e_dx:.2e}", dgate=f"{e_dg:.2e}")
+    assert e_dx <= 2e-2 and e_dg <= 2e-2
+    del g, gpu, inp
+    torch.cuda.empty_cache()

@@ -592,3 +592,16 @@ def test_backward_gate_gradient_is_the_output_dot():
                             gate="softmax_topk", logit_bias=p["logit_bias"])
     assert np.abs(g["dlogits"]).max() == 0.0
     assert np.abs(g["dw_router"]).max() == 0.0
+
+
+def test_backward_rows_match_full_backward():
+    """The token-by-token path gives the full backward's rows."""
+    p, dy = _tiny_layer(13, shared=True, T=9)
+    sh = (p["ws1"], p["ws3"], p["ws2"])
+    kw = dict(k=2, gate="softmax_all_topk", C=4, logit_bias=p["logit_bias"], shared=sh)
+    full = oracle.moe_backward(p["x"], p["w_router"], p["w1"], p["w3"], p["w2"], dy, **kw)
+    tok = np.array([7, 0, 3])
+    part = oracle.moe_backward(p["x"], p["w_router"], p["w1"], p["w3"], p["w2"], dy, tokens=tok,
+                               **kw)
+    for key in ("dx", "dgate", "dlogits"):
+        np.testing.assert_allclose(part[key], full[key][tok], rtol=1e-12, atol=1e-12)
