@@ -225,24 +225,29 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FI][4], const T
           for (int e = 0; e < 2; ++e) {
             const int r = 4 * b + 2 * p + e;
             const float z = acc[i][j][r];
-            v[e] = SWIGLU ? z / (1.f + __expf(-z)) * acc[i][j + 2][r] : z;
+            // silu(z) * a3 = z * a3 / (1 + e^-z), e^-z = 2^(-z * log2(e)):
+            // hardware exp2 and reciprocal (the result is rounded to bf16)
+            v[e] = SWIGLU ? z * acc[i][j + 2][r] *
+                                __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f))
+                          : z;
           }
           q[b][p] = pack_bf16x2(v[0], v[1]);
         }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        // the low lane keeps run 2c and receives the high lane's run 2c;
-        // the high lane keeps run 2c+1 and receives the low lane's run 2c+1
-        uint32_t keep[2], give[2], got[2];
+        // v_permlane32_swap trades the high half of its first operand with
+        // the low half of its second: with runs 2c and 2c+1 as the operands,
+        // lane l < 32 gets (its run 2c, lane l+32's run 2c) and lane l+32
+        // (lane l's run 2c+1, its run 2c+1), 8 consecutive columns each
+        uint32_t lo[2], up[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          keep[p] = hi ? q[2 * c + 1][p] : q[2 * c][p];
-          give[p] = hi ? q[2 * c][p] : q[2 * c + 1][p];
-          got[p] = (uint32_t)__shfl_xor((int)give[p], 32, 64);
+          const auto r = __builtin_amdgcn_permlane32_swap(q[2 * c][p], q[2 * c + 1][p], false, false);
+          lo[p] = r[0];
+          up[p] = r[1];
         }
-        const uint4 v = hi ? uint4{got[0], got[1], keep[0], keep[1]}
-                           : uint4{keep[0], keep[1], got[0], got[1]};
-        if (ok) *reinterpret_cast<uint4*>(orow + col0 + 16 * c + 8 * hi) = v;
+        if (ok)
+          *reinterpret_cast<uint4*>(orow + col0 + 16 * c + 8 * hi) = uint4{lo[0], lo[1], up[0], up[1]};
       }
     }
   }
