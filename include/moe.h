@@ -291,10 +291,11 @@ int moe_load_balance(const moe_cfg_t* cfg, const float* logits,
  *   route    the routing outputs of the forward: logits, topk_idx, topk_gate,
  *            expert_counts, expert_offsets, assign_row (all required)
  *   dy [T,h] dtype in;  grads  see moe_grads_t.
- * bf16 layers and the TOPK / TOPK_SCORE_DROP routings only (else
- * MOE_ERR_UNSUPPORTED).  Gradient sums in fp32; dx, weight gradients and the
- * intermediates (a1, a3, u, dO, dU, dA, dx_perm) stored as bf16.  Every sum
- * has a fixed order: the same bits on every run.                          */
+ * bf16 and fp32 layers, the TOPK / TOPK_SCORE_DROP routings (expert
+ * choice: MOE_ERR_UNSUPPORTED).  Gradient sums in fp32; dx, weight
+ * gradients and the intermediates (a1, a3, u, dO, dU, dA, dx_perm) stored in
+ * the layer's dtype.  Every sum has a fixed order: the same bits on every
+ * run.                                                                    */
 int moe_backward_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes);
 int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
                  const void* dy, const moe_route_out_t* route, const moe_grads_t* grads,

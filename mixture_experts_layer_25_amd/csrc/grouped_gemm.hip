@@ -644,27 +644,55 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GroupedGemmArgs a) {
   __shared__ float B3s[SWIGLU ? FBK : 1][FBN + 4];
 
   const int NT = a.N / FBN;
-  const int64_t L = plain_tile(a, NT, blockIdx.x);
-  if (L < 0) return;
-  const Tile tl = tile_of(a, NT, L, FBM);
+  Tile tl;
+  int kbeg = 0, klen = a.K;
+  if (a.kgroup) {
+    // every group: MT x NT tiles of its m_fixed x N output, row tile
+    // fastest, reduced over the group's own K range
+    const int MT = (a.m_fixed + FBM - 1) / FBM;
+    const int64_t L = blockIdx.x;
+    if (L >= (int64_t)a.G * MT * NT) return;
+    const int64_t per = (int64_t)MT * NT;
+    const int gl = (int)(L / per);
+    tl.g = a.kg0 + gl;
+    const int64_t rem = L - (int64_t)gl * per;
+    tl.nt = (int)(rem / MT);
+    tl.mt = (int)(rem - (int64_t)tl.nt * MT);
+    tl.m_valid = min(FBM, a.m_fixed - tl.mt * FBM);
+    tl.a_row = (int64_t)tl.mt * FBM;
+    tl.o_row = tl.a_row;
+    kbeg = a.ktab[tl.g];
+    klen = a.ktab[a.kt_size + tl.g];
+  } else {
+    const int64_t L = plain_tile(a, NT, blockIdx.x);
+    if (L < 0) return;
+    tl = tile_of(a, NT, L, FBM);
+  }
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int K = a.K, N = a.N;
-  const bool shared = tl.g >= a.E_routed;
+  const int N = a.N;
+  const bool shared = !a.kgroup && tl.g >= a.E_routed;
   const bool a_shared = shared && !a.a_from_out_rows;
   const float* A = (const float*)(a_shared ? a.A_shared : a.A);
   const int lda = a_shared ? a.lda_shared : a.lda;
+  const int64_t ldb = a.ldb ? a.ldb : a.K;
   const float* B0 = (const float*)(shared ? a.B0s : a.B0);
   const float* B1 = (const float*)(shared ? a.B1s : a.B1);
-  if (!shared) {
+  if (!shared && !a.kgroup) {
     B0 += (int64_t)tl.g * a.b_stride;
-    if (SWIGLU) B1 += (int64_t)tl.g * a.b_stride;
+    if (SWIGLU || a.b_split) B1 += (int64_t)tl.g * a.b_stride;
   }
   const int lr = tid >> 2, lk = (tid & 3) * 4;
   const int ar = lr < tl.m_valid ? lr : tl.m_valid - 1;
   const float* ap = A + (tl.a_row + ar) * lda + lk;
   const int64_t n0 = (int64_t)tl.nt * FBN;
-  const float* bp = B0 + (n0 + lr) * K + lk;
-  const float* b3p = SWIGLU ? B1 + (n0 + lr) * K + lk : nullptr;
+  // b_split: B rows [0, N/2) from B0, [N/2, N) from B1 (64-row tiles never
+  // straddle N/2, a multiple of 64)
+  const float* bp;
+  if (!SWIGLU && a.b_split && n0 >= N / 2)
+    bp = B1 + (n0 - N / 2 + lr) * ldb + lk;
+  else
+    bp = B0 + (n0 + lr) * ldb + lk;
+  const float* b3p = SWIGLU ? B1 + (n0 + lr) * ldb + lk : nullptr;
 
   float acc[4][4], acc3[4][4];
 #pragma unroll
@@ -672,7 +700,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GroupedGemmArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[i][c] = acc3[i][c] = 0.f;
 
-  for (int k0 = 0; k0 < K; k0 += FBK) {
+  for (int k0 = kbeg; k0 < kbeg + klen; k0 += FBK) {
     const float4 av = *reinterpret_cast<const float4*>(ap + k0);
     const float4 bv = *reinterpret_cast<const float4*>(bp + k0);
     As[lk + 0][lr] = av.x; As[lk + 1][lr] = av.y; As[lk + 2][lr] = av.z; As[lk + 3][lr] = av.w;
@@ -704,17 +732,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GroupedGemmArgs a) {
     }
     __syncthreads();
   }
-  float* out = (float*)a.out;
+  // output row r of the group: out0 + r*ldo, or out1 + (r - split_rows)*ldo
+  // from split_rows on; groups split along K write group g at
+  // (g - kg0)*out_stride
+  const int64_t go = a.kgroup ? (int64_t)(tl.g - a.kg0) * a.out_stride : 0;
+  float* out0 = (float*)a.out + go;
+  float* out1 = a.out1 ? (float*)a.out1 + go : nullptr;
+  const int64_t split = (a.out1 && a.split_rows > 0) ? a.split_rows : INT64_MAX;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = ty * 4 + i;
     if (row >= tl.m_valid) continue;
+    const int64_t r = tl.o_row + row;
+    float* orow = r < split ? out0 + r * a.ldo : out1 + (r - split) * a.ldo;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int64_t col = n0 + tx + 16 * c;
       float v = acc[i][c];
       if (SWIGLU) v = v / (1.f + expf(-v)) * acc3[i][c];
-      out[(tl.o_row + row) * a.ldo + col] = v;
+      orow[col] = v;
     }
   }
 }
@@ -745,7 +781,8 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, const GroupedGemmArgs& a,
     }
   } else {
     const int NT = a.N / FBN;
-    const int64_t nb = a.max_m_tiles * NT;
+    const int64_t nb = a.kgroup ? (int64_t)a.G * ((a.m_fixed + FBM - 1) / FBM) * NT
+                                : a.max_m_tiles * NT;
     if (nb <= 0) return hipSuccess;
     if (swiglu)
       hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, a);

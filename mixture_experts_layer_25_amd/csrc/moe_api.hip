@@ -335,14 +335,16 @@ MOE_API int moe_load_balance(const moe_cfg_t* cfg, const float* logits,
 
 namespace {
 
-// Workspace of moe_backward (bf16): tile and K tables, the recomputed and
+// Workspace of moe_backward: tile and K tables, the recomputed and
 // backward activations (rows padded like the forward's), the transposed
-// weights, and the K-major copies the weight-gradient GEMMs read.
+// weights, and the K-major copies the weight-gradient GEMMs read; tensors
+// are in the layer's element type (2 or 4 bytes).
 struct BwdLayout {
   size_t gtab, kta, kto, rowtok, dg, dl, rpart, partials, xp, a13, u, o, dO, dU, dA, dxp;
   size_t w2t, w13t, dOT, uT, dAT, xpT, total;
   int ldh, ldf, ld13;
   int64_t ktb;
+  size_t esz;
 };
 
 BwdLayout bwd_layout_of(const moe_cfg_t& c) {
@@ -355,6 +357,8 @@ BwdLayout bwd_layout_of(const moe_cfg_t& c) {
   L.ldf = (int)F + 64;
   L.ld13 = 2 * (int)F + 64;
   L.ktb = (rows_all + 64 * G + 63) / 64 * 64;   // every group's rows rounded up to 64
+  L.esz = c.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const size_t es = L.esz;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -369,20 +373,20 @@ BwdLayout bwd_layout_of(const moe_cfg_t& c) {
   L.dl = take((size_t)(T * E) * 4);
   L.rpart = take((size_t)(32 * E * h) * 4);
   L.partials = take((size_t)moe::kSplitPartialFloats * 4);
-  L.xp = take((size_t)rows * L.ldh * 2);
-  L.a13 = take((size_t)rows_all * L.ld13 * 2);
-  L.u = take((size_t)rows_all * L.ldf * 2);
-  L.o = take((size_t)rows_all * L.ldh * 2);
-  L.dO = take((size_t)rows_all * L.ldh * 2);
-  L.dU = take((size_t)rows_all * L.ldf * 2);
-  L.dA = take((size_t)rows_all * L.ld13 * 2);
-  L.dxp = take((size_t)rows_all * L.ldh * 2);
-  L.w2t = take((size_t)(G * F * h) * 2);
-  L.w13t = take((size_t)(G * h * 2 * F) * 2);
-  L.dOT = take((size_t)(h * L.ktb) * 2);
-  L.uT = take((size_t)(F * L.ktb) * 2);
-  L.dAT = take((size_t)(2 * F * L.ktb) * 2);
-  L.xpT = take((size_t)(h * L.ktb) * 2);
+  L.xp = take((size_t)rows * L.ldh * es);
+  L.a13 = take((size_t)rows_all * L.ld13 * es);
+  L.u = take((size_t)rows_all * L.ldf * es);
+  L.o = take((size_t)rows_all * L.ldh * es);
+  L.dO = take((size_t)rows_all * L.ldh * es);
+  L.dU = take((size_t)rows_all * L.ldf * es);
+  L.dA = take((size_t)rows_all * L.ld13 * es);
+  L.dxp = take((size_t)rows_all * L.ldh * es);
+  L.w2t = take((size_t)(G * F * h) * es);
+  L.w13t = take((size_t)(G * h * 2 * F) * es);
+  L.dOT = take((size_t)(h * L.ktb) * es);
+  L.uT = take((size_t)(F * L.ktb) * es);
+  L.dAT = take((size_t)(2 * F * L.ktb) * es);
+  L.xpT = take((size_t)(h * L.ktb) * es);
   L.total = off;
   return L;
 }
@@ -404,8 +408,7 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
   if (st != MOE_OK) return st;
   const moe_cfg_t& c = *cfg;
   if (c.T == 0) return MOE_OK;
-  if (c.dtype != MOE_DTYPE_BF16 || c.routing == MOE_ROUTE_EXPERT_CHOICE)
-    return MOE_ERR_UNSUPPORTED;
+  if (c.routing == MOE_ROUTE_EXPERT_CHOICE) return MOE_ERR_UNSUPPORTED;
   if (!w || !x || !dy || !route || !grads || !w->w_router || !w->w1 || !w->w3 || !w->w2)
     return MOE_ERR_INVALID_ARG;
   const moe_route_out_t& r = *route;
@@ -460,16 +463,16 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
   MOE_TRY(moe::launch_permute(c.dtype, x, r.assign_row, r.expert_counts, T, h, E, k, c.capacity,
                               xp, L.ldh, at<int32_t>(ws, L.rowtok), s));
   // transposed weights: w2t[g] = w2[g]^T [F,h]; w13t[g] = [w1[g]^T | w3[g]^T] [h,2F]
-  MOE_TRY(moe::launch_transpose(w->w2, (int64_t)h * F, h, F, w2t, (int64_t)F * h, h, 0, E, s));
-  MOE_TRY(moe::launch_transpose(w->w1, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F, 2 * F, 0,
+  MOE_TRY(moe::launch_transpose(c.dtype, w->w2, (int64_t)h * F, h, F, w2t, (int64_t)F * h, h, 0, E, s));
+  MOE_TRY(moe::launch_transpose(c.dtype, w->w1, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F, 2 * F, 0,
                                 E, s));
-  MOE_TRY(moe::launch_transpose(w->w3, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F, 2 * F, F,
+  MOE_TRY(moe::launch_transpose(c.dtype, w->w3, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F, 2 * F, F,
                                 E, s));
   if (c.has_shared) {
-    MOE_TRY(moe::launch_transpose(w->ws2, 0, h, F, w2t + (size_t)E * F * h * 2, 0, h, 0, 1, s));
-    MOE_TRY(moe::launch_transpose(w->ws1, 0, F, h, w13t + (size_t)E * h * 2 * F * 2, 0, 2 * F, 0,
+    MOE_TRY(moe::launch_transpose(c.dtype, w->ws2, 0, h, F, w2t + (size_t)E * F * h * L.esz, 0, h, 0, 1, s));
+    MOE_TRY(moe::launch_transpose(c.dtype, w->ws1, 0, F, h, w13t + (size_t)E * h * 2 * F * L.esz, 0, 2 * F, 0,
                                   1, s));
-    MOE_TRY(moe::launch_transpose(w->ws3, 0, F, h, w13t + (size_t)E * h * 2 * F * 2, 0, 2 * F, F,
+    MOE_TRY(moe::launch_transpose(c.dtype, w->ws3, 0, F, h, w13t + (size_t)E * h * 2 * F * L.esz, 0, 2 * F, F,
                                   1, s));
   }
 
@@ -486,7 +489,7 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
   a.B0 = w->w1; a.B1 = w->w3; a.B0s = w->ws1; a.B1s = w->ws3; a.b_split = 1;
   a.b_stride = (int64_t)F * h; a.K = h; a.N = 2 * F; a.out = a13; a.ldo = L.ld13;
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
-  MOE_TRY(moe::launch_swiglu_fwd(a13, L.ld13, rows_all, F, u, L.ldf, s));
+  MOE_TRY(moe::launch_swiglu_fwd(c.dtype, a13, L.ld13, rows_all, F, u, L.ldf, s));
   // expert outputs o = u w2^T (the forward's y_perm)
   a = base;
   a.A = u; a.lda = L.ldf; a.a_from_out_rows = 1;
@@ -494,27 +497,27 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
   a.out = o; a.ldo = L.ldh;
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
   // dO rows, gate gradients
-  MOE_TRY(moe::launch_scatter_dy(dy, r.assign_row, r.topk_gate, r.expert_counts, T, h, E, k,
+  MOE_TRY(moe::launch_scatter_dy(c.dtype, dy, r.assign_row, r.topk_gate, r.expert_counts, T, h, E, k,
                                  c.capacity, rows, c.has_shared, dO, L.ldh, s));
-  MOE_TRY(moe::launch_gate_grad(dy, o, L.ldh, r.assign_row, T, h, k, dg, s));
+  MOE_TRY(moe::launch_gate_grad(c.dtype, dy, o, L.ldh, r.assign_row, T, h, k, dg, s));
   // dU = dO w2, then dA, then dx_perm = dA [w1; w3]
   a = base;
   a.A = dO; a.lda = L.ldh; a.a_from_out_rows = 1;
-  a.B0 = w2t; a.B0s = w2t + (size_t)E * F * h * 2; a.b_stride = (int64_t)F * h;
+  a.B0 = w2t; a.B0s = w2t + (size_t)E * F * h * L.esz; a.b_stride = (int64_t)F * h;
   a.K = h; a.N = F; a.out = dU; a.ldo = L.ldf;
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
-  MOE_TRY(moe::launch_swiglu_bwd(a13, L.ld13, dU, L.ldf, rows_all, F, dA, L.ld13, s));
+  MOE_TRY(moe::launch_swiglu_bwd(c.dtype, a13, L.ld13, dU, L.ldf, rows_all, F, dA, L.ld13, s));
   a = base;
   a.A = dA; a.lda = L.ld13; a.a_from_out_rows = 1;
-  a.B0 = w13t; a.B0s = w13t + (size_t)E * h * 2 * F * 2; a.b_stride = (int64_t)h * 2 * F;
+  a.B0 = w13t; a.B0s = w13t + (size_t)E * h * 2 * F * L.esz; a.b_stride = (int64_t)h * 2 * F;
   a.K = 2 * F; a.N = h; a.out = dxp; a.ldo = L.ldh;
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
   // K-major copies of each group's rows, then the weight gradients
-  MOE_TRY(moe::launch_transpose_groups(dO, L.ldh, dO, L.ldh, G, kto, G, h, L.ktb, dOT, ktb, s));
-  MOE_TRY(moe::launch_transpose_groups(u, L.ldf, u, L.ldf, G, kto, G, F, L.ktb, uT, ktb, s));
-  MOE_TRY(moe::launch_transpose_groups(dA, L.ld13, dA, L.ld13, G, kto, G, 2 * F, L.ktb, dAT, ktb,
+  MOE_TRY(moe::launch_transpose_groups(c.dtype, dO, L.ldh, dO, L.ldh, G, kto, G, h, L.ktb, dOT, ktb, s));
+  MOE_TRY(moe::launch_transpose_groups(c.dtype, u, L.ldf, u, L.ldf, G, kto, G, F, L.ktb, uT, ktb, s));
+  MOE_TRY(moe::launch_transpose_groups(c.dtype, dA, L.ld13, dA, L.ld13, G, kto, G, 2 * F, L.ktb, dAT, ktb,
                                        s));
-  MOE_TRY(moe::launch_transpose_groups(xp, L.ldh, x, h, E, kta, G, h, L.ktb, xpT, ktb, s));
+  MOE_TRY(moe::launch_transpose_groups(c.dtype, xp, L.ldh, x, h, E, kta, G, h, L.ktb, xpT, ktb, s));
   for (int pass = 0; pass < (c.has_shared ? 2 : 1); ++pass) {
     const bool sh = pass == 1;
     moe::GroupedGemmArgs wg{};
@@ -531,9 +534,9 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
     MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, wg, s));
   }
   // router: dl, dw_router, dlogit_bias; then dx
-  MOE_TRY(moe::launch_router_bwd(r.logits, r.topk_idx, r.topk_gate, dg, c.gate, T, E, k, x, h,
+  MOE_TRY(moe::launch_router_bwd(c.dtype, r.logits, r.topk_idx, r.topk_gate, dg, c.gate, T, E, k, x, h,
                                  dl, at<float>(ws, L.rpart), gr.dw_router, gr.dlogit_bias, s));
-  MOE_TRY(moe::launch_dx_final(dxp, L.ldh, r.assign_row, k, rows, c.has_shared, dl, w->w_router,
+  MOE_TRY(moe::launch_dx_final(c.dtype, dxp, L.ldh, r.assign_row, k, rows, c.has_shared, dl, w->w_router,
                                T, h, E, gr.dx, s));
   return MOE_OK;
 }

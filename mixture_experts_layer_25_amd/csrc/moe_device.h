@@ -44,6 +44,46 @@ __device__ __forceinline__ void st16(void* p, uint4 v) {
   *reinterpret_cast<uint4*>(p) = v;
 }
 
+// Element types of the layer's tensors: bf16 (held as uint16_t bits) or
+// fp32.  Elt<T> converts one element, and 16 bytes (8 bf16 or 4 fp32) at a
+// time, to and from fp32; bf16 stores round to nearest even.
+template <typename T>
+struct Elt;
+template <>
+struct Elt<uint16_t> {
+  static constexpr int kVec = 8;
+  static __device__ __forceinline__ float ld(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+  static __device__ __forceinline__ void st(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+  static __device__ __forceinline__ void unpack(uint4 q, float (&f)[8]) {
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      f[2 * p] = bf16_bits_to_f32(u[p] & 0xFFFFu);
+      f[2 * p + 1] = bf16_bits_to_f32(u[p] >> 16);
+    }
+  }
+  static __device__ __forceinline__ uint4 pack(const float (&f)[8]) {
+    return uint4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                 pack_bf16x2(f[6], f[7])};
+  }
+};
+template <>
+struct Elt<float> {
+  static constexpr int kVec = 4;
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ void unpack(uint4 q, float (&f)[4]) {
+    f[0] = __uint_as_float(q.x);
+    f[1] = __uint_as_float(q.y);
+    f[2] = __uint_as_float(q.z);
+    f[3] = __uint_as_float(q.w);
+  }
+  static __device__ __forceinline__ uint4 pack(const float (&f)[4]) {
+    return uint4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                 __float_as_uint(f[3])};
+  }
+};
+
 // Monotone map of an fp32 value to uint32 (larger float -> larger integer).
 // -0.0 is folded onto +0.0 first so that the two compare equal, as floats do.
 __device__ __forceinline__ uint32_t ordered_bits(float f) {

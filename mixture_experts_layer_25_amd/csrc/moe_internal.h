@@ -92,29 +92,32 @@ hipError_t launch_groups_from_counts(const int32_t* counts, const int32_t* offse
                                      int64_t C, int64_t T, int has_shared, int BM,
                                      int64_t rows, int32_t* gtab, hipStream_t s);
 
-// Backward kernels (backward.hip).
-hipError_t launch_transpose(const void* src, int64_t src_bs, int R, int Cc, void* dst,
+// Backward kernels (backward.hip); dtype as in the ABI (1: bf16, 0: fp32)
+// selects the element type of every tensor argument.
+hipError_t launch_transpose(int dtype, const void* src, int64_t src_bs, int R, int Cc, void* dst,
                             int64_t dst_bs, int dld, int col0, int batches, hipStream_t s);
 hipError_t launch_ktab(const int32_t* gtab, int G, int use_a_rows, int32_t* kt, hipStream_t s);
-hipError_t launch_transpose_groups(const void* src, int sld, const void* src_shared,
+hipError_t launch_transpose_groups(int dtype, const void* src, int sld, const void* src_shared,
                                    int sld_shared, int E_routed, const int32_t* kt, int G,
                                    int Cc, int64_t ktot_bound, void* dst, int dld,
                                    hipStream_t s);
-hipError_t launch_scatter_dy(const void* dy, const int32_t* assign_row, const float* gate,
-                             const int32_t* counts, int64_t T, int h, int E, int k, int64_t C,
-                             int64_t rows, int has_shared, void* dO, int ld, hipStream_t s);
-hipError_t launch_gate_grad(const void* dy, const void* o, int ld, const int32_t* assign_row,
-                            int64_t T, int h, int k, float* dg, hipStream_t s);
-hipError_t launch_swiglu_fwd(const void* a13, int lda13, int64_t rows, int F, void* u, int ldu,
+hipError_t launch_scatter_dy(int dtype, const void* dy, const int32_t* assign_row,
+                             const float* gate, const int32_t* counts, int64_t T, int h, int E,
+                             int k, int64_t C, int64_t rows, int has_shared, void* dO, int ld,
                              hipStream_t s);
-hipError_t launch_swiglu_bwd(const void* a13, int lda13, const void* dU, int ldu, int64_t rows,
-                             int F, void* dA, int ldda, hipStream_t s);
+hipError_t launch_gate_grad(int dtype, const void* dy, const void* o, int ld,
+                            const int32_t* assign_row, int64_t T, int h, int k, float* dg,
+                            hipStream_t s);
+hipError_t launch_swiglu_fwd(int dtype, const void* a13, int lda13, int64_t rows, int F, void* u,
+                             int ldu, hipStream_t s);
+hipError_t launch_swiglu_bwd(int dtype, const void* a13, int lda13, const void* dU, int ldu,
+                             int64_t rows, int F, void* dA, int ldda, hipStream_t s);
 // rpart: 32 * E * h floats of slice sums for dw_router.
-hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gate,
-                             const float* dg, int gate_mode, int64_t T, int E, int k,
-                             const void* x, int h, float* dl, float* rpart, void* dw_router,
-                             float* dlogit_bias, hipStream_t s);
-hipError_t launch_dx_final(const void* dxp, int ldp, const int32_t* assign_row, int k,
+hipError_t launch_router_bwd(int dtype, const float* logits, const int32_t* idx,
+                             const float* gate, const float* dg, int gate_mode, int64_t T, int E,
+                             int k, const void* x, int h, float* dl, float* rpart,
+                             void* dw_router, float* dlogit_bias, hipStream_t s);
+hipError_t launch_dx_final(int dtype, const void* dxp, int ldp, const int32_t* assign_row, int k,
                            int64_t rows, int has_shared, const float* dl, const void* w_router,
                            int64_t T, int h, int E, void* dx, hipStream_t s);
 

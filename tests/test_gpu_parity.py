@@ -84,13 +84,14 @@ def test_forward_matches_oracle(cfg):
 # ------------------------------------------------------------------ backward
 BACKWARD = ["dropless_softmax", "capacity_heavy_drop", "worked_example_small",
             "sigmoid_bias_shared", "zipf_dropless", "split_k_tail", "e40_ragged",
-            "mixtral_bias", "e256_k8_shared", "k_equals_e"]
+            "mixtral_bias", "e256_k8_shared", "k_equals_e",
+            "tiny_fp32", "f32_capacity", "f32_sigmoid_shared"]
 
 
 def run_backward(cfg, inp, C_lib, gpu, dy, routing="topk"):
     c = lib_cfg(cfg, C_lib, routing)
     T, E, k, h, F = cfg.T, cfg.E, cfg.k, cfg.h, cfg.F
-    bf = torch.bfloat16
+    bf = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
     def nan(*shape, dtype=bf):
         return torch.full(shape, float("nan"), dtype=dtype, device=DEV)
@@ -113,13 +114,14 @@ def run_backward(cfg, inp, C_lib, gpu, dy, routing="topk"):
 @pytest.mark.parametrize("name", BACKWARD)
 def test_backward_matches_oracle(name):
     """Every gradient of sum(y * dy) against the oracle's chain rule on the
-    GPU's own routing (top-k choice and drops held fixed)."""
+    GPU's own routing (top-k choice and drops held fixed); normwise max
+    relative error within 2e-2 (bf16 tensors) or 1e-5 (fp32)."""
     cfg = next(c for c in MEDIUM if c.name == name)
     print(f"[case] backward {name}", flush=True)
     inp = gen_inputs(cfg)
     C_lib, C_ref = capacity_of(cfg)
     gpu = run_forward(cfg, inp, C_lib)
-    dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=DEV)
+    dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=DEV, dtype=cfg.dtype)
     g = run_backward(cfg, inp, C_lib, gpu, dy)
     x, wr, w1, w3, w2, lb, shared = oracle_weights(cfg, inp)
     sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
@@ -140,7 +142,7 @@ def test_backward_matches_oracle(name):
         errs[gk] = rel_err(np32(g[gk]), r)
     _report(f"backward_{name}", **{kk: f"{v:.2e}" for kk, v in errs.items()})
     for kk, v in errs.items():
-        assert v <= 2e-2, (kk, v)
+        assert v <= tol_of(cfg), (kk, v)
 
 
 def test_backward_is_deterministic():
