@@ -24,7 +24,8 @@ no permutation buffer, no blocking and no fusion:
 8. two routing variants: capacity drops by gate score instead of token
    order, and expert choice (every expert takes its C best-scoring tokens);
 9. the backward of the layer: gradients of sum(y * dy) with respect to the
-   input, the router and every expert weight, with the routing held fixed.
+   input, the router and every expert weight, with the routing held fixed
+   (token choice, and expert choice with the experts' choices held fixed).
 
 Sources (pages and the part of each that is followed):
 
@@ -554,6 +555,53 @@ def moe_backward(x, w_router, w1, w3, w2, dy, *, k: int, gate: str, C: Optional[
     out["dx"] = dx + dl @ _f64(w_router)
     out["idx"] = idx
     out["maps"] = fwd["maps"]
+    return out
+
+
+def expert_choice_backward(x, w_router, w1, w3, w2, dy, *, C: int, gate: str,
+                           logit_bias=None, shared=None, scores=None) -> dict:
+    """Gradients of L = sum(y * dy) for expert_choice_forward, the experts'
+    choices held fixed.  The gate of a chosen (t, e) is router_probs[t, e]
+    itself, not renormalised over the experts that chose t, so the logits
+    get the Jacobian of router_probs applied to dgate [T,E] (zero where e did
+    not choose t): the token-choice gate Jacobians with every expert as a
+    slot (softmax over all E; sigmoids normalised over all E).  Returns fp64
+    dx, dw_router, dlogit_bias, dw1/dw3/dw2, dws1/dws3/dws2 (shared expert),
+    dgate [T,E], dlogits [T,E]."""
+    x = np.asarray(x)
+    T, h = x.shape
+    logits = router_logits(x, w_router, logit_bias)
+    m = expert_choice(logits, C, gate, scores)
+    E = m["sel_row"].shape[1]
+    chosen = m["sel_row"] >= 0
+    g = _f64(m["gate"])
+    xs = _f64(x)
+    dY = _f64(dy)
+    dx = np.zeros((T, h))
+    dg = np.zeros((T, E))
+    dw1, dw3, dw2 = [], [], []
+    for e in range(E):                      # C >= 1: every expert has rows
+        tt = np.nonzero(chosen[:, e])[0]
+        dO = g[tt, e][:, None] * dY[tt]
+        o, dxe, d1, d3, d2 = _ffn_backward(xs[tt], dO, w1[e], w3[e], w2[e])
+        dw1.append(d1)
+        dw3.append(d3)
+        dw2.append(d2)
+        dg[tt, e] = (dY[tt] * o).sum(axis=1)
+        np.add.at(dx, tt, dxe)
+    out = {"dw1": np.stack(dw1), "dw3": np.stack(dw3), "dw2": np.stack(dw2), "dgate": dg}
+    if shared is not None:
+        ws1, ws3, ws2 = shared
+        _, dxs, out["dws1"], out["dws3"], out["dws2"] = _ffn_backward(xs, dY, ws1, ws3, ws2)
+        dx += dxs
+    every = np.tile(np.arange(E), (T, 1))
+    mode = "sigmoid_topk_norm" if gate == "sigmoid_topk_norm" else "softmax_all_topk"
+    dl = _gates_backward(_f64(logits), every, dg, mode)
+    out["dlogits"] = dl
+    out["dlogit_bias"] = dl.sum(axis=0)
+    out["dw_router"] = dl.T @ xs
+    out["dx"] = dx + dl @ _f64(w_router)
+    out["maps"] = m
     return out
 
 

@@ -584,6 +584,55 @@ def test_backward_matches_finite_differences(gate, C, drop, shared):
         assert float(np.abs(fd - grad).max()) <= 2e-3 * scale, name
 
 
+def _ec_loss(p, dy, C, gate):
+    sh = (p["ws1"], p["ws3"], p["ws2"]) if "ws1" in p else None
+    y = oracle.expert_choice_forward(p["x"], p["w_router"], p["w1"], p["w3"], p["w2"], C=C,
+                                     gate=gate, logit_bias=p["logit_bias"], shared=sh)["y"]
+    return float((y * dy).sum())
+
+
+@pytest.mark.parametrize("gate,shared", [("softmax_all_topk", False),
+                                         ("sigmoid_topk_norm", True)])
+def test_expert_choice_backward_matches_finite_differences(gate, shared):
+    """Every gradient of the oracle's expert-choice backward against central
+    differences of sum(y * dy) through the oracle's expert-choice forward,
+    on a tiny layer whose choices do not move under the perturbation (the
+    C-th and (C+1)-th scores of every expert well apart)."""
+    C = 2
+    for seed in range(21, 200):
+        p, dy = _tiny_layer(seed, shared)
+        lg = oracle.router_logits(p["x"], p["w_router"], p["logit_bias"])
+        sc = -np.sort(-oracle.router_probs(lg, gate), axis=0)
+        if (sc[C - 1] - sc[C]).min() > 0.01:
+            break
+    else:
+        raise AssertionError("no well-separated layer")
+    sh = (p["ws1"], p["ws3"], p["ws2"]) if shared else None
+    g = oracle.expert_choice_backward(p["x"], p["w_router"], p["w1"], p["w3"], p["w2"], dy, C=C,
+                                      gate=gate, logit_bias=p["logit_bias"], shared=sh)
+    # some token is chosen by several experts and some by none
+    n_chosen = (g["maps"]["sel_row"] >= 0).sum(axis=1)
+    assert n_chosen.max() >= 2 and n_chosen.min() == 0
+    names = {"x": "dx", "w_router": "dw_router", "w1": "dw1", "w3": "dw3", "w2": "dw2",
+             "logit_bias": "dlogit_bias"}
+    if shared:
+        names.update({"ws1": "dws1", "ws3": "dws3", "ws2": "dws2"})
+    eps = 1e-3
+    for name, gname in names.items():
+        grad = g[gname]
+        fd = np.zeros_like(grad)
+        for i in np.ndindex(grad.shape):
+            old = p[name][i]
+            p[name][i] = old + eps
+            lp = _ec_loss(p, dy, C, gate)
+            p[name][i] = old - eps
+            lm = _ec_loss(p, dy, C, gate)
+            p[name][i] = old
+            fd[i] = (lp - lm) / (2 * eps)
+        scale = max(1.0, float(np.abs(fd).max()))
+        assert float(np.abs(fd - grad).max()) <= 2e-3 * scale, name
+
+
 def test_backward_gate_gradient_is_the_output_dot():
     """k = 1 with softmax over the selected expert: the gate is 1 whatever
     the logits, so the router gets no gradient at all."""
