@@ -260,17 +260,20 @@ def main() -> int:
     # backward of the same layer with this routing (not part of the step):
     # gradients of sum(y * dy) for x, the router and every expert weight
     bwd = None
-    if args.routing != "expert_choice" and cfg.dtype == "bf16" and not args.no_backward:
+    if not args.no_backward:
         from moe_inputs import normal
-        dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=dev)
+        dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=dev, dtype=cfg.dtype)
+        slots = cfg.E if args.routing == "expert_choice" else cfg.k
         full_route = {"logits": logits,
                       "topk_idx": torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev),
-                      "topk_gate": torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev),
+                      "topk_gate": torch.empty((cfg.T, slots), dtype=torch.float32, device=dev),
                       "expert_counts": counts,
                       "expert_offsets": torch.empty(cfg.E + 1, dtype=torch.int32, device=dev),
-                      "assign_row": torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev)}
+                      "assign_row": torch.empty(cfg.T * slots, dtype=torch.int32, device=dev)}
+        if args.routing == "expert_choice":
+            full_route["probs"] = torch.empty((cfg.E, cfg.T), dtype=torch.float32, device=dev)
         moe.moe_forward(c, weights, inp["x"], y, full_route, ws)
-        bf = torch.bfloat16
+        bf = tdt
         grads = {"dx": torch.empty((cfg.T, cfg.h), dtype=bf, device=dev),
                  "dw_router": torch.empty((cfg.E, cfg.h), dtype=bf, device=dev),
                  "dw1": torch.empty((cfg.E, cfg.F, cfg.h), dtype=bf, device=dev),

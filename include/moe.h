@@ -169,7 +169,7 @@ typedef struct moe_grads {
   void* dws1;          /* shared expert [F,h], required iff has_shared */
   void* dws3;          /* [F,h] */
   void* dws2;          /* [h,F] */
-  float* dgate;        /* [T,k] fp32 dL/dgate, or NULL (kept in the workspace) */
+  float* dgate;        /* [T,k] ([T,E] expert choice) fp32 dL/dgate, or NULL */
 } moe_grads_t;
 
 /* Host-only helpers (no device work, callable without a GPU). ---------- */
@@ -291,11 +291,14 @@ int moe_load_balance(const moe_cfg_t* cfg, const float* logits,
  *   route    the routing outputs of the forward: logits, topk_idx, topk_gate,
  *            expert_counts, expert_offsets, assign_row (all required)
  *   dy [T,h] dtype in;  grads  see moe_grads_t.
- * bf16 and fp32 layers, the TOPK / TOPK_SCORE_DROP routings (expert
- * choice: MOE_ERR_UNSUPPORTED).  Gradient sums in fp32; dx, weight
- * gradients and the intermediates (a1, a3, u, dO, dU, dA, dx_perm) stored in
- * the layer's dtype.  Every sum has a fixed order: the same bits on every
- * run.                                                                    */
+ * bf16 and fp32 layers, every routing.  With MOE_ROUTE_EXPERT_CHOICE the
+ * experts' choices are held fixed, topk_idx is not read, topk_gate and
+ * assign_row are the forward's [T,E] slots and dgate is [T,E]; the gate of
+ * a chosen (t, e) is the router probability itself, so the logits get that
+ * distribution's Jacobian over all E (10.5 section 10.5.6).  Gradient sums
+ * in fp32; dx, weight gradients and the intermediates (a1, a3, u, dO, dU,
+ * dA, dx_perm) stored in the layer's dtype.  Every sum has a fixed order:
+ * the same bits on every run.                                             */
 int moe_backward_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes);
 int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
                  const void* dy, const moe_route_out_t* route, const moe_grads_t* grads,

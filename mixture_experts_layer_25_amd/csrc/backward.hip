@@ -266,6 +266,9 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict
 }
 
 // dl[t,:] from dg[t,:] for the gate modes (one thread per token; fp32).
+// idx NULL: slot j is expert j (expert choice, k = E slots, the gate of an
+// unchosen slot 0), with mode 1 for the softmax over all E and mode 2 for
+// the sigmoids normalised over all E.
 __global__ __launch_bounds__(256) void gates_bwd_kernel(const float* __restrict__ logits,
                                                         const int32_t* __restrict__ idx,
                                                         const float* __restrict__ gate,
@@ -276,13 +279,14 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const float* __restrict_
   if (t >= T) return;
   const float* l = logits + t * E;
   float* d = dl + t * E;
+  auto ex = [&](int j) { return idx ? idx[t * k + j] : j; };
   for (int e = 0; e < E; ++e) d[e] = 0.f;
   float gd = 0.f;                     // sum_j g_j dg_j
   for (int j = 0; j < k; ++j) gd += gate[t * k + j] * dg[t * k + j];
   if (gate_mode == 0) {               // softmax over the selected
     for (int j = 0; j < k; ++j) {
       const float g = gate[t * k + j];
-      d[idx[t * k + j]] += g * (dg[t * k + j] - gd);
+      d[ex(j)] += g * (dg[t * k + j] - gd);
     }
   } else if (gate_mode == 1) {        // softmax over all E, selected values
     float m = -INFINITY;
@@ -291,14 +295,14 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const float* __restrict_
     for (int e = 0; e < E; ++e) den += expf(l[e] - m);
     for (int e = 0; e < E; ++e) d[e] = -(expf(l[e] - m) / den) * gd;
     for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
+      const int e = ex(j);
       d[e] += (expf(l[e] - m) / den) * dg[t * k + j];
     }
   } else {                            // sigmoid normalised over the selected
     float S = 0.f;
-    for (int j = 0; j < k; ++j) S += 1.f / (1.f + expf(-l[idx[t * k + j]]));
+    for (int j = 0; j < k; ++j) S += 1.f / (1.f + expf(-l[ex(j)]));
     for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
+      const int e = ex(j);
       const float s = 1.f / (1.f + expf(-l[e]));
       d[e] += (dg[t * k + j] - gd) / S * s * (1.f - s);
     }

@@ -369,7 +369,8 @@ BwdLayout bwd_layout_of(const moe_cfg_t& c) {
   L.kta = take((size_t)(4 * G) * 4);
   L.kto = take((size_t)(4 * G) * 4);
   L.rowtok = take((size_t)rows * 4);
-  L.dg = take((size_t)(T * k) * 4);
+  const int64_t slots = c.routing == MOE_ROUTE_EXPERT_CHOICE ? E : k;   // gates per token
+  L.dg = take((size_t)(T * slots) * 4);
   L.dl = take((size_t)(T * E) * 4);
   L.rpart = take((size_t)(32 * E * h) * 4);
   L.partials = take((size_t)moe::kSplitPartialFloats * 4);
@@ -408,13 +409,15 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
   if (st != MOE_OK) return st;
   const moe_cfg_t& c = *cfg;
   if (c.T == 0) return MOE_OK;
-  if (c.routing == MOE_ROUTE_EXPERT_CHOICE) return MOE_ERR_UNSUPPORTED;
+  // expert choice: the E experts are each token's slots (assign_row and
+  // topk_gate [T,E] as the forward wrote them; no topk_idx)
+  const bool ec = c.routing == MOE_ROUTE_EXPERT_CHOICE;
   if (!w || !x || !dy || !route || !grads || !w->w_router || !w->w1 || !w->w3 || !w->w2)
     return MOE_ERR_INVALID_ARG;
   const moe_route_out_t& r = *route;
   const moe_grads_t& gr = *grads;
-  if (!r.logits || !r.topk_idx || !r.topk_gate || !r.expert_counts || !r.expert_offsets ||
-      !r.assign_row || !gr.dx || !gr.dw1 || !gr.dw3 || !gr.dw2)
+  if (!r.logits || (!ec && !r.topk_idx) || !r.topk_gate || !r.expert_counts ||
+      !r.expert_offsets || !r.assign_row || !gr.dx || !gr.dw1 || !gr.dw3 || !gr.dw2)
     return MOE_ERR_INVALID_ARG;
   if (c.has_shared && (!w->ws1 || !w->ws3 || !w->ws2 || !gr.dws1 || !gr.dws3 || !gr.dws2))
     return MOE_ERR_INVALID_ARG;
@@ -428,7 +431,8 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
   const BwdLayout L = bwd_layout_of(c);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   const hipStream_t s = (hipStream_t)stream;
-  const int E = c.E, k = c.k, h = c.h, F = c.F;
+  const int E = c.E, h = c.h, F = c.F;
+  const int k = ec ? c.E : c.k;        // gate slots per token
   const int G = E + c.has_shared;
   const int64_t T = c.T;
   const int64_t rows = rows_of(c);
@@ -534,7 +538,11 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
     MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, wg, s));
   }
   // router: dl, dw_router, dlogit_bias; then dx
-  MOE_TRY(moe::launch_router_bwd(c.dtype, r.logits, r.topk_idx, r.topk_gate, dg, c.gate, T, E, k, x, h,
+  // expert choice: the probabilities over all E, softmax (mode 1) or
+  // normalised sigmoids (mode 2), slot j = expert j
+  const int gmode = ec ? (c.gate == MOE_GATE_SIGMOID_TOPK_NORM ? 2 : 1) : c.gate;
+  MOE_TRY(moe::launch_router_bwd(c.dtype, r.logits, ec ? nullptr : r.topk_idx, r.topk_gate, dg,
+                                 gmode, T, E, k, x, h,
                                  dl, at<float>(ws, L.rpart), gr.dw_router, gr.dlogit_bias, s));
   MOE_TRY(moe::launch_dx_final(c.dtype, dxp, L.ldh, r.assign_row, k, rows, c.has_shared, dl, w->w_router,
                                T, h, E, gr.dx, s));

@@ -91,6 +91,7 @@ BACKWARD = ["dropless_softmax", "capacity_heavy_drop", "worked_example_small",
 def run_backward(cfg, inp, C_lib, gpu, dy, routing="topk"):
     c = lib_cfg(cfg, C_lib, routing)
     T, E, k, h, F = cfg.T, cfg.E, cfg.k, cfg.h, cfg.F
+    slots = E if routing == "expert_choice" else k
     bf = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
     def nan(*shape, dtype=bf):
@@ -98,7 +99,7 @@ def run_backward(cfg, inp, C_lib, gpu, dy, routing="topk"):
 
     grads = {"dx": nan(T, h), "dw_router": nan(E, h), "dlogit_bias": nan(E, dtype=torch.float32),
              "dw1": nan(E, F, h), "dw3": nan(E, F, h), "dw2": nan(E, h, F),
-             "dgate": nan(T, k, dtype=torch.float32)}
+             "dgate": nan(T, slots, dtype=torch.float32)}
     if cfg.shared:
         grads.update({"dws1": nan(F, h), "dws3": nan(F, h), "dws2": nan(h, F)})
     ws = torch.empty(moe.moe_backward_workspace_bytes(c), dtype=torch.uint8, device=DEV)
@@ -128,19 +129,23 @@ def test_backward_matches_oracle(name):
     ref = oracle.moe_backward(x, wr, w1, w3, w2, np32(dy), k=cfg.k, gate=cfg.gate, C=C_ref,
                               logit_bias=lb, select_bias=sb, shared=shared,
                               idx=gpu["topk_idx"].cpu().numpy())
-    pairs = [("dx", "dx"), ("dw1", "dw1"), ("dw3", "dw3"), ("dw2", "dw2"),
-             ("dw_router", "dw_router"), ("dlogit_bias", "dlogit_bias"), ("dgate", "dgate")]
+    _check_grads(cfg, g, ref, f"backward_{name}")
+
+
+def _check_grads(cfg, g, ref, label):
+    """Every gradient the library wrote against the oracle's, normwise."""
+    names = ["dx", "dw1", "dw3", "dw2", "dw_router", "dlogit_bias", "dgate"]
     if cfg.shared:
-        pairs += [("dws1", "dws1"), ("dws3", "dws3"), ("dws2", "dws2")]
+        names += ["dws1", "dws3", "dws2"]
     errs = {}
-    for gk, rk in pairs:
-        r = ref[rk]
+    for n in names:
+        r = ref[n]
         if np.abs(r).max() == 0:
-            assert float(np.abs(np32(g[gk])).max()) == 0.0, gk
-            errs[gk] = 0.0
+            assert float(np.abs(np32(g[n])).max()) == 0.0, n
+            errs[n] = 0.0
             continue
-        errs[gk] = rel_err(np32(g[gk]), r)
-    _report(f"backward_{name}", **{kk: f"{v:.2e}" for kk, v in errs.items()})
+        errs[n] = rel_err(np32(g[n]), r)
+    _report(label, **{kk: f"{v:.2e}" for kk, v in errs.items()})
     for kk, v in errs.items():
         assert v <= tol_of(cfg), (kk, v)
 
@@ -240,6 +245,24 @@ def test_expert_choice_matches_oracle(cfg):
     _report(f"expert_choice_{cfg.name}", rel_err=f"{err:.2e}", max_dprob=f"{dp:.1e}", C=C_lib,
             unrouted_tokens=int((per_token == 0).sum()), max_experts_per_token=int(per_token.max()))
     assert err <= tol_of(cfg)
+
+
+@pytest.mark.parametrize("cfg", EXPERT_CHOICE, ids=lambda c: c.name)
+def test_expert_choice_backward_matches_oracle(cfg):
+    """Backward with expert-choice routing: every gradient against the
+    oracle's chain rule with the experts' choices held fixed (decided on the
+    GPU's own probabilities)."""
+    print(f"[case] expert choice backward {cfg.name}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    gpu = run_forward(cfg, inp, C_lib, routing="expert_choice")
+    dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=DEV, dtype=cfg.dtype)
+    g = run_backward(cfg, inp, C_lib, gpu, dy, routing="expert_choice")
+    x, wr, w1, w3, w2, lb, shared = oracle_weights(cfg, inp)
+    ref = oracle.expert_choice_backward(x, wr, w1, w3, w2, np32(dy), C=C_ref, gate=cfg.gate,
+                                        logit_bias=lb, shared=shared,
+                                        scores=gpu["probs"].cpu().numpy().T)
+    _check_grads(cfg, g, ref, f"expert_choice_backward_{cfg.name}")
 
 
 BALANCE = ["worked_example_small", "sigmoid_bias_shared", "zipf_dropless", "e256_k8_shared",
