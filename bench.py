@@ -217,6 +217,27 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    # The combine kernel alone (moe_unpermute_combine), 50 back-to-back calls
+    # on this step's routing over a dense expert-output buffer of the same
+    # shape, one pair of events around them (no per-stage event overhead).
+    comb_alone = None
+    if args.routing == "topk" and not cfg.shared:
+        cr = {"topk_gate": torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev),
+              "assign_row": torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev)}
+        moe.moe_forward(c, weights, inp["x"], y, cr, ws)
+        yp = torch.empty((rows, cfg.h), dtype=tdt, device=dev).normal_()
+        yc = torch.empty_like(y)
+        for _ in range(5):
+            moe.moe_unpermute_combine(c, yp, cr["assign_row"], cr["topk_gate"], None, yc)
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ce[0].record()
+        for _ in range(50):
+            moe.moe_unpermute_combine(c, yp, cr["assign_row"], cr["topk_gate"], None, yc)
+        ce[1].record()
+        torch.cuda.synchronize()
+        comb_alone = ce[0].elapsed_time(ce[1]) * 1e3 / 50
+        del yp, yc
+
     # The same step from a cold last-level cache (256 MB on the MI355X): a
     # 512 MiB fill before each step, every step timed by its own events on
     # the launch stream, medians reported.  Not part of `value`.
@@ -342,7 +363,10 @@ def main() -> int:
         "permute": {"gbs": round(perm_gbs, 1), "frac_hbm": round(perm_gbs / PEAK_HBM_GBS, 4),
                     "bytes": pb},
         "combine": {"gbs": round(comb_gbs, 1), "frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
-                    "bytes": cb},
+                    "bytes": cb,
+                    "standalone_us": None if comb_alone is None else round(comb_alone, 2),
+                    "standalone_frac_hbm": (None if comb_alone is None else
+                                            round(cb / (comb_alone * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))},
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "backward": (None if bwd is None else {
             "ms": round(bwd, 4),

@@ -13,9 +13,10 @@
 // bf16 kernel (gfx950): 256 threads = 4 waves in a 2x2 grid, a 256x256
 // output tile per workgroup, each wave a 128x128 sub-tile held as 4x4
 // v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, in AGPRs).  The
-// last row tile of a group is cut to 64 or 128 rows when that holds its
-// rows (waves then hold 1x4 or 2x4 fragments), so a group's leftover rows
-// cost a quarter or half of a tile instead of a whole one.
+// last row tile of a group is cut to 64, 128 or 192 rows when that holds its
+// rows (waves then hold 1x4, 2x4 or 3x4 fragments), so a group's leftover
+// rows cost a quarter, half or three quarters of a tile instead of a whole
+// one.
 // K advances in slices of 64 (128-byte rows, whole cache lines per row).
 // Slices are copied global -> LDS directly (buffer_load_dwordx4 ... lds, no
 // registers in between) into a ring of three A slots and two B slots of
@@ -163,10 +164,10 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* p) {
 }
 
 // Row fragments (32 rows) per wave for a tile of m_valid rows.  The last
-// row tile of a group is only as tall as its rows need (64, 128 or 256), so
-// a group's few leftover rows do not cost a whole 256-row tile.
+// row tile of a group is only as tall as its rows need (64, 128, 192 or
+// 256), so a group's few leftover rows do not cost a whole 256-row tile.
 __device__ __forceinline__ int frags_of(int m_valid) {
-  return m_valid > 128 ? 4 : (m_valid > 64 ? 2 : 1);
+  return m_valid > 192 ? 4 : (m_valid > 128 ? 3 : (m_valid > 64 ? 2 : 1));
 }
 
 // Where output row r (within the tile's group) lives: out0 + r*ldo, or
@@ -404,6 +405,13 @@ __device__ __forceinline__ void tile_body(const GroupedGemmArgs& a, const Tile& 
     COPY(5); RDB(RFB, SBP, S, 1); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                  \
     COPY(6); RDB(RFB, SBP, S, 2); MF(FA, FB, 3, 0); MF(FA, FB, 3, 1); SB();                  \
     COPY(7); RDB(RFB, SBP, S, 3); MF(FA, FB, 3, 2); MF(FA, FB, 3, 3); SB();                  \
+  } else if constexpr (FI == 3) {                                                          \
+    COPY(0); RDA(RFA, SA, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                   \
+    COPY(1); RDA(RFA, SA, S, 1); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                   \
+    COPY(2); RDA(RFA, SA, S, 2); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB();                   \
+    COPY(3); RDB(RFB, SBP, S, 0); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                  \
+    COPY(4); RDB(RFB, SBP, S, 1); RDB(RFB, SBP, S, 2); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB(); \
+    COPY(5); RDB(RFB, SBP, S, 3); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                  \
   } else if constexpr (FI == 2) {                                                          \
     COPY(0); RDA(RFA, SA, S, 0); RDB(RFB, SBP, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB(); \
     COPY(1); RDA(RFA, SA, S, 1); RDB(RFB, SBP, S, 1); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB(); \
@@ -466,11 +474,14 @@ __device__ __forceinline__ void tile_body(const GroupedGemmArgs& a, const Tile& 
     const uint8_t* sbb = smem + kOffB + (kt & 1) * kPart;
     const uint8_t* na = smem + ((kt + 1) % kSlotsA) * kPart;
     const uint8_t* nbb = smem + kOffB + ((kt + 1) & 1) * kPart;
-// A(kt+2): FI = 4: blocks 0-2, 3-5, 6-7 in sub-steps 1, 2, 3; FI = 2:
-// blocks 0-1, 2, 3; FI = 1: blocks 0, 1.  B(kt+2) after the barrier.
+// A(kt+2): FI = 4: blocks 0-2, 3-5, 6-7 in sub-steps 1, 2, 3; FI = 3:
+// blocks 0-1, 2-3, 4-5; FI = 2: blocks 0-1, 2, 3; FI = 1: blocks 0, 1.
+// B(kt+2) after the barrier, one or two per MFMA pair.
 #define COPY_A1(I)                                                                 \
   if constexpr (FI == 4) {                                                         \
     if ((I) == 1 || (I) == 4 || (I) == 7) DMA_A(kt + 2, (I) / 3);                  \
+  } else if constexpr (FI == 3) {                                                  \
+    if ((I) == 1 || (I) == 4) DMA_A(kt + 2, (I) / 4);                              \
   } else if constexpr (FI == 2) {                                                  \
     if ((I) == 1 || (I) == 3) DMA_A(kt + 2, (I) / 2);                              \
   } else {                                                                         \
@@ -479,6 +490,8 @@ __device__ __forceinline__ void tile_body(const GroupedGemmArgs& a, const Tile& 
 #define COPY_A2(I)                                                                 \
   if constexpr (FI == 4) {                                                         \
     if ((I) == 1 || (I) == 4 || (I) == 7) DMA_A(kt + 2, 3 + (I) / 3);              \
+  } else if constexpr (FI == 3) {                                                  \
+    if ((I) == 1 || (I) == 4) DMA_A(kt + 2, 2 + (I) / 4);                          \
   } else if constexpr (FI == 2) {                                                  \
     if ((I) == 2) DMA_A(kt + 2, 2);                                                \
   } else {                                                                         \
@@ -487,11 +500,23 @@ __device__ __forceinline__ void tile_body(const GroupedGemmArgs& a, const Tile& 
 #define COPY_A3(I)                                                                 \
   if constexpr (FI == 4) {                                                         \
     if ((I) == 2 || (I) == 6) DMA_A(kt + 2, 6 + (I) / 4);                          \
+  } else if constexpr (FI == 3) {                                                  \
+    if ((I) == 1 || (I) == 4) DMA_A(kt + 2, 4 + (I) / 4);                          \
   } else if constexpr (FI == 2) {                                                  \
     if ((I) == 2) DMA_A(kt + 2, 3);                                                \
   }
 #define COPY_B(I)                                                                  \
-  _Pragma("unroll") for (int u = 0; u < 8 / (2 * FI); ++u) DMA_B(kt + 2, (I) * (8 / (2 * FI)) + u);
+  if constexpr (FI == 3) {                                                         \
+    if ((I) < 2) {                                                                 \
+      DMA_B(kt + 2, 2 * (I));                                                      \
+      DMA_B(kt + 2, 2 * (I) + 1);                                                  \
+    } else {                                                                       \
+      DMA_B(kt + 2, (I) + 2);                                                      \
+    }                                                                              \
+  } else {                                                                         \
+    _Pragma("unroll") for (int u = 0; u < 8 / (2 * FI); ++u)                       \
+        DMA_B(kt + 2, (I) * (8 / (2 * FI)) + u);                                   \
+  }
     SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 1, COPY_A1);
     SUBSTEP(fa1, fb1, fa0, fb0, sa, sbb, 2, COPY_A2);
     SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 3, COPY_A3);
@@ -575,6 +600,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
   const int fi = frags_of(tl.m_valid);
   if (fi == 4)
     tile_body<SWIGLU, 4>(a, tl, part, parts, wk.slot, smem);
+  else if (fi == 3)
+    tile_body<SWIGLU, 3>(a, tl, part, parts, wk.slot, smem);
   else if (fi == 2)
     tile_body<SWIGLU, 2>(a, tl, part, parts, wk.slot, smem);
   else
@@ -627,6 +654,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_reduce_kernel(GroupedGemmArgs a
   const int fi = frags_of(tl.m_valid);
   if (fi == 4)
     reduce_body<SWIGLU, 4>(a, tl, s, slot);
+  else if (fi == 3)
+    reduce_body<SWIGLU, 3>(a, tl, s, slot);
   else if (fi == 2)
     reduce_body<SWIGLU, 2>(a, tl, s, slot);
   else

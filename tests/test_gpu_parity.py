@@ -310,11 +310,12 @@ STAGED = ["dropless_softmax", "capacity_heavy_drop", "sigmoid_bias_shared", "spl
 @pytest.mark.parametrize("hF", [(512, 512), (1024, 1024)], ids=["whole_tiles", "k_split"])
 def test_grouped_gemm_tile_heights(hF):
     """Standalone grouped GEMM on groups whose last row tile falls in each
-    height class (64, 128 or 256 rows, the class boundaries included), plus
-    an empty and a one-row group.  With K = 1024 every tile of both GEMMs is
-    in the last partial round and is split along K; with K = 512 none is."""
+    height class (64, 128, 192 or 256 rows, the class boundaries included),
+    plus an empty and a one-row group.  With K = 1024 every tile of both
+    GEMMs is in the last partial round and is split along K; with K = 512
+    none is."""
     h, F = hF
-    counts = [300, 100, 1, 0, 256, 530, 384, 320, 449]
+    counts = [300, 100, 1, 0, 256, 384, 320, 449, 192, 385, 160]
     E, T = len(counts), sum(counts)
     print(f"[case] tile heights h={h} F={F} counts={counts}", flush=True)
     cfg = MoEConfig("tile_heights", T=T, h=h, E=E, k=1, F=F, gate="softmax_topk")
