@@ -51,6 +51,11 @@ def expert_flops(kept_rows: int, h: int, F: int) -> int:
     return gemm1_flops(kept_rows, h, F) + gemm2_flops(kept_rows, h, F)
 
 
+def router_bytes(T: int, h: int, E: int, esz: int) -> int:
+    """Read the tokens and the router weights once, write fp32 logits."""
+    return (T + E) * h * esz + T * E * 4
+
+
 def permute_bytes(T: int, h: int, rows: int, esz: int) -> int:
     """Read every token row once, write every row of the dispatch buffer
     (kept copies and zero padding)."""
@@ -333,6 +338,8 @@ def main() -> int:
     if args.routing == "expert_choice":      # a row gather: every row read and written
         pb = 2 * rows * cfg.h * esz
     cb = combine_bytes(kept, cfg.T, cfg.h, esz, cfg.shared)
+    rb = router_bytes(cfg.T, cfg.h, cfg.E, esz)
+    router_gbs = rb / (stage_ms["router"] * 1e-3) / 1e9
     perm_gbs = pb / (stage_ms["permute"] * 1e-3) / 1e9
     comb_gbs = cb / (stage_ms["combine"] * 1e-3) / 1e9
 
@@ -360,6 +367,8 @@ def main() -> int:
                                  if args.routing == "topk" else None)},
         "grouped_gemm": {"tflops": round(gg, 1), "frac_of_peak": round(gg / peak, 4),
                          "gemm1_tflops": round(g1, 1), "gemm2_tflops": round(g2, 1)},
+        "router": {"gbs": round(router_gbs, 1), "frac_hbm": round(router_gbs / PEAK_HBM_GBS, 4),
+                   "bytes": rb},
         "permute": {"gbs": round(perm_gbs, 1), "frac_hbm": round(perm_gbs / PEAK_HBM_GBS, 4),
                     "bytes": pb},
         "combine": {"gbs": round(comb_gbs, 1), "frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),

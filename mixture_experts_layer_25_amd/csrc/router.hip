@@ -5,10 +5,11 @@
 // "router" ([T,h] x [h,E] -> [T,E]).  Logits are fp32.
 //
 // bf16 layers use MFMA v_mfma_f32_16x16x32_bf16, and in both kernels the
-// 4 waves of a workgroup split the reduction over h into quarters whose
+// waves of a workgroup split the reduction over h into equal parts whose
 // partial sums meet in LDS in a fixed order.  Up to 16 experts: one
 // workgroup takes 16 tokens and every expert, so x and the small w_router
-// are each read once.  More experts: one workgroup per tile of 64 tokens x
+// are each read once; its 16 (or 8, or 4) waves each take an equal share
+// of h, so that a workgroup's whole slice of x is in flight at once.  More experts: one workgroup per tile of 64 tokens x
 // 64 experts (4x4 MFMA tiles per wave), which bounds the re-reads of
 // w_router to one per 64 tokens and keeps the grid wide.  bf16 x bf16
 // products are exact in fp32 and accumulate in fp32.
@@ -22,15 +23,22 @@ namespace {
 constexpr int kRouterTok = 16;       // tokens per workgroup (up to 16 experts)
 constexpr int kRouterBatch = 8;      // 32-deep steps whose loads are issued together
 
-__global__ __launch_bounds__(256) void router_bf16_kernel(
+constexpr int kRouterMaxWaves = 16;
+
+// Waves per workgroup of the small-E router: the most (16, 8 or 4) whose
+// share of h is a multiple of 32 (h % 128 == 0, so 4 always is).
+inline int router_waves(int h) { return h % (16 * 32) == 0 ? 16 : (h % (8 * 32) == 0 ? 8 : 4); }
+
+__global__ __launch_bounds__(64 * kRouterMaxWaves) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, float* __restrict__ logits, int64_t T,
     int h, int E) {
-  __shared__ float red[4][kRouterTok][16];
+  __shared__ float red[kRouterMaxWaves][kRouterTok][16];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;         // waves: 16, 8 or 4
   const int64_t t0 = (int64_t)blockIdx.x * kRouterTok;
-  const int kq = h >> 2;                  // h % 128 == 0: kq % 32 == 0
+  const int kq = h / nw;                  // a multiple of 32
   const int koff = w * kq + (lane >> 4) * 8;
   // MFMA 16x16x32 operands: lane l holds row (l & 15) and 8 consecutive k
   // values at k-group (l >> 4); A and B use the same k placement.  Rows
@@ -73,10 +81,9 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   __syncthreads();
   const int tk = threadIdx.x >> 4, ee = threadIdx.x & 15;
   const int64_t t = t0 + tk;
-  if (ee < E && t < T) {
-    float s = red[0][tk][ee] + red[1][tk][ee];
-    s += red[2][tk][ee];
-    s += red[3][tk][ee];
+  if (threadIdx.x < 256 && ee < E && t < T) {
+    float s = red[0][tk][ee];             // wave partials in wave order
+    for (int q = 1; q < nw; ++q) s += red[q][tk][ee];
     if (bias) s += bias[ee];
     logits[t * E + ee] = s;
   }
@@ -201,7 +208,7 @@ hipError_t launch_router(int dtype, const void* x, const void* w_router,
                        logit_bias, logits, T, h, E);
   } else if (dtype == 1) {
     const int64_t nb = (T + kRouterTok - 1) / kRouterTok;
-    hipLaunchKernelGGL(router_bf16_kernel, dim3((unsigned)nb), dim3(256), 0, s,
+    hipLaunchKernelGGL(router_bf16_kernel, dim3((unsigned)nb), dim3(64 * router_waves(h)), 0, s,
                        (const uint16_t*)x, (const uint16_t*)w_router,
                        logit_bias, logits, T, h, E);
   } else {
