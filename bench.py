@@ -223,21 +223,25 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
 
     # On-box HBM yardstick: a plain 1 GiB device-to-device copy (torch),
-    # best of 5, read + write bytes over its event time.
-    cp_src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-    cp_dst = torch.empty_like(cp_src)
-    cp_dst.copy_(cp_src)
-    cp_best = None
-    for _ in range(5):
-        ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ce0.record()
+    # best of 5, read + write bytes over its event time.  Skipped in the
+    # counter runs (--copy-calibration-mib), whose only large copy must be
+    # the calibration copy.
+    copy_gbs = None
+    if args.copy_calibration_mib == 0:
+        cp_src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        cp_dst = torch.empty_like(cp_src)
         cp_dst.copy_(cp_src)
-        ce1.record()
-        torch.cuda.synchronize()
-        ms = ce0.elapsed_time(ce1)
-        cp_best = ms if cp_best is None else min(cp_best, ms)
-    copy_gbs = 2 * cp_src.numel() * 4 / (cp_best * 1e-3) / 1e9
-    del cp_src, cp_dst
+        cp_best = None
+        for _ in range(5):
+            ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ce0.record()
+            cp_dst.copy_(cp_src)
+            ce1.record()
+            torch.cuda.synchronize()
+            ms = ce0.elapsed_time(ce1)
+            cp_best = ms if cp_best is None else min(cp_best, ms)
+        copy_gbs = 2 * cp_src.numel() * 4 / (cp_best * 1e-3) / 1e9
+        del cp_src, cp_dst
 
     # The combine kernel alone (moe_unpermute_combine), 50 back-to-back calls
     # on this step's routing over a dense expert-output buffer of the same
@@ -384,13 +388,13 @@ def main() -> int:
                                  if args.routing == "topk" else None)},
         "grouped_gemm": {"tflops": round(gg, 1), "frac_of_peak": round(gg / peak, 4),
                          "gemm1_tflops": round(g1, 1), "gemm2_tflops": round(g2, 1)},
-        "hbm_copy_gbs": round(copy_gbs, 1),
+        "hbm_copy_gbs": None if copy_gbs is None else round(copy_gbs, 1),
         "router": {"gbs": round(router_gbs, 1), "frac_hbm": round(router_gbs / PEAK_HBM_GBS, 4),
-                   "frac_copy": round(router_gbs / copy_gbs, 4), "bytes": rb},
+                   "frac_copy": None if copy_gbs is None else round(router_gbs / copy_gbs, 4), "bytes": rb},
         "permute": {"gbs": round(perm_gbs, 1), "frac_hbm": round(perm_gbs / PEAK_HBM_GBS, 4),
-                    "frac_copy": round(perm_gbs / copy_gbs, 4), "bytes": pb},
+                    "frac_copy": None if copy_gbs is None else round(perm_gbs / copy_gbs, 4), "bytes": pb},
         "combine": {"gbs": round(comb_gbs, 1), "frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
-                    "frac_copy": round(comb_gbs / copy_gbs, 4), "bytes": cb,
+                    "frac_copy": None if copy_gbs is None else round(comb_gbs / copy_gbs, 4), "bytes": cb,
                     "standalone_us": None if comb_alone is None else round(comb_alone, 2),
                     "standalone_frac_hbm": (None if comb_alone is None else
                                             round(cb / (comb_alone * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))},
