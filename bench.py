@@ -341,7 +341,29 @@ def main() -> int:
         bw_ev[1].record()
         torch.cuda.synchronize()
         bwd = bw_ev[0].elapsed_time(bw_ev[1]) / nb
-        del wsb, grads
+        # the same backward from activations the forward kept
+        # (save_for_backward): the forward's cost with the flag, then the
+        # saved backward
+        cs = moe.make_cfg(cfg.T, cfg.h, cfg.F, cfg.E, cfg.k, cfg.dtype, cfg.gate, capacity=C,
+                          has_shared=cfg.shared, routing=args.routing, save_for_backward=True)
+        wsf = torch.empty(moe.moe_workspace_bytes(cs), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            moe.moe_forward(cs, weights, inp["x"], y, full_route, wsf)
+        sv_ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        sv_ev[0].record()
+        for _ in range(nb):
+            moe.moe_forward(cs, weights, inp["x"], y, full_route, wsf)
+        sv_ev[1].record()
+        for _ in range(2):
+            moe.moe_backward_saved(cs, weights, inp["x"], dy, full_route, wsf, grads, wsb)
+        sv_ev[2].record()
+        for _ in range(nb):
+            moe.moe_backward_saved(cs, weights, inp["x"], dy, full_route, wsf, grads, wsb)
+        sv_ev[3].record()
+        torch.cuda.synchronize()
+        fwd_save_ms = sv_ev[0].elapsed_time(sv_ev[1]) / nb
+        bwd_saved_ms = sv_ev[2].elapsed_time(sv_ev[3]) / nb
+        del wsb, grads, wsf
 
     stage_ms = {}
     for s, name in enumerate(moe.STAGE_NAMES):
@@ -405,7 +427,13 @@ def main() -> int:
             # the recomputed [a1 | a3] and expert outputs as well
             "tflops": round(12 * kept_all * cfg.h * cfg.F / (bwd * 1e-3) / 1e12, 1),
             "tflops_with_recompute": round(18 * kept_all * cfg.h * cfg.F / (bwd * 1e-3) / 1e12, 1),
-            "frac_of_peak": round(18 * kept_all * cfg.h * cfg.F / (bwd * 1e-3) / 1e12 / peak, 4)}),
+            "frac_of_peak": round(18 * kept_all * cfg.h * cfg.F / (bwd * 1e-3) / 1e12 / peak, 4),
+            # forward with save_for_backward + moe_backward_saved: no recompute
+            "forward_save_ms": round(fwd_save_ms, 4),
+            "saved_ms": round(bwd_saved_ms, 4),
+            "saved_tflops": round(12 * kept_all * cfg.h * cfg.F / (bwd_saved_ms * 1e-3) / 1e12, 1),
+            "saved_frac_of_peak": round(12 * kept_all * cfg.h * cfg.F / (bwd_saved_ms * 1e-3)
+                                        / 1e12 / peak, 4)}),
         "cold_cache": cold,
         "load_balance": {"us": round(lb_us, 2),
                          "gbs": round(cfg.T * cfg.E * 4 / (lb_us * 1e-6) / 1e9, 1),

@@ -102,6 +102,16 @@ extern "C" {
  *                     moe_unpermute_combine and moe_load_balance accept it.
  * Selection decisions are integer compares of fp32 keys on the device, so
  * every run routes the same.                                              */
+/* Flags of moe_cfg_t.flags.
+ *   SAVE_FOR_BACKWARD  moe_forward keeps in its workspace what the backward
+ *                      needs (the dispatch buffer, the pre-activations
+ *                      [a1 | a3], the activations and the expert outputs),
+ *                      so that moe_backward_saved can skip recomputing them.
+ *                      moe_workspace_bytes grows by rows x (2F + 128 bytes)
+ *                      elements for [a1 | a3]; the layer's output is the
+ *                      same bit for bit.  Other bits: MOE_ERR_INVALID_ARG. */
+#define MOE_FLAG_SAVE_FOR_BACKWARD 1
+
 #define MOE_ROUTE_TOPK 0
 #define MOE_ROUTE_TOPK_SCORE_DROP 1
 #define MOE_ROUTE_EXPERT_CHOICE 2
@@ -126,7 +136,7 @@ typedef struct moe_cfg {
   int32_t has_shared;  /* 1: one shared expert of shape (h, F) on every token */
   int64_t capacity;    /* 0: dropless; > 0: capacity C rows per expert */
   int32_t routing;     /* MOE_ROUTE_* */
-  int32_t reserved;    /* 0 */
+  int32_t flags;       /* MOE_FLAG_* bits, 0 for none */
 } moe_cfg_t;
 
 typedef struct moe_weights {
@@ -303,6 +313,20 @@ int moe_backward_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes);
 int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
                  const void* dy, const moe_route_out_t* route, const moe_grads_t* grads,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* The same backward from the activations a moe_forward call kept (cfg with
+ * MOE_FLAG_SAVE_FOR_BACKWARD, the same cfg, weights and x): the dispatch
+ * buffer, [a1 | a3], the activations and the expert outputs are read from
+ * that call's workspace fwd_ws (fwd_ws_bytes >= moe_workspace_bytes(cfg),
+ * untouched since) instead of being recomputed, which skips the permute,
+ * two of the six grouped GEMMs and the SwiGLU pass.  The results equal
+ * moe_backward's up to the rounding of the kept bf16 values (the forward
+ * sums its K slices in another order).  cfg without the flag, or fwd_ws
+ * NULL or too small: MOE_ERR_INVALID_ARG / MOE_ERR_WORKSPACE.             */
+int moe_backward_saved(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
+                       const void* dy, const moe_route_out_t* route, const void* fwd_ws,
+                       size_t fwd_ws_bytes, const moe_grads_t* grads, void* ws,
+                       size_t ws_bytes, void* stream);
 
 /* The fused layer: stages 1-4 (+ the shared expert as one more group of
  * the grouped GEMM) on one stream, no host synchronisation.

@@ -55,7 +55,7 @@ ABI_SYMBOLS = (
     "moe_strerror", "moe_capacity", "moe_num_rows", "moe_workspace_bytes",
     "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu",
     "moe_unpermute_combine", "moe_load_balance", "moe_backward_workspace_bytes",
-    "moe_backward", "moe_forward",
+    "moe_backward", "moe_backward_saved", "moe_forward",
 )
 
 
@@ -72,7 +72,7 @@ class MoECfg(ctypes.Structure):
         ("has_shared", ctypes.c_int32),
         ("capacity", ctypes.c_int64),
         ("routing", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -128,6 +128,9 @@ def lib() -> ctypes.CDLL:
             "moe_backward": (ctypes.c_int, [cfgp, ctypes.POINTER(MoEWeights), P, P,
                                             ctypes.POINTER(MoERouteOut),
                                             ctypes.POINTER(MoEGrads), P, SZ, P]),
+            "moe_backward_saved": (ctypes.c_int, [cfgp, ctypes.POINTER(MoEWeights), P, P,
+                                                  ctypes.POINTER(MoERouteOut), P, SZ,
+                                                  ctypes.POINTER(MoEGrads), P, SZ, P]),
             "moe_forward": (ctypes.c_int, [cfgp, ctypes.POINTER(MoEWeights), P, P,
                                            ctypes.POINTER(MoERouteOut), P, SZ, P, P]),
         }
@@ -163,9 +166,12 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+MOE_FLAG_SAVE_FOR_BACKWARD = 1
+
+
 def make_cfg(T: int, h: int, F: int, E: int, k: int, dtype="bf16",
              gate="softmax_topk", capacity: int = 0, has_shared: bool = False,
-             routing="topk") -> MoECfg:
+             routing="topk", save_for_backward: bool = False) -> MoECfg:
     c = MoECfg()
     c.struct_size = ctypes.sizeof(MoECfg)
     c.dtype = DTYPE_BY_NAME[dtype] if isinstance(dtype, str) else int(dtype)
@@ -174,7 +180,7 @@ def make_cfg(T: int, h: int, F: int, E: int, k: int, dtype="bf16",
     c.has_shared = int(bool(has_shared))
     c.capacity = int(capacity)
     c.routing = ROUTING_BY_NAME[routing] if isinstance(routing, str) else int(routing)
-    c.reserved = 0
+    c.flags = MOE_FLAG_SAVE_FOR_BACKWARD if save_for_backward else 0
     return c
 
 
@@ -264,6 +270,21 @@ def moe_backward(cfg, weights: dict, x, dy, route: dict, grads: dict, ws, stream
     _check("moe_backward", lib().moe_backward(
         ctypes.byref(cfg), ctypes.byref(weights_struct(weights)), _ptr(x), _ptr(dy),
         ctypes.byref(route_struct(route)), ctypes.byref(g), wp, wb, _stream(stream)))
+
+
+def moe_backward_saved(cfg, weights: dict, x, dy, route: dict, fwd_ws, grads: dict, ws,
+                       stream=None) -> None:
+    """moe_backward from the activations the moe_forward call kept in its
+    workspace ``fwd_ws`` (cfg made with save_for_backward=True; the same
+    cfg, weights, x and routing outputs)."""
+    fp, fb = _ws(fwd_ws)
+    wp, wb = _ws(ws)
+    g = MoEGrads()
+    for name, _ in MoEGrads._fields_:
+        setattr(g, name, _ptr(grads.get(name)))
+    _check("moe_backward_saved", lib().moe_backward_saved(
+        ctypes.byref(cfg), ctypes.byref(weights_struct(weights)), _ptr(x), _ptr(dy),
+        ctypes.byref(route_struct(route)), fp, fb, ctypes.byref(g), wp, wb, _stream(stream)))
 
 
 def weights_struct(w: dict) -> MoEWeights:

@@ -178,6 +178,8 @@ struct OutMap {
   uint16_t* out1;
   int64_t split;
   int64_t ldo;
+  uint16_t* a13;   // SwiGLU: pre-activations [a1 | a3] too, or NULL
+  int64_t ld13;
   __device__ __forceinline__ uint16_t* row(int64_t r) const {
     return r < split ? out0 + r * ldo : out1 + (r - split) * ldo;
   }
@@ -190,6 +192,8 @@ __device__ __forceinline__ OutMap out_map(const GroupedGemmArgs& a, int g) {
   m.out1 = a.out1 ? (uint16_t*)a.out1 + go : nullptr;
   m.split = (a.out1 && a.split_rows > 0) ? a.split_rows : INT64_MAX;
   m.ldo = a.ldo;
+  m.a13 = (uint16_t*)a.out13;
+  m.ld13 = a.ld13;
   return m;
 }
 
@@ -206,6 +210,31 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FI][4], const T
                                            int wm, int wn, const OutMap& om, int N) {
   const int hi = lane >> 5;
   constexpr int NJ = SWIGLU ? 2 : 4;
+  // v_permlane32_swap trades the high half of its first operand with the
+  // low half of its second: with runs 2c and 2c+1 as the operands, lane
+  // l < 32 gets (its run 2c, lane l+32's run 2c) and lane l+32 (lane l's
+  // run 2c+1, its run 2c+1), 8 consecutive columns each
+  auto emit = [&](const uint32_t (&q)[4][2], uint16_t* rowp, int64_t col0, bool ok) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t lo[2], up[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const auto r = __builtin_amdgcn_permlane32_swap(q[2 * c][p], q[2 * c + 1][p], false, false);
+        lo[p] = r[0];
+        up[p] = r[1];
+      }
+      if (ok)
+        *reinterpret_cast<uint4*>(rowp + col0 + 16 * c + 8 * hi) = uint4{lo[0], lo[1], up[0], up[1]};
+    }
+  };
+  // run b of fragment f as two bf16 pairs
+  auto pack_runs = [&](const floatx16& f, uint32_t (&q)[4][2]) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) q[b][p] = pack_bf16x2(f[4 * b + 2 * p], f[4 * b + 2 * p + 1]);
+  };
 #pragma unroll
   for (int i = 0; i < FI; ++i) {
     const int row = wm * 32 * FI + i * 32 + (lane & 31);
@@ -216,39 +245,37 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FI][4], const T
       const int64_t col0 = SWIGLU ? (int64_t)tl.nt * 128 + wn * 64 + j * 32
                                   : (int64_t)tl.nt * BN + wn * 128 + j * 32;
       if (!SWIGLU && col0 >= N) continue;
-      uint32_t q[4][2];   // run b as two bf16 pairs
+      uint32_t q[4][2];
+      if constexpr (SWIGLU) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          float v[2];
+          for (int p = 0; p < 2; ++p) {
+            float v[2];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 4 * b + 2 * p + e;
-            const float z = acc[i][j][r];
-            // silu(z) * a3 = z * a3 / (1 + e^-z), e^-z = 2^(-z * log2(e)):
-            // hardware exp2 and reciprocal (the result is rounded to bf16)
-            v[e] = SWIGLU ? z * acc[i][j + 2][r] *
-                                __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f))
-                          : z;
+            for (int e = 0; e < 2; ++e) {
+              const int r = 4 * b + 2 * p + e;
+              const float z = acc[i][j][r];
+              // silu(z) * a3 = z * a3 / (1 + e^-z), e^-z = 2^(-z * log2(e)):
+              // hardware exp2 and reciprocal (the result is rounded to bf16)
+              v[e] = z * acc[i][j + 2][r] *
+                     __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+            }
+            q[b][p] = pack_bf16x2(v[0], v[1]);
           }
-          q[b][p] = pack_bf16x2(v[0], v[1]);
+      } else {
+        pack_runs(acc[i][j], q);
+      }
+      emit(q, orow, col0, ok);
+      if constexpr (SWIGLU) {
+        if (om.a13) {             // the pre-activations a1 and a3 as well
+          uint16_t* r13 = om.a13 + (tl.o_row + row) * om.ld13;
+          uint32_t q1[4][2], q3[4][2];
+          pack_runs(acc[i][j], q1);
+          pack_runs(acc[i][j + 2], q3);
+          emit(q1, r13, col0, ok);
+          emit(q3, r13, col0 + N, ok);
         }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        // v_permlane32_swap trades the high half of its first operand with
-        // the low half of its second: with runs 2c and 2c+1 as the operands,
-        // lane l < 32 gets (its run 2c, lane l+32's run 2c) and lane l+32
-        // (lane l's run 2c+1, its run 2c+1), 8 consecutive columns each
-        uint32_t lo[2], up[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const auto r = __builtin_amdgcn_permlane32_swap(q[2 * c][p], q[2 * c + 1][p], false, false);
-          lo[p] = r[0];
-          up[p] = r[1];
-        }
-        if (ok)
-          *reinterpret_cast<uint4*>(orow + col0 + 16 * c + 8 * hi) = uint4{lo[0], lo[1], up[0], up[1]};
       }
     }
   }
@@ -778,7 +805,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GroupedGemmArgs a) {
     for (int c = 0; c < 4; ++c) {
       const int64_t col = n0 + tx + 16 * c;
       float v = acc[i][c];
-      if (SWIGLU) v = v / (1.f + expf(-v)) * acc3[i][c];
+      if (SWIGLU) {
+        if (a.out13) {             // the pre-activations a1 and a3 as well
+          float* r13 = (float*)a.out13 + r * a.ld13;
+          r13[col] = acc[i][c];
+          r13[N + col] = acc3[i][c];
+        }
+        v = v / (1.f + expf(-v)) * acc3[i][c];
+      }
       orow[col] = v;
     }
   }

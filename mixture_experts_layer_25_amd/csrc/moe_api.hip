@@ -32,6 +32,10 @@ int64_t rows_of(const moe_cfg_t& c) {
 int ld_h(const moe_cfg_t& c) { return c.h + 128 / esize(c); }
 int ld_f(const moe_cfg_t& c) { return c.F + 128 / esize(c); }
 
+// Row stride of the kept pre-activations [a1 | a3] (2F elements + 128 B).
+int ld_13(const moe_cfg_t& c) { return 2 * c.F + 128 / esize(c); }
+bool saves(const moe_cfg_t& c) { return (c.flags & MOE_FLAG_SAVE_FOR_BACKWARD) != 0; }
+
 int row_tile(const moe_cfg_t& c) {
   return c.dtype == MOE_DTYPE_BF16 ? moe::kGemmBM_bf16 : moe::kGemmBM_f32;
 }
@@ -45,7 +49,8 @@ int check_cfg(const moe_cfg_t* c) {
   if (c->T < 0 || c->h <= 0 || c->F <= 0 || c->E <= 0 || c->k <= 0 || c->capacity < 0)
     return MOE_ERR_INVALID_ARG;
   if (c->has_shared != 0 && c->has_shared != 1) return MOE_ERR_INVALID_ARG;
-  if (c->routing < MOE_ROUTE_TOPK || c->routing > MOE_ROUTE_EXPERT_CHOICE || c->reserved != 0)
+  if (c->routing < MOE_ROUTE_TOPK || c->routing > MOE_ROUTE_EXPERT_CHOICE ||
+      (c->flags & ~MOE_FLAG_SAVE_FOR_BACKWARD) != 0)
     return MOE_ERR_INVALID_ARG;
   if (c->routing == MOE_ROUTE_TOPK_SCORE_DROP && c->capacity <= 0) return MOE_ERR_INVALID_ARG;
   if (c->routing == MOE_ROUTE_EXPERT_CHOICE && c->T > 0 &&
@@ -65,7 +70,7 @@ struct Layout {
   // routing variants: expert choice (probs, selection rows and gates per
   // (token, expert)); score drop (the dropless maps it ranks within)
   size_t probs, selrow, gatete, offs_dl, gtab_dl, assign_dl, rowtok_dl, key_dl, aid_dl;
-  size_t partials, xperm, act, yperm, total;
+  size_t partials, xperm, act, yperm, a13, total;
 };
 
 Layout layout_of(const moe_cfg_t& c) {
@@ -110,6 +115,7 @@ Layout layout_of(const moe_cfg_t& c) {
   L.xperm = take((size_t)rows * ld_h(c) * es);
   L.act = take((size_t)rows_all * ld_f(c) * es);
   L.yperm = take((size_t)rows_all * ld_h(c) * es);
+  L.a13 = take(saves(c) ? (size_t)rows_all * ld_13(c) * es : 0);
   L.total = off;
   return L;
 }
@@ -402,12 +408,26 @@ MOE_API int moe_backward_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes) {
   return MOE_OK;
 }
 
-MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
-                         const void* dy, const moe_route_out_t* route, const moe_grads_t* grads,
-                         void* ws, size_t ws_bytes, void* stream) {
-  int st = check_cfg(cfg);
-  if (st != MOE_OK) return st;
-  const moe_cfg_t& c = *cfg;
+namespace {
+
+// Activations a forward call kept for the backward (pointers and row
+// strides in elements): the dispatch buffer, [a1 | a3], the activations and
+// the expert outputs.
+struct Saved {
+  const void* xp;
+  int ldxp;
+  const void* a13;
+  int ld13;
+  const void* u;
+  int ldu;
+  const void* o;
+  int ldo;
+};
+
+// The backward; sv NULL: the activations are recomputed into ws.
+int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, const void* dy,
+                  const moe_route_out_t* route, const moe_grads_t* grads, void* ws,
+                  size_t ws_bytes, void* stream, const Saved* sv) {
   if (c.T == 0) return MOE_OK;
   // expert choice: the E experts are each token's slots (assign_row and
   // topk_gate [T,E] as the forward wrote them; no topk_idx)
@@ -443,10 +463,18 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
   int32_t* kto = at<int32_t>(ws, L.kto);
   float* dg = gr.dgate ? gr.dgate : at<float>(ws, L.dg);
   float* dl = at<float>(ws, L.dl);
-  void* xp = at<char>(ws, L.xp);
-  void* a13 = at<char>(ws, L.a13);
-  void* u = at<char>(ws, L.u);
-  void* o = at<char>(ws, L.o);
+  // recomputed (or kept) activations and their row strides
+  const void* xp = at<char>(ws, L.xp);
+  const void* a13 = at<char>(ws, L.a13);
+  const void* u = at<char>(ws, L.u);
+  const void* o = at<char>(ws, L.o);
+  int ldxp = L.ldh, ld13 = L.ld13, ldu = L.ldf, ldo = L.ldh;
+  if (sv) {
+    xp = sv->xp; ldxp = sv->ldxp;
+    a13 = sv->a13; ld13 = sv->ld13;
+    u = sv->u; ldu = sv->ldu;
+    o = sv->o; ldo = sv->ldo;
+  }
   void* dO = at<char>(ws, L.dO);
   void* dU = at<char>(ws, L.dU);
   void* dA = at<char>(ws, L.dA);
@@ -464,8 +492,10 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
                                          c.has_shared, BM, rows, gtab, s));
   MOE_TRY(moe::launch_ktab(gtab, G, 1, kta, s));
   MOE_TRY(moe::launch_ktab(gtab, G, 0, kto, s));
-  MOE_TRY(moe::launch_permute(c.dtype, x, r.assign_row, r.expert_counts, T, h, E, k, c.capacity,
-                              xp, L.ldh, at<int32_t>(ws, L.rowtok), s));
+  if (!sv)
+    MOE_TRY(moe::launch_permute(c.dtype, x, r.assign_row, r.expert_counts, T, h, E, k,
+                                c.capacity, at<char>(ws, L.xp), L.ldh, at<int32_t>(ws, L.rowtok),
+                                s));
   // transposed weights: w2t[g] = w2[g]^T [F,h]; w13t[g] = [w1[g]^T | w3[g]^T] [h,2F]
   MOE_TRY(moe::launch_transpose(c.dtype, w->w2, (int64_t)h * F, h, F, w2t, (int64_t)F * h, h, 0, E, s));
   MOE_TRY(moe::launch_transpose(c.dtype, w->w1, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F, 2 * F, 0,
@@ -487,30 +517,34 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
   base.max_m_tiles = max_m_tiles(rows, E, BM) + (c.has_shared ? (T + BM - 1) / BM : 0);
   base.num_cu = device_cus();
   base.partials = at<float>(ws, L.partials);
-  // [a1 | a3] = x_perm [w1; w3]^T (the shared group reads x)
   moe::GroupedGemmArgs a = base;
-  a.A = xp; a.lda = L.ldh; a.A_shared = x; a.lda_shared = h;
-  a.B0 = w->w1; a.B1 = w->w3; a.B0s = w->ws1; a.B1s = w->ws3; a.b_split = 1;
-  a.b_stride = (int64_t)F * h; a.K = h; a.N = 2 * F; a.out = a13; a.ldo = L.ld13;
-  MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
-  MOE_TRY(moe::launch_swiglu_fwd(c.dtype, a13, L.ld13, rows_all, F, u, L.ldf, s));
-  // expert outputs o = u w2^T (the forward's y_perm)
-  a = base;
-  a.A = u; a.lda = L.ldf; a.a_from_out_rows = 1;
-  a.B0 = w->w2; a.B0s = w->ws2; a.b_stride = (int64_t)h * F; a.K = F; a.N = h;
-  a.out = o; a.ldo = L.ldh;
-  MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
+  if (!sv) {
+    // [a1 | a3] = x_perm [w1; w3]^T (the shared group reads x)
+    a.A = xp; a.lda = L.ldh; a.A_shared = x; a.lda_shared = h;
+    a.B0 = w->w1; a.B1 = w->w3; a.B0s = w->ws1; a.B1s = w->ws3; a.b_split = 1;
+    a.b_stride = (int64_t)F * h; a.K = h; a.N = 2 * F; a.out = at<char>(ws, L.a13);
+    a.ldo = L.ld13;
+    MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
+    MOE_TRY(moe::launch_swiglu_fwd(c.dtype, a13, L.ld13, rows_all, F, at<char>(ws, L.u), L.ldf,
+                                   s));
+    // expert outputs o = u w2^T (the forward's y_perm)
+    a = base;
+    a.A = u; a.lda = L.ldf; a.a_from_out_rows = 1;
+    a.B0 = w->w2; a.B0s = w->ws2; a.b_stride = (int64_t)h * F; a.K = F; a.N = h;
+    a.out = at<char>(ws, L.o); a.ldo = L.ldh;
+    MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
+  }
   // dO rows, gate gradients
   MOE_TRY(moe::launch_scatter_dy(c.dtype, dy, r.assign_row, r.topk_gate, r.expert_counts, T, h, E, k,
                                  c.capacity, rows, c.has_shared, dO, L.ldh, s));
-  MOE_TRY(moe::launch_gate_grad(c.dtype, dy, o, L.ldh, r.assign_row, T, h, k, dg, s));
+  MOE_TRY(moe::launch_gate_grad(c.dtype, dy, o, ldo, r.assign_row, T, h, k, dg, s));
   // dU = dO w2, then dA, then dx_perm = dA [w1; w3]
   a = base;
   a.A = dO; a.lda = L.ldh; a.a_from_out_rows = 1;
   a.B0 = w2t; a.B0s = w2t + (size_t)E * F * h * L.esz; a.b_stride = (int64_t)F * h;
   a.K = h; a.N = F; a.out = dU; a.ldo = L.ldf;
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
-  MOE_TRY(moe::launch_swiglu_bwd(c.dtype, a13, L.ld13, dU, L.ldf, rows_all, F, dA, L.ld13, s));
+  MOE_TRY(moe::launch_swiglu_bwd(c.dtype, a13, ld13, dU, L.ldf, rows_all, F, dA, L.ld13, s));
   a = base;
   a.A = dA; a.lda = L.ld13; a.a_from_out_rows = 1;
   a.B0 = w13t; a.B0s = w13t + (size_t)E * h * 2 * F * L.esz; a.b_stride = (int64_t)h * 2 * F;
@@ -518,10 +552,10 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
   // K-major copies of each group's rows, then the weight gradients
   MOE_TRY(moe::launch_transpose_groups(c.dtype, dO, L.ldh, dO, L.ldh, G, kto, G, h, L.ktb, dOT, ktb, s));
-  MOE_TRY(moe::launch_transpose_groups(c.dtype, u, L.ldf, u, L.ldf, G, kto, G, F, L.ktb, uT, ktb, s));
+  MOE_TRY(moe::launch_transpose_groups(c.dtype, u, ldu, u, ldu, G, kto, G, F, L.ktb, uT, ktb, s));
   MOE_TRY(moe::launch_transpose_groups(c.dtype, dA, L.ld13, dA, L.ld13, G, kto, G, 2 * F, L.ktb, dAT, ktb,
                                        s));
-  MOE_TRY(moe::launch_transpose_groups(c.dtype, xp, L.ldh, x, h, E, kta, G, h, L.ktb, xpT, ktb, s));
+  MOE_TRY(moe::launch_transpose_groups(c.dtype, xp, ldxp, x, h, E, kta, G, h, L.ktb, xpT, ktb, s));
   for (int pass = 0; pass < (c.has_shared ? 2 : 1); ++pass) {
     const bool sh = pass == 1;
     moe::GroupedGemmArgs wg{};
@@ -547,6 +581,33 @@ MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const voi
   MOE_TRY(moe::launch_dx_final(c.dtype, dxp, L.ldh, r.assign_row, k, rows, c.has_shared, dl, w->w_router,
                                T, h, E, gr.dx, s));
   return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
+                         const void* dy, const moe_route_out_t* route, const moe_grads_t* grads,
+                         void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  return backward_impl(*cfg, w, x, dy, route, grads, ws, ws_bytes, stream, nullptr);
+}
+
+MOE_API int moe_backward_saved(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
+                               const void* dy, const moe_route_out_t* route, const void* fwd_ws,
+                               size_t fwd_ws_bytes, const moe_grads_t* grads, void* ws,
+                               size_t ws_bytes, void* stream) {
+  const int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const moe_cfg_t& c = *cfg;
+  if (!saves(c) || misaligned(fwd_ws)) return MOE_ERR_INVALID_ARG;
+  if (c.T == 0) return MOE_OK;
+  const Layout F = layout_of(c);
+  if (!fwd_ws || fwd_ws_bytes < F.total) return MOE_ERR_WORKSPACE;
+  void* fw = const_cast<void*>(fwd_ws);
+  const Saved sv{at<char>(fw, F.xperm), ld_h(c), at<char>(fw, F.a13), ld_13(c),
+                 at<char>(fw, F.act), ld_f(c), at<char>(fw, F.yperm), ld_h(c)};
+  return backward_impl(c, w, x, dy, route, grads, ws, ws_bytes, stream, &sv);
 }
 
 MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
@@ -670,8 +731,13 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   a.a_from_out_rows = 0;
   a.max_m_tiles = max_m_tiles(rows, c.E, BM) + (c.has_shared ? (c.T + BM - 1) / BM : 0);
   set_split(a, c, ws, L);
+  if (saves(c)) {                     // [a1 | a3] kept for moe_backward_saved
+    a.out13 = at<char>(ws, L.a13);
+    a.ld13 = ld_13(c);
+  }
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, true, a, s));
   MOE_TRY(mark(6));
+  a.out13 = nullptr;
   a.A = act;
   a.A_shared = nullptr;
   a.B0 = w->w2;

@@ -60,6 +60,10 @@ struct GroupedGemmArgs {
   // group's offset, row - split_rows (0: no split).
   void* out1;
   int split_rows;
+  // SwiGLU mode: also store the pre-activations, a1 at columns [0, N) and
+  // a3 at [N, 2N) of out13's output row (row stride ld13), or NULL.
+  void* out13;
+  int ld13;
 };
 
 hipError_t launch_router(int dtype, const void* x, const void* w_router,

@@ -41,15 +41,18 @@ def capacity_of(cfg: MoEConfig):
     return c_lib, c_ref
 
 
-def lib_cfg(cfg: MoEConfig, C: int, routing: str = "topk"):
+def lib_cfg(cfg: MoEConfig, C: int, routing: str = "topk", save: bool = False):
     return moe.make_cfg(cfg.T, cfg.h, cfg.F, cfg.E, cfg.k, cfg.dtype, cfg.gate,
-                        capacity=C, has_shared=cfg.shared, routing=routing)
+                        capacity=C, has_shared=cfg.shared, routing=routing,
+                        save_for_backward=save)
 
 
-def run_forward(cfg: MoEConfig, inp: dict, C: int, routing: str = "topk") -> dict:
+def run_forward(cfg: MoEConfig, inp: dict, C: int, routing: str = "topk",
+                save: bool = False) -> dict:
     """moe_forward with every routing output requested; tensors stay on GPU.
-    With expert choice the per-token slots are the E experts."""
-    c = lib_cfg(cfg, C, routing)
+    With expert choice the per-token slots are the E experts.  save: the
+    forward keeps its activations for moe_backward_saved (out["ws"])."""
+    c = lib_cfg(cfg, C, routing, save)
     T, E, k, h = cfg.T, cfg.E, cfg.k, cfg.h
     slots = E if routing == "expert_choice" else k
     rows = moe.moe_num_rows(c)

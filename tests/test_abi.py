@@ -139,6 +139,40 @@ def test_misaligned_pointers_are_rejected(arg):
     assert _raw_status(_cfg(T=0), **{arg: 16 * 7 + 8}) == moe.MOE_OK   # nothing to read
 
 
+def test_flags_validation_and_saved_workspace():
+    """Unknown flag bits are rejected; the save-for-backward flag grows the
+    forward workspace by the kept [a1 | a3] (rows x (2F + 128 B) elements)."""
+    c = _cfg(T=300)
+    c.flags = 2
+    out = ctypes.c_size_t()
+    L = moe.lib()
+    assert L.moe_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == moe.MOE_ERR_INVALID_ARG
+    plain = moe.moe_workspace_bytes(_cfg(T=300))
+    saved = moe.moe_workspace_bytes(_cfg(T=300, save_for_backward=True))
+    rows = moe.moe_num_rows(_cfg(T=300))
+    need = rows * (2 * 128 + 64) * 2
+    assert need <= saved - plain <= need + 256
+
+
+def test_backward_saved_argument_checks():
+    """moe_backward_saved needs the flag and the forward's workspace; both
+    checks run on the host before any device work."""
+    L = moe.lib()
+    w = moe.MoEWeights(w_router=16, w1=32, w3=48, w2=64)
+    r = moe.MoERouteOut(logits=16, topk_idx=32, topk_gate=48, expert_counts=64,
+                        expert_offsets=80, assign_row=96)
+    g = moe.MoEGrads(dx=16, dw1=32, dw3=48, dw2=64)
+
+    def call(cfg, fws, fwb):
+        return L.moe_backward_saved(ctypes.byref(cfg), ctypes.byref(w), 16, 32, ctypes.byref(r),
+                                    fws, fwb, ctypes.byref(g), None, 0, None)
+    assert call(_cfg(T=300), 4096, 1 << 40) == moe.MOE_ERR_INVALID_ARG       # no flag
+    c = _cfg(T=300, save_for_backward=True)
+    assert call(c, None, 0) == moe.MOE_ERR_WORKSPACE
+    assert call(c, 4096, 1024) == moe.MOE_ERR_WORKSPACE                       # too small
+    assert call(c, 4096 + 8, 1 << 40) == moe.MOE_ERR_INVALID_ARG              # misaligned
+
+
 def test_strerror():
     assert moe.strerror(moe.MOE_OK) == "ok"
     assert "workspace" in moe.strerror(moe.MOE_ERR_WORKSPACE)

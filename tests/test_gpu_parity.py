@@ -88,8 +88,10 @@ BACKWARD = ["dropless_softmax", "capacity_heavy_drop", "worked_example_small",
             "tiny_fp32", "f32_capacity", "f32_sigmoid_shared"]
 
 
-def run_backward(cfg, inp, C_lib, gpu, dy, routing="topk"):
-    c = lib_cfg(cfg, C_lib, routing)
+def run_backward(cfg, inp, C_lib, gpu, dy, routing="topk", saved=False):
+    """moe_backward on the forward's routing outputs; saved: the forward ran
+    with save_for_backward and moe_backward_saved reads its workspace."""
+    c = lib_cfg(cfg, C_lib, routing, saved)
     T, E, k, h, F = cfg.T, cfg.E, cfg.k, cfg.h, cfg.F
     slots = E if routing == "expert_choice" else k
     bf = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -107,7 +109,10 @@ def run_backward(cfg, inp, C_lib, gpu, dy, routing="topk"):
                                    "ws1", "ws3", "ws2")}
     route = {n: gpu[n] for n in ("logits", "topk_idx", "topk_gate", "expert_counts",
                                  "expert_offsets", "assign_row")}
-    moe.moe_backward(c, weights, inp["x"], dy, route, grads, ws)
+    if saved:
+        moe.moe_backward_saved(c, weights, inp["x"], dy, route, gpu["ws"], grads, ws)
+    else:
+        moe.moe_backward(c, weights, inp["x"], dy, route, grads, ws)
     torch.cuda.synchronize()
     return grads
 
@@ -161,6 +166,51 @@ def test_backward_is_deterministic():
     for key in a:
         assert torch.equal(a[key].view(torch.int16) if a[key].dtype == torch.bfloat16 else a[key],
                            b[key].view(torch.int16) if b[key].dtype == torch.bfloat16 else b[key]), key
+
+
+SAVED = ["worked_example_small", "sigmoid_bias_shared", "capacity_heavy_drop", "split_k_tail",
+         "zipf_dropless", "e40_ragged", "tiny_fp32", "f32_sigmoid_shared"]
+
+
+@pytest.mark.parametrize("name", SAVED)
+def test_backward_saved_matches_oracle(name):
+    """Forward with save_for_backward (same output bits as without), then
+    the backward from its kept activations: every gradient against the
+    oracle's chain rule on the GPU's routing."""
+    cfg = next(c for c in MEDIUM if c.name == name)
+    print(f"[case] saved backward {name}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    plain = run_forward(cfg, inp, C_lib)
+    gpu = run_forward(cfg, inp, C_lib, save=True)
+    y0, y1 = plain["y"], gpu["y"]
+    if y0.dtype == torch.bfloat16:
+        y0, y1 = y0.view(torch.int16), y1.view(torch.int16)
+    assert torch.equal(y0, y1), "the flag changed the layer output"
+    dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=DEV, dtype=cfg.dtype)
+    g = run_backward(cfg, inp, C_lib, gpu, dy, saved=True)
+    x, wr, w1, w3, w2, lb, shared = oracle_weights(cfg, inp)
+    sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
+    ref = oracle.moe_backward(x, wr, w1, w3, w2, np32(dy), k=cfg.k, gate=cfg.gate, C=C_ref,
+                              logit_bias=lb, select_bias=sb, shared=shared,
+                              idx=gpu["topk_idx"].cpu().numpy())
+    _check_grads(cfg, g, ref, f"saved_backward_{name}")
+
+
+@pytest.mark.parametrize("name", ["ec_sigmoid_shared", "ec_e40_ragged_f32"])
+def test_expert_choice_backward_saved_matches_oracle(name):
+    cfg = next(c for c in EXPERT_CHOICE if c.name == name)
+    print(f"[case] expert choice saved backward {name}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    gpu = run_forward(cfg, inp, C_lib, routing="expert_choice", save=True)
+    dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=DEV, dtype=cfg.dtype)
+    g = run_backward(cfg, inp, C_lib, gpu, dy, routing="expert_choice", saved=True)
+    x, wr, w1, w3, w2, lb, shared = oracle_weights(cfg, inp)
+    ref = oracle.expert_choice_backward(x, wr, w1, w3, w2, np32(dy), C=C_ref, gate=cfg.gate,
+                                        logit_bias=lb, shared=shared,
+                                        scores=gpu["probs"].cpu().numpy().T)
+    _check_grads(cfg, g, ref, f"expert_choice_saved_backward_{name}")
 
 
 # ------------------------------------------------------------ routing variants
