@@ -593,20 +593,22 @@ def test_full_size_routing_and_sampled_outputs(name):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["worked_example", "deepseek_v3"])
-def test_full_size_backward_sampled(name):
-    """The backward at full size, launched as the benchmark launches it:
-    dx and the gate gradients of sampled tokens against the oracle's
-    token-by-token rows; every gradient finite."""
+@pytest.mark.parametrize("name,saved", [("worked_example", False), ("deepseek_v3", False),
+                                        ("worked_example", True)])
+def test_full_size_backward_sampled(name, saved):
+    """The backward at full size, launched as the benchmark launches it
+    (saved: from the activations the forward kept): dx and the gate
+    gradients of sampled tokens against the oracle's token-by-token rows;
+    every gradient finite."""
     cfg = CONFIGS[name]
-    print(f"[case] full backward {name} T={cfg.T} h={cfg.h} E={cfg.E} k={cfg.k} F={cfg.F}",
-          flush=True)
+    print(f"[case] full backward {name} saved={saved} T={cfg.T} h={cfg.h} E={cfg.E} "
+          f"k={cfg.k} F={cfg.F}", flush=True)
     torch.cuda.empty_cache()
     inp = gen_inputs(cfg)
     C_lib, C_ref = capacity_of(cfg)
-    gpu = run_forward(cfg, inp, C_lib)
+    gpu = run_forward(cfg, inp, C_lib, save=saved)
     dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=DEV)
-    g = run_backward(cfg, inp, C_lib, gpu, dy)
+    g = run_backward(cfg, inp, C_lib, gpu, dy, saved=saved)
     for key, v in g.items():
         assert bool(torch.isfinite(v.float()).all()), key
     rng = np.random.default_rng(1)
@@ -619,7 +621,8 @@ def test_full_size_backward_sampled(name):
     t = torch.as_tensor(tok, device=DEV)
     e_dx = rel_err(np32(g["dx"][t]), ref["dx"])
     e_dg = rel_err(np32(g["dgate"][t]), ref["dgate"])
-    _report(f"full_backward_{name}", sampled=len(tok), dx=f"{e_dx:.2e}", dgate=f"{e_dg:.2e}")
+    _report(f"full_backward_{name}{'_saved' if saved else ''}", sampled=len(tok),
+            dx=f"{e_dx:.2e}", dgate=f"{e_dg:.2e}")
     assert e_dx <= 2e-2 and e_dg <= 2e-2
     del g, gpu, inp
     torch.cuda.empty_cache()
