@@ -254,6 +254,65 @@ def test_autograd_layer_matches_oracle(name):
         assert v <= tol_of(cfg), (n, v)
 
 
+def _random_configs(n=16, seed=2024):
+    """Seeded draws over every axis of the layer (shape, gate, biases,
+    capacity, shared expert, dtype), small enough for the oracle."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 24, 40, 64]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        gate = str(rng.choice(["softmax_topk", "softmax_all_topk", "sigmoid_topk_norm"]))
+        cf = [None, (1, 2), (1, 1), (5, 4), (3, 1)][int(rng.integers(0, 5))]
+        out.append(MoEConfig(
+            f"rand{i}", T=int(rng.integers(1, 600)), h=int(rng.choice([128, 256, 384, 512])),
+            E=E, k=k, F=int(rng.choice([128, 256, 384])),
+            dtype="f32" if rng.random() < 0.2 else "bf16", gate=gate, cf=cf,
+            shared=bool(rng.random() < 0.3),
+            logit_bias=("normal", 0.5) if rng.random() < 0.3 else None,
+            select_bias=("normal", 0.1) if gate == "sigmoid_topk_norm" and rng.random() < 0.5
+            else None,
+            seed=int(rng.integers(0, 1000))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(), ids=lambda c: c.name)
+def test_random_configs_forward_and_backward(cfg):
+    """Forward (routing checks and output) and backward (every gradient)
+    against the oracle on seeded random layers."""
+    print(f"[case] random {cfg}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    gpu = run_forward(cfg, inp, C_lib)
+    ref = oracle_forward(cfg, inp, C_ref, maps_only=True)
+    rep = check_routing(cfg, gpu, ref, C_ref, inp)
+    ref_y = oracle_forward(cfg, inp, C_ref, idx=gpu["topk_idx"].cpu().numpy())["y"]
+    y = np32(gpu["y"])
+    assert np.isfinite(y).all()
+    err = rel_err(y, ref_y) if np.abs(ref_y).max() > 0 else float(np.abs(y).max())
+    assert err <= tol_of(cfg), err
+    dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=DEV, dtype=cfg.dtype)
+    g = run_backward(cfg, inp, C_lib, gpu, dy)
+    x, wr, w1, w3, w2, lb, shared = oracle_weights(cfg, inp)
+    sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
+    refb = oracle.moe_backward(x, wr, w1, w3, w2, np32(dy), k=cfg.k, gate=cfg.gate, C=C_ref,
+                               logit_bias=lb, select_bias=sb, shared=shared,
+                               idx=gpu["topk_idx"].cpu().numpy())
+    if lb is None:
+        g.pop("dlogit_bias", None)
+        refb.pop("dlogit_bias", None)
+    names = [n for n in ("dx", "dw1", "dw3", "dw2", "dw_router", "dlogit_bias", "dgate",
+                         "dws1", "dws3", "dws2") if n in g and n in refb]
+    errs = {}
+    for n in names:
+        r = refb[n]
+        errs[n] = (float(np.abs(np32(g[n])).max()) if np.abs(r).max() == 0
+                   else rel_err(np32(g[n]), r))
+    _report(cfg.name, fwd=f"{err:.2e}", **{n: f"{v:.2e}" for n, v in errs.items()}, **rep)
+    for n, v in errs.items():
+        assert v <= tol_of(cfg), (n, v)
+
+
 # ------------------------------------------------------------ routing variants
 SCORE_DROP = ["capacity_heavy_drop", "zipf_cf1", "worked_example_small",
               "split_k_tail_capacity_shared", "f32_capacity"]
