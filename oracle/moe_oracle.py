@@ -21,8 +21,9 @@ no permutation buffer, no blocking and no fusion:
 7. (separately) the load-balance statistics of a routing: the share of
    assignments per expert, the router's mean probability per expert and the
    Switch auxiliary loss built from them;
-8. two routing variants: capacity drops by gate score instead of token
-   order, and expert choice (every expert takes its C best-scoring tokens);
+8. three routing variants: capacity drops by gate score instead of token
+   order, expert choice (every expert takes its C best-scoring tokens), and
+   Sinkhorn balancing of the routing matrix before the top-k;
 9. the backward of the layer: gradients of sum(y * dy) with respect to the
    input, the router and every expert weight, with the routing held fixed
    (token choice, and expert choice with the experts' choices held fixed).
@@ -33,7 +34,8 @@ Sources (pages and the part of each that is followed):
   (swordlidev.github.io): section "MoE 层的数据流" (router → dispatch →
   experts → combine, optional shared experts added) and section
   "Router：token 怎么选专家" (logits = hidden · W_router, then top-k with
-  softmax or sigmoid weights).
+  softmax or sigmoid weights), and its load-balancing table (the sinkhorn
+  row: Sinkhorn iterations make the routing matrix doubly stochastic).
 * "v6:长序列和 MoE:Context Parallel 与 Expert Parallel"
   (charliedreemur.github.io, infra-l7): section "MoE:参数很多,每个 token
   只算一点" (an expert is the SwiGLU FFN h → F → h with three matrices) and
@@ -61,6 +63,9 @@ Readings where the pages are silent or disagree (all listed in the design doc):
   nothing and the other gates are not renormalised;
 * the expert FFN is W2 · (silu(W1 x) ⊙ (W3 x)) with silu(z) = z/(1+e^-z);
 * the layer output excludes the residual; the shared expert has weight 1;
+* Sinkhorn: exp(l) scaled alternately, rows to sum 1 then columns to sum
+  T/E, a given number of times; top-k over the rows of the result; gates
+  from the logits;
 * load balance: f_i counts routed assignments over T*k (before capacity
   drops); P_i averages the router's distribution over all E (softmax of the
   logits, or the sigmoids normalised over E); the loss coefficient alpha is
@@ -260,7 +265,8 @@ def swiglu_ffn(xrows, w1, w3, w2) -> np.ndarray:
 def moe_forward(x, w_router, w1, w3, w2, *, k: int, gate: str,
                 C: Optional[int] = None, logit_bias=None, select_bias=None,
                 shared=None, tokens=None, idx=None, maps_only=False,
-                drop: str = "token", priority=None) -> dict:
+                drop: str = "token", priority=None,
+                sinkhorn_iters: Optional[int] = None) -> dict:
     """Reference forward.
 
     x [T,h]; w_router [E,h]; w1, w3 [E,F,h]; w2 [E,h,F] (any array-likes of
@@ -272,7 +278,9 @@ def moe_forward(x, w_router, w1, w3, w2, *, k: int, gate: str,
     a capacity, "token" keeps the first C assignments of an expert in token
     order, "score" the C with the largest gate (route_maps_score_drop),
     deciding on ``priority`` [T,k] fp32 when given (e.g. the device's own
-    gates) and on this oracle's gates otherwise.
+    gates) and on this oracle's gates otherwise.  ``sinkhorn_iters``: the
+    selection takes the Sinkhorn-balanced top-k (``sinkhorn``; then no
+    select_bias), returned as ``sinkhorn_bias``.
     Returns logits, keys, idx, gates, near_tie, maps, and ``y`` (fp64) for the
     requested tokens, in the order of ``tokens``.
     """
@@ -280,6 +288,11 @@ def moe_forward(x, w_router, w1, w3, w2, *, k: int, gate: str,
     T = x.shape[0]
     E = np.asarray(w_router).shape[0]
     logits = router_logits(x, w_router, logit_bias)
+    sk_bias = None
+    if sinkhorn_iters is not None:
+        if select_bias is not None:
+            raise ValueError("Sinkhorn routing takes no select_bias")
+        select_bias = sk_bias = sinkhorn(logits, sinkhorn_iters)["bias"]
     keys = selection_keys(logits, select_bias)
     if idx is None:
         idx = topk(keys, k)
@@ -294,7 +307,7 @@ def moe_forward(x, w_router, w1, w3, w2, *, k: int, gate: str,
     else:
         raise ValueError(f"unknown drop rule {drop!r}")
     out = {"logits": logits, "keys": keys, "idx": idx, "gates": g,
-           "near_tie": near_tie(keys, k), "maps": maps}
+           "near_tie": near_tie(keys, k), "maps": maps, "sinkhorn_bias": sk_bias}
     if maps_only:
         return out
 
@@ -444,6 +457,41 @@ def expert_choice_forward(x, w_router, w1, w3, w2, *, C: int, gate: str, logit_b
         y += swiglu_ffn(xs, ws1, ws3, ws2)
     m.update({"logits": logits, "y": y, "tokens": tok})
     return m
+
+
+# ---------------------------------------------------------------------------
+# 8b. Sinkhorn routing.  Megatron-LM part 6, "负载均衡" table, row sinkhorn:
+# Sinkhorn iterations rescale the routing matrix until it is doubly
+# stochastic, which evens out the load with no auxiliary loss.  The page
+# gives nothing more; the reading taken: the matrix is exp(l) [T,E]; one
+# iteration scales every row to sum 1 and then every column to sum T/E
+# (the T x E form of a doubly stochastic matrix); the iteration count is an
+# input; each token takes the k largest entries of its row of the balanced
+# matrix, and its gates come from the logits as for plain top-k.
+# ---------------------------------------------------------------------------
+def sinkhorn(logits, iters: int) -> dict:
+    """Sinkhorn-Knopp balancing of exp(logits), fp64.
+
+    Returns ``P`` [T,E] after ``iters`` row-then-column scalings, ``col``
+    [E], the product of every column factor applied (so that
+    P = diag(r) exp(l) diag(col) for some row factors r), and ``bias`` =
+    fp32(ln col).  Within row t the row factor is common and ln is
+    increasing, so ranking P[t] is ranking l[t,e] + ln col[e]: the balanced
+    top-k is topk(selection_keys(l, bias), k).  Each row is shifted by its
+    maximum before exp (the first row scaling cancels any per-row factor).
+    """
+    if iters < 1:
+        raise ValueError("need iters >= 1")
+    l = _f64(logits)
+    T, E = l.shape
+    P = np.exp(l - l.max(axis=1, keepdims=True))
+    col = np.ones(E)
+    for _ in range(iters):
+        P = P / P.sum(axis=1, keepdims=True)        # rows to 1
+        f = (T / E) / P.sum(axis=0)                 # columns to T/E
+        P = P * f[None, :]
+        col = col * f
+    return {"P": P, "col": col, "bias": np.log(col).astype(np.float32)}
 
 
 # ---------------------------------------------------------------------------

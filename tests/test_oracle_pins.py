@@ -654,3 +654,92 @@ def test_backward_rows_match_full_backward():
                                **kw)
     for key in ("dx", "dgate", "dlogits"):
         np.testing.assert_allclose(part[key], full[key][tok], rtol=1e-12, atol=1e-12)
+
+
+# ---- Sinkhorn routing (Megatron-LM part 6, load-balancing table, sinkhorn row)
+
+def test_sinkhorn_two_by_two_limit():
+    """Closed form: scaling rows and columns of [[p, q], [r, s]] keeps the
+    cross ratio ps/(qr), so the doubly stochastic limit is [[x, 1-x],
+    [1-x, x]] with x/(1-x) = sqrt(ps/(qr))."""
+    p, q, r, s = 3.0, 0.5, 1.2, 2.0
+    m = oracle.sinkhorn(np.log([[p, q], [r, s]]), 400)
+    x = math.sqrt(p * s) / (math.sqrt(p * s) + math.sqrt(q * r))
+    np.testing.assert_allclose(m["P"], [[x, 1 - x], [1 - x, x]], atol=1e-12)
+
+
+def test_sinkhorn_rank_one_is_uniform_after_one_iteration():
+    """l[t,e] = a_t + b_e: one row scaling leaves e^{b_e}/Z in every row; the
+    column scaling then makes every entry 1/E, and its factors undo b."""
+    rng = np.random.default_rng(5)
+    a, b = rng.normal(size=7), 2 * rng.normal(size=3)
+    m = oracle.sinkhorn(a[:, None] + b[None, :], 1)
+    np.testing.assert_allclose(m["P"], np.full((7, 3), 1 / 3), rtol=1e-12)
+    assert np.ptp(m["bias"].astype(np.float64) + b) < 1e-5
+
+
+def test_sinkhorn_marginals_and_form():
+    """Columns sum to T/E after every iteration, rows to 1 at convergence,
+    and the result is diag(r) exp(l) diag(col)."""
+    rng = np.random.default_rng(11)
+    T, E = 40, 6
+    l = 2 * rng.normal(size=(T, E))
+    np.testing.assert_allclose(oracle.sinkhorn(l, 1)["P"].sum(0), np.full(E, T / E), rtol=1e-12)
+    m = oracle.sinkhorn(l, 300)
+    np.testing.assert_allclose(m["P"].sum(1), 1.0, atol=1e-9)
+    np.testing.assert_allclose(m["P"].sum(0), T / E, rtol=1e-12)
+    R = m["P"] / (np.exp(l) * m["col"][None, :])
+    np.testing.assert_allclose(R, np.repeat(R[:, :1], E, axis=1), rtol=1e-12)
+
+
+def test_sinkhorn_cancels_expert_offsets():
+    """Adding c_e to column e of the logits leaves the balanced matrix, and
+    so the selection, unchanged at convergence; the bias absorbs -c_e."""
+    rng = np.random.default_rng(3)
+    l, c = rng.normal(size=(64, 8)), 3 * rng.normal(size=8)
+    m0, m1 = oracle.sinkhorn(l, 500), oracle.sinkhorn(l + c, 500)
+    np.testing.assert_allclose(m1["P"], m0["P"], atol=1e-9)
+    assert np.ptp(np.log(m1["col"]) - np.log(m0["col"]) + c) < 1e-9
+
+
+def test_sinkhorn_topk_ranks_the_balanced_matrix():
+    """The top-k of selection_keys(l, bias) is the top-k of the rows of P."""
+    rng = np.random.default_rng(8)
+    l = (rng.normal(size=(300, 16)) + np.linspace(0, 3, 16)).astype(np.float32)
+    m = oracle.sinkhorn(l, 20)
+    keys = oracle.selection_keys(l, m["bias"])
+    k = 3
+    ok = ~oracle.near_tie(keys, k, 1e-4)
+    assert ok.mean() > 0.95
+    via_p = np.argsort(-m["P"], axis=1, kind="stable")[:, :k]
+    np.testing.assert_array_equal(oracle.topk(keys, k)[ok], via_p[ok])
+
+
+def test_sinkhorn_evens_out_a_skewed_router():
+    """Zipf-biased logits send several times the mean load to the hottest
+    expert under plain top-k; after balancing every load is near the mean."""
+    rng = np.random.default_rng(1)
+    T, E, k = 4096, 16, 2
+    l = (rng.normal(size=(T, E)) - 1.2 * np.log(np.arange(E) + 1)).astype(np.float32)
+    mean = T * k / E
+    plain = np.bincount(oracle.topk(l, k).ravel(), minlength=E)
+    assert plain.max() > 3 * mean
+    m = oracle.sinkhorn(l, 50)
+    bal = np.bincount(oracle.topk(oracle.selection_keys(l, m["bias"]), k).ravel(), minlength=E)
+    assert 0.75 * mean < bal.min() and bal.max() < 1.25 * mean
+
+
+def test_moe_forward_sinkhorn_route():
+    """moe_forward with Sinkhorn routing selects on the balanced keys; the
+    gates still come from the logits of the selected experts."""
+    cfg = CONFIGS["tiny_fp32"]
+    inp = make_inputs(cfg, device="cpu")
+    a = [inp[n].float().numpy() for n in ("x", "w_router", "w1", "w3", "w2")]
+    out = oracle.moe_forward(*a, k=cfg.k, gate=cfg.gate, sinkhorn_iters=5, maps_only=True)
+    bias = oracle.sinkhorn(out["logits"], 5)["bias"]
+    np.testing.assert_array_equal(out["sinkhorn_bias"], bias)
+    np.testing.assert_array_equal(out["idx"], oracle.topk(oracle.selection_keys(out["logits"], bias), cfg.k))
+    np.testing.assert_array_equal(out["gates"], oracle.gates(out["logits"], out["idx"], cfg.gate))
+    with pytest.raises(ValueError):
+        oracle.moe_forward(*a, k=cfg.k, gate=cfg.gate, sinkhorn_iters=5,
+                           select_bias=np.zeros(cfg.E, np.float32), maps_only=True)
