@@ -100,6 +100,19 @@ extern "C" {
  *                     select_bias is rejected (MOE_ERR_INVALID_ARG).  Only
  *                     moe_forward, moe_grouped_gemm_swiglu,
  *                     moe_unpermute_combine and moe_load_balance accept it.
+ *   SINKHORN          token choice on the Sinkhorn-balanced router
+ *                     (Megatron-LM part 6, load-balancing table, row
+ *                     sinkhorn: the routing matrix is rescaled until doubly
+ *                     stochastic).  exp(logits) [T,E] is scaled
+ *                     sinkhorn_iters times, rows to sum 1 then columns to sum
+ *                     T/E; each token takes the k largest entries of its row
+ *                     of the result, which is the top-k of the key
+ *                     logit + bias[e] with bias = ln of the product of the
+ *                     column factors (fp32, written to route_bias).  Gates
+ *                     come from the logits (cfg.gate) as for TOPK, and a
+ *                     capacity drops in token order as for TOPK.  A
+ *                     select_bias is rejected (MOE_ERR_INVALID_ARG); every
+ *                     later stage treats the selection as TOPK's.
  * Selection decisions are integer compares of fp32 keys on the device, so
  * every run routes the same.                                              */
 /* Flags of moe_cfg_t.flags.
@@ -115,9 +128,12 @@ extern "C" {
 #define MOE_ROUTE_TOPK 0
 #define MOE_ROUTE_TOPK_SCORE_DROP 1
 #define MOE_ROUTE_EXPERT_CHOICE 2
+#define MOE_ROUTE_SINKHORN 3
+#define MOE_MAX_SINKHORN_ITERS 1000
 
 /* Kernels moe_forward launches, in order, each one a timed stage:
- *   0 router GEMM, 1 top-k + gates + chunk histogram, 2 scan (counts,
+ *   0 router GEMM, 1 top-k + gates + chunk histogram (after the Sinkhorn
+ *   iterations with SINKHORN routing), 2 scan (counts,
  *   offsets, GEMM tile table), 3 assign (ranks, rows), 4 permute copy,
  *   5 grouped GEMM 1 + SwiGLU, 6 grouped GEMM 2, 7 combine.
  * MOE_NUM_EVENTS events bracket them (see moe_forward).                   */
@@ -137,6 +153,8 @@ typedef struct moe_cfg {
   int64_t capacity;    /* 0: dropless; > 0: capacity C rows per expert */
   int32_t routing;     /* MOE_ROUTE_* */
   int32_t flags;       /* MOE_FLAG_* bits, 0 for none */
+  int32_t sinkhorn_iters; /* SINKHORN: 1..MOE_MAX_SINKHORN_ITERS iterations;
+                             0 for every other routing */
 } moe_cfg_t;
 
 typedef struct moe_weights {
@@ -166,6 +184,7 @@ typedef struct moe_route_out {
   int32_t* assign_row;     /* [T*k] row of (t,j) in x_perm, -1 if dropped */
   int32_t* row_token;      /* [rows] token of each row, -1 for padding */
   float* probs;            /* [E,T] expert choice only */
+  float* route_bias;       /* [E] Sinkhorn only: the selection bias found */
 } moe_route_out_t;
 
 /* Gradients written by moe_backward (device pointers in a host struct). */
@@ -209,7 +228,9 @@ int moe_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes);
  *   logits       [T,E] fp32 out, or NULL (then kept in the workspace)
  *   topk_idx     [T,k] int32 out: slot 0 = largest key
  *   topk_gate    [T,k] fp32 out: gate of each slot (cfg->gate)
- *   ws, ws_bytes workspace (moe_workspace_bytes)                          */
+ *   ws, ws_bytes workspace (moe_workspace_bytes); required with SINKHORN
+ *                routing, whose selection bias is kept there
+ * Expert choice: MOE_ERR_UNSUPPORTED (moe_forward routes it).             */
 int moe_router_topk(const moe_cfg_t* cfg, const void* x, const void* w_router,
                     const float* logit_bias, const float* select_bias,
                     float* logits, int32_t* topk_idx, float* topk_gate,

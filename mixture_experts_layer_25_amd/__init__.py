@@ -44,10 +44,13 @@ DTYPE_BY_NAME = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16}
 MOE_ROUTE_TOPK = 0
 MOE_ROUTE_TOPK_SCORE_DROP = 1
 MOE_ROUTE_EXPERT_CHOICE = 2
+MOE_ROUTE_SINKHORN = 3
+MOE_MAX_SINKHORN_ITERS = 1000
 ROUTING_BY_NAME = {
     "topk": MOE_ROUTE_TOPK,
     "topk_score_drop": MOE_ROUTE_TOPK_SCORE_DROP,
     "expert_choice": MOE_ROUTE_EXPERT_CHOICE,
+    "sinkhorn": MOE_ROUTE_SINKHORN,
 }
 
 # Every symbol include/moe.h declares.
@@ -73,6 +76,7 @@ class MoECfg(ctypes.Structure):
         ("capacity", ctypes.c_int64),
         ("routing", ctypes.c_int32),
         ("flags", ctypes.c_int32),
+        ("sinkhorn_iters", ctypes.c_int32),
     ]
 
 
@@ -84,7 +88,7 @@ class MoEWeights(ctypes.Structure):
 class MoERouteOut(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_idx", "topk_gate", "expert_counts", "expert_offsets",
-        "assign_row", "row_token", "probs")]
+        "assign_row", "row_token", "probs", "route_bias")]
 
 
 class MoEGrads(ctypes.Structure):
@@ -171,7 +175,8 @@ MOE_FLAG_SAVE_FOR_BACKWARD = 1
 
 def make_cfg(T: int, h: int, F: int, E: int, k: int, dtype="bf16",
              gate="softmax_topk", capacity: int = 0, has_shared: bool = False,
-             routing="topk", save_for_backward: bool = False) -> MoECfg:
+             routing="topk", save_for_backward: bool = False,
+             sinkhorn_iters: int = 0) -> MoECfg:
     c = MoECfg()
     c.struct_size = ctypes.sizeof(MoECfg)
     c.dtype = DTYPE_BY_NAME[dtype] if isinstance(dtype, str) else int(dtype)
@@ -181,6 +186,7 @@ def make_cfg(T: int, h: int, F: int, E: int, k: int, dtype="bf16",
     c.capacity = int(capacity)
     c.routing = ROUTING_BY_NAME[routing] if isinstance(routing, str) else int(routing)
     c.flags = MOE_FLAG_SAVE_FOR_BACKWARD if save_for_backward else 0
+    c.sinkhorn_iters = int(sinkhorn_iters)
     return c
 
 
@@ -308,7 +314,8 @@ def moe_forward(cfg, weights: dict, x, y, route: Optional[dict] = None, ws=None,
     """Fused layer.  ``weights``: dict with w_router, w1, w3, w2 and optional
     logit_bias, select_bias, ws1, ws3, ws2.  ``route``: optional dict of
     output tensors (logits, topk_idx, topk_gate, expert_counts,
-    expert_offsets, assign_row, row_token).  ``events``: None or
+    expert_offsets, assign_row, row_token; probs for expert choice,
+    route_bias for Sinkhorn routing).  ``events``: None or
     MOE_NUM_EVENTS ``torch.cuda.Event(enable_timing=True)``."""
     wp, wb = _ws(ws)
     ws_struct = weights_struct(weights)

@@ -49,7 +49,8 @@ class _MoELayer(torch.autograd.Function):
         shared = ws1 is not None
         cfg = make_cfg(T, h, F, E, settings["k"], dtype, settings["gate"],
                        capacity=settings["capacity"], has_shared=shared,
-                       routing=settings["routing"], save_for_backward=True)
+                       routing=settings["routing"], save_for_backward=True,
+                       sinkhorn_iters=settings["sinkhorn_iters"])
         ws = torch.empty(max(moe_workspace_bytes(cfg), 1), dtype=torch.uint8, device=x.device)
         route = _route_buffers(T, E, settings["k"], settings["routing"] == "expert_choice",
                                x.device)
@@ -85,14 +86,17 @@ class _MoELayer(torch.autograd.Function):
 
 def moe_layer(x: torch.Tensor, w_router: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor,
               w2: torch.Tensor, *, k: int, gate: str = "softmax_topk", capacity: int = 0,
-              routing: str = "topk", logit_bias: Optional[torch.Tensor] = None,
+              routing: str = "topk", sinkhorn_iters: int = 0,
+              logit_bias: Optional[torch.Tensor] = None,
               select_bias: Optional[torch.Tensor] = None,
               shared: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
               ) -> torch.Tensor:
     """The MoE layer y [T,h] of x [T,h] with gradients for x, w_router, w1,
     w3, w2, logit_bias and the shared expert's (ws1, ws3, ws2); select_bias
-    gets none (it only decides the top-k)."""
+    gets none (it only decides the top-k).  routing: "topk",
+    "topk_score_drop", "expert_choice" or "sinkhorn" (with sinkhorn_iters)."""
     ws1, ws3, ws2 = shared if shared is not None else (None, None, None)
-    settings = {"k": k, "gate": gate, "capacity": capacity, "routing": routing}
+    settings = {"k": k, "gate": gate, "capacity": capacity, "routing": routing,
+                "sinkhorn_iters": sinkhorn_iters}
     return _MoELayer.apply(settings, x, w_router, w1, w3, w2, logit_bias, select_bias,
                            ws1, ws3, ws2)

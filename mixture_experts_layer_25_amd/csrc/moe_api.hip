@@ -49,8 +49,11 @@ int check_cfg(const moe_cfg_t* c) {
   if (c->T < 0 || c->h <= 0 || c->F <= 0 || c->E <= 0 || c->k <= 0 || c->capacity < 0)
     return MOE_ERR_INVALID_ARG;
   if (c->has_shared != 0 && c->has_shared != 1) return MOE_ERR_INVALID_ARG;
-  if (c->routing < MOE_ROUTE_TOPK || c->routing > MOE_ROUTE_EXPERT_CHOICE ||
+  if (c->routing < MOE_ROUTE_TOPK || c->routing > MOE_ROUTE_SINKHORN ||
       (c->flags & ~MOE_FLAG_SAVE_FOR_BACKWARD) != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->sinkhorn_iters < 0 || c->sinkhorn_iters > MOE_MAX_SINKHORN_ITERS ||
+      (c->routing == MOE_ROUTE_SINKHORN) != (c->sinkhorn_iters > 0))
     return MOE_ERR_INVALID_ARG;
   if (c->routing == MOE_ROUTE_TOPK_SCORE_DROP && c->capacity <= 0) return MOE_ERR_INVALID_ARG;
   if (c->routing == MOE_ROUTE_EXPERT_CHOICE && c->T > 0 &&
@@ -70,6 +73,9 @@ struct Layout {
   // routing variants: expert choice (probs, selection rows and gates per
   // (token, expert)); score drop (the dropless maps it ranks within)
   size_t probs, selrow, gatete, offs_dl, gtab_dl, assign_dl, rowtok_dl, key_dl, aid_dl;
+  // Sinkhorn routing: the per-block column pairs (two iterations' worth)
+  // and the selection bias
+  size_t skpart, skbias;
   size_t partials, xperm, act, yperm, a13, total;
 };
 
@@ -111,6 +117,9 @@ Layout layout_of(const moe_cfg_t& c) {
   L.rowtok_dl = take(sd ? (size_t)(T * k) * 4 : 0);
   L.key_dl = take(sd ? (size_t)(T * k) * 8 : 0);
   L.aid_dl = take(sd ? (size_t)(T * k) * 4 : 0);
+  const bool sk = c.routing == MOE_ROUTE_SINKHORN;
+  L.skpart = take(sk ? (size_t)(2 * moe::sinkhorn_blocks(T, (int)E) * E) * 8 : 0);
+  L.skbias = take(sk ? (size_t)E * 4 : 0);
   L.partials = take(c.dtype == MOE_DTYPE_BF16 ? (size_t)moe::kSplitPartialFloats * 4 : 0);
   L.xperm = take((size_t)rows * ld_h(c) * es);
   L.act = take((size_t)rows_all * ld_f(c) * es);
@@ -212,15 +221,24 @@ MOE_API int moe_router_topk(const moe_cfg_t* cfg, const void* x, const void* w_r
   const moe_cfg_t& c = *cfg;
   if (c.T == 0) return MOE_OK;
   if (c.routing == MOE_ROUTE_EXPERT_CHOICE) return MOE_ERR_UNSUPPORTED;
-  if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  const bool sk = c.routing == MOE_ROUTE_SINKHORN;
+  if (!x || !w_router || !topk_idx || !topk_gate || (sk && select_bias))
+    return MOE_ERR_INVALID_ARG;
   if (misaligned(x, w_router, logit_bias, select_bias, logits, topk_idx, topk_gate, ws))
     return MOE_ERR_INVALID_ARG;
-  if (!logits && (st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  if ((!logits || sk) && (st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
-  float* lg = logits ? logits : at<float>(ws, layout_of(c).logits);
+  const Layout L = layout_of(c);
+  float* lg = logits ? logits : at<float>(ws, L.logits);
   MOE_TRY(moe::launch_router(c.dtype, x, w_router, logit_bias, lg, c.T, c.h, c.E, s));
-  MOE_TRY(moe::launch_topk(lg, select_bias, c.gate, c.T, c.E, c.k, topk_idx, topk_gate,
-                           nullptr, s));
+  const float* sb = select_bias;
+  if (sk) {
+    float* bias = at<float>(ws, L.skbias);
+    MOE_TRY(moe::launch_sinkhorn(lg, c.T, c.E, c.sinkhorn_iters, at<float2>(ws, L.skpart), bias,
+                                 s));
+    sb = bias;
+  }
+  MOE_TRY(moe::launch_topk(lg, sb, c.gate, c.T, c.E, c.k, topk_idx, topk_gate, nullptr, s));
   return MOE_OK;
 }
 
@@ -232,7 +250,7 @@ MOE_API int moe_permute(const moe_cfg_t* cfg, const void* x, const int32_t* topk
   if (st != MOE_OK) return st;
   const moe_cfg_t& c = *cfg;
   if (c.T == 0) return MOE_OK;
-  if (c.routing != MOE_ROUTE_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (c.routing != MOE_ROUTE_TOPK && c.routing != MOE_ROUTE_SINKHORN) return MOE_ERR_UNSUPPORTED;
   if (!x || !topk_idx || !expert_counts || !expert_offsets || !assign_row || !row_token ||
       !x_perm)
     return MOE_ERR_INVALID_ARG;
@@ -623,12 +641,14 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   // expert choice ranks by router probability; a selection-only bias has
   // no meaning there
   if (c.routing == MOE_ROUTE_EXPERT_CHOICE && w->select_bias) return MOE_ERR_INVALID_ARG;
+  // Sinkhorn routing finds its own selection bias
+  if (c.routing == MOE_ROUTE_SINKHORN && w->select_bias) return MOE_ERR_INVALID_ARG;
   if (misaligned(x, y, ws, w->w_router, w->w1, w->w3, w->w2, w->logit_bias, w->select_bias) ||
       misaligned(w->ws1, w->ws3, w->ws2))
     return MOE_ERR_INVALID_ARG;
   if (route && (misaligned(route->logits, route->topk_idx, route->topk_gate, route->expert_counts,
                            route->expert_offsets, route->assign_row, route->row_token) ||
-                misaligned(route->probs)))
+                misaligned(route->probs, route->route_bias)))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
@@ -680,8 +700,14 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
     MOE_TRY(mark(4));
     MOE_TRY(moe::launch_gather_rows(c.dtype, x, rowtok, rows, c.T, c.h, xperm, ld_h(c), s));
   } else {
-    MOE_TRY(moe::launch_topk(logits, w->select_bias, c.gate, c.T, c.E, c.k, idx, gate,
-                             hist, s));
+    const float* sb = w->select_bias;
+    if (c.routing == MOE_ROUTE_SINKHORN) {
+      float* bias = r.route_bias ? r.route_bias : at<float>(ws, L.skbias);
+      MOE_TRY(moe::launch_sinkhorn(logits, c.T, c.E, c.sinkhorn_iters, at<float2>(ws, L.skpart),
+                                   bias, s));
+      sb = bias;
+    }
+    MOE_TRY(moe::launch_topk(logits, sb, c.gate, c.T, c.E, c.k, idx, gate, hist, s));
     MOE_TRY(mark(2));
     if (c.routing == MOE_ROUTE_TOPK_SCORE_DROP) {
       // dropless ranks first: each expert's assignments in token order

@@ -138,6 +138,13 @@ hipError_t launch_load_balance(const float* logits, const int32_t* counts, int g
 hipError_t launch_router_probs(const float* logits, int gate, int64_t T, int E, float* probs_et,
                                hipStream_t st);
 
+// Sinkhorn routing (sinkhorn.hip): bias[E] = ln of the column factors of
+// iters row/column scalings of exp(logits).  parts: 2 * sinkhorn_blocks(T,
+// E) * E float2 of scratch.
+int sinkhorn_blocks(int64_t T, int E);
+hipError_t launch_sinkhorn(const float* logits, int64_t T, int E, int iters, float2* parts,
+                           float* bias, hipStream_t s);
+
 hipError_t launch_topk(const float* logits, const float* select_bias,
                        int gate, int64_t T, int E, int k, int32_t* idx,
                        float* gate_out, int32_t* hist, hipStream_t s);

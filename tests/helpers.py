@@ -41,18 +41,19 @@ def capacity_of(cfg: MoEConfig):
     return c_lib, c_ref
 
 
-def lib_cfg(cfg: MoEConfig, C: int, routing: str = "topk", save: bool = False):
+def lib_cfg(cfg: MoEConfig, C: int, routing: str = "topk", save: bool = False,
+            sinkhorn_iters: int = 0):
     return moe.make_cfg(cfg.T, cfg.h, cfg.F, cfg.E, cfg.k, cfg.dtype, cfg.gate,
                         capacity=C, has_shared=cfg.shared, routing=routing,
-                        save_for_backward=save)
+                        save_for_backward=save, sinkhorn_iters=sinkhorn_iters)
 
 
 def run_forward(cfg: MoEConfig, inp: dict, C: int, routing: str = "topk",
-                save: bool = False) -> dict:
+                save: bool = False, sinkhorn_iters: int = 0) -> dict:
     """moe_forward with every routing output requested; tensors stay on GPU.
     With expert choice the per-token slots are the E experts.  save: the
     forward keeps its activations for moe_backward_saved (out["ws"])."""
-    c = lib_cfg(cfg, C, routing, save)
+    c = lib_cfg(cfg, C, routing, save, sinkhorn_iters)
     T, E, k, h = cfg.T, cfg.E, cfg.k, cfg.h
     slots = E if routing == "expert_choice" else k
     rows = moe.moe_num_rows(c)
@@ -68,6 +69,8 @@ def run_forward(cfg: MoEConfig, inp: dict, C: int, routing: str = "topk",
     }
     if routing == "expert_choice":
         route["probs"] = torch.empty((E, T), dtype=torch.float32, device=DEV)
+    if routing == "sinkhorn":
+        route["route_bias"] = torch.empty((E,), dtype=torch.float32, device=DEV)
     # fill outputs with garbage so that an unwritten entry shows up
     for v in route.values():
         v.fill_(-7)
@@ -95,7 +98,7 @@ def oracle_weights(cfg: MoEConfig, inp: dict):
 
 
 def oracle_forward(cfg: MoEConfig, inp: dict, C_ref, tokens=None, idx=None,
-                   maps_only=False, drop="token", priority=None):
+                   maps_only=False, drop="token", priority=None, sinkhorn_iters=None):
     x = np32(inp["x"])
     wr = np32(inp["w_router"])
     lb = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
@@ -109,17 +112,22 @@ def oracle_forward(cfg: MoEConfig, inp: dict, C_ref, tokens=None, idx=None,
     return oracle.moe_forward(x, wr, w1, w3, w2, k=cfg.k, gate=cfg.gate, C=C_ref,
                               logit_bias=lb, select_bias=sb, shared=shared,
                               tokens=tokens, idx=idx, maps_only=maps_only, drop=drop,
-                              priority=priority)
+                              priority=priority, sinkhorn_iters=sinkhorn_iters)
 
 
 def check_routing(cfg: MoEConfig, gpu: dict, ref: dict, C_ref, inp: dict,
-                  drop: str = "token") -> dict:
+                  drop: str = "token", tie: float = 1e-5) -> dict:
     """Routing checks; returns a small report.  drop="score": the capacity
-    maps are the score-priority ones, decided on the GPU's own gates."""
+    maps are the score-priority ones, decided on the GPU's own gates.  With
+    Sinkhorn routing the GPU's own keys add the GPU's route_bias, and tokens
+    whose oracle key gap is below ``tie`` may choose either way."""
     g_logits = gpu["logits"].cpu().numpy()
     g_idx = gpu["topk_idx"].cpu().numpy()
     g_gate = gpu["topk_gate"].cpu().numpy()
     sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
+    if "route_bias" in gpu:
+        assert sb is None
+        sb = gpu["route_bias"].cpu().numpy()
     # logits: fp32-accumulated on the GPU vs fp64-accumulated then rounded
     dl = float(np.abs(g_logits - ref["logits"]).max())
     scale = max(1.0, float(np.abs(ref["logits"]).max()))
@@ -128,13 +136,14 @@ def check_routing(cfg: MoEConfig, gpu: dict, ref: dict, C_ref, inp: dict,
     keys_gpu = oracle.selection_keys(g_logits, sb)
     np.testing.assert_array_equal(oracle.topk(keys_gpu, cfg.k), g_idx)
     # 2. selection vs the oracle's logits: exact off near-ties, valid on them
-    tie = ref["near_tie"]
+    thr = tie
+    tie = oracle.near_tie(ref["keys"], cfg.k, thr)
     same = (np.sort(g_idx, 1) == np.sort(ref["idx"], 1)).all(1)
     assert same[~tie].all(), f"{(~same & ~tie).sum()} non-tie tokens route differently"
     if tie.any():
         kth = -np.sort(-ref["keys"].astype(np.float64), 1)[:, cfg.k - 1]
         chosen = np.take_along_axis(ref["keys"].astype(np.float64), g_idx.astype(np.int64), 1)
-        assert (chosen[tie] >= kth[tie, None] - 1e-5).all()
+        assert (chosen[tie] >= kth[tie, None] - thr).all()
     # 3. gates from the GPU's logits and selection
     g_ref = oracle.gates(g_logits, g_idx, cfg.gate)
     dg = float(np.abs(g_gate - g_ref).max())

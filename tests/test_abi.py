@@ -43,6 +43,8 @@ def test_struct_layouts_match_header(tmp_path):
         " sizeof(moe_route_out_t), offsetof(moe_weights_t, ws2), offsetof(moe_cfg_t, routing),"
         " offsetof(moe_route_out_t, probs));\n"
         'printf("%zu %zu\\n", sizeof(moe_grads_t), offsetof(moe_grads_t, dgate));\n'
+        'printf("%zu %zu %d\\n", offsetof(moe_cfg_t, sinkhorn_iters),'
+        ' offsetof(moe_route_out_t, route_bias), MOE_MAX_SINKHORN_ITERS);\n'
         'printf("%d %d\\n", MOE_NUM_STAGES, MOE_NUM_EVENTS);\n'
         "return 0;}\n")
     exe = tmp_path / "layout"
@@ -54,9 +56,12 @@ def test_struct_layouts_match_header(tmp_path):
           ctypes.sizeof(moe.MoERouteOut), moe.MoEWeights.ws2.offset, moe.MoECfg.routing.offset,
           moe.MoERouteOut.probs.offset]
     assert c == py
-    assert [int(v) for v in lines[2].split()] == [moe.MOE_NUM_STAGES, moe.MOE_NUM_EVENTS]
+    assert [int(v) for v in lines[3].split()] == [moe.MOE_NUM_STAGES, moe.MOE_NUM_EVENTS]
     assert [int(v) for v in lines[1].split()] == [ctypes.sizeof(moe.MoEGrads),
                                                   moe.MoEGrads.dgate.offset]
+    assert [int(v) for v in lines[2].split()] == [moe.MoECfg.sinkhorn_iters.offset,
+                                                  moe.MoERouteOut.route_bias.offset,
+                                                  moe.MOE_MAX_SINKHORN_ITERS]
 
 
 @pytest.mark.parametrize("T,E,k,num,den", [
@@ -152,6 +157,27 @@ def test_flags_validation_and_saved_workspace():
     rows = moe.moe_num_rows(_cfg(T=300))
     need = rows * (2 * 128 + 64) * 2
     assert need <= saved - plain <= need + 256
+
+
+def test_sinkhorn_validation_and_workspace():
+    """Sinkhorn routing needs 1..MOE_MAX_SINKHORN_ITERS iterations and every
+    other routing none; it takes no select_bias and keeps its bias and
+    column pairs in the workspace, which moe_router_topk then requires."""
+    out = ctypes.c_size_t()
+    L = moe.lib()
+    for kw in (dict(routing="sinkhorn"), dict(sinkhorn_iters=3),
+               dict(routing="sinkhorn", sinkhorn_iters=moe.MOE_MAX_SINKHORN_ITERS + 1),
+               dict(routing="sinkhorn", sinkhorn_iters=-1)):
+        c = _cfg(T=300, **kw)
+        assert L.moe_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == \
+            moe.MOE_ERR_INVALID_ARG, kw
+    c = _cfg(T=300, routing="sinkhorn", sinkhorn_iters=moe.MOE_MAX_SINKHORN_ITERS)
+    assert L.moe_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == moe.MOE_OK
+    c = _cfg(T=300, routing="sinkhorn", sinkhorn_iters=4)
+    assert _raw_status(c, sb=96) == moe.MOE_ERR_INVALID_ARG
+    assert _raw_status(c) == moe.MOE_ERR_WORKSPACE        # logits given, bias needs ws
+    grow = moe.moe_workspace_bytes(c) - moe.moe_workspace_bytes(_cfg(T=300))
+    assert 0 < grow <= 2 * 256 * 8 * 8 + 8 * 4 + 512
 
 
 def test_backward_saved_argument_checks():

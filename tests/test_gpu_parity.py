@@ -91,7 +91,11 @@ BACKWARD = ["dropless_softmax", "capacity_heavy_drop", "worked_example_small",
 def run_backward(cfg, inp, C_lib, gpu, dy, routing="topk", saved=False):
     """moe_backward on the forward's routing outputs; saved: the forward ran
     with save_for_backward and moe_backward_saved reads its workspace."""
-    c = lib_cfg(cfg, C_lib, routing, saved)
+    return _backward_with_cfg(cfg, lib_cfg(cfg, C_lib, routing, saved), inp, gpu, dy,
+                              routing, saved)
+
+
+def _backward_with_cfg(cfg, c, inp, gpu, dy, routing="topk", saved=False):
     T, E, k, h, F = cfg.T, cfg.E, cfg.k, cfg.h, cfg.F
     slots = E if routing == "expert_choice" else k
     bf = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -413,6 +417,99 @@ def test_expert_choice_backward_matches_oracle(cfg):
                                         logit_bias=lb, shared=shared,
                                         scores=gpu["probs"].cpu().numpy().T)
     _check_grads(cfg, g, ref, f"expert_choice_backward_{cfg.name}")
+
+
+# Sinkhorn routing: (config, iterations).  Covers one- to 16-entry lanes
+# (E = 8 .. 1024), one token, fp32, capacity drops and an uneven router.
+SINKHORN = [("zipf_dropless", 8), ("zipf_cf1", 30), ("worked_example_small", 5),
+            ("mixtral_bias", 1), ("e1024_k16", 3), ("e40_ragged", 4), ("tiny_fp32", 10),
+            ("f32_capacity", 6), ("one_token", 3), ("k_equals_e", 2)]
+# |bias_gpu - bias_oracle| on the same logits: fp32 log-sum-exp over at most
+# T terms per column against fp64; keys near-tied within twice that (plus the
+# logits' own rounding) may select either way.
+SK_BIAS_TOL = 5e-5
+SK_TIE = 2 * SK_BIAS_TOL + 1e-5
+
+
+def _sinkhorn_case(cfg, iters, C_lib, C_ref):
+    inp = gen_inputs(cfg)
+    gpu = run_forward(cfg, inp, C_lib, routing="sinkhorn", sinkhorn_iters=iters)
+    sk = oracle.sinkhorn(gpu["logits"].cpu().numpy(), iters)
+    db = float(np.abs(gpu["route_bias"].cpu().numpy().astype(np.float64) -
+                      np.log(sk["col"])).max())
+    ref = oracle_forward(cfg, inp, C_ref, maps_only=True, sinkhorn_iters=iters)
+    rep = check_routing(cfg, gpu, ref, C_ref, inp, tie=SK_TIE)
+    return inp, gpu, ref, db, rep
+
+
+@pytest.mark.parametrize("name,iters", SINKHORN)
+def test_sinkhorn_matches_oracle(name, iters):
+    """Sinkhorn routing: the GPU's selection bias within SK_BIAS_TOL of the
+    oracle's balancing of the same logits; selection bit-exact on the GPU's
+    own keys and equal to the oracle's off near-ties; maps bit-exact; every
+    output row against the oracle's layer on the GPU's selection."""
+    cfg = next(c for c in MEDIUM if c.name == name)
+    print(f"[case] sinkhorn {name} iters={iters}", flush=True)
+    C_lib, C_ref = capacity_of(cfg)
+    inp, gpu, ref, db, rep = _sinkhorn_case(cfg, iters, C_lib, C_ref)
+    ref_y = oracle_forward(cfg, inp, C_ref, idx=gpu["topk_idx"].cpu().numpy())["y"]
+    err = rel_err(np32(gpu["y"]), ref_y)
+    counts = gpu["expert_counts"].cpu().numpy()
+    _report(f"sinkhorn_{name}", rel_err=f"{err:.2e}", bias_err=f"{db:.1e}",
+            max_over_mean=f"{counts.max() / counts.mean():.2f}", **rep)
+    assert db <= SK_BIAS_TOL
+    assert err <= tol_of(cfg)
+
+
+def test_sinkhorn_evens_out_zipf_load():
+    """With the Zipf-biased router the hottest expert gets several times the
+    mean under plain top-k; 30 Sinkhorn iterations bring every load within
+    25 % of the mean (the balancing the routing exists for)."""
+    cfg = next(c for c in MEDIUM if c.name == "zipf_dropless")
+    inp = gen_inputs(cfg)
+    plain = run_forward(cfg, inp, 0)["expert_counts"].cpu().numpy()
+    bal = run_forward(cfg, inp, 0, routing="sinkhorn",
+                      sinkhorn_iters=30)["expert_counts"].cpu().numpy()
+    mean = cfg.T * cfg.k / cfg.E
+    _report("sinkhorn_balance", plain_max=int(plain.max()), sinkhorn_max=int(bal.max()),
+            sinkhorn_min=int(bal.min()), mean=mean)
+    assert plain.max() > 3 * mean
+    assert 0.75 * mean < bal.min() and bal.max() < 1.25 * mean
+
+
+@pytest.mark.parametrize("name,iters", [("zipf_cf1", 10), ("tiny_fp32", 4)])
+def test_sinkhorn_backward_matches_oracle(name, iters):
+    """The backward with the Sinkhorn selection held fixed equals the top-k
+    backward on that selection (the bias only chose the experts)."""
+    cfg = next(c for c in MEDIUM if c.name == name)
+    print(f"[case] sinkhorn backward {name}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    gpu = run_forward(cfg, inp, C_lib, routing="sinkhorn", sinkhorn_iters=iters)
+    dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=DEV, dtype=cfg.dtype)
+    c = lib_cfg(cfg, C_lib, "sinkhorn", sinkhorn_iters=iters)
+    g = _backward_with_cfg(cfg, c, inp, gpu, dy)
+    x, wr, w1, w3, w2, lb, shared = oracle_weights(cfg, inp)
+    ref = oracle.moe_backward(x, wr, w1, w3, w2, np32(dy), k=cfg.k, gate=cfg.gate, C=C_ref,
+                              logit_bias=lb, shared=shared, idx=gpu["topk_idx"].cpu().numpy())
+    _check_grads(cfg, g, ref, f"sinkhorn_backward_{name}")
+
+
+def test_sinkhorn_full_size_skewed_routing():
+    """Sinkhorn routing on the skewed workload's full router (T=16384, E=64,
+    k=4, 256 blocks of 64 tokens): bias, selection and maps as above, and the
+    load evened out."""
+    cfg = CONFIGS["skewed"]
+    print("[case] sinkhorn full skewed", flush=True)
+    torch.cuda.empty_cache()
+    inp, gpu, ref, db, rep = _sinkhorn_case(cfg, 10, 0, None)
+    counts = gpu["expert_counts"].cpu().numpy()
+    _report("sinkhorn_full_skewed", bias_err=f"{db:.1e}",
+            max_over_mean=f"{counts.max() / counts.mean():.2f}", **rep)
+    assert db <= SK_BIAS_TOL
+    assert counts.max() < 1.25 * counts.mean()
+    del gpu, inp
+    torch.cuda.empty_cache()
 
 
 BALANCE = ["worked_example_small", "sigmoid_bias_shared", "zipf_dropless", "e256_k8_shared",
