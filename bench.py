@@ -151,8 +151,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="worked_example")
     ap.add_argument("--routing", default="topk",
-                    choices=("topk", "topk_score_drop", "expert_choice"),
+                    choices=("topk", "topk_score_drop", "expert_choice", "sinkhorn"),
                     help="routing variant (the headline workload uses topk)")
+    ap.add_argument("--sinkhorn-iters", type=int, default=10,
+                    help="Sinkhorn iterations (--routing sinkhorn, and the Sinkhorn leg "
+                         "of a topk run; 0 skips that leg)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--cpu-sample", type=int, default=1024)
@@ -179,14 +182,17 @@ def main() -> int:
     torch.cuda.set_device(0)
     inp = make_inputs(cfg, device=dev)
     C = moe.moe_capacity(cfg.T, cfg.E, cfg.k, *cfg.cf) if cfg.cf else 0
-    if args.routing != "topk" and C == 0:
+    if args.routing not in ("topk", "sinkhorn") and C == 0:
         print(f"--routing {args.routing} needs a workload with a capacity", file=sys.stderr)
         return 2
     if args.routing == "expert_choice":
         C = min(C, cfg.T)
         inp["select_bias"] = None      # expert choice ranks by probability only
+    sk_iters = args.sinkhorn_iters if args.routing == "sinkhorn" else 0
+    if args.routing == "sinkhorn":
+        inp["select_bias"] = None      # the balancing finds its own selection bias
     c = moe.make_cfg(cfg.T, cfg.h, cfg.F, cfg.E, cfg.k, cfg.dtype, cfg.gate, capacity=C,
-                     has_shared=cfg.shared, routing=args.routing)
+                     has_shared=cfg.shared, routing=args.routing, sinkhorn_iters=sk_iters)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     esz = 2 if cfg.dtype == "bf16" else 4
     rows = moe.moe_num_rows(c)
@@ -345,7 +351,8 @@ def main() -> int:
         # (save_for_backward): the forward's cost with the flag, then the
         # saved backward
         cs = moe.make_cfg(cfg.T, cfg.h, cfg.F, cfg.E, cfg.k, cfg.dtype, cfg.gate, capacity=C,
-                          has_shared=cfg.shared, routing=args.routing, save_for_backward=True)
+                          has_shared=cfg.shared, routing=args.routing, save_for_backward=True,
+                          sinkhorn_iters=sk_iters)
         wsf = torch.empty(moe.moe_workspace_bytes(cs), dtype=torch.uint8, device=dev)
         for _ in range(2):
             moe.moe_forward(cs, weights, inp["x"], y, full_route, wsf)
@@ -364,6 +371,36 @@ def main() -> int:
         fwd_save_ms = sv_ev[0].elapsed_time(sv_ev[1]) / nb
         bwd_saved_ms = sv_ev[2].elapsed_time(sv_ev[3]) / nb
         del wsb, grads, wsf
+
+    # Sinkhorn routing on the same workload (not part of the step): the
+    # balancing runs inside the top-k stage; the per-expert load it gives
+    # against the plain top-k's
+    sk = None
+    if args.routing == "topk" and inp["select_bias"] is None and args.sinkhorn_iters > 0:
+        csk = moe.make_cfg(cfg.T, cfg.h, cfg.F, cfg.E, cfg.k, cfg.dtype, cfg.gate, capacity=C,
+                           has_shared=cfg.shared, routing="sinkhorn",
+                           sinkhorn_iters=args.sinkhorn_iters)
+        wsk = torch.empty(moe.moe_workspace_bytes(csk), dtype=torch.uint8, device=dev)
+        sk_counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            moe.moe_forward(csk, weights, inp["x"], y, {"expert_counts": sk_counts}, wsk)
+        nsk = max(3, K // 4)
+        skev = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_EVENTS)]
+                for _ in range(nsk)]
+        for es in skev:
+            for e in es:
+                e.record()
+        torch.cuda.synchronize()
+        for i in range(nsk):
+            moe.moe_forward(csk, weights, inp["x"], y, {"expert_counts": sk_counts}, wsk,
+                            events=skev[i])
+        torch.cuda.synchronize()
+        skc = sk_counts.cpu().tolist()
+        sk = {"iters": args.sinkhorn_iters,
+              "ms_per_step": round(sum(es[0].elapsed_time(es[-1]) for es in skev) / nsk, 4),
+              "topk_stage_ms": round(sum(es[1].elapsed_time(es[2]) for es in skev) / nsk, 5),
+              "max_over_mean_load": round(max(skc) * cfg.E / sum(skc), 3)}
+        del wsk
 
     stage_ms = {}
     for s, name in enumerate(moe.STAGE_NAMES):
@@ -435,7 +472,9 @@ def main() -> int:
             "saved_frac_of_peak": round(12 * kept_all * cfg.h * cfg.F / (bwd_saved_ms * 1e-3)
                                         / 1e12 / peak, 4)}),
         "cold_cache": cold,
+        "sinkhorn": sk,
         "load_balance": {"us": round(lb_us, 2),
+                         "max_over_mean_load": round(max(cnt) * cfg.E / sum(cnt), 3),
                          "gbs": round(cfg.T * cfg.E * 4 / (lb_us * 1e-6) / 1e9, 1),
                          "aux_loss": round(float(lb_loss.item()), 6)},
     }
