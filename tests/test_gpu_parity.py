@@ -696,6 +696,49 @@ def test_errors_are_reported_before_launch():
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
 
 
+# ------------------------------------------------------------ maximum sizes
+def test_beyond_int32_element_counts():
+    """x [2^19 + 77, 4096] bf16 holds more than 2^31 elements and the
+    dispatch buffers x_perm and y_perm more than 2^32 (rows of 4096 + 64),
+    so a 32-bit index or byte offset anywhere on the path would show: the
+    routing on the GPU's own keys, gates and maps compared for every token,
+    logits and outputs of sampled tokens (the first and last among them)
+    against the oracle."""
+    cfg = MoEConfig("beyond_int32", T=(1 << 19) + 77, h=4096, E=8, k=2, F=128,
+                    gate="softmax_topk")
+    print(f"[case] beyond int32 T={cfg.T} h={cfg.h}", flush=True)
+    torch.cuda.empty_cache()
+    inp = gen_inputs(cfg)
+    assert inp["x"].numel() > 2 ** 31
+    gpu = run_forward(cfg, inp, 0)
+    assert gpu["rows"] * (cfg.h + 64) > 2 ** 32
+    g_logits = gpu["logits"].cpu().numpy()
+    g_idx = gpu["topk_idx"].cpu().numpy()
+    np.testing.assert_array_equal(oracle.topk(g_logits, cfg.k), g_idx)
+    dg = float(np.abs(gpu["topk_gate"].cpu().numpy() - oracle.gates(g_logits, g_idx, cfg.gate)).max())
+    assert dg <= 2e-6
+    m = oracle.route_maps(g_idx, cfg.E)
+    np.testing.assert_array_equal(gpu["expert_counts"].cpu().numpy(), m["counts"])
+    np.testing.assert_array_equal(gpu["expert_offsets"].cpu().numpy(), m["offsets"])
+    np.testing.assert_array_equal(gpu["assign_row"].cpu().numpy().reshape(-1, cfg.k),
+                                  m["assign_row"])
+    np.testing.assert_array_equal(gpu["row_token"].cpu().numpy(), m["row_token"])
+    rng = np.random.default_rng(7)
+    tok = np.array(sorted(set(rng.choice(cfg.T, 24, replace=False).tolist()) | {0, cfg.T - 1}))
+    tt = torch.as_tensor(tok, device=DEV)
+    ref = oracle.moe_forward(np32(inp["x"][tt]), np32(inp["w_router"]), LazyExperts(inp["w1"]),
+                             LazyExperts(inp["w3"]), LazyExperts(inp["w2"]), k=cfg.k,
+                             gate=cfg.gate, idx=g_idx[tok])
+    dl = float(np.abs(ref["logits"] - g_logits[tok]).max())
+    assert dl <= 5e-5 * max(1.0, float(np.abs(ref["logits"]).max()))
+    err = rel_err(np32(gpu["y"][tt]), ref["y"])
+    _report("beyond_int32", rel_err=f"{err:.2e}", max_dlogit=dl, max_dgate=dg,
+            rows=gpu["rows"], sampled=len(tok))
+    assert err <= 2e-2
+    del gpu, inp
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------ full sizes
 FULL = ["worked_example", "mixtral", "deepseek_v3", "skewed", "skewed_cf1"]
 
