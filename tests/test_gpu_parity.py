@@ -512,6 +512,95 @@ def test_sinkhorn_full_size_skewed_routing():
     torch.cuda.empty_cache()
 
 
+def _random_variant_cases(n=12, seed=4096):
+    """Seeded (layer, routing, Sinkhorn iterations) draws for the three
+    routing variants: score drop, expert choice and Sinkhorn."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        routing = ("topk_score_drop", "expert_choice", "sinkhorn")[i % 3]
+        E = int(rng.choice([2, 3, 5, 8, 13, 16, 24, 40, 64, 100]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        gate = str(rng.choice(["softmax_topk", "softmax_all_topk", "sigmoid_topk_norm"]))
+        cf = [(1, 2), (1, 1), (5, 4)][int(rng.integers(0, 3))]
+        if routing == "sinkhorn" and rng.random() < 0.5:
+            cf = None
+        cfg = MoEConfig(
+            f"rv{i}_{routing}", T=int(rng.integers(2, 500)), h=int(rng.choice([128, 256, 384])),
+            E=E, k=k, F=int(rng.choice([128, 256])),
+            dtype="f32" if rng.random() < 0.25 else "bf16", gate=gate, cf=cf,
+            shared=bool(rng.random() < 0.3),
+            logit_bias=("normal", 0.5) if rng.random() < 0.4 else None,
+            select_bias=("normal", 0.1) if routing == "topk_score_drop" and rng.random() < 0.5
+            else None,
+            seed=int(rng.integers(0, 1000)))
+        out.append((cfg, routing, int(rng.integers(1, 25)) if routing == "sinkhorn" else 0))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_variant_cases(), ids=lambda c: c[0].name)
+def test_random_routing_variants_forward_and_backward(case):
+    """Seeded random layers under each routing variant: routing checked as
+    in the variant's own test, the output and every gradient against the
+    oracle with that routing held fixed."""
+    cfg, routing, iters = case
+    print(f"[case] random variant {cfg} iters={iters}", flush=True)
+    inp = gen_inputs(cfg)
+    C_lib, C_ref = capacity_of(cfg)
+    T, E = cfg.T, cfg.E
+    if routing == "expert_choice":
+        C_lib, C_ref = min(C_lib, T), min(C_ref, T)
+    gpu = run_forward(cfg, inp, C_lib, routing=routing, sinkhorn_iters=iters)
+    x, wr, w1, w3, w2, lb, shared = oracle_weights(cfg, inp)
+    dy = normal((T, cfg.h), 1.0, cfg.seed, "dy", device=DEV, dtype=cfg.dtype)
+    c = lib_cfg(cfg, C_lib, routing, sinkhorn_iters=iters)
+    g = _backward_with_cfg(cfg, c, inp, gpu, dy, routing)
+    if routing == "expert_choice":
+        scores = gpu["probs"].cpu().numpy().T
+        m = oracle.expert_choice(gpu["logits"].cpu().numpy(), C_ref, cfg.gate, scores=scores)
+        np.testing.assert_array_equal(gpu["assign_row"].cpu().numpy().reshape(T, E), m["sel_row"])
+        np.testing.assert_array_equal(gpu["row_token"].cpu().numpy(), m["row_token"])
+        ref_y = oracle.expert_choice_forward(x, wr, w1, w3, w2, C=C_ref, gate=cfg.gate,
+                                             logit_bias=lb, shared=shared, scores=scores)["y"]
+        refb = oracle.expert_choice_backward(x, wr, w1, w3, w2, np32(dy), C=C_ref, gate=cfg.gate,
+                                             logit_bias=lb, shared=shared, scores=scores)
+        rep = {}
+    else:
+        g_idx = gpu["topk_idx"].cpu().numpy()
+        sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
+        if routing == "sinkhorn":
+            ref = oracle_forward(cfg, inp, C_ref, maps_only=True, sinkhorn_iters=iters)
+            rep = check_routing(cfg, gpu, ref, C_ref, inp, tie=SK_TIE)
+            kw = {}
+        else:
+            g_gate = gpu["topk_gate"].cpu().numpy()
+            ref = oracle_forward(cfg, inp, C_ref, idx=g_idx, drop="score", priority=g_gate,
+                                 maps_only=True)
+            rep = check_routing(cfg, gpu, ref, C_ref, inp, drop="score")
+            kw = {"drop": "score", "priority": g_gate}
+        ref_y = oracle_forward(cfg, inp, C_ref, idx=g_idx, **kw)["y"]
+        refb = oracle.moe_backward(x, wr, w1, w3, w2, np32(dy), k=cfg.k, gate=cfg.gate,
+                                   C=C_ref, logit_bias=lb, select_bias=sb, shared=shared,
+                                   idx=g_idx, **kw)
+    y = np32(gpu["y"])
+    assert np.isfinite(y).all()
+    err = rel_err(y, ref_y) if np.abs(ref_y).max() > 0 else float(np.abs(y).max())
+    if lb is None:
+        g.pop("dlogit_bias", None)
+        refb.pop("dlogit_bias", None)
+    errs = {}
+    for n in ("dx", "dw1", "dw3", "dw2", "dw_router", "dlogit_bias", "dgate", "dws1", "dws3",
+              "dws2"):
+        if n in g and n in refb:
+            r = refb[n]
+            errs[n] = (float(np.abs(np32(g[n])).max()) if np.abs(r).max() == 0
+                       else rel_err(np32(g[n]), r))
+    _report(cfg.name, fwd=f"{err:.2e}", **{n: f"{v:.2e}" for n, v in errs.items()}, **rep)
+    assert err <= tol_of(cfg), err
+    for n, v in errs.items():
+        assert v <= tol_of(cfg), (n, v)
+
+
 BALANCE = ["worked_example_small", "sigmoid_bias_shared", "zipf_dropless", "e256_k8_shared",
            "e1024_k16", "one_token", "e40_ragged", "k_equals_e", "f32_capacity"]
 
