@@ -217,23 +217,27 @@ def test_expert_choice_backward_saved_matches_oracle(name):
     _check_grads(cfg, g, ref, f"expert_choice_saved_backward_{name}")
 
 
-@pytest.mark.parametrize("name", ["sigmoid_bias_shared", "mixtral_bias", "tiny_fp32"])
-def test_autograd_layer_matches_oracle(name):
-    """The torch.autograd wrapper: its output is moe_forward's bit for bit,
-    and the leaves' gradients of sum(y * dy) meet the oracle's bound."""
+@pytest.mark.parametrize("name,routing,iters", [
+    ("sigmoid_bias_shared", "topk", 0), ("mixtral_bias", "topk", 0), ("tiny_fp32", "topk", 0),
+    ("mixtral_bias", "sinkhorn", 6), ("capacity_heavy_drop", "topk_score_drop", 0),
+    ("ec_sigmoid_shared", "expert_choice", 0)])
+def test_autograd_layer_matches_oracle(name, routing, iters):
+    """The torch.autograd wrapper under each routing: its output is
+    moe_forward's bit for bit, and the leaves' gradients of sum(y * dy) meet
+    the oracle's bound (the routing held fixed as the forward chose it)."""
     from mixture_experts_layer_25_amd.autograd import moe_layer
-    cfg = next(c for c in MEDIUM if c.name == name)
-    print(f"[case] autograd layer {name}", flush=True)
+    cfg = next(c for c in MEDIUM + EXPERT_CHOICE if c.name == name)
+    print(f"[case] autograd layer {name} {routing}", flush=True)
     inp = gen_inputs(cfg)
     C_lib, C_ref = capacity_of(cfg)
-    gpu = run_forward(cfg, inp, C_lib)
+    gpu = run_forward(cfg, inp, C_lib, routing=routing, sinkhorn_iters=iters)
     leaf = {n: inp[n].clone().requires_grad_(True) for n in ("x", "w_router", "w1", "w3", "w2")}
     lb = None if inp["logit_bias"] is None else inp["logit_bias"].clone().requires_grad_(True)
     sh = (tuple(inp[n].clone().requires_grad_(True) for n in ("ws1", "ws3", "ws2"))
           if cfg.shared else None)
     y = moe_layer(leaf["x"], leaf["w_router"], leaf["w1"], leaf["w3"], leaf["w2"], k=cfg.k,
-                  gate=cfg.gate, capacity=C_lib, logit_bias=lb, select_bias=inp["select_bias"],
-                  shared=sh)
+                  gate=cfg.gate, capacity=C_lib, routing=routing, sinkhorn_iters=iters,
+                  logit_bias=lb, select_bias=inp["select_bias"], shared=sh)
     y0, y1 = gpu["y"], y.detach()
     if y0.dtype == torch.bfloat16:
         y0, y1 = y0.view(torch.int16), y1.view(torch.int16)
@@ -243,9 +247,16 @@ def test_autograd_layer_matches_oracle(name):
     torch.cuda.synchronize()
     x, wr, w1, w3, w2, lbn, shared = oracle_weights(cfg, inp)
     sb = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
-    ref = oracle.moe_backward(x, wr, w1, w3, w2, np32(dy), k=cfg.k, gate=cfg.gate, C=C_ref,
-                              logit_bias=lbn, select_bias=sb, shared=shared,
-                              idx=gpu["topk_idx"].cpu().numpy())
+    if routing == "expert_choice":
+        ref = oracle.expert_choice_backward(x, wr, w1, w3, w2, np32(dy), C=C_ref, gate=cfg.gate,
+                                            logit_bias=lbn, shared=shared,
+                                            scores=gpu["probs"].cpu().numpy().T)
+    else:
+        kw = ({"drop": "score", "priority": gpu["topk_gate"].cpu().numpy()}
+              if routing == "topk_score_drop" else {})
+        ref = oracle.moe_backward(x, wr, w1, w3, w2, np32(dy), k=cfg.k, gate=cfg.gate, C=C_ref,
+                                  logit_bias=lbn, select_bias=sb, shared=shared,
+                                  idx=gpu["topk_idx"].cpu().numpy(), **kw)
     got = {"dx": leaf["x"].grad, "dw_router": leaf["w_router"].grad, "dw1": leaf["w1"].grad,
            "dw3": leaf["w3"].grad, "dw2": leaf["w2"].grad}
     if lb is not None:
@@ -253,7 +264,7 @@ def test_autograd_layer_matches_oracle(name):
     if sh is not None:
         got.update({"dws1": sh[0].grad, "dws3": sh[1].grad, "dws2": sh[2].grad})
     errs = {n: rel_err(np32(t), ref[n]) for n, t in got.items()}
-    _report(f"autograd_{name}", **{n: f"{v:.2e}" for n, v in errs.items()})
+    _report(f"autograd_{name}_{routing}", **{n: f"{v:.2e}" for n, v in errs.items()})
     for n, v in errs.items():
         assert v <= tol_of(cfg), (n, v)
 
