@@ -693,17 +693,20 @@ def test_grouped_gemm_tile_heights(hF):
     _report(f"tile_heights_{h}", rel_err=f"{worst:.2e}")
 
 
-@pytest.mark.parametrize("name", STAGED)
-def test_stage_calls_equal_fused_call(name):
+@pytest.mark.parametrize("name,routing,iters",
+                         [(n, "topk", 0) for n in STAGED] +
+                         [("dropless_softmax", "sinkhorn", 4), ("capacity_heavy_drop", "sinkhorn", 7)])
+def test_stage_calls_equal_fused_call(name, routing, iters):
     """router_topk -> permute -> grouped_gemm_swiglu (+ the shared expert as
-    its own E=1 call) -> combine gives bit-for-bit the fused layer's output;
-    x_perm holds exact copies of token rows and zero padding rows."""
+    its own E=1 call) -> combine gives bit-for-bit the fused layer's output
+    (top-k or Sinkhorn routing); x_perm holds exact copies of token rows and
+    zero padding rows."""
     cfg = next(c for c in MEDIUM if c.name == name)
-    print(f"[case] staged {name}", flush=True)
+    print(f"[case] staged {name} {routing}", flush=True)
     inp = gen_inputs(cfg)
     C_lib, _ = capacity_of(cfg)
-    fused = run_forward(cfg, inp, C_lib)
-    c = lib_cfg(cfg, C_lib)
+    fused = run_forward(cfg, inp, C_lib, routing=routing, sinkhorn_iters=iters)
+    c = lib_cfg(cfg, C_lib, routing, sinkhorn_iters=iters)
     T, E, k, h, F = cfg.T, cfg.E, cfg.k, cfg.h, cfg.F
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     rows = moe.moe_num_rows(c)
