@@ -215,18 +215,26 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # `value`: K steps with no instrumentation, host clock between two
+    # synchronisations.  The per-stage times come from K more steps that
+    # record an event between every two kernels (their small launch gaps are
+    # in those stage times, not in `value`).
     K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        moe.moe_forward(c, weights, inp["x"], y, route, ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_EVENTS)]
            for _ in range(K)]
     for es in evs:             # create the events outside the timed region
         for e in es:
             e.record()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(K):
         moe.moe_forward(c, weights, inp["x"], y, route, ws, events=evs[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
 
     # On-box HBM yardstick: a plain 1 GiB device-to-device copy (torch),
     # best of 5, read + write bytes over its event time.  Skipped in the
