@@ -36,6 +36,9 @@
  *             exception crosses the ABI.
  *   Threads   Stateless: concurrent calls are safe on different streams
  *             with different workspaces and outputs.
+ *   Graphs    No call allocates, sets memory or synchronises, so a call can
+ *             be captured in a HIP graph; each replay recomputes from the
+ *             buffers' contents at replay time.
  *   Shapes    h % 128 == 0, F % 128 == 0, 1 <= k <= min(E, 16), E <= 1024,
  *             T >= 0 (T == 0 enqueues nothing and reads no pointer).  Otherwise
  *             MOE_ERR_UNSUPPORTED.

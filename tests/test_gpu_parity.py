@@ -772,6 +772,82 @@ def test_deterministic():
     assert torch.equal(a["y"].view(torch.int16), b["y"].view(torch.int16))
 
 
+def _layer_buffers(cfg, C, routing="topk"):
+    """Library cfg, workspace, output and routing buffers of one layer."""
+    c = lib_cfg(cfg, C, routing)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    ws = torch.empty(max(moe.moe_workspace_bytes(c), 1), dtype=torch.uint8, device=DEV)
+    y = torch.empty((cfg.T, cfg.h), dtype=tdt, device=DEV)
+    route = {"topk_idx": torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV),
+             "assign_row": torch.empty((cfg.T * cfg.k,), dtype=torch.int32, device=DEV)}
+    return c, ws, y, route
+
+
+def _weights(inp):
+    return {n: inp[n] for n in ("w_router", "w1", "w3", "w2", "logit_bias", "select_bias",
+                                "ws1", "ws3", "ws2")}
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two layers enqueued alternately on two streams (each with its own
+    workspace and outputs), several times over: every output equals the
+    same layer run alone, bit for bit (the library keeps no state)."""
+    cfgs = [next(c for c in MEDIUM if c.name == n)
+            for n in ("worked_example_small", "split_k_tail_capacity_shared")]
+    inps = [gen_inputs(c) for c in cfgs]
+    Cs = [capacity_of(c)[0] for c in cfgs]
+    refs = [run_forward(c, i, C) for c, i, C in zip(cfgs, inps, Cs)]
+    bufs = [_layer_buffers(c, C) for c, C in zip(cfgs, Cs)]
+    streams = [torch.cuda.Stream() for _ in cfgs]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for inp, (c, ws, y, route), st in zip(inps, bufs, streams):
+            with torch.cuda.stream(st):
+                moe.moe_forward(c, _weights(inp), inp["x"], y, route, ws)
+    torch.cuda.synchronize()
+    for ref, (c, ws, y, route) in zip(refs, bufs):
+        assert torch.equal(route["topk_idx"], ref["topk_idx"])
+        assert torch.equal(route["assign_row"], ref["assign_row"])
+        assert torch.equal(y.view(torch.int16), ref["y"].view(torch.int16))
+
+
+def test_forward_captured_in_a_graph():
+    """moe_forward captured once in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed with eager work and synchronisations in between, also after new
+    token values are copied into the captured input: every replay equals an
+    eager forward on the same values, bit for bit."""
+    cfg = next(c for c in MEDIUM if c.name == "worked_example_small")
+    inp = gen_inputs(cfg)
+    C, _ = capacity_of(cfg)
+    ref0 = run_forward(cfg, inp, C)
+    x1 = normal((cfg.T, cfg.h), 1.0, cfg.seed + 1, "x", device=DEV, dtype=cfg.dtype)
+    ref1 = run_forward(cfg, dict(inp, x=x1), C)
+    c, ws, y, route = _layer_buffers(cfg, C)
+    x = inp["x"].clone()
+    w = _weights(inp)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_forward(c, w, x, y, route, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_forward(c, w, x, y, route, ws)
+    torch.cuda.synchronize()
+    for rep, (xv, ref) in enumerate([(inp["x"], ref0), (x1, ref1), (inp["x"], ref0),
+                                     (x1, ref1)]):
+        x.copy_(xv)
+        y.fill_(float("nan"))
+        route["topk_idx"].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(route["topk_idx"], ref["topk_idx"]), rep
+        assert torch.equal(y.view(torch.int16), ref["y"].view(torch.int16)), rep
+        run_forward(cfg, inp, C)          # eager work between the replays
+
+
 def test_empty_input_is_a_no_op():
     cfg = MoEConfig("empty", T=0, h=128, E=4, k=2, F=128)
     c = lib_cfg(cfg, 0)
