@@ -421,29 +421,52 @@ __device__ __forceinline__ void tile_body(const GroupedGemmArgs& a, const Tile& 
       rsB, LDS_AS(dstB + ((KT) & 1) * kPart + (I) * 1024), 16, voffB[I],                      \
       (KT) < nsteps ? (uint32_t)(I) * 8u * browbytes + KOFF(KT) : KOFF(KT), 0, 0)
 // One sub-step: groups of [copy] [fragment reads for the next sub-step]
-// [2 MFMAs]; 4*FI MFMAs and FI + 4 reads per sub-step.
-#define SUBSTEP(FA, FB, RFA, RFB, SA, SBP, S, COPY)                                        \
-  if constexpr (FI == 4) {                                                                 \
-    COPY(0); RDA(RFA, SA, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                   \
-    COPY(1); RDA(RFA, SA, S, 1); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                   \
-    COPY(2); RDA(RFA, SA, S, 2); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB();                   \
-    COPY(3); RDA(RFA, SA, S, 3); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                   \
-    COPY(4); RDB(RFB, SBP, S, 0); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();                  \
-    COPY(5); RDB(RFB, SBP, S, 1); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                  \
-    COPY(6); RDB(RFB, SBP, S, 2); MF(FA, FB, 3, 0); MF(FA, FB, 3, 1); SB();                  \
-    COPY(7); RDB(RFB, SBP, S, 3); MF(FA, FB, 3, 2); MF(FA, FB, 3, 3); SB();                  \
+// [2 MFMAs]; 4*FI MFMAs and FI + 4 reads per sub-step.  MFMA pair p of a
+// sub-step uses A fragment p/2 (FI = 4) and every B fragment within the
+// first two pairs, so the reads go B-first: each fragment is read at least
+// five pairs (four for FI <= 2) before the pair that uses it.  EARLY (the
+// sub-step before the slice barrier, whose wait covers every read) puts all
+// reads in the first half, so they have landed when the wait comes.
+#define SUBSTEP(FA, FB, RFA, RFB, SA, SBP, S, COPY, EARLY)                                 \
+  if constexpr (FI == 4 && !(EARLY)) {                                                     \
+    COPY(0); RDB(RFB, SBP, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                  \
+    COPY(1); RDB(RFB, SBP, S, 1); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                  \
+    COPY(2); RDA(RFA, SA, S, 0); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB();                   \
+    COPY(3); RDB(RFB, SBP, S, 2); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                  \
+    COPY(4); RDB(RFB, SBP, S, 3); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();                  \
+    COPY(5); RDA(RFA, SA, S, 1); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                   \
+    COPY(6); RDA(RFA, SA, S, 2); MF(FA, FB, 3, 0); MF(FA, FB, 3, 1); SB();                   \
+    COPY(7); RDA(RFA, SA, S, 3); MF(FA, FB, 3, 2); MF(FA, FB, 3, 3); SB();                   \
+  } else if constexpr (FI == 4) {                                                          \
+    COPY(0); RDB(RFB, SBP, S, 0); RDB(RFB, SBP, S, 1); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB(); \
+    COPY(1); RDA(RFA, SA, S, 0); RDB(RFB, SBP, S, 2); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB(); \
+    COPY(2); RDB(RFB, SBP, S, 3); RDA(RFA, SA, S, 1); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB(); \
+    COPY(3); RDA(RFA, SA, S, 2); RDA(RFA, SA, S, 3); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB(); \
+    COPY(4); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();                                     \
+    COPY(5); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                                     \
+    COPY(6); MF(FA, FB, 3, 0); MF(FA, FB, 3, 1); SB();                                     \
+    COPY(7); MF(FA, FB, 3, 2); MF(FA, FB, 3, 3); SB();                                     \
+  } else if constexpr (FI == 3 && !(EARLY)) {                                              \
+    COPY(0); RDB(RFB, SBP, S, 0); RDB(RFB, SBP, S, 1); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB(); \
+    COPY(1); RDA(RFA, SA, S, 0); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                   \
+    COPY(2); RDB(RFB, SBP, S, 2); RDB(RFB, SBP, S, 3); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB(); \
+    COPY(3); RDA(RFA, SA, S, 1); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                   \
+    COPY(4); RDA(RFA, SA, S, 2); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();                   \
+    COPY(5); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                                     \
   } else if constexpr (FI == 3) {                                                          \
-    COPY(0); RDA(RFA, SA, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                   \
-    COPY(1); RDA(RFA, SA, S, 1); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                   \
-    COPY(2); RDA(RFA, SA, S, 2); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB();                   \
-    COPY(3); RDB(RFB, SBP, S, 0); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                  \
-    COPY(4); RDB(RFB, SBP, S, 1); RDB(RFB, SBP, S, 2); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB(); \
-    COPY(5); RDB(RFB, SBP, S, 3); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                  \
+    COPY(0); RDB(RFB, SBP, S, 0); RDB(RFB, SBP, S, 1); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB(); \
+    COPY(1); RDA(RFA, SA, S, 0); RDB(RFB, SBP, S, 2); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB(); \
+    COPY(2); RDB(RFB, SBP, S, 3); RDA(RFA, SA, S, 1); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB(); \
+    COPY(3); RDA(RFA, SA, S, 2); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                   \
+    COPY(4); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();                                     \
+    COPY(5); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                                     \
   } else if constexpr (FI == 2) {                                                          \
-    COPY(0); RDA(RFA, SA, S, 0); RDB(RFB, SBP, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB(); \
-    COPY(1); RDA(RFA, SA, S, 1); RDB(RFB, SBP, S, 1); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB(); \
-    COPY(2); RDB(RFB, SBP, S, 2); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB();                  \
-    COPY(3); RDB(RFB, SBP, S, 3); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                  \
+    COPY(0); RDB(RFB, SBP, S, 0); RDB(RFB, SBP, S, 1); RDA(RFA, SA, S, 0);                   \
+    MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                                              \
+    COPY(1); RDB(RFB, SBP, S, 2); RDB(RFB, SBP, S, 3); if constexpr (EARLY) RDA(RFA, SA, S, 1); \
+    MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                                              \
+    COPY(2); if constexpr (!(EARLY)) RDA(RFA, SA, S, 1); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB(); \
+    COPY(3); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                                     \
   } else {                                                                                 \
     COPY(0); RDA(RFA, SA, S, 0); RDB(RFB, SBP, S, 0); RDB(RFB, SBP, S, 1);                   \
     MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                                              \
@@ -544,11 +567,11 @@ __device__ __forceinline__ void tile_body(const GroupedGemmArgs& a, const Tile& 
     _Pragma("unroll") for (int u = 0; u < 8 / (2 * FI); ++u)                       \
         DMA_B(kt + 2, (I) * (8 / (2 * FI)) + u);                                   \
   }
-    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 1, COPY_A1);
-    SUBSTEP(fa1, fb1, fa0, fb0, sa, sbb, 2, COPY_A2);
-    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 3, COPY_A3);
+    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 1, COPY_A1, false);
+    SUBSTEP(fa1, fb1, fa0, fb0, sa, sbb, 2, COPY_A2, false);
+    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 3, COPY_A3, true);
     WG_BARRIER(kWaitLoop);
-    SUBSTEP(fa1, fb1, fa0, fb0, na, nbb, 0, COPY_B);
+    SUBSTEP(fa1, fb1, fa0, fb0, na, nbb, 0, COPY_B, true);
 #undef COPY_A1
 #undef COPY_A2
 #undef COPY_A3
