@@ -39,8 +39,10 @@
  *   Graphs    No call allocates, sets memory or synchronises, so a call can
  *             be captured in a HIP graph; each replay recomputes from the
  *             buffers' contents at replay time.
- *   Shapes    h % 128 == 0, F % 128 == 0, 1 <= k <= min(E, 16), E <= 1024,
- *             T >= 0 (T == 0 enqueues nothing and reads no pointer).  Otherwise
+ *   Shapes    h % 128 == 0, F % 128 == 0, h <= 65536, F <= 65536,
+ *             1 <= k <= min(E, 16), E <= 1024, T >= 0 (T == 0 enqueues
+ *             nothing and reads no pointer), dispatch rows (T*k, or E*C
+ *             with a capacity, + T with a shared expert) <= 2^30.  Otherwise
  *             MOE_ERR_UNSUPPORTED.
  *   Numerics  bf16 layers: bf16 inputs, fp32 accumulation, fp32 router
  *             logits and gates, bf16 round-to-nearest-even stores of the
@@ -332,7 +334,9 @@ int moe_load_balance(const moe_cfg_t* cfg, const float* logits,
  * distribution's Jacobian over all E (10.5 section 10.5.6).  Gradient sums
  * in fp32; dx, weight gradients and the intermediates (a1, a3, u, dO, dU,
  * dA, dx_perm) stored in the layer's dtype.  Every sum has a fixed order:
- * the same bits on every run.                                             */
+ * the same bits on every run.  Size limit: the dispatch rows plus 64 per
+ * group (E, + 1 with a shared expert), rounded up to 64, stay below 2^25;
+ * beyond it both calls return MOE_ERR_UNSUPPORTED.                        */
 int moe_backward_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes);
 int moe_backward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
                  const void* dy, const moe_route_out_t* route, const moe_grads_t* grads,

@@ -17,6 +17,12 @@ namespace {
 using moe::gtab_ints;
 
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
+// Widest h and F: the bf16 GEMM addresses a 64-row block of a ragged group
+// through a buffer descriptor with 32-bit extent and offsets.
+constexpr int kMaxWidth = 65536;
+// Backward: the weight-gradient GEMMs read K-major copies whose rows hold
+// every group's rows (padded to 64); 64 of those rows must span < 4 GiB.
+constexpr int64_t kMaxBwdKRows = (int64_t)1 << 25;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -61,6 +67,7 @@ int check_cfg(const moe_cfg_t* c) {
     return MOE_ERR_INVALID_ARG;
   if (c->k > c->E) return MOE_ERR_INVALID_ARG;
   if (c->h % 128 != 0 || c->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (c->h > kMaxWidth || c->F > kMaxWidth) return MOE_ERR_UNSUPPORTED;
   if (c->E > 1024 || c->k > 16 || c->E + c->has_shared > 1024) return MOE_ERR_UNSUPPORTED;
   if (c->T > kMaxRows || c->capacity > kMaxRows) return MOE_ERR_UNSUPPORTED;
   const int64_t rows_all = rows_of(*c) + (c->has_shared ? c->T : 0);
@@ -422,7 +429,13 @@ MOE_API int moe_backward_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes) {
   const int st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (!bytes) return MOE_ERR_INVALID_ARG;
-  *bytes = cfg->T == 0 ? 0 : bwd_layout_of(*cfg).total;
+  if (cfg->T == 0) {
+    *bytes = 0;
+    return MOE_OK;
+  }
+  const BwdLayout L = bwd_layout_of(*cfg);
+  if (L.ktb >= kMaxBwdKRows) return MOE_ERR_UNSUPPORTED;
+  *bytes = L.total;
   return MOE_OK;
 }
 
@@ -467,6 +480,7 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
       misaligned(gr.dgate))
     return MOE_ERR_INVALID_ARG;
   const BwdLayout L = bwd_layout_of(c);
+  if (L.ktb >= kMaxBwdKRows) return MOE_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   const hipStream_t s = (hipStream_t)stream;
   const int E = c.E, h = c.h, F = c.F;

@@ -115,6 +115,10 @@ def _cfg(**kw):
     (dict(k=0), moe.MOE_ERR_INVALID_ARG),
     (dict(h=100), moe.MOE_ERR_UNSUPPORTED),          # h % 128
     (dict(F=200), moe.MOE_ERR_UNSUPPORTED),          # F % 128
+    (dict(h=65536 + 128), moe.MOE_ERR_UNSUPPORTED),  # wider than the GEMM's 32-bit offsets
+    (dict(F=65536 + 128), moe.MOE_ERR_UNSUPPORTED),
+    (dict(h=65536, F=65536), moe.MOE_OK),
+    (dict(T=(1 << 29) + 1), moe.MOE_ERR_UNSUPPORTED),  # T*k dispatch rows > 2^30
     (dict(E=2000, k=2), moe.MOE_ERR_UNSUPPORTED),    # E > 1024
     (dict(E=32, k=17), moe.MOE_ERR_UNSUPPORTED),     # k > 16
     (dict(dtype=5), moe.MOE_ERR_INVALID_ARG),
@@ -124,6 +128,20 @@ def _cfg(**kw):
 ])
 def test_validation_codes(kw, status):
     assert _raw_status(_cfg(**kw)) == status
+
+
+def test_backward_row_limit():
+    """The backward's K-major copies hold every group's rows padded to 64;
+    64 such rows must span less than 4 GiB of bf16 (the GEMM's 32-bit buffer
+    extent), so rows + 64 per group, rounded up to 64, stay below 2^25."""
+    E, k = 8, 2
+    t_max = ((1 << 25) - 64 - 64 * E) // k          # largest T inside the limit
+    assert moe.moe_backward_workspace_bytes(_cfg(T=t_max, E=E, k=k)) > 0
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_backward_workspace_bytes(_cfg(T=t_max + 32, E=E, k=k))
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    # the forward has no such limit at that size
+    assert moe.moe_workspace_bytes(_cfg(T=t_max + 32, E=E, k=k)) > 0
 
 
 def test_validation_of_struct_and_pointers():
