@@ -16,7 +16,13 @@ namespace {
 
 using moe::gtab_ints;
 
-constexpr int64_t kMaxRows = (int64_t)1 << 30;
+// Sizes are bounded so that every launch's grid stays below 2^32 work-items
+// (the dispatch packet's grid size is 32-bit): some launches run one
+// 256-thread workgroup per token, the permute and gather launches 128
+// work-items per dispatch row; the grouped GEMMs are checked in grids_fit.
+constexpr int64_t kMaxTokens = ((int64_t)1 << 24) - 1;
+constexpr int64_t kMaxRows = ((int64_t)1 << 25) - 1;
+constexpr uint64_t kMaxWorkItems = 0xFFFFFFFFull;
 // Widest h and F: the bf16 GEMM addresses a 64-row block of a ragged group
 // through a buffer descriptor with 32-bit extent and offsets.
 constexpr int kMaxWidth = 65536;
@@ -46,6 +52,27 @@ int row_tile(const moe_cfg_t& c) {
   return c.dtype == MOE_DTYPE_BF16 ? moe::kGemmBM_bf16 : moe::kGemmBM_f32;
 }
 
+// Upper bounds on the work-items of the widest launches (grouped GEMMs,
+// the fp32 router: one thread per logit, and for the backward the SwiGLU passes and the
+// weight-gradient GEMMs) are below 2^32.  Column tiles are at least 128
+// (bf16) or 64 (fp32) wide; the widest GEMM output is max(2F, h).
+bool grids_fit(const moe_cfg_t& c, bool backward) {
+  const uint64_t T = (uint64_t)c.T, G = (uint64_t)c.E + (uint64_t)c.has_shared;
+  const uint64_t rows_all = (uint64_t)rows_of(c) + (c.has_shared ? T : 0);
+  const uint64_t BM = (uint64_t)row_tile(c);
+  const uint64_t ntile = c.dtype == MOE_DTYPE_BF16 ? 128 : 64;
+  const uint64_t wmax = std::max<uint64_t>(2 * (uint64_t)c.F, (uint64_t)c.h);
+  const uint64_t m_tiles = (rows_all + BM - 1) / BM + G + 1;
+  if ((m_tiles * (wmax / ntile) + 256) * 256 > kMaxWorkItems) return false;
+  if (c.dtype == MOE_DTYPE_F32 && T * (uint64_t)c.E > kMaxWorkItems) return false;  // fp32 router
+  if (backward) {
+    const uint64_t vec = c.dtype == MOE_DTYPE_BF16 ? 8 : 4;
+    if (rows_all * ((uint64_t)c.F / vec) + 256 > kMaxWorkItems) return false;
+    if (G * ((wmax + BM - 1) / BM) * (wmax / ntile) * 256 > kMaxWorkItems) return false;
+  }
+  return true;
+}
+
 int check_cfg(const moe_cfg_t* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->struct_size != (int32_t)sizeof(moe_cfg_t)) return MOE_ERR_INVALID_ARG;
@@ -69,9 +96,10 @@ int check_cfg(const moe_cfg_t* c) {
   if (c->h % 128 != 0 || c->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (c->h > kMaxWidth || c->F > kMaxWidth) return MOE_ERR_UNSUPPORTED;
   if (c->E > 1024 || c->k > 16 || c->E + c->has_shared > 1024) return MOE_ERR_UNSUPPORTED;
-  if (c->T > kMaxRows || c->capacity > kMaxRows) return MOE_ERR_UNSUPPORTED;
+  if (c->T > kMaxTokens || c->capacity > kMaxRows) return MOE_ERR_UNSUPPORTED;
   const int64_t rows_all = rows_of(*c) + (c->has_shared ? c->T : 0);
   if (rows_all > kMaxRows) return MOE_ERR_UNSUPPORTED;
+  if (!grids_fit(*c, false)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -434,7 +462,7 @@ MOE_API int moe_backward_workspace_bytes(const moe_cfg_t* cfg, size_t* bytes) {
     return MOE_OK;
   }
   const BwdLayout L = bwd_layout_of(*cfg);
-  if (L.ktb >= kMaxBwdKRows) return MOE_ERR_UNSUPPORTED;
+  if (L.ktb >= kMaxBwdKRows || !grids_fit(*cfg, true)) return MOE_ERR_UNSUPPORTED;
   *bytes = L.total;
   return MOE_OK;
 }
@@ -480,7 +508,7 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
       misaligned(gr.dgate))
     return MOE_ERR_INVALID_ARG;
   const BwdLayout L = bwd_layout_of(c);
-  if (L.ktb >= kMaxBwdKRows) return MOE_ERR_UNSUPPORTED;
+  if (L.ktb >= kMaxBwdKRows || !grids_fit(c, true)) return MOE_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   const hipStream_t s = (hipStream_t)stream;
   const int E = c.E, h = c.h, F = c.F;

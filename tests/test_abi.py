@@ -117,8 +117,7 @@ def _cfg(**kw):
     (dict(F=200), moe.MOE_ERR_UNSUPPORTED),          # F % 128
     (dict(h=65536 + 128), moe.MOE_ERR_UNSUPPORTED),  # wider than the GEMM's 32-bit offsets
     (dict(F=65536 + 128), moe.MOE_ERR_UNSUPPORTED),
-    (dict(h=65536, F=65536), moe.MOE_OK),
-    (dict(T=(1 << 29) + 1), moe.MOE_ERR_UNSUPPORTED),  # T*k dispatch rows > 2^30
+    (dict(T=1 << 24), moe.MOE_ERR_UNSUPPORTED),      # a 256-thread workgroup per token
     (dict(E=2000, k=2), moe.MOE_ERR_UNSUPPORTED),    # E > 1024
     (dict(E=32, k=17), moe.MOE_ERR_UNSUPPORTED),     # k > 16
     (dict(dtype=5), moe.MOE_ERR_INVALID_ARG),
@@ -128,6 +127,25 @@ def _cfg(**kw):
 ])
 def test_validation_codes(kw, status):
     assert _raw_status(_cfg(**kw)) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=65536, F=65536), moe.MOE_OK),
+    (dict(h=65536 + 128), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 24), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=(1 << 24) - 1), moe.MOE_OK),                          # 2^25 - 2 dispatch rows
+    (dict(T=(1 << 24) - 1, k=3), moe.MOE_ERR_UNSUPPORTED),        # rows > 2^25 - 1
+    (dict(T=1 << 20, k=8, F=65536), moe.MOE_ERR_UNSUPPORTED),     # GEMM grid >= 2^32 work-items
+    (dict(T=1 << 20, k=2, F=65536), moe.MOE_OK),
+    (dict(T=1 << 22, E=1024, k=1, dtype="f32"), moe.MOE_ERR_UNSUPPORTED),  # fp32 router T*E
+    (dict(T=1 << 22, E=1024, k=1), moe.MOE_OK),                   # the bf16 router has no T*E grid
+])
+def test_size_limits(kw, status):
+    """Every launch's grid stays below 2^32 work-items and the GEMM's 32-bit
+    buffer offsets cannot wrap: larger sizes are refused before any launch
+    (host-only call, no pointer is passed)."""
+    n = ctypes.c_size_t(0)
+    assert moe.lib().moe_workspace_bytes(ctypes.byref(_cfg(**kw)), ctypes.byref(n)) == status
 
 
 def test_backward_row_limit():
@@ -142,6 +160,12 @@ def test_backward_row_limit():
     assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
     # the forward has no such limit at that size
     assert moe.moe_workspace_bytes(_cfg(T=t_max + 32, E=E, k=k)) > 0
+    # the SwiGLU passes of the backward: rows * F / 8 work-items
+    big = _cfg(T=1 << 20, E=E, k=2, F=65536)
+    assert moe.moe_workspace_bytes(big) > 0
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_backward_workspace_bytes(big)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_validation_of_struct_and_pointers():
