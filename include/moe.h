@@ -34,6 +34,13 @@
  *             MOE_ERR_HIP reports a failed kernel launch.  Device faults
  *             surface at the caller's next synchronisation.  No C++
  *             exception crosses the ABI.
+ *   Maps      Index arrays a call reads on the device (topk_idx,
+ *             expert_counts, expert_offsets, assign_row) cannot be checked
+ *             on the host without a synchronisation.  The kernels ignore a
+ *             slot whose expert id is outside [0, E) or whose row is
+ *             outside [0, rows), and clamp groups to [0, rows): values
+ *             other than the ones the forward writes give unspecified
+ *             results, but no access outside the caller's buffers.
  *   Threads   Stateless: concurrent calls are safe on different streams
  *             with different workspaces and outputs.
  *   Graphs    No call allocates, sets memory or synchronises, so a call can

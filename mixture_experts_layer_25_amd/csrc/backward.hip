@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void scatter_dy_kernel(
         Elt<T>::unpack(q, f);
         for (int j = 0; j < k; ++j) {
           const int r = assign_row[t * k + j];
-          if (r < 0) continue;
+          if (r < 0 || r >= rows) continue;   // dropped (or outside the rows)
           const float g = gate[t * k + j];
           float o[V];
 #pragma unroll
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void scatter_dy_kernel(
   }
   const int64_t pb = b - ntb;
   for (int e = 0; e < E; ++e) {
-    const int64_t kept = min((int64_t)counts[e], C);
+    const int64_t kept = max(min((int64_t)counts[e], C), (int64_t)0);
     for (int64_t r = e * C + kept + pb; r < (e + 1) * C; r += 256) {
       for (int v = threadIdx.x; v < nv; v += 256) dO[r * pv + v] = uint4{0u, 0u, 0u, 0u};
     }
@@ -191,14 +191,15 @@ template <typename T>
 __global__ __launch_bounds__(256) void gate_grad_kernel(const uint4* __restrict__ dy,
                                                         const uint4* __restrict__ o, int64_t pv,
                                                         const int32_t* __restrict__ assign_row,
-                                                        int nv, int k, float* __restrict__ dg) {
+                                                        int64_t rows, int nv, int k,
+                                                        float* __restrict__ dg) {
   constexpr int V = Elt<T>::kVec;
   __shared__ float red[256];
   const int64_t t = blockIdx.x;
   for (int j = 0; j < k; ++j) {
     const int r = assign_row[t * k + j];
     float acc = 0.f;
-    if (r >= 0) {
+    if (r >= 0 && r < rows) {
       for (int v = threadIdx.x; v < nv; v += 256) {
         float fa[V], fb[V];
         Elt<T>::unpack(dy[t * nv + v], fa);
@@ -279,12 +280,16 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const float* __restrict_
   if (t >= T) return;
   const float* l = logits + t * E;
   float* d = dl + t * E;
+  // a slot whose expert id is outside [0, E) (a caller's map) is ignored
   auto ex = [&](int j) { return idx ? idx[t * k + j] : j; };
+  auto ok = [&](int j) { return (unsigned)ex(j) < (unsigned)E; };
   for (int e = 0; e < E; ++e) d[e] = 0.f;
   float gd = 0.f;                     // sum_j g_j dg_j
-  for (int j = 0; j < k; ++j) gd += gate[t * k + j] * dg[t * k + j];
+  for (int j = 0; j < k; ++j)
+    if (ok(j)) gd += gate[t * k + j] * dg[t * k + j];
   if (gate_mode == 0) {               // softmax over the selected
     for (int j = 0; j < k; ++j) {
+      if (!ok(j)) continue;
       const float g = gate[t * k + j];
       d[ex(j)] += g * (dg[t * k + j] - gd);
     }
@@ -295,13 +300,16 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const float* __restrict_
     for (int e = 0; e < E; ++e) den += expf(l[e] - m);
     for (int e = 0; e < E; ++e) d[e] = -(expf(l[e] - m) / den) * gd;
     for (int j = 0; j < k; ++j) {
+      if (!ok(j)) continue;
       const int e = ex(j);
       d[e] += (expf(l[e] - m) / den) * dg[t * k + j];
     }
   } else {                            // sigmoid normalised over the selected
     float S = 0.f;
-    for (int j = 0; j < k; ++j) S += 1.f / (1.f + expf(-l[ex(j)]));
+    for (int j = 0; j < k; ++j)
+      if (ok(j)) S += 1.f / (1.f + expf(-l[ex(j)]));
     for (int j = 0; j < k; ++j) {
+      if (!ok(j)) continue;
       const int e = ex(j);
       const float s = 1.f / (1.f + expf(-l[e]));
       d[e] += (dg[t * k + j] - gd) / S * s * (1.f - s);
@@ -420,7 +428,7 @@ __global__ __launch_bounds__(256) void dx_final_kernel(
     float acc = 0.f;
     for (int j = 0; j < k; ++j) {
       const int r = assign_row[t * k + j];
-      if (r >= 0) acc += Elt<T>::ld(dxp + (int64_t)r * ldp + i0 + ii);
+      if (r >= 0 && r < rows) acc += Elt<T>::ld(dxp + (int64_t)r * ldp + i0 + ii);
     }
     if (has_shared) acc += Elt<T>::ld(dxp + (rows + t) * ldp + i0 + ii);
     Elt<T>::st(dx + t * h + i0 + ii, acc + racc[m]);
@@ -489,11 +497,11 @@ hipError_t launch_scatter_dy(int dtype, const void* dy, const int32_t* assign_ro
 }
 
 hipError_t launch_gate_grad(int dtype, const void* dy, const void* o, int ld,
-                            const int32_t* assign_row, int64_t T, int h, int k, float* dg,
-                            hipStream_t s) {
+                            const int32_t* assign_row, int64_t rows, int64_t T, int h, int k,
+                            float* dg, hipStream_t s) {
   const int V = vec_of(dtype);
   MOE_BY_DTYPE(dtype, gate_grad_kernel, dim3((unsigned)T), (const uint4*)dy, (const uint4*)o,
-               (int64_t)ld / V, assign_row, h / V, k, dg);
+               (int64_t)ld / V, assign_row, rows, h / V, k, dg);
   return hipGetLastError();
 }
 

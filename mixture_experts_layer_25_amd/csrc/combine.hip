@@ -9,7 +9,9 @@
 // kCombTok tokens per workgroup; each thread gathers 16-byte vectors of the
 // k expert rows, sums in fp32 in slot order (shared expert last) and stores
 // one 16-byte vector of y.  With expert-choice routing the slots of a token
-// are the E experts (row -1 where an expert did not choose it).
+// are the E experts (row -1 where an expert did not choose it).  A slot
+// whose row is outside [0, nrows) (-1: dropped) contributes nothing, so a
+// caller's map can never send a read past the expert outputs.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -23,7 +25,7 @@ template <int KMAX>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(
     const uint4* __restrict__ yp, int64_t pv, const int32_t* __restrict__ assign_row,
     const float* __restrict__ gate, const uint4* __restrict__ shared_y,
-    uint4* __restrict__ y, int64_t T, int nv, int k) {
+    uint4* __restrict__ y, int64_t T, int nv, int k, int nrows) {
   for (int tt = 0; tt < kCombTok; ++tt) {
     const int64_t t = (int64_t)blockIdx.x * kCombTok + tt;
     if (t >= T) return;
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
       for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
-        if (rows[j] >= 0) {
+        if ((uint32_t)rows[j] < (uint32_t)nrows) {
           const uint4 q = yp[(int64_t)rows[j] * pv + v];
           const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -73,7 +75,7 @@ template <int KMAX>
 __global__ __launch_bounds__(256) void combine_f32_kernel(
     const float4* __restrict__ yp, int64_t pv, const int32_t* __restrict__ assign_row,
     const float* __restrict__ gate, const float4* __restrict__ shared_y,
-    float4* __restrict__ y, int64_t T, int nv, int k) {
+    float4* __restrict__ y, int64_t T, int nv, int k, int nrows) {
   for (int tt = 0; tt < kCombTok; ++tt) {
     const int64_t t = (int64_t)blockIdx.x * kCombTok + tt;
     if (t >= T) return;
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(
       float4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
-        if (rows[j] >= 0) {
+        if ((uint32_t)rows[j] < (uint32_t)nrows) {
           const float4 q = yp[(int64_t)rows[j] * pv + v];
           acc.x = fmaf(g[j], q.x, acc.x);
           acc.y = fmaf(g[j], q.y, acc.y);
@@ -139,7 +141,7 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void combine_sparse_kernel(
     const void* __restrict__ yp_, int64_t pv, const int32_t* __restrict__ assign_row,
     const float* __restrict__ gate, const void* __restrict__ shared_y_, void* __restrict__ y_,
-    int64_t T, int nv, int k) {
+    int64_t T, int nv, int k, int nrows) {
   __shared__ int32_t lrow[1024];
   __shared__ float lgate[1024];
   __shared__ int tmp[8];
@@ -148,9 +150,10 @@ __global__ __launch_bounds__(256) void combine_sparse_kernel(
   for (int j0 = 0; j0 < k; j0 += 256) {
     const int j = j0 + threadIdx.x;
     const int r = j < k ? assign_row[t * k + j] : -1;
+    const bool kept = (uint32_t)r < (uint32_t)nrows;
     int tot;
-    const int pos = block_exclusive_scan_256c(r >= 0 ? 1 : 0, tmp, &tot);
-    if (r >= 0) {
+    const int pos = block_exclusive_scan_256c(kept ? 1 : 0, tmp, &tot);
+    if (kept) {
       lrow[n + pos] = r;
       lgate[n + pos] = gate[t * k + j];
     }
@@ -212,17 +215,17 @@ __global__ __launch_bounds__(256) void combine_sparse_kernel(
 
 template <int KMAX>
 void launch_combine_t(int dtype, const void* yp, int ld, const int32_t* ar, const float* g,
-                      const void* sy, void* y, int64_t T, int h, int k,
+                      const void* sy, void* y, int64_t T, int h, int k, int nrows,
                       hipStream_t s) {
   const int64_t nb = (T + kCombTok - 1) / kCombTok;
   if (dtype == 1)
     hipLaunchKernelGGL((combine_bf16_kernel<KMAX>), dim3((unsigned)nb), dim3(256), 0, s,
                        (const uint4*)yp, (int64_t)ld / 8, ar, g, (const uint4*)sy, (uint4*)y, T,
-                       h / 8, k);
+                       h / 8, k, nrows);
   else
     hipLaunchKernelGGL((combine_f32_kernel<KMAX>), dim3((unsigned)nb), dim3(256), 0, s,
                        (const float4*)yp, (int64_t)ld / 4, ar, g, (const float4*)sy, (float4*)y,
-                       T, h / 4, k);
+                       T, h / 4, k, nrows);
 }
 
 }  // namespace
@@ -230,23 +233,23 @@ void launch_combine_t(int dtype, const void* yp, int ld, const int32_t* ar, cons
 hipError_t launch_combine(int dtype, const void* y_perm, int ld_perm,
                           const int32_t* assign_row, const float* gate,
                           const void* shared_y, void* y, int64_t T, int h, int k,
-                          hipStream_t s) {
+                          int64_t nrows, hipStream_t s) {
   if (k <= 1)
-    launch_combine_t<1>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, s);
+    launch_combine_t<1>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, (int)nrows, s);
   else if (k <= 2)
-    launch_combine_t<2>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, s);
+    launch_combine_t<2>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, (int)nrows, s);
   else if (k <= 4)
-    launch_combine_t<4>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, s);
+    launch_combine_t<4>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, (int)nrows, s);
   else if (k <= 8)
-    launch_combine_t<8>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, s);
+    launch_combine_t<8>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, (int)nrows, s);
   else if (k <= 16)
-    launch_combine_t<16>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, s);
+    launch_combine_t<16>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, (int)nrows, s);
   else if (dtype == 1)
     hipLaunchKernelGGL(combine_sparse_kernel<true>, dim3((unsigned)T), dim3(256), 0, s, y_perm,
-                       (int64_t)ld_perm / 8, assign_row, gate, shared_y, y, T, h / 8, k);
+                       (int64_t)ld_perm / 8, assign_row, gate, shared_y, y, T, h / 8, k, (int)nrows);
   else
     hipLaunchKernelGGL(combine_sparse_kernel<false>, dim3((unsigned)T), dim3(256), 0, s, y_perm,
-                       (int64_t)ld_perm / 4, assign_row, gate, shared_y, y, T, h / 4, k);
+                       (int64_t)ld_perm / 4, assign_row, gate, shared_y, y, T, h / 4, k, (int)nrows);
   return hipGetLastError();
 }
 

@@ -371,7 +371,7 @@ MOE_API int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
   if (misaligned(y_perm, assign_row, topk_gate, shared_y, y)) return MOE_ERR_INVALID_ARG;
   const int slots = c.routing == MOE_ROUTE_EXPERT_CHOICE ? c.E : c.k;
   MOE_TRY(moe::launch_combine(c.dtype, y_perm, c.h, assign_row, topk_gate, shared_y, y,
-                              c.T, c.h, slots, (hipStream_t)stream));
+                              c.T, c.h, slots, rows_of(c), (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -597,7 +597,7 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
   // dO rows, gate gradients
   MOE_TRY(moe::launch_scatter_dy(c.dtype, dy, r.assign_row, r.topk_gate, r.expert_counts, T, h, E, k,
                                  c.capacity, rows, c.has_shared, dO, L.ldh, s));
-  MOE_TRY(moe::launch_gate_grad(c.dtype, dy, o, ldo, r.assign_row, T, h, k, dg, s));
+  MOE_TRY(moe::launch_gate_grad(c.dtype, dy, o, ldo, r.assign_row, rows, T, h, k, dg, s));
   // dU = dO w2, then dA, then dx_perm = dA [w1; w3]
   a = base;
   a.A = dO; a.lda = L.ldh; a.a_from_out_rows = 1;
@@ -823,7 +823,7 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   const void* shared_y =
       c.has_shared ? (const void*)(at<char>(yperm, (size_t)rows * ld_h(c) * esize(c))) : nullptr;
   MOE_TRY(moe::launch_combine(c.dtype, yperm, ld_h(c), assign, gate, shared_y, y, c.T, c.h,
-                              slots, s));
+                              slots, rows, s));
   MOE_TRY(mark(8));
   return MOE_OK;
 }

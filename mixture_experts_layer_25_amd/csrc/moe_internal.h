@@ -110,8 +110,8 @@ hipError_t launch_scatter_dy(int dtype, const void* dy, const int32_t* assign_ro
                              int k, int64_t C, int64_t rows, int has_shared, void* dO, int ld,
                              hipStream_t s);
 hipError_t launch_gate_grad(int dtype, const void* dy, const void* o, int ld,
-                            const int32_t* assign_row, int64_t T, int h, int k, float* dg,
-                            hipStream_t s);
+                            const int32_t* assign_row, int64_t rows, int64_t T, int h, int k,
+                            float* dg, hipStream_t s);
 hipError_t launch_swiglu_fwd(int dtype, const void* a13, int lda13, int64_t rows, int F, void* u,
                              int ldu, hipStream_t s);
 hipError_t launch_swiglu_bwd(int dtype, const void* a13, int lda13, const void* dU, int ldu,
@@ -176,10 +176,11 @@ hipError_t launch_gtab(const int32_t* counts, const int32_t* offsets, int E,
 hipError_t launch_grouped_gemm(int dtype, bool swiglu,
                                const GroupedGemmArgs& a, hipStream_t s);
 
-// y_perm and shared_y rows are ld_perm elements apart (>= h).
+// y_perm and shared_y rows are ld_perm elements apart (>= h); slots whose
+// row is outside [0, nrows) contribute nothing.
 hipError_t launch_combine(int dtype, const void* y_perm, int ld_perm,
                           const int32_t* assign_row, const float* gate,
                           const void* shared_y, void* y, int64_t T, int h,
-                          int k, hipStream_t s);
+                          int k, int64_t nrows, hipStream_t s);
 
 }  // namespace moe

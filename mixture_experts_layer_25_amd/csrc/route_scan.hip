@@ -338,8 +338,8 @@ __global__ __launch_bounds__(1024) void fixed_groups_kernel(int E, int C, int64_
   write_gtab(e, G, valid, a0, o0, BM, tmp, gtab);
 }
 
-// Backward: groups from the forward's counts and offsets.  One workgroup of
-// 1024 threads.
+// Backward: groups from the forward's counts and offsets, each clamped to
+// the rows [0, rows) of the dispatch buffers.  One workgroup of 1024 threads.
 __global__ __launch_bounds__(1024) void groups_from_counts_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int E, int64_t C,
     int64_t T, int has_shared, int BM, int64_t rows, int32_t* __restrict__ gtab) {
@@ -349,7 +349,8 @@ __global__ __launch_bounds__(1024) void groups_from_counts_kernel(
   int valid = 0, a0 = 0, o0 = 0;
   if (e < E) {
     valid = C > 0 ? min(counts[e], (int)C) : counts[e];
-    a0 = o0 = offsets[e];
+    a0 = o0 = min(max(offsets[e], 0), (int)rows);
+    valid = max(min(valid, (int)rows - a0), 0);
   } else if (e == E && has_shared) {
     valid = (int)T;
     a0 = 0;

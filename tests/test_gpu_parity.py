@@ -875,6 +875,38 @@ def test_errors_are_reported_before_launch():
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("k", [2, 20])
+def test_combine_ignores_rows_outside_the_expert_outputs(k):
+    """A caller's map with rows outside [0, rows) (negative, rows, past it,
+    INT32_MAX): those slots contribute nothing, exactly as dropped slots
+    (-1) do, bit for bit; k = 20 takes the many-slot combine (expert choice
+    over 20 experts)."""
+    T, h, E = 64, 256, max(k, 4)
+    print(f"[case] combine with out-of-range rows T={T} h={h} k={k}", flush=True)
+    routing = "expert_choice" if k > 16 else "topk"
+    c = moe.make_cfg(T, h, 128, E, k if k <= 16 else 2, "bf16", "softmax_topk",
+                     capacity=(T if k > 16 else 0), routing=routing)
+    rows = moe.moe_num_rows(c)
+    slots = E if k > 16 else k
+    g = torch.Generator().manual_seed(11)
+    y_perm = torch.randn((rows, h), generator=g).to(torch.bfloat16).to(DEV)
+    gate = torch.rand((T, slots), generator=g).to(DEV)
+    good = torch.randint(0, rows, (T * slots,), generator=g, dtype=torch.int32)
+    bad_vals = torch.tensor([-5, rows, rows + 100, 2 ** 31 - 1], dtype=torch.int32)
+    pos = torch.randperm(T * slots, generator=g)[:T]          # one in `slots` slots
+    bad = good.clone()
+    bad[pos] = bad_vals[torch.arange(T) % 4]
+    dropped = good.clone()
+    dropped[pos] = -1
+    y_bad = torch.empty((T, h), dtype=torch.bfloat16, device=DEV)
+    y_drop = torch.empty_like(y_bad)
+    moe.moe_unpermute_combine(c, y_perm, bad.to(DEV), gate, None, y_bad)
+    moe.moe_unpermute_combine(c, y_perm, dropped.to(DEV), gate, None, y_drop)
+    torch.cuda.synchronize()
+    assert torch.equal(y_bad.view(torch.int16), y_drop.view(torch.int16))
+    assert y_drop.abs().sum().item() > 0
+
+
 # ------------------------------------------------------------ maximum sizes
 def test_beyond_int32_element_counts():
     """x [2^19 + 77, 4096] bf16 holds more than 2^31 elements and the
