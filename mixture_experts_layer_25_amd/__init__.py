@@ -155,13 +155,52 @@ def _check(fn: str, status: int) -> None:
         raise MoEError(fn, status)
 
 
-def _ptr(t) -> Optional[int]:
-    """Device pointer of a tensor (None stays NULL)."""
+def _ptr(t, nbytes: int = 0, name: str = "tensor") -> Optional[int]:
+    """Device pointer of a tensor (None stays NULL).  The kernels take the
+    pointer as a device address and trust the sizes the config implies, so a
+    host tensor or one smaller than ``nbytes`` is refused here."""
     if t is None:
         return None
+    if not t.is_cuda:
+        raise ValueError(f"libmoe takes device tensors: {name} is on {t.device}")
     if not t.is_contiguous():
-        raise ValueError("libmoe takes contiguous tensors")
+        raise ValueError(f"libmoe takes contiguous tensors: {name} is not")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, the config needs {nbytes}")
     return t.data_ptr()
+
+
+def _sizes(cfg) -> dict:
+    """Bytes each named tensor of a call must hold for ``cfg`` (empty when
+    the library refuses the config: the call itself then reports why)."""
+    rows = ctypes.c_int64()
+    if lib().moe_num_rows(ctypes.byref(cfg), ctypes.byref(rows)) != MOE_OK:
+        return {}
+    T, h, F, E, k = cfg.T, cfg.h, cfg.F, cfg.E, cfg.k
+    R = rows.value
+    es = 2 if cfg.dtype == MOE_DTYPE_BF16 else 4
+    slots = E if cfg.routing == MOE_ROUTE_EXPERT_CHOICE else k
+    return {
+        "x": T * h * es, "y": T * h * es, "dy": T * h * es, "dx": T * h * es,
+        "shared_y": T * h * es,
+        "w_router": E * h * es, "dw_router": E * h * es,
+        "w1": E * F * h * es, "w3": E * F * h * es, "w2": E * h * F * es,
+        "dw1": E * F * h * es, "dw3": E * F * h * es, "dw2": E * h * F * es,
+        "ws1": F * h * es, "ws3": F * h * es, "ws2": h * F * es,
+        "dws1": F * h * es, "dws3": F * h * es, "dws2": h * F * es,
+        "logit_bias": E * 4, "select_bias": E * 4, "dlogit_bias": E * 4, "route_bias": E * 4,
+        "logits": T * E * 4, "probs": E * T * 4,
+        "topk_idx": T * k * 4, "topk_gate": T * slots * 4, "assign_row": T * slots * 4,
+        "dgate": T * slots * 4,
+        "expert_counts": E * 4, "expert_offsets": (E + 1) * 4, "row_token": R * 4,
+        "x_perm": R * h * es, "act": R * F * es, "y_perm": R * h * es,
+        "f": E * 4, "P": E * 4, "aux_loss": 4,
+    }
+
+
+def _p(sizes: dict, name: str, t) -> Optional[int]:
+    return _ptr(t, sizes.get(name, 0), name)
 
 
 def _stream(stream) -> Optional[int]:
@@ -209,41 +248,54 @@ def moe_workspace_bytes(cfg: MoECfg) -> int:
 
 
 def _ws(ws):
+    """Workspace pointer and size (the library checks the size itself)."""
     if ws is None:
         return None, 0
+    if not ws.is_cuda:
+        raise ValueError(f"libmoe takes a device workspace: it is on {ws.device}")
     return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
 def moe_router_topk(cfg, x, w_router, logit_bias, select_bias, logits, topk_idx,
                     topk_gate, ws=None, stream=None) -> None:
     wp, wb = _ws(ws)
+    z = _sizes(cfg)
     _check("moe_router_topk", lib().moe_router_topk(
-        ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias),
-        _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), wp, wb, _stream(stream)))
+        ctypes.byref(cfg), _p(z, "x", x), _p(z, "w_router", w_router),
+        _p(z, "logit_bias", logit_bias), _p(z, "select_bias", select_bias),
+        _p(z, "logits", logits), _p(z, "topk_idx", topk_idx), _p(z, "topk_gate", topk_gate),
+        wp, wb, _stream(stream)))
 
 
 def moe_permute(cfg, x, topk_idx, expert_counts, expert_offsets, assign_row,
                 row_token, x_perm, ws, stream=None) -> None:
     wp, wb = _ws(ws)
+    z = _sizes(cfg)
     _check("moe_permute", lib().moe_permute(
-        ctypes.byref(cfg), _ptr(x), _ptr(topk_idx), _ptr(expert_counts),
-        _ptr(expert_offsets), _ptr(assign_row), _ptr(row_token), _ptr(x_perm), wp, wb,
-        _stream(stream)))
+        ctypes.byref(cfg), _p(z, "x", x), _p(z, "topk_idx", topk_idx),
+        _p(z, "expert_counts", expert_counts), _p(z, "expert_offsets", expert_offsets),
+        _p(z, "assign_row", assign_row), _p(z, "row_token", row_token),
+        _p(z, "x_perm", x_perm), wp, wb, _stream(stream)))
 
 
 def moe_grouped_gemm_swiglu(cfg, x_perm, expert_counts, expert_offsets, w1, w3, w2,
                             act, y_perm, ws, stream=None) -> None:
     wp, wb = _ws(ws)
+    z = _sizes(cfg)
     _check("moe_grouped_gemm_swiglu", lib().moe_grouped_gemm_swiglu(
-        ctypes.byref(cfg), _ptr(x_perm), _ptr(expert_counts), _ptr(expert_offsets),
-        _ptr(w1), _ptr(w3), _ptr(w2), _ptr(act), _ptr(y_perm), wp, wb, _stream(stream)))
+        ctypes.byref(cfg), _p(z, "x_perm", x_perm), _p(z, "expert_counts", expert_counts),
+        _p(z, "expert_offsets", expert_offsets), _p(z, "w1", w1), _p(z, "w3", w3),
+        _p(z, "w2", w2), _p(z, "act", act), _p(z, "y_perm", y_perm), wp, wb,
+        _stream(stream)))
 
 
 def moe_unpermute_combine(cfg, y_perm, assign_row, topk_gate, shared_y, y,
                           stream=None) -> None:
+    z = _sizes(cfg)
     _check("moe_unpermute_combine", lib().moe_unpermute_combine(
-        ctypes.byref(cfg), _ptr(y_perm), _ptr(assign_row), _ptr(topk_gate),
-        _ptr(shared_y), _ptr(y), _stream(stream)))
+        ctypes.byref(cfg), _p(z, "y_perm", y_perm), _p(z, "assign_row", assign_row),
+        _p(z, "topk_gate", topk_gate), _p(z, "shared_y", shared_y), _p(z, "y", y),
+        _stream(stream)))
 
 
 def moe_load_balance(cfg, logits, expert_counts, alpha: float, f, P, aux_loss, ws,
@@ -251,9 +303,11 @@ def moe_load_balance(cfg, logits, expert_counts, alpha: float, f, P, aux_loss, w
     """Share of assignments f [E], mean router probability P [E] and the
     Switch loss alpha*E*sum(f*P) [1] of a routing (fp32 device outputs)."""
     wp, wb = _ws(ws)
+    z = _sizes(cfg)
     _check("moe_load_balance", lib().moe_load_balance(
-        ctypes.byref(cfg), _ptr(logits), _ptr(expert_counts), float(alpha), _ptr(f), _ptr(P),
-        _ptr(aux_loss), wp, wb, _stream(stream)))
+        ctypes.byref(cfg), _p(z, "logits", logits), _p(z, "expert_counts", expert_counts),
+        float(alpha), _p(z, "f", f), _p(z, "P", P), _p(z, "aux_loss", aux_loss), wp, wb,
+        _stream(stream)))
 
 
 def moe_backward_workspace_bytes(cfg: MoECfg) -> int:
@@ -270,12 +324,12 @@ def moe_backward(cfg, weights: dict, x, dy, route: dict, grads: dict, ws, stream
     tensors (dx, dw1, dw3, dw2 required; dw_router, dlogit_bias, dgate and
     the shared expert's dws1/dws3/dws2 as needed)."""
     wp, wb = _ws(ws)
-    g = MoEGrads()
-    for name, _ in MoEGrads._fields_:
-        setattr(g, name, _ptr(grads.get(name)))
+    z = _sizes(cfg)
+    g = _struct(MoEGrads, grads, z)
     _check("moe_backward", lib().moe_backward(
-        ctypes.byref(cfg), ctypes.byref(weights_struct(weights)), _ptr(x), _ptr(dy),
-        ctypes.byref(route_struct(route)), ctypes.byref(g), wp, wb, _stream(stream)))
+        ctypes.byref(cfg), ctypes.byref(weights_struct(weights, cfg)), _p(z, "x", x),
+        _p(z, "dy", dy), ctypes.byref(route_struct(route, cfg)), ctypes.byref(g), wp, wb,
+        _stream(stream)))
 
 
 def moe_backward_saved(cfg, weights: dict, x, dy, route: dict, fwd_ws, grads: dict, ws,
@@ -285,28 +339,29 @@ def moe_backward_saved(cfg, weights: dict, x, dy, route: dict, fwd_ws, grads: di
     cfg, weights, x and routing outputs)."""
     fp, fb = _ws(fwd_ws)
     wp, wb = _ws(ws)
-    g = MoEGrads()
-    for name, _ in MoEGrads._fields_:
-        setattr(g, name, _ptr(grads.get(name)))
+    z = _sizes(cfg)
+    g = _struct(MoEGrads, grads, z)
     _check("moe_backward_saved", lib().moe_backward_saved(
-        ctypes.byref(cfg), ctypes.byref(weights_struct(weights)), _ptr(x), _ptr(dy),
-        ctypes.byref(route_struct(route)), fp, fb, ctypes.byref(g), wp, wb, _stream(stream)))
+        ctypes.byref(cfg), ctypes.byref(weights_struct(weights, cfg)), _p(z, "x", x),
+        _p(z, "dy", dy), ctypes.byref(route_struct(route, cfg)), fp, fb, ctypes.byref(g),
+        wp, wb, _stream(stream)))
 
 
-def weights_struct(w: dict) -> MoEWeights:
-    s = MoEWeights()
-    for name, _ in MoEWeights._fields_:
-        setattr(s, name, _ptr(w.get(name)))
+def _struct(kind, tensors: dict, sizes: dict):
+    s = kind()
+    for name, _ in kind._fields_:
+        setattr(s, name, _p(sizes, name, tensors.get(name)))
     return s
 
 
-def route_struct(r: Optional[dict]) -> Optional[MoERouteOut]:
+def weights_struct(w: dict, cfg: Optional[MoECfg] = None) -> MoEWeights:
+    return _struct(MoEWeights, w, _sizes(cfg) if cfg is not None else {})
+
+
+def route_struct(r: Optional[dict], cfg: Optional[MoECfg] = None) -> Optional[MoERouteOut]:
     if r is None:
         return None
-    s = MoERouteOut()
-    for name, _ in MoERouteOut._fields_:
-        setattr(s, name, _ptr(r.get(name)))
-    return s
+    return _struct(MoERouteOut, r, _sizes(cfg) if cfg is not None else {})
 
 
 def moe_forward(cfg, weights: dict, x, y, route: Optional[dict] = None, ws=None,
@@ -318,8 +373,9 @@ def moe_forward(cfg, weights: dict, x, y, route: Optional[dict] = None, ws=None,
     route_bias for Sinkhorn routing).  ``events``: None or
     MOE_NUM_EVENTS ``torch.cuda.Event(enable_timing=True)``."""
     wp, wb = _ws(ws)
-    ws_struct = weights_struct(weights)
-    rs = route_struct(route)
+    z = _sizes(cfg)
+    ws_struct = weights_struct(weights, cfg)
+    rs = route_struct(route, cfg)
     ev = None
     if events is not None:
         if len(events) != MOE_NUM_EVENTS:
@@ -331,5 +387,5 @@ def moe_forward(cfg, weights: dict, x, y, route: Optional[dict] = None, ws=None,
             handles.append(e.cuda_event)
         ev = (ctypes.c_void_p * MOE_NUM_EVENTS)(*handles)
     _check("moe_forward", lib().moe_forward(
-        ctypes.byref(cfg), ctypes.byref(ws_struct), _ptr(x), _ptr(y),
+        ctypes.byref(cfg), ctypes.byref(ws_struct), _p(z, "x", x), _p(z, "y", y),
         ctypes.byref(rs) if rs is not None else None, wp, wb, ev, _stream(stream)))

@@ -241,6 +241,18 @@ def test_backward_saved_argument_checks():
     assert call(c, 4096 + 8, 1 << 40) == moe.MOE_ERR_INVALID_ARG              # misaligned
 
 
+def test_binding_refuses_host_tensors():
+    """The binding hands data_ptr() to kernels as a device address: a host
+    tensor is refused before anything reaches the library."""
+    import torch
+    c = _cfg(T=8)
+    x = torch.zeros((8, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensors: x"):
+        moe.moe_router_topk(c, x, x, None, None, None, x, x)
+    with pytest.raises(ValueError, match="device workspace"):
+        moe.moe_permute(c, None, None, None, None, None, None, None, ws=x)
+
+
 def test_strerror():
     assert moe.strerror(moe.MOE_OK) == "ok"
     assert "workspace" in moe.strerror(moe.MOE_ERR_WORKSPACE)

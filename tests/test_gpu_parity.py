@@ -875,6 +875,23 @@ def test_errors_are_reported_before_launch():
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
 
 
+def test_binding_refuses_tensors_smaller_than_the_config():
+    """A tensor smaller than the config implies would send the kernels past
+    its end: the binding refuses it before any launch."""
+    cfg = CONFIGS["tiny_fp32"]
+    inp = gen_inputs(cfg)
+    c = lib_cfg(cfg, 0)
+    ws = torch.empty(moe.moe_workspace_bytes(c), dtype=torch.uint8, device=DEV)
+    w = {n: inp[n] for n in ("w_router", "w1", "w3", "w2")}
+    y_short = torch.empty((cfg.T - 1, cfg.h), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError, match="y holds"):
+        moe.moe_forward(c, w, inp["x"], y_short, None, ws)
+    w_short = dict(w, w2=inp["w2"][:-1])
+    y = torch.empty((cfg.T, cfg.h), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError, match="w2 holds"):
+        moe.moe_forward(c, w_short, inp["x"], y, None, ws)
+
+
 @pytest.mark.parametrize("k", [2, 20])
 def test_combine_ignores_rows_outside_the_expert_outputs(k):
     """A caller's map with rows outside [0, rows) (negative, rows, past it,
