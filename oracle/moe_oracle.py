@@ -20,7 +20,8 @@ no permutation buffer, no blocking and no fusion:
    shared expert's output when there is one;
 7. (separately) the load-balance statistics of a routing: the share of
    assignments per expert, the router's mean probability per expert and the
-   Switch auxiliary loss built from them;
+   Switch auxiliary loss built from them; and one step of the aux-loss-free
+   update of the per-expert selection bias;
 8. three routing variants: capacity drops by gate score instead of token
    order, expert choice (every expert takes its C best-scoring tokens), and
    Sinkhorn balancing of the routing matrix before the top-k;
@@ -371,6 +372,26 @@ def load_balance(logits, counts, k: int, gate: str, alpha: float) -> dict:
     loss = float(alpha) * E * float(np.dot(f, P))
     return {"f": f.astype(np.float32), "P": P.astype(np.float32),
             "loss": np.float32(loss)}
+
+
+def select_bias_update(select_bias, counts, T: int, k: int, gamma: float) -> np.ndarray:
+    """One step of aux-loss-free balancing.  infra-l7, "NVIDIA 原题" notes on
+    the load balancing loss: DeepSeek-V3 drops the auxiliary loss and gives
+    every expert a bias that only enters the top-k selection, kept outside
+    the loss.  The pages name the bias but not how it moves; the reading
+    taken: after a routing, an expert that received more than the mean
+    T*k/E assignments has its bias lowered by gamma, one that received fewer
+    has it raised by gamma, one exactly at the mean keeps it.  The
+    comparison is T*k against E*count in exact integers; the step is one fp32
+    addition, and an expert at the mean keeps its bias bit for bit."""
+    b = np.asarray(select_bias, dtype=np.float32).copy()
+    c = np.asarray(counts, dtype=np.int64)
+    E = b.shape[0]
+    under = T * k - E * c          # > 0: fewer than the mean, < 0: more
+    step = np.float32(gamma)
+    b[under > 0] = b[under > 0] + step
+    b[under < 0] = b[under < 0] - step
+    return b
 
 
 # ---------------------------------------------------------------------------

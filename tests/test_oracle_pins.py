@@ -743,3 +743,48 @@ def test_moe_forward_sinkhorn_route():
     with pytest.raises(ValueError):
         oracle.moe_forward(*a, k=cfg.k, gate=cfg.gate, sinkhorn_iters=5,
                            select_bias=np.zeros(cfg.E, np.float32), maps_only=True)
+
+
+# ------------------------------------------------------------ aux-loss-free selection bias
+def test_select_bias_update_hand_case():
+    """T*k = 12 assignments over E = 4 experts (mean 3): loads 5, 3, 2, 2 give
+    the steps -1/8, 0, +1/8, +1/8, worked by hand."""
+    b = np.array([0.5, -0.25, 0.0, 1.0], np.float32)
+    out = oracle.select_bias_update(b, [5, 3, 2, 2], T=6, k=2, gamma=0.125)
+    np.testing.assert_array_equal(out, np.array([0.375, -0.25, 0.125, 1.125], np.float32))
+    np.testing.assert_array_equal(b, [0.5, -0.25, 0.0, 1.0])      # input untouched
+
+
+def test_select_bias_update_fractional_mean_and_rounding():
+    """Mean 10/4 = 2.5 is never hit, so every expert moves; the step is one fp32
+    addition (1 + 2^-30 rounds back to 1 in fp32)."""
+    out = oracle.select_bias_update(np.ones(4, np.float32), [3, 2, 3, 2], T=5, k=2,
+                                    gamma=2.0 ** -30)
+    np.testing.assert_array_equal(out, np.ones(4, np.float32))
+    out = oracle.select_bias_update(np.zeros(4, np.float32), [3, 2, 3, 2], T=5, k=2, gamma=0.5)
+    np.testing.assert_array_equal(out, [-0.5, 0.5, -0.5, 0.5])
+
+
+def test_select_bias_update_even_load_keeps_every_bit():
+    b = np.array([-0.0, 0.1, -3.5, 7.25e-8], np.float32)
+    out = oracle.select_bias_update(b, [6, 6, 6, 6], T=8, k=3, gamma=0.01)
+    np.testing.assert_array_equal(out.view(np.uint32), b.view(np.uint32))
+
+
+def test_select_bias_update_evens_out_a_skewed_router():
+    """The sign convention closes the loop: routing a Zipf-skewed router on
+    its logits plus the bias, then updating the bias from that routing's
+    loads, brings the hottest expert from several times the mean load to
+    near it; a flipped sign would make the skew worse."""
+    rng = np.random.default_rng(3)
+    T, E, k, gamma = 2048, 16, 2, 0.02
+    l = (rng.normal(size=(T, E)) - 1.2 * np.log(np.arange(E) + 1)).astype(np.float32)
+    mean = T * k / E
+    b = np.zeros(E, np.float32)
+    first = None
+    for _ in range(200):
+        counts = np.bincount(oracle.topk(oracle.selection_keys(l, b), k).ravel(), minlength=E)
+        first = counts if first is None else first
+        b = oracle.select_bias_update(b, counts, T, k, gamma)
+    assert first.max() > 3 * mean
+    assert counts.max() < 1.25 * mean and counts.min() > 0.75 * mean
