@@ -316,6 +316,23 @@ int moe_load_balance(const moe_cfg_t* cfg, const float* logits,
                      const int32_t* expert_counts, float alpha, float* f, float* P,
                      float* aux_loss, void* ws, size_t ws_bytes, void* stream);
 
+/* Aux-loss-free balancing step ----------------------------------------------
+ * infra-l7, "NVIDIA 原题" notes on the load balancing loss: DeepSeek-V3
+ * replaces the auxiliary loss with a per-expert bias that enters only the
+ * top-k selection (select_bias of moe_router_topk / moe_forward) and is kept
+ * out of the loss.  The pages do not say how the bias moves; this call takes
+ * one fixed step per routing: for expert e, with c = expert_counts[e] (the
+ * routed assignments before any drop, as moe_permute / moe_forward write
+ * them), T*k > E*c (fewer than the mean) raises select_bias[e] by gamma,
+ * T*k < E*c lowers it by gamma, T*k == E*c leaves it unchanged; one fp32
+ * addition each, compared in exact integers.
+ *   expert_counts [E] int32 in;  select_bias [E] fp32 in/out (in place);
+ *   gamma: step, finite (else MOE_ERR_INVALID_ARG).
+ * Top-k routing (with or without score drop) only; other routings:
+ * MOE_ERR_UNSUPPORTED.  T == 0: nothing is enqueued.                       */
+int moe_select_bias_update(const moe_cfg_t* cfg, const int32_t* expert_counts,
+                           float gamma, float* select_bias, void* stream);
+
 /* Backward of the layer -------------------------------------------------
  * 专家并行 page, "EP+DP" BWD (each GPU computes its experts' weight
  * gradients; the gradients go back along the routing path) and Megatron-LM

@@ -57,7 +57,8 @@ ROUTING_BY_NAME = {
 ABI_SYMBOLS = (
     "moe_strerror", "moe_capacity", "moe_num_rows", "moe_workspace_bytes",
     "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu",
-    "moe_unpermute_combine", "moe_load_balance", "moe_backward_workspace_bytes",
+    "moe_unpermute_combine", "moe_load_balance", "moe_select_bias_update",
+    "moe_backward_workspace_bytes",
     "moe_backward", "moe_backward_saved", "moe_forward",
 )
 
@@ -128,6 +129,7 @@ def lib() -> ctypes.CDLL:
             "moe_unpermute_combine": (ctypes.c_int, [cfgp, P, P, P, P, P, P]),
             "moe_load_balance": (ctypes.c_int, [cfgp, P, P, ctypes.c_float, P, P, P, P, SZ,
                                                 P]),
+            "moe_select_bias_update": (ctypes.c_int, [cfgp, P, ctypes.c_float, P, P]),
             "moe_backward_workspace_bytes": (ctypes.c_int, [cfgp, ctypes.POINTER(SZ)]),
             "moe_backward": (ctypes.c_int, [cfgp, ctypes.POINTER(MoEWeights), P, P,
                                             ctypes.POINTER(MoERouteOut),
@@ -308,6 +310,16 @@ def moe_load_balance(cfg, logits, expert_counts, alpha: float, f, P, aux_loss, w
         ctypes.byref(cfg), _p(z, "logits", logits), _p(z, "expert_counts", expert_counts),
         float(alpha), _p(z, "f", f), _p(z, "P", P), _p(z, "aux_loss", aux_loss), wp, wb,
         _stream(stream)))
+
+
+def moe_select_bias_update(cfg, expert_counts, gamma: float, select_bias, stream=None) -> None:
+    """One aux-loss-free balancing step, in place on select_bias [E] fp32: an
+    expert with more than the mean T*k/E routed assignments (expert_counts
+    [E] int32) loses gamma, one with fewer gains gamma."""
+    z = _sizes(cfg)
+    _check("moe_select_bias_update", lib().moe_select_bias_update(
+        ctypes.byref(cfg), _p(z, "expert_counts", expert_counts), float(gamma),
+        _p(z, "select_bias", select_bias), _stream(stream)))
 
 
 def moe_backward_workspace_bytes(cfg: MoECfg) -> int:

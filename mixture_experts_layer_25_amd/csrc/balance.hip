@@ -16,6 +16,9 @@
 //            parallel slices, combined in slice order), f = counts/(T*k),
 //            P = sum/T, loss = alpha*E*sum f*P by a fixed tree.
 // Every sum has a fixed order, so the results are the same on every run.
+//
+// The aux-loss-free selection-bias step moves each expert's bias one fixed
+// step against its load (below).
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -172,7 +175,32 @@ __global__ __launch_bounds__(1024) void balance_final_kernel(
   if (tid == 0) loss_out[0] = alpha * (float)E * red[0];
 }
 
+// One aux-loss-free balancing step (DeepSeek-V3 in the same notes: a
+// per-expert bias that enters only the top-k selection).  Expert e's load is
+// compared with the mean T*k/E in exact integers (T*k against E*count): an
+// over-loaded expert's bias drops by gamma, an under-loaded one's rises by
+// gamma, one at the mean is left untouched.  One thread per expert.
+__global__ __launch_bounds__(256) void select_bias_update_kernel(const int32_t* __restrict__ counts,
+                                                                 int64_t T, int E, int k,
+                                                                 float gamma,
+                                                                 float* __restrict__ bias) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const int64_t under = T * k - (int64_t)E * counts[e];
+  if (under > 0)
+    bias[e] = bias[e] + gamma;
+  else if (under < 0)
+    bias[e] = bias[e] - gamma;
+}
+
 }  // namespace
+
+hipError_t launch_select_bias_update(const int32_t* counts, int64_t T, int E, int k, float gamma,
+                                     float* bias, hipStream_t st) {
+  hipLaunchKernelGGL(select_bias_update_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0,
+                     st, counts, T, E, k, gamma, bias);
+  return hipGetLastError();
+}
 
 hipError_t launch_load_balance(const float* logits, const int32_t* counts, int gate, int64_t T,
                                int E, int k, float alpha, float* partial, float* f, float* P,

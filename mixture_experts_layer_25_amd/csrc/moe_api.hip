@@ -375,6 +375,22 @@ MOE_API int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
   return MOE_OK;
 }
 
+MOE_API int moe_select_bias_update(const moe_cfg_t* cfg, const int32_t* expert_counts,
+                                   float gamma, float* select_bias, void* stream) {
+  const int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const moe_cfg_t& c = *cfg;
+  if (c.routing != MOE_ROUTE_TOPK && c.routing != MOE_ROUTE_TOPK_SCORE_DROP)
+    return MOE_ERR_UNSUPPORTED;
+  if (!(gamma - gamma == 0.f)) return MOE_ERR_INVALID_ARG;   // NaN or infinite
+  if (c.T == 0) return MOE_OK;
+  if (!expert_counts || !select_bias) return MOE_ERR_INVALID_ARG;
+  if (misaligned(expert_counts, select_bias)) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(moe::launch_select_bias_update(expert_counts, c.T, c.E, c.k, gamma, select_bias,
+                                         (hipStream_t)stream));
+  return MOE_OK;
+}
+
 MOE_API int moe_load_balance(const moe_cfg_t* cfg, const float* logits,
                              const int32_t* expert_counts, float alpha, float* f, float* P,
                              float* aux_loss, void* ws, size_t ws_bytes, void* stream) {

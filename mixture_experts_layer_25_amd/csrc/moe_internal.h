@@ -131,6 +131,8 @@ hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token
 // Router distribution summed per expert over token groups (partial:
 // [ceil(T / topk_tokens_per_wg(E))][E] floats), then f, P and the Switch
 // loss (one workgroup).
+hipError_t launch_select_bias_update(const int32_t* counts, int64_t T, int E, int k, float gamma,
+                                     float* bias, hipStream_t st);
 hipError_t launch_load_balance(const float* logits, const int32_t* counts, int gate, int64_t T,
                                int E, int k, float alpha, float* partial, float* f, float* P,
                                float* loss, hipStream_t st);

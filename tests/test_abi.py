@@ -253,6 +253,22 @@ def test_binding_refuses_host_tensors():
         moe.moe_permute(c, None, None, None, None, None, None, None, ws=x)
 
 
+def test_select_bias_update_validation():
+    """Host checks of the bias step; every case returns before any launch."""
+    L = moe.lib()
+    c = _cfg(T=8)
+    assert L.moe_select_bias_update(ctypes.byref(c), 16, float("nan"), 32, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_select_bias_update(ctypes.byref(c), 16, float("inf"), 32, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert L.moe_select_bias_update(ctypes.byref(c), None, 0.1, 32, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    ec = _cfg(T=8, capacity=4, routing="expert_choice")
+    assert L.moe_select_bias_update(ctypes.byref(ec), 16, 0.1, 32, None) == \
+        moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_select_bias_update(ctypes.byref(_cfg(T=0)), None, 0.1, None, None) == moe.MOE_OK
+
+
 def test_strerror():
     assert moe.strerror(moe.MOE_OK) == "ok"
     assert "workspace" in moe.strerror(moe.MOE_ERR_WORKSPACE)

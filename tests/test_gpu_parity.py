@@ -875,6 +875,62 @@ def test_errors_are_reported_before_launch():
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
 
 
+def test_select_bias_update_matches_oracle():
+    """Random loads and biases: the step equals the oracle's bit for bit,
+    experts exactly at the mean load keep their bias (a -0.0 included)."""
+    g = torch.Generator().manual_seed(5)
+    for T, E, k in [(12, 4, 2), (4096, 8, 2), (4096, 256, 8), (1000, 1024, 16)]:
+        print(f"[case] select-bias step T={T} E={E} k={k}", flush=True)
+        c = moe.make_cfg(T, 128, 128, E, k, "bf16", "sigmoid_topk_norm")
+        mean = T * k // E
+        counts = torch.randint(max(0, mean - 3), mean + 4, (E,), generator=g, dtype=torch.int32)
+        bias = (torch.randn(E, generator=g) * 0.3).float()
+        bias[0] = -0.0
+        counts[1] = mean
+        gb = bias.to(DEV)
+        moe.moe_select_bias_update(c, counts.to(DEV), 1e-3, gb)
+        ref = oracle.select_bias_update(bias.numpy(), counts.numpy(), T, k, 1e-3)
+        np.testing.assert_array_equal(gb.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_select_bias_update_evens_a_skewed_router():
+    """Route with the bias, count, step the bias, 150 times on a Zipf-skewed
+    router: every step equals the oracle's step from the GPU's own counts
+    (which equal the counts of the GPU's selection), and the loads end near
+    the mean."""
+    cfg = MoEConfig("bias_loop", T=2048, h=128, E=16, k=2, F=128, gate="softmax_topk",
+                    logit_bias=("zipf", 1.2))
+    print(f"[case] select-bias loop T={cfg.T} E={cfg.E} k={cfg.k}", flush=True)
+    inp = gen_inputs(cfg)
+    c = lib_cfg(cfg, 0)
+    T, E, k, h = cfg.T, cfg.E, cfg.k, cfg.h
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    counts = torch.empty((E,), dtype=torch.int32, device=DEV)
+    offs = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
+    assign = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    rowtok = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    xperm = torch.empty((T * k, h), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(moe.moe_workspace_bytes(c), dtype=torch.uint8, device=DEV)
+    bias = torch.zeros((E,), dtype=torch.float32, device=DEV)
+    mean = T * k / E
+    first = None
+    for _ in range(150):
+        prev = bias.cpu().numpy()
+        moe.moe_router_topk(c, inp["x"], inp["w_router"], inp["logit_bias"], bias, logits, idx,
+                            gate, ws)
+        moe.moe_permute(c, inp["x"], idx, counts, offs, assign, rowtok, xperm, ws)
+        moe.moe_select_bias_update(c, counts, 0.02, bias)
+        cnt = counts.cpu().numpy()
+        np.testing.assert_array_equal(cnt, np.bincount(idx.cpu().numpy().ravel(), minlength=E))
+        np.testing.assert_array_equal(bias.cpu().numpy(),
+                                      oracle.select_bias_update(prev, cnt, T, k, 0.02))
+        first = cnt if first is None else first
+    assert first.max() > 2.5 * mean
+    assert cnt.max() < 1.25 * mean and cnt.min() > 0.75 * mean
+
+
 def test_binding_refuses_tensors_smaller_than_the_config():
     """A tensor smaller than the config implies would send the kernels past
     its end: the binding refuses it before any launch."""
