@@ -77,24 +77,52 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def _machine_fields(path: str) -> dict:
+    """The ``name: value`` lines of a committed profile summary."""
+    kv = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            for line in f:
+                m = re.match(r"^([a-z_0-9]+):\s*(\S+)", line)
+                if m:
+                    kv[m.group(1)] = m.group(2)
+    return kv
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch of GEMM 1 from the committed counter summary, or
     None when the summary is missing, is for another workload, or was taken
     on a different version of the kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    kv = _machine_fields(TRAFFIC_FILE)
+    if not kv:
         return None
-    kv = {}
-    with open(TRAFFIC_FILE) as f:
-        for line in f:
-            m = re.match(r"^([a-z_0-9]+):\s*(\S+)", line)
-            if m:
-                kv[m.group(1)] = m.group(2)
     if kv.get("kernel_source_sha256_16") != source_hash(GEMM_SOURCE):
         return None
     if kv.get("workload") != workload.split(":")[0]:
         return None
     try:
         return int(kv["gemm1_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_worked_example.md")
+TRACE_SOURCES = {"permute": "route_scan.hip", "combine": "combine.hip"}
+
+
+def traced_kernel_us(workload: str, stage: str):
+    """Median duration (us) of the permute or combine kernel in the committed
+    rocprofv3 kernel trace, or None when the trace is missing, is of another
+    workload, or that kernel's source has changed since it was taken.  The
+    per-stage event times include the gaps the events themselves add."""
+    kv = _machine_fields(TRACE_FILE)
+    if kv.get("workload") != workload.split(":")[0]:
+        return None
+    src = os.path.join(ROOT, "mixture_experts_layer_25_amd", "csrc", TRACE_SOURCES[stage])
+    if kv.get(f"{stage}_source_sha256_16") != source_hash(src):
+        return None
+    try:
+        return float(kv[f"{stage}_kernel_median_us"])
     except (KeyError, ValueError):
         return None
 
@@ -430,6 +458,11 @@ def main() -> int:
     router_gbs = rb / (stage_ms["router"] * 1e-3) / 1e9
     perm_gbs = pb / (stage_ms["permute"] * 1e-3) / 1e9
     comb_gbs = cb / (stage_ms["combine"] * 1e-3) / 1e9
+    wl = _workload_name(cfg, C, args.routing)
+    perm_tr = traced_kernel_us(wl, "permute") if args.routing == "topk" else None
+    comb_tr = traced_kernel_us(wl, "combine") if args.routing == "topk" else None
+    trace_frac = lambda nbytes, us: (None if us is None else  # noqa: E731
+                                     round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
 
     out = {
         "metric": METRIC,
@@ -459,12 +492,14 @@ def main() -> int:
         "router": {"gbs": round(router_gbs, 1), "frac_hbm": round(router_gbs / PEAK_HBM_GBS, 4),
                    "frac_copy": None if copy_gbs is None else round(router_gbs / copy_gbs, 4), "bytes": rb},
         "permute": {"gbs": round(perm_gbs, 1), "frac_hbm": round(perm_gbs / PEAK_HBM_GBS, 4),
-                    "frac_copy": None if copy_gbs is None else round(perm_gbs / copy_gbs, 4), "bytes": pb},
+                    "frac_copy": None if copy_gbs is None else round(perm_gbs / copy_gbs, 4), "bytes": pb,
+                    "trace_us": perm_tr, "trace_frac_hbm": trace_frac(pb, perm_tr)},
         "combine": {"gbs": round(comb_gbs, 1), "frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
                     "frac_copy": None if copy_gbs is None else round(comb_gbs / copy_gbs, 4), "bytes": cb,
                     "standalone_us": None if comb_alone is None else round(comb_alone, 2),
                     "standalone_frac_hbm": (None if comb_alone is None else
-                                            round(cb / (comb_alone * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))},
+                                            round(cb / (comb_alone * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)),
+                    "trace_us": comb_tr, "trace_frac_hbm": trace_frac(cb, comb_tr)},
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "backward": (None if bwd is None else {
             "ms": round(bwd, 4),
