@@ -51,6 +51,15 @@ def expert_flops(kept_rows: int, h: int, F: int) -> int:
     return gemm1_flops(kept_rows, h, F) + gemm2_flops(kept_rows, h, F)
 
 
+def gemm1_bytes(kept_per_expert, T: int, h: int, F: int, esz: int, shared: bool) -> int:
+    """GEMM 1's compulsory HBM bytes: w1 and w3 of every expert with a row
+    (and of the shared expert), the input rows read once, the activations
+    written once."""
+    active = sum(1 for n in kept_per_expert if n > 0) + (1 if shared else 0)
+    rows = sum(kept_per_expert) + (T if shared else 0)
+    return (2 * active * F * h + rows * h + rows * F) * esz
+
+
 def router_bytes(T: int, h: int, E: int, esz: int) -> int:
     """Read the tokens and the router weights once, write fp32 logits."""
     return (T + E) * h * esz + T * E * 4
@@ -450,6 +459,14 @@ def main() -> int:
     gg = expert_flops(kept_all, cfg.h, cfg.F) / (
         (stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    # GEMM 1 is MFMA-bound when its flops per compulsory byte exceed the
+    # ridge point peak / HBM bandwidth (312.5 flop/B for bf16), else bound by
+    # streaming its weights (few rows per expert)
+    kept_e = [min(n, C) for n in cnt] if C else cnt
+    g1_bytes = gemm1_bytes(kept_e, cfg.T, cfg.h, cfg.F, esz, cfg.shared)
+    g1_intensity = gemm1_flops(kept_all, cfg.h, cfg.F) / g1_bytes
+    hbm_bound = cfg.dtype == "bf16" and g1_intensity < peak / PEAK_HBM_GBS * 1e3
+    g1_gbs = g1_bytes / (stage_ms["gemm1_swiglu"] * 1e-3) / 1e9
     pb = permute_bytes(cfg.T, cfg.h, rows, esz)
     if args.routing == "expert_choice":      # a row gather: every row read and written
         pb = 2 * rows * cfg.h * esz
@@ -480,12 +497,15 @@ def main() -> int:
         "config": {"workload": _workload_name(cfg, C, args.routing), "routing": args.routing, "T": cfg.T, "h": cfg.h, "E": cfg.E,
                    "k": cfg.k, "F": cfg.F, "capacity": C, "gate": cfg.gate,
                    "kept_rows": kept, "dispatch_rows": rows, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma" if cfg.dtype == "bf16" else "alu",
+        "roofline": {"bound": "hbm" if hbm_bound else ("mfma" if cfg.dtype == "bf16" else "alu"),
                      "kernel": "gemm1_swiglu",
-                     "achieved": round(g1, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(g1 / peak, 4),
+                     "achieved": round(g1_gbs if hbm_bound else g1, 1),
+                     "peak": PEAK_HBM_GBS if hbm_bound else peak,
+                     "unit": "GB/s" if hbm_bound else "TFLOP/s",
+                     "frac": round(g1_gbs / PEAK_HBM_GBS if hbm_bound else g1 / peak, 4),
                      "traffic": (measured_traffic(_workload_name(cfg, C))
-                                 if args.routing == "topk" else None)},
+                                 if args.routing == "topk" else None),
+                     "flop_per_byte": round(g1_intensity, 1)},
         "grouped_gemm": {"tflops": round(gg, 1), "frac_of_peak": round(gg / peak, 4),
                          "gemm1_tflops": round(g1, 1), "gemm2_tflops": round(g2, 1)},
         "hbm_copy_gbs": None if copy_gbs is None else round(copy_gbs, 1),
