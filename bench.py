@@ -8,12 +8,15 @@ seeded synthetic input already resident in HBM.  Default workload: the
 worked example T=4096, h=4096, E=8, k=2, F=12288, capacity factor 5/4
 (C = 1280), softmax over all E then the top-2 gate values.
 
-Prints ONE JSON line: tokens/s over the K timed steps, per-stage kernel
-durations from HIP events recorded on the launch stream inside the timed
-region, the grouped-GEMM roofline (algorithmic FLOPs / event duration vs the
-bf16 dense MFMA peak), permute/combine algorithmic bytes vs HBM, the same
-step timed from a cold last-level cache (medians), and the CPU oracle timed
-on a bounded sample of the same workload.
+Prints ONE JSON line: tokens/s over the K timed steps (no instrumentation),
+per-stage kernel durations from K more steps whose stages carry HIP start/stop
+events bound to their kernels (hipExtLaunchKernel: the kernels' own
+timestamps, the figures rocprofv3's kernel trace reports), the grouped-GEMM
+roofline (algorithmic FLOPs / GEMM 1's kernel time vs the bf16 dense MFMA
+peak, or its compulsory bytes vs HBM when it streams weights),
+permute/combine algorithmic bytes vs HBM, the same step timed from a cold
+last-level cache (medians), and the CPU oracle timed on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -29,8 +32,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-METRIC = ("MoE-layer fwd tokens/s and grouped-GEMM TFLOPS (% MFMA peak), "
-          "T=4096 h=4096 E=8 k=2")
+def metric_label(T: int, h: int, E: int, k: int) -> str:
+    """The metric's name for a workload of T tokens, width h, E experts,
+    top-k (the headline workload's is the T=4096 h=4096 E=8 k=2 one)."""
+    return ("MoE-layer fwd tokens/s and grouped-GEMM TFLOPS (% MFMA peak), "
+            f"T={T} h={h} E={E} k={k}")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
@@ -69,6 +75,12 @@ def permute_bytes(T: int, h: int, rows: int, esz: int) -> int:
     """Read every token row once, write every row of the dispatch buffer
     (kept copies and zero padding)."""
     return (T + rows) * h * esz
+
+
+def dispatch_payload_bytes(T: int, k: int, h: int, esz: int) -> int:
+    """The T*k token copies of a dropless dispatch (the part of the permute's
+    writes that the expert-parallel all-to-all would carry)."""
+    return T * k * h * esz
 
 
 def combine_bytes(kept_rows: int, T: int, h: int, esz: int, shared: bool) -> int:
@@ -115,27 +127,6 @@ def measured_traffic(workload: str):
         return None
 
 
-TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_worked_example.md")
-TRACE_SOURCES = {"permute": "route_scan.hip", "combine": "combine.hip"}
-
-
-def traced_kernel_us(workload: str, stage: str):
-    """Median duration (us) of the permute or combine kernel in the committed
-    rocprofv3 kernel trace, or None when the trace is missing, is of another
-    workload, or that kernel's source has changed since it was taken.  The
-    per-stage event times include the gaps the events themselves add."""
-    kv = _machine_fields(TRACE_FILE)
-    if kv.get("workload") != workload.split(":")[0]:
-        return None
-    src = os.path.join(ROOT, "mixture_experts_layer_25_amd", "csrc", TRACE_SOURCES[stage])
-    if kv.get(f"{stage}_source_sha256_16") != source_hash(src):
-        return None
-    try:
-        return float(kv[f"{stage}_kernel_median_us"])
-    except (KeyError, ValueError):
-        return None
-
-
 # --------------------------------------------------------------------- bench
 def _workload_name(cfg, C, routing="topk"):
     s = (f"{cfg.name}: T={cfg.T} h={cfg.h} E={cfg.E} k={cfg.k} F={cfg.F} {cfg.dtype} "
@@ -146,6 +137,25 @@ def _workload_name(cfg, C, routing="topk"):
     if cfg.shared:
         s += " +1 shared expert"
     return s
+
+
+def routing_stats(logits, select_bias, assign_row, k: int, tie: float = 1e-5) -> dict:
+    """Counts of the step's routing, from the device's own outputs: tokens
+    whose k-th and (k+1)-th fp32 selection keys are closer than `tie` (where
+    another fp32 summation order of the logits could choose differently),
+    dropped assignments and tokens that lost every slot."""
+    import numpy as np
+    keys = logits.astype(np.float32)
+    if select_bias is not None:
+        keys = keys + select_bias.astype(np.float32)[None, :]
+    E = keys.shape[1]
+    near = 0
+    if k < E:
+        srt = -np.sort(-keys.astype(np.float64), axis=1)
+        near = int((srt[:, k - 1] - srt[:, k] < tie).sum())
+    a = assign_row.reshape(-1, k)
+    return {"near_ties": near, "dropped_assignments": int((a < 0).sum()),
+            "tokens_all_dropped": int((a < 0).all(1).sum())}
 
 
 def cpu_baseline(cfg, inp, C, sample_tokens: int, min_seconds: float) -> dict:
@@ -253,9 +263,7 @@ def main() -> int:
         del src, dst
 
     # `value`: K steps with no instrumentation, host clock between two
-    # synchronisations.  The per-stage times come from K more steps that
-    # record an event between every two kernels (their small launch gaps are
-    # in those stage times, not in `value`).
+    # synchronisations.
     K = args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -263,15 +271,35 @@ def main() -> int:
         moe.moe_forward(c, weights, inp["x"], y, route, ws)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_EVENTS)]
-           for _ in range(K)]
-    for es in evs:             # create the events outside the timed region
-        for e in es:
-            e.record()
+
+    # Kernel times: K more steps whose stages carry start/stop events bound
+    # to their first and last kernels (the kernels' own timestamps).
+    NS = moe.MOE_NUM_STAGES
+
+    def new_events(n):
+        out = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_EVENTS)]
+               for _ in range(n)]
+        for es in out:         # create the events outside the timed region
+            for e in es:
+                e.record()
+        return out
+
+    def stage_lists(ev_sets):
+        return {name: [es[2 * st].elapsed_time(es[2 * st + 1]) for es in ev_sets]
+                for st, name in enumerate(moe.STAGE_NAMES)}
+
+    def median(v):
+        v = sorted(v)
+        return 0.5 * (v[(len(v) - 1) // 2] + v[len(v) // 2])
+
+    evs = new_events(K)
     torch.cuda.synchronize()
     for i in range(K):
         moe.moe_forward(c, weights, inp["x"], y, route, ws, events=evs[i])
     torch.cuda.synchronize()
+    kern = stage_lists(evs)
+    stage_ms = {name: sum(v) / K for name, v in kern.items()}
+    kernel_span_ms = sum(es[0].elapsed_time(es[2 * NS - 1]) for es in evs) / K
 
     # On-box HBM yardstick: a plain 1 GiB device-to-device copy (torch),
     # best of 5, read + write bytes over its event time.  Skipped in the
@@ -294,55 +322,69 @@ def main() -> int:
         copy_gbs = 2 * cp_src.numel() * 4 / (cp_best * 1e-3) / 1e9
         del cp_src, cp_dst
 
-    # The combine kernel alone (moe_unpermute_combine), 50 back-to-back calls
-    # on this step's routing over a dense expert-output buffer of the same
-    # shape, one pair of events around them (no per-stage event overhead).
+    # The step's routing, read back once (not timed): counts of near-tied
+    # selection keys and of drops, for the record.
+    rs_route = {"logits": torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev),
+                "expert_counts": counts}
+    slots = cfg.E if args.routing == "expert_choice" else cfg.k
+    rs_route["assign_row"] = torch.empty(cfg.T * slots, dtype=torch.int32, device=dev)
+    rs_route["topk_gate"] = torch.empty((cfg.T, slots), dtype=torch.float32, device=dev)
+    moe.moe_forward(c, weights, inp["x"], y, rs_route, ws)
+    torch.cuda.synchronize()
+    if args.routing == "expert_choice":
+        a = rs_route["assign_row"].view(cfg.T, cfg.E).cpu().numpy()
+        rstats = {"tokens_no_expert": int((a < 0).all(1).sum())}
+    else:
+        sb_np = None if inp["select_bias"] is None else inp["select_bias"].cpu().numpy()
+        rstats = routing_stats(rs_route["logits"].cpu().numpy(), sb_np,
+                               rs_route["assign_row"].cpu().numpy(), cfg.k)
+
+    # The combine kernel alone (moe_unpermute_combine) on this step's
+    # routing, cycling over enough buffer sets (expert outputs + y) that
+    # each call's operands have left the 256 MB last-level cache; 10 rounds
+    # over the sets between one pair of events.
     comb_alone = None
+    comb_sets = 0
     if args.routing == "topk" and not cfg.shared:
-        cr = {"topk_gate": torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev),
-              "assign_row": torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev)}
-        moe.moe_forward(c, weights, inp["x"], y, cr, ws)
-        yp = torch.empty((rows, cfg.h), dtype=tdt, device=dev).normal_()
-        yc = torch.empty_like(y)
-        for _ in range(5):
-            moe.moe_unpermute_combine(c, yp, cr["assign_row"], cr["topk_gate"], None, yc)
+        set_bytes = (rows + cfg.T) * cfg.h * esz
+        comb_sets = max(2, min(8, -(-(512 << 20) // set_bytes)))
+        sets = [(torch.empty((rows, cfg.h), dtype=tdt, device=dev).normal_(), torch.empty_like(y))
+                for _ in range(comb_sets)]
+        for yp, yc in sets:
+            moe.moe_unpermute_combine(c, yp, rs_route["assign_row"], rs_route["topk_gate"], None, yc)
         ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ce[0].record()
-        for _ in range(50):
-            moe.moe_unpermute_combine(c, yp, cr["assign_row"], cr["topk_gate"], None, yc)
+        for _ in range(10):
+            for yp, yc in sets:
+                moe.moe_unpermute_combine(c, yp, rs_route["assign_row"], rs_route["topk_gate"],
+                                          None, yc)
         ce[1].record()
         torch.cuda.synchronize()
-        comb_alone = ce[0].elapsed_time(ce[1]) * 1e3 / 50
-        del yp, yc
+        comb_alone = ce[0].elapsed_time(ce[1]) * 1e3 / (10 * comb_sets)
+        del sets
 
     # The same step from a cold last-level cache (256 MB on the MI355X): a
-    # 512 MiB fill before each step, every step timed by its own events on
-    # the launch stream, medians reported.  Not part of `value`.
+    # 512 MiB fill before each step, every step's kernels timed by their own
+    # events, medians reported.  Not part of `value`.
     cold = None
     if args.cold_steps > 0:
         junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_EVENTS)]
-               for _ in range(args.cold_steps)]
+        cev = new_events(args.cold_steps)
+        torch.cuda.synchronize()
         for i in range(args.cold_steps):
             junk.fill_(i & 0xFF)
             moe.moe_forward(c, weights, inp["x"], y, route, ws, events=cev[i])
         torch.cuda.synchronize()
         del junk
-
-        def median(v):
-            v = sorted(v)
-            return 0.5 * (v[(len(v) - 1) // 2] + v[len(v) // 2])
+        ck = stage_lists(cev)
         cold = {"steps": args.cold_steps,
-                "ms_per_step": round(median([es[0].elapsed_time(es[-1]) for es in cev]), 4)}
-        cold["tokens_per_s"] = round(cfg.T / (cold["ms_per_step"] * 1e-3), 1)
-        cold["stage_ms"] = {name: round(median([es[s].elapsed_time(es[s + 1]) for es in cev]), 5)
-                            for s, name in enumerate(moe.STAGE_NAMES)}
+                "kernel_span_ms": round(median([es[0].elapsed_time(es[2 * NS - 1])
+                                                for es in cev]), 4)}
+        cold["stage_ms"] = {name: round(median(v), 5) for name, v in ck.items()}
 
     # load-balance statistics of the last step's routing (not part of the
     # step): reads the logits once (T*E*4 bytes)
-    logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
-    route_lb = {"logits": logits, "expert_counts": counts}
-    moe.moe_forward(c, weights, inp["x"], y, route_lb, ws)
+    logits = rs_route["logits"]
     lb_out = [torch.empty(cfg.E, dtype=torch.float32, device=dev) for _ in range(2)]
     lb_loss = torch.empty(1, dtype=torch.float32, device=dev)
     for _ in range(3):
@@ -361,7 +403,6 @@ def main() -> int:
     if not args.no_backward:
         from moe_inputs import normal
         dy = normal((cfg.T, cfg.h), 1.0, cfg.seed, "dy", device=dev, dtype=cfg.dtype)
-        slots = cfg.E if args.routing == "expert_choice" else cfg.k
         full_route = {"logits": logits,
                       "topk_idx": torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev),
                       "topk_gate": torch.empty((cfg.T, slots), dtype=torch.float32, device=dev),
@@ -430,11 +471,13 @@ def main() -> int:
         for _ in range(2):
             moe.moe_forward(csk, weights, inp["x"], y, {"expert_counts": sk_counts}, wsk)
         nsk = max(3, K // 4)
-        skev = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_EVENTS)]
-                for _ in range(nsk)]
-        for es in skev:
-            for e in es:
-                e.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(nsk):
+            moe.moe_forward(csk, weights, inp["x"], y, {"expert_counts": sk_counts}, wsk)
+        torch.cuda.synchronize()
+        sk_ms = (time.perf_counter() - t1) * 1e3 / nsk
+        skev = new_events(nsk)
         torch.cuda.synchronize()
         for i in range(nsk):
             moe.moe_forward(csk, weights, inp["x"], y, {"expert_counts": sk_counts}, wsk,
@@ -442,22 +485,19 @@ def main() -> int:
         torch.cuda.synchronize()
         skc = sk_counts.cpu().tolist()
         sk = {"iters": args.sinkhorn_iters,
-              "ms_per_step": round(sum(es[0].elapsed_time(es[-1]) for es in skev) / nsk, 4),
-              "topk_stage_ms": round(sum(es[1].elapsed_time(es[2]) for es in skev) / nsk, 5),
+              "ms_per_step": round(sk_ms, 4),
+              "topk_stage_ms": round(sum(es[2].elapsed_time(es[3]) for es in skev) / nsk, 5),
               "max_over_mean_load": round(max(skc) * cfg.E / sum(skc), 3)}
         del wsk
 
-    stage_ms = {}
-    for s, name in enumerate(moe.STAGE_NAMES):
-        stage_ms[name] = sum(evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(K)) / K
     cnt = counts.cpu().tolist()
     kept = sum(min(n, C) for n in cnt) if C else sum(cnt)   # expert choice: E*C
     kept_all = kept + (cfg.T if cfg.shared else 0)
     ms_step = elapsed * 1e3 / K
-    g1 = gemm1_flops(kept_all, cfg.h, cfg.F) / (stage_ms["gemm1_swiglu"] * 1e-3) / 1e12
-    g2 = gemm2_flops(kept_all, cfg.h, cfg.F) / (stage_ms["gemm2"] * 1e-3) / 1e12
-    gg = expert_flops(kept_all, cfg.h, cfg.F) / (
-        (stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]) * 1e-3) / 1e12
+    g1_ms, g2_ms = stage_ms["gemm1_swiglu"], stage_ms["gemm2"]
+    g1 = gemm1_flops(kept_all, cfg.h, cfg.F) / (g1_ms * 1e-3) / 1e12
+    g2 = gemm2_flops(kept_all, cfg.h, cfg.F) / (g2_ms * 1e-3) / 1e12
+    gg = expert_flops(kept_all, cfg.h, cfg.F) / ((g1_ms + g2_ms) * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     # GEMM 1 is MFMA-bound when its flops per compulsory byte exceed the
     # ridge point peak / HBM bandwidth (312.5 flop/B for bf16), else bound by
@@ -466,23 +506,31 @@ def main() -> int:
     g1_bytes = gemm1_bytes(kept_e, cfg.T, cfg.h, cfg.F, esz, cfg.shared)
     g1_intensity = gemm1_flops(kept_all, cfg.h, cfg.F) / g1_bytes
     hbm_bound = cfg.dtype == "bf16" and g1_intensity < peak / PEAK_HBM_GBS * 1e3
-    g1_gbs = g1_bytes / (stage_ms["gemm1_swiglu"] * 1e-3) / 1e9
+    g1_gbs = g1_bytes / (g1_ms * 1e-3) / 1e9
     pb = permute_bytes(cfg.T, cfg.h, rows, esz)
     if args.routing == "expert_choice":      # a row gather: every row read and written
         pb = 2 * rows * cfg.h * esz
     cb = combine_bytes(kept, cfg.T, cfg.h, esz, cfg.shared)
     rb = router_bytes(cfg.T, cfg.h, cfg.E, esz)
-    router_gbs = rb / (stage_ms["router"] * 1e-3) / 1e9
-    perm_gbs = pb / (stage_ms["permute"] * 1e-3) / 1e9
-    comb_gbs = cb / (stage_ms["combine"] * 1e-3) / 1e9
-    wl = _workload_name(cfg, C, args.routing)
-    perm_tr = traced_kernel_us(wl, "permute") if args.routing == "topk" else None
-    comb_tr = traced_kernel_us(wl, "combine") if args.routing == "topk" else None
-    trace_frac = lambda nbytes, us: (None if us is None else  # noqa: E731
-                                     round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9          # noqa: E731
+    frac = lambda nbytes, ms: round(gbs(nbytes, ms) / PEAK_HBM_GBS, 4)  # noqa: E731
+    fcopy = lambda nbytes, ms: (None if copy_gbs is None else    # noqa: E731
+                                round(gbs(nbytes, ms) / copy_gbs, 4))
+
+    def hbm_stage(name, nbytes, extra=None):
+        d = {"kernel_us": round(stage_ms[name] * 1e3, 2),
+             "kernel_us_min": round(min(kern[name]) * 1e3, 2),
+             "gbs": round(gbs(nbytes, stage_ms[name]), 1), "frac_hbm": frac(nbytes, stage_ms[name]),
+             "frac_copy": fcopy(nbytes, stage_ms[name]), "bytes": nbytes}
+        if cold is not None:
+            cm = cold["stage_ms"][name]
+            d.update({"cold_kernel_us": round(cm * 1e3, 2), "cold_frac_hbm": frac(nbytes, cm)})
+        if extra:
+            d.update(extra)
+        return d
 
     out = {
-        "metric": METRIC,
+        "metric": metric_label(cfg.T, cfg.h, cfg.E, cfg.k),
         "value": round(cfg.T * K / elapsed, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -494,9 +542,10 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) tokens, fan-in-scaled N(0,1/fan_in) random weights)",
-        "config": {"workload": _workload_name(cfg, C, args.routing), "routing": args.routing, "T": cfg.T, "h": cfg.h, "E": cfg.E,
-                   "k": cfg.k, "F": cfg.F, "capacity": C, "gate": cfg.gate,
-                   "kept_rows": kept, "dispatch_rows": rows, "parallelism": "single GPU"},
+        "config": {"workload": _workload_name(cfg, C, args.routing), "routing": args.routing,
+                   "T": cfg.T, "h": cfg.h, "E": cfg.E, "k": cfg.k, "F": cfg.F, "capacity": C,
+                   "gate": cfg.gate, "kept_rows": kept, "dispatch_rows": rows,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm" if hbm_bound else ("mfma" if cfg.dtype == "bf16" else "alu"),
                      "kernel": "gemm1_swiglu",
                      "achieved": round(g1_gbs if hbm_bound else g1, 1),
@@ -505,22 +554,23 @@ def main() -> int:
                      "frac": round(g1_gbs / PEAK_HBM_GBS if hbm_bound else g1 / peak, 4),
                      "traffic": (measured_traffic(_workload_name(cfg, C))
                                  if args.routing == "topk" else None),
-                     "flop_per_byte": round(g1_intensity, 1)},
+                     "flop_per_byte": round(g1_intensity, 1),
+                     "kernel_ms": round(g1_ms, 5),
+                     "pass": (f"{K} steps after the timed ones, GEMM 1's kernels (grouped GEMM "
+                              "+ split-K reduce) timed by start/stop events bound to them")},
         "grouped_gemm": {"tflops": round(gg, 1), "frac_of_peak": round(gg / peak, 4),
-                         "gemm1_tflops": round(g1, 1), "gemm2_tflops": round(g2, 1)},
+                         "gemm1_tflops": round(g1, 1), "gemm2_tflops": round(g2, 1),
+                         "gemm1_frac": round(g1 / peak, 4), "gemm2_frac": round(g2 / peak, 4)},
+        "routing_stats": rstats,
         "hbm_copy_gbs": None if copy_gbs is None else round(copy_gbs, 1),
-        "router": {"gbs": round(router_gbs, 1), "frac_hbm": round(router_gbs / PEAK_HBM_GBS, 4),
-                   "frac_copy": None if copy_gbs is None else round(router_gbs / copy_gbs, 4), "bytes": rb},
-        "permute": {"gbs": round(perm_gbs, 1), "frac_hbm": round(perm_gbs / PEAK_HBM_GBS, 4),
-                    "frac_copy": None if copy_gbs is None else round(perm_gbs / copy_gbs, 4), "bytes": pb,
-                    "trace_us": perm_tr, "trace_frac_hbm": trace_frac(pb, perm_tr)},
-        "combine": {"gbs": round(comb_gbs, 1), "frac_hbm": round(comb_gbs / PEAK_HBM_GBS, 4),
-                    "frac_copy": None if copy_gbs is None else round(comb_gbs / copy_gbs, 4), "bytes": cb,
-                    "standalone_us": None if comb_alone is None else round(comb_alone, 2),
-                    "standalone_frac_hbm": (None if comb_alone is None else
-                                            round(cb / (comb_alone * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)),
-                    "trace_us": comb_tr, "trace_frac_hbm": trace_frac(cb, comb_tr)},
+        "router": hbm_stage("router", rb),
+        "permute": hbm_stage("permute", pb),
+        "combine": hbm_stage("combine", cb, {
+            "standalone_us": None if comb_alone is None else round(comb_alone, 2),
+            "standalone_frac_hbm": None if comb_alone is None else frac(cb, comb_alone * 1e-3),
+            "standalone_buffer_sets": comb_sets}),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "kernel_span_ms": round(kernel_span_ms, 4),
         "backward": (None if bwd is None else {
             "ms": round(bwd, 4),
             # 12*kept*h*F: dgrad and wgrad of both GEMMs; 18*kept*h*F counts

@@ -143,14 +143,16 @@ extern "C" {
 #define MOE_ROUTE_SINKHORN 3
 #define MOE_MAX_SINKHORN_ITERS 1000
 
-/* Kernels moe_forward launches, in order, each one a timed stage:
+/* Stages of moe_forward, in launch order, each one timed on request:
  *   0 router GEMM, 1 top-k + gates + chunk histogram (after the Sinkhorn
  *   iterations with SINKHORN routing), 2 scan (counts,
  *   offsets, GEMM tile table), 3 assign (ranks, rows), 4 permute copy,
- *   5 grouped GEMM 1 + SwiGLU, 6 grouped GEMM 2, 7 combine.
- * MOE_NUM_EVENTS events bracket them (see moe_forward).                   */
+ *   5 grouped GEMM 1 + SwiGLU (+ its split-K reduce), 6 grouped GEMM 2
+ *   (+ reduce), 7 combine.  (Routing variants launch their own kernels in
+ *   stages 1-4.)  MOE_NUM_EVENTS events, a start and a stop per stage, time
+ *   them (see moe_forward).                                                */
 #define MOE_NUM_STAGES 8
-#define MOE_NUM_EVENTS (MOE_NUM_STAGES + 1)
+#define MOE_NUM_EVENTS (2 * MOE_NUM_STAGES)
 
 typedef struct moe_cfg {
   int32_t struct_size; /* sizeof(moe_cfg_t) */
@@ -386,8 +388,15 @@ int moe_backward_saved(const moe_cfg_t* cfg, const moe_weights_t* w, const void*
  *   x [T,h]  in;  y [T,h] out
  *   route    optional extra outputs (host struct of device pointers) or NULL
  *   events   NULL, or MOE_NUM_EVENTS hipEvent_t (as void*) created by the
- *            caller; event i is recorded on `stream` before stage i and the
- *            last one after the final stage, for per-stage timing.        */
+ *            caller with timing enabled, for per-stage kernel timing:
+ *            events[2i] is bound to the start of stage i's first kernel and
+ *            events[2i+1] to the end of its last kernel (hipExtLaunchKernel
+ *            start/stop events, taken from the kernels' own timestamps), so
+ *            hipEventElapsedTime(events[2i], events[2i+1]) is the stage's
+ *            kernel time and (events[0], events[2*MOE_NUM_STAGES-1]) spans
+ *            the layer from its first kernel's start to its last kernel's
+ *            end.  A stage that launches nothing records both events on
+ *            `stream` at that point (an empty interval).                    */
 int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
                 void* y, const moe_route_out_t* route, void* ws,
                 size_t ws_bytes, void* const* events, void* stream);

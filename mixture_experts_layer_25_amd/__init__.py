@@ -31,7 +31,7 @@ MOE_GATE_SOFTMAX_ALL_TOPK = 1
 MOE_GATE_SIGMOID_TOPK_NORM = 2
 
 MOE_NUM_STAGES = 8
-MOE_NUM_EVENTS = MOE_NUM_STAGES + 1
+MOE_NUM_EVENTS = 2 * MOE_NUM_STAGES     # a start and a stop event per stage
 STAGE_NAMES = ("router", "topk", "scan", "assign", "permute", "gemm1_swiglu",
                "gemm2", "combine")
 
@@ -383,7 +383,10 @@ def moe_forward(cfg, weights: dict, x, y, route: Optional[dict] = None, ws=None,
     output tensors (logits, topk_idx, topk_gate, expert_counts,
     expert_offsets, assign_row, row_token; probs for expert choice,
     route_bias for Sinkhorn routing).  ``events``: None or
-    MOE_NUM_EVENTS ``torch.cuda.Event(enable_timing=True)``."""
+    MOE_NUM_EVENTS ``torch.cuda.Event(enable_timing=True)``: events[2i] and
+    events[2i+1] are bound to the start of stage i's first kernel and the end
+    of its last kernel (``events[2*i].elapsed_time(events[2*i+1])`` is the
+    stage's kernel time in ms)."""
     wp, wb = _ws(ws)
     z = _sizes(cfg)
     ws_struct = weights_struct(weights, cfg)

@@ -446,25 +446,25 @@ inline int vec_of(int dtype) { return dtype == 1 ? 8 : 4; }
 #define MOE_BY_DTYPE(DT, KERNEL, GRID, ...)                                         \
   do {                                                                              \
     if ((DT) == 1)                                                                  \
-      hipLaunchKernelGGL(KERNEL<uint16_t>, GRID, dim3(256), 0, s, __VA_ARGS__);     \
+      MOE_LAUNCH(KERNEL<uint16_t>, GRID, dim3(256), 0, s, __VA_ARGS__);     \
     else                                                                            \
-      hipLaunchKernelGGL(KERNEL<float>, GRID, dim3(256), 0, s, __VA_ARGS__);        \
+      MOE_LAUNCH(KERNEL<float>, GRID, dim3(256), 0, s, __VA_ARGS__);        \
   } while (0)
 
 hipError_t launch_transpose(int dtype, const void* src, int64_t src_bs, int R, int Cc, void* dst,
                             int64_t dst_bs, int dld, int col0, int batches, hipStream_t s) {
   const dim3 grid(Cc / kTr, R / kTr, batches);
   if (dtype == 1)
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)src,
+    MOE_LAUNCH(transpose_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)src,
                        src_bs, R, Cc, (uint16_t*)dst, dst_bs, dld, col0);
   else
-    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, (const float*)src, src_bs,
+    MOE_LAUNCH(transpose_kernel<float>, grid, dim3(256), 0, s, (const float*)src, src_bs,
                        R, Cc, (float*)dst, dst_bs, dld, col0);
   return hipGetLastError();
 }
 
 hipError_t launch_ktab(const int32_t* gtab, int G, int use_a_rows, int32_t* kt, hipStream_t s) {
-  hipLaunchKernelGGL(ktab_kernel, dim3(1), dim3(1024), 0, s, gtab, G, use_a_rows, kt);
+  MOE_LAUNCH(ktab_kernel, dim3(1), dim3(1024), 0, s, gtab, G, use_a_rows, kt);
   return hipGetLastError();
 }
 
@@ -474,11 +474,11 @@ hipError_t launch_transpose_groups(int dtype, const void* src, int sld, const vo
                                    hipStream_t s) {
   const dim3 grid(Cc / kTr, (unsigned)((ktot_bound + kTr - 1) / kTr));
   if (dtype == 1)
-    hipLaunchKernelGGL(transpose_groups_kernel<uint16_t>, grid, dim3(256), 0, s,
+    MOE_LAUNCH(transpose_groups_kernel<uint16_t>, grid, dim3(256), 0, s,
                        (const uint16_t*)src, sld, (const uint16_t*)src_shared, sld_shared,
                        E_routed, kt, G, Cc, (uint16_t*)dst, dld);
   else
-    hipLaunchKernelGGL(transpose_groups_kernel<float>, grid, dim3(256), 0, s, (const float*)src,
+    MOE_LAUNCH(transpose_groups_kernel<float>, grid, dim3(256), 0, s, (const float*)src,
                        sld, (const float*)src_shared, sld_shared, E_routed, kt, G, Cc,
                        (float*)dst, dld);
   return hipGetLastError();
@@ -528,7 +528,7 @@ hipError_t launch_router_bwd(int dtype, const float* logits, const int32_t* idx,
                              const float* gate, const float* dg, int gate_mode, int64_t T, int E,
                              int k, const void* x, int h, float* dl, float* rpart,
                              void* dw_router, float* dlogit_bias, hipStream_t s) {
-  hipLaunchKernelGGL(gates_bwd_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s,
+  MOE_LAUNCH(gates_bwd_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s,
                      logits, idx, gate, dg, gate_mode, T, E, k, dl);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -537,24 +537,24 @@ hipError_t launch_router_bwd(int dtype, const float* logits, const int32_t* idx,
     const int slices = (int)((T + tc - 1) / tc);
     const dim3 grid(h / 64, (E + kRbE - 1) / kRbE, slices);
     if (dtype == 1)
-      hipLaunchKernelGGL(router_wgrad_kernel<uint16_t>, grid, dim3(256), 0, s, dl,
+      MOE_LAUNCH(router_wgrad_kernel<uint16_t>, grid, dim3(256), 0, s, dl,
                          (const uint16_t*)x, T, h, E, tc, rpart);
     else
-      hipLaunchKernelGGL(router_wgrad_kernel<float>, grid, dim3(256), 0, s, dl, (const float*)x,
+      MOE_LAUNCH(router_wgrad_kernel<float>, grid, dim3(256), 0, s, dl, (const float*)x,
                          T, h, E, tc, rpart);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t n = (int64_t)E * h;
     const dim3 g2((unsigned)((n + 255) / 256));
     if (dtype == 1)
-      hipLaunchKernelGGL(router_wgrad_sum_kernel<uint16_t>, g2, dim3(256), 0, s, rpart, slices, n,
+      MOE_LAUNCH(router_wgrad_sum_kernel<uint16_t>, g2, dim3(256), 0, s, rpart, slices, n,
                          (uint16_t*)dw_router);
     else
-      hipLaunchKernelGGL(router_wgrad_sum_kernel<float>, g2, dim3(256), 0, s, rpart, slices, n,
+      MOE_LAUNCH(router_wgrad_sum_kernel<float>, g2, dim3(256), 0, s, rpart, slices, n,
                          (float*)dw_router);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (dlogit_bias) {
-    hipLaunchKernelGGL(bias_grad_kernel, dim3(E), dim3(256), 0, s, dl, T, E, dlogit_bias);
+    MOE_LAUNCH(bias_grad_kernel, dim3(E), dim3(256), 0, s, dl, T, E, dlogit_bias);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;
@@ -565,11 +565,11 @@ hipError_t launch_dx_final(int dtype, const void* dxp, int ldp, const int32_t* a
                            int64_t T, int h, int E, void* dx, hipStream_t s) {
   const dim3 grid(h / 64, (unsigned)((T + kDxTok - 1) / kDxTok));
   if (dtype == 1)
-    hipLaunchKernelGGL(dx_final_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)dxp,
+    MOE_LAUNCH(dx_final_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)dxp,
                        (int64_t)ldp, assign_row, k, rows, has_shared, dl,
                        (const uint16_t*)w_router, T, h, E, (uint16_t*)dx);
   else
-    hipLaunchKernelGGL(dx_final_kernel<float>, grid, dim3(256), 0, s, (const float*)dxp,
+    MOE_LAUNCH(dx_final_kernel<float>, grid, dim3(256), 0, s, (const float*)dxp,
                        (int64_t)ldp, assign_row, k, rows, has_shared, dl, (const float*)w_router,
                        T, h, E, (float*)dx);
   return hipGetLastError();

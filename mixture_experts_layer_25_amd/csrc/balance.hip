@@ -103,7 +103,7 @@ template <int G, int NPL>
 void launch_probsum_t(const float* logits, int gate, int64_t T, int E, float* partial,
                       float* probs_et, hipStream_t st) {
   const int64_t nwg = (T + 4 * (256 / G) - 1) / (4 * (256 / G));
-  hipLaunchKernelGGL((probsum_kernel<G, NPL>), dim3((unsigned)nwg), dim3(256), 0, st, logits,
+  MOE_LAUNCH((probsum_kernel<G, NPL>), dim3((unsigned)nwg), dim3(256), 0, st, logits,
                      gate, T, E, partial, probs_et);
 }
 
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void select_bias_update_kernel(const int32_t* 
 
 hipError_t launch_select_bias_update(const int32_t* counts, int64_t T, int E, int k, float gamma,
                                      float* bias, hipStream_t st) {
-  hipLaunchKernelGGL(select_bias_update_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0,
+  MOE_LAUNCH(select_bias_update_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0,
                      st, counts, T, E, k, gamma, bias);
   return hipGetLastError();
 }
@@ -209,7 +209,7 @@ hipError_t launch_load_balance(const float* logits, const int32_t* counts, int g
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t ngroups = (T + topk_tokens_per_wg(E) - 1) / topk_tokens_per_wg(E);
-  hipLaunchKernelGGL(balance_final_kernel, dim3(1), dim3(1024), 0, st, partial, ngroups, counts,
+  MOE_LAUNCH(balance_final_kernel, dim3(1), dim3(1024), 0, st, partial, ngroups, counts,
                      T, E, k, alpha, f, P, loss);
   return hipGetLastError();
 }

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kSelThreads) void score_drop_kernel(
 
 hipError_t launch_expert_choice(const float* probs_et, int64_t T, int E, int C, int32_t* sel_row,
                                 float* gate_te, int32_t* row_token, hipStream_t s) {
-  hipLaunchKernelGGL(expert_choice_kernel, dim3((unsigned)E), dim3(kSelThreads), 0, s, probs_et, T, E, C,
+  MOE_LAUNCH(expert_choice_kernel, dim3((unsigned)E), dim3(kSelThreads), 0, s, probs_et, T, E, C,
                      sel_row, gate_te, row_token);
   return hipGetLastError();
 }
@@ -212,11 +212,11 @@ hipError_t launch_score_drop(const int32_t* idx, const float* gate, const int32_
                              uint64_t* key_dl, int32_t* aid_dl, int32_t* assign_row,
                              int32_t* row_token, hipStream_t s) {
   const int64_t n = T * k;
-  hipLaunchKernelGGL(score_keys_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx,
+  MOE_LAUNCH(score_keys_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx,
                      gate, assign_dl, offsets_dl, n, E, key_dl, aid_dl);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(score_drop_kernel, dim3((unsigned)E), dim3(kSelThreads), 0, s, key_dl, aid_dl,
+  MOE_LAUNCH(score_drop_kernel, dim3((unsigned)E), dim3(kSelThreads), 0, s, key_dl, aid_dl,
                      offsets_dl, k, C, assign_row, row_token);
   return hipGetLastError();
 }

@@ -219,11 +219,11 @@ void launch_combine_t(int dtype, const void* yp, int ld, const int32_t* ar, cons
                       hipStream_t s) {
   const int64_t nb = (T + kCombTok - 1) / kCombTok;
   if (dtype == 1)
-    hipLaunchKernelGGL((combine_bf16_kernel<KMAX>), dim3((unsigned)nb), dim3(256), 0, s,
+    MOE_LAUNCH((combine_bf16_kernel<KMAX>), dim3((unsigned)nb), dim3(256), 0, s,
                        (const uint4*)yp, (int64_t)ld / 8, ar, g, (const uint4*)sy, (uint4*)y, T,
                        h / 8, k, nrows);
   else
-    hipLaunchKernelGGL((combine_f32_kernel<KMAX>), dim3((unsigned)nb), dim3(256), 0, s,
+    MOE_LAUNCH((combine_f32_kernel<KMAX>), dim3((unsigned)nb), dim3(256), 0, s,
                        (const float4*)yp, (int64_t)ld / 4, ar, g, (const float4*)sy, (float4*)y,
                        T, h / 4, k, nrows);
 }
@@ -245,10 +245,10 @@ hipError_t launch_combine(int dtype, const void* y_perm, int ld_perm,
   else if (k <= 16)
     launch_combine_t<16>(dtype, y_perm, ld_perm, assign_row, gate, shared_y, y, T, h, k, (int)nrows, s);
   else if (dtype == 1)
-    hipLaunchKernelGGL(combine_sparse_kernel<true>, dim3((unsigned)T), dim3(256), 0, s, y_perm,
+    MOE_LAUNCH(combine_sparse_kernel<true>, dim3((unsigned)T), dim3(256), 0, s, y_perm,
                        (int64_t)ld_perm / 8, assign_row, gate, shared_y, y, T, h / 8, k, (int)nrows);
   else
-    hipLaunchKernelGGL(combine_sparse_kernel<false>, dim3((unsigned)T), dim3(256), 0, s, y_perm,
+    MOE_LAUNCH(combine_sparse_kernel<false>, dim3((unsigned)T), dim3(256), 0, s, y_perm,
                        (int64_t)ld_perm / 4, assign_row, gate, shared_y, y, T, h / 4, k, (int)nrows);
   return hipGetLastError();
 }

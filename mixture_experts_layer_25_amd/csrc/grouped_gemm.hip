@@ -853,17 +853,17 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, const GroupedGemmArgs& a,
                                 : a.max_m_tiles * NT + (a.partials ? a.num_cu : 0);
     if (nb <= 0) return hipSuccess;
     if (swiglu)
-      hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, a);
+      MOE_LAUNCH(gemm_bf16_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, a);
+      MOE_LAUNCH(gemm_bf16_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, a);
     if (a.partials && !a.kgroup) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       // one workgroup per possible split tile (fewer than num_cu)
       if (swiglu)
-        hipLaunchKernelGGL(gemm_bf16_reduce_kernel<true>, dim3((unsigned)a.num_cu), dim3(256), 0, s, a);
+        MOE_LAUNCH(gemm_bf16_reduce_kernel<true>, dim3((unsigned)a.num_cu), dim3(256), 0, s, a);
       else
-        hipLaunchKernelGGL(gemm_bf16_reduce_kernel<false>, dim3((unsigned)a.num_cu), dim3(256), 0, s, a);
+        MOE_LAUNCH(gemm_bf16_reduce_kernel<false>, dim3((unsigned)a.num_cu), dim3(256), 0, s, a);
     }
   } else {
     const int NT = a.N / FBN;
@@ -871,9 +871,9 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, const GroupedGemmArgs& a,
                                 : a.max_m_tiles * NT;
     if (nb <= 0) return hipSuccess;
     if (swiglu)
-      hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, a);
+      MOE_LAUNCH(gemm_f32_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, a);
+      MOE_LAUNCH(gemm_f32_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -307,26 +307,17 @@ MOE_API int moe_permute(const moe_cfg_t* cfg, const void* x, const int32_t* topk
   return MOE_OK;
 }
 
-MOE_API int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
-                                    const int32_t* expert_counts,
-                                    const int32_t* expert_offsets, const void* w1,
-                                    const void* w3, const void* w2, void* act,
-                                    void* y_perm, void* ws, size_t ws_bytes,
-                                    void* stream) {
-  int st = check_cfg(cfg);
-  if (st != MOE_OK) return st;
-  const moe_cfg_t& c = *cfg;
-  if (c.T == 0) return MOE_OK;
-  if (!x_perm || !expert_counts || !expert_offsets || !w1 || !w3 || !w2 || !act || !y_perm)
-    return MOE_ERR_INVALID_ARG;
-  if (misaligned(x_perm, expert_counts, expert_offsets, w1, w3, w2, act, y_perm, ws))
-    return MOE_ERR_INVALID_ARG;
-  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
-  const hipStream_t s = (hipStream_t)stream;
-  const Layout L = layout_of(c);
+namespace {
+
+// The standalone grouped GEMM (both entry points): groups from the caller's
+// counts and offsets into the tile table `gtab` (gtab_ints(E) ints), split-K
+// partial tiles (bf16) in `partials` (kSplitPartialFloats floats).
+int grouped_gemm_impl(const moe_cfg_t& c, const void* x_perm, const int32_t* expert_counts,
+                      const int32_t* expert_offsets, const void* w1, const void* w3,
+                      const void* w2, void* act, void* y_perm, int32_t* gtab, float* partials,
+                      hipStream_t s) {
   const int BM = row_tile(c);
   const int64_t rows = rows_of(c);
-  int32_t* gtab = at<int32_t>(ws, L.gtab);
   MOE_TRY(moe::launch_gtab(expert_counts, expert_offsets, c.E, BM, (int)rows, gtab, s));
   moe::GroupedGemmArgs a{};
   a.A = x_perm;
@@ -345,7 +336,8 @@ MOE_API int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
   a.E_routed = c.E;
   a.a_from_out_rows = 0;
   a.max_m_tiles = max_m_tiles(rows, c.E, BM);
-  set_split(a, c, ws, L);
+  a.num_cu = device_cus();
+  a.partials = c.dtype == MOE_DTYPE_BF16 ? partials : nullptr;
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, true, a, s));
   a.A = act;
   a.B0 = w2;
@@ -358,6 +350,38 @@ MOE_API int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
   a.a_from_out_rows = 1;
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
   return MOE_OK;
+}
+
+int check_gemm_args(const moe_cfg_t* cfg, const void* x_perm, const int32_t* expert_counts,
+                    const int32_t* expert_offsets, const void* w1, const void* w3,
+                    const void* w2, const void* act, const void* y_perm) {
+  const int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x_perm || !expert_counts || !expert_offsets || !w1 || !w3 || !w2 || !act || !y_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (misaligned(x_perm, expert_counts, expert_offsets, w1, w3, w2, act, y_perm))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
+                                    const int32_t* expert_counts,
+                                    const int32_t* expert_offsets, const void* w1,
+                                    const void* w3, const void* w2, void* act,
+                                    void* y_perm, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  int st = check_gemm_args(cfg, x_perm, expert_counts, expert_offsets, w1, w3, w2, act, y_perm);
+  if (st != MOE_OK || cfg->T == 0) return st;
+  const moe_cfg_t& c = *cfg;
+  if (misaligned(ws)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(c, ws, ws_bytes)) != MOE_OK) return st;
+  const Layout L = layout_of(c);
+  return grouped_gemm_impl(c, x_perm, expert_counts, expert_offsets, w1, w3, w2, act, y_perm,
+                           at<int32_t>(ws, L.gtab), at<float>(ws, L.partials),
+                           (hipStream_t)stream);
 }
 
 MOE_API int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
@@ -730,8 +754,27 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   const int64_t nch = (c.T + hg - 1) / hg;
   const int64_t rows = rows_of(c);
   const int BM = row_tile(c);
-  auto mark = [&](int i) -> hipError_t {
-    return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
+  // Stage timing: while stage i runs, its first kernel carries
+  // events[2i] and every kernel events[2i+1] (bound to the kernels; see
+  // moe::StageEvents).  A stage that launched nothing gets an empty interval.
+  moe::StageEvents sev{};
+  int stage = -1;
+  struct ClearStage {
+    ~ClearStage() { moe::stage_events() = nullptr; }
+  } clear_stage_on_return;
+  auto mark = [&](int i) -> hipError_t {   // stage i begins; i == MOE_NUM_STAGES: all done
+    if (!events) return hipSuccess;
+    moe::stage_events() = nullptr;
+    if (stage >= 0 && sev.launched == 0) {
+      hipError_t e = hipEventRecord((hipEvent_t)events[2 * stage], s);
+      if (e == hipSuccess) e = hipEventRecord((hipEvent_t)events[2 * stage + 1], s);
+      if (e != hipSuccess) return e;
+    }
+    if (i >= MOE_NUM_STAGES) return hipSuccess;
+    stage = i;
+    sev = moe::StageEvents{(hipEvent_t)events[2 * i], (hipEvent_t)events[2 * i + 1], 0};
+    moe::stage_events() = &sev;
+    return hipSuccess;
   };
 
   const bool ec = c.routing == MOE_ROUTE_EXPERT_CHOICE;

@@ -1,12 +1,44 @@
 // Internal launchers of the libmoe kernels (host side, not part of the ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "moe_device.h"
 
 namespace moe {
+
+// Timing of one stage of a timed moe_forward call: the first kernel the
+// stage launches takes `start` and every kernel takes `stop`, bound to the
+// kernels themselves (hipExtLaunchKernel), so the pair spans the stage's
+// kernels from the first one's start to the last one's end, without the
+// gaps of separately recorded markers.  Set for the duration of one stage
+// on the calling thread only; NULL otherwise.
+struct StageEvents {
+  hipEvent_t start, stop;
+  int launched;   // kernels launched in the stage so far
+};
+
+inline StageEvents*& stage_events() {
+  static thread_local StageEvents* cur = nullptr;
+  return cur;
+}
+
+// Every kernel launch of the library goes through this: a plain launch, or
+// one carrying the current stage's events.
+#define MOE_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                \
+  do {                                                                                   \
+    ::moe::StageEvents* moe_ev_ = ::moe::stage_events();                                 \
+    if (moe_ev_) {                                                                       \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM,                          \
+                            moe_ev_->launched ? nullptr : moe_ev_->start, moe_ev_->stop, \
+                            0u, __VA_ARGS__);                                            \
+      ++moe_ev_->launched;                                                               \
+    } else {                                                                             \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);               \
+    }                                                                                    \
+  } while (0)
 
 // Tile table written by the scan kernels and read by the grouped GEMMs.
 // For G groups it holds 4*G+1 int32:

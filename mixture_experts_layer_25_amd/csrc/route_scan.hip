@@ -267,7 +267,7 @@ void launch_assign_t(const int32_t* idx, const int32_t* base, int gpc, const int
                      int64_t T, int E, int k, int nbits, int64_t C, int32_t* ar,
                      int32_t* rt, hipStream_t s) {
   const int64_t nch = (T + kChunkTokens - 1) / kChunkTokens;
-  hipLaunchKernelGGL((assign_kernel<KMAX>), dim3((unsigned)nch), dim3(256), 0, s,
+  MOE_LAUNCH((assign_kernel<KMAX>), dim3((unsigned)nch), dim3(256), 0, s,
                      idx, base, gpc, off, T, E, k, nbits, C, ar, rt);
 }
 
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
 
 hipError_t launch_fixed_groups(int E, int C, int64_t T, int has_shared, int BM, int32_t* counts,
                                int32_t* offsets, int32_t* gtab, hipStream_t s) {
-  hipLaunchKernelGGL(fixed_groups_kernel, dim3(1), dim3(1024), 0, s, E, C, T, has_shared, BM,
+  MOE_LAUNCH(fixed_groups_kernel, dim3(1), dim3(1024), 0, s, E, C, T, has_shared, BM,
                      counts, offsets, gtab);
   return hipGetLastError();
 }
@@ -391,7 +391,7 @@ hipError_t launch_fixed_groups(int E, int C, int64_t T, int has_shared, int BM, 
 hipError_t launch_groups_from_counts(const int32_t* counts, const int32_t* offsets, int E,
                                      int64_t C, int64_t T, int has_shared, int BM,
                                      int64_t rows, int32_t* gtab, hipStream_t s) {
-  hipLaunchKernelGGL(groups_from_counts_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E,
+  MOE_LAUNCH(groups_from_counts_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E,
                      C, T, has_shared, BM, rows, gtab);
   return hipGetLastError();
 }
@@ -400,7 +400,7 @@ hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token
                               int64_t T, int h, void* x_perm, int ld_perm, hipStream_t s) {
   const int esz = dtype == 1 ? 2 : 4;
   const int64_t nb = (rows + kPermTok - 1) / kPermTok;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)nb), dim3(256), 0, s, (const uint4*)x,
+  MOE_LAUNCH(gather_rows_kernel, dim3((unsigned)nb), dim3(256), 0, s, (const uint4*)x,
                      row_token, rows, T, h * esz / 16, (uint4*)x_perm,
                      (int64_t)ld_perm * esz / 16);
   return hipGetLastError();
@@ -409,7 +409,7 @@ hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token
 hipError_t launch_hist(const int32_t* idx, int64_t T, int E, int k,
                        int32_t* chunk_hist, hipStream_t s) {
   const int64_t nch = (T + kChunkTokens - 1) / kChunkTokens;
-  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nch), dim3(256), 0, s, idx, T,
+  MOE_LAUNCH(hist_kernel, dim3((unsigned)nch), dim3(256), 0, s, idx, T,
                      E, k, chunk_hist);
   return hipGetLastError();
 }
@@ -418,14 +418,14 @@ hipError_t launch_scan(const int32_t* chunk_hist, int64_t nch, int E, int64_t C,
                        int64_t T, int k, int has_shared, int BM,
                        int32_t* chunk_base, int32_t* counts, int32_t* offsets,
                        int32_t* gtab, hipStream_t s) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_hist, nch, E,
+  MOE_LAUNCH(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_hist, nch, E,
                      C, T, k, has_shared, BM, chunk_base, counts, offsets, gtab);
   return hipGetLastError();
 }
 
 hipError_t launch_gtab(const int32_t* counts, const int32_t* offsets, int E,
                        int BM, int rows, int32_t* gtab, hipStream_t s) {
-  hipLaunchKernelGGL(gtab_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E,
+  MOE_LAUNCH(gtab_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E,
                      BM, rows, gtab);
   return hipGetLastError();
 }
@@ -459,7 +459,7 @@ hipError_t launch_permute(int dtype, const void* x, const int32_t* assign_row,
   const int64_t pv = (int64_t)ld_perm * esz / 16;
   const int64_t ntb = (T + kPermTok - 1) / kPermTok;
   const int64_t nb = ntb + (C > 0 ? kPadBlocks : 0);
-  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)nb), dim3(256), 0, s,
+  MOE_LAUNCH(permute_kernel, dim3((unsigned)nb), dim3(256), 0, s,
                      (const uint4*)x, assign_row, counts, T, nv, E, k, C, ntb,
                      (uint4*)x_perm, pv, row_token);
   return hipGetLastError();

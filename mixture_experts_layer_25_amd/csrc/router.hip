@@ -203,17 +203,17 @@ hipError_t launch_router(int dtype, const void* x, const void* w_router,
                          int h, int E, hipStream_t s) {
   if (dtype == 1 && E > 16) {
     const dim3 grid((unsigned)((T + kTileT - 1) / kTileT), (unsigned)((E + kTileE - 1) / kTileE));
-    hipLaunchKernelGGL(router_bf16_tile_kernel, grid, dim3(256), 0, s,
+    MOE_LAUNCH(router_bf16_tile_kernel, grid, dim3(256), 0, s,
                        (const uint16_t*)x, (const uint16_t*)w_router,
                        logit_bias, logits, T, h, E);
   } else if (dtype == 1) {
     const int64_t nb = (T + kRouterTok - 1) / kRouterTok;
-    hipLaunchKernelGGL(router_bf16_kernel, dim3((unsigned)nb), dim3(64 * router_waves(h)), 0, s,
+    MOE_LAUNCH(router_bf16_kernel, dim3((unsigned)nb), dim3(64 * router_waves(h)), 0, s,
                        (const uint16_t*)x, (const uint16_t*)w_router,
                        logit_bias, logits, T, h, E);
   } else {
     const int64_t nb = (T * E + 255) / 256;
-    hipLaunchKernelGGL(router_f32_kernel, dim3((unsigned)nb), dim3(256), 0, s,
+    MOE_LAUNCH(router_f32_kernel, dim3((unsigned)nb), dim3(256), 0, s,
                        (const float*)x, (const float*)w_router, logit_bias,
                        logits, T, h, E);
   }

@@ -203,13 +203,13 @@ hipError_t launch_steps(const float* logits, int64_t T, int E, int iters, float2
   float2* buf[2] = {parts, parts + (int64_t)B * E};
   const size_t lds = (size_t)((E + 1) & ~1) * 4 + (size_t)kSkWaves * E * 8;   // <= 132 KiB
   for (int it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL((sinkhorn_step_kernel<G, NPL>), dim3(B), dim3(kSkThreads), lds, st, logits,
+    MOE_LAUNCH((sinkhorn_step_kernel<G, NPL>), dim3(B), dim3(kSkThreads), lds, st, logits,
                        it ? (const float2*)buf[(it - 1) & 1] : nullptr, buf[it & 1], T, E, tpb,
                        ln_cols);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(sinkhorn_finish_kernel, dim3(1), dim3(kSkThreads), 0, st,
+  MOE_LAUNCH(sinkhorn_finish_kernel, dim3(1), dim3(kSkThreads), 0, st,
                      (const float2*)buf[(iters - 1) & 1], B, E, ln_cols, bias);
   return hipGetLastError();
 }

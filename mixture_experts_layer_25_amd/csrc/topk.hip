@@ -129,7 +129,7 @@ void launch_topk_t(const float* logits, const float* sb, int gate, int64_t T,
                    int E, int k, int32_t* idx, float* g, int32_t* hist,
                    hipStream_t s) {
   const int64_t nwg = (T + 4 * (256 / G) - 1) / (4 * (256 / G));
-  hipLaunchKernelGGL((topk_kernel<G, NPL>), dim3((unsigned)nwg), dim3(256), 0,
+  MOE_LAUNCH((topk_kernel<G, NPL>), dim3((unsigned)nwg), dim3(256), 0,
                      s, logits, sb, gate, T, E, k, idx, g, hist);
 }
 
