@@ -14,17 +14,23 @@ DEV = "cuda"
 
 class LazyExperts:
     """Per-expert fp32 numpy view of a [E, ...] device tensor, fetched on use,
-    so the oracle only pulls the experts it needs."""
+    so the oracle only pulls the experts it needs.  cache=False fetches on
+    every use and keeps nothing (the oracle's forward touches each expert
+    once; a 256-expert layer would otherwise hold tens of GB of fp32)."""
 
-    def __init__(self, t: torch.Tensor):
+    def __init__(self, t: torch.Tensor, cache: bool = True):
         self.t = t
+        self.keep = cache
         self.cache = {}
 
     def __getitem__(self, e):
         e = int(e)
-        if e not in self.cache:
-            self.cache[e] = self.t[e].float().cpu().numpy()
-        return self.cache[e]
+        if e in self.cache:
+            return self.cache[e]
+        v = self.t[e].float().cpu().numpy()
+        if self.keep:
+            self.cache[e] = v
+        return v
 
 
 def np32(t: torch.Tensor) -> np.ndarray:
@@ -98,7 +104,8 @@ def oracle_weights(cfg: MoEConfig, inp: dict):
 
 
 def oracle_forward(cfg: MoEConfig, inp: dict, C_ref, tokens=None, idx=None,
-                   maps_only=False, drop="token", priority=None, sinkhorn_iters=None):
+                   maps_only=False, drop="token", priority=None, sinkhorn_iters=None,
+                   cache_experts=True):
     x = np32(inp["x"])
     wr = np32(inp["w_router"])
     lb = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
@@ -106,9 +113,8 @@ def oracle_forward(cfg: MoEConfig, inp: dict, C_ref, tokens=None, idx=None,
     shared = None
     if cfg.shared and not maps_only:
         shared = (np32(inp["ws1"]), np32(inp["ws3"]), np32(inp["ws2"]))
-    w1 = LazyExperts(inp["w1"]) if inp["w1"] is not None else None
-    w3 = LazyExperts(inp["w3"]) if inp["w3"] is not None else None
-    w2 = LazyExperts(inp["w2"]) if inp["w2"] is not None else None
+    lz = lambda t: None if t is None else LazyExperts(t, cache_experts)  # noqa: E731
+    w1, w3, w2 = lz(inp["w1"]), lz(inp["w3"]), lz(inp["w2"])
     return oracle.moe_forward(x, wr, w1, w3, w2, k=cfg.k, gate=cfg.gate, C=C_ref,
                               logit_bias=lb, select_bias=sb, shared=shared,
                               tokens=tokens, idx=idx, maps_only=maps_only, drop=drop,
@@ -165,6 +171,41 @@ def check_routing(cfg: MoEConfig, gpu: dict, ref: dict, C_ref, inp: dict,
 def rel_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
     """max |y_gpu - y_ref| / max |y_ref| (normwise max relative error)."""
     return float(np.abs(y_gpu.astype(np.float64) - y_ref).max() / np.abs(y_ref).max())
+
+
+def token_rel_err(y_gpu: np.ndarray, y_ref: np.ndarray):
+    """Per-token normwise error: for each row t, max_i |y_gpu - y_ref| over
+    max_i |y_ref| of that row alone.  Rows whose reference is exactly zero
+    (every slot dropped, no shared expert) are returned separately: their
+    output must be exactly zero, which ``assert_dropped_rows_zero`` checks.
+    Returns (max over the non-zero rows, index of that row, zero-row mask)."""
+    d = np.abs(y_gpu.astype(np.float64) - y_ref).max(1)
+    m = np.abs(y_ref).max(1)
+    zero = m == 0
+    r = np.where(zero, 0.0, d / np.where(zero, 1.0, m))
+    i = int(r.argmax()) if len(r) else 0
+    return (float(r[i]) if len(r) else 0.0), i, zero
+
+
+def assert_dropped_rows_zero(y_gpu: np.ndarray, zero_rows: np.ndarray) -> int:
+    """Rows whose every slot was dropped (and no shared expert) carry no
+    expert output at all: each element must be exactly +0.0 or -0.0."""
+    if zero_rows.any():
+        bad = np.count_nonzero(y_gpu[zero_rows] != 0)
+        assert bad == 0, f"{bad} elements of fully dropped tokens are not zero"
+    return int(zero_rows.sum())
+
+
+def check_outputs(cfg: MoEConfig, y_gpu: np.ndarray, y_ref: np.ndarray, label: str) -> dict:
+    """The output bars: normwise over all compared rows and per token, both
+    within the layer's tolerance; fully dropped rows exactly zero."""
+    tol = tol_of(cfg)
+    err = rel_err(y_gpu, y_ref) if np.abs(y_ref).max() > 0 else float(np.abs(y_gpu).max())
+    terr, worst, zero = token_rel_err(y_gpu, y_ref)
+    nzero = assert_dropped_rows_zero(y_gpu, zero)
+    assert err <= tol, f"{label}: normwise error {err:.3e} > {tol}"
+    assert terr <= tol, f"{label}: token {worst} error {terr:.3e} > {tol}"
+    return {"rel_err": f"{err:.2e}", "token_rel_err": f"{terr:.2e}", "zero_rows": nzero}
 
 
 def tol_of(cfg: MoEConfig) -> float:
