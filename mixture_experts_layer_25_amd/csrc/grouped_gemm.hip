@@ -10,7 +10,13 @@
 // Every operand is K-contiguous (weights stored [out,in]), so both GEMMs are
 // C = A · B^T with 16-byte loads along K for A and B alike.
 //
-// bf16 kernel (gfx950): 256 threads = 4 waves in a 2x2 grid, a 256x256
+// bf16 layers run the eight-wave ping-pong kernel (gemm_pp_kernel, described
+// where it is defined) for every routed/shared-group GEMM; the four-wave
+// kernel below runs the weight-gradient GEMMs whose groups split along K.
+// Both share the tile table, the tile order, the split-K plan and the
+// register-order epilogue, and give the same bits.
+//
+// Four-wave bf16 kernel (gfx950): 256 threads = 4 waves in a 2x2 grid, a 256x256
 // output tile per workgroup, each wave a 128x128 sub-tile held as 4x4
 // v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, in AGPRs).  The
 // last row tile of a group is cut to 64, 128 or 192 rows when that holds its
@@ -712,6 +718,415 @@ __global__ __launch_bounds__(256) void gemm_bf16_reduce_kernel(GroupedGemmArgs a
     reduce_body<SWIGLU, 1>(a, tl, s, slot);
 }
 
+// ---------------------------------------------------------------------------
+// Eight-wave ping-pong kernel (bf16; every mode except groups split along K).
+//
+// 512 threads in two groups of four waves, one wave of each group on every
+// SIMD.  For a tile of 64*FI rows x 256 columns, group g owns rows
+// [32*FI*g, 32*FI*(g+1)) and its wave q the 64 columns [64q, 64q + 64): FI x 2
+// fragments of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane, so
+// two waves share a SIMD's registers).  K advances in slices of 64 (rows of
+// 128 bytes, as in the four-wave kernel) through three A slots and two B
+// slots of 32 KiB.  The two groups take turns, a barrier ending every phase:
+// while one group runs the 8*FI MFMAs of a slice from its registers at
+// raised priority, the other reads its fragments of its next slice from LDS
+// into registers and issues global -> LDS copies: group 0 the B slice t + 1
+// while it reads slice t, group 1 the A slice t + 2.  A wave's copies and
+// LDS reads thus never sit between its own MFMAs, and the MFMA pipe of every
+// SIMD is fed by one wave or the other.  Slice t is read by group 0 in phase
+// 2t - 1 and by group 1 in phase 2t; B slice t + 1 goes into the slot of
+// slice t - 1 (free after phase 2t - 2) and is first read in phase 2t + 1,
+// A slice t + 2 into the slot of slice t - 1 and first read in phase 2t + 3;
+// each wave waits for its copies at the end of its next (MFMA) phase.  The
+// MFMAs of every accumulator come in the same K order as in the four-wave
+// kernel, so both give the same bits.
+constexpr int kPPA = 3 * kPart;              // B slots follow three A slots
+constexpr int kPPLds = 5 * kPart;            // 160 KiB
+
+// Where split-K partial register group c (= (i*2 + j)*4 + r4) of wave w goes
+// within its 256x256 fp32 tile.
+template <int FI>
+__device__ __forceinline__ int64_t part_off_pp(int w, int c, int lane) {
+  return ((int64_t)(w * 8 * FI + c) * 64 + lane) * 4;
+}
+
+// Epilogue of the ping-pong kernel: wave (grp, q) holds rows 32*FI*grp + 32i +
+// (lane & 31) and, per fragment j, C^T runs of 4 columns as in store_tile.
+template <bool SWIGLU, int FI>
+__device__ __forceinline__ void store_tile_pp(const floatx16 (&acc)[FI][2], const Tile& tl,
+                                              int lane, int grp, int q, const OutMap& om, int N) {
+  const int hi = lane >> 5;
+  auto emit = [&](const uint32_t (&v)[4][2], uint16_t* rowp, int64_t col0, bool ok) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t lo[2], up[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const auto r = __builtin_amdgcn_permlane32_swap(v[2 * c][p], v[2 * c + 1][p], false, false);
+        lo[p] = r[0];
+        up[p] = r[1];
+      }
+      if (ok)
+        *reinterpret_cast<uint4*>(rowp + col0 + 16 * c + 8 * hi) = uint4{lo[0], lo[1], up[0], up[1]};
+    }
+  };
+  auto pack_runs = [&](const floatx16& f, uint32_t (&v)[4][2]) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) v[b][p] = pack_bf16x2(f[4 * b + 2 * p], f[4 * b + 2 * p + 1]);
+  };
+#pragma unroll
+  for (int i = 0; i < FI; ++i) {
+    const int row = grp * 32 * FI + i * 32 + (lane & 31);
+    const bool ok = row < tl.m_valid;
+    uint16_t* orow = om.row(tl.o_row + row);
+    if constexpr (SWIGLU) {
+      // fragment 0 holds a1 = x.w1 and fragment 1 a3 = x.w3 of the same 32
+      // activation columns
+      const int64_t col0 = (int64_t)tl.nt * 128 + 32 * q;
+      uint32_t v[4][2];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          float u[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 4 * b + 2 * p + e;
+            const float z = acc[i][0][r];
+            u[e] = z * acc[i][1][r] *
+                   __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+          }
+          v[b][p] = pack_bf16x2(u[0], u[1]);
+        }
+      emit(v, orow, col0, ok);
+      if (om.a13) {
+        uint16_t* r13 = om.a13 + (tl.o_row + row) * om.ld13;
+        uint32_t v1[4][2], v3[4][2];
+        pack_runs(acc[i][0], v1);
+        pack_runs(acc[i][1], v3);
+        emit(v1, r13, col0, ok);
+        emit(v3, r13, col0 + N, ok);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col0 = (int64_t)tl.nt * BN + 64 * q + 32 * j;
+        if (col0 >= N) continue;
+        uint32_t v[4][2];
+        pack_runs(acc[i][j], v);
+        emit(v, orow, col0, ok);
+      }
+    }
+  }
+}
+
+template <bool SWIGLU, int FI>
+__device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Tile& tl, int part,
+                                             int parts, int64_t slot, uint8_t* smem) {
+  constexpr int AB = 2 * FI;    // A blocks of 8 rows each wave copies per slice
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2, q = w & 3;
+  const int K = a.K, N = a.N;
+  const int nk = K / BK;
+  const bool shared = tl.g >= a.E_routed;
+  const bool a_shared = shared && !a.a_from_out_rows;
+  const uint16_t* A = (const uint16_t*)(a_shared ? a.A_shared : a.A);
+  const int lda = a_shared ? a.lda_shared : a.lda;
+  const int ldb = a.ldb ? a.ldb : K;
+  const uint32_t browbytes = (uint32_t)ldb * 2;
+  const uint32_t arowbytes = (uint32_t)lda * 2;
+  const uint16_t* B0 = (const uint16_t*)(shared ? a.B0s : a.B0);
+  const uint16_t* B1 = (const uint16_t*)(shared ? a.B1s : a.B1);
+  if (!shared) {
+    B0 += (int64_t)tl.g * a.b_stride;
+    if (SWIGLU || a.b_split) B1 += (int64_t)tl.g * a.b_stride;
+  }
+  // K slices [kbeg, kbeg + nsteps) (part `part` of K); a whole tile of a
+  // routed group starts at slice g*nk/8 and wraps around
+  const int kbeg = (int)((int64_t)part * nk / parts);
+  const int nsteps = (int)((int64_t)(part + 1) * nk / parts) - kbeg;
+  const int krot = (parts == 1 && a.rotate_k && !shared) ? (int)(((int64_t)tl.g * nk / 8) % nk) : 0;
+
+  // Copies, 8 rows (1 KiB) per instruction; lane l lands at byte 16*l of the
+  // block: row l >> 3, stored chunk l & 7, which holds logical chunk
+  // (l & 7) ^ swz(row) = (l & 7) ^ (l >> 3) ^ (m & 7) for the tile's 8-row
+  // block m.  Group 1's wave q copies A rows q*16*FI .. (blocks m = 2*FI*q +
+  // b), group 0's wave q the B rows 64q .. 64q + 63 (blocks m = 8q + b).
+  rsrc_t rs0, rs1;
+  uint32_t rowb;
+  if (grp == 1) {
+    const int a_rows = __builtin_amdgcn_readfirstlane(min(max(tl.m_valid - q * 16 * FI, 0), 16 * FI));
+    rs0 = make_rsrc(A + (tl.a_row + q * 16 * FI) * (int64_t)lda, (uint32_t)a_rows * arowbytes);
+    rs1 = rs0;
+    rowb = arowbytes;
+  } else if (SWIGLU) {
+    // B rows 64q .. 64q + 63 of the tile: w1 then w3 rows f0 + 32q .. + 31
+    const int64_t f = (int64_t)tl.nt * 128 + 32 * q;
+    rs0 = make_rsrc(B0 + f * K, 32u * browbytes);
+    rs1 = make_rsrc(B1 + f * K, 32u * browbytes);
+    rowb = browbytes;
+  } else {
+    // b_split: rows [0, N/2) of B come from B0, [N/2, N) from B1 (64-row
+    // blocks never straddle N/2, a multiple of 64)
+    int64_t brow = (int64_t)tl.nt * BN + 64 * q;
+    int64_t nrows = N;
+    const uint16_t* Bb = B0;
+    if (a.b_split) {
+      nrows = N / 2;
+      if (brow >= nrows) {
+        Bb = B1;
+        brow -= nrows;
+      }
+    }
+    const int nb = __builtin_amdgcn_readfirstlane(
+        (int)min(max(nrows - brow, (int64_t)0), (int64_t)64));
+    rs0 = make_rsrc(Bb + min(brow, nrows - 1) * ldb, (uint32_t)nb * browbytes);
+    rs1 = rs0;
+    rowb = browbytes;
+  }
+  const uint32_t vrow = (uint32_t)(lane >> 3) * rowb;
+  const uint32_t vx = (uint32_t)((lane & 7) ^ (lane >> 3));
+  const int mbase = grp == 1 ? 2 * FI * q : 8 * q;
+
+  // Fragment reads: lane l reads row (l & 31) of a 32-row fragment and
+  // logical chunk 2*k + (l >> 5) of sub-step k; a fragment starting at row
+  // 32*r has swz = (l & 7) ^ (4*(r & 1) + ((l >> 3) & 3)): A fragment i has
+  // r = FI*grp + i, B fragment j has r = 2q + j.
+  const int rA = (grp * 32 * FI + (lane & 31)) * (BK * 2);
+  const int rB = kPPA + (64 * q + (lane & 31)) * (BK * 2);
+  const int fe = (lane & 7) ^ ((lane >> 3) & 3);
+  const int fo = (lane & 7) ^ (4 | ((lane >> 3) & 3));
+  const bool aflip = (FI * grp) & 1;   // A fragment i has parity (i & 1) ^ aflip
+  int cx[4][2], cxa[4][2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    cx[k][0] = ((2 * k + (lane >> 5)) ^ fe) << 4;
+    cx[k][1] = ((2 * k + (lane >> 5)) ^ fo) << 4;
+    cxa[k][0] = aflip ? cx[k][1] : cx[k][0];
+    cxa[k][1] = aflip ? cx[k][0] : cx[k][1];
+  }
+
+  floatx16 acc[FI][2];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  bf16x8 fa[4][FI], fb[4][2];
+
+#define PP_SB() __builtin_amdgcn_sched_barrier(0)
+// K byte offset of slice T within a row (out of the buffer past the last one)
+#define PP_KOFF(T)                                                                             \
+  ((T) < nsteps ? (uint32_t)(kbeg + ((T) + krot >= nsteps ? (T) + krot - nsteps : (T) + krot)) * \
+                      (BK * 2)                                                                 \
+                : 0x7FFFFFF0u)
+// Copy block b of slice T: group 0 a B block into B slot T & 1, group 1 an
+// A block into A slot T % 3 (the caller's group decides which)
+#define PP_COPY_B(T, B)                                                                        \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
+      (SWIGLU && (B) >= 4) ? rs1 : rs0,                                                        \
+      LDS_AS(smem + kPPA + ((T) & 1) * kPart + (8 * q + (B)) * 1024), 16,                      \
+      vrow + ((vx ^ (uint32_t)(((B)) & 7)) << 4),                                              \
+      (T) < nsteps ? (uint32_t)(SWIGLU ? ((B) & 3) : (B)) * 8u * browbytes + PP_KOFF(T)        \
+                   : PP_KOFF(T),                                                               \
+      0, 0)
+#define PP_COPY_A(T, B)                                                                        \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
+      rs0, LDS_AS(smem + ((T) % 3) * kPart + (mbase + (B)) * 1024), 16,                        \
+      vrow + ((vx ^ (uint32_t)((mbase + (B)) & 7)) << 4),                                      \
+      (T) < nsteps ? (uint32_t)(B) * 8u * arowbytes + PP_KOFF(T) : PP_KOFF(T), 0, 0)
+// Memory phase: the group's copies (group 0: B slice T + 1, 8 blocks; group
+// 1: A slice T + 2, 2*FI blocks), then this wave's fragments of slice T.
+#define PP_READS(T)                                                                            \
+  {                                                                                            \
+    if (grp == 0) {                                                                            \
+      _Pragma("unroll") for (int c = 0; c < 8; ++c) PP_COPY_B((T) + 1, c);                     \
+    } else {                                                                                   \
+      _Pragma("unroll") for (int c = 0; c < AB; ++c) PP_COPY_A((T) + 2, c);                    \
+    }                                                                                          \
+    const uint8_t* SA = smem + ((T) % 3) * kPart;                                              \
+    const uint8_t* SB = smem + ((T) & 1) * kPart;                                              \
+    _Pragma("unroll") for (int k = 0; k < 4; ++k) {                                            \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) fb[k][j] =                                 \
+          lds_frag(SB + rB + j * 4096 + cx[k][j]);                                             \
+      _Pragma("unroll") for (int i = 0; i < FI; ++i) fa[k][i] =                                \
+          lds_frag(SA + rA + i * 4096 + cxa[k][i & 1]);                                        \
+    }                                                                                          \
+  }
+#define PP_MFMAS()                                                                             \
+  {                                                                                            \
+    __builtin_amdgcn_s_setprio(1);                                                             \
+    _Pragma("unroll") for (int k = 0; k < 4; ++k)                                              \
+        _Pragma("unroll") for (int i = 0; i < FI; ++i)                                         \
+            _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =                          \
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[k][j], fa[k][i], acc[i][j], 0, 0, 0); \
+    __builtin_amdgcn_s_setprio(0);                                                             \
+  }
+#define PP_VMCNT(n) (0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+#define PP_BARRIER()                       \
+  PP_SB();                                 \
+  asm volatile("s_barrier" ::: "memory");  \
+  PP_SB()
+// end of a memory phase: fragments in registers; the copies just issued may
+// stay in flight (group 0: 8, group 1: 2*FI)
+#define PP_END_MEM()                                                \
+  PP_SB();                                                          \
+  if (grp == 0)                                                     \
+    __builtin_amdgcn_s_waitcnt(PP_VMCNT(8) & ~0x0F00);              \
+  else                                                              \
+    __builtin_amdgcn_s_waitcnt(PP_VMCNT(AB) & ~0x0F00);             \
+  PP_BARRIER()
+  constexpr int kWaitAll = PP_VMCNT(0) & ~0x0F00;          // vmcnt(0) lgkmcnt(0)
+
+  // Every wave runs the same sequence, group 1 one barrier behind group 0:
+  //   prologue copies | barrier | (group 1: barrier) |
+  //   [reads of slice t (+ copies) | barrier | MFMAs of slice t | barrier] ...
+  // so that group 0's MFMAs of slice t run beside group 1's reads of slice t,
+  // and group 1's MFMAs of slice t beside group 0's reads of slice t + 1.
+  // Prologue: group 0 copies B slice 0, group 1 A slices 0 and 1; slice 0
+  // has landed at the first barrier.
+  if (grp == 0) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) PP_COPY_B(0, b);
+    PP_SB();
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    PP_BARRIER();
+  } else {
+#pragma unroll
+    for (int b = 0; b < AB; ++b) PP_COPY_A(0, b);
+#pragma unroll
+    for (int b = 0; b < AB; ++b) PP_COPY_A(1, b);
+    PP_SB();
+    __builtin_amdgcn_s_waitcnt(PP_VMCNT(AB) & ~0x0F00);
+    PP_BARRIER();
+    PP_BARRIER();
+  }
+  for (int t = 0; t < nsteps; ++t) {
+    PP_READS(t);
+    PP_END_MEM();
+    PP_MFMAS();
+    // the last barrier of group 1 is left out, which keeps the two groups'
+    // barrier counts equal (group 1 had one more at the start)
+    PP_SB();
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    if (grp == 0 || t + 1 < nsteps) asm volatile("s_barrier" ::: "memory");
+    PP_SB();
+  }
+  // every copy of this wave has landed (each MFMA phase ends with vmcnt(0))
+#undef PP_SB
+#undef PP_KOFF
+#undef PP_COPY_A
+#undef PP_COPY_B
+#undef PP_READS
+#undef PP_MFMAS
+#undef PP_VMCNT
+#undef PP_BARRIER
+#undef PP_END_MEM
+
+  if (parts > 1) {
+    float* P = a.partials + (slot * parts + part) * (int64_t)(256 * 256);
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int c = (i * 2 + j) * 4 + r4;
+          *reinterpret_cast<floatx4*>(P + part_off_pp<FI>(w, c, lane)) =
+              floatx4{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
+                      acc[i][j][4 * r4 + 3]};
+        }
+    return;
+  }
+  store_tile_pp<SWIGLU, FI>(acc, tl, lane, grp, q, out_map(a, tl.g), N);
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPPLds];   // 160 KiB
+  const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
+  const int nk = a.K / BK;
+  const Work wk = plan_work(a, NT, nk, blockIdx.x);
+  if (wk.L < 0) return;
+  Tile tl = tile_of(a, NT, wk.L, BM);
+  // Tile fields are workgroup-uniform; saying so keeps the buffer
+  // descriptors in scalar registers.
+  tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+  tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
+  tl.m_valid = __builtin_amdgcn_readfirstlane(tl.m_valid);
+  tl.a_row = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tl.a_row >> 32)) << 32) |
+             (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.a_row);
+  tl.o_row = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tl.o_row >> 32)) << 32) |
+             (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.o_row);
+  const int part = __builtin_amdgcn_readfirstlane(wk.part);
+  const int parts = __builtin_amdgcn_readfirstlane(wk.parts);
+  const int fi = frags_of(tl.m_valid);
+  if (fi == 4)
+    tile_body_pp<SWIGLU, 4>(a, tl, part, parts, wk.slot, smem);
+  else if (fi == 3)
+    tile_body_pp<SWIGLU, 3>(a, tl, part, parts, wk.slot, smem);
+  else if (fi == 2)
+    tile_body_pp<SWIGLU, 2>(a, tl, part, parts, wk.slot, smem);
+  else
+    tile_body_pp<SWIGLU, 1>(a, tl, part, parts, wk.slot, smem);
+}
+
+template <bool SWIGLU, int FI>
+__device__ __forceinline__ void reduce_body_pp(const GroupedGemmArgs& a, const Tile& tl, int s,
+                                               int64_t slot) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  floatx16 acc[FI][2];
+  const float* P0 = a.partials + slot * s * (int64_t)(256 * 256);
+  // per row fragment: the 8 loads of a part issued together, parts added in
+  // part order (the sum is the same for every launch)
+#pragma unroll
+  for (int i = 0; i < FI; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int p = 0; p < s; ++p) {
+      const float* P = P0 + p * (int64_t)(256 * 256);
+      floatx4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = *reinterpret_cast<const floatx4*>(P + part_off_pp<FI>(w, i * 8 + u, lane));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * r4 + e] += v[j * 4 + r4][e];
+    }
+  }
+  store_tile_pp<SWIGLU, FI>(acc, tl, lane, w >> 2, w & 3, out_map(a, tl.g), a.N);
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(512) void gemm_pp_reduce_kernel(GroupedGemmArgs a) {
+  const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
+  const int nk = a.K / BK;
+  int64_t V, whole;
+  int s;
+  split_shape(a, NT, nk, V, whole, s);
+  const int64_t slot = blockIdx.x;
+  if (s < 2 || whole + slot >= V) return;
+  const Tile tl = tile_of(a, NT, whole + slot, BM);
+  const int fi = frags_of(tl.m_valid);
+  if (fi == 4)
+    reduce_body_pp<SWIGLU, 4>(a, tl, s, slot);
+  else if (fi == 3)
+    reduce_body_pp<SWIGLU, 3>(a, tl, s, slot);
+  else if (fi == 2)
+    reduce_body_pp<SWIGLU, 2>(a, tl, s, slot);
+  else
+    reduce_body_pp<SWIGLU, 1>(a, tl, s, slot);
+}
+
 // fp32 layers: 64x64 tiles, BK = 16, fp32 FMA, each thread 4 rows x 4
 // columns (columns strided by 16 for conflict-free LDS reads).
 constexpr int FBM = kGemmBM_f32, FBN = 64, FBK = 16;
@@ -845,10 +1260,27 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GroupedGemmArgs a) {
 
 hipError_t launch_grouped_gemm(int dtype, bool swiglu, const GroupedGemmArgs& a,
                                hipStream_t s) {
-  if (dtype == 1) {
+  if (dtype == 1 && !a.kgroup) {
+    // the ping-pong kernel: whole tiles plus at most num_cu split-part
+    // workgroups, then (with split tiles) the reduce
     const int NT = swiglu ? a.N / 128 : (a.N + BN - 1) / BN;
-    // whole tiles plus at most num_cu split-part workgroups; groups split
-    // along K: exactly G x MT x NT tiles
+    const int64_t nb = a.max_m_tiles * NT + (a.partials ? a.num_cu : 0);
+    if (nb <= 0) return hipSuccess;
+    if (swiglu)
+      MOE_LAUNCH(gemm_pp_kernel<true>, dim3((unsigned)nb), dim3(512), 0, s, a);
+    else
+      MOE_LAUNCH(gemm_pp_kernel<false>, dim3((unsigned)nb), dim3(512), 0, s, a);
+    if (a.partials) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      if (swiglu)
+        MOE_LAUNCH(gemm_pp_reduce_kernel<true>, dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
+      else
+        MOE_LAUNCH(gemm_pp_reduce_kernel<false>, dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
+    }
+  } else if (dtype == 1) {
+    const int NT = swiglu ? a.N / 128 : (a.N + BN - 1) / BN;
+    // groups split along K: exactly G x MT x NT tiles
     const int64_t nb = a.kgroup ? (int64_t)a.G * ((a.m_fixed + BM - 1) / BM) * NT
                                 : a.max_m_tiles * NT + (a.partials ? a.num_cu : 0);
     if (nb <= 0) return hipSuccess;
