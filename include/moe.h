@@ -288,6 +288,28 @@ int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
                             void* y_perm, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* The same grouped GEMM without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, results and errors are those
+ * of moe_grouped_gemm_swiglu (bit-identical outputs), without ws/ws_bytes:
+ * its scratch (the tile table and the split-K partial tiles) is a
+ * file-scope device array of MOE_NOALLOC_SCRATCH_BYTES in the library,
+ * one per GPU, held from the library's load until the process ends.  Limit:
+ * every config the library accepts fits it (E <= 1024 groups, at most 256
+ * split-K parts); a config needing more returns MOE_ERR_UNSUPPORTED before
+ * any device work.  The call allocates and frees nothing and sets no
+ * memory: every scratch byte a kernel reads was written earlier in the same
+ * call.  All calls on one GPU share that GPU's scratch, so calls that
+ * overlap on one GPU (different streams, or threads) race and give
+ * unspecified results; calls in one stream are ordered and safe.
+ * MOE_ERR_HIP if the scratch's device address cannot be obtained.          */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16640 + (size_t)67108864)
+int moe_grouped_gemm_swiglu_noalloc(const moe_cfg_t* cfg, const void* x_perm,
+                                    const int32_t* expert_counts,
+                                    const int32_t* expert_offsets, const void* w1,
+                                    const void* w3, const void* w2, void* act,
+                                    void* y_perm, void* stream);
+
 /* Stage 4: combine / unpermute -----------------------------------------------
  * 专家并行, "EP+DP" forward (each token's top-k outputs summed with their
  * weights); infra-l7 "NVIDIA 原题" row combine.

@@ -57,7 +57,7 @@ ROUTING_BY_NAME = {
 ABI_SYMBOLS = (
     "moe_strerror", "moe_capacity", "moe_num_rows", "moe_workspace_bytes",
     "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu",
-    "moe_unpermute_combine", "moe_load_balance", "moe_select_bias_update",
+    "moe_grouped_gemm_swiglu_noalloc", "moe_unpermute_combine", "moe_load_balance", "moe_select_bias_update",
     "moe_backward_workspace_bytes",
     "moe_backward", "moe_backward_saved", "moe_forward",
 )
@@ -126,6 +126,7 @@ def lib() -> ctypes.CDLL:
             "moe_router_topk": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_permute": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_grouped_gemm_swiglu": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "moe_grouped_gemm_swiglu_noalloc": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, P]),
             "moe_unpermute_combine": (ctypes.c_int, [cfgp, P, P, P, P, P, P]),
             "moe_load_balance": (ctypes.c_int, [cfgp, P, P, ctypes.c_float, P, P, P, P, SZ,
                                                 P]),
@@ -289,6 +290,17 @@ def moe_grouped_gemm_swiglu(cfg, x_perm, expert_counts, expert_offsets, w1, w3, 
         _p(z, "expert_offsets", expert_offsets), _p(z, "w1", w1), _p(z, "w3", w3),
         _p(z, "w2", w2), _p(z, "act", act), _p(z, "y_perm", y_perm), wp, wb,
         _stream(stream)))
+
+
+def moe_grouped_gemm_swiglu_noalloc(cfg, x_perm, expert_counts, expert_offsets, w1, w3, w2,
+                                    act, y_perm, stream=None) -> None:
+    """moe_grouped_gemm_swiglu with the library's own per-GPU scratch instead
+    of a workspace (allocates nothing; calls overlapping on one GPU race)."""
+    z = _sizes(cfg)
+    _check("moe_grouped_gemm_swiglu_noalloc", lib().moe_grouped_gemm_swiglu_noalloc(
+        ctypes.byref(cfg), _p(z, "x_perm", x_perm), _p(z, "expert_counts", expert_counts),
+        _p(z, "expert_offsets", expert_offsets), _p(z, "w1", w1), _p(z, "w3", w3),
+        _p(z, "w2", w2), _p(z, "act", act), _p(z, "y_perm", y_perm), _stream(stream)))
 
 
 def moe_unpermute_combine(cfg, y_perm, assign_row, topk_gate, shared_y, y,

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -365,6 +366,35 @@ int check_gemm_args(const moe_cfg_t* cfg, const void* x_perm, const int32_t* exp
   return MOE_OK;
 }
 
+// ---- the grouped GEMM without a caller workspace ------------------------
+// File-scope device scratch: the tile table (room for 1024 routed groups +
+// 1) and the split-K partial tiles (at most 256 parts of 256 x 256 fp32).
+// In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address, one per GPU, comes from hipGetSymbolAddress
+// (scratch_on_current_device) and only that address reaches a kernel.
+constexpr size_t kScratchGtabBytes = (size_t)((4 * 1025 + 1) * 4 + 255) / 256 * 256;
+constexpr size_t kScratchBytes = kScratchGtabBytes + (size_t)moe::kSplitPartialFloats * 4;
+static_assert(kScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch size as documented");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current; NULL if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 MOE_API int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
@@ -382,6 +412,29 @@ MOE_API int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
   return grouped_gemm_impl(c, x_perm, expert_counts, expert_offsets, w1, w3, w2, act, y_perm,
                            at<int32_t>(ws, L.gtab), at<float>(ws, L.partials),
                            (hipStream_t)stream);
+}
+
+MOE_API int moe_grouped_gemm_swiglu_noalloc(const moe_cfg_t* cfg, const void* x_perm,
+                                            const int32_t* expert_counts,
+                                            const int32_t* expert_offsets, const void* w1,
+                                            const void* w3, const void* w2, void* act,
+                                            void* y_perm, void* stream) {
+  const int st = check_gemm_args(cfg, x_perm, expert_counts, expert_offsets, w1, w3, w2, act,
+                                 y_perm);
+  if (st != MOE_OK || cfg->T == 0) return st;
+  const moe_cfg_t& c = *cfg;
+  // the tile table of E groups and (bf16) the partials must fit the scratch
+  const size_t need = (size_t)gtab_ints(c.E) * 4 <= kScratchGtabBytes
+                          ? kScratchGtabBytes + (c.dtype == MOE_DTYPE_BF16
+                                                     ? (size_t)moe::kSplitPartialFloats * 4
+                                                     : 0)
+                          : kScratchBytes + 1;
+  if (need > kScratchBytes) return MOE_ERR_UNSUPPORTED;
+  char* sp = static_cast<char*>(scratch_on_current_device());
+  if (!sp) return MOE_ERR_HIP;
+  return grouped_gemm_impl(c, x_perm, expert_counts, expert_offsets, w1, w3, w2, act, y_perm,
+                           reinterpret_cast<int32_t*>(sp),
+                           reinterpret_cast<float*>(sp + kScratchGtabBytes), (hipStream_t)stream);
 }
 
 MOE_API int moe_unpermute_combine(const moe_cfg_t* cfg, const void* y_perm,
