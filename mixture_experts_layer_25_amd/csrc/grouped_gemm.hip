@@ -68,8 +68,8 @@ __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Largest g with mtp[g] * NT <= L (mtp non-decreasing, mtp[0] = 0,
 // mtp[G] * NT > L).
-__device__ __forceinline__ int find_group(const int32_t* mtp, int G, int64_t L,
-                                          int NT) {
+template <typename GT>
+__device__ __forceinline__ int find_group(const GT* mtp, int G, int64_t L, int NT) {
   int lo = 0, hi = G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -87,9 +87,10 @@ struct Tile {
 };
 
 // Tile of logical index L (row tile fastest within (group, column tile)).
-__device__ __forceinline__ Tile tile_of(const GroupedGemmArgs& a, int NT, int64_t L, int BMx) {
+template <typename GT>
+__device__ __forceinline__ Tile tile_of(const GroupedGemmArgs& a, const GT* gt, int NT, int64_t L,
+                                        int BMx) {
   const int G = a.G;
-  const int32_t* gt = a.gtab;
   Tile t;
   const int g = find_group(gt, G, L, NT);
   const int me = gt[g + 1] - gt[g];
@@ -124,9 +125,9 @@ struct Work {
   int64_t slot;     // split tiles: index among the split tiles
 };
 
-__device__ __forceinline__ void split_shape(const GroupedGemmArgs& a, int NT, int nk,
-                                            int64_t& V, int64_t& whole, int& s) {
-  V = (int64_t)a.gtab[a.G] * NT;
+__device__ __forceinline__ void split_shape(const GroupedGemmArgs& a, int32_t tiles, int NT,
+                                            int nk, int64_t& V, int64_t& whole, int& s) {
+  V = (int64_t)tiles * NT;
   const int64_t P = a.num_cu > 0 ? a.num_cu : 1;
   const int64_t r = V % P;
   s = 1;
@@ -137,10 +138,11 @@ __device__ __forceinline__ void split_shape(const GroupedGemmArgs& a, int NT, in
   whole = s >= 2 ? V - r : V;
 }
 
-__device__ __forceinline__ Work plan_work(const GroupedGemmArgs& a, int NT, int nk, int64_t b) {
+__device__ __forceinline__ Work plan_work(const GroupedGemmArgs& a, int32_t tiles, int NT, int nk,
+                                          int64_t b) {
   int64_t V, whole;
   int s;
-  split_shape(a, NT, nk, V, whole, s);
+  split_shape(a, tiles, NT, nk, V, whole, s);
   Work wk{-1, 0, 1, 0};
   if (b < whole) {
     const int64_t x = b & 7, q = whole >> 3, r8 = whole & 7;
@@ -638,9 +640,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
     tl.o_row = tl.a_row;
     wk.L = L;
   } else {
-    wk = plan_work(a, NT, nk, blockIdx.x);
+    wk = plan_work(a, a.gtab[a.G], NT, nk, blockIdx.x);
     if (wk.L < 0) return;
-    tl = tile_of(a, NT, wk.L, BM);
+    tl = tile_of(a, a.gtab, NT, wk.L, BM);
   }
   // Tile fields are workgroup-uniform; saying so keeps the buffer
   // descriptors in scalar registers.
@@ -703,10 +705,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_reduce_kernel(GroupedGemmArgs a
   const int nk = a.K / BK;
   int64_t V, whole;
   int s;
-  split_shape(a, NT, nk, V, whole, s);
+  split_shape(a, a.gtab[a.G], NT, nk, V, whole, s);
   const int64_t slot = blockIdx.x;
   if (s < 2 || whole + slot >= V) return;
-  const Tile tl = tile_of(a, NT, whole + slot, BM);
+  const Tile tl = tile_of(a, a.gtab, NT, whole + slot, BM);
   const int fi = frags_of(tl.m_valid);
   if (fi == 4)
     reduce_body<SWIGLU, 4>(a, tl, s, slot);
@@ -1050,9 +1052,16 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kPPLds];   // 160 KiB
   const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
   const int nk = a.K / BK;
-  const Work wk = plan_work(a, NT, nk, blockIdx.x);
+  // The tile table (4G + 1 ints, at most 16.4 KiB) is staged in LDS by one
+  // parallel load, in the second B slot, which no copy touches before the
+  // first barrier; the group search then runs on LDS instead of a chain of
+  // dependent global loads.
+  int32_t* gt = reinterpret_cast<int32_t*>(smem + kPPA + kPart);
+  for (int i = threadIdx.x; i < 4 * a.G + 1; i += 512) gt[i] = a.gtab[i];
+  __syncthreads();
+  const Work wk = plan_work(a, gt[a.G], NT, nk, blockIdx.x);
   if (wk.L < 0) return;
-  Tile tl = tile_of(a, NT, wk.L, BM);
+  Tile tl = tile_of(a, gt, NT, wk.L, BM);
   // Tile fields are workgroup-uniform; saying so keeps the buffer
   // descriptors in scalar registers.
   tl.g = __builtin_amdgcn_readfirstlane(tl.g);
@@ -1112,10 +1121,10 @@ __global__ __launch_bounds__(512) void gemm_pp_reduce_kernel(GroupedGemmArgs a) 
   const int nk = a.K / BK;
   int64_t V, whole;
   int s;
-  split_shape(a, NT, nk, V, whole, s);
+  split_shape(a, a.gtab[a.G], NT, nk, V, whole, s);
   const int64_t slot = blockIdx.x;
   if (s < 2 || whole + slot >= V) return;
-  const Tile tl = tile_of(a, NT, whole + slot, BM);
+  const Tile tl = tile_of(a, a.gtab, NT, whole + slot, BM);
   const int fi = frags_of(tl.m_valid);
   if (fi == 4)
     reduce_body_pp<SWIGLU, 4>(a, tl, s, slot);
@@ -1160,7 +1169,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GroupedGemmArgs a) {
   } else {
     const int64_t L = plain_tile(a, NT, blockIdx.x);
     if (L < 0) return;
-    tl = tile_of(a, NT, L, FBM);
+    tl = tile_of(a, a.gtab, NT, L, FBM);
   }
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int N = a.N;
