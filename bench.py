@@ -381,6 +381,8 @@ def main() -> int:
                 "kernel_span_ms": round(median([es[0].elapsed_time(es[2 * NS - 1])
                                                 for es in cev]), 4)}
         cold["stage_ms"] = {name: round(median(v), 5) for name, v in ck.items()}
+        if cfg.dtype == "bf16" and cfg.E <= 16 and args.routing in ("topk", "topk_score_drop"):
+            cold["stage_ms"]["topk"] = None
 
     # load-balance statistics of the last step's routing (not part of the
     # step): reads the logits once (T*E*4 bytes)
@@ -529,6 +531,12 @@ def main() -> int:
             d.update(extra)
         return d
 
+    # bf16 layers of up to 16 experts with plain or score-drop top-k run the
+    # router, top-k, gates and histogram as one kernel (stage "router"); the
+    # "topk" stage then launches nothing and its events hold two markers
+    fused_front = (cfg.dtype == "bf16" and cfg.E <= 16
+                   and args.routing in ("topk", "topk_score_drop"))
+    front = ["router", "scan", "assign"] + ([] if fused_front else ["topk"])
     out = {
         "metric": metric_label(cfg.T, cfg.h, cfg.E, cfg.k),
         "value": round(cfg.T * K / elapsed, 1),
@@ -569,7 +577,10 @@ def main() -> int:
             "standalone_us": None if comb_alone is None else round(comb_alone, 2),
             "standalone_frac_hbm": None if comb_alone is None else frac(cb, comb_alone * 1e-3),
             "standalone_buffer_sets": comb_sets}),
-        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "stage_ms": {k: (None if (k == "topk" and fused_front) else round(v, 5))
+                     for k, v in stage_ms.items()},
+        "front_end_kernel_us": round(sum(stage_ms[n] for n in front) * 1e3, 2),
+        "router_topk_fused": fused_front,
         "kernel_span_ms": round(kernel_span_ms, 4),
         "backward": (None if bwd is None else {
             "ms": round(bwd, 4),

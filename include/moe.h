@@ -149,8 +149,11 @@ extern "C" {
  *   offsets, GEMM tile table), 3 assign (ranks, rows), 4 permute copy,
  *   5 grouped GEMM 1 + SwiGLU (+ its split-K reduce), 6 grouped GEMM 2
  *   (+ reduce), 7 combine.  (Routing variants launch their own kernels in
- *   stages 1-4.)  MOE_NUM_EVENTS events, a start and a stop per stage, time
- *   them (see moe_forward).                                                */
+ *   stages 1-4.)  bf16 layers of up to 16 experts with TOPK or
+ *   TOPK_SCORE_DROP routing run the router, the top-k, the gates and the
+ *   histogram as one kernel in stage 0; their stage 1 launches no kernel.
+ *   MOE_NUM_EVENTS events, a start and a stop per stage, time them (see
+ *   moe_forward).                                                          */
 #define MOE_NUM_STAGES 8
 #define MOE_NUM_EVENTS (2 * MOE_NUM_STAGES)
 
@@ -418,7 +421,8 @@ int moe_backward_saved(const moe_cfg_t* cfg, const moe_weights_t* w, const void*
  *            kernel time and (events[0], events[2*MOE_NUM_STAGES-1]) spans
  *            the layer from its first kernel's start to its last kernel's
  *            end.  A stage that launches nothing records both events on
- *            `stream` at that point (an empty interval).                    */
+ *            `stream` at that point (an interval of two back-to-back
+ *            markers, a few microseconds, not kernel time).                 */
 int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void* x,
                 void* y, const moe_route_out_t* route, void* ws,
                 size_t ws_bytes, void* const* events, void* stream);

@@ -134,8 +134,11 @@ Layout layout_of(const moe_cfg_t& c) {
   L.logits = take((size_t)(T * E) * 4);
   L.idx = take((size_t)(T * k) * 4);
   L.gate = take((size_t)(T * k) * 4);
-  L.hist = take((size_t)(nch * E) * 4);
-  L.base = take((size_t)(nch * E) * 4);
+  // histogram rows: at most one per kRouteFusedTokens tokens (the fused
+  // router's workgroups; the separate top-k kernel's groups are larger)
+  const int64_t nrow = (T + moe::kRouteFusedTokens - 1) / moe::kRouteFusedTokens;
+  L.hist = take((size_t)(nrow * E) * 4);
+  L.base = take((size_t)(nrow * E) * 4);
   L.pbal = take((size_t)(nch * E) * 4);
   L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);
@@ -266,6 +269,11 @@ MOE_API int moe_router_topk(const moe_cfg_t* cfg, const void* x, const void* w_r
   const hipStream_t s = (hipStream_t)stream;
   const Layout L = layout_of(c);
   float* lg = logits ? logits : at<float>(ws, L.logits);
+  if (!sk && moe::router_topk_fused(c.dtype, c.E)) {
+    MOE_TRY(moe::launch_router_topk(x, w_router, logit_bias, lg, select_bias, c.gate, c.T, c.h,
+                                    c.E, c.k, topk_idx, topk_gate, nullptr, s));
+    return MOE_OK;
+  }
   MOE_TRY(moe::launch_router(c.dtype, x, w_router, logit_bias, lg, c.T, c.h, c.E, s));
   const float* sb = select_bias;
   if (sk) {
@@ -803,7 +811,11 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   void* xperm = at<char>(ws, L.xperm);
   void* act = at<char>(ws, L.act);
   void* yperm = at<char>(ws, L.yperm);
-  const int hg = moe::topk_tokens_per_wg(c.E);
+  // the router fused with the top-k (bf16, up to 16 experts, plain or
+  // score-drop token choice): one histogram row per workgroup of 16 tokens
+  const bool fused = moe::router_topk_fused(c.dtype, c.E) &&
+                     (c.routing == MOE_ROUTE_TOPK || c.routing == MOE_ROUTE_TOPK_SCORE_DROP);
+  const int hg = fused ? moe::kRouteFusedTokens : moe::topk_tokens_per_wg(c.E);
   const int64_t nch = (c.T + hg - 1) / hg;
   const int64_t rows = rows_of(c);
   const int BM = row_tile(c);
@@ -839,8 +851,12 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   const int slots = ec ? c.E : c.k;
 
   MOE_TRY(mark(0));
-  MOE_TRY(moe::launch_router(c.dtype, x, w->w_router, w->logit_bias, logits, c.T, c.h,
-                             c.E, s));
+  if (fused)
+    MOE_TRY(moe::launch_router_topk(x, w->w_router, w->logit_bias, logits, w->select_bias,
+                                    c.gate, c.T, c.h, c.E, c.k, idx, gate, hist, s));
+  else
+    MOE_TRY(moe::launch_router(c.dtype, x, w->w_router, w->logit_bias, logits, c.T, c.h,
+                               c.E, s));
   MOE_TRY(mark(1));
   if (ec) {
     // probabilities -> each expert's C best tokens -> fixed groups -> gather
@@ -861,7 +877,7 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
                                    bias, s));
       sb = bias;
     }
-    MOE_TRY(moe::launch_topk(logits, sb, c.gate, c.T, c.E, c.k, idx, gate, hist, s));
+    if (!fused) MOE_TRY(moe::launch_topk(logits, sb, c.gate, c.T, c.E, c.k, idx, gate, hist, s));
     MOE_TRY(mark(2));
     if (c.routing == MOE_ROUTE_TOPK_SCORE_DROP) {
       // dropless ranks first: each expert's assignments in token order

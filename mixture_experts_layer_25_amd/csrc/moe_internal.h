@@ -102,6 +102,17 @@ hipError_t launch_router(int dtype, const void* x, const void* w_router,
                          const float* logit_bias, float* logits, int64_t T,
                          int h, int E, hipStream_t s);
 
+// The router fused with top-k, gates and histogram (bf16 layers of up to 16
+// experts, router_topk_fused): writes logits, idx and gates like
+// launch_router + launch_topk, and, if chunk_hist is given, one histogram
+// row per kRouteFusedTokens tokens.
+constexpr int kRouteFusedTokens = 16;
+bool router_topk_fused(int dtype, int E);
+hipError_t launch_router_topk(const void* x, const void* w_router, const float* logit_bias,
+                              float* logits, const float* select_bias, int gate, int64_t T,
+                              int h, int E, int k, int32_t* idx, float* gate_out,
+                              int32_t* chunk_hist, hipStream_t s);
+
 // Tokens one top-k workgroup handles (4 passes of 256/G tokens, G = lanes
 // per token); its expert histogram covers that many tokens.  Always a
 // divisor of 256.

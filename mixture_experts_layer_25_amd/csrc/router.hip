@@ -15,6 +15,7 @@
 // products are exact in fp32 and accumulate in fp32.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "topk_device.h"
 
 namespace moe {
 
@@ -86,6 +87,88 @@ __global__ __launch_bounds__(64 * kRouterMaxWaves) void router_bf16_kernel(
     for (int q = 1; q < nw; ++q) s += red[q][tk][ee];
     if (bias) s += bias[ee];
     logits[t * E + ee] = s;
+  }
+}
+
+// The router GEMM of up to 16 experts fused with the top-k, the gates and
+// the histogram of the selected experts: the workgroup's 16 tokens are 16
+// top-k segments of 16 lanes (one expert per lane), so the logits never
+// leave the workgroup before the selection (they are still written out).
+// chunk_hist, if given, gets one row of E counts per workgroup (16 tokens).
+__global__ __launch_bounds__(64 * kRouterMaxWaves) void router_topk_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, float* __restrict__ logits,
+    const float* __restrict__ sbias, int gate_mode, int64_t T, int h, int E, int k,
+    int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
+    int32_t* __restrict__ chunk_hist) {
+  __shared__ float red[kRouterMaxWaves][kRouterTok][16];
+  __shared__ int32_t sel_e[kRouterTok][16];
+  __shared__ float sel_l[kRouterTok][16];
+  __shared__ int32_t hist[16];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;         // waves: 16, 8 or 4
+  const int64_t t0 = (int64_t)blockIdx.x * kRouterTok;
+  const int kq = h / nw;                  // a multiple of 32
+  const int koff = w * kq + (lane >> 4) * 8;
+  // MFMA operands as in router_bf16_kernel
+  int64_t trow = t0 + (lane & 15);
+  trow = trow < T ? trow : T - 1;
+  const int e = lane & 15;
+  const bool ez = e >= E;
+  const uint16_t* xp = x + trow * h + koff;
+  const uint16_t* wp = wr + (int64_t)(ez ? E - 1 : e) * h + koff;
+
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  int kk = 0;
+  for (; kk + 32 * kRouterBatch <= kq; kk += 32 * kRouterBatch) {
+    uint4 a[kRouterBatch], b[kRouterBatch];
+#pragma unroll
+    for (int u = 0; u < kRouterBatch; ++u) {
+      a[u] = ld16(xp + kk + 32 * u);
+      b[u] = ld16(wp + kk + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < kRouterBatch; ++u) {
+      if (ez) b[u] = uint4{0u, 0u, 0u, 0u};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                    __builtin_bit_cast(bf16x8, b[u]), acc,
+                                                    0, 0, 0);
+    }
+  }
+  for (; kk < kq; kk += 32) {
+    const uint4 a = ld16(xp + kk);
+    uint4 b = ld16(wp + kk);
+    if (ez) b = uint4{0u, 0u, 0u, 0u};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[w][4 * (lane >> 4) + i][lane & 15] = acc[i];
+  if (threadIdx.x < 16) hist[threadIdx.x] = 0;
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    // thread (tk, ee): token tk's logit of expert ee, wave partials summed
+    // in wave order; then the token's 16 lanes select its top k
+    const int tk = threadIdx.x >> 4, ee = threadIdx.x & 15;
+    const int64_t t = t0 + tk;
+    const bool valid = t < T;
+    float lg[1] = {-INFINITY};
+    uint64_t key[1] = {0};
+    if (valid && ee < E) {
+      float sum = red[0][tk][ee];
+      for (int q = 1; q < nw; ++q) sum += red[q][tk][ee];
+      if (bias) sum += bias[ee];
+      logits[t * E + ee] = sum;
+      lg[0] = sum;
+      key[0] = topk_key(sbias ? sum + sbias[ee] : sum, ee);
+    }
+    topk_segment<16, 1>(valid, ee, E, k, gate_mode, lg, key, sel_e[tk], sel_l[tk],
+                        chunk_hist ? hist : nullptr, idx_out + t * k, gate_out + t * k);
+  }
+  if (chunk_hist) {
+    __syncthreads();
+    if ((int)threadIdx.x < E) chunk_hist[blockIdx.x * (int64_t)E + threadIdx.x] = hist[threadIdx.x];
   }
 }
 
@@ -197,6 +280,19 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 }
 
 }  // namespace
+
+bool router_topk_fused(int dtype, int E) { return dtype == 1 && E <= 16; }
+
+hipError_t launch_router_topk(const void* x, const void* w_router, const float* logit_bias,
+                              float* logits, const float* select_bias, int gate, int64_t T,
+                              int h, int E, int k, int32_t* idx, float* gate_out,
+                              int32_t* chunk_hist, hipStream_t s) {
+  const int64_t nb = (T + kRouterTok - 1) / kRouterTok;
+  MOE_LAUNCH(router_topk_bf16_kernel, dim3((unsigned)nb), dim3(64 * router_waves(h)), 0, s,
+             (const uint16_t*)x, (const uint16_t*)w_router, logit_bias, logits, select_bias,
+             gate, T, h, E, k, idx, gate_out, chunk_hist);
+  return hipGetLastError();
+}
 
 hipError_t launch_router(int dtype, const void* x, const void* w_router,
                          const float* logit_bias, float* logits, int64_t T,

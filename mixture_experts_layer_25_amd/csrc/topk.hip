@@ -15,20 +15,11 @@
 // of those tokens, which the scan kernel turns into ranks and offsets.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "topk_device.h"
 
 namespace moe {
 
 namespace {
-
-template <int G>
-__device__ __forceinline__ uint64_t seg_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 1; m < G; m <<= 1) {
-    const uint64_t o = __shfl_xor(v, m, G);
-    v = o > v ? o : v;
-  }
-  return v;
-}
 
 template <int G, int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(
@@ -63,60 +54,12 @@ __global__ __launch_bounds__(256) void topk_kernel(
       lg[i] = -INFINITY;
       if (valid && e < E) {
         const float l = logits[t * E + e];
-        const float kv = sbias ? l + sbias[e] : l;
         lg[i] = l;
-        key[i] = ((uint64_t)ordered_bits(kv) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+        key[i] = topk_key(sbias ? l + sbias[e] : l, e);
       }
     }
-    for (int r = 0; r < k; ++r) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int i = 0; i < NPL; ++i) best = key[i] > best ? key[i] : best;
-      const uint64_t win = seg_max_u64<G>(best);
-      if (win != 0) {
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-          if (key[i] == win) {
-            key[i] = 0;
-            const int e = (int)(0xFFFFFFFFu - (uint32_t)win);
-            sel_e[tl][r] = e;
-            sel_l[tl][r] = lg[i];
-            atomicAdd(&hist[e], 1);
-          }
-        }
-      }
-    }
-    // Segment lanes see the winners written by other lanes of the same wave.
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-
-    const bool slot = valid && s < k;
-    const float l = slot ? sel_l[tl][s] : -INFINITY;
-    float g = 0.f;
-    if (gate_mode == 0) {          // softmax over the k selected
-      const float m = seg_max_f32<G>(l);
-      const float num = slot ? expf(l - m) : 0.f;
-      const float den = seg_sum_f32<G>(num);
-      g = num / den;
-    } else if (gate_mode == 1) {   // softmax over all E, selected values
-      float m = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < NPL; ++i) m = fmaxf(m, lg[i]);
-      m = seg_max_f32<G>(m);
-      float part = 0.f;
-#pragma unroll
-      for (int i = 0; i < NPL; ++i) part += (s + G * i < E) ? expf(lg[i] - m) : 0.f;
-      const float den = seg_sum_f32<G>(part);
-      g = (slot ? expf(l - m) : 0.f) / den;
-    } else {                       // sigmoid, normalised over the k selected
-      const float sg = slot ? 1.f / (1.f + expf(-l)) : 0.f;
-      const float den = seg_sum_f32<G>(sg);
-      g = sg / den;
-    }
-    if (slot) {
-      idx_out[t * k + s] = sel_e[tl][s];
-      gate_out[t * k + s] = g;
-    }
+    topk_segment<G, NPL>(valid, s, E, k, gate_mode, lg, key, sel_e[tl], sel_l[tl], hist,
+                         idx_out + t * k, gate_out + t * k);
   }
   if (chunk_hist) {
     __syncthreads();
