@@ -8,36 +8,21 @@
 //   GEMM 2:           out[r,i]  = act[r]·w2[e,i]
 //
 // Every operand is K-contiguous (weights stored [out,in]), so both GEMMs are
-// C = A · B^T with 16-byte loads along K for A and B alike.
+// C = A · B^T with 16-byte loads along K for A and B alike.  The same kernel
+// runs the backward's GEMMs (input gradients on transposed weights, and
+// weight gradients whose groups split along K over K-major copies).
 //
-// bf16 layers run the eight-wave ping-pong kernel (gemm_pp_kernel, described
-// where it is defined) for every routed/shared-group GEMM; the four-wave
-// kernel below runs the weight-gradient GEMMs whose groups split along K.
-// Both share the tile table, the tile order, the split-K plan and the
-// register-order epilogue, and give the same bits.
+// bf16: the eight-wave ping-pong kernel (gemm_pp_kernel, described where it
+// is defined), a 256x256 output tile per workgroup.  The last row tile of a
+// group is cut to 64, 128 or 192 rows when that holds its rows, so a group's
+// leftover rows cost a quarter, half or three quarters of a tile instead of
+// a whole one.  Routed group g starts its K loop at slice g*nk/8: groups run
+// on different XCDs, and staggered K offsets spread their weight reads over
+// the memory channels (the row strides are powers of two).
 //
-// Four-wave bf16 kernel (gfx950): 256 threads = 4 waves in a 2x2 grid, a 256x256
-// output tile per workgroup, each wave a 128x128 sub-tile held as 4x4
-// v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, in AGPRs).  The
-// last row tile of a group is cut to 64, 128 or 192 rows when that holds its
-// rows (waves then hold 1x4, 2x4 or 3x4 fragments), so a group's leftover
-// rows cost a quarter, half or three quarters of a tile instead of a whole
-// one.
-// K advances in slices of 64 (128-byte rows, whole cache lines per row).
-// Slices are copied global -> LDS directly (buffer_load_dwordx4 ... lds, no
-// registers in between) into a ring of three A slots and two B slots of
-// 32 KiB each (all 160 KiB of LDS), A up to two slices and B one slice ahead
-// of the MFMAs; buffer bounds return zeros for rows past a ragged group's end.  The
-// instruction order is fixed by hand: every MFMA pair is accompanied by one
-// LDS fragment read for the next sub-step, and the copies of the next slices
-// are spread over the step (one or two per MFMA pair), so the wave never
-// stalls on a burst of memory instructions.  Routed group g starts its K loop at slice g*nk/8: groups
-// run on different XCDs, and staggered K offsets spread their weight reads
-// over the memory channels (the row strides are powers of two).
-//
-// For GEMM 1 the 256 B-tile rows are [w1 f0..f0+63 | w3 f0..f0+63 |
-// w1 f0+64..f0+127 | w3 f0+64..f0+127]: each wave's 128 columns hold 64 w1
-// columns and the matching 64 w3 columns, so silu(a1) * a3 is formed in
+// For GEMM 1 the 256 B-tile rows are [w1 f0..f0+31 | w3 f0..f0+31 |
+// w1 f0+32..f0+63 | w3 f0+32..f0+63 | ...]: each wave's 64 columns hold 32
+// w1 columns and the matching 32 w3 columns, so silu(a1) * a3 is formed in
 // registers and a tile writes 128 activation columns.
 //
 // Tiles: each group (expert) has ceil(rows/256) row tiles; the scan kernel
@@ -46,6 +31,10 @@
 // same few weight column tiles and token row tiles.  Workgroup b runs on
 // XCD b % 8; consecutive logical tiles are handed to the same XCD so that
 // they share its L2.  Workgroups past the real tile count exit at once.
+// The tiles of the last, partial round of workgroups are split along K and
+// summed by a reduce kernel in part order.
+//
+// fp32 layers: a 64x64-tile FMA kernel (gemm_f32_kernel).
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -55,16 +44,6 @@ namespace {
 
 constexpr int BM = kGemmBM_bf16, BN = 256, BK = 64;
 constexpr int kPart = BM * BK * 2;          // 32 KiB: one K slice of the A (or B) tile
-constexpr int kSlotsA = 3, kSlotsB = 2;     // LDS ring slots for A and for B slices
-constexpr int kOffB = kSlotsA * kPart;      // B slots follow the A slots
-constexpr int kLds = (kSlotsA + kSlotsB) * kPart;   // 160 KiB
-
-// LDS rows are BK * 2 = 128 bytes (8 chunks of 16 B); chunk c of row r is
-// stored at c ^ swz(r).  An MFMA operand read has 16 lanes on 16 consecutive
-// rows and one chunk: with this swizzle they fall in 16 distinct 16-byte
-// slots of 256 bytes (64 banks), and any 8 consecutive rows in 8 distinct
-// slots of 128 bytes (32 banks).
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Largest g with mtp[g] * NT <= L (mtp non-decreasing, mtp[0] = 0,
 // mtp[G] * NT > L).
@@ -205,543 +184,40 @@ __device__ __forceinline__ OutMap out_map(const GroupedGemmArgs& a, int g) {
   return m;
 }
 
-// Epilogue of a (64*FI) x 256 tile.  The MFMAs take the weight fragment
-// first, so fragment (i, j) holds C^T: lane l has output row (l & 31) of row
-// block i and, in registers 4b..4b+3, the 4 consecutive columns
-// 8b + 4*(l >> 5) + 0..3 of column block j.  Lanes l and l ^ 32 (same row)
-// trade one 4-column run so that each ends up with 8 consecutive columns:
-// 16-byte stores, the two lanes of a row writing 32 contiguous bytes.
-// GEMM 1 writes silu(a1) * a3 (w1 blocks j = 0, 1 pair with the w3 blocks
-// j + 2 of the same columns); GEMM 2 writes the product.
-template <bool SWIGLU, int FI>
-__device__ __forceinline__ void store_tile(const floatx16 (&acc)[FI][4], const Tile& tl, int lane,
-                                           int wm, int wn, const OutMap& om, int N) {
-  const int hi = lane >> 5;
-  constexpr int NJ = SWIGLU ? 2 : 4;
-  // v_permlane32_swap trades the high half of its first operand with the
-  // low half of its second: with runs 2c and 2c+1 as the operands, lane
-  // l < 32 gets (its run 2c, lane l+32's run 2c) and lane l+32 (lane l's
-  // run 2c+1, its run 2c+1), 8 consecutive columns each
-  auto emit = [&](const uint32_t (&q)[4][2], uint16_t* rowp, int64_t col0, bool ok) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint32_t lo[2], up[2];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const auto r = __builtin_amdgcn_permlane32_swap(q[2 * c][p], q[2 * c + 1][p], false, false);
-        lo[p] = r[0];
-        up[p] = r[1];
-      }
-      if (ok)
-        *reinterpret_cast<uint4*>(rowp + col0 + 16 * c + 8 * hi) = uint4{lo[0], lo[1], up[0], up[1]};
-    }
-  };
-  // run b of fragment f as two bf16 pairs
-  auto pack_runs = [&](const floatx16& f, uint32_t (&q)[4][2]) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) q[b][p] = pack_bf16x2(f[4 * b + 2 * p], f[4 * b + 2 * p + 1]);
-  };
-#pragma unroll
-  for (int i = 0; i < FI; ++i) {
-    const int row = wm * 32 * FI + i * 32 + (lane & 31);
-    const bool ok = row < tl.m_valid;
-    uint16_t* orow = om.row(tl.o_row + row);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t col0 = SWIGLU ? (int64_t)tl.nt * 128 + wn * 64 + j * 32
-                                  : (int64_t)tl.nt * BN + wn * 128 + j * 32;
-      if (!SWIGLU && col0 >= N) continue;
-      uint32_t q[4][2];
-      if constexpr (SWIGLU) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            float v[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int r = 4 * b + 2 * p + e;
-              const float z = acc[i][j][r];
-              // silu(z) * a3 = z * a3 / (1 + e^-z), e^-z = 2^(-z * log2(e)):
-              // hardware exp2 and reciprocal (the result is rounded to bf16)
-              v[e] = z * acc[i][j + 2][r] *
-                     __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
-            }
-            q[b][p] = pack_bf16x2(v[0], v[1]);
-          }
-      } else {
-        pack_runs(acc[i][j], q);
-      }
-      emit(q, orow, col0, ok);
-      if constexpr (SWIGLU) {
-        if (om.a13) {             // the pre-activations a1 and a3 as well
-          uint16_t* r13 = om.a13 + (tl.o_row + row) * om.ld13;
-          uint32_t q1[4][2], q3[4][2];
-          pack_runs(acc[i][j], q1);
-          pack_runs(acc[i][j + 2], q3);
-          emit(q1, r13, col0, ok);
-          emit(q3, r13, col0 + N, ok);
-        }
-      }
-    }
-  }
-}
-
-// fp32 partial of a split tile, in register order: register group q of
-// fragment (i, j) of wave w, c = (i*4 + j)*4 + q, lands at
-// ((w*16*FI + c)*64 + lane)*4 (1 KiB per store instruction).
-template <int FI>
-__device__ __forceinline__ int64_t part_off(int w, int c, int lane) {
-  return ((int64_t)(w * 16 * FI + c) * 64 + lane) * 4;
-}
-
-// One (64*FI) x 256 output tile, or one K part of it.  Waves form a 2x2
-// grid: wave (wm, wn) owns rows wm*32*FI + [0, 32*FI) and columns
-// wn*128 + [0, 128), i.e. FI x 4 MFMA fragments.
-template <bool SWIGLU, int FI>
-__device__ __forceinline__ void tile_body(const GroupedGemmArgs& a, const Tile& tl, int part,
-                                          int parts, int64_t slot, uint8_t* smem) {
-  constexpr int WR = 16 * FI;   // A rows each wave copies: 2*FI blocks of 8
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
-  const int K = a.K, N = a.N;
-  const int nk = K / BK;
-  const bool shared = !a.kgroup && tl.g >= a.E_routed;
-  const bool a_shared = shared && !a.a_from_out_rows;
-  const uint16_t* A = (const uint16_t*)(a_shared ? a.A_shared : a.A);
-  const int lda = a_shared ? a.lda_shared : a.lda;
-  const int ldb = a.ldb ? a.ldb : K;              // weights: dense [out, K]
-  const uint32_t browbytes = (uint32_t)ldb * 2;
-  const uint32_t arowbytes = (uint32_t)lda * 2;
-  const uint16_t* B0 = (const uint16_t*)(shared ? a.B0s : a.B0);
-  const uint16_t* B1 = (const uint16_t*)(shared ? a.B1s : a.B1);
-  if (!shared && !a.kgroup) {
-    B0 += (int64_t)tl.g * a.b_stride;
-    if (SWIGLU || a.b_split) B1 += (int64_t)tl.g * a.b_stride;
-  }
-  // K slices [kbeg, kbeg + nsteps): the group's own K range (weight
-  // gradients), or part `part` of K; a whole tile of a routed group starts
-  // at slice g*nk/8 and wraps around
-  int kbeg, nsteps;
-  if (a.kgroup) {
-    kbeg = __builtin_amdgcn_readfirstlane(a.ktab[tl.g] / BK);
-    nsteps = __builtin_amdgcn_readfirstlane(a.ktab[a.kt_size + tl.g] / BK);
-  } else {
-    kbeg = (int)((int64_t)part * nk / parts);
-    nsteps = (int)((int64_t)(part + 1) * nk / parts) - kbeg;
-  }
-  const int krot = (parts == 1 && a.rotate_k && !shared && !a.kgroup)
-                       ? (int)(((int64_t)tl.g * nk / 8) % nk) : 0;
-
-  // Global -> LDS copies: wave w fills rows w*WR .. w*WR+WR-1 of the A slice
-  // and rows w*64 .. w*64+63 of the B slice, 8 rows (1 KiB) per instruction;
-  // lane l lands at byte 16*l of the block: row l >> 3, stored chunk l & 7,
-  // which holds logical chunk (l & 7) ^ swz(row).  For block i of A,
-  // row = w*WR + 8*i + (l >> 3), so swz(row) = (l >> 3) ^ ((2*FI*w + i) & 7);
-  // for B it is (l >> 3) ^ i.
-  const int a_rows = __builtin_amdgcn_readfirstlane(min(max(tl.m_valid - w * WR, 0), WR));
-  const rsrc_t rsA = make_rsrc(A + (tl.a_row + w * WR) * (int64_t)lda, (uint32_t)a_rows * arowbytes);
-  rsrc_t rsB;
-  if (SWIGLU) {
-    // B rows of the tile: [w1 f0.. | w3 f0.. | w1 f0+64.. | w3 f0+64..], 64 each
-    const uint16_t* W = (w & 1) ? B1 : B0;
-    rsB = make_rsrc(W + ((int64_t)tl.nt * 128 + (w >> 1) * 64) * K, 64u * browbytes);
-  } else {
-    // b_split: rows [0, N/2) of B come from B0, [N/2, N) from B1 (64-row
-    // blocks never straddle N/2, a multiple of 64)
-    int64_t brow = (int64_t)tl.nt * BN + w * 64;
-    int64_t nrows = N;
-    const uint16_t* Bb = B0;
-    if (a.b_split) {
-      nrows = N / 2;
-      if (brow >= nrows) {
-        Bb = B1;
-        brow -= nrows;
-      }
-    }
-    const int nb = __builtin_amdgcn_readfirstlane(
-        (int)min(max(nrows - brow, (int64_t)0), (int64_t)64));
-    rsB = make_rsrc(Bb + min(brow, nrows - 1) * ldb, (uint32_t)nb * browbytes);
-  }
-  uint32_t voffA[2 * FI], voffB[8];
-#pragma unroll
-  for (int i = 0; i < 2 * FI; ++i) {
-    const uint32_t c = (uint32_t)((((lane & 7) ^ (lane >> 3) ^ (2 * FI * w + i)) & 7) << 4);
-    voffA[i] = (uint32_t)(lane >> 3) * arowbytes + c;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t c = (uint32_t)((((lane & 7) ^ (lane >> 3) ^ i) & 7) << 4);
-    voffB[i] = (uint32_t)(lane >> 3) * browbytes + c;
-  }
-  uint8_t* const dstA = smem + w * (WR * BK * 2);
-  uint8_t* const dstB = smem + kOffB + w * 8192;
-
-  // MFMA operand reads: lane l reads row (l & 31) of a 32-row fragment and
-  // logical chunk 2*s + (l >> 5) of sub-step s.  The fragment's first row
-  // is a multiple of 32, 32*q say, and swz of its row is
-  // (l & 7) ^ (4*(q & 1) + ((l >> 3) & 3)): q = FI*wm + i for A fragment i,
-  // q = 4*wn + j for B fragment j.
-  const int rA = (wm * 32 * FI + (lane & 31)) * (BK * 2);
-  const int rB = (wn * 128 + (lane & 31)) * (BK * 2);
-  const int fe = (lane & 7) ^ ((lane >> 3) & 3);
-  const int fo = (lane & 7) ^ (4 | ((lane >> 3) & 3));
-  const bool aflip = (FI * wm) & 1;   // A fragment i has parity (i & 1) ^ aflip
-  int cx[4][2], cxa[4][2];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    cx[s][0] = ((2 * s + (lane >> 5)) ^ fe) << 4;
-    cx[s][1] = ((2 * s + (lane >> 5)) ^ fo) << 4;
-    cxa[s][0] = aflip ? cx[s][1] : cx[s][0];
-    cxa[s][1] = aflip ? cx[s][0] : cx[s][1];
-  }
-
-  floatx16 acc[FI][4];
-#pragma unroll
-  for (int i = 0; i < FI; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  bf16x8 fa0[FI], fb0[4], fa1[FI], fb1[4];
-
-#define SB() __builtin_amdgcn_sched_barrier(0)
-// weight fragment as the MFMA's first operand: the accumulator holds C^T,
-// so each lane ends up with runs of 4 consecutive output columns of one row
-#define MF(FA, FB, I, J) \
-  acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[J], FA[I], acc[I][J], 0, 0, 0)
-#define RDA(F, SA, S, I) F[I] = lds_frag((SA) + rA + (I) * 4096 + cxa[S][(I) & 1])
-#define RDB(F, SBP, S, J) F[J] = lds_frag((SBP) + rB + (J) * 4096 + cx[S][(J) & 1])
-// K slice of step KT (rotated); past the end the offset leaves the buffer
-// and the copy returns zeros
-#define KSL(KT) (kbeg + ((KT) + krot >= nsteps ? (KT) + krot - nsteps : (KT) + krot))
-#define KOFF(KT) ((KT) < nsteps ? (uint32_t)KSL(KT) * (BK * 2) : 0x7FFFFFF0u)
-#define DMA_A(KT, I)                                                                          \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                   \
-      rsA, LDS_AS(dstA + ((KT) % kSlotsA) * kPart + (I) * 1024), 16, voffA[I],                \
-      (KT) < nsteps ? (uint32_t)(I) * 8u * arowbytes + KOFF(KT) : KOFF(KT), 0, 0)
-#define DMA_B(KT, I)                                                                          \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                   \
-      rsB, LDS_AS(dstB + ((KT) & 1) * kPart + (I) * 1024), 16, voffB[I],                      \
-      (KT) < nsteps ? (uint32_t)(I) * 8u * browbytes + KOFF(KT) : KOFF(KT), 0, 0)
-// One sub-step: groups of [copy] [fragment reads for the next sub-step]
-// [2 MFMAs]; 4*FI MFMAs and FI + 4 reads per sub-step.  MFMA pair p of a
-// sub-step uses A fragment p/2 (FI = 4) and every B fragment within the
-// first two pairs, so the reads go B-first: each fragment is read at least
-// five pairs (four for FI <= 2) before the pair that uses it.  EARLY (the
-// sub-step before the slice barrier, whose wait covers every read) puts all
-// reads in the first half, so they have landed when the wait comes.
-#define SUBSTEP(FA, FB, RFA, RFB, SA, SBP, S, COPY, EARLY)                                 \
-  if constexpr (FI == 4 && !(EARLY)) {                                                     \
-    COPY(0); RDB(RFB, SBP, S, 0); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                  \
-    COPY(1); RDB(RFB, SBP, S, 1); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                  \
-    COPY(2); RDA(RFA, SA, S, 0); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB();                   \
-    COPY(3); RDB(RFB, SBP, S, 2); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                  \
-    COPY(4); RDB(RFB, SBP, S, 3); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();                  \
-    COPY(5); RDA(RFA, SA, S, 1); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                   \
-    COPY(6); RDA(RFA, SA, S, 2); MF(FA, FB, 3, 0); MF(FA, FB, 3, 1); SB();                   \
-    COPY(7); RDA(RFA, SA, S, 3); MF(FA, FB, 3, 2); MF(FA, FB, 3, 3); SB();                   \
-  } else if constexpr (FI == 4) {                                                          \
-    COPY(0); RDB(RFB, SBP, S, 0); RDB(RFB, SBP, S, 1); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB(); \
-    COPY(1); RDA(RFA, SA, S, 0); RDB(RFB, SBP, S, 2); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB(); \
-    COPY(2); RDB(RFB, SBP, S, 3); RDA(RFA, SA, S, 1); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB(); \
-    COPY(3); RDA(RFA, SA, S, 2); RDA(RFA, SA, S, 3); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB(); \
-    COPY(4); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();                                     \
-    COPY(5); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                                     \
-    COPY(6); MF(FA, FB, 3, 0); MF(FA, FB, 3, 1); SB();                                     \
-    COPY(7); MF(FA, FB, 3, 2); MF(FA, FB, 3, 3); SB();                                     \
-  } else if constexpr (FI == 3 && !(EARLY)) {                                              \
-    COPY(0); RDB(RFB, SBP, S, 0); RDB(RFB, SBP, S, 1); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB(); \
-    COPY(1); RDA(RFA, SA, S, 0); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                   \
-    COPY(2); RDB(RFB, SBP, S, 2); RDB(RFB, SBP, S, 3); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB(); \
-    COPY(3); RDA(RFA, SA, S, 1); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                   \
-    COPY(4); RDA(RFA, SA, S, 2); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();                   \
-    COPY(5); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                                     \
-  } else if constexpr (FI == 3) {                                                          \
-    COPY(0); RDB(RFB, SBP, S, 0); RDB(RFB, SBP, S, 1); MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB(); \
-    COPY(1); RDA(RFA, SA, S, 0); RDB(RFB, SBP, S, 2); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB(); \
-    COPY(2); RDB(RFB, SBP, S, 3); RDA(RFA, SA, S, 1); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB(); \
-    COPY(3); RDA(RFA, SA, S, 2); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                   \
-    COPY(4); MF(FA, FB, 2, 0); MF(FA, FB, 2, 1); SB();                                     \
-    COPY(5); MF(FA, FB, 2, 2); MF(FA, FB, 2, 3); SB();                                     \
-  } else if constexpr (FI == 2) {                                                          \
-    COPY(0); RDB(RFB, SBP, S, 0); RDB(RFB, SBP, S, 1); RDA(RFA, SA, S, 0);                   \
-    MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                                              \
-    COPY(1); RDB(RFB, SBP, S, 2); RDB(RFB, SBP, S, 3); if constexpr (EARLY) RDA(RFA, SA, S, 1); \
-    MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB();                                              \
-    COPY(2); if constexpr (!(EARLY)) RDA(RFA, SA, S, 1); MF(FA, FB, 1, 0); MF(FA, FB, 1, 1); SB(); \
-    COPY(3); MF(FA, FB, 1, 2); MF(FA, FB, 1, 3); SB();                                     \
-  } else {                                                                                 \
-    COPY(0); RDA(RFA, SA, S, 0); RDB(RFB, SBP, S, 0); RDB(RFB, SBP, S, 1);                   \
-    MF(FA, FB, 0, 0); MF(FA, FB, 0, 1); SB();                                              \
-    COPY(1); RDB(RFB, SBP, S, 2); RDB(RFB, SBP, S, 3); MF(FA, FB, 0, 2); MF(FA, FB, 0, 3); SB(); \
-  }
-
-  // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
-  // expcnt and lgkmcnt left at "no wait")
-#define VMCNT(n) (0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
-#define VMCNT_LGKM0(n) (VMCNT(n) & ~0x0F00)
-  constexpr int kWaitAll = VMCNT(0);
-  constexpr int kWaitLoop = VMCNT_LGKM0(2 * FI);       // A(kt+2) may stay in flight
-  constexpr int kWaitPrologue = VMCNT_LGKM0(2 * FI + 8);
-// Workgroup barrier without a memory fence.  __syncthreads() would release
-// every copy issued so far (a wait for all of them, in-flight A(kt+2)
-// included); what the ring needs is narrower and is waited for explicitly
-// just before: this wave's copies up to slice kt+1 landed (vmcnt) and its
-// fragment reads of the retiring slots done (lgkmcnt).  The asm's memory
-// clobber keeps the compiler from moving LDS accesses across it.
-#define WG_BARRIER(WAIT)                      \
-  __builtin_amdgcn_s_waitcnt(WAIT);           \
-  asm volatile("s_barrier" ::: "memory")
-
-  // Prologue: A(0), B(0), A(1), B(1) in flight; wait for slice 0.
-#pragma unroll
-  for (int i = 0; i < 2 * FI; ++i) DMA_A(0, i);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) DMA_B(0, i);
-#pragma unroll
-  for (int i = 0; i < 2 * FI; ++i) DMA_A(1, i);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) DMA_B(1, i);
-  WG_BARRIER(kWaitPrologue);
-#pragma unroll
-  for (int i = 0; i < FI; ++i) RDA(fa0, smem, 0, i);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) RDB(fb0, smem + kOffB, 0, j);
-
-  // Step kt (slice kt in A slot kt%3, B slot kt%2; sub-step 0 fragments
-  // already in registers):
-  //   s0..s2: MFMAs of sub-steps 0..2, reads of sub-steps 1..3, and the
-  //       2*FI copies of A(kt+2) spread over them (its slot held slice
-  //       kt-1, retired at the previous barrier);
-  //   wait until at most 2*FI copies (A(kt+2)'s) may be in flight ->
-  //   A(kt+1), B(kt+1) landed;
-  //   barrier: slice kt+1 visible to all, slice kt's slots free
-  //   s3: MFMAs of sub-step 3, reads of slice kt+1 sub-step 0, the 8 copies
-  //       of B(kt+2) into slice kt's B slot.
-  //   Copies complete in issue order, so "at most 2*FI copies in flight" at
-  //   the next barrier means everything up to B(kt+2) has landed.  Keeping
-  //   the copies apart keeps the address unit from backing up the waves'
-  //   in-order issue (and with it the MFMAs).
-  for (int kt = 0; kt < nsteps; ++kt) {
-    const uint8_t* sa = smem + (kt % kSlotsA) * kPart;
-    const uint8_t* sbb = smem + kOffB + (kt & 1) * kPart;
-    const uint8_t* na = smem + ((kt + 1) % kSlotsA) * kPart;
-    const uint8_t* nbb = smem + kOffB + ((kt + 1) & 1) * kPart;
-// A(kt+2): FI = 4: blocks 0-2, 3-5, 6-7 in sub-steps 1, 2, 3; FI = 3:
-// blocks 0-1, 2-3, 4-5; FI = 2: blocks 0-1, 2, 3; FI = 1: blocks 0, 1.
-// B(kt+2) after the barrier, one or two per MFMA pair.
-#define COPY_A1(I)                                                                 \
-  if constexpr (FI == 4) {                                                         \
-    if ((I) == 1 || (I) == 4 || (I) == 7) DMA_A(kt + 2, (I) / 3);                  \
-  } else if constexpr (FI == 3) {                                                  \
-    if ((I) == 1 || (I) == 4) DMA_A(kt + 2, (I) / 4);                              \
-  } else if constexpr (FI == 2) {                                                  \
-    if ((I) == 1 || (I) == 3) DMA_A(kt + 2, (I) / 2);                              \
-  } else {                                                                         \
-    if ((I) == 1) DMA_A(kt + 2, 0);                                                \
-  }
-#define COPY_A2(I)                                                                 \
-  if constexpr (FI == 4) {                                                         \
-    if ((I) == 1 || (I) == 4 || (I) == 7) DMA_A(kt + 2, 3 + (I) / 3);              \
-  } else if constexpr (FI == 3) {                                                  \
-    if ((I) == 1 || (I) == 4) DMA_A(kt + 2, 2 + (I) / 4);                          \
-  } else if constexpr (FI == 2) {                                                  \
-    if ((I) == 2) DMA_A(kt + 2, 2);                                                \
-  } else {                                                                         \
-    if ((I) == 1) DMA_A(kt + 2, 1);                                                \
-  }
-#define COPY_A3(I)                                                                 \
-  if constexpr (FI == 4) {                                                         \
-    if ((I) == 2 || (I) == 6) DMA_A(kt + 2, 6 + (I) / 4);                          \
-  } else if constexpr (FI == 3) {                                                  \
-    if ((I) == 1 || (I) == 4) DMA_A(kt + 2, 4 + (I) / 4);                          \
-  } else if constexpr (FI == 2) {                                                  \
-    if ((I) == 2) DMA_A(kt + 2, 3);                                                \
-  }
-#define COPY_B(I)                                                                  \
-  if constexpr (FI == 3) {                                                         \
-    if ((I) < 2) {                                                                 \
-      DMA_B(kt + 2, 2 * (I));                                                      \
-      DMA_B(kt + 2, 2 * (I) + 1);                                                  \
-    } else {                                                                       \
-      DMA_B(kt + 2, (I) + 2);                                                      \
-    }                                                                              \
-  } else {                                                                         \
-    _Pragma("unroll") for (int u = 0; u < 8 / (2 * FI); ++u)                       \
-        DMA_B(kt + 2, (I) * (8 / (2 * FI)) + u);                                   \
-  }
-    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 1, COPY_A1, false);
-    SUBSTEP(fa1, fb1, fa0, fb0, sa, sbb, 2, COPY_A2, false);
-    SUBSTEP(fa0, fb0, fa1, fb1, sa, sbb, 3, COPY_A3, true);
-    WG_BARRIER(kWaitLoop);
-    SUBSTEP(fa1, fb1, fa0, fb0, na, nbb, 0, COPY_B, true);
-#undef COPY_A1
-#undef COPY_A2
-#undef COPY_A3
-#undef COPY_B
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitAll);
-#undef SB
-#undef MF
-#undef RDA
-#undef RDB
-#undef KSL
-#undef KOFF
-#undef DMA_A
-#undef DMA_B
-#undef SUBSTEP
-#undef VMCNT
-#undef VMCNT_LGKM0
-#undef WG_BARRIER
-
-  if (parts > 1) {
-    float* P = a.partials + (slot * parts + part) * (int64_t)(256 * 256);
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = (i * 4 + j) * 4 + q;
-          *reinterpret_cast<floatx4*>(P + part_off<FI>(w, c, lane)) =
-              floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        }
-    return;
-  }
-  store_tile<SWIGLU, FI>(acc, tl, lane, wm, wn, out_map(a, tl.g), N);
-}
-
-template <bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GroupedGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];   // 160 KiB
-
-  const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
-  const int nk = a.K / BK;
-  Work wk{-1, 0, 1, 0};
-  Tile tl;
-  if (a.kgroup) {
-    // every group: MT x NT tiles of its m_fixed x N output, row tile fastest
-    const int MT = (a.m_fixed + BM - 1) / BM;
-    const int64_t L = blockIdx.x;
-    if (L >= (int64_t)a.G * MT * NT) return;
-    const int64_t per = (int64_t)MT * NT;
-    const int gl = (int)(L / per);                // group within this launch
-    tl.g = a.kg0 + gl;
-    const int64_t rem = L - (int64_t)gl * per;
-    tl.nt = (int)(rem / MT);
-    tl.mt = (int)(rem - (int64_t)tl.nt * MT);
-    tl.m_valid = min(BM, a.m_fixed - tl.mt * BM);
-    tl.a_row = (int64_t)tl.mt * BM;
-    tl.o_row = tl.a_row;
-    wk.L = L;
-  } else {
-    wk = plan_work(a, a.gtab[a.G], NT, nk, blockIdx.x);
-    if (wk.L < 0) return;
-    tl = tile_of(a, a.gtab, NT, wk.L, BM);
-  }
-  // Tile fields are workgroup-uniform; saying so keeps the buffer
-  // descriptors in scalar registers.
-  tl.g = __builtin_amdgcn_readfirstlane(tl.g);
-  tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
-  tl.m_valid = __builtin_amdgcn_readfirstlane(tl.m_valid);
-  tl.a_row = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tl.a_row >> 32)) << 32) |
-             (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.a_row);
-  tl.o_row = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tl.o_row >> 32)) << 32) |
-             (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.o_row);
-  const int part = __builtin_amdgcn_readfirstlane(wk.part);
-  const int parts = __builtin_amdgcn_readfirstlane(wk.parts);
-  const int fi = frags_of(tl.m_valid);
-  if (fi == 4)
-    tile_body<SWIGLU, 4>(a, tl, part, parts, wk.slot, smem);
-  else if (fi == 3)
-    tile_body<SWIGLU, 3>(a, tl, part, parts, wk.slot, smem);
-  else if (fi == 2)
-    tile_body<SWIGLU, 2>(a, tl, part, parts, wk.slot, smem);
-  else
-    tile_body<SWIGLU, 1>(a, tl, part, parts, wk.slot, smem);
-}
-
-template <bool SWIGLU, int FI>
-__device__ __forceinline__ void reduce_body(const GroupedGemmArgs& a, const Tile& tl, int s,
-                                            int64_t slot) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  floatx16 acc[FI][4];
-  const float* P0 = a.partials + slot * s * (int64_t)(256 * 256);
-  // Per row block: the 16 loads of a part are issued together, then added;
-  // parts are added in part order (the sum is the same for every launch).
-#pragma unroll
-  for (int i = 0; i < FI; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    for (int p = 0; p < s; ++p) {
-      const float* P = P0 + p * (int64_t)(256 * 256);
-      floatx4 v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        v[u] = *reinterpret_cast<const floatx4*>(P + part_off<FI>(w, i * 16 + u, lane));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[j * 4 + q][e];
-    }
-  }
-  store_tile<SWIGLU, FI>(acc, tl, lane, w >> 1, w & 1, out_map(a, tl.g), a.N);
-}
-
-// Sums the K parts of the split tiles (in part order) and stores them like
-// the GEMM kernel does.  Workgroup b handles split tile b.
-template <bool SWIGLU>
-__global__ __launch_bounds__(256) void gemm_bf16_reduce_kernel(GroupedGemmArgs a) {
-  const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
-  const int nk = a.K / BK;
-  int64_t V, whole;
-  int s;
-  split_shape(a, a.gtab[a.G], NT, nk, V, whole, s);
-  const int64_t slot = blockIdx.x;
-  if (s < 2 || whole + slot >= V) return;
-  const Tile tl = tile_of(a, a.gtab, NT, whole + slot, BM);
-  const int fi = frags_of(tl.m_valid);
-  if (fi == 4)
-    reduce_body<SWIGLU, 4>(a, tl, s, slot);
-  else if (fi == 3)
-    reduce_body<SWIGLU, 3>(a, tl, s, slot);
-  else if (fi == 2)
-    reduce_body<SWIGLU, 2>(a, tl, s, slot);
-  else
-    reduce_body<SWIGLU, 1>(a, tl, s, slot);
-}
-
 // ---------------------------------------------------------------------------
-// Eight-wave ping-pong kernel (bf16; every mode except groups split along K).
+// Eight-wave ping-pong kernel (bf16, every mode).
 //
 // 512 threads in two groups of four waves, one wave of each group on every
 // SIMD.  For a tile of 64*FI rows x 256 columns, group g owns rows
 // [32*FI*g, 32*FI*(g+1)) and its wave q the 64 columns [64q, 64q + 64): FI x 2
 // fragments of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane, so
-// two waves share a SIMD's registers).  K advances in slices of 64 (rows of
-// 128 bytes, as in the four-wave kernel) through three A slots and two B
-// slots of 32 KiB.  The two groups take turns, a barrier ending every phase:
-// while one group runs the 8*FI MFMAs of a slice from its registers at
-// raised priority, the other reads its fragments of its next slice from LDS
-// into registers and issues global -> LDS copies: group 0 the B slice t + 1
-// while it reads slice t, group 1 the A slice t + 2.  A wave's copies and
-// LDS reads thus never sit between its own MFMAs, and the MFMA pipe of every
+// two waves share a SIMD's registers).  K advances in slices of 64, copied
+// global -> LDS directly (buffer_load_dwordx4 ... lds, 8 rows of 128 bytes
+// per instruction, no registers in between; buffer bounds return zeros for
+// rows past a ragged group's end) through three A slots and two B slots of
+// 32 KiB (all 160 KiB of LDS).  The two groups take turns, a barrier ending
+// every phase: while one group runs the 8*FI MFMAs of a slice from its
+// registers at raised priority, the other reads its fragments of its next
+// slice from LDS into registers and issues global -> LDS copies: group 0
+// the B slice t + 1 while it reads slice t, group 1 the A slice t + 2.  A
+// wave's copies and LDS reads thus never sit between its own MFMAs (in a
+// wave's in-order stream they held the MFMAs up), and the MFMA pipe of every
 // SIMD is fed by one wave or the other.  Slice t is read by group 0 in phase
 // 2t - 1 and by group 1 in phase 2t; B slice t + 1 goes into the slot of
 // slice t - 1 (free after phase 2t - 2) and is first read in phase 2t + 1,
 // A slice t + 2 into the slot of slice t - 1 and first read in phase 2t + 3;
-// each wave waits for its copies at the end of its next (MFMA) phase.  The
-// MFMAs of every accumulator come in the same K order as in the four-wave
-// kernel, so both give the same bits.
+// each wave waits for its copies at the end of its next (MFMA) phase.
+//
+// LDS rows are 128 bytes (8 chunks of 16 B); chunk c of row r is stored at
+// c ^ ((r ^ (r >> 3)) & 7).  An MFMA operand read has 16 lanes on 16
+// consecutive rows and one chunk: with this swizzle they fall in 16
+// distinct 16-byte slots of 256 bytes (64 banks).
+//
+// Epilogue: the MFMAs take the weight fragment first, so fragment (i, j)
+// holds C^T: lane l has output row (l & 31) of row fragment i and, in
+// registers 4b..4b+3, the 4 consecutive columns 8b + 4*(l >> 5) + 0..3 of
+// column fragment j.  Lanes l and l ^ 32 (same row) trade one 4-column run
+// so that each ends up with 8 consecutive columns: 16-byte stores.
 constexpr int kPPA = 3 * kPart;              // B slots follow three A slots
 constexpr int kPPLds = 5 * kPart;            // 160 KiB
 
@@ -752,8 +228,8 @@ __device__ __forceinline__ int64_t part_off_pp(int w, int c, int lane) {
   return ((int64_t)(w * 8 * FI + c) * 64 + lane) * 4;
 }
 
-// Epilogue of the ping-pong kernel: wave (grp, q) holds rows 32*FI*grp + 32i +
-// (lane & 31) and, per fragment j, C^T runs of 4 columns as in store_tile.
+// Epilogue: wave (grp, q) holds rows 32*FI*grp + 32i + (lane & 31) and, per
+// fragment j, C^T runs of 4 columns (see above).
 template <bool SWIGLU, int FI>
 __device__ __forceinline__ void store_tile_pp(const floatx16 (&acc)[FI][2], const Tile& tl,
                                               int lane, int grp, int q, const OutMap& om, int N) {
@@ -824,16 +300,18 @@ __device__ __forceinline__ void store_tile_pp(const floatx16 (&acc)[FI][2], cons
   }
 }
 
+// One tile, or one K part of it: K slices [kbeg, kbeg + nsteps) starting at
+// slice kbeg + krot and wrapping around.
 template <bool SWIGLU, int FI>
-__device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Tile& tl, int part,
-                                             int parts, int64_t slot, uint8_t* smem) {
+__device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Tile& tl, int kbeg,
+                                             int nsteps, int krot, int part, int parts,
+                                             int64_t slot, uint8_t* smem) {
   constexpr int AB = 2 * FI;    // A blocks of 8 rows each wave copies per slice
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = w >> 2, q = w & 3;
   const int K = a.K, N = a.N;
-  const int nk = K / BK;
-  const bool shared = tl.g >= a.E_routed;
+  const bool shared = !a.kgroup && tl.g >= a.E_routed;
   const bool a_shared = shared && !a.a_from_out_rows;
   const uint16_t* A = (const uint16_t*)(a_shared ? a.A_shared : a.A);
   const int lda = a_shared ? a.lda_shared : a.lda;
@@ -842,19 +320,14 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   const uint32_t arowbytes = (uint32_t)lda * 2;
   const uint16_t* B0 = (const uint16_t*)(shared ? a.B0s : a.B0);
   const uint16_t* B1 = (const uint16_t*)(shared ? a.B1s : a.B1);
-  if (!shared) {
+  if (!shared && !a.kgroup) {
     B0 += (int64_t)tl.g * a.b_stride;
     if (SWIGLU || a.b_split) B1 += (int64_t)tl.g * a.b_stride;
   }
-  // K slices [kbeg, kbeg + nsteps) (part `part` of K); a whole tile of a
-  // routed group starts at slice g*nk/8 and wraps around
-  const int kbeg = (int)((int64_t)part * nk / parts);
-  const int nsteps = (int)((int64_t)(part + 1) * nk / parts) - kbeg;
-  const int krot = (parts == 1 && a.rotate_k && !shared) ? (int)(((int64_t)tl.g * nk / 8) % nk) : 0;
 
   // Copies, 8 rows (1 KiB) per instruction; lane l lands at byte 16*l of the
   // block: row l >> 3, stored chunk l & 7, which holds logical chunk
-  // (l & 7) ^ swz(row) = (l & 7) ^ (l >> 3) ^ (m & 7) for the tile's 8-row
+  // (l & 7) ^ (row ^ (row >> 3)) & 7 = (l & 7) ^ (l >> 3) ^ (m & 7) for the 8-row
   // block m.  Group 1's wave q copies A rows q*16*FI .. (blocks m = 2*FI*q +
   // b), group 0's wave q the B rows 64q .. 64q + 63 (blocks m = 8q + b).
   rsrc_t rs0, rs1;
@@ -1052,16 +525,44 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kPPLds];   // 160 KiB
   const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
   const int nk = a.K / BK;
-  // The tile table (4G + 1 ints, at most 16.4 KiB) is staged in LDS by one
-  // parallel load, in the second B slot, which no copy touches before the
-  // first barrier; the group search then runs on LDS instead of a chain of
-  // dependent global loads.
-  int32_t* gt = reinterpret_cast<int32_t*>(smem + kPPA + kPart);
-  for (int i = threadIdx.x; i < 4 * a.G + 1; i += 512) gt[i] = a.gtab[i];
-  __syncthreads();
-  const Work wk = plan_work(a, gt[a.G], NT, nk, blockIdx.x);
-  if (wk.L < 0) return;
-  Tile tl = tile_of(a, gt, NT, wk.L, BM);
+  Work wk{-1, 0, 1, 0};
+  Tile tl;
+  int kbeg, nsteps, krot = 0;
+  if (a.kgroup) {
+    // every group: MT x NT tiles of its m_fixed x N output, row tile
+    // fastest, reduced over the group's own K range
+    const int MT = (a.m_fixed + BM - 1) / BM;
+    const int64_t L = blockIdx.x;
+    if (L >= (int64_t)a.G * MT * NT) return;
+    const int64_t per = (int64_t)MT * NT;
+    const int gl = (int)(L / per);
+    tl.g = a.kg0 + gl;
+    const int64_t rem = L - (int64_t)gl * per;
+    tl.nt = (int)(rem / MT);
+    tl.mt = (int)(rem - (int64_t)tl.nt * MT);
+    tl.m_valid = min(BM, a.m_fixed - tl.mt * BM);
+    tl.a_row = (int64_t)tl.mt * BM;
+    tl.o_row = tl.a_row;
+    kbeg = __builtin_amdgcn_readfirstlane(a.ktab[tl.g] / BK);
+    nsteps = __builtin_amdgcn_readfirstlane(a.ktab[a.kt_size + tl.g] / BK);
+    wk.L = L;
+  } else {
+    // The tile table (4G + 1 ints, at most 16.4 KiB) is staged in LDS by
+    // one parallel load, in the second B slot, which no copy touches before
+    // the first barrier; the group search then runs on LDS instead of a
+    // chain of dependent global loads.
+    int32_t* gt = reinterpret_cast<int32_t*>(smem + kPPA + kPart);
+    for (int i = threadIdx.x; i < 4 * a.G + 1; i += 512) gt[i] = a.gtab[i];
+    __syncthreads();
+    wk = plan_work(a, gt[a.G], NT, nk, blockIdx.x);
+    if (wk.L < 0) return;
+    tl = tile_of(a, gt, NT, wk.L, BM);
+    // part `part` of K; a whole tile of a routed group starts at slice
+    // g*nk/8 and wraps around
+    kbeg = (int)((int64_t)wk.part * nk / wk.parts);
+    nsteps = (int)((int64_t)(wk.part + 1) * nk / wk.parts) - kbeg;
+    if (wk.parts == 1 && a.rotate_k && tl.g < a.E_routed) krot = (int)(((int64_t)tl.g * nk / 8) % nk);
+  }
   // Tile fields are workgroup-uniform; saying so keeps the buffer
   // descriptors in scalar registers.
   tl.g = __builtin_amdgcn_readfirstlane(tl.g);
@@ -1073,15 +574,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
              (uint32_t)__builtin_amdgcn_readfirstlane((int)tl.o_row);
   const int part = __builtin_amdgcn_readfirstlane(wk.part);
   const int parts = __builtin_amdgcn_readfirstlane(wk.parts);
+  kbeg = __builtin_amdgcn_readfirstlane(kbeg);
+  nsteps = __builtin_amdgcn_readfirstlane(nsteps);
+  krot = __builtin_amdgcn_readfirstlane(krot);
   const int fi = frags_of(tl.m_valid);
   if (fi == 4)
-    tile_body_pp<SWIGLU, 4>(a, tl, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 4>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
   else if (fi == 3)
-    tile_body_pp<SWIGLU, 3>(a, tl, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 3>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
   else if (fi == 2)
-    tile_body_pp<SWIGLU, 2>(a, tl, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 2>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
   else
-    tile_body_pp<SWIGLU, 1>(a, tl, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 1>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
 }
 
 template <bool SWIGLU, int FI>
@@ -1269,42 +773,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GroupedGemmArgs a) {
 
 hipError_t launch_grouped_gemm(int dtype, bool swiglu, const GroupedGemmArgs& a,
                                hipStream_t s) {
-  if (dtype == 1 && !a.kgroup) {
+  if (dtype == 1) {
     // the ping-pong kernel: whole tiles plus at most num_cu split-part
-    // workgroups, then (with split tiles) the reduce
+    // workgroups, then (with split tiles) the reduce; groups split along K:
+    // exactly G x MT x NT tiles
     const int NT = swiglu ? a.N / 128 : (a.N + BN - 1) / BN;
-    const int64_t nb = a.max_m_tiles * NT + (a.partials ? a.num_cu : 0);
+    const int64_t nb = a.kgroup ? (int64_t)a.G * ((a.m_fixed + BM - 1) / BM) * NT
+                                : a.max_m_tiles * NT + (a.partials ? a.num_cu : 0);
     if (nb <= 0) return hipSuccess;
     if (swiglu)
       MOE_LAUNCH(gemm_pp_kernel<true>, dim3((unsigned)nb), dim3(512), 0, s, a);
     else
       MOE_LAUNCH(gemm_pp_kernel<false>, dim3((unsigned)nb), dim3(512), 0, s, a);
-    if (a.partials) {
+    if (a.partials && !a.kgroup) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       if (swiglu)
         MOE_LAUNCH(gemm_pp_reduce_kernel<true>, dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
       else
         MOE_LAUNCH(gemm_pp_reduce_kernel<false>, dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
-    }
-  } else if (dtype == 1) {
-    const int NT = swiglu ? a.N / 128 : (a.N + BN - 1) / BN;
-    // groups split along K: exactly G x MT x NT tiles
-    const int64_t nb = a.kgroup ? (int64_t)a.G * ((a.m_fixed + BM - 1) / BM) * NT
-                                : a.max_m_tiles * NT + (a.partials ? a.num_cu : 0);
-    if (nb <= 0) return hipSuccess;
-    if (swiglu)
-      MOE_LAUNCH(gemm_bf16_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, a);
-    else
-      MOE_LAUNCH(gemm_bf16_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, a);
-    if (a.partials && !a.kgroup) {
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      // one workgroup per possible split tile (fewer than num_cu)
-      if (swiglu)
-        MOE_LAUNCH(gemm_bf16_reduce_kernel<true>, dim3((unsigned)a.num_cu), dim3(256), 0, s, a);
-      else
-        MOE_LAUNCH(gemm_bf16_reduce_kernel<false>, dim3((unsigned)a.num_cu), dim3(256), 0, s, a);
     }
   } else {
     const int NT = a.N / FBN;
