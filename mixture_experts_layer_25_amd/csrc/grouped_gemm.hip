@@ -302,11 +302,16 @@ __device__ __forceinline__ void store_tile_pp(const floatx16 (&acc)[FI][2], cons
 
 // One tile, or one K part of it: K slices [kbeg, kbeg + nsteps) starting at
 // slice kbeg + krot and wrapping around.
-template <bool SWIGLU, int FI>
+template <bool SWIGLU, int FI, int NB>
 __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Tile& tl, int kbeg,
                                              int nsteps, int krot, int part, int parts,
                                              int64_t slot, uint8_t* smem) {
   constexpr int AB = 2 * FI;    // A blocks of 8 rows each wave copies per slice
+  // LDS: three A slots of kAS bytes, then NB B slots of kPart bytes
+  constexpr int kAS = NB == 3 ? FI * 8192 : kPart;
+  constexpr int kBO = 3 * kAS;
+  static_assert(NB == 2 || NB == 3, "two or three B slots");
+  static_assert(kBO + NB * kPart <= kPPLds, "LDS");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = w >> 2, q = w & 3;
@@ -371,7 +376,7 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   // 32*r has swz = (l & 7) ^ (4*(r & 1) + ((l >> 3) & 3)): A fragment i has
   // r = FI*grp + i, B fragment j has r = 2q + j.
   const int rA = (grp * 32 * FI + (lane & 31)) * (BK * 2);
-  const int rB = kPPA + (64 * q + (lane & 31)) * (BK * 2);
+  const int rB = kBO + (64 * q + (lane & 31)) * (BK * 2);
   const int fe = (lane & 7) ^ ((lane >> 3) & 3);
   const int fo = (lane & 7) ^ (4 | ((lane >> 3) & 3));
   const bool aflip = (FI * grp) & 1;   // A fragment i has parity (i & 1) ^ aflip
@@ -399,32 +404,32 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   ((T) < nsteps ? (uint32_t)(kbeg + ((T) + krot >= nsteps ? (T) + krot - nsteps : (T) + krot)) * \
                       (BK * 2)                                                                 \
                 : 0x7FFFFFF0u)
-// Copy block b of slice T: group 0 a B block into B slot T & 1, group 1 an
+// Copy block b of slice T: group 0 a B block into B slot T % NB, group 1 an
 // A block into A slot T % 3 (the caller's group decides which)
 #define PP_COPY_B(T, B)                                                                        \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
       (SWIGLU && (B) >= 4) ? rs1 : rs0,                                                        \
-      LDS_AS(smem + kPPA + ((T) & 1) * kPart + (8 * q + (B)) * 1024), 16,                      \
+      LDS_AS(smem + kBO + ((T) % NB) * kPart + (8 * q + (B)) * 1024), 16,                      \
       vrow + ((vx ^ (uint32_t)(((B)) & 7)) << 4),                                              \
       (T) < nsteps ? (uint32_t)(SWIGLU ? ((B) & 3) : (B)) * 8u * browbytes + PP_KOFF(T)        \
                    : PP_KOFF(T),                                                               \
       0, 0)
 #define PP_COPY_A(T, B)                                                                        \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
-      rs0, LDS_AS(smem + ((T) % 3) * kPart + (mbase + (B)) * 1024), 16,                        \
+      rs0, LDS_AS(smem + ((T) % 3) * kAS + (mbase + (B)) * 1024), 16,                          \
       vrow + ((vx ^ (uint32_t)((mbase + (B)) & 7)) << 4),                                      \
       (T) < nsteps ? (uint32_t)(B) * 8u * arowbytes + PP_KOFF(T) : PP_KOFF(T), 0, 0)
-// Memory phase: the group's copies (group 0: B slice T + 1, 8 blocks; group
-// 1: A slice T + 2, 2*FI blocks), then this wave's fragments of slice T.
+// Memory phase: the group's copies (group 0: B slice T + NB - 1, 8 blocks;
+// group 1: A slice T + 2, 2*FI blocks), then this wave's fragments of slice T.
 #define PP_READS(T)                                                                            \
   {                                                                                            \
     if (grp == 0) {                                                                            \
-      _Pragma("unroll") for (int c = 0; c < 8; ++c) PP_COPY_B((T) + 1, c);                     \
+      _Pragma("unroll") for (int c = 0; c < 8; ++c) PP_COPY_B((T) + NB - 1, c);                \
     } else {                                                                                   \
       _Pragma("unroll") for (int c = 0; c < AB; ++c) PP_COPY_A((T) + 2, c);                    \
     }                                                                                          \
-    const uint8_t* SA = smem + ((T) % 3) * kPart;                                              \
-    const uint8_t* SB = smem + ((T) & 1) * kPart;                                              \
+    const uint8_t* SA = smem + ((T) % 3) * kAS;                                                \
+    const uint8_t* SB = smem + ((T) % NB) * kPart;                                             \
     _Pragma("unroll") for (int k = 0; k < 4; ++k) {                                            \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) fb[k][j] =                                 \
           lds_frag(SB + rB + j * 4096 + cx[k][j]);                                             \
@@ -447,11 +452,12 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   asm volatile("s_barrier" ::: "memory");  \
   PP_SB()
 // end of a memory phase: fragments in registers; the copies just issued may
-// stay in flight (group 0: 8, group 1: 2*FI)
+// stay in flight (group 0: 8, with three B slots also the 8 before them;
+// group 1: 2*FI)
 #define PP_END_MEM()                                                \
   PP_SB();                                                          \
   if (grp == 0)                                                     \
-    __builtin_amdgcn_s_waitcnt(PP_VMCNT(8) & ~0x0F00);              \
+    __builtin_amdgcn_s_waitcnt(PP_VMCNT(NB == 3 ? 16 : 8) & ~0x0F00); \
   else                                                              \
     __builtin_amdgcn_s_waitcnt(PP_VMCNT(AB) & ~0x0F00);             \
   PP_BARRIER()
@@ -462,13 +468,26 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   //   [reads of slice t (+ copies) | barrier | MFMAs of slice t | barrier] ...
   // so that group 0's MFMAs of slice t run beside group 1's reads of slice t,
   // and group 1's MFMAs of slice t beside group 0's reads of slice t + 1.
-  // Prologue: group 0 copies B slice 0, group 1 A slices 0 and 1; slice 0
-  // has landed at the first barrier.
+  // Prologue: group 0 copies B slices 0 .. NB - 2, group 1 A slices 0 and 1;
+  // slice 0 has landed at the first barrier.
+  //
+  // A copy must land before the barrier that precedes its first reader.
+  // Group 1's A slice t + 2 (issued in its reads of slice t) is first read
+  // by group 0 after group 1's next memory phase: group 1 waits for it at
+  // the end of that phase (vmcnt(2*FI) leaves only the newer copies in
+  // flight).  Group 0's B slice t + NB - 1 (issued in its reads of slice t)
+  // is first read in its memory phase for that slice: group 0 waits for it
+  // at the end of the MFMA phase before, one phase after issuing it with two
+  // B slots, three phases after with three.
   if (grp == 0) {
 #pragma unroll
     for (int b = 0; b < 8; ++b) PP_COPY_B(0, b);
+    if (NB == 3) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) PP_COPY_B(1, b);
+    }
     PP_SB();
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_waitcnt((NB == 3 ? PP_VMCNT(8) : PP_VMCNT(0)) & ~0x0F00);
     PP_BARRIER();
   } else {
 #pragma unroll
@@ -487,11 +506,13 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
     // the last barrier of group 1 is left out, which keeps the two groups'
     // barrier counts equal (group 1 had one more at the start)
     PP_SB();
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    if (grp == 0) __builtin_amdgcn_s_waitcnt((NB == 3 ? PP_VMCNT(8) : PP_VMCNT(0)) & ~0x0F00);
     if (grp == 0 || t + 1 < nsteps) asm volatile("s_barrier" ::: "memory");
     PP_SB();
   }
-  // every copy of this wave has landed (each MFMA phase ends with vmcnt(0))
+  // the copies past the last slice (zeros from out-of-range offsets) land
+  // before the workgroup ends and its LDS is handed to another
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
 #undef PP_SB
 #undef PP_KOFF
 #undef PP_COPY_A
@@ -577,15 +598,16 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
   kbeg = __builtin_amdgcn_readfirstlane(kbeg);
   nsteps = __builtin_amdgcn_readfirstlane(nsteps);
   krot = __builtin_amdgcn_readfirstlane(krot);
+  // tiles of at most 128 rows have A slices small enough for a third B slot
   const int fi = frags_of(tl.m_valid);
   if (fi == 4)
-    tile_body_pp<SWIGLU, 4>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 4, 2>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
   else if (fi == 3)
-    tile_body_pp<SWIGLU, 3>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 3, 2>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
   else if (fi == 2)
-    tile_body_pp<SWIGLU, 2>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 2, 3>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
   else
-    tile_body_pp<SWIGLU, 1>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 1, 3>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
 }
 
 template <bool SWIGLU, int FI>
