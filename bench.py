@@ -90,7 +90,11 @@ def combine_bytes(kept_rows: int, T: int, h: int, esz: int, shared: bool) -> int
 
 # ------------------------------------------------------------ HBM traffic
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_25_amd", "csrc", "grouped_gemm.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_swiglu_worked_example_traffic.txt")
+
+
+def traffic_file(workload: str) -> str:
+    """The committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary of a workload."""
+    return os.path.join(ROOT, "profiles", f"grouped_gemm_traffic_{workload.split(':')[0]}.txt")
 
 
 def source_hash(path: str) -> str:
@@ -114,7 +118,7 @@ def measured_traffic(workload: str):
     """HBM bytes per launch of GEMM 1 from the committed counter summary, or
     None when the summary is missing, is for another workload, or was taken
     on a different version of the kernel source."""
-    kv = _machine_fields(TRAFFIC_FILE)
+    kv = _machine_fields(traffic_file(workload))
     if not kv:
         return None
     if kv.get("kernel_source_sha256_16") != source_hash(GEMM_SOURCE):
@@ -563,6 +567,8 @@ def main() -> int:
                      "traffic": (measured_traffic(_workload_name(cfg, C))
                                  if args.routing == "topk" else None),
                      "flop_per_byte": round(g1_intensity, 1),
+                     "algorithmic_bytes": g1_bytes,
+                     "algorithmic_flops": gemm1_flops(kept_all, cfg.h, cfg.F),
                      "kernel_ms": round(g1_ms, 5),
                      "pass": (f"{K} steps after the timed ones, GEMM 1's kernels (grouped GEMM "
                               "+ split-K reduce) timed by start/stop events bound to them")},

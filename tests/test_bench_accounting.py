@@ -73,3 +73,27 @@ def test_routing_stats_counts():
     # a selection bias moves the keys apart
     st = bench.routing_stats(logits, np.array([0.0, 0.5, 0.0], dtype=np.float32), assign, 2)
     assert st["near_ties"] == 0
+
+
+def test_committed_traffic_summaries_are_keyed_to_their_workload():
+    # every committed FETCH_SIZE/WRITE_SIZE summary names its workload, the
+    # kernel source it was taken on and plausible byte counts; bench.py
+    # reports its traffic only for that workload and that source
+    import glob
+    files = glob.glob(os.path.join(bench.ROOT, "profiles", "grouped_gemm_traffic_*.txt"))
+    assert files
+    for f in files:
+        w = os.path.basename(f)[len("grouped_gemm_traffic_"):-len(".txt")]
+        assert bench.traffic_file(f"{w}: T=1") == f
+        kv = bench._machine_fields(f)
+        assert kv["workload"] == w
+        assert len(kv["kernel_source_sha256_16"]) == 16
+        comp, meas = int(kv["gemm1_compulsory_bytes"]), int(kv["gemm1_hbm_bytes_per_launch"])
+        # the counters never read less than the compulsory bytes (within
+        # the calibration's rounding)
+        assert meas > 0.98 * comp > 0
+        if kv["kernel_source_sha256_16"] == bench.source_hash(bench.GEMM_SOURCE):
+            assert bench.measured_traffic(f"{w}: T=1") == meas
+        else:
+            assert bench.measured_traffic(f"{w}: T=1") is None
+    assert bench.measured_traffic("no_such_workload: T=1") is None
