@@ -131,6 +131,13 @@ def measured_traffic(workload: str):
         return None
 
 
+def fused_router_topk(dtype: str, E: int, routing: str) -> bool:
+    """bf16 layers of up to 64 experts with plain or score-drop top-k run the
+    router, top-k, gates and histogram as one kernel (stage "router"); the
+    "topk" stage then launches nothing and its events hold two markers."""
+    return dtype == "bf16" and E <= 64 and routing in ("topk", "topk_score_drop")
+
+
 # --------------------------------------------------------------------- bench
 def _workload_name(cfg, C, routing="topk"):
     s = (f"{cfg.name}: T={cfg.T} h={cfg.h} E={cfg.E} k={cfg.k} F={cfg.F} {cfg.dtype} "
@@ -385,7 +392,7 @@ def main() -> int:
                 "kernel_span_ms": round(median([es[0].elapsed_time(es[2 * NS - 1])
                                                 for es in cev]), 4)}
         cold["stage_ms"] = {name: round(median(v), 5) for name, v in ck.items()}
-        if cfg.dtype == "bf16" and cfg.E <= 16 and args.routing in ("topk", "topk_score_drop"):
+        if fused_router_topk(cfg.dtype, cfg.E, args.routing):
             cold["stage_ms"]["topk"] = None
 
     # load-balance statistics of the last step's routing (not part of the
@@ -535,11 +542,7 @@ def main() -> int:
             d.update(extra)
         return d
 
-    # bf16 layers of up to 16 experts with plain or score-drop top-k run the
-    # router, top-k, gates and histogram as one kernel (stage "router"); the
-    # "topk" stage then launches nothing and its events hold two markers
-    fused_front = (cfg.dtype == "bf16" and cfg.E <= 16
-                   and args.routing in ("topk", "topk_score_drop"))
+    fused_front = fused_router_topk(cfg.dtype, cfg.E, args.routing)
     front = ["router", "scan", "assign"] + ([] if fused_front else ["topk"])
     out = {
         "metric": metric_label(cfg.T, cfg.h, cfg.E, cfg.k),

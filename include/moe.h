@@ -149,7 +149,7 @@ extern "C" {
  *   offsets, GEMM tile table), 3 assign (ranks, rows), 4 permute copy,
  *   5 grouped GEMM 1 + SwiGLU (+ its split-K reduce), 6 grouped GEMM 2
  *   (+ reduce), 7 combine.  (Routing variants launch their own kernels in
- *   stages 1-4.)  bf16 layers of up to 16 experts with TOPK or
+ *   stages 1-4.)  bf16 layers of up to 64 experts with TOPK or
  *   TOPK_SCORE_DROP routing run the router, the top-k, the gates and the
  *   histogram as one kernel in stage 0; their stage 1 launches no kernel.
  *   MOE_NUM_EVENTS events, a start and a stop per stage, time them (see

@@ -811,11 +811,11 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   void* xperm = at<char>(ws, L.xperm);
   void* act = at<char>(ws, L.act);
   void* yperm = at<char>(ws, L.yperm);
-  // the router fused with the top-k (bf16, up to 16 experts, plain or
-  // score-drop token choice): one histogram row per workgroup of 16 tokens
+  // the router fused with the top-k (bf16, up to 64 experts, plain or
+  // score-drop token choice): one histogram row per router workgroup
   const bool fused = moe::router_topk_fused(c.dtype, c.E) &&
                      (c.routing == MOE_ROUTE_TOPK || c.routing == MOE_ROUTE_TOPK_SCORE_DROP);
-  const int hg = fused ? moe::kRouteFusedTokens : moe::topk_tokens_per_wg(c.E);
+  const int hg = fused ? moe::router_topk_tokens(c.E) : moe::topk_tokens_per_wg(c.E);
   const int64_t nch = (c.T + hg - 1) / hg;
   const int64_t rows = rows_of(c);
   const int BM = row_tile(c);

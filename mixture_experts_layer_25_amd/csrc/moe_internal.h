@@ -102,12 +102,14 @@ hipError_t launch_router(int dtype, const void* x, const void* w_router,
                          const float* logit_bias, float* logits, int64_t T,
                          int h, int E, hipStream_t s);
 
-// The router fused with top-k, gates and histogram (bf16 layers of up to 16
+// The router fused with top-k, gates and histogram (bf16 layers of up to 64
 // experts, router_topk_fused): writes logits, idx and gates like
 // launch_router + launch_topk, and, if chunk_hist is given, one histogram
-// row per kRouteFusedTokens tokens.
+// row per router_topk_tokens(E) tokens (16 up to 16 experts, else 64; at
+// least kRouteFusedTokens, a divisor of kChunkTokens).
 constexpr int kRouteFusedTokens = 16;
 bool router_topk_fused(int dtype, int E);
+int router_topk_tokens(int E);
 hipError_t launch_router_topk(const void* x, const void* w_router, const float* logit_bias,
                               float* logits, const float* select_bias, int gate, int64_t T,
                               int h, int E, int k, int32_t* idx, float* gate_out,

@@ -13,6 +13,11 @@
 // 64 experts (4x4 MFMA tiles per wave), which bounds the re-reads of
 // w_router to one per 64 tokens and keeps the grid wide.  bf16 x bf16
 // products are exact in fp32 and accumulate in fp32.
+//
+// Up to 64 experts, the router kernel also runs the top-k, the gates and the
+// expert histogram (the tile then holds every expert's logit of its tokens),
+// so the logits do not make a round trip through memory before the
+// selection and no separate top-k kernel runs.
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "topk_device.h"
@@ -262,6 +267,122 @@ __global__ __launch_bounds__(256) void router_bf16_tile_kernel(
   }
 }
 
+// The tile router of up to 64 experts fused with the top-k, the gates and
+// the histogram.  The MFMA tile covers the workgroup's 64 tokens and every
+// expert; its NW waves (8 when h is a multiple of 256, else 4) each take an
+// equal share of h, so twice the loads of router_bf16_tile_kernel are in
+// flight per compute unit.  The partial sums meet in LDS in wave order; then
+// the tokens go through the top-k in segments of 16 lanes, lane s holding
+// experts s, s + 16, ... (NPL of them), 16 * NW / 4 tokens at a time.  The
+// logits are still written out.  chunk_hist, if given, gets one row of E
+// counts per workgroup (64 tokens).
+template <int NW, int NPL>
+__global__ __launch_bounds__(64 * NW) void router_topk_tile_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, float* __restrict__ logits,
+    const float* __restrict__ sbias, int gate_mode, int64_t T, int h, int E, int k,
+    int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
+    int32_t* __restrict__ chunk_hist) {
+  static_assert(NPL * 16 <= kTileE, "up to 64 experts");
+  __shared__ float red[NW][kTileT][kRedLd];  // 68 KiB per 4 waves
+  __shared__ int32_t sel_e[kTileT][16];
+  __shared__ float sel_l[kTileT][16];
+  __shared__ int32_t hist[kTileE];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * kTileT;
+  const int kq = h / NW;                  // a multiple of 32
+  const int koff = w * kq + (lane >> 4) * 8;
+  // MFMA operands as in router_bf16_tile_kernel (one tile of 64 experts)
+  const uint16_t* ap[4];
+  const uint16_t* bp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int64_t t = t0 + 16 * i + (lane & 15);
+    t = t < T ? t : T - 1;
+    ap[i] = x + t * h + koff;
+    int e = 16 * i + (lane & 15);
+    e = e < E ? e : E - 1;
+    bp[i] = wr + (int64_t)e * h + koff;
+  }
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  int kk = 0;
+  for (; kk + 64 <= kq; kk += 64) {
+    bf16x8 a[2][4], b[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[u][i] = __builtin_bit_cast(bf16x8, ld16(ap[i] + kk + 32 * u));
+        b[u][i] = __builtin_bit_cast(bf16x8, ld16(bp[i] + kk + 32 * u));
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
+  }
+  if (kk < kq) {
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = __builtin_bit_cast(bf16x8, ld16(ap[i] + kk));
+      b[i] = __builtin_bit_cast(bf16x8, ld16(bp[i] + kk));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[w][16 * i + 4 * (lane >> 4) + r][16 * j + (lane & 15)] = acc[i][j][r];
+  if (threadIdx.x < kTileE) hist[threadIdx.x] = 0;
+  __syncthreads();
+  constexpr int kPerPass = 4 * NW;         // 16-lane segments per pass
+  const int seg = threadIdx.x >> 4, sl = threadIdx.x & 15;
+  for (int p = 0; p < kTileT / kPerPass; ++p) {
+    const int tk = p * kPerPass + seg;
+    const int64_t t = t0 + tk;
+    const bool valid = t < T;
+    float lg[NPL];
+    uint64_t key[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int ee = sl + 16 * i;
+      lg[i] = -INFINITY;
+      key[i] = 0;
+      if (valid && ee < E) {
+        float sum = red[0][tk][ee];
+#pragma unroll
+        for (int q = 1; q < NW; ++q) sum += red[q][tk][ee];
+        if (bias) sum += bias[ee];
+        logits[t * E + ee] = sum;
+        lg[i] = sum;
+        key[i] = topk_key(sbias ? sum + sbias[ee] : sum, ee);
+      }
+    }
+    topk_segment<16, NPL>(valid, sl, E, k, gate_mode, lg, key, sel_e[tk], sel_l[tk],
+                          chunk_hist ? hist : nullptr, idx_out + t * k, gate_out + t * k);
+  }
+  if (chunk_hist) {
+    __syncthreads();
+    if ((int)threadIdx.x < E) chunk_hist[blockIdx.x * (int64_t)E + threadIdx.x] = hist[threadIdx.x];
+  }
+}
+
 // fp32 layers: one thread per (token, expert), fp32 FMA over h.
 __global__ __launch_bounds__(256) void router_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wr,
@@ -281,16 +402,36 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 
 }  // namespace
 
-bool router_topk_fused(int dtype, int E) { return dtype == 1 && E <= 16; }
+bool router_topk_fused(int dtype, int E) { return dtype == 1 && E <= 64; }
+
+int router_topk_tokens(int E) { return E <= 16 ? kRouterTok : kTileT; }
 
 hipError_t launch_router_topk(const void* x, const void* w_router, const float* logit_bias,
                               float* logits, const float* select_bias, int gate, int64_t T,
                               int h, int E, int k, int32_t* idx, float* gate_out,
                               int32_t* chunk_hist, hipStream_t s) {
-  const int64_t nb = (T + kRouterTok - 1) / kRouterTok;
-  MOE_LAUNCH(router_topk_bf16_kernel, dim3((unsigned)nb), dim3(64 * router_waves(h)), 0, s,
-             (const uint16_t*)x, (const uint16_t*)w_router, logit_bias, logits, select_bias,
-             gate, T, h, E, k, idx, gate_out, chunk_hist);
+  const int tok = router_topk_tokens(E);
+  const int64_t nb = (T + tok - 1) / tok;
+  if (E <= 16)
+    MOE_LAUNCH(router_topk_bf16_kernel, dim3((unsigned)nb), dim3(64 * router_waves(h)), 0, s,
+               (const uint16_t*)x, (const uint16_t*)w_router, logit_bias, logits, select_bias,
+               gate, T, h, E, k, idx, gate_out, chunk_hist);
+  else if (h % 256 == 0 && E <= 32)
+    MOE_LAUNCH((router_topk_tile_bf16_kernel<8, 2>), dim3((unsigned)nb), dim3(512), 0, s,
+               (const uint16_t*)x, (const uint16_t*)w_router, logit_bias, logits, select_bias,
+               gate, T, h, E, k, idx, gate_out, chunk_hist);
+  else if (h % 256 == 0)
+    MOE_LAUNCH((router_topk_tile_bf16_kernel<8, 4>), dim3((unsigned)nb), dim3(512), 0, s,
+               (const uint16_t*)x, (const uint16_t*)w_router, logit_bias, logits, select_bias,
+               gate, T, h, E, k, idx, gate_out, chunk_hist);
+  else if (E <= 32)
+    MOE_LAUNCH((router_topk_tile_bf16_kernel<4, 2>), dim3((unsigned)nb), dim3(256), 0, s,
+               (const uint16_t*)x, (const uint16_t*)w_router, logit_bias, logits, select_bias,
+               gate, T, h, E, k, idx, gate_out, chunk_hist);
+  else
+    MOE_LAUNCH((router_topk_tile_bf16_kernel<4, 4>), dim3((unsigned)nb), dim3(256), 0, s,
+               (const uint16_t*)x, (const uint16_t*)w_router, logit_bias, logits, select_bias,
+               gate, T, h, E, k, idx, gate_out, chunk_hist);
   return hipGetLastError();
 }
 

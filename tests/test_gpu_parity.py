@@ -51,6 +51,9 @@ MEDIUM = [
     # odd multiple of 128 (router K loop tail)
     MoEConfig("e40_ragged", T=333, h=384, E=40, k=3, F=256, gate="softmax_all_topk",
               cf=(3, 2)),
+    # 17..32 experts: the router tile's top-k runs in 32-lane segments
+    MoEConfig("e24_sigmoid_bias", T=517, h=384, E=24, k=3, F=256, gate="sigmoid_topk_norm",
+              select_bias=("normal", 0.1), cf=(5, 4)),
     # K long enough (>= 16 slices of 64) that the tiles of the last partial
     # round are split along K and reduced (GEMM 1 and GEMM 2)
     MoEConfig("split_k_tail", T=600, h=1024, E=4, k=2, F=1024, gate="softmax_topk"),
@@ -336,7 +339,7 @@ def test_random_configs_forward_and_backward(cfg):
 
 # ------------------------------------------------------------ routing variants
 SCORE_DROP = ["capacity_heavy_drop", "zipf_cf1", "worked_example_small",
-              "split_k_tail_capacity_shared", "f32_capacity"]
+              "split_k_tail_capacity_shared", "f32_capacity", "e24_sigmoid_bias"]
 
 
 @pytest.mark.parametrize("name", SCORE_DROP)
@@ -654,7 +657,8 @@ def test_load_balance_matches_oracle(name):
 
 
 STAGED = ["dropless_softmax", "capacity_heavy_drop", "sigmoid_bias_shared", "split_k_tail",
-          "f32_capacity", "f32_sigmoid_shared", "drop_all_shared"]
+          "f32_capacity", "f32_sigmoid_shared", "drop_all_shared", "e24_sigmoid_bias",
+          "zipf_cf1"]
 
 
 @pytest.mark.parametrize("hF", [(512, 512), (1024, 1024)], ids=["whole_tiles", "k_split"])
