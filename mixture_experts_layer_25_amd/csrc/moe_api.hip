@@ -815,7 +815,7 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   // score-drop token choice): one histogram row per router workgroup
   const bool fused = moe::router_topk_fused(c.dtype, c.E) &&
                      (c.routing == MOE_ROUTE_TOPK || c.routing == MOE_ROUTE_TOPK_SCORE_DROP);
-  const int hg = fused ? moe::router_topk_tokens(c.E) : moe::topk_tokens_per_wg(c.E);
+  const int hg = fused ? moe::router_topk_tokens(c.E) : moe::topk_kernel_tokens(c.E);
   const int64_t nch = (c.T + hg - 1) / hg;
   const int64_t rows = rows_of(c);
   const int BM = row_tile(c);

@@ -115,10 +115,21 @@ hipError_t launch_router_topk(const void* x, const void* w_router, const float* 
                               int h, int E, int k, int32_t* idx, float* gate_out,
                               int32_t* chunk_hist, hipStream_t s);
 
-// Tokens one top-k workgroup handles (4 passes of 256/G tokens, G = lanes
-// per token); its expert histogram covers that many tokens.  Always a
-// divisor of 256.
+// Tokens one probability-sum workgroup handles (4 passes of 256/G tokens,
+// G = seg_lanes(E)).  Always a divisor of 256.
 inline int topk_tokens_per_wg(int E) { return 4 * 256 / seg_lanes(E); }
+
+// Lanes per token of the top-k kernel: one expert per lane up to 64
+// experts; 65..256 experts in 16-lane segments (up to 16 experts per lane,
+// 16 tokens per wave); more in 64-lane segments.
+inline int topk_lanes(int E) { return E <= 64 ? seg_lanes(E) : (E <= 256 ? 16 : 64); }
+
+// Tokens one top-k workgroup handles (4 passes of 256/G tokens, G =
+// topk_lanes(E); one pass of 16 for 65..256 experts); its expert histogram
+// covers that many tokens.  Always a divisor of 256.
+inline int topk_kernel_tokens(int E) {
+  return (E > 64 && E <= 256) ? 16 : 4 * 256 / topk_lanes(E);
+}
 
 // Routing variants (choice.hip, route_scan.hip).  Expert choice: expert e
 // takes its C best tokens by probs_et[e][t]; sel_row/gate_te [T,E],

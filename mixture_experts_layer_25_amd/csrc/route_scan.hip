@@ -173,18 +173,19 @@ __global__ __launch_bounds__(1024) void gtab_kernel(const int32_t* __restrict__ 
   write_gtab(e, E, valid, off, off, BM, tmp, gtab);
 }
 
-// One workgroup (4 waves) per chunk of 256 tokens; lane = token.
+// One workgroup of NW waves per chunk of 64 * NW tokens; lane = token.
 // chunk_base rows are per group of hg tokens; chunk c starts at group
-// c * 256 / hg.
-template <int KMAX>
-__global__ __launch_bounds__(256) void assign_kernel(
+// c * gpc, gpc = 64 * NW / hg (one wave per chunk when hg <= 64, so that
+// small T still spreads over many compute units).
+template <int KMAX, int NW>
+__global__ __launch_bounds__(64 * NW) void assign_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ chunk_base, int gpc,
     const int32_t* __restrict__ offsets, int64_t T, int E, int k, int nbits,
     int64_t C, int32_t* __restrict__ assign_row, int32_t* __restrict__ row_token) {
-  __shared__ int32_t cnt[4][1024];
+  __shared__ int32_t cnt[NW][1024];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t chunk = blockIdx.x;
-  const int64_t t = chunk * kChunkTokens + tid;
+  const int64_t t = chunk * (64 * NW) + tid;
   const bool valid = t < T;
 
   // Expert ids outside [0, E) (possible only through the standalone permute
@@ -198,17 +199,17 @@ __global__ __launch_bounds__(256) void assign_kernel(
     if (!ok[j]) ex[j] = 0;
   }
 
-  for (int i = tid; i < 4 * E; i += 256) cnt[i / E][i % E] = 0;
+  for (int i = tid; i < NW * E; i += 64 * NW) cnt[i / E][i % E] = 0;
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < KMAX; ++j)
     if (ok[j]) atomicAdd(&cnt[w][ex[j]], 1);
   __syncthreads();
   // wave bases: chunk base of the expert plus the counts of earlier waves
-  for (int e = tid; e < E; e += 256) {
+  for (int e = tid; e < E; e += 64 * NW) {
     int run = chunk_base[chunk * gpc * E + e];
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const int c = cnt[ww][e];
       cnt[ww][e] = run;
       run += c;
@@ -263,12 +264,18 @@ __global__ __launch_bounds__(256) void assign_kernel(
 }
 
 template <int KMAX>
-void launch_assign_t(const int32_t* idx, const int32_t* base, int gpc, const int32_t* off,
+void launch_assign_t(const int32_t* idx, const int32_t* base, int hg, const int32_t* off,
                      int64_t T, int E, int k, int nbits, int64_t C, int32_t* ar,
                      int32_t* rt, hipStream_t s) {
-  const int64_t nch = (T + kChunkTokens - 1) / kChunkTokens;
-  MOE_LAUNCH((assign_kernel<KMAX>), dim3((unsigned)nch), dim3(256), 0, s,
-                     idx, base, gpc, off, T, E, k, nbits, C, ar, rt);
+  if (hg <= 64) {
+    const int64_t nch = (T + 63) / 64;
+    MOE_LAUNCH((assign_kernel<KMAX, 1>), dim3((unsigned)nch), dim3(64), 0, s,
+               idx, base, 64 / hg, off, T, E, k, nbits, C, ar, rt);
+  } else {
+    const int64_t nch = (T + kChunkTokens - 1) / kChunkTokens;
+    MOE_LAUNCH((assign_kernel<KMAX, 4>), dim3((unsigned)nch), dim3(256), 0, s,
+               idx, base, kChunkTokens / hg, off, T, E, k, nbits, C, ar, rt);
+  }
 }
 
 constexpr int kPermTok = 2;      // tokens per permute workgroup
@@ -436,17 +443,16 @@ hipError_t launch_assign(const int32_t* idx, const int32_t* chunk_base, int hg,
                          hipStream_t s) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  const int gpc = kChunkTokens / hg;
   if (k <= 1)
-    launch_assign_t<1>(idx, chunk_base, gpc, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+    launch_assign_t<1>(idx, chunk_base, hg, offsets, T, E, k, nbits, C, assign_row, row_token, s);
   else if (k <= 2)
-    launch_assign_t<2>(idx, chunk_base, gpc, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+    launch_assign_t<2>(idx, chunk_base, hg, offsets, T, E, k, nbits, C, assign_row, row_token, s);
   else if (k <= 4)
-    launch_assign_t<4>(idx, chunk_base, gpc, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+    launch_assign_t<4>(idx, chunk_base, hg, offsets, T, E, k, nbits, C, assign_row, row_token, s);
   else if (k <= 8)
-    launch_assign_t<8>(idx, chunk_base, gpc, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+    launch_assign_t<8>(idx, chunk_base, hg, offsets, T, E, k, nbits, C, assign_row, row_token, s);
   else
-    launch_assign_t<16>(idx, chunk_base, gpc, offsets, T, E, k, nbits, C, assign_row, row_token, s);
+    launch_assign_t<16>(idx, chunk_base, hg, offsets, T, E, k, nbits, C, assign_row, row_token, s);
   return hipGetLastError();
 }
 

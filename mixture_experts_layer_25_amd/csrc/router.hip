@@ -181,16 +181,19 @@ constexpr int kTileT = 64;           // tokens per tile
 constexpr int kTileE = 64;           // experts per tile
 constexpr int kRedLd = kTileE + 4;   // LDS row stride of the partial sums
 
-__global__ __launch_bounds__(256) void router_bf16_tile_kernel(
+// NW waves (8 when h is a multiple of 256, else 4) each take an equal share
+// of h, their partial sums meeting in LDS in wave order.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void router_bf16_tile_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, float* __restrict__ logits, int64_t T,
     int h, int E) {
-  __shared__ float red[4][kTileT][kRedLd];  // 68 KiB
+  __shared__ float red[NW][kTileT][kRedLd];  // 68 KiB per 4 waves
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * kTileT;
   const int e0 = blockIdx.y * kTileE;
-  const int kq = h >> 2;                  // h % 128 == 0: kq % 32 == 0
+  const int kq = h / NW;                  // a multiple of 32
   const int koff = w * kq + (lane >> 4) * 8;
   // Rows past T or E are clamped to the last one; their sums are dropped.
   const uint16_t* ap[4];
@@ -253,14 +256,14 @@ __global__ __launch_bounds__(256) void router_bf16_tile_kernel(
       for (int r = 0; r < 4; ++r)
         red[w][16 * i + 4 * (lane >> 4) + r][16 * j + (lane & 15)] = acc[i][j][r];
   __syncthreads();
-  for (int p = threadIdx.x; p < kTileT * kTileE; p += 256) {
+  for (int p = threadIdx.x; p < kTileT * kTileE; p += 64 * NW) {
     const int tk = p / kTileE, ee = p % kTileE;
     const int64_t t = t0 + tk;
     const int e = e0 + ee;
     if (t < T && e < E) {
-      float s = red[0][tk][ee] + red[1][tk][ee];
-      s += red[2][tk][ee];
-      s += red[3][tk][ee];
+      float s = red[0][tk][ee];
+#pragma unroll
+      for (int q = 1; q < NW; ++q) s += red[q][tk][ee];
       if (bias) s += bias[e];
       logits[t * E + e] = s;
     }
@@ -440,9 +443,12 @@ hipError_t launch_router(int dtype, const void* x, const void* w_router,
                          int h, int E, hipStream_t s) {
   if (dtype == 1 && E > 16) {
     const dim3 grid((unsigned)((T + kTileT - 1) / kTileT), (unsigned)((E + kTileE - 1) / kTileE));
-    MOE_LAUNCH(router_bf16_tile_kernel, grid, dim3(256), 0, s,
-                       (const uint16_t*)x, (const uint16_t*)w_router,
-                       logit_bias, logits, T, h, E);
+    if (h % 256 == 0)
+      MOE_LAUNCH(router_bf16_tile_kernel<8>, grid, dim3(512), 0, s, (const uint16_t*)x,
+                 (const uint16_t*)w_router, logit_bias, logits, T, h, E);
+    else
+      MOE_LAUNCH(router_bf16_tile_kernel<4>, grid, dim3(256), 0, s, (const uint16_t*)x,
+                 (const uint16_t*)w_router, logit_bias, logits, T, h, E);
   } else if (dtype == 1) {
     const int64_t nb = (T + kRouterTok - 1) / kRouterTok;
     MOE_LAUNCH(router_bf16_kernel, dim3((unsigned)nb), dim3(64 * router_waves(h)), 0, s,

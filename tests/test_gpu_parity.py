@@ -51,9 +51,14 @@ MEDIUM = [
     # odd multiple of 128 (router K loop tail)
     MoEConfig("e40_ragged", T=333, h=384, E=40, k=3, F=256, gate="softmax_all_topk",
               cf=(3, 2)),
-    # 17..32 experts: the router tile's top-k runs in 32-lane segments
+    # 17..32 and 33..64 experts: the fused router tile with 4 waves (h an
+    # odd multiple of 128) and with 8 (h a multiple of 256), two or four
+    # experts per top-k lane
     MoEConfig("e24_sigmoid_bias", T=517, h=384, E=24, k=3, F=256, gate="sigmoid_topk_norm",
               select_bias=("normal", 0.1), cf=(5, 4)),
+    MoEConfig("e20_wide", T=300, h=512, E=20, k=2, F=256, gate="softmax_all_topk", cf=(1, 1)),
+    # 65..128 experts: the top-k kernel's 16-lane segments of 8 experts
+    MoEConfig("e100_k6", T=400, h=256, E=100, k=6, F=128, gate="softmax_topk"),
     # K long enough (>= 16 slices of 64) that the tiles of the last partial
     # round are split along K and reduced (GEMM 1 and GEMM 2)
     MoEConfig("split_k_tail", T=600, h=1024, E=4, k=2, F=1024, gate="softmax_topk"),
