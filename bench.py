@@ -374,6 +374,30 @@ def main() -> int:
         comb_alone = ce[0].elapsed_time(ce[1]) * 1e3 / (10 * comb_sets)
         del sets
 
+    # The permute kernel alone (moe_permute_rows: the step's routing applied
+    # to other token tensors), cycling over enough buffer sets (tokens +
+    # dispatch buffer) that each call's operands have left the 256 MB
+    # last-level cache; 10 rounds over the sets between one pair of events.
+    perm_alone = None
+    perm_sets = 0
+    if args.routing != "expert_choice":
+        set_bytes = (cfg.T + rows) * cfg.h * esz
+        perm_sets = max(2, min(8, -(-(512 << 20) // set_bytes)))
+        psets = [(torch.empty((cfg.T, cfg.h), dtype=tdt, device=dev).normal_(),
+                  torch.empty((rows, cfg.h), dtype=tdt, device=dev)) for _ in range(perm_sets)]
+        ptok = torch.empty(rows, dtype=torch.int32, device=dev)
+        for xs, xp in psets:
+            moe.moe_permute_rows(c, xs, rs_route["assign_row"], counts, ptok, xp)
+        pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        pe[0].record()
+        for _ in range(10):
+            for xs, xp in psets:
+                moe.moe_permute_rows(c, xs, rs_route["assign_row"], counts, ptok, xp)
+        pe[1].record()
+        torch.cuda.synchronize()
+        perm_alone = pe[0].elapsed_time(pe[1]) * 1e3 / (10 * perm_sets)
+        del psets, ptok
+
     # The same step from a cold last-level cache (256 MB on the MI355X): a
     # 512 MiB fill before each step, every step's kernels timed by their own
     # events, medians reported.  Not part of `value`.
@@ -581,7 +605,10 @@ def main() -> int:
         "routing_stats": rstats,
         "hbm_copy_gbs": None if copy_gbs is None else round(copy_gbs, 1),
         "router": hbm_stage("router", rb),
-        "permute": hbm_stage("permute", pb),
+        "permute": hbm_stage("permute", pb, {
+            "standalone_us": None if perm_alone is None else round(perm_alone, 2),
+            "standalone_frac_hbm": None if perm_alone is None else frac(pb, perm_alone * 1e-3),
+            "standalone_buffer_sets": perm_sets}),
         "combine": hbm_stage("combine", cb, {
             "standalone_us": None if comb_alone is None else round(comb_alone, 2),
             "standalone_frac_hbm": None if comb_alone is None else frac(cb, comb_alone * 1e-3),

@@ -273,6 +273,23 @@ int moe_permute(const moe_cfg_t* cfg, const void* x, const int32_t* topk_idx,
                 int32_t* assign_row, int32_t* row_token, void* x_perm,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* Stage 2 with a routing already made: dispatch another [T,h] tensor by the
+ * maps moe_permute or moe_forward wrote (infra-l7, "NVIDIA 原题" row
+ * dispatch; "自测": rows sorted by expert, unused places padded).
+ *   x              [T,h] dtype
+ *   assign_row     [T*k] int32: row of (t,j), -1 if dropped
+ *   expert_counts  [E] int32: assignments per expert before dropping
+ *   row_token      [rows] int32 out: -1 written for the padding rows of the
+ *                  capacity layout (kept rows are left as they are)
+ *   x_perm         [rows,h] dtype out: x_perm[assign_row[t,j]] = x[t];
+ *                  capacity layout: rows e*C + min(counts[e], C) ..
+ *                  e*C + C - 1 are zero
+ * Token-choice routings only (TOPK, TOPK_SCORE_DROP, SINKHORN); expert
+ * choice gives MOE_ERR_UNSUPPORTED.  Needs no workspace.                  */
+int moe_permute_rows(const moe_cfg_t* cfg, const void* x, const int32_t* assign_row,
+                     const int32_t* expert_counts, int32_t* row_token, void* x_perm,
+                     void* stream);
+
 /* Stage 3: grouped GEMM running every expert's SwiGLU FFN ------------------
  * infra-l7, "MoE:参数很多" (SwiGLU FFN h->F->h) and "自测" (one grouped GEMM
  * over tokens sorted by expert); Megatron-LM part 6 (experts as GroupedGEMM).

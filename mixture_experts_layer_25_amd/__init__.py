@@ -56,7 +56,7 @@ ROUTING_BY_NAME = {
 # Every symbol include/moe.h declares.
 ABI_SYMBOLS = (
     "moe_strerror", "moe_capacity", "moe_num_rows", "moe_workspace_bytes",
-    "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu",
+    "moe_router_topk", "moe_permute", "moe_permute_rows", "moe_grouped_gemm_swiglu",
     "moe_grouped_gemm_swiglu_noalloc", "moe_unpermute_combine", "moe_load_balance", "moe_select_bias_update",
     "moe_backward_workspace_bytes",
     "moe_backward", "moe_backward_saved", "moe_forward",
@@ -125,6 +125,7 @@ def lib() -> ctypes.CDLL:
             "moe_workspace_bytes": (ctypes.c_int, [cfgp, ctypes.POINTER(SZ)]),
             "moe_router_topk": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_permute": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, SZ, P]),
+            "moe_permute_rows": (ctypes.c_int, [cfgp, P, P, P, P, P, P]),
             "moe_grouped_gemm_swiglu": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_grouped_gemm_swiglu_noalloc": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, P]),
             "moe_unpermute_combine": (ctypes.c_int, [cfgp, P, P, P, P, P, P]),
@@ -279,6 +280,17 @@ def moe_permute(cfg, x, topk_idx, expert_counts, expert_offsets, assign_row,
         _p(z, "expert_counts", expert_counts), _p(z, "expert_offsets", expert_offsets),
         _p(z, "assign_row", assign_row), _p(z, "row_token", row_token),
         _p(z, "x_perm", x_perm), wp, wb, _stream(stream)))
+
+
+def moe_permute_rows(cfg, x, assign_row, expert_counts, row_token, x_perm,
+                     stream=None) -> None:
+    """Dispatch x by a routing already made (assign_row, expert_counts from
+    moe_permute or moe_forward)."""
+    z = _sizes(cfg)
+    _check("moe_permute_rows", lib().moe_permute_rows(
+        ctypes.byref(cfg), _p(z, "x", x), _p(z, "assign_row", assign_row),
+        _p(z, "expert_counts", expert_counts), _p(z, "row_token", row_token),
+        _p(z, "x_perm", x_perm), _stream(stream)))
 
 
 def moe_grouped_gemm_swiglu(cfg, x_perm, expert_counts, expert_offsets, w1, w3, w2,

@@ -316,6 +316,21 @@ MOE_API int moe_permute(const moe_cfg_t* cfg, const void* x, const int32_t* topk
   return MOE_OK;
 }
 
+MOE_API int moe_permute_rows(const moe_cfg_t* cfg, const void* x, const int32_t* assign_row,
+                             const int32_t* expert_counts, int32_t* row_token, void* x_perm,
+                             void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const moe_cfg_t& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (c.routing == MOE_ROUTE_EXPERT_CHOICE) return MOE_ERR_UNSUPPORTED;
+  if (!x || !assign_row || !expert_counts || !row_token || !x_perm) return MOE_ERR_INVALID_ARG;
+  if (misaligned(x, assign_row, expert_counts, row_token, x_perm)) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(moe::launch_permute(c.dtype, x, assign_row, expert_counts, c.T, c.h, c.E, c.k,
+                              c.capacity, x_perm, c.h, row_token, (hipStream_t)stream));
+  return MOE_OK;
+}
+
 namespace {
 
 // The standalone grouped GEMM (both entry points): groups from the caller's

@@ -48,6 +48,7 @@ _TENSOR_ID = {
     "logit_bias": 9,
     "select_bias": 10,
     "dy": 11,           # output gradient of the backward tests and benchmark
+    "x_second": 12,     # a second token tensor dispatched by an existing routing
 }
 
 

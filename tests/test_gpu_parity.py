@@ -781,6 +781,17 @@ def test_stage_calls_equal_fused_call(name, routing, iters):
     a0 = assign.view(T, k)[:, 0].long()
     ok = a0 >= 0
     assert torch.equal(pb[a0[ok]], xb[ok])
+    # the same routing applied to another tensor (moe_permute_rows): the
+    # buffer moe_permute gives for that tensor, bit for bit, pads included
+    x2 = normal((T, h), 1.0, cfg.seed, "x_second", device=DEV, dtype=cfg.dtype)
+    want = torch.full((rows, h), 3.0, dtype=tdt, device=DEV)
+    moe.moe_permute(c, x2, idx, counts, offsets, assign, rowtok, want, ws)
+    got = torch.full((rows, h), 5.0, dtype=tdt, device=DEV)
+    rowtok2 = rowtok.clone()
+    moe.moe_permute_rows(c, x2, assign, counts, rowtok2, got)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(pb.dtype), want.view(pb.dtype))
+    assert torch.equal(rowtok2, rowtok)
 
 
 def test_deterministic():
