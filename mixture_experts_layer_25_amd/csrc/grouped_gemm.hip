@@ -218,8 +218,12 @@ __device__ __forceinline__ OutMap out_map(const GroupedGemmArgs& a, int g) {
 // registers 4b..4b+3, the 4 consecutive columns 8b + 4*(l >> 5) + 0..3 of
 // column fragment j.  Lanes l and l ^ 32 (same row) trade one 4-column run
 // so that each ends up with 8 consecutive columns: 16-byte stores.
-constexpr int kPPA = 3 * kPart;              // B slots follow three A slots
 constexpr int kPPLds = 5 * kPart;            // 160 KiB
+// slot counts of the 192- and 256-row tiles (A, B)
+constexpr int kTallNA = 3, kTallNB = 2;
+// The tile table is staged at [128 KiB, 144.4 KiB): in every slot layout
+// the copies issued before a tile's first barrier stay below 128 KiB.
+constexpr int kTableOff = 4 * kPart;
 
 // Where split-K partial register group c (= (i*2 + j)*4 + r4) of wave w goes
 // within its 256x256 fp32 tile.
@@ -302,16 +306,23 @@ __device__ __forceinline__ void store_tile_pp(const floatx16 (&acc)[FI][2], cons
 
 // One tile, or one K part of it: K slices [kbeg, kbeg + nsteps) starting at
 // slice kbeg + krot and wrapping around.
-template <bool SWIGLU, int FI, int NB>
+//
+// NA A slots and NB B slots: an operand with n slots is copied n - 1 slices
+// ahead of its reads.  With three A slots group 1 copies A and group 0 B;
+// with two A slots (and three B slots) the roles swap, so that the weight
+// operand B always has the longer lead.
+template <bool SWIGLU, int FI, int NA, int NB>
 __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Tile& tl, int kbeg,
                                              int nsteps, int krot, int part, int parts,
                                              int64_t slot, uint8_t* smem) {
   constexpr int AB = 2 * FI;    // A blocks of 8 rows each wave copies per slice
-  // LDS: three A slots of kAS bytes, then NB B slots of kPart bytes
-  constexpr int kAS = NB == 3 ? FI * 8192 : kPart;
-  constexpr int kBO = 3 * kAS;
-  static_assert(NB == 2 || NB == 3, "two or three B slots");
+  // LDS: NA A slots of kAS bytes, then NB B slots of kPart bytes
+  constexpr int kAS = (NA == 3 && NB == 2) ? kPart : FI * 8192;
+  constexpr int kBO = NA * kAS;
+  static_assert((NA == 3 && (NB == 2 || NB == 3)) || (NA == 2 && NB == 3), "slot counts");
   static_assert(kBO + NB * kPart <= kPPLds, "LDS");
+  constexpr int gA = NA == 3 ? 1 : 0;   // the group that copies A; the other copies B
+  constexpr int dA = NA - 1, dB = NB - 1;   // slices a copy runs ahead of its reads
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = w >> 2, q = w & 3;
@@ -333,11 +344,12 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   // Copies, 8 rows (1 KiB) per instruction; lane l lands at byte 16*l of the
   // block: row l >> 3, stored chunk l & 7, which holds logical chunk
   // (l & 7) ^ (row ^ (row >> 3)) & 7 = (l & 7) ^ (l >> 3) ^ (m & 7) for the 8-row
-  // block m.  Group 1's wave q copies A rows q*16*FI .. (blocks m = 2*FI*q +
-  // b), group 0's wave q the B rows 64q .. 64q + 63 (blocks m = 8q + b).
+  // block m.  In the A-copying group wave q copies A rows q*16*FI ..
+  // (blocks m = 2*FI*q + b), in the other wave q the B rows 64q .. 64q + 63
+  // (blocks m = 8q + b).
   rsrc_t rs0, rs1;
   uint32_t rowb;
-  if (grp == 1) {
+  if (grp == gA) {
     const int a_rows = __builtin_amdgcn_readfirstlane(min(max(tl.m_valid - q * 16 * FI, 0), 16 * FI));
     rs0 = make_rsrc(A + (tl.a_row + q * 16 * FI) * (int64_t)lda, (uint32_t)a_rows * arowbytes);
     rs1 = rs0;
@@ -369,7 +381,7 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   }
   const uint32_t vrow = (uint32_t)(lane >> 3) * rowb;
   const uint32_t vx = (uint32_t)((lane & 7) ^ (lane >> 3));
-  const int mbase = grp == 1 ? 2 * FI * q : 8 * q;
+  const int mbase = grp == gA ? 2 * FI * q : 8 * q;
 
   // Fragment reads: lane l reads row (l & 31) of a 32-row fragment and
   // logical chunk 2*k + (l >> 5) of sub-step k; a fragment starting at row
@@ -404,8 +416,8 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   ((T) < nsteps ? (uint32_t)(kbeg + ((T) + krot >= nsteps ? (T) + krot - nsteps : (T) + krot)) * \
                       (BK * 2)                                                                 \
                 : 0x7FFFFFF0u)
-// Copy block b of slice T: group 0 a B block into B slot T % NB, group 1 an
-// A block into A slot T % 3 (the caller's group decides which)
+// Copy block b of slice T: a B block into B slot T % NB, or an A block into
+// A slot T % NA (the caller's group decides which)
 #define PP_COPY_B(T, B)                                                                        \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
       (SWIGLU && (B) >= 4) ? rs1 : rs0,                                                        \
@@ -416,19 +428,19 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
       0, 0)
 #define PP_COPY_A(T, B)                                                                        \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
-      rs0, LDS_AS(smem + ((T) % 3) * kAS + (mbase + (B)) * 1024), 16,                          \
+      rs0, LDS_AS(smem + ((T) % NA) * kAS + (mbase + (B)) * 1024), 16,                         \
       vrow + ((vx ^ (uint32_t)((mbase + (B)) & 7)) << 4),                                      \
       (T) < nsteps ? (uint32_t)(B) * 8u * arowbytes + PP_KOFF(T) : PP_KOFF(T), 0, 0)
-// Memory phase: the group's copies (group 0: B slice T + NB - 1, 8 blocks;
-// group 1: A slice T + 2, 2*FI blocks), then this wave's fragments of slice T.
+// Memory phase: the group's copies (B slice T + dB, 8 blocks, or A slice
+// T + dA, 2*FI blocks), then this wave's fragments of slice T.
 #define PP_READS(T)                                                                            \
   {                                                                                            \
-    if (grp == 0) {                                                                            \
-      _Pragma("unroll") for (int c = 0; c < 8; ++c) PP_COPY_B((T) + NB - 1, c);                \
+    if (grp != gA) {                                                                           \
+      _Pragma("unroll") for (int c = 0; c < 8; ++c) PP_COPY_B((T) + dB, c);                    \
     } else {                                                                                   \
-      _Pragma("unroll") for (int c = 0; c < AB; ++c) PP_COPY_A((T) + 2, c);                    \
+      _Pragma("unroll") for (int c = 0; c < AB; ++c) PP_COPY_A((T) + dA, c);                   \
     }                                                                                          \
-    const uint8_t* SA = smem + ((T) % 3) * kAS;                                                \
+    const uint8_t* SA = smem + ((T) % NA) * kAS;                                               \
     const uint8_t* SB = smem + ((T) % NB) * kPart;                                             \
     _Pragma("unroll") for (int k = 0; k < 4; ++k) {                                            \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) fb[k][j] =                                 \
@@ -451,15 +463,21 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   PP_SB();                                 \
   asm volatile("s_barrier" ::: "memory");  \
   PP_SB()
-// end of a memory phase: fragments in registers; the copies just issued may
-// stay in flight (group 0: 8, with three B slots also the 8 before them;
-// group 1: 2*FI)
+// Copies in flight a group may leave at the end of its memory phase
+// (kMemLeft) and of its MFMA phase (kMfmaLeft, group 0 only): its copies
+// per slice times the slices after the one that must have landed (see
+// below).
+  constexpr int kCopies0 = gA == 0 ? AB : 8, kCopies1 = gA == 1 ? AB : 8;
+  constexpr int kLead0 = gA == 0 ? dA : dB, kLead1 = gA == 1 ? dA : dB;
+  constexpr int kMemLeft0 = kLead0 * kCopies0, kMfmaLeft0 = (kLead0 - 1) * kCopies0;
+  constexpr int kMemLeft1 = (kLead1 - 1) * kCopies1;
+// end of a memory phase: fragments in registers, copies waited as above
 #define PP_END_MEM()                                                \
   PP_SB();                                                          \
   if (grp == 0)                                                     \
-    __builtin_amdgcn_s_waitcnt(PP_VMCNT(NB == 3 ? 16 : 8) & ~0x0F00); \
+    __builtin_amdgcn_s_waitcnt(PP_VMCNT(kMemLeft0) & ~0x0F00);      \
   else                                                              \
-    __builtin_amdgcn_s_waitcnt(PP_VMCNT(AB) & ~0x0F00);             \
+    __builtin_amdgcn_s_waitcnt(PP_VMCNT(kMemLeft1) & ~0x0F00);      \
   PP_BARRIER()
   constexpr int kWaitAll = PP_VMCNT(0) & ~0x0F00;          // vmcnt(0) lgkmcnt(0)
 
@@ -468,34 +486,38 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   //   [reads of slice t (+ copies) | barrier | MFMAs of slice t | barrier] ...
   // so that group 0's MFMAs of slice t run beside group 1's reads of slice t,
   // and group 1's MFMAs of slice t beside group 0's reads of slice t + 1.
-  // Prologue: group 0 copies B slices 0 .. NB - 2, group 1 A slices 0 and 1;
-  // slice 0 has landed at the first barrier.
+  // Prologue: each group copies the first d slices of its operand (d its
+  // lead); slice 0 has landed at the first barrier.
   //
-  // A copy must land before the barrier that precedes its first reader.
-  // Group 1's A slice t + 2 (issued in its reads of slice t) is first read
-  // by group 0 after group 1's next memory phase: group 1 waits for it at
-  // the end of that phase (vmcnt(2*FI) leaves only the newer copies in
-  // flight).  Group 0's B slice t + NB - 1 (issued in its reads of slice t)
-  // is first read in its memory phase for that slice: group 0 waits for it
-  // at the end of the MFMA phase before, one phase after issuing it with two
-  // B slots, three phases after with three.
-  if (grp == 0) {
+  // A copy must land before the barrier that precedes its first reader,
+  // group 0's memory phase for that slice (after barrier 2s for slice s).
+  // A group copies slice t + d in its memory phase for slice t into the slot
+  // of slice t - 1, whose last reader (group 1, before barrier 2t) is done.
+  // Group 0 waits for slice t + 1 at the end of its MFMA phase for slice t
+  // (the copies of the d - 1 later slices may stay in flight); group 1 at
+  // the end of its memory phase for slice t.  A lead of d gives a copy about
+  // 2d - 1 phases (group 0) or 2d - 2 phases (group 1) to land.
+  if (grp == gA) {
+#pragma unroll
+    for (int b = 0; b < AB; ++b) PP_COPY_A(0, b);
+    if (dA == 2) {
+#pragma unroll
+      for (int b = 0; b < AB; ++b) PP_COPY_A(1, b);
+    }
+  } else {
 #pragma unroll
     for (int b = 0; b < 8; ++b) PP_COPY_B(0, b);
-    if (NB == 3) {
+    if (dB == 2) {
 #pragma unroll
       for (int b = 0; b < 8; ++b) PP_COPY_B(1, b);
     }
-    PP_SB();
-    __builtin_amdgcn_s_waitcnt((NB == 3 ? PP_VMCNT(8) : PP_VMCNT(0)) & ~0x0F00);
+  }
+  PP_SB();
+  if (grp == 0) {
+    __builtin_amdgcn_s_waitcnt(PP_VMCNT(kMfmaLeft0) & ~0x0F00);
     PP_BARRIER();
   } else {
-#pragma unroll
-    for (int b = 0; b < AB; ++b) PP_COPY_A(0, b);
-#pragma unroll
-    for (int b = 0; b < AB; ++b) PP_COPY_A(1, b);
-    PP_SB();
-    __builtin_amdgcn_s_waitcnt(PP_VMCNT(AB) & ~0x0F00);
+    __builtin_amdgcn_s_waitcnt(PP_VMCNT(kMemLeft1) & ~0x0F00);
     PP_BARRIER();
     PP_BARRIER();
   }
@@ -506,7 +528,7 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
     // the last barrier of group 1 is left out, which keeps the two groups'
     // barrier counts equal (group 1 had one more at the start)
     PP_SB();
-    if (grp == 0) __builtin_amdgcn_s_waitcnt((NB == 3 ? PP_VMCNT(8) : PP_VMCNT(0)) & ~0x0F00);
+    if (grp == 0) __builtin_amdgcn_s_waitcnt(PP_VMCNT(kMfmaLeft0) & ~0x0F00);
     if (grp == 0 || t + 1 < nsteps) asm volatile("s_barrier" ::: "memory");
     PP_SB();
   }
@@ -569,10 +591,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
     wk.L = L;
   } else {
     // The tile table (4G + 1 ints, at most 16.4 KiB) is staged in LDS by
-    // one parallel load, in the second B slot, which no copy touches before
-    // the first barrier; the group search then runs on LDS instead of a
-    // chain of dependent global loads.
-    int32_t* gt = reinterpret_cast<int32_t*>(smem + kPPA + kPart);
+    // one parallel load, at kTableOff, which no copy touches before the
+    // first barrier; the group search then runs on LDS instead of a chain
+    // of dependent global loads.
+    int32_t* gt = reinterpret_cast<int32_t*>(smem + kTableOff);
     for (int i = threadIdx.x; i < 4 * a.G + 1; i += 512) gt[i] = a.gtab[i];
     __syncthreads();
     wk = plan_work(a, gt[a.G], NT, nk, blockIdx.x);
@@ -598,16 +620,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
   kbeg = __builtin_amdgcn_readfirstlane(kbeg);
   nsteps = __builtin_amdgcn_readfirstlane(nsteps);
   krot = __builtin_amdgcn_readfirstlane(krot);
-  // tiles of at most 128 rows have A slices small enough for a third B slot
+  // tiles of at most 128 rows have A slices small enough for three A and
+  // three B slots; taller tiles take three A and two B slots (two A and
+  // three B, the weights given the longer lead, measured the same)
   const int fi = frags_of(tl.m_valid);
   if (fi == 4)
-    tile_body_pp<SWIGLU, 4, 2>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 4, kTallNA, kTallNB>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
   else if (fi == 3)
-    tile_body_pp<SWIGLU, 3, 2>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 3, kTallNA, kTallNB>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
   else if (fi == 2)
-    tile_body_pp<SWIGLU, 2, 3>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 2, 3, 3>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
   else
-    tile_body_pp<SWIGLU, 1, 3>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    tile_body_pp<SWIGLU, 1, 3, 3>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
 }
 
 template <bool SWIGLU, int FI>
