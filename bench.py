@@ -57,13 +57,17 @@ def expert_flops(kept_rows: int, h: int, F: int) -> int:
     return gemm1_flops(kept_rows, h, F) + gemm2_flops(kept_rows, h, F)
 
 
-def gemm1_bytes(kept_per_expert, T: int, h: int, F: int, esz: int, shared: bool) -> int:
+def gemm1_bytes(kept_per_expert, T: int, h: int, F: int, esz: int, shared: bool,
+                in_rows=None) -> int:
     """GEMM 1's compulsory HBM bytes: w1 and w3 of every expert with a row
     (and of the shared expert), the input rows read once, the activations
-    written once."""
+    written once.  The input rows are the dispatch rows, or `in_rows` token
+    rows when the GEMM gathers them from the tokens (each distinct token
+    once)."""
     active = sum(1 for n in kept_per_expert if n > 0) + (1 if shared else 0)
     rows = sum(kept_per_expert) + (T if shared else 0)
-    return (2 * active * F * h + rows * h + rows * F) * esz
+    a_rows = rows if in_rows is None else in_rows
+    return (2 * active * F * h + a_rows * h + rows * F) * esz
 
 
 def router_bytes(T: int, h: int, E: int, esz: int) -> int:
@@ -129,6 +133,13 @@ def measured_traffic(workload: str):
         return int(kv["gemm1_hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def gathered_dispatch(dtype: str, T: int, h: int) -> bool:
+    """bf16 forwards that keep no activations read GEMM 1's token rows from x
+    through row_token: no dispatch buffer is written and the permute stage
+    launches nothing (its events hold two markers)."""
+    return dtype == "bf16" and T * h * 2 < (1 << 31)
 
 
 def fused_router_topk(dtype: str, E: int, routing: str) -> bool:
@@ -418,6 +429,8 @@ def main() -> int:
         cold["stage_ms"] = {name: round(median(v), 5) for name, v in ck.items()}
         if fused_router_topk(cfg.dtype, cfg.E, args.routing):
             cold["stage_ms"]["topk"] = None
+        if gathered_dispatch(cfg.dtype, cfg.T, cfg.h):
+            cold["stage_ms"]["permute"] = None
 
     # load-balance statistics of the last step's routing (not part of the
     # step): reads the logits once (T*E*4 bytes)
@@ -540,7 +553,13 @@ def main() -> int:
     # ridge point peak / HBM bandwidth (312.5 flop/B for bf16), else bound by
     # streaming its weights (few rows per expert)
     kept_e = [min(n, C) for n in cnt] if C else cnt
-    g1_bytes = gemm1_bytes(kept_e, cfg.T, cfg.h, cfg.F, esz, cfg.shared)
+    # a gathering GEMM 1 reads each token with a kept slot (all of them with
+    # a shared expert) once
+    in_rows = None
+    if gathered_dispatch(cfg.dtype, cfg.T, cfg.h):
+        lost = rstats.get("tokens_all_dropped", rstats.get("tokens_no_expert", 0))
+        in_rows = cfg.T if cfg.shared else cfg.T - lost
+    g1_bytes = gemm1_bytes(kept_e, cfg.T, cfg.h, cfg.F, esz, cfg.shared, in_rows)
     g1_intensity = gemm1_flops(kept_all, cfg.h, cfg.F) / g1_bytes
     hbm_bound = cfg.dtype == "bf16" and g1_intensity < peak / PEAK_HBM_GBS * 1e3
     g1_gbs = g1_bytes / (g1_ms * 1e-3) / 1e9
@@ -555,6 +574,11 @@ def main() -> int:
                                 round(gbs(nbytes, ms) / copy_gbs, 4))
 
     def hbm_stage(name, nbytes, extra=None):
+        if name == "permute" and gathered:
+            # no permute kernel in the layer: only the standalone figures
+            d = {"kernel_us": None, "in_layer": "gathered by GEMM 1's copies", "bytes": nbytes}
+            d.update(extra or {})
+            return d
         d = {"kernel_us": round(stage_ms[name] * 1e3, 2),
              "kernel_us_min": round(min(kern[name]) * 1e3, 2),
              "gbs": round(gbs(nbytes, stage_ms[name]), 1), "frac_hbm": frac(nbytes, stage_ms[name]),
@@ -567,6 +591,7 @@ def main() -> int:
         return d
 
     fused_front = fused_router_topk(cfg.dtype, cfg.E, args.routing)
+    gathered = gathered_dispatch(cfg.dtype, cfg.T, cfg.h)
     front = ["router", "scan", "assign"] + ([] if fused_front else ["topk"])
     out = {
         "metric": metric_label(cfg.T, cfg.h, cfg.E, cfg.k),
@@ -613,7 +638,8 @@ def main() -> int:
             "standalone_us": None if comb_alone is None else round(comb_alone, 2),
             "standalone_frac_hbm": None if comb_alone is None else frac(cb, comb_alone * 1e-3),
             "standalone_buffer_sets": comb_sets}),
-        "stage_ms": {k: (None if (k == "topk" and fused_front) else round(v, 5))
+        "stage_ms": {k: (None if (k == "topk" and fused_front) or (k == "permute" and gathered)
+                         else round(v, 5))
                      for k, v in stage_ms.items()},
         "front_end_kernel_us": round(sum(stage_ms[n] for n in front) * 1e3, 2),
         "router_topk_fused": fused_front,

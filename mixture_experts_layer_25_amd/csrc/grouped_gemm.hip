@@ -311,7 +311,10 @@ __device__ __forceinline__ void store_tile_pp(const floatx16 (&acc)[FI][2], cons
 // ahead of its reads.  With three A slots group 1 copies A and group 0 B;
 // with two A slots (and three B slots) the roles swap, so that the weight
 // operand B always has the longer lead.
-template <bool SWIGLU, int FI, int NA, int NB>
+//
+// GATHER: the A-copying waves read routed rows through a.a_map (one source
+// row per lane and 8-row block, out of range for rows past the tile's).
+template <bool SWIGLU, int FI, int NA, int NB, bool GATHER>
 __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Tile& tl, int kbeg,
                                              int nsteps, int krot, int part, int parts,
                                              int64_t slot, uint8_t* smem) {
@@ -349,9 +352,24 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   // (blocks m = 8q + b).
   rsrc_t rs0, rs1;
   uint32_t rowb;
+  uint32_t gofs[GATHER ? AB : 1];   // GATHER: byte offset of this lane's row, per block
   if (grp == gA) {
     const int a_rows = __builtin_amdgcn_readfirstlane(min(max(tl.m_valid - q * 16 * FI, 0), 16 * FI));
-    rs0 = make_rsrc(A + (tl.a_row + q * 16 * FI) * (int64_t)lda, (uint32_t)a_rows * arowbytes);
+    if (GATHER && !a_shared) {
+      rs0 = make_rsrc(A, (uint32_t)(a.a_rows * arowbytes));
+#pragma unroll
+      for (int b = 0; b < AB; ++b) {
+        const int lr = b * 8 + (lane >> 3);
+        gofs[b] = lr < a_rows ? (uint32_t)a.a_map[tl.a_row + q * 16 * FI + lr] * arowbytes
+                              : 0x80000000u;
+      }
+    } else {
+      rs0 = make_rsrc(A + (tl.a_row + q * 16 * FI) * (int64_t)lda, (uint32_t)a_rows * arowbytes);
+      if (GATHER) {
+#pragma unroll
+        for (int b = 0; b < AB; ++b) gofs[b] = (uint32_t)(b * 8 + (lane >> 3)) * arowbytes;
+      }
+    }
     rs1 = rs0;
     rowb = arowbytes;
   } else if (SWIGLU) {
@@ -429,8 +447,8 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
 #define PP_COPY_A(T, B)                                                                        \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
       rs0, LDS_AS(smem + ((T) % NA) * kAS + (mbase + (B)) * 1024), 16,                         \
-      vrow + ((vx ^ (uint32_t)((mbase + (B)) & 7)) << 4),                                      \
-      (T) < nsteps ? (uint32_t)(B) * 8u * arowbytes + PP_KOFF(T) : PP_KOFF(T), 0, 0)
+      (GATHER ? gofs[(B)] : vrow) + ((vx ^ (uint32_t)((mbase + (B)) & 7)) << 4),               \
+      (T) < nsteps && !GATHER ? (uint32_t)(B) * 8u * arowbytes + PP_KOFF(T) : PP_KOFF(T), 0, 0)
 // Memory phase: the group's copies (B slice T + dB, 8 blocks, or A slice
 // T + dA, 2*FI blocks), then this wave's fragments of slice T.
 #define PP_READS(T)                                                                            \
@@ -563,6 +581,20 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   store_tile_pp<SWIGLU, FI>(acc, tl, lane, grp, q, out_map(a, tl.g), N);
 }
 
+template <bool SWIGLU, bool GATHER>
+__device__ __forceinline__ void tile_dispatch_pp(const GroupedGemmArgs& a, const Tile& tl, int fi,
+                                                 int kbeg, int nsteps, int krot, int part,
+                                                 int parts, int64_t slot, uint8_t* smem) {
+  if (fi == 4)
+    tile_body_pp<SWIGLU, 4, kTallNA, kTallNB, GATHER>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+  else if (fi == 3)
+    tile_body_pp<SWIGLU, 3, kTallNA, kTallNB, GATHER>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+  else if (fi == 2)
+    tile_body_pp<SWIGLU, 2, 3, 3, GATHER>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+  else
+    tile_body_pp<SWIGLU, 1, 3, 3, GATHER>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+}
+
 template <bool SWIGLU>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kPPLds];   // 160 KiB
@@ -624,14 +656,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
   // three B slots; taller tiles take three A and two B slots (two A and
   // three B, the weights given the longer lead, measured the same)
   const int fi = frags_of(tl.m_valid);
-  if (fi == 4)
-    tile_body_pp<SWIGLU, 4, kTallNA, kTallNB>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
-  else if (fi == 3)
-    tile_body_pp<SWIGLU, 3, kTallNA, kTallNB>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
-  else if (fi == 2)
-    tile_body_pp<SWIGLU, 2, 3, 3>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+  if (SWIGLU && a.a_map)
+    tile_dispatch_pp<SWIGLU, true>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
   else
-    tile_body_pp<SWIGLU, 1, 3, 3>(a, tl, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    tile_dispatch_pp<SWIGLU, false>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
 }
 
 template <bool SWIGLU, int FI>

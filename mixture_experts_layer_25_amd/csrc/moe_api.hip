@@ -858,6 +858,11 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   };
 
   const bool ec = c.routing == MOE_ROUTE_EXPERT_CHOICE;
+  // bf16 layers that keep no activations gather GEMM 1's token rows from x
+  // through row_token: no dispatch buffer is written (the permute stage
+  // launches nothing)
+  const bool gather = c.dtype == MOE_DTYPE_BF16 && !saves(c) &&
+                      (int64_t)c.T * c.h * 2 < ((int64_t)1 << 31);
   // expert choice: per-(token, expert) slots
   if (ec) {
     gate = r.topk_gate ? r.topk_gate : at<float>(ws, L.gatete);
@@ -883,7 +888,8 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
     MOE_TRY(moe::launch_fixed_groups(c.E, (int)c.capacity, c.T, c.has_shared, BM, counts, offsets,
                                      gtab, s));
     MOE_TRY(mark(4));
-    MOE_TRY(moe::launch_gather_rows(c.dtype, x, rowtok, rows, c.T, c.h, xperm, ld_h(c), s));
+    if (!gather)
+      MOE_TRY(moe::launch_gather_rows(c.dtype, x, rowtok, rows, c.T, c.h, xperm, ld_h(c), s));
   } else {
     const float* sb = w->select_bias;
     if (c.routing == MOE_ROUTE_SINKHORN) {
@@ -908,21 +914,26 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
                                      at<int32_t>(ws, L.aid_dl), assign, rowtok, s));
       // the capacity layout's counts, offsets and tile table
       MOE_TRY(moe::launch_scan(hist, nch, c.E, c.capacity, c.T, c.k, c.has_shared, BM, base,
-                               counts, offsets, gtab, s));
+                               counts, offsets, gtab, s, gather ? r.row_token : nullptr));
     } else {
       MOE_TRY(moe::launch_scan(hist, nch, c.E, c.capacity, c.T, c.k, c.has_shared, BM, base,
-                               counts, offsets, gtab, s));
+                               counts, offsets, gtab, s, gather ? r.row_token : nullptr));
       MOE_TRY(mark(3));
       MOE_TRY(moe::launch_assign(idx, base, hg, offsets, c.T, c.E, c.k, c.capacity, assign,
                                  rowtok, s));
     }
     MOE_TRY(mark(4));
-    MOE_TRY(moe::launch_permute(c.dtype, x, assign, counts, c.T, c.h, c.E, c.k, c.capacity,
-                                xperm, ld_h(c), rowtok, s));
+    if (!gather)
+      MOE_TRY(moe::launch_permute(c.dtype, x, assign, counts, c.T, c.h, c.E, c.k, c.capacity,
+                                  xperm, ld_h(c), rowtok, s));
   }
   MOE_TRY(mark(5));
   moe::GroupedGemmArgs a{};
-  a.A = xperm;
+  a.A = gather ? x : xperm;
+  if (gather) {
+    a.a_map = rowtok;
+    a.a_rows = c.T;
+  }
   a.A_shared = x;
   a.B0 = w->w1;
   a.B1 = w->w3;
@@ -932,7 +943,7 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   a.out = act;
   a.K = c.h;
   a.N = c.F;
-  a.lda = ld_h(c);
+  a.lda = gather ? c.h : ld_h(c);
   a.lda_shared = c.h;
   a.ldo = ld_f(c);
   a.rotate_k = 1;

@@ -96,6 +96,11 @@ struct GroupedGemmArgs {
   // a3 at [N, 2N) of out13's output row (row stride ld13), or NULL.
   void* out13;
   int ld13;
+  // bf16 SwiGLU mode: if set, routed row r is row a_map[r] of A (a_rows rows
+  // of stride lda, a_rows * lda * 2 < 2^31 bytes): the tokens are gathered
+  // by the copies themselves instead of from a dispatch buffer.
+  const int32_t* a_map;
+  int64_t a_rows;
 };
 
 hipError_t launch_router(int dtype, const void* x, const void* w_router,
@@ -211,10 +216,12 @@ hipError_t launch_hist(const int32_t* idx, int64_t T, int E, int k,
                        int32_t* chunk_hist, hipStream_t s);
 
 // hist/base: one row of E counts per group of hg tokens (hg divides 256).
+// pad_row_token (capacity layout, or NULL): its padding rows are set to -1
+// (for callers whose permute, which also does so, does not run).
 hipError_t launch_scan(const int32_t* hist, int64_t ngroups, int E,
                        int64_t C, int64_t T, int k, int has_shared, int BM,
                        int32_t* base, int32_t* counts, int32_t* offsets,
-                       int32_t* gtab, hipStream_t s);
+                       int32_t* gtab, hipStream_t s, int32_t* pad_row_token = nullptr);
 
 hipError_t launch_assign(const int32_t* idx, const int32_t* base, int hg,
                          const int32_t* offsets, int64_t T, int E, int k,

@@ -94,9 +94,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     const int32_t* __restrict__ chunk_hist, int64_t nch, int E, int64_t C,
     int64_t T, int k, int has_shared, int BM, int32_t* __restrict__ chunk_base,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ gtab) {
+    int32_t* __restrict__ gtab, int32_t* __restrict__ pad_row_token) {
   __shared__ int tmp[32];
   __shared__ int slice_sum[1024];
+  __shared__ int kept_s[1024];
   int S = 1;
   while (2 * S * E <= 1024) S *= 2;
   const int tid = threadIdx.x;
@@ -154,6 +155,17 @@ __global__ __launch_bounds__(1024) void scan_kernel(
     o0 = rows_routed;       // and writes after the routed rows
   }
   write_gtab(e, G, valid, a0, o0, BM, tmp, gtab);
+  // capacity layout, when no permute runs after it: the padding rows
+  // e*C + kept_e .. e*C + C - 1 get row_token -1
+  if (C > 0 && pad_row_token) {
+    if (e < E) kept_s[e] = valid;
+    __syncthreads();
+    const int64_t nrow = (int64_t)E * C;
+    for (int64_t r = tid; r < nrow; r += 1024) {
+      const int64_t ex = r / C;
+      if (r - ex * C >= kept_s[ex]) pad_row_token[r] = -1;
+    }
+  }
 }
 
 // Standalone grouped GEMM: groups straight from counts and offsets, each
@@ -424,9 +436,9 @@ hipError_t launch_hist(const int32_t* idx, int64_t T, int E, int k,
 hipError_t launch_scan(const int32_t* chunk_hist, int64_t nch, int E, int64_t C,
                        int64_t T, int k, int has_shared, int BM,
                        int32_t* chunk_base, int32_t* counts, int32_t* offsets,
-                       int32_t* gtab, hipStream_t s) {
+                       int32_t* gtab, hipStream_t s, int32_t* pad_row_token) {
   MOE_LAUNCH(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_hist, nch, E,
-                     C, T, k, has_shared, BM, chunk_base, counts, offsets, gtab);
+                     C, T, k, has_shared, BM, chunk_base, counts, offsets, gtab, pad_row_token);
   return hipGetLastError();
 }
 

@@ -55,6 +55,9 @@ def test_gemm1_bytes_and_bound():
     b = bench.gemm1_bytes(rows, T, h, F, 2, shared=True)
     assert b == (2 * 257 * F * h + (32768 + T) * h + (32768 + T) * F) * 2
     assert bench.gemm1_flops(32768 + T, h, F) / b < 312.5
+    # gathering the rows from the tokens reads each token once
+    bg = bench.gemm1_bytes(rows, T, h, F, 2, shared=True, in_rows=T)
+    assert b - bg == 32768 * h * 2
 
 
 def test_metric_label_follows_the_workload():
