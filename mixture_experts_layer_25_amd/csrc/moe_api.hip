@@ -960,6 +960,7 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, true, a, s));
   MOE_TRY(mark(6));
   a.out13 = nullptr;
+  a.a_map = nullptr;
   a.A = act;
   a.A_shared = nullptr;
   a.B0 = w->w2;
