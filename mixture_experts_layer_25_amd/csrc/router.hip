@@ -178,6 +178,48 @@ __global__ __launch_bounds__(64 * kRouterMaxWaves) void router_topk_bf16_kernel(
 }
 
 constexpr int kTileT = 64;           // tokens per tile
+
+// The K loop of a 64x64 router tile (4x4 MFMA 16x16x32 tiles per wave):
+// U 32-deep steps per iteration, all of their loads (32 * U bytes per lane
+// and row) issued before the MFMAs, then single 32-deep steps for the rest
+// of kq (a multiple of 32).
+template <int U>
+__device__ __forceinline__ void tile_mfma_loop(const uint16_t* const (&ap)[4],
+                                               const uint16_t* const (&bp)[4], int kq,
+                                               floatx4 (&acc)[4][4]) {
+  int kk = 0;
+  for (; kk + 32 * U <= kq; kk += 32 * U) {
+    bf16x8 a[U][4], b[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[u][i] = __builtin_bit_cast(bf16x8, ld16(ap[i] + kk + 32 * u));
+        b[u][i] = __builtin_bit_cast(bf16x8, ld16(bp[i] + kk + 32 * u));
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
+  }
+  for (; kk < kq; kk += 32) {
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = __builtin_bit_cast(bf16x8, ld16(ap[i] + kk));
+      b[i] = __builtin_bit_cast(bf16x8, ld16(bp[i] + kk));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
 constexpr int kTileE = 64;           // experts per tile
 constexpr int kRedLd = kTileE + 4;   // LDS row stride of the partial sums
 
@@ -215,38 +257,7 @@ __global__ __launch_bounds__(64 * NW) void router_bf16_tile_kernel(
 
   // Two 32-deep steps per iteration so 16 loads are in flight; a 32-deep
   // tail when kq is an odd multiple of 32.
-  int kk = 0;
-  for (; kk + 64 <= kq; kk += 64) {
-    bf16x8 a[2][4], b[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[u][i] = __builtin_bit_cast(bf16x8, ld16(ap[i] + kk + 32 * u));
-        b[u][i] = __builtin_bit_cast(bf16x8, ld16(bp[i] + kk + 32 * u));
-      }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
-  }
-  if (kk < kq) {
-    bf16x8 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = __builtin_bit_cast(bf16x8, ld16(ap[i] + kk));
-      b[i] = __builtin_bit_cast(bf16x8, ld16(bp[i] + kk));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
+  tile_mfma_loop<2>(ap, bp, kq, acc);
   // C layout: lane l holds expert column (l & 15), token rows 4*(l>>4)+r.
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -313,38 +324,7 @@ __global__ __launch_bounds__(64 * NW) void router_topk_tile_bf16_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  int kk = 0;
-  for (; kk + 64 <= kq; kk += 64) {
-    bf16x8 a[2][4], b[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[u][i] = __builtin_bit_cast(bf16x8, ld16(ap[i] + kk + 32 * u));
-        b[u][i] = __builtin_bit_cast(bf16x8, ld16(bp[i] + kk + 32 * u));
-      }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][j], acc[i][j], 0, 0, 0);
-  }
-  if (kk < kq) {
-    bf16x8 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = __builtin_bit_cast(bf16x8, ld16(ap[i] + kk));
-      b[i] = __builtin_bit_cast(bf16x8, ld16(bp[i] + kk));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
+  tile_mfma_loop<2>(ap, bp, kq, acc);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
