@@ -150,6 +150,19 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+// A K-major B fragment: rows +0..3 at p and +4..7 at p + 4 rows (2 KiB),
+// through transposing reads (lane i of a 16-lane group gets column i).
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 lds_frag_tr(const uint8_t* p) {
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)(p));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)(p + 2048));
+  const shortx8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Row fragments (32 rows) per wave for a tile of m_valid rows.  The last
 // row tile of a group is only as tall as its rows need (64, 128, 192 or
 // 256), so a group's few leftover rows do not cost a whole 256-row tile.
@@ -314,7 +327,13 @@ __device__ __forceinline__ void store_tile_pp(const floatx16 (&acc)[FI][2], cons
 //
 // GATHER: the A-copying waves read routed rows through a.a_map (one source
 // row per lane and 8-row block, out of range for rows past the tile's).
-template <bool SWIGLU, int FI, int NA, int NB, bool GATHER>
+// BKM: B is K-major (a.b_kmajor).  Its slice is 64 K rows of 256 columns
+// (512 bytes) in LDS, 16-byte chunk c of row r stored at c ^ 4*(r & 3), and
+// the fragments come out of it through transposing reads (two
+// ds_read_b64_tr_b16 per fragment: in a 16-lane group, lane 4*j + r
+// addresses row j, columns 4r .. 4r + 3, and lane i receives column i of
+// rows 0 .. 3).
+template <bool SWIGLU, int FI, int NA, int NB, bool GATHER, bool BKM>
 __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Tile& tl, int kbeg,
                                              int nsteps, int krot, int part, int parts,
                                              int64_t slot, uint8_t* smem) {
@@ -341,7 +360,7 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   const uint16_t* B1 = (const uint16_t*)(shared ? a.B1s : a.B1);
   if (!shared && !a.kgroup) {
     B0 += (int64_t)tl.g * a.b_stride;
-    if (SWIGLU || a.b_split) B1 += (int64_t)tl.g * a.b_stride;
+    if (SWIGLU || a.b_split || a.b_ksplit) B1 += (int64_t)tl.g * a.b_stride;
   }
 
   // Copies, 8 rows (1 KiB) per instruction; lane l lands at byte 16*l of the
@@ -353,6 +372,7 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   rsrc_t rs0, rs1;
   uint32_t rowb;
   uint32_t gofs[GATHER ? AB : 1];   // GATHER: byte offset of this lane's row, per block
+  uint32_t bofs[BKM ? 8 : 1];       // BKM: byte offset of this lane's chunk, per copy
   if (grp == gA) {
     const int a_rows = __builtin_amdgcn_readfirstlane(min(max(tl.m_valid - q * 16 * FI, 0), 16 * FI));
     if (GATHER && !a_shared) {
@@ -378,6 +398,22 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
     rs0 = make_rsrc(B0 + f * K, 32u * browbytes);
     rs1 = make_rsrc(B1 + f * K, 32u * browbytes);
     rowb = browbytes;
+  } else if (BKM) {
+    // K-major B: wave q copies slice rows 16q .. 16q + 15, two per copy (lane
+    // l: row 16q + 2b + (l >> 5), stored chunk l & 31 = logical chunk
+    // (l & 31) ^ 4*(row & 3), columns n0 + 8*chunk .. + 7; chunks past N out
+    // of range)
+    const int64_t n0 = (int64_t)tl.nt * BN;
+    const int64_t krows0 = a.b_ksplit > 0 ? a.b_ksplit : K;
+    rs0 = make_rsrc(B0 + n0, (uint32_t)((krows0 * ldb - n0) * 2));
+    rs1 = a.b_ksplit > 0 ? make_rsrc(B1 + n0, (uint32_t)(((K - krows0) * ldb - n0) * 2)) : rs0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int row = 16 * q + 2 * b + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (row & 3));
+      bofs[b] = n0 + 8 * c < N ? (uint32_t)((row * ldb + 8 * c) * 2) : 0x80000000u;
+    }
+    rowb = 0;
   } else {
     // b_split: rows [0, N/2) of B come from B0, [N/2, N) from B1 (64-row
     // blocks never straddle N/2, a multiple of 64)
@@ -407,6 +443,16 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   // r = FI*grp + i, B fragment j has r = 2q + j.
   const int rA = (grp * 32 * FI + (lane & 31)) * (BK * 2);
   const int rB = kBO + (64 * q + (lane & 31)) * (BK * 2);
+  // BKM fragment reads: lane l = 16G + 4jj + r4 addresses row
+  // 16k + 8(G >> 1) + 4h + jj and columns 64q + 32j + 16(G & 1) + 4r4 .. + 3
+  int tbr = 0, tbc[2] = {0, 0};
+  if (BKM) {
+    const int G = lane >> 4, jj = (lane >> 2) & 3, r4 = lane & 3;
+    tbr = kBO + (8 * (G >> 1) + jj) * 512;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      tbc[j] = (((8 * q + 4 * j + 2 * (G & 1) + (r4 >> 1)) ^ (4 * jj)) << 4) + (r4 & 1) * 8;
+  }
   const int fe = (lane & 7) ^ ((lane >> 3) & 3);
   const int fo = (lane & 7) ^ (4 | ((lane >> 3) & 3));
   const bool aflip = (FI * grp) & 1;   // A fragment i has parity (i & 1) ^ aflip
@@ -436,14 +482,26 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
                 : 0x7FFFFFF0u)
 // Copy block b of slice T: a B block into B slot T % NB, or an A block into
 // A slot T % NA (the caller's group decides which)
+// K-major B: slice T's first K row (-1 past the last slice)
+#define PP_KSL(T)                                                                              \
+  ((T) < nsteps ? (kbeg + ((T) + krot >= nsteps ? (T) + krot - nsteps : (T) + krot)) * BK : -1)
 #define PP_COPY_B(T, B)                                                                        \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
-      (SWIGLU && (B) >= 4) ? rs1 : rs0,                                                        \
-      LDS_AS(smem + kBO + ((T) % NB) * kPart + (8 * q + (B)) * 1024), 16,                      \
-      vrow + ((vx ^ (uint32_t)(((B)) & 7)) << 4),                                              \
-      (T) < nsteps ? (uint32_t)(SWIGLU ? ((B) & 3) : (B)) * 8u * browbytes + PP_KOFF(T)        \
-                   : PP_KOFF(T),                                                               \
-      0, 0)
+  if (BKM) {                                                                                   \
+    const int kr_ = PP_KSL(T);                                                                 \
+    const bool hi_ = a.b_ksplit > 0 && kr_ >= a.b_ksplit;                                      \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                  \
+        hi_ ? rs1 : rs0, LDS_AS(smem + kBO + ((T) % NB) * kPart + (8 * q + (B)) * 1024), 16,   \
+        bofs[(B)],                                                                             \
+        kr_ < 0 ? 0x7FFFFFF0u : (uint32_t)((kr_ - (hi_ ? a.b_ksplit : 0)) * ldb * 2), 0, 0);   \
+  } else {                                                                                     \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                  \
+        (SWIGLU && (B) >= 4) ? rs1 : rs0,                                                      \
+        LDS_AS(smem + kBO + ((T) % NB) * kPart + (8 * q + (B)) * 1024), 16,                    \
+        vrow + ((vx ^ (uint32_t)(((B)) & 7)) << 4),                                            \
+        (T) < nsteps ? (uint32_t)(SWIGLU ? ((B) & 3) : (B)) * 8u * browbytes + PP_KOFF(T)      \
+                     : PP_KOFF(T),                                                             \
+        0, 0);                                                                                 \
+  }
 #define PP_COPY_A(T, B)                                                                        \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
       rs0, LDS_AS(smem + ((T) % NA) * kAS + (mbase + (B)) * 1024), 16,                         \
@@ -462,7 +520,8 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
     const uint8_t* SB = smem + ((T) % NB) * kPart;                                             \
     _Pragma("unroll") for (int k = 0; k < 4; ++k) {                                            \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) fb[k][j] =                                 \
-          lds_frag(SB + rB + j * 4096 + cx[k][j]);                                             \
+          BKM ? lds_frag_tr(SB + tbr + k * 8192 + tbc[j])                                      \
+              : lds_frag(SB + rB + j * 4096 + cx[k][j]);                                       \
       _Pragma("unroll") for (int i = 0; i < FI; ++i) fa[k][i] =                                \
           lds_frag(SA + rA + i * 4096 + cxa[k][i & 1]);                                        \
     }                                                                                          \
@@ -581,18 +640,18 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
   store_tile_pp<SWIGLU, FI>(acc, tl, lane, grp, q, out_map(a, tl.g), N);
 }
 
-template <bool SWIGLU, bool GATHER>
+template <bool SWIGLU, bool GATHER, bool BKM>
 __device__ __forceinline__ void tile_dispatch_pp(const GroupedGemmArgs& a, const Tile& tl, int fi,
                                                  int kbeg, int nsteps, int krot, int part,
                                                  int parts, int64_t slot, uint8_t* smem) {
   if (fi == 4)
-    tile_body_pp<SWIGLU, 4, kTallNA, kTallNB, GATHER>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+    tile_body_pp<SWIGLU, 4, kTallNA, kTallNB, GATHER, BKM>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
   else if (fi == 3)
-    tile_body_pp<SWIGLU, 3, kTallNA, kTallNB, GATHER>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+    tile_body_pp<SWIGLU, 3, kTallNA, kTallNB, GATHER, BKM>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
   else if (fi == 2)
-    tile_body_pp<SWIGLU, 2, 3, 3, GATHER>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+    tile_body_pp<SWIGLU, 2, 3, 3, GATHER, BKM>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
   else
-    tile_body_pp<SWIGLU, 1, 3, 3, GATHER>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+    tile_body_pp<SWIGLU, 1, 3, 3, GATHER, BKM>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
 }
 
 template <bool SWIGLU>
@@ -657,9 +716,11 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
   // three B, the weights given the longer lead, measured the same)
   const int fi = frags_of(tl.m_valid);
   if (SWIGLU && a.a_map)
-    tile_dispatch_pp<SWIGLU, true>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    tile_dispatch_pp<SWIGLU, true, false>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+  else if (!SWIGLU && a.b_kmajor)
+    tile_dispatch_pp<SWIGLU, false, true>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
   else
-    tile_dispatch_pp<SWIGLU, false>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    tile_dispatch_pp<SWIGLU, false, false>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
 }
 
 template <bool SWIGLU, int FI>

@@ -522,6 +522,19 @@ struct BwdLayout {
   size_t esz;
 };
 
+// bf16 backward with at most 512 dispatch rows per expert on average: the
+// input-gradient GEMMs read w2 and [w1; w3] in their own [K, N] layouts
+// (K-major B operand) instead of transposed copies.  The transposing LDS
+// reads cost GEMM time in proportion to the rows, the transposes in
+// proportion to the weights: at 128 rows per expert (256 experts) the
+// K-major reads save a third of the backward; at 1024 rows per expert
+// (16384 tokens, 64 experts, top-4) they are 2.5 % slower than the
+// transposes.
+bool kmajor_weights(const moe_cfg_t& c) {
+  return c.dtype == MOE_DTYPE_BF16 && (int64_t)c.F * c.h * 2 < ((int64_t)1 << 31) &&
+         rows_of(c) <= (int64_t)512 * c.E;
+}
+
 BwdLayout bwd_layout_of(const moe_cfg_t& c) {
   BwdLayout L{};
   const int64_t T = c.T, E = c.E, k = c.k, h = c.h, F = c.F;
@@ -557,8 +570,9 @@ BwdLayout bwd_layout_of(const moe_cfg_t& c) {
   L.dU = take((size_t)rows_all * L.ldf * es);
   L.dA = take((size_t)rows_all * L.ld13 * es);
   L.dxp = take((size_t)rows_all * L.ldh * es);
-  L.w2t = take((size_t)(G * F * h) * es);
-  L.w13t = take((size_t)(G * h * 2 * F) * es);
+  const bool wt = !kmajor_weights(c);   // transposed weight copies needed
+  L.w2t = take(wt ? (size_t)(G * F * h) * es : 0);
+  L.w13t = take(wt ? (size_t)(G * h * 2 * F) * es : 0);
   L.dOT = take((size_t)(h * L.ktb) * es);
   L.uT = take((size_t)(F * L.ktb) * es);
   L.dAT = take((size_t)(2 * F * L.ktb) * es);
@@ -672,13 +686,17 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
     MOE_TRY(moe::launch_permute(c.dtype, x, r.assign_row, r.expert_counts, T, h, E, k,
                                 c.capacity, at<char>(ws, L.xp), L.ldh, at<int32_t>(ws, L.rowtok),
                                 s));
-  // transposed weights: w2t[g] = w2[g]^T [F,h]; w13t[g] = [w1[g]^T | w3[g]^T] [h,2F]
+  // transposed weights (unless the GEMMs read them K-major): w2t[g] =
+  // w2[g]^T [F,h]; w13t[g] = [w1[g]^T | w3[g]^T] [h,2F]
+  const bool km = kmajor_weights(c);
+  if (!km) {
   MOE_TRY(moe::launch_transpose(c.dtype, w->w2, (int64_t)h * F, h, F, w2t, (int64_t)F * h, h, 0, E, s));
   MOE_TRY(moe::launch_transpose(c.dtype, w->w1, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F, 2 * F, 0,
                                 E, s));
   MOE_TRY(moe::launch_transpose(c.dtype, w->w3, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F, 2 * F, F,
                                 E, s));
-  if (c.has_shared) {
+  }
+  if (c.has_shared && !km) {
     MOE_TRY(moe::launch_transpose(c.dtype, w->ws2, 0, h, F, w2t + (size_t)E * F * h * L.esz, 0, h, 0, 1, s));
     MOE_TRY(moe::launch_transpose(c.dtype, w->ws1, 0, F, h, w13t + (size_t)E * h * 2 * F * L.esz, 0, 2 * F, 0,
                                   1, s));
@@ -717,13 +735,23 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
   // dU = dO w2, then dA, then dx_perm = dA [w1; w3]
   a = base;
   a.A = dO; a.lda = L.ldh; a.a_from_out_rows = 1;
-  a.B0 = w2t; a.B0s = w2t + (size_t)E * F * h * L.esz; a.b_stride = (int64_t)F * h;
+  if (km) {           // w2 [h,F] is K-major for dU
+    a.B0 = w->w2; a.B0s = w->ws2; a.b_kmajor = 1; a.ldb = F;
+  } else {
+    a.B0 = w2t; a.B0s = w2t + (size_t)E * F * h * L.esz;
+  }
+  a.b_stride = (int64_t)F * h;
   a.K = h; a.N = F; a.out = dU; a.ldo = L.ldf;
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
   MOE_TRY(moe::launch_swiglu_bwd(c.dtype, a13, ld13, dU, L.ldf, rows_all, F, dA, L.ld13, s));
   a = base;
   a.A = dA; a.lda = L.ld13; a.a_from_out_rows = 1;
-  a.B0 = w13t; a.B0s = w13t + (size_t)E * h * 2 * F * L.esz; a.b_stride = (int64_t)h * 2 * F;
+  if (km) {           // w1, w3 [F,h] are the K-major rows [0,F) and [F,2F)
+    a.B0 = w->w1; a.B1 = w->w3; a.B0s = w->ws1; a.B1s = w->ws3;
+    a.b_kmajor = 1; a.b_ksplit = F; a.ldb = h; a.b_stride = (int64_t)F * h;
+  } else {
+    a.B0 = w13t; a.B0s = w13t + (size_t)E * h * 2 * F * L.esz; a.b_stride = (int64_t)h * 2 * F;
+  }
   a.K = 2 * F; a.N = h; a.out = dxp; a.ldo = L.ldh;
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
   // K-major copies of each group's rows, then the weight gradients

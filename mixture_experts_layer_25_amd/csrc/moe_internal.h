@@ -101,6 +101,12 @@ struct GroupedGemmArgs {
   // by the copies themselves instead of from a dispatch buffer.
   const int32_t* a_map;
   int64_t a_rows;
+  // bf16 plain mode: B is stored K-major, element (n, k) at B[k * ldb + n]
+  // (a weight read in its own [K, N] layout, no transposed copy); with
+  // b_ksplit > 0, K rows [0, b_ksplit) come from B0 and the rest from B1
+  // (row k - b_ksplit).  Each operand's rows * ldb * 2 < 2^31 bytes.
+  int b_kmajor;
+  int b_ksplit;
 };
 
 hipError_t launch_router(int dtype, const void* x, const void* w_router,
