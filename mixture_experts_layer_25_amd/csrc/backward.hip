@@ -270,14 +270,28 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict
 // idx NULL: slot j is expert j (expert choice, k = E slots, the gate of an
 // unchosen slot 0), with mode 1 for the softmax over all E and mode 2 for
 // the sigmoids normalised over all E.
+//
+// With dl_hl, dl also as bf16 parts: hi = bf16(dl), lo = bf16(dl - hi), in
+// dl_hl[t][e] / dl_hl[t][Ep + e] and dlT_hl[e][t] / dlT_hl[e][Tp + t], zero
+// for e >= E and (dlT_hl) T <= t < Tp.
 __global__ __launch_bounds__(256) void gates_bwd_kernel(const float* __restrict__ logits,
                                                         const int32_t* __restrict__ idx,
                                                         const float* __restrict__ gate,
                                                         const float* __restrict__ dg,
                                                         int gate_mode, int64_t T, int E, int k,
-                                                        float* __restrict__ dl) {
+                                                        float* __restrict__ dl,
+                                                        uint16_t* __restrict__ dl_hl, int Ep,
+                                                        uint16_t* __restrict__ dlT_hl,
+                                                        int64_t Tp) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= T) return;
+  if (t >= T) {
+    if (dl_hl && t < Tp)
+      for (int e = 0; e < Ep; ++e) {
+        dlT_hl[(int64_t)e * 2 * Tp + t] = 0;
+        dlT_hl[(int64_t)e * 2 * Tp + Tp + t] = 0;
+      }
+    return;
+  }
   const float* l = logits + t * E;
   float* d = dl + t * E;
   // a slot whose expert id is outside [0, E) (a caller's map) is ignored
@@ -315,6 +329,120 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const float* __restrict_
       d[e] += (dg[t * k + j] - gd) / S * s * (1.f - s);
     }
   }
+  if (dl_hl) {
+    for (int e = 0; e < Ep; ++e) {
+      const float v = e < E ? d[e] : 0.f;
+      const uint16_t hi = f32_to_bf16_bits(v);
+      const uint16_t lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+      dl_hl[t * 2 * Ep + e] = hi;
+      dl_hl[t * 2 * Ep + Ep + e] = lo;
+      dlT_hl[(int64_t)e * 2 * Tp + t] = hi;
+      dlT_hl[(int64_t)e * 2 * Tp + Tp + t] = lo;
+    }
+  }
+}
+
+// dl[t,:] from dg[t,:] as gates_bwd_kernel computes it, with the bf16 parts
+// dl_hl / dlT_hl, for up to 256 experts: 16 tokens per workgroup, one wave
+// per token at a time.  A token's slots sit in lanes (lane j: slot j's
+// expert, gate and gate gradient; expert choice: lane e's experts), its sums
+// are wave reductions, and the lanes then run over the experts, so dl and
+// dl_hl rows are written by consecutive lanes; the parts are staged in LDS
+// so that dlT_hl's token-contiguous rows are written 32 bytes at a time.
+constexpr int kGbTok = 16, kGbMaxE = 256;
+__global__ __launch_bounds__(256) void gates_bwd_split_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx,
+    const float* __restrict__ gate, const float* __restrict__ dg, int gate_mode, int64_t T, int E,
+    int k, float* __restrict__ dl, uint16_t* __restrict__ dl_hl, int Ep,
+    uint16_t* __restrict__ dlT_hl, int64_t Tp) {
+  __shared__ uint32_t sh[kGbMaxE][kGbTok + 1];   // hi | lo << 16
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * kGbTok;
+  for (int tt = w; tt < kGbTok; tt += 4) {
+    const int64_t t = t0 + tt;
+    if (t >= T) {
+      for (int e = lane; e < Ep; e += 64) sh[e][tt] = 0u;
+      continue;
+    }
+    const float* l = logits + t * E;
+    // top-k: lane j < k holds slot j (an expert id outside [0, E) is
+    // ignored); expert choice (idx NULL): slot j is expert j
+    int exl = -1;
+    float gl = 0.f, dgl = 0.f;
+    if (idx && lane < k) {
+      exl = idx[t * k + lane];
+      gl = gate[t * k + lane];
+      dgl = dg[t * k + lane];
+      if ((unsigned)exl >= (unsigned)E) exl = -1;
+    }
+    float gd = 0.f, S = 0.f;   // sum_j g_j dg_j; sigmoid mode: sum_j s(l[ex(j)])
+    if (idx) {
+      gd = exl >= 0 ? gl * dgl : 0.f;
+      if (gate_mode == 2 && exl >= 0) S = 1.f / (1.f + expf(-l[exl]));
+    } else {
+      for (int e = lane; e < E; e += 64) {
+        gd += gate[t * k + e] * dg[t * k + e];
+        if (gate_mode == 2) S += 1.f / (1.f + expf(-l[e]));
+      }
+    }
+    gd = seg_sum_f32<64>(gd);
+    if (gate_mode == 2) S = seg_sum_f32<64>(S);
+    float m = -INFINITY, den = 0.f;
+    if (gate_mode == 1) {
+      for (int e = lane; e < E; e += 64) m = fmaxf(m, l[e]);
+      m = seg_max_f32<64>(m);
+      for (int e = lane; e < E; e += 64) den += expf(l[e] - m);
+      den = seg_sum_f32<64>(den);
+    }
+    auto term = [&](int e, float g, float dgj) {
+      if (gate_mode == 0) return g * (dgj - gd);
+      if (gate_mode == 1) return (expf(l[e] - m) / den) * dgj;
+      const float sg = 1.f / (1.f + expf(-l[e]));
+      return (dgj - gd) / S * sg * (1.f - sg);
+    };
+    for (int e0 = 0; e0 < Ep; e0 += 64) {
+      const int e = e0 + lane;
+      float d = 0.f;
+      if (e < E && gate_mode == 1) d = -(expf(l[e] - m) / den) * gd;
+      if (idx) {
+        for (int j = 0; j < k; ++j) {   // slots in order
+          const int ej = __shfl(exl, j, 64);
+          const float gj = __shfl(gl, j, 64), dj = __shfl(dgl, j, 64);
+          if (ej == e) d += term(e, gj, dj);
+        }
+      } else if (e < E) {
+        d += term(e, gate[t * k + e], dg[t * k + e]);
+      }
+      if (e < E) dl[t * E + e] = d;
+      if (e < Ep) {
+        const uint16_t hi = f32_to_bf16_bits(d);
+        const uint16_t lo = f32_to_bf16_bits(d - bf16_bits_to_f32(hi));
+        dl_hl[t * 2 * Ep + e] = hi;
+        dl_hl[t * 2 * Ep + Ep + e] = lo;
+        sh[e][tt] = (uint32_t)hi | ((uint32_t)lo << 16);
+      }
+    }
+  }
+  __syncthreads();
+  // 16 lanes per expert row (its 16 tokens), 16 rows at a time
+  const int tl = threadIdx.x & 15, er = threadIdx.x >> 4;
+  const int64_t t = t0 + tl;
+  if (t < Tp)
+    for (int e = er; e < Ep; e += 16) {
+      const uint32_t v = sh[e][tl];
+      dlT_hl[(int64_t)e * 2 * Tp + t] = (uint16_t)(v & 0xFFFFu);
+      dlT_hl[(int64_t)e * 2 * Tp + Tp + t] = (uint16_t)(v >> 16);
+    }
+}
+
+// Tile table (4G + 1 ints, G = 1) of one group of `rows` rows: its row
+// tiles, first A row 0, its rows, first output row 0.
+__global__ void single_group_gtab_kernel(int32_t* gt, int64_t rows, int BM) {
+  gt[0] = 0;
+  gt[1] = (int32_t)((rows + BM - 1) / BM);
+  gt[2] = 0;
+  gt[3] = (int32_t)rows;
+  gt[4] = 0;
 }
 
 // dW_router[e, i] = sum_t dl[t,e] x[t,i]: workgroup (column tile, 32
@@ -529,7 +657,8 @@ hipError_t launch_router_bwd(int dtype, const float* logits, const int32_t* idx,
                              int k, const void* x, int h, float* dl, float* rpart,
                              void* dw_router, float* dlogit_bias, hipStream_t s) {
   MOE_LAUNCH(gates_bwd_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s,
-                     logits, idx, gate, dg, gate_mode, T, E, k, dl);
+                     logits, idx, gate, dg, gate_mode, T, E, k, dl, (uint16_t*)nullptr, 0,
+                     (uint16_t*)nullptr, (int64_t)0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (dw_router) {
@@ -558,6 +687,32 @@ hipError_t launch_router_bwd(int dtype, const float* logits, const int32_t* idx,
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+hipError_t launch_gates_bwd(const float* logits, const int32_t* idx, const float* gate,
+                            const float* dg, int gate_mode, int64_t T, int E, int k, float* dl,
+                            uint16_t* dl_hl, int Ep, uint16_t* dlT_hl, int64_t Tp,
+                            hipStream_t s) {
+  if (dl_hl && Ep <= kGbMaxE) {
+    MOE_LAUNCH(gates_bwd_split_kernel, dim3((unsigned)(Tp / kGbTok)), dim3(256), 0, s, logits,
+               idx, gate, dg, gate_mode, T, E, k, dl, dl_hl, Ep, dlT_hl, Tp);
+    return hipGetLastError();
+  }
+  const int64_t n = dl_hl ? (T > Tp ? T : Tp) : T;
+  MOE_LAUNCH(gates_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, logits, idx,
+             gate, dg, gate_mode, T, E, k, dl, dl_hl, Ep, dlT_hl, Tp);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_grad(const float* dl, int64_t T, int E, float* dlogit_bias,
+                            hipStream_t s) {
+  MOE_LAUNCH(bias_grad_kernel, dim3(E), dim3(256), 0, s, dl, T, E, dlogit_bias);
+  return hipGetLastError();
+}
+
+hipError_t launch_single_group_gtab(int32_t* gtab, int64_t rows, int BM, hipStream_t s) {
+  MOE_LAUNCH(single_group_gtab_kernel, dim3(1), dim3(1), 0, s, gtab, rows, BM);
+  return hipGetLastError();
 }
 
 hipError_t launch_dx_final(int dtype, const void* dxp, int ldp, const int32_t* assign_row, int k,

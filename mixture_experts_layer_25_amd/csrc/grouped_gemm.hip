@@ -170,6 +170,11 @@ __device__ __forceinline__ int frags_of(int m_valid) {
   return m_valid > 192 ? 4 : (m_valid > 128 ? 3 : (m_valid > 64 ? 2 : 1));
 }
 
+// Epilogues of the plain product: store it (rounded to bf16), turn dU into
+// the SwiGLU backward's dA, or add the gathered dx_perm rows of the layer's
+// dx to the router term.
+constexpr int kEpiPlain = 0, kEpiDSwiglu = 1, kEpiDxGather = 2;
+
 // Where output row r (within the tile's group) lives: out0 + r*ldo, or
 // out1 + (r - split)*ldo from row `split` on (weight gradients of w1 and w3
 // computed as one [2F, h] product).
@@ -180,6 +185,12 @@ struct OutMap {
   int64_t ldo;
   uint16_t* a13;   // SwiGLU: pre-activations [a1 | a3] too, or NULL
   int64_t ld13;
+  const uint16_t* dsw;   // plain: [a1 | a3] of the SwiGLU backward, or NULL
+  int64_t ldsw;
+  const uint16_t* dxg;   // plain: dx_perm rows gathered into dx, or NULL
+  const int32_t* dxg_assign;
+  int dxg_k, dxg_shared;
+  int64_t dxg_rows, dxg_ld;
   __device__ __forceinline__ uint16_t* row(int64_t r) const {
     return r < split ? out0 + r * ldo : out1 + (r - split) * ldo;
   }
@@ -194,6 +205,14 @@ __device__ __forceinline__ OutMap out_map(const GroupedGemmArgs& a, int g) {
   m.ldo = a.ldo;
   m.a13 = (uint16_t*)a.out13;
   m.ld13 = a.ld13;
+  m.dsw = (const uint16_t*)a.dsw_a13;
+  m.ldsw = a.dsw_ld13;
+  m.dxg = (const uint16_t*)a.dxg;
+  m.dxg_assign = a.dxg_assign;
+  m.dxg_k = a.dxg_k;
+  m.dxg_shared = a.dxg_shared;
+  m.dxg_rows = a.dxg_rows;
+  m.dxg_ld = a.dxg_ld;
   return m;
 }
 
@@ -247,7 +266,7 @@ __device__ __forceinline__ int64_t part_off_pp(int w, int c, int lane) {
 
 // Epilogue: wave (grp, q) holds rows 32*FI*grp + 32i + (lane & 31) and, per
 // fragment j, C^T runs of 4 columns (see above).
-template <bool SWIGLU, int FI>
+template <bool SWIGLU, int FI, int EPI = 0>
 __device__ __forceinline__ void store_tile_pp(const floatx16 (&acc)[FI][2], const Tile& tl,
                                               int lane, int grp, int q, const OutMap& om, int N) {
   const int hi = lane >> 5;
@@ -271,6 +290,191 @@ __device__ __forceinline__ void store_tile_pp(const floatx16 (&acc)[FI][2], cons
 #pragma unroll
       for (int p = 0; p < 2; ++p) v[b][p] = pack_bf16x2(f[4 * b + 2 * p], f[4 * b + 2 * p + 1]);
   };
+  if constexpr (EPI == kEpiDxGather) {
+    // dx of the layer: the tile's rows are tokens and the product is the
+    // router term dl W_router.  After the exchange with lane l ^ 32 a lane
+    // holds 8 consecutive columns of it (fp32); it adds the token's dx_perm
+    // rows (its slots in order, then the shared expert's row) to that sum
+    // and rounds once.  The row ids of the first 8 slots are loaded once per
+    // row fragment.
+    const uint16_t* src = om.dxg;
+    const int kk = om.dxg_k;
+    const int64_t rows = om.dxg_rows, ldp = om.dxg_ld;
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const int row = grp * 32 * FI + i * 32 + (lane & 31);
+      const bool ok = row < tl.m_valid;
+      const int64_t t = tl.o_row + row;
+      int ids[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ids[u] = (ok && u < kk) ? om.dxg_assign[t * kk + u] : -1;
+      uint16_t* orow = om.row(t);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col0 = (int64_t)tl.nt * BN + 64 * q + 32 * j;
+        if (col0 >= N) continue;
+        float rt[2][8];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // (the elements go through values: a bit cast of a vector
+            // element designator reads element 0)
+            const float x0 = acc[i][j][8 * c + e], x1 = acc[i][j][8 * c + 4 + e];
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0),
+                                                            __float_as_uint(x1), false, false);
+            rt[c][e] = __uint_as_float((uint32_t)r[0]);
+            rt[c][4 + e] = __uint_as_float((uint32_t)r[1]);
+          }
+        if (!ok) continue;
+        const int64_t cl[2] = {col0 + 8 * hi, col0 + 16 + 8 * hi};
+        float sum[2][8];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum[c][e] = 0.f;
+        auto add_rows = [&](const int (&rr)[4]) {
+          uint4 v[4][2];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              v[u][c] = (rr[u] >= 0 && rr[u] < rows)
+                            ? *reinterpret_cast<const uint4*>(src + rr[u] * ldp + cl[c])
+                            : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (rr[u] < 0 || rr[u] >= rows) continue;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const uint32_t w[4] = {v[u][c].x, v[u][c].y, v[u][c].z, v[u][c].w};
+#pragma unroll
+              for (int p = 0; p < 4; ++p) {
+                sum[c][2 * p] += __uint_as_float(w[p] << 16);
+                sum[c][2 * p + 1] += __uint_as_float(w[p] & 0xFFFF0000u);
+              }
+            }
+          }
+        };
+        {
+          const int r0[4] = {ids[0], ids[1], ids[2], ids[3]};
+          add_rows(r0);
+        }
+        if (kk > 4) {
+          const int r1[4] = {ids[4], ids[5], ids[6], ids[7]};
+          add_rows(r1);
+        }
+        for (int s0 = 8; s0 < kk; s0 += 4) {
+          int rr[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) rr[u] = s0 + u < kk ? om.dxg_assign[t * kk + s0 + u] : -1;
+          add_rows(rr);
+        }
+        if (om.dxg_shared) {   // the shared expert's row rows + t
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const uint4 q4 = *reinterpret_cast<const uint4*>(src + (rows + t) * ldp + cl[c]);
+            const uint32_t w[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              sum[c][2 * p] += __uint_as_float(w[p] << 16);
+              sum[c][2 * p + 1] += __uint_as_float(w[p] & 0xFFFF0000u);
+            }
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          uint32_t o[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            o[p] = pack_bf16x2(sum[c][2 * p] + rt[c][2 * p], sum[c][2 * p + 1] + rt[c][2 * p + 1]);
+          *reinterpret_cast<uint4*>(orow + cl[c]) = uint4{o[0], o[1], o[2], o[3]};
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (EPI == kEpiDSwiglu) {
+    // SwiGLU backward: after the exchange with lane l ^ 32 a lane holds dU
+    // (fp32) of 8 consecutive columns; with a1 and a3 of the same columns
+    // it writes dA1 and dA3 (N columns apart).  The a1/a3 loads of row
+    // fragment i + 1 are issued before fragment i is computed and stored.
+    uint4 ld[2][2][2];   // [j][c][a1, a3] of the current row fragment
+    auto issue = [&](int i, uint4 (&dst)[2][2][2]) {
+      const int row = grp * 32 * FI + i * 32 + (lane & 31);
+      if (row >= tl.m_valid) return;
+      const uint16_t* r13 = om.dsw + (tl.o_row + row) * om.ldsw;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col0 = (int64_t)tl.nt * BN + 64 * q + 32 * j;
+        if (col0 >= N) continue;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int64_t col = col0 + 16 * c + 8 * hi;
+          dst[j][c][0] = *reinterpret_cast<const uint4*>(r13 + col);
+          dst[j][c][1] = *reinterpret_cast<const uint4*>(r13 + N + col);
+        }
+      }
+    };
+    issue(0, ld);
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      uint4 cur[2][2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          cur[j][c][0] = ld[j][c][0];
+          cur[j][c][1] = ld[j][c][1];
+        }
+      if (i + 1 < FI) issue(i + 1, ld);
+      const int row = grp * 32 * FI + i * 32 + (lane & 31);
+      const bool ok = row < tl.m_valid;
+      uint16_t* orow = om.row(tl.o_row + row);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col0 = (int64_t)tl.nt * BN + 64 * q + 32 * j;
+        if (col0 >= N) continue;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          float d[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // (the elements go through values: a bit cast of a vector
+            // element designator reads element 0)
+            const float x0 = acc[i][j][8 * c + e], x1 = acc[i][j][8 * c + 4 + e];
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0),
+                                                            __float_as_uint(x1), false, false);
+            d[e] = __uint_as_float((uint32_t)r[0]);
+            d[4 + e] = __uint_as_float((uint32_t)r[1]);
+          }
+          if (!ok) continue;
+          const int64_t col = col0 + 16 * c + 8 * hi;
+          const uint4 q1 = cur[j][c][0], q3 = cur[j][c][1];
+          const uint32_t w1[4] = {q1.x, q1.y, q1.z, q1.w}, w3[4] = {q3.x, q3.y, q3.z, q3.w};
+          uint32_t o1[4], o3[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            float g1[2], g3[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const float a1 = __uint_as_float(e ? w1[p] & 0xFFFF0000u : w1[p] << 16);
+              const float a3 = __uint_as_float(e ? w3[p] & 0xFFFF0000u : w3[p] << 16);
+              const float du = d[2 * p + e];
+              const float sg = 1.f / (1.f + __expf(-a1));
+              g1[e] = du * a3 * sg * (1.f + a1 * (1.f - sg));
+              g3[e] = du * a1 * sg;
+            }
+            o1[p] = pack_bf16x2(g1[0], g1[1]);
+            o3[p] = pack_bf16x2(g3[0], g3[1]);
+          }
+          *reinterpret_cast<uint4*>(orow + col) = uint4{o1[0], o1[1], o1[2], o1[3]};
+          *reinterpret_cast<uint4*>(orow + N + col) = uint4{o3[0], o3[1], o3[2], o3[3]};
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FI; ++i) {
     const int row = grp * 32 * FI + i * 32 + (lane & 31);
@@ -333,7 +537,7 @@ __device__ __forceinline__ void store_tile_pp(const floatx16 (&acc)[FI][2], cons
 // ds_read_b64_tr_b16 per fragment: in a 16-lane group, lane 4*j + r
 // addresses row j, columns 4r .. 4r + 3, and lane i receives column i of
 // rows 0 .. 3).
-template <bool SWIGLU, int FI, int NA, int NB, bool GATHER, bool BKM>
+template <bool SWIGLU, int FI, int NA, int NB, bool GATHER, bool BKM, int EPI>
 __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Tile& tl, int kbeg,
                                              int nsteps, int krot, int part, int parts,
                                              int64_t slot, uint8_t* smem) {
@@ -405,8 +609,10 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
     // of range)
     const int64_t n0 = (int64_t)tl.nt * BN;
     const int64_t krows0 = a.b_ksplit > 0 ? a.b_ksplit : K;
-    rs0 = make_rsrc(B0 + n0, (uint32_t)((krows0 * ldb - n0) * 2));
-    rs1 = a.b_ksplit > 0 ? make_rsrc(B1 + n0, (uint32_t)(((K - krows0) * ldb - n0) * 2)) : rs0;
+    const int64_t kv0 = a.b_krows > 0 ? a.b_krows : krows0;
+    const int64_t kv1 = a.b_krows > 0 ? a.b_krows : K - krows0;
+    rs0 = make_rsrc(B0 + n0, (uint32_t)((kv0 * ldb - n0) * 2));
+    rs1 = a.b_ksplit > 0 ? make_rsrc(B1 + n0, (uint32_t)((kv1 * ldb - n0) * 2)) : rs0;
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const int row = 16 * q + 2 * b + (lane >> 5);
@@ -637,24 +843,27 @@ __device__ __forceinline__ void tile_body_pp(const GroupedGemmArgs& a, const Til
         }
     return;
   }
-  store_tile_pp<SWIGLU, FI>(acc, tl, lane, grp, q, out_map(a, tl.g), N);
+  store_tile_pp<SWIGLU, FI, EPI>(acc, tl, lane, grp, q, out_map(a, tl.g), N);
 }
 
-template <bool SWIGLU, bool GATHER, bool BKM>
+template <bool SWIGLU, bool GATHER, bool BKM, int EPI>
 __device__ __forceinline__ void tile_dispatch_pp(const GroupedGemmArgs& a, const Tile& tl, int fi,
                                                  int kbeg, int nsteps, int krot, int part,
                                                  int parts, int64_t slot, uint8_t* smem) {
   if (fi == 4)
-    tile_body_pp<SWIGLU, 4, kTallNA, kTallNB, GATHER, BKM>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+    tile_body_pp<SWIGLU, 4, kTallNA, kTallNB, GATHER, BKM, EPI>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
   else if (fi == 3)
-    tile_body_pp<SWIGLU, 3, kTallNA, kTallNB, GATHER, BKM>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+    tile_body_pp<SWIGLU, 3, kTallNA, kTallNB, GATHER, BKM, EPI>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
   else if (fi == 2)
-    tile_body_pp<SWIGLU, 2, 3, 3, GATHER, BKM>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+    tile_body_pp<SWIGLU, 2, 3, 3, GATHER, BKM, EPI>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
   else
-    tile_body_pp<SWIGLU, 1, 3, 3, GATHER, BKM>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
+    tile_body_pp<SWIGLU, 1, 3, 3, GATHER, BKM, EPI>(a, tl, kbeg, nsteps, krot, part, parts, slot, smem);
 }
 
-template <bool SWIGLU>
+// EPI: the epilogue of a plain product (kEpiPlain, kEpiDSwiglu with
+// a.dsw_a13, kEpiDxGather with a.dxg), each a kernel of its own so that the
+// others keep their register allocation.
+template <bool SWIGLU, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kPPLds];   // 160 KiB
   const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
@@ -715,15 +924,24 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
   // three B slots; taller tiles take three A and two B slots (two A and
   // three B, the weights given the longer lead, measured the same)
   const int fi = frags_of(tl.m_valid);
-  if (SWIGLU && a.a_map)
-    tile_dispatch_pp<SWIGLU, true, false>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
-  else if (!SWIGLU && a.b_kmajor)
-    tile_dispatch_pp<SWIGLU, false, true>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
-  else
-    tile_dispatch_pp<SWIGLU, false, false>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+  // gathered A rows: SwiGLU mode only; K-major B: plain mode only (the
+  // dx-gathering epilogue always reads W_router K-major)
+  if constexpr (SWIGLU) {
+    if (a.a_map)
+      tile_dispatch_pp<SWIGLU, true, false, EPI>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    else
+      tile_dispatch_pp<SWIGLU, false, false, EPI>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+  } else if constexpr (EPI == kEpiDxGather) {
+    tile_dispatch_pp<SWIGLU, false, true, EPI>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+  } else {
+    if (a.b_kmajor)
+      tile_dispatch_pp<SWIGLU, false, true, EPI>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+    else
+      tile_dispatch_pp<SWIGLU, false, false, EPI>(a, tl, fi, kbeg, nsteps, krot, part, parts, wk.slot, smem);
+  }
 }
 
-template <bool SWIGLU, int FI>
+template <bool SWIGLU, int FI, int EPI>
 __device__ __forceinline__ void reduce_body_pp(const GroupedGemmArgs& a, const Tile& tl, int s,
                                                int64_t slot) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -751,10 +969,23 @@ __device__ __forceinline__ void reduce_body_pp(const GroupedGemmArgs& a, const T
           for (int e = 0; e < 4; ++e) acc[i][j][4 * r4 + e] += v[j * 4 + r4][e];
     }
   }
-  store_tile_pp<SWIGLU, FI>(acc, tl, lane, w >> 2, w & 3, out_map(a, tl.g), a.N);
+  store_tile_pp<SWIGLU, FI, EPI>(acc, tl, lane, w >> 2, w & 3, out_map(a, tl.g), a.N);
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, int EPI>
+__device__ __forceinline__ void reduce_dispatch_pp(const GroupedGemmArgs& a, const Tile& tl, int fi,
+                                                   int s, int64_t slot) {
+  if (fi == 4)
+    reduce_body_pp<SWIGLU, 4, EPI>(a, tl, s, slot);
+  else if (fi == 3)
+    reduce_body_pp<SWIGLU, 3, EPI>(a, tl, s, slot);
+  else if (fi == 2)
+    reduce_body_pp<SWIGLU, 2, EPI>(a, tl, s, slot);
+  else
+    reduce_body_pp<SWIGLU, 1, EPI>(a, tl, s, slot);
+}
+
+template <bool SWIGLU, int EPI>
 __global__ __launch_bounds__(512) void gemm_pp_reduce_kernel(GroupedGemmArgs a) {
   const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
   const int nk = a.K / BK;
@@ -764,15 +995,7 @@ __global__ __launch_bounds__(512) void gemm_pp_reduce_kernel(GroupedGemmArgs a) 
   const int64_t slot = blockIdx.x;
   if (s < 2 || whole + slot >= V) return;
   const Tile tl = tile_of(a, a.gtab, NT, whole + slot, BM);
-  const int fi = frags_of(tl.m_valid);
-  if (fi == 4)
-    reduce_body_pp<SWIGLU, 4>(a, tl, s, slot);
-  else if (fi == 3)
-    reduce_body_pp<SWIGLU, 3>(a, tl, s, slot);
-  else if (fi == 2)
-    reduce_body_pp<SWIGLU, 2>(a, tl, s, slot);
-  else
-    reduce_body_pp<SWIGLU, 1>(a, tl, s, slot);
+  reduce_dispatch_pp<SWIGLU, EPI>(a, tl, frags_of(tl.m_valid), s, slot);
 }
 
 // fp32 layers: 64x64 tiles, BK = 16, fp32 FMA, each thread 4 rows x 4
@@ -917,16 +1140,24 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, const GroupedGemmArgs& a,
                                 : a.max_m_tiles * NT + (a.partials ? a.num_cu : 0);
     if (nb <= 0) return hipSuccess;
     if (swiglu)
-      MOE_LAUNCH(gemm_pp_kernel<true>, dim3((unsigned)nb), dim3(512), 0, s, a);
+      MOE_LAUNCH((gemm_pp_kernel<true, kEpiPlain>), dim3((unsigned)nb), dim3(512), 0, s, a);
+    else if (a.dsw_a13)
+      MOE_LAUNCH((gemm_pp_kernel<false, kEpiDSwiglu>), dim3((unsigned)nb), dim3(512), 0, s, a);
+    else if (a.dxg)
+      MOE_LAUNCH((gemm_pp_kernel<false, kEpiDxGather>), dim3((unsigned)nb), dim3(512), 0, s, a);
     else
-      MOE_LAUNCH(gemm_pp_kernel<false>, dim3((unsigned)nb), dim3(512), 0, s, a);
+      MOE_LAUNCH((gemm_pp_kernel<false, kEpiPlain>), dim3((unsigned)nb), dim3(512), 0, s, a);
     if (a.partials && !a.kgroup) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       if (swiglu)
-        MOE_LAUNCH(gemm_pp_reduce_kernel<true>, dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
+        MOE_LAUNCH((gemm_pp_reduce_kernel<true, kEpiPlain>), dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
+      else if (a.dsw_a13)
+        MOE_LAUNCH((gemm_pp_reduce_kernel<false, kEpiDSwiglu>), dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
+      else if (a.dxg)
+        MOE_LAUNCH((gemm_pp_reduce_kernel<false, kEpiDxGather>), dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
       else
-        MOE_LAUNCH(gemm_pp_reduce_kernel<false>, dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
+        MOE_LAUNCH((gemm_pp_reduce_kernel<false, kEpiPlain>), dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
     }
   } else {
     const int NT = a.N / FBN;

@@ -516,6 +516,9 @@ namespace {
 // are in the layer's element type (2 or 4 bytes).
 struct BwdLayout {
   size_t gtab, kta, kto, rowtok, dg, dl, rpart, partials, xp, a13, u, o, dO, dU, dA, dxp;
+  size_t dl_hl, dlT_hl, gt_router, gt_tokens;
+  int Ep;
+  int64_t Tp;
   size_t w2t, w13t, dOT, uT, dAT, xpT, total;
   int ldh, ldf, ld13;
   int64_t ktb;
@@ -533,6 +536,12 @@ struct BwdLayout {
 bool kmajor_weights(const moe_cfg_t& c) {
   return c.dtype == MOE_DTYPE_BF16 && (int64_t)c.F * c.h * 2 < ((int64_t)1 << 31) &&
          rows_of(c) <= (int64_t)512 * c.E;
+}
+
+// bf16 backward: the router's gradients (dl^T x and dl W_router, with dl
+// as bf16 hi + lo parts) run on the grouped GEMM, x read K-major.
+bool router_grads_on_gemm(const moe_cfg_t& c) {
+  return c.dtype == MOE_DTYPE_BF16 && (int64_t)c.T * c.h * 2 < ((int64_t)1 << 31);
 }
 
 BwdLayout bwd_layout_of(const moe_cfg_t& c) {
@@ -560,14 +569,15 @@ BwdLayout bwd_layout_of(const moe_cfg_t& c) {
   const int64_t slots = c.routing == MOE_ROUTE_EXPERT_CHOICE ? E : k;   // gates per token
   L.dg = take((size_t)(T * slots) * 4);
   L.dl = take((size_t)(T * E) * 4);
-  L.rpart = take((size_t)(32 * E * h) * 4);
+  const bool rg = router_grads_on_gemm(c);
+  L.rpart = take(rg ? 0 : (size_t)(32 * E * h) * 4);
   L.partials = take((size_t)moe::kSplitPartialFloats * 4);
   L.xp = take((size_t)rows * L.ldh * es);
   L.a13 = take((size_t)rows_all * L.ld13 * es);
   L.u = take((size_t)rows_all * L.ldf * es);
   L.o = take((size_t)rows_all * L.ldh * es);
   L.dO = take((size_t)rows_all * L.ldh * es);
-  L.dU = take((size_t)rows_all * L.ldf * es);
+  L.dU = take(c.dtype == MOE_DTYPE_BF16 ? 0 : (size_t)rows_all * L.ldf * es);
   L.dA = take((size_t)rows_all * L.ld13 * es);
   L.dxp = take((size_t)rows_all * L.ldh * es);
   const bool wt = !kmajor_weights(c);   // transposed weight copies needed
@@ -577,6 +587,12 @@ BwdLayout bwd_layout_of(const moe_cfg_t& c) {
   L.uT = take((size_t)(F * L.ktb) * es);
   L.dAT = take((size_t)(2 * F * L.ktb) * es);
   L.xpT = take((size_t)(h * L.ktb) * es);
+  L.Ep = (int)((E + 63) / 64 * 64);
+  L.Tp = (T + 63) / 64 * 64;
+  L.dl_hl = take(rg ? (size_t)(T * 2 * L.Ep) * 2 : 0);
+  L.dlT_hl = take(rg ? (size_t)(L.Ep * 2 * L.Tp) * 2 : 0);
+  L.gt_router = take(rg ? (size_t)gtab_ints(1) * 4 : 0);
+  L.gt_tokens = take(rg ? (size_t)gtab_ints(1) * 4 : 0);
   L.total = off;
   return L;
 }
@@ -741,9 +757,16 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
     a.B0 = w2t; a.B0s = w2t + (size_t)E * F * h * L.esz;
   }
   a.b_stride = (int64_t)F * h;
-  a.K = h; a.N = F; a.out = dU; a.ldo = L.ldf;
-  MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
-  MOE_TRY(moe::launch_swiglu_bwd(c.dtype, a13, ld13, dU, L.ldf, rows_all, F, dA, L.ld13, s));
+  a.K = h; a.N = F;
+  if (c.dtype == MOE_DTYPE_BF16) {
+    // the GEMM's epilogue turns dU into dA itself
+    a.out = dA; a.ldo = L.ld13; a.dsw_a13 = a13; a.dsw_ld13 = ld13;
+    MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
+  } else {
+    a.out = dU; a.ldo = L.ldf;
+    MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
+    MOE_TRY(moe::launch_swiglu_bwd(c.dtype, a13, ld13, dU, L.ldf, rows_all, F, dA, L.ld13, s));
+  }
   a = base;
   a.A = dA; a.lda = L.ld13; a.a_from_out_rows = 1;
   if (km) {           // w1, w3 [F,h] are the K-major rows [0,F) and [F,2F)
@@ -779,11 +802,61 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
   // expert choice: the probabilities over all E, softmax (mode 1) or
   // normalised sigmoids (mode 2), slot j = expert j
   const int gmode = ec ? (c.gate == MOE_GATE_SIGMOID_TOPK_NORM ? 2 : 1) : c.gate;
-  MOE_TRY(moe::launch_router_bwd(c.dtype, r.logits, ec ? nullptr : r.topk_idx, r.topk_gate, dg,
-                                 gmode, T, E, k, x, h,
-                                 dl, at<float>(ws, L.rpart), gr.dw_router, gr.dlogit_bias, s));
-  MOE_TRY(moe::launch_dx_final(c.dtype, dxp, L.ldh, r.assign_row, k, rows, c.has_shared, dl, w->w_router,
-                               T, h, E, gr.dx, s));
+  if (!router_grads_on_gemm(c)) {
+    MOE_TRY(moe::launch_router_bwd(c.dtype, r.logits, ec ? nullptr : r.topk_idx, r.topk_gate, dg,
+                                   gmode, T, E, k, x, h,
+                                   dl, at<float>(ws, L.rpart), gr.dw_router, gr.dlogit_bias, s));
+    MOE_TRY(moe::launch_dx_final(c.dtype, dxp, L.ldh, r.assign_row, k, rows, c.has_shared, dl,
+                                 w->w_router, T, h, E, gr.dx, s));
+    return MOE_OK;
+  }
+  // dl, and dl as bf16 hi + lo parts: [hi | lo] rows of 2*Ep per token and
+  // of 2*Tp per expert, so that one bf16 product over K = 2*Ep (or 2*Tp)
+  // against W_router (or x) read twice gives dl's products to ~2^-17
+  uint16_t* dl_hl = at<uint16_t>(ws, L.dl_hl);
+  uint16_t* dlT_hl = at<uint16_t>(ws, L.dlT_hl);
+  int32_t* gt_router = at<int32_t>(ws, L.gt_router);
+  int32_t* gt_tokens = at<int32_t>(ws, L.gt_tokens);
+  const int Ep = L.Ep;
+  const int64_t Tp = L.Tp;
+  MOE_TRY(moe::launch_gates_bwd(r.logits, ec ? nullptr : r.topk_idx, r.topk_gate, dg, gmode, T, E,
+                                k, dl, dl_hl, Ep, dlT_hl, Tp, s));
+  moe::GroupedGemmArgs one{};
+  one.G = 1;
+  one.E_routed = 1;
+  one.num_cu = device_cus();
+  one.partials = at<float>(ws, L.partials);
+  one.b_kmajor = 1;
+  one.ldb = h;
+  one.N = h;
+  one.ldo = h;
+  if (gr.dw_router) {
+    // dw_router [E,h] = dl^T x: A = dlT_hl [E rows of 2*Tp], B = x (K-major)
+    // for K rows [0, Tp) and again for [Tp, 2*Tp)
+    MOE_TRY(moe::launch_single_group_gtab(gt_router, E, BM, s));
+    moe::GroupedGemmArgs g = one;
+    g.gtab = gt_router;
+    g.max_m_tiles = (E + BM - 1) / BM;
+    g.A = dlT_hl; g.lda = (int)(2 * Tp);
+    g.B0 = x; g.B1 = x; g.b_ksplit = (int)Tp; g.b_krows = (int)T;
+    g.K = (int)(2 * Tp);
+    g.out = gr.dw_router;
+    MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, g, s));
+  }
+  if (gr.dlogit_bias) MOE_TRY(moe::launch_bias_grad(dl, T, E, gr.dlogit_bias, s));
+  // dx [T,h] = dl W_router (A = dl_hl [T rows of 2*Ep], B = W_router K-major
+  // twice) plus, in the epilogue, each token's dx_perm rows
+  MOE_TRY(moe::launch_single_group_gtab(gt_tokens, T, BM, s));
+  moe::GroupedGemmArgs g = one;
+  g.gtab = gt_tokens;
+  g.max_m_tiles = (T + BM - 1) / BM;
+  g.A = dl_hl; g.lda = 2 * Ep;
+  g.B0 = w->w_router; g.B1 = w->w_router; g.b_ksplit = Ep; g.b_krows = E;
+  g.K = 2 * Ep;
+  g.out = gr.dx;
+  g.dxg = dxp; g.dxg_assign = r.assign_row; g.dxg_k = k; g.dxg_shared = c.has_shared;
+  g.dxg_rows = rows; g.dxg_ld = L.ldh;
+  MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, g, s));
   return MOE_OK;
 }
 

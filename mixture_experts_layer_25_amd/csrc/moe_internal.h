@@ -96,6 +96,24 @@ struct GroupedGemmArgs {
   // a3 at [N, 2N) of out13's output row (row stride ld13), or NULL.
   void* out13;
   int ld13;
+  // bf16 plain mode, backward of the SwiGLU (N = F): if set, the product is
+  // dU and the tile writes dA1 = dU a3 s (1 + a1 (1 - s)) at columns [0, N)
+  // and dA3 = dU a1 s at [N, 2N) of its output row (s = sigmoid(a1); a1 and
+  // a3 from row r of dsw_a13, columns [0, N) and [N, 2N), row stride
+  // dsw_ld13) instead of dU.
+  const void* dsw_a13;
+  int dsw_ld13;
+  // bf16 plain mode, dx of the layer: if dxg is set, the tile's rows are
+  // tokens and output row t is, rounded once, the product plus the dx_perm
+  // rows dxg[dxg_assign[t * dxg_k + j]] of its slots j in order (ids
+  // outside [0, dxg_rows) skipped) plus, with dxg_shared, dxg[dxg_rows + t]
+  // (row stride dxg_ld).
+  const void* dxg;
+  const int32_t* dxg_assign;
+  int dxg_k;
+  int dxg_shared;
+  int64_t dxg_rows;
+  int64_t dxg_ld;
   // bf16 SwiGLU mode: if set, routed row r is row a_map[r] of A (a_rows rows
   // of stride lda, a_rows * lda * 2 < 2^31 bytes): the tokens are gathered
   // by the copies themselves instead of from a dispatch buffer.
@@ -107,6 +125,9 @@ struct GroupedGemmArgs {
   // (row k - b_ksplit).  Each operand's rows * ldb * 2 < 2^31 bytes.
   int b_kmajor;
   int b_ksplit;
+  // K-major B: K rows each of B0 and B1 holds (0: all of its half); rows
+  // past them read as zero.
+  int b_krows;
 };
 
 hipError_t launch_router(int dtype, const void* x, const void* w_router,
@@ -188,6 +209,19 @@ hipError_t launch_router_bwd(int dtype, const float* logits, const int32_t* idx,
                              const float* gate, const float* dg, int gate_mode, int64_t T, int E,
                              int k, const void* x, int h, float* dl, float* rpart,
                              void* dw_router, float* dlogit_bias, hipStream_t s);
+// dl from dg alone (the first step of launch_router_bwd), and with dl_hl
+// also dl as bf16 parts hi + lo (hi = dl rounded, lo = the rest rounded):
+// dl_hl [T][2Ep] holds [hi | lo] per token and dlT_hl [Ep][2Tp] [hi | lo]
+// per expert (token-contiguous), zero past E experts and T tokens (Ep, Tp
+// multiples of 64).
+hipError_t launch_gates_bwd(const float* logits, const int32_t* idx, const float* gate,
+                            const float* dg, int gate_mode, int64_t T, int E, int k, float* dl,
+                            uint16_t* dl_hl, int Ep, uint16_t* dlT_hl, int64_t Tp,
+                            hipStream_t s);
+hipError_t launch_bias_grad(const float* dl, int64_t T, int E, float* dlogit_bias,
+                            hipStream_t s);
+// Tile table of a single group of `rows` rows (A and output rows from 0).
+hipError_t launch_single_group_gtab(int32_t* gtab, int64_t rows, int BM, hipStream_t s);
 hipError_t launch_dx_final(int dtype, const void* dxp, int ldp, const int32_t* assign_row, int k,
                            int64_t rows, int has_shared, const float* dl, const void* w_router,
                            int64_t T, int h, int E, void* dx, hipStream_t s);
