@@ -525,17 +525,25 @@ struct BwdLayout {
   size_t esz;
 };
 
-// bf16 backward with at most 512 dispatch rows per expert on average: the
-// input-gradient GEMMs read w2 and [w1; w3] in their own [K, N] layouts
-// (K-major B operand) instead of transposed copies.  The transposing LDS
-// reads cost GEMM time in proportion to the rows, the transposes in
-// proportion to the weights: at 128 rows per expert (256 experts) the
-// K-major reads save a third of the backward; at 1024 rows per expert
-// (16384 tokens, 64 experts, top-4) they are 2.5 % slower than the
-// transposes.
-bool kmajor_weights(const moe_cfg_t& c) {
-  return c.dtype == MOE_DTYPE_BF16 && (int64_t)c.F * c.h * 2 < ((int64_t)1 << 31) &&
-         rows_of(c) <= (int64_t)512 * c.E;
+// bf16 backward: the input-gradient GEMMs may read w2 (for dU) and [w1; w3]
+// (for dx_perm) in their own [K, N] layouts (K-major B operand) instead of
+// transposed copies.  The transposing LDS reads cost GEMM time in proportion
+// to the dispatch rows, the transposes in proportion to the weights, so each
+// weight is read K-major up to a number of dispatch rows per expert.  With
+// the transposes at ~5 TB/s, the GEMMs at ~1.1 PFLOP/s and the transposing
+// reads adding ~43 % to dU's GEMM and ~31 % to dx_perm's, the two costs meet
+// near 1000 rows per expert for w2 and 1400 for [w1; w3] (measured: [w1; w3]
+// K-major saves 3 % of the backward at 1280 rows per expert and costs 2 %
+// at 2048).
+constexpr int64_t kKmajorRowsW2 = 512, kKmajorRowsW13 = 1536;
+bool kmajor_ok(const moe_cfg_t& c) {
+  return c.dtype == MOE_DTYPE_BF16 && (int64_t)c.F * c.h * 2 < ((int64_t)1 << 31);
+}
+bool kmajor_w2(const moe_cfg_t& c) {
+  return kmajor_ok(c) && rows_of(c) <= kKmajorRowsW2 * c.E;
+}
+bool kmajor_w13(const moe_cfg_t& c) {
+  return kmajor_ok(c) && rows_of(c) <= kKmajorRowsW13 * c.E;
 }
 
 // bf16 backward: the router's gradients (dl^T x and dl W_router, with dl
@@ -580,9 +588,8 @@ BwdLayout bwd_layout_of(const moe_cfg_t& c) {
   L.dU = take(c.dtype == MOE_DTYPE_BF16 ? 0 : (size_t)rows_all * L.ldf * es);
   L.dA = take((size_t)rows_all * L.ld13 * es);
   L.dxp = take((size_t)rows_all * L.ldh * es);
-  const bool wt = !kmajor_weights(c);   // transposed weight copies needed
-  L.w2t = take(wt ? (size_t)(G * F * h) * es : 0);
-  L.w13t = take(wt ? (size_t)(G * h * 2 * F) * es : 0);
+  L.w2t = take(kmajor_w2(c) ? 0 : (size_t)(G * F * h) * es);   // transposed copies
+  L.w13t = take(kmajor_w13(c) ? 0 : (size_t)(G * h * 2 * F) * es);
   L.dOT = take((size_t)(h * L.ktb) * es);
   L.uT = take((size_t)(F * L.ktb) * es);
   L.dAT = take((size_t)(2 * F * L.ktb) * es);
@@ -704,20 +711,25 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
                                 s));
   // transposed weights (unless the GEMMs read them K-major): w2t[g] =
   // w2[g]^T [F,h]; w13t[g] = [w1[g]^T | w3[g]^T] [h,2F]
-  const bool km = kmajor_weights(c);
-  if (!km) {
-  MOE_TRY(moe::launch_transpose(c.dtype, w->w2, (int64_t)h * F, h, F, w2t, (int64_t)F * h, h, 0, E, s));
-  MOE_TRY(moe::launch_transpose(c.dtype, w->w1, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F, 2 * F, 0,
-                                E, s));
-  MOE_TRY(moe::launch_transpose(c.dtype, w->w3, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F, 2 * F, F,
-                                E, s));
+  const bool km2 = kmajor_w2(c), km13 = kmajor_w13(c);
+  if (!km2) {
+    MOE_TRY(moe::launch_transpose(c.dtype, w->w2, (int64_t)h * F, h, F, w2t, (int64_t)F * h, h, 0,
+                                  E, s));
+    if (c.has_shared)
+      MOE_TRY(moe::launch_transpose(c.dtype, w->ws2, 0, h, F, w2t + (size_t)E * F * h * L.esz, 0,
+                                    h, 0, 1, s));
   }
-  if (c.has_shared && !km) {
-    MOE_TRY(moe::launch_transpose(c.dtype, w->ws2, 0, h, F, w2t + (size_t)E * F * h * L.esz, 0, h, 0, 1, s));
-    MOE_TRY(moe::launch_transpose(c.dtype, w->ws1, 0, F, h, w13t + (size_t)E * h * 2 * F * L.esz, 0, 2 * F, 0,
-                                  1, s));
-    MOE_TRY(moe::launch_transpose(c.dtype, w->ws3, 0, F, h, w13t + (size_t)E * h * 2 * F * L.esz, 0, 2 * F, F,
-                                  1, s));
+  if (!km13) {
+    MOE_TRY(moe::launch_transpose(c.dtype, w->w1, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F,
+                                  2 * F, 0, E, s));
+    MOE_TRY(moe::launch_transpose(c.dtype, w->w3, (int64_t)F * h, F, h, w13t, (int64_t)h * 2 * F,
+                                  2 * F, F, E, s));
+    if (c.has_shared) {
+      MOE_TRY(moe::launch_transpose(c.dtype, w->ws1, 0, F, h, w13t + (size_t)E * h * 2 * F * L.esz,
+                                    0, 2 * F, 0, 1, s));
+      MOE_TRY(moe::launch_transpose(c.dtype, w->ws3, 0, F, h, w13t + (size_t)E * h * 2 * F * L.esz,
+                                    0, 2 * F, F, 1, s));
+    }
   }
 
   moe::GroupedGemmArgs base{};
@@ -751,7 +763,7 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
   // dU = dO w2, then dA, then dx_perm = dA [w1; w3]
   a = base;
   a.A = dO; a.lda = L.ldh; a.a_from_out_rows = 1;
-  if (km) {           // w2 [h,F] is K-major for dU
+  if (km2) {          // w2 [h,F] is K-major for dU
     a.B0 = w->w2; a.B0s = w->ws2; a.b_kmajor = 1; a.ldb = F;
   } else {
     a.B0 = w2t; a.B0s = w2t + (size_t)E * F * h * L.esz;
@@ -769,7 +781,7 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
   }
   a = base;
   a.A = dA; a.lda = L.ld13; a.a_from_out_rows = 1;
-  if (km) {           // w1, w3 [F,h] are the K-major rows [0,F) and [F,2F)
+  if (km13) {         // w1, w3 [F,h] are the K-major rows [0,F) and [F,2F)
     a.B0 = w->w1; a.B1 = w->w3; a.B0s = w->ws1; a.B1s = w->ws3;
     a.b_kmajor = 1; a.b_ksplit = F; a.ldb = h; a.b_stride = (int64_t)F * h;
   } else {

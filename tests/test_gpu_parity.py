@@ -59,9 +59,12 @@ MEDIUM = [
     MoEConfig("e20_wide", T=300, h=512, E=20, k=2, F=256, gate="softmax_all_topk", cf=(1, 1)),
     # 65..128 experts: the top-k kernel's 16-lane segments of 8 experts
     MoEConfig("e100_k6", T=400, h=256, E=100, k=6, F=128, gate="softmax_topk"),
-    # more than 512 dispatch rows per expert: the bf16 backward reads
-    # transposed weight copies (with fewer, the weights K-major)
+    # the bf16 backward reads w2 through a transposed copy past 512 dispatch
+    # rows per expert and [w1; w3] past 1536 (with fewer, K-major): 600 rows
+    # per expert transpose w2 only, 1600 both
     MoEConfig("bwd_many_rows", T=1200, h=256, E=4, k=2, F=384, gate="sigmoid_topk_norm",
+              shared=True),
+    MoEConfig("bwd_more_rows", T=1600, h=256, E=2, k=2, F=256, gate="softmax_topk",
               shared=True),
     # K long enough (>= 16 slices of 64) that the tiles of the last partial
     # round are split along K and reduced (GEMM 1 and GEMM 2)
@@ -101,9 +104,12 @@ def test_forward_matches_oracle(cfg):
 
 
 # ------------------------------------------------------------------ backward
+# e1024_k16: more than 256 experts (the gates backward's per-thread kernel);
+# drop_all_shared: most slots dropped, dx mostly the shared expert's rows
 BACKWARD = ["dropless_softmax", "capacity_heavy_drop", "worked_example_small",
             "sigmoid_bias_shared", "zipf_dropless", "split_k_tail", "e40_ragged",
             "mixtral_bias", "e256_k8_shared", "k_equals_e", "bwd_many_rows",
+            "bwd_more_rows", "e1024_k16", "drop_all_shared",
             "tiny_fp32", "f32_capacity", "f32_sigmoid_shared"]
 
 
@@ -192,7 +198,8 @@ def test_backward_is_deterministic():
 
 
 SAVED = ["worked_example_small", "sigmoid_bias_shared", "capacity_heavy_drop", "split_k_tail",
-         "zipf_dropless", "e40_ragged", "bwd_many_rows", "tiny_fp32", "f32_sigmoid_shared"]
+         "zipf_dropless", "e40_ragged", "bwd_many_rows", "bwd_more_rows", "tiny_fp32",
+         "f32_sigmoid_shared"]
 
 
 @pytest.mark.parametrize("name", SAVED)
