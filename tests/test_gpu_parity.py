@@ -66,6 +66,10 @@ MEDIUM = [
               shared=True),
     MoEConfig("bwd_more_rows", T=1600, h=256, E=2, k=2, F=256, gate="softmax_topk",
               shared=True),
+    # few rows per expert and at most 256 tokens: every weight gradient,
+    # the shared expert's too, on the 128x128 small-K tiles
+    MoEConfig("bwd_few_rows_shared", T=200, h=384, E=8, k=2, F=256, gate="sigmoid_topk_norm",
+              shared=True),
     # K long enough (>= 16 slices of 64) that the tiles of the last partial
     # round are split along K and reduced (GEMM 1 and GEMM 2)
     MoEConfig("split_k_tail", T=600, h=1024, E=4, k=2, F=1024, gate="softmax_topk"),
@@ -109,7 +113,7 @@ def test_forward_matches_oracle(cfg):
 BACKWARD = ["dropless_softmax", "capacity_heavy_drop", "worked_example_small",
             "sigmoid_bias_shared", "zipf_dropless", "split_k_tail", "e40_ragged",
             "mixtral_bias", "e256_k8_shared", "k_equals_e", "bwd_many_rows",
-            "bwd_more_rows", "e1024_k16", "drop_all_shared",
+            "bwd_more_rows", "bwd_few_rows_shared", "e1024_k16", "drop_all_shared",
             "tiny_fp32", "f32_capacity", "f32_sigmoid_shared"]
 
 
@@ -198,7 +202,8 @@ def test_backward_is_deterministic():
 
 
 SAVED = ["worked_example_small", "sigmoid_bias_shared", "capacity_heavy_drop", "split_k_tail",
-         "zipf_dropless", "e40_ragged", "bwd_many_rows", "bwd_more_rows", "tiny_fp32",
+         "zipf_dropless", "e40_ragged", "bwd_many_rows", "bwd_more_rows", "bwd_few_rows_shared",
+         "tiny_fp32",
          "f32_sigmoid_shared"]
 
 
