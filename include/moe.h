@@ -400,8 +400,11 @@ int moe_select_bias_update(const moe_cfg_t* cfg, const int32_t* expert_counts,
  * assign_row are the forward's [T,E] slots and dgate is [T,E]; the gate of
  * a chosen (t, e) is the router probability itself, so the logits get that
  * distribution's Jacobian over all E (10.5 section 10.5.6).  Gradient sums
- * in fp32; dx, weight gradients and the intermediates (a1, a3, u, dO, dU,
- * dA, dx_perm) stored in the layer's dtype.  Every sum has a fixed order:
+ * in fp32; dx, weight gradients and the intermediates (a1, a3, u, dO, dA,
+ * dx_perm; fp32 layers also dU) stored in the layer's dtype.  bf16 layers
+ * form dA from dU in fp32 registers, and take dl^T x and dl w_router as
+ * bf16 products of dl's parts hi = bf16(dl), lo = bf16(dl - hi), which
+ * carry dl to about 2^-17 of its size.  Every sum has a fixed order:
  * the same bits on every run.  Size limit: the dispatch rows plus 64 per
  * group (E, + 1 with a shared expert), rounded up to 64, stay below 2^25;
  * beyond it both calls return MOE_ERR_UNSUPPORTED.                        */
