@@ -312,9 +312,10 @@ int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Arguments, results and errors are those
  * of moe_grouped_gemm_swiglu (bit-identical outputs), without ws/ws_bytes:
- * its scratch (the tile table and the split-K partial tiles) is a
- * file-scope device array of MOE_NOALLOC_SCRATCH_BYTES in the library,
- * one per GPU, held from the library's load until the process ends.  Limit:
+ * its scratch (the tile table with its tile-claim counters and the split-K
+ * partial tiles) is a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES
+ * in the library, one per GPU, held from the library's load until the
+ * process ends.  Limit:
  * every config the library accepts fits it (E <= 1024 groups, at most 256
  * split-K parts); a config needing more returns MOE_ERR_UNSUPPORTED before
  * any device work.  The call allocates and frees nothing and sets no
@@ -323,7 +324,7 @@ int moe_grouped_gemm_swiglu(const moe_cfg_t* cfg, const void* x_perm,
  * overlap on one GPU (different streams, or threads) race and give
  * unspecified results; calls in one stream are ordered and safe.
  * MOE_ERR_HIP if the scratch's device address cannot be obtained.          */
-#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16640 + (size_t)67108864)
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)25856 + (size_t)67108864)
 int moe_grouped_gemm_swiglu_noalloc(const moe_cfg_t* cfg, const void* x_perm,
                                     const int32_t* expert_counts,
                                     const int32_t* expert_offsets, const void* w1,

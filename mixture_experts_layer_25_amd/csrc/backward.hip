@@ -436,13 +436,18 @@ __global__ __launch_bounds__(256) void gates_bwd_split_kernel(
 }
 
 // Tile table (4G + 1 ints, G = 1) of one group of `rows` rows: its row
-// tiles, first A row 0, its rows, first output row 0.
+// tiles, first A row 0, its rows, first output row 0; its claim blocks
+// zeroed.  One workgroup of 256 threads.
 __global__ void single_group_gtab_kernel(int32_t* gt, int64_t rows, int BM) {
-  gt[0] = 0;
-  gt[1] = (int32_t)((rows + BM - 1) / BM);
-  gt[2] = 0;
-  gt[3] = (int32_t)rows;
-  gt[4] = 0;
+  for (int i = threadIdx.x; i < kClaimBlocks * kClaimBlockInts; i += 256)
+    gt[gtab_claims_off(1) + i] = 0;
+  if (threadIdx.x == 0) {
+    gt[0] = 0;
+    gt[1] = (int32_t)((rows + BM - 1) / BM);
+    gt[2] = 0;
+    gt[3] = (int32_t)rows;
+    gt[4] = 0;
+  }
 }
 
 // dW_router[e, i] = sum_t dl[t,e] x[t,i]: workgroup (column tile, 32
@@ -711,7 +716,7 @@ hipError_t launch_bias_grad(const float* dl, int64_t T, int E, float* dlogit_bia
 }
 
 hipError_t launch_single_group_gtab(int32_t* gtab, int64_t rows, int BM, hipStream_t s) {
-  MOE_LAUNCH(single_group_gtab_kernel, dim3(1), dim3(1), 0, s, gtab, rows, BM);
+  MOE_LAUNCH(single_group_gtab_kernel, dim3(1), dim3(256), 0, s, gtab, rows, BM);
   return hipGetLastError();
 }
 

@@ -96,13 +96,35 @@ __device__ __forceinline__ int64_t plain_tile(const GroupedGemmArgs& a, int NT, 
 // tiles would leave most units idle in a final round, so each is split
 // along K into s = min(P / r, nk / 8) parts (when s >= 2), computed by r*s
 // workgroups that write fp32 partial tiles; a reduce kernel sums them.
-// Whole tiles: workgroup b runs on XCD b % 8, and consecutive logical tiles
-// are handed to the same XCD so that they share its L2.
+// Whole tiles: workgroup b runs on XCD b % 8, and XCD x owns the x-th of
+// eight contiguous runs of logical tiles, so that the workgroups sharing a
+// weight column tile and a token row tile share its L2.  Without claim
+// counters, workgroup 8j + x computes tile j of run x and the split parts
+// follow the whole tiles in workgroup order.  With them (a.claims), every
+// workgroup claims its work: the next tile of its own run, or, once that
+// run is empty, the last unclaimed tile of the fullest other run (an XCD
+// that finishes early takes over the end of a slower one's run), or, once
+// every run is empty, the next split part.
 struct Work {
   int64_t L;        // logical tile, -1: nothing to do
   int part, parts;  // K part of a split tile (parts == 1: whole tile)
   int64_t slot;     // split tiles: index among the split tiles
 };
+static_assert(sizeof(Work) <= 32, "a claimed Work fits the last 32 bytes of LDS");
+
+// Workgroups per XCD beyond the bound on the tiles and split parts, which
+// find work only in the runs of other XCDs.
+constexpr int kClaimSlack = 32;
+// Distance between two claim counters in uint64.
+constexpr int kClaimU64 = kClaimStride / 8;
+
+// Workgroups of a bf16 launch that is not split along groups' K: a bound on
+// the whole tiles and split parts (all row tiles times the column tiles,
+// plus one compute unit's worth of parts), and with claim counters the
+// slack of every XCD.
+__host__ __device__ inline int64_t pp_workgroups(const GroupedGemmArgs& a, int NT) {
+  return a.max_m_tiles * NT + (a.partials ? a.num_cu : 0) + (a.claims ? 8 * kClaimSlack : 0);
+}
 
 __device__ __forceinline__ void split_shape(const GroupedGemmArgs& a, int32_t tiles, int NT,
                                             int nk, int64_t& V, int64_t& whole, int& s) {
@@ -117,6 +139,104 @@ __device__ __forceinline__ void split_shape(const GroupedGemmArgs& a, int32_t ti
   whole = s >= 2 ? V - r : V;
 }
 
+// Run x of the whole tiles: [start, start + n).
+__device__ __forceinline__ void xcd_run(int64_t whole, int x, int64_t& start, int64_t& n) {
+  const int64_t q = whole >> 3, r8 = whole & 7;
+  start = x * q + (x < r8 ? x : r8);
+  n = q + (x < r8 ? 1 : 0);
+}
+
+// A whole tile for a workgroup of XCD run x whose claim on its own run
+// returned `own` (counter value before its increment), or -1 when every
+// run is empty.  A counter holds the tiles taken from the front of its run
+// (low 32 bits) and from the back (high 32 bits); an increment claims a
+// tile exactly when the two together were below the run's length, so each
+// tile is claimed once.  Every failed claim marks a run as empty: at most
+// eight rounds.
+__device__ int64_t claim_whole_tile(unsigned long long* cl, unsigned long long own, int x,
+                                    int64_t whole) {
+  int64_t st, n;
+  xcd_run(whole, x, st, n);
+  {
+    const int64_t h = (uint32_t)own, t = (int64_t)(own >> 32);
+    if (h + t < n) return st + h;
+  }
+  unsigned empty = 1u << x;
+  for (int it = 0; it < 8; ++it) {
+    unsigned long long v[8];
+#pragma unroll
+    for (int y = 0; y < 8; ++y)
+      v[y] = ((empty >> y) & 1) ? 0ull
+                                : __hip_atomic_load(cl + y * kClaimU64, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+    int best = -1;
+    int64_t brem = 0;
+#pragma unroll
+    for (int y = 0; y < 8; ++y) {
+      if ((empty >> y) & 1) continue;
+      int64_t sy, ny;
+      xcd_run(whole, y, sy, ny);
+      const int64_t rem = ny - ((int64_t)(uint32_t)v[y] + (int64_t)(v[y] >> 32));
+      if (rem <= 0)
+        empty |= 1u << y;
+      else if (rem > brem) {
+        brem = rem;
+        best = y;
+      }
+    }
+    if (best < 0) return -1;
+    const unsigned long long o = atomicAdd(cl + best * kClaimU64, 1ull << 32);
+    int64_t sb, nb;
+    xcd_run(whole, best, sb, nb);
+    const int64_t h = (uint32_t)o, t = (int64_t)(o >> 32);
+    if (h + t < nb) return sb + nb - 1 - t;
+    empty |= 1u << best;
+  }
+  return -1;
+}
+
+// Split part q of the split tiles (s parts each).
+__device__ __forceinline__ Work split_part(int64_t whole, int s, int64_t q) {
+  Work wk{-1, 0, 1, 0};
+  wk.slot = q / s;
+  wk.L = whole + wk.slot;
+  wk.part = (int)(q - wk.slot * s);
+  wk.parts = s;
+  return wk;
+}
+
+// Work of workgroup b with claim counters `cl` (8 run counters, then the
+// split-part counter), its claim on its own run having returned `own`:
+// that tile, else (workgroups below the number of tiles and parts plus the
+// slack) another run's tile or the next split part, else nothing.  Every
+// workgroup of that number ends with work or after seeing all work
+// claimed, and there are more of them than pieces of work, so all of it is
+// claimed.
+__device__ Work claim_work(unsigned long long* cl, unsigned long long own, int64_t b, int64_t V,
+                           int64_t whole, int s) {
+  Work wk{-1, 0, 1, 0};
+  const int x = (int)(b & 7);
+  {
+    int64_t st, n;
+    xcd_run(whole, x, st, n);
+    const int64_t h = (uint32_t)own, t = (int64_t)(own >> 32);
+    if (h + t < n) {
+      wk.L = st + h;
+      return wk;
+    }
+  }
+  const int64_t parts = s >= 2 ? (V - whole) * s : 0;
+  if (b >= whole + parts + 8 * kClaimSlack) return wk;
+  wk.L = claim_whole_tile(cl, own, x, whole);
+  if (wk.L < 0 && parts > 0) {
+    const int64_t q = (int64_t)atomicAdd(cl + 8 * kClaimU64, 1ull);
+    if (q < parts) wk = split_part(whole, s, q);
+  }
+  return wk;
+}
+
+// Work of workgroup b without claim counters: its whole tile by index, or
+// its split part (split workgroups follow the whole tiles).
 __device__ __forceinline__ Work plan_work(const GroupedGemmArgs& a, int32_t tiles, int NT, int nk,
                                           int64_t b) {
   int64_t V, whole;
@@ -124,9 +244,10 @@ __device__ __forceinline__ Work plan_work(const GroupedGemmArgs& a, int32_t tile
   split_shape(a, tiles, NT, nk, V, whole, s);
   Work wk{-1, 0, 1, 0};
   if (b < whole) {
-    const int64_t x = b & 7, q = whole >> 3, r8 = whole & 7;
-    wk.L = x * q + (x < r8 ? x : r8) + (b >> 3);
-  } else if (s >= 2 && b < whole + (V - whole) * s) {
+    int64_t st, n;
+    xcd_run(whole, (int)(b & 7), st, n);
+    wk.L = st + (b >> 3);
+  } else if (s >= 2 && b - whole < (V - whole) * s) {
     const int64_t qd = b - whole;
     wk.slot = qd / s;
     wk.L = whole + wk.slot;
@@ -253,8 +374,9 @@ __device__ __forceinline__ OutMap out_map(const GroupedGemmArgs& a, int g) {
 constexpr int kPPLds = 5 * kPart;            // 160 KiB
 // slot counts of the 192- and 256-row tiles (A, B)
 constexpr int kTallNA = 3, kTallNB = 2;
-// The tile table is staged at [128 KiB, 144.4 KiB): in every slot layout
-// the copies issued before a tile's first barrier stay below 128 KiB.
+// The tile table is staged at [128 KiB, 144.4 KiB) and a claimed tile's
+// work passed on in the last 32 bytes: in every slot layout the copies
+// issued before a tile's first barrier stay below 128 KiB.
 constexpr int kTableOff = 4 * kPart;
 
 // Where split-K partial register group c (= (i*2 + j)*4 + r4) of wave w goes
@@ -894,10 +1016,28 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
     // one parallel load, at kTableOff, which no copy touches before the
     // first barrier; the group search then runs on LDS instead of a chain
     // of dependent global loads.
+    // With claim counters, the claim on the workgroup's own run is issued
+    // with the table load, so that its latency hides behind the load's;
+    // the work then reaches the other waves through the last 32 bytes of
+    // LDS, which no copy touches before the tile's first barrier.
     int32_t* gt = reinterpret_cast<int32_t*>(smem + kTableOff);
+    unsigned long long own = 0;
+    if (a.claims && threadIdx.x == 0) own = atomicAdd(a.claims + (blockIdx.x & 7) * kClaimU64, 1ull);
     for (int i = threadIdx.x; i < 4 * a.G + 1; i += 512) gt[i] = a.gtab[i];
     __syncthreads();
-    wk = plan_work(a, gt[a.G], NT, nk, blockIdx.x);
+    if (a.claims) {
+      Work* slot_w = reinterpret_cast<Work*>(smem + kPPLds - 32);
+      if (threadIdx.x == 0) {
+        int64_t V, whole;
+        int s;
+        split_shape(a, gt[a.G], NT, nk, V, whole, s);
+        *slot_w = claim_work(a.claims, own, blockIdx.x, V, whole, s);
+      }
+      __syncthreads();
+      wk = *slot_w;
+    } else {
+      wk = plan_work(a, gt[a.G], NT, nk, blockIdx.x);
+    }
     if (wk.L < 0) return;
     tl = tile_of(a, gt, NT, wk.L, BM);
     // part `part` of K; a whole tile of a routed group starts at slice
@@ -1137,7 +1277,7 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, const GroupedGemmArgs& a,
     // exactly G x MT x NT tiles
     const int NT = swiglu ? a.N / 128 : (a.N + BN - 1) / BN;
     const int64_t nb = a.kgroup ? (int64_t)a.G * ((a.m_fixed + BM - 1) / BM) * NT
-                                : a.max_m_tiles * NT + (a.partials ? a.num_cu : 0);
+                                : pp_workgroups(a, NT);
     if (nb <= 0) return hipSuccess;
     if (swiglu)
       MOE_LAUNCH((gemm_pp_kernel<true, kEpiPlain>), dim3((unsigned)nb), dim3(512), 0, s, a);

@@ -362,7 +362,9 @@ int grouped_gemm_impl(const moe_cfg_t& c, const void* x_perm, const int32_t* exp
   a.max_m_tiles = max_m_tiles(rows, c.E, BM);
   a.num_cu = device_cus();
   a.partials = c.dtype == MOE_DTYPE_BF16 ? partials : nullptr;
+  a.claims = moe::claim_block(gtab, c.E, 0);
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, true, a, s));
+  a.claims = moe::claim_block(gtab, c.E, 1);
   a.A = act;
   a.B0 = w2;
   a.B1 = nullptr;
@@ -390,12 +392,13 @@ int check_gemm_args(const moe_cfg_t* cfg, const void* x_perm, const int32_t* exp
 }
 
 // ---- the grouped GEMM without a caller workspace ------------------------
-// File-scope device scratch: the tile table (room for 1024 routed groups +
-// 1) and the split-K partial tiles (at most 256 parts of 256 x 256 fp32).
+// File-scope device scratch: the tile table with its claim blocks (room for
+// 1024 routed groups + 1) and the split-K partial tiles (at most 256 parts
+// of 256 x 256 fp32).
 // In host code `scratch` names a host-side stand-in, never the device
 // memory: its device address, one per GPU, comes from hipGetSymbolAddress
 // (scratch_on_current_device) and only that address reaches a kernel.
-constexpr size_t kScratchGtabBytes = (size_t)((4 * 1025 + 1) * 4 + 255) / 256 * 256;
+constexpr size_t kScratchGtabBytes = (size_t)(moe::gtab_ints(1025) * 4 + 255) / 256 * 256;
 constexpr size_t kScratchBytes = kScratchGtabBytes + (size_t)moe::kSplitPartialFloats * 4;
 static_assert(kScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch size as documented");
 __device__ __align__(256) unsigned char scratch[kScratchBytes];
@@ -745,7 +748,7 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
     a.A = xp; a.lda = L.ldh; a.A_shared = x; a.lda_shared = h;
     a.B0 = w->w1; a.B1 = w->w3; a.B0s = w->ws1; a.B1s = w->ws3; a.b_split = 1;
     a.b_stride = (int64_t)F * h; a.K = h; a.N = 2 * F; a.out = at<char>(ws, L.a13);
-    a.ldo = L.ld13;
+    a.ldo = L.ld13; a.claims = moe::claim_block(gtab, G, 0);
     MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
     MOE_TRY(moe::launch_swiglu_fwd(c.dtype, a13, L.ld13, rows_all, F, at<char>(ws, L.u), L.ldf,
                                    s));
@@ -753,7 +756,7 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
     a = base;
     a.A = u; a.lda = L.ldf; a.a_from_out_rows = 1;
     a.B0 = w->w2; a.B0s = w->ws2; a.b_stride = (int64_t)h * F; a.K = F; a.N = h;
-    a.out = at<char>(ws, L.o); a.ldo = L.ldh;
+    a.out = at<char>(ws, L.o); a.ldo = L.ldh; a.claims = moe::claim_block(gtab, G, 1);
     MOE_TRY(moe::launch_grouped_gemm(c.dtype, false, a, s));
   }
   // dO rows, gate gradients
@@ -762,7 +765,7 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
   MOE_TRY(moe::launch_gate_grad(c.dtype, dy, o, ldo, r.assign_row, rows, T, h, k, dg, s));
   // dU = dO w2, then dA, then dx_perm = dA [w1; w3]
   a = base;
-  a.A = dO; a.lda = L.ldh; a.a_from_out_rows = 1;
+  a.A = dO; a.lda = L.ldh; a.a_from_out_rows = 1; a.claims = moe::claim_block(gtab, G, 2);
   if (km2) {          // w2 [h,F] is K-major for dU
     a.B0 = w->w2; a.B0s = w->ws2; a.b_kmajor = 1; a.ldb = F;
   } else {
@@ -780,7 +783,7 @@ int backward_impl(const moe_cfg_t& c, const moe_weights_t* w, const void* x, con
     MOE_TRY(moe::launch_swiglu_bwd(c.dtype, a13, ld13, dU, L.ldf, rows_all, F, dA, L.ld13, s));
   }
   a = base;
-  a.A = dA; a.lda = L.ld13; a.a_from_out_rows = 1;
+  a.A = dA; a.lda = L.ld13; a.a_from_out_rows = 1; a.claims = moe::claim_block(gtab, G, 3);
   if (km13) {         // w1, w3 [F,h] are the K-major rows [0,F) and [F,2F)
     a.B0 = w->w1; a.B1 = w->w3; a.B0s = w->ws1; a.B1s = w->ws3;
     a.b_kmajor = 1; a.b_ksplit = F; a.ldb = h; a.b_stride = (int64_t)F * h;
@@ -1070,8 +1073,10 @@ MOE_API int moe_forward(const moe_cfg_t* cfg, const moe_weights_t* w, const void
     a.out13 = at<char>(ws, L.a13);
     a.ld13 = ld_13(c);
   }
+  a.claims = moe::claim_block(gtab, a.G, 0);
   MOE_TRY(moe::launch_grouped_gemm(c.dtype, true, a, s));
   MOE_TRY(mark(6));
+  a.claims = moe::claim_block(gtab, a.G, 1);
   a.out13 = nullptr;
   a.a_map = nullptr;
   a.A = act;

@@ -46,7 +46,24 @@ inline StageEvents*& stage_events() {
 //   [G+1 .. 2G]     first A row of each group
 //   [2G+1 .. 3G]    rows computed in each group
 //   [3G+1 .. 4G]    first output row of each group
-inline int64_t gtab_ints(int G) { return 4 * (int64_t)G + 1; }
+// then, from int gtab_claims_off(G) (a multiple of 32), kClaimBlocks claim
+// blocks: the work-claim counters of one bf16 grouped GEMM launch each,
+// kClaimCounters uint64 kClaimStride bytes apart (each in a memory line of
+// its own): one per XCD run of whole tiles, counting the tiles taken from
+// its front in the low half and from its back in the high half, then the
+// split parts taken.  Every kernel that writes a tile table zeroes its
+// claim blocks; a launch uses a block of its own.
+constexpr int kClaimBlocks = 4;
+constexpr int kClaimCounters = 9;
+constexpr int kClaimStride = 256;
+constexpr int kClaimBlockInts = kClaimCounters * kClaimStride / 4;
+constexpr int64_t gtab_claims_off(int G) { return (4 * (int64_t)G + 1 + 63) / 64 * 64; }
+constexpr int64_t gtab_ints(int G) { return gtab_claims_off(G) + kClaimBlocks * kClaimBlockInts; }
+// Claim block i (0 <= i < kClaimBlocks) of the tile table `gtab` of G groups.
+inline unsigned long long* claim_block(int32_t* gtab, int G, int i) {
+  return reinterpret_cast<unsigned long long*>(gtab + gtab_claims_off(G) +
+                                               (int64_t)i * kClaimBlockInts);
+}
 
 // Tiles of the last, partial round of a bf16 grouped GEMM are split along K
 // into up to num_cu/r parts whose fp32 partial tiles go to this many floats
@@ -128,6 +145,12 @@ struct GroupedGemmArgs {
   // K-major B: K rows each of B0 and B1 holds (0: all of its half); rows
   // past them read as zero.
   int b_krows;
+  // bf16, not kgroup: if set, workgroups claim their work through these
+  // zeroed counters (a claim block of gtab, used by no other launch since it
+  // was zeroed) instead of taking it by workgroup index: workgroup b takes
+  // the next tile of XCD run b & 7, once that run is empty the last
+  // unclaimed tile of the fullest other run, then the next split part.
+  unsigned long long* claims;
 };
 
 hipError_t launch_router(int dtype, const void* x, const void* w_router,

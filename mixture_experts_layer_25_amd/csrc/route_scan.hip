@@ -53,10 +53,12 @@ __device__ int block_exclusive_scan_1024(int v, int* tmp, int* tot) {
 }
 
 // Tile table of G groups (rows computed per group `valid`, first rows
-// a_row0 / o_row0) for row tiles of BM.  Called by all 1024 threads of the
-// scan workgroups with g = threadIdx.x (G <= 1024).
+// a_row0 / o_row0) for row tiles of BM, and its claim blocks zeroed.
+// Called by all 1024 threads of the scan workgroups with g = threadIdx.x
+// (G <= 1024).
 __device__ void write_gtab(int g, int G, int valid, int a_row0, int o_row0,
                            int BM, int* tmp, int32_t* gtab) {
+  for (int i = g; i < kClaimBlocks * kClaimBlockInts; i += 1024) gtab[gtab_claims_off(G) + i] = 0;
   const int mt = (g < G) ? (valid + BM - 1) / BM : 0;
   int tot;
   const int pre = block_exclusive_scan_1024(mt, tmp, &tot);
