@@ -1083,8 +1083,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GroupedGemmArgs a) {
 
 template <bool SWIGLU, int FI, int EPI>
 __device__ __forceinline__ void reduce_body_pp(const GroupedGemmArgs& a, const Tile& tl, int s,
-                                               int64_t slot) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+                                               int64_t slot, int w) {
+  const int lane = threadIdx.x & 63;
   floatx16 acc[FI][2];
   const float* P0 = a.partials + slot * s * (int64_t)(256 * 256);
   // per row fragment: the 8 loads of a part issued together, parts added in
@@ -1114,28 +1114,31 @@ __device__ __forceinline__ void reduce_body_pp(const GroupedGemmArgs& a, const T
 
 template <bool SWIGLU, int EPI>
 __device__ __forceinline__ void reduce_dispatch_pp(const GroupedGemmArgs& a, const Tile& tl, int fi,
-                                                   int s, int64_t slot) {
+                                                   int s, int64_t slot, int w) {
   if (fi == 4)
-    reduce_body_pp<SWIGLU, 4, EPI>(a, tl, s, slot);
+    reduce_body_pp<SWIGLU, 4, EPI>(a, tl, s, slot, w);
   else if (fi == 3)
-    reduce_body_pp<SWIGLU, 3, EPI>(a, tl, s, slot);
+    reduce_body_pp<SWIGLU, 3, EPI>(a, tl, s, slot, w);
   else if (fi == 2)
-    reduce_body_pp<SWIGLU, 2, EPI>(a, tl, s, slot);
+    reduce_body_pp<SWIGLU, 2, EPI>(a, tl, s, slot, w);
   else
-    reduce_body_pp<SWIGLU, 1, EPI>(a, tl, s, slot);
+    reduce_body_pp<SWIGLU, 1, EPI>(a, tl, s, slot, w);
 }
 
+// One wave per workgroup: workgroup 8 * slot + w sums and stores the part
+// of split tile `slot` that wave w of the product computed (the epilogue
+// is per wave), so the r split tiles occupy 8r compute units, not r.
 template <bool SWIGLU, int EPI>
-__global__ __launch_bounds__(512) void gemm_pp_reduce_kernel(GroupedGemmArgs a) {
+__global__ __launch_bounds__(64) void gemm_pp_reduce_kernel(GroupedGemmArgs a) {
   const int NT = SWIGLU ? a.N / 128 : (a.N + BN - 1) / BN;
   const int nk = a.K / BK;
   int64_t V, whole;
   int s;
   split_shape(a, a.gtab[a.G], NT, nk, V, whole, s);
-  const int64_t slot = blockIdx.x;
+  const int64_t slot = blockIdx.x >> 3;
   if (s < 2 || whole + slot >= V) return;
   const Tile tl = tile_of(a, a.gtab, NT, whole + slot, BM);
-  reduce_dispatch_pp<SWIGLU, EPI>(a, tl, frags_of(tl.m_valid), s, slot);
+  reduce_dispatch_pp<SWIGLU, EPI>(a, tl, frags_of(tl.m_valid), s, slot, (int)(blockIdx.x & 7));
 }
 
 // fp32 layers: 64x64 tiles, BK = 16, fp32 FMA, each thread 4 rows x 4
@@ -1291,13 +1294,13 @@ hipError_t launch_grouped_gemm(int dtype, bool swiglu, const GroupedGemmArgs& a,
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       if (swiglu)
-        MOE_LAUNCH((gemm_pp_reduce_kernel<true, kEpiPlain>), dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
+        MOE_LAUNCH((gemm_pp_reduce_kernel<true, kEpiPlain>), dim3((unsigned)a.num_cu * 8), dim3(64), 0, s, a);
       else if (a.dsw_a13)
-        MOE_LAUNCH((gemm_pp_reduce_kernel<false, kEpiDSwiglu>), dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
+        MOE_LAUNCH((gemm_pp_reduce_kernel<false, kEpiDSwiglu>), dim3((unsigned)a.num_cu * 8), dim3(64), 0, s, a);
       else if (a.dxg)
-        MOE_LAUNCH((gemm_pp_reduce_kernel<false, kEpiDxGather>), dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
+        MOE_LAUNCH((gemm_pp_reduce_kernel<false, kEpiDxGather>), dim3((unsigned)a.num_cu * 8), dim3(64), 0, s, a);
       else
-        MOE_LAUNCH((gemm_pp_reduce_kernel<false, kEpiPlain>), dim3((unsigned)a.num_cu), dim3(512), 0, s, a);
+        MOE_LAUNCH((gemm_pp_reduce_kernel<false, kEpiPlain>), dim3((unsigned)a.num_cu * 8), dim3(64), 0, s, a);
     }
   } else {
     const int NT = a.N / FBN;
