@@ -59,8 +59,10 @@ constexpr int kClaimStride = 256;
 constexpr int kClaimBlockInts = kClaimCounters * kClaimStride / 4;
 constexpr int64_t gtab_claims_off(int G) { return (4 * (int64_t)G + 1 + 63) / 64 * 64; }
 constexpr int64_t gtab_ints(int G) { return gtab_claims_off(G) + kClaimBlocks * kClaimBlockInts; }
-// Claim block i (0 <= i < kClaimBlocks) of the tile table `gtab` of G groups.
+// Claim block i of the tile table `gtab` of G groups; NULL (the launch
+// then takes its work by workgroup index) for i outside [0, kClaimBlocks).
 inline unsigned long long* claim_block(int32_t* gtab, int G, int i) {
+  if (i < 0 || i >= kClaimBlocks) return nullptr;
   return reinterpret_cast<unsigned long long*>(gtab + gtab_claims_off(G) +
                                                (int64_t)i * kClaimBlockInts);
 }
