@@ -277,6 +277,70 @@ __global__ __launch_bounds__(64 * NW) void assign_kernel(
   }
 }
 
+// The same ranks for k > 2 slots when the histogram groups hold at most 64
+// tokens: one workgroup of KP waves per 64 tokens, lane = (token, slot):
+// wave w takes the chunk's tokens [w * 64/KP, (w + 1) * 64/KP), lane l
+// token l / KP and slot l % KP (KP a power of two >= k).  A slot's rank is
+// the chunk's base for its expert, plus the slots of the earlier waves'
+// tokens that hold that expert (LDS counts summed in wave order), plus
+// those of the earlier tokens of its own wave (lanes below its token's
+// first lane whose expert id agrees bit by bit, one ballot per bit), so
+// the rows are those of assign_kernel with a handful of ballots per wave
+// instead of k * k * bits per lane.
+template <int KP>
+__global__ __launch_bounds__(64 * KP) void assign_pairs_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ chunk_base, int gpc,
+    const int32_t* __restrict__ offsets, int64_t T, int E, int k, int nbits,
+    int64_t C, int32_t* __restrict__ assign_row, int32_t* __restrict__ row_token) {
+  constexpr int TPW = 64 / KP;           // tokens per wave
+  __shared__ int32_t cnt[KP][1024];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tl = lane / KP, j = lane % KP;
+  const int64_t chunk = blockIdx.x;
+  const int64_t t = chunk * 64 + w * TPW + tl;
+  const bool valid = t < T && j < k;
+  int ex = valid ? idx[t * k + j] : 0;
+  // expert ids outside [0, E) take no row and do not count
+  const bool ok = valid && (unsigned)ex < (unsigned)E;
+  if (!ok) ex = 0;
+  for (int ww = 0; ww < KP; ++ww)
+    for (int e = tid; e < E; e += 64 * KP) cnt[ww][e] = 0;
+  __syncthreads();
+  if (ok) atomicAdd(&cnt[w][ex], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += 64 * KP) {
+    int run = chunk_base[chunk * gpc * E + e];
+#pragma unroll
+    for (int ww = 0; ww < KP; ++ww) {
+      const int c = cnt[ww][e];
+      cnt[ww][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const uint64_t below = tl == 0 ? 0ull : (~0ull >> (64 - KP * tl));
+  uint64_t m = __ballot(ok) & below;
+#pragma unroll
+  for (int b = 0; b < 10; ++b) {
+    if (b < nbits) {
+      const uint64_t bb = __ballot((ex >> b) & 1);
+      m &= ((ex >> b) & 1) ? bb : ~bb;
+    }
+  }
+  if (valid) {
+    int row = -1;
+    if (ok) {
+      const int rank = cnt[w][ex] + __popcll(m);
+      if (C == 0)
+        row = offsets[ex] + rank;
+      else
+        row = (rank < C) ? ex * (int)C + rank : -1;
+    }
+    assign_row[t * k + j] = row;
+    if (row >= 0) row_token[row] = (int32_t)t;
+  }
+}
+
 template <int KMAX>
 void launch_assign_t(const int32_t* idx, const int32_t* base, int hg, const int32_t* off,
                      int64_t T, int E, int k, int nbits, int64_t C, int32_t* ar,
@@ -457,6 +521,19 @@ hipError_t launch_assign(const int32_t* idx, const int32_t* chunk_base, int hg,
                          hipStream_t s) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  if (k > 2 && hg <= 64) {
+    const int64_t nch = (T + 63) / 64;
+    if (k <= 4)
+      MOE_LAUNCH(assign_pairs_kernel<4>, dim3((unsigned)nch), dim3(256), 0, s, idx, chunk_base,
+                 64 / hg, offsets, T, E, k, nbits, C, assign_row, row_token);
+    else if (k <= 8)
+      MOE_LAUNCH(assign_pairs_kernel<8>, dim3((unsigned)nch), dim3(512), 0, s, idx, chunk_base,
+                 64 / hg, offsets, T, E, k, nbits, C, assign_row, row_token);
+    else
+      MOE_LAUNCH(assign_pairs_kernel<16>, dim3((unsigned)nch), dim3(1024), 0, s, idx, chunk_base,
+                 64 / hg, offsets, T, E, k, nbits, C, assign_row, row_token);
+    return hipGetLastError();
+  }
   if (k <= 1)
     launch_assign_t<1>(idx, chunk_base, hg, offsets, T, E, k, nbits, C, assign_row, row_token, s);
   else if (k <= 2)
