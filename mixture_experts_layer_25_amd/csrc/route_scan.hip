@@ -106,15 +106,17 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   const int sl = tid / E, es = tid % E;
   const int64_t L = (nch + S - 1) / S;
   const int64_t g0 = sl * L, g1 = min(nch, g0 + L);
+  // 16 loads in flight per thread: with many experts a slice spans dozens
+  // of groups, and each batch costs one memory round trip
   if (sl < S) {
     int sum = 0;
     int64_t c = g0;
-    for (; c + 8 <= g1; c += 8) {
-      int v[8];
+    for (; c + 16 <= g1; c += 16) {
+      int v[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = chunk_hist[(c + i) * E + es];
+      for (int i = 0; i < 16; ++i) v[i] = chunk_hist[(c + i) * E + es];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sum += v[i];
+      for (int i = 0; i < 16; ++i) sum += v[i];
     }
     for (; c < g1; ++c) sum += chunk_hist[c * E + es];
     slice_sum[tid] = sum;
@@ -123,7 +125,18 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   if (sl < S) {
     int run = 0;
     for (int q = 0; q < sl; ++q) run += slice_sum[q * E + es];
-    for (int64_t c = g0; c < g1; ++c) {
+    int64_t c = g0;
+    for (; c + 16 <= g1; c += 16) {
+      int v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = chunk_hist[(c + i) * E + es];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        chunk_base[(c + i) * E + es] = run;
+        run += v[i];
+      }
+    }
+    for (; c < g1; ++c) {
       chunk_base[c * E + es] = run;
       run += chunk_hist[c * E + es];
     }
